@@ -1,0 +1,216 @@
+"""CPU oracle for the int4 dequantizing matmul -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the CPU-baseline leg of the benchmark may
+import this package.  The library never does, and shares no code with it.
+
+The arithmetic lives in ``q4_oracle.c`` (plain C, f64, one term at a time);
+this module compiles it with gcc into ``liboracle.so`` beside the source and
+wraps each entry point for numpy arrays.  See the C file's header for the
+format definition and the page citations.
+
+Parity status: every function here is pinned by the CPU tests in
+``tests/test_oracle_pins.py`` (exact rational brute force, closed forms, one-hot
+inputs, identities, the numpy f16 codec, and the byte-level layout spec); the
+mutation test in ``tests/test_oracle_mutants.py`` shows that plausible slips
+in the C source fail those pins.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "q4_oracle.c")
+LIBRARY = os.path.join(HERE, "liboracle.so")
+
+CFLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
+          "-fno-fast-math", "-Wall", "-Wextra"]
+
+
+def build(out: str = LIBRARY, source: str = SOURCE) -> str:
+    """Compile the oracle with gcc; returns the library path."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.run(["gcc", *CFLAGS, source, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+class Oracle:
+    """numpy-facing wrapper around one loaded oracle library."""
+
+    def __init__(self, path: str):
+        self.path = path
+        lib = ctypes.CDLL(path)
+        lib.q4o_half_to_double.argtypes = [ctypes.c_uint16]
+        lib.q4o_half_to_double.restype = ctypes.c_double
+        lib.q4o_double_to_half.argtypes = [ctypes.c_double]
+        lib.q4o_double_to_half.restype = ctypes.c_uint16
+        lib.q4o_gemv.argtypes = [_P, _P, _P, _I64, _I64, _P, _P]
+        lib.q4o_gemv.restype = ctypes.c_int
+        lib.q4o_gemm.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P, _P]
+        lib.q4o_gemm.restype = ctypes.c_int
+        lib.q4o_silu.argtypes = [ctypes.c_double]
+        lib.q4o_silu.restype = ctypes.c_double
+        lib.q4o_ffn_gate_up_silu.argtypes = [_P, _P, _P, _P, _P, _I64, _I64,
+                                             _P, _P, _P, _P, _P]
+        lib.q4o_ffn_gate_up_silu.restype = ctypes.c_int
+        lib.q4o_argmax.argtypes = [_P, _I64]
+        lib.q4o_argmax.restype = ctypes.c_int64
+        lib.q4o_lmhead.argtypes = [_P, _P, _P, _I64, _I64, _P, _P]
+        lib.q4o_lmhead.restype = ctypes.c_int64
+        lib.q4o_layout_geometry.argtypes = [_I64, _I64, _P]
+        lib.q4o_layout_geometry.restype = ctypes.c_int
+        lib.q4o_layout_bytes.argtypes = [_I64, _I64]
+        lib.q4o_layout_bytes.restype = ctypes.c_int64
+        lib.q4o_encode_rows.argtypes = [_P, _P, _I64, _I64, _P]
+        lib.q4o_encode_rows.restype = ctypes.c_int
+        lib.q4o_encode_gate_up.argtypes = [_P, _P, _P, _P, _I64, _I64, _P]
+        lib.q4o_encode_gate_up.restype = ctypes.c_int
+        self.lib = lib
+
+    # -- f16 codec -------------------------------------------------------
+    def half_to_double(self, bits: int) -> float:
+        return self.lib.q4o_half_to_double(int(bits))
+
+    def double_to_half(self, v: float) -> int:
+        return int(self.lib.q4o_double_to_half(float(v)))
+
+    def halves_to_doubles(self, bits: np.ndarray) -> np.ndarray:
+        flat = np.ascontiguousarray(bits, dtype=np.uint16).ravel()
+        out = np.fromiter((self.lib.q4o_half_to_double(int(b)) for b in flat),
+                          dtype=np.float64, count=flat.size)
+        return out.reshape(np.shape(bits))
+
+    def doubles_to_halves(self, v: np.ndarray) -> np.ndarray:
+        flat = np.ascontiguousarray(v, dtype=np.float64).ravel()
+        out = np.fromiter((self.lib.q4o_double_to_half(float(x)) for x in flat),
+                          dtype=np.uint16, count=flat.size)
+        return out.reshape(np.shape(v))
+
+    # -- the matmul and its variants -------------------------------------
+    @staticmethod
+    def _check_w(words, scales, n, k):
+        assert words.dtype == np.uint32 and words.shape == (n, k // 8)
+        assert scales.dtype == np.uint16 and scales.shape == (n, k // 32)
+
+    def gemv(self, words, scales, x):
+        """(y, a) in f64: y = x.dequant(W)^T, a = sum |x_k w_k|."""
+        n = words.shape[0]
+        k = x.shape[0]
+        self._check_w(words, scales, n, k)
+        words, scales = np.ascontiguousarray(words), np.ascontiguousarray(scales)
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        y = np.empty(n, np.float64)
+        a = np.empty(n, np.float64)
+        rc = self.lib.q4o_gemv(_ptr(words), _ptr(scales), _ptr(x), n, k,
+                               _ptr(y), _ptr(a))
+        assert rc == 0
+        return y, a
+
+    def gemm(self, words, scales, X):
+        m, k = X.shape
+        n = words.shape[0]
+        self._check_w(words, scales, n, k)
+        words, scales = np.ascontiguousarray(words), np.ascontiguousarray(scales)
+        X = np.ascontiguousarray(X, dtype=np.uint16)
+        Y = np.empty((m, n), np.float64)
+        A = np.empty((m, n), np.float64)
+        rc = self.lib.q4o_gemm(_ptr(words), _ptr(scales), _ptr(X), m, n, k,
+                               _ptr(Y), _ptr(A))
+        assert rc == 0
+        return Y, A
+
+    def silu(self, g: float) -> float:
+        return self.lib.q4o_silu(float(g))
+
+    def ffn_gate_up_silu(self, gw, gs, uw, us, x):
+        """dict with h, g, u, ag, au (all f64 [n])."""
+        n = gw.shape[0]
+        k = x.shape[0]
+        self._check_w(gw, gs, n, k)
+        self._check_w(uw, us, n, k)
+        arrs = [np.ascontiguousarray(a) for a in (gw, gs, uw, us)]
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        out = {name: np.empty(n, np.float64) for name in ("h", "g", "u", "ag", "au")}
+        rc = self.lib.q4o_ffn_gate_up_silu(
+            *[_ptr(a) for a in arrs], _ptr(x), n, k,
+            *[_ptr(out[name]) for name in ("h", "g", "u", "ag", "au")])
+        assert rc == 0
+        return out
+
+    def argmax(self, v) -> int:
+        v = np.ascontiguousarray(v, dtype=np.float64)
+        return int(self.lib.q4o_argmax(_ptr(v), v.size))
+
+    def lmhead(self, words, scales, x):
+        """(logits f64, a f64, argmax index)."""
+        n = words.shape[0]
+        k = x.shape[0]
+        self._check_w(words, scales, n, k)
+        words, scales = np.ascontiguousarray(words), np.ascontiguousarray(scales)
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        y = np.empty(n, np.float64)
+        a = np.empty(n, np.float64)
+        idx = self.lib.q4o_lmhead(_ptr(words), _ptr(scales), _ptr(x), n, k,
+                                  _ptr(y), _ptr(a))
+        return y, a, int(idx)
+
+    # -- device layout encoder (for the byte-exact pack test) ------------
+    def layout_geometry(self, rows: int, k: int) -> dict:
+        out = np.zeros(6, np.int64)
+        rc = self.lib.q4o_layout_geometry(rows, k, _ptr(out))
+        assert rc == 0
+        return dict(zip(("L", "CG", "P", "TR", "tiles", "tile_bytes"),
+                        (int(v) for v in out)))
+
+    def layout_bytes(self, rows: int, k: int) -> int:
+        return int(self.lib.q4o_layout_bytes(rows, k))
+
+    def encode_rows(self, words, scales) -> np.ndarray:
+        n, k = words.shape[0], words.shape[1] * 8
+        self._check_w(words, scales, n, k)
+        words, scales = np.ascontiguousarray(words), np.ascontiguousarray(scales)
+        dst = np.full(self.layout_bytes(n, k), 0xA5, np.uint8)
+        rc = self.lib.q4o_encode_rows(_ptr(words), _ptr(scales), n, k, _ptr(dst))
+        assert rc == 0
+        return dst
+
+    def encode_gate_up(self, gw, gs, uw, us) -> np.ndarray:
+        n, k = gw.shape[0], gw.shape[1] * 8
+        self._check_w(gw, gs, n, k)
+        self._check_w(uw, us, n, k)
+        arrs = [np.ascontiguousarray(a) for a in (gw, gs, uw, us)]
+        dst = np.full(self.layout_bytes(2 * n, k), 0xA5, np.uint8)
+        rc = self.lib.q4o_encode_gate_up(*[_ptr(a) for a in arrs], n, k, _ptr(dst))
+        assert rc == 0
+        return dst
+
+
+_DEFAULT: Optional[Oracle] = None
+
+
+def load(path: Optional[str] = None) -> Oracle:
+    """Load the oracle (building it first if the library is missing or older
+    than its source)."""
+    global _DEFAULT
+    if path is not None:
+        return Oracle(path)
+    if _DEFAULT is None:
+        if (not os.path.exists(LIBRARY) or
+                os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE)):
+            build()
+        _DEFAULT = Oracle(LIBRARY)
+    return _DEFAULT

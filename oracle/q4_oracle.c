@@ -1,0 +1,360 @@
+/*
+ * q4_oracle.c -- plain, slow, obviously correct CPU reference for the int4
+ * dequantizing matrix multiply.  TEST INFRASTRUCTURE ONLY: it is loaded by the
+ * tests, by the smoke check and by the CPU-baseline leg of the benchmark, and
+ * never by the library.  It shares no source with the HIP path.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [P1] "Zero-TVM：手写 WGSL 着色器在浏览器中运行 Phi-3-mini，挑战编译器霸权"
+ *        (zingnex.cn forum article).  Section 完整的推理流水线 names the int4
+ *        dequantizing matmul as the core of decode, with an f32-output variant
+ *        for the LM head and a greedy argmax dispatch; section 内核融合 fuses
+ *        gate, up and SiLU into one pass; section 性能基准 says matmul and int4
+ *        dequant are where the time goes; 技术栈对比 / 性能基准 name the weights
+ *        "Phi-3-mini q4f16_1".
+ *   [P4] the Zero-TVM README (abgnydn/zero-tvm): repacking is tested
+ *        byte-for-byte; every kernel is tested against a plain reference.
+ *
+ * The pages name the weight format (q4f16_1: 4-bit codes with f16 scales) but
+ * never define it bit by bit.  This library's definition, which the oracle
+ * follows literally:
+ *   - codes q in 0..15, packed 8 per uint32 along K; code k = 8*j + i of a row
+ *     sits in bits 4*i .. 4*i+3 of that row's word j (low nibble first);
+ *   - one f16 scale per group of 32 consecutive k of a row; scales [N][K/32];
+ *   - weight value w = (q - 8) * scale;
+ *   - y[n] = sum_k x[k] * w[n][k].
+ * Everything is computed in IEEE double (f64), k ascending, one term at a time.
+ * Each product x*(q-8)*s needs at most 11+4+11 = 26 significant bits, so the
+ * products are exact in f64; only the running sum rounds.
+ *
+ * Also here: an f16 decoder and an f64->f16 round-to-nearest-even encoder of
+ * its own, and an encoder of the library's device layout (layout version 1),
+ * written from that layout's specification by walking the logical matrix and
+ * computing each destination address.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ f16 -- */
+
+/* IEEE 754 binary16 bits -> double.  Normal: (1024+m) * 2^(e-25);
+ * subnormal: m * 2^-24; e == 31: infinity or NaN. */
+double q4o_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int m = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);
+    return sign ? -v : v;
+}
+
+/* round a non-negative double (< 2^52) to the nearest integer, ties to even */
+static double round_half_even(double q)
+{
+    double f = floor(q);
+    double d = q - f;            /* exact for q < 2^52 */
+    if (d > 0.5)
+        return f + 1.0;
+    if (d < 0.5)
+        return f;
+    return (fmod(f, 2.0) == 0.0) ? f : f + 1.0;
+}
+
+/* double -> binary16 bits, round to nearest, ties to even; overflow -> inf */
+uint16_t q4o_double_to_half(double v)
+{
+    if (isnan(v))
+        return 0x7e00;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isinf(a))
+        return sign | 0x7c00;
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal range: count units of 2^-24; 1024 units is the smallest
+         * normal, whose encoding 0x0400 is the same integer */
+        double r = round_half_even(ldexp(a, 24));
+        return sign | (uint16_t)r;
+    }
+    int e2;
+    frexp(a, &e2);               /* a = f * 2^e2, f in [0.5, 1) */
+    int E = e2 - 1;              /* 2^E <= a < 2^(E+1) */
+    double r = round_half_even(ldexp(a, 10 - E)); /* in [1024, 2048] */
+    if (r == 2048.0) {
+        r = 1024.0;
+        E += 1;
+    }
+    if (E > 15)
+        return sign | 0x7c00;
+    return sign | (uint16_t)((E + 15) << 10) | (uint16_t)(r - 1024.0);
+}
+
+/* ------------------------------------------------------- the definition -- */
+
+/* code of row r at position kk (K = k columns): word kk/8, nibble kk%8 */
+static int code_at(const uint32_t *words, int64_t r, int64_t kk, int64_t k)
+{
+    uint32_t word = words[r * (k / 8) + kk / 8];
+    return (int)((word >> (4 * (kk % 8))) & 15u);
+}
+
+/* dequantized weight w[r][kk] = (q - 8) * scale, exact in f64 */
+static double weight_at(const uint32_t *words, const uint16_t *scales,
+                        int64_t r, int64_t kk, int64_t k)
+{
+    int q = code_at(words, r, kk, k);
+    double s = q4o_half_to_double(scales[r * (k / 32) + kk / 32]);
+    return (double)(q - 8) * s;
+}
+
+/*
+ * y = x . dequant(W)^T for one activation vector ([P1] 完整的推理流水线).
+ * words [n][k/8], scales [n][k/32], x [k] f16 bits.
+ * y[r] = sum_k x_k * w[r][k]; a[r] = sum_k |x_k * w[r][k]| (the magnitude sum
+ * that sizes the tolerance).  a may be NULL.  Returns 0, or -1 on a bad shape.
+ */
+int q4o_gemv(const uint32_t *words, const uint16_t *scales, const uint16_t *x,
+             int64_t n, int64_t k, double *y, double *a)
+{
+    if (n < 0 || k < 32 || k % 32 != 0)
+        return -1;
+    for (int64_t r = 0; r < n; ++r) {
+        double sum = 0.0, asum = 0.0;
+        for (int64_t kk = 0; kk < k; ++kk) {
+            double term = q4o_half_to_double(x[kk]) *
+                          weight_at(words, scales, r, kk, k);
+            sum += term;
+            asum += fabs(term);
+        }
+        y[r] = sum;
+        if (a)
+            a[r] = asum;
+    }
+    return 0;
+}
+
+/*
+ * Y = X . dequant(W)^T for m activation rows (the batched form of the same
+ * matmul).  X [m][k] f16 bits row-major; Y, A [m][n] row-major.
+ */
+int q4o_gemm(const uint32_t *words, const uint16_t *scales, const uint16_t *X,
+             int64_t m, int64_t n, int64_t k, double *Y, double *A)
+{
+    if (m < 0 || n < 0 || k < 32 || k % 32 != 0)
+        return -1;
+    for (int64_t i = 0; i < m; ++i) {
+        int rc = q4o_gemv(words, scales, X + i * k, n, k, Y + i * n,
+                          A ? A + i * n : NULL);
+        if (rc)
+            return rc;
+    }
+    return 0;
+}
+
+/* SiLU(g) = g * sigmoid(g) = g / (1 + e^-g) */
+double q4o_silu(double g)
+{
+    return g / (1.0 + exp(-g));
+}
+
+/*
+ * Fused gate/up + SiLU ([P1] 内核融合, fused_ffn): h = SiLU(x.Wg^T) * (x.Wu^T),
+ * elementwise over the n intermediate rows.  Also returns the gate and up
+ * pre-activations and their magnitude sums (any of g, u, ag, au may be NULL).
+ */
+int q4o_ffn_gate_up_silu(const uint32_t *gw, const uint16_t *gs,
+                         const uint32_t *uw, const uint16_t *us,
+                         const uint16_t *x, int64_t n, int64_t k, double *h,
+                         double *g, double *u, double *ag, double *au)
+{
+    if (n < 0 || k < 32 || k % 32 != 0)
+        return -1;
+    for (int64_t r = 0; r < n; ++r) {
+        double gv, uv, agv, auv;
+        q4o_gemv(gw + r * (k / 8), gs + r * (k / 32), x, 1, k, &gv, &agv);
+        q4o_gemv(uw + r * (k / 8), us + r * (k / 32), x, 1, k, &uv, &auv);
+        h[r] = q4o_silu(gv) * uv;
+        if (g)
+            g[r] = gv;
+        if (u)
+            u[r] = uv;
+        if (ag)
+            ag[r] = agv;
+        if (au)
+            au[r] = auv;
+    }
+    return 0;
+}
+
+/* greedy argmax ([P1] 完整的推理流水线, 贪婪解码采样): the lowest index that
+ * holds the maximum.  Returns -1 for n < 1. */
+int64_t q4o_argmax(const double *v, int64_t n)
+{
+    if (n < 1)
+        return -1;
+    int64_t best = 0;
+    for (int64_t i = 1; i < n; ++i)
+        if (v[i] > v[best])
+            best = i;
+    return best;
+}
+
+/*
+ * LM head with f32 logits ([P1] 完整的推理流水线): the same matmul; the
+ * oracle keeps f64 logits, and returns the greedy argmax of them.
+ */
+int64_t q4o_lmhead(const uint32_t *words, const uint16_t *scales,
+                   const uint16_t *x, int64_t n, int64_t k, double *logits,
+                   double *a)
+{
+    if (q4o_gemv(words, scales, x, n, k, logits, a))
+        return -1;
+    return q4o_argmax(logits, n);
+}
+
+/* --------------------------------------------- device layout, version 1 --
+ *
+ * Specification (the library's own design; no page describes one):
+ *   G = k/32 groups per row.  P = ceil(G/256) passes; Gp = ceil(G/P).
+ *   (L, CG): L in {64,32,16,8,4,2,1} lanes per row, CG in {1,2,3,4} groups per
+ *   lane, with L*CG >= Gp; the least L*CG wins, ties go to the larger L.
+ *   U = 2 rows per lane slot; RW = 64/L slots; TR = 2*RW rows per tile.
+ *   Tiles T = ceil(rows / TR); pass bytes PB = CG*2304; tile bytes TB = P*PB.
+ *   Logical (row r, group g) with r < T*TR and g < P*L*CG lives at
+ *     t = r / TR, s = (r % TR) / 2, u = r % 2,
+ *     p = g / (L*CG), c = (g % (L*CG)) / CG, j = g % CG, lane = s*L + c,
+ *     codes (4 words, canonical order) at t*TB + p*PB + (u*CG + j)*1024 + lane*16,
+ *     scale (f16)                      at t*TB + p*PB + 2*CG*1024 + lane*4*CG
+ *                                          + (u*CG + j)*2.
+ *   Rows >= rows or groups >= G are padding: words 0x88888888, scale 0x0000.
+ *   Gate/up layout: logical row 2i is gate row i, row 2i+1 is up row i
+ *   (2n logical rows in all), then the same placement.
+ */
+static void geometry(int64_t k, int *L_out, int *CG_out, int *P_out)
+{
+    int64_t G = k / 32;
+    int64_t P = (G + 255) / 256;
+    int64_t Gp = (G + P - 1) / P;
+    int bestL = 0, bestCG = 0;
+    int64_t bestCover = 0;
+    for (int L = 64; L >= 1; L /= 2) {
+        for (int CG = 1; CG <= 4; ++CG) {
+            int64_t cover = (int64_t)L * CG;
+            if (cover < Gp)
+                continue;
+            if (bestL == 0 || cover < bestCover) {
+                bestL = L;
+                bestCG = CG;
+                bestCover = cover;
+            }
+        }
+    }
+    *L_out = bestL;
+    *CG_out = bestCG;
+    *P_out = (int)P;
+}
+
+/* geometry as seen by the tests: out[0..5] = L, CG, P, TR, tiles, tile bytes */
+int q4o_layout_geometry(int64_t rows, int64_t k, int64_t *out)
+{
+    if (rows < 1 || k < 32 || k % 32 != 0)
+        return -1;
+    int L, CG, P;
+    geometry(k, &L, &CG, &P);
+    int64_t TR = 2 * (64 / L);
+    out[0] = L;
+    out[1] = CG;
+    out[2] = P;
+    out[3] = TR;
+    out[4] = (rows + TR - 1) / TR;
+    out[5] = (int64_t)P * CG * 2304;
+    return 0;
+}
+
+/* bytes of the device layout for `rows` logical rows (gate/up: 2n) */
+int64_t q4o_layout_bytes(int64_t rows, int64_t k)
+{
+    int64_t g[6];
+    if (q4o_layout_geometry(rows, k, g))
+        return 0;
+    return g[4] * g[5];
+}
+
+/* place one logical (row, group) at its destination; src words may be NULL
+ * (padding) */
+static void place(uint8_t *dst, int64_t r, int64_t g, int L, int CG,
+                  int64_t TR, int64_t TB, const uint32_t *src_words,
+                  uint16_t src_scale)
+{
+    int64_t PB = (int64_t)CG * 2304;
+    int64_t t = r / TR, s = (r % TR) / 2, u = r % 2;
+    int64_t p = g / ((int64_t)L * CG);
+    int64_t c = (g % ((int64_t)L * CG)) / CG, j = g % CG;
+    int64_t lane = s * L + c;
+    int64_t base = t * TB + p * PB;
+    uint8_t *code_dst = dst + base + (u * CG + j) * 1024 + lane * 16;
+    uint8_t *scale_dst = dst + base + (int64_t)2 * CG * 1024 + lane * 4 * CG +
+                         (u * CG + j) * 2;
+    for (int w = 0; w < 4; ++w) {
+        uint32_t word = src_words ? src_words[w] : 0x88888888u;
+        memcpy(code_dst + 4 * w, &word, 4); /* little-endian, as on the GPU */
+    }
+    memcpy(scale_dst, &src_scale, 2);
+}
+
+/* shared walk: logical row r is produced by `pick` (gate/up interleave or
+ * plain rows) */
+static int encode(const uint32_t *w0, const uint16_t *s0, const uint32_t *w1,
+                  const uint16_t *s1, int64_t rows, int64_t k, int interleave,
+                  uint8_t *dst)
+{
+    int64_t geo[6];
+    if (q4o_layout_geometry(rows, k, geo))
+        return -1;
+    int L = (int)geo[0], CG = (int)geo[1], P = (int)geo[2];
+    int64_t TR = geo[3], T = geo[4], TB = geo[5];
+    int64_t G = k / 32;
+    for (int64_t r = 0; r < T * TR; ++r) {
+        const uint32_t *rw = NULL;
+        const uint16_t *rs = NULL;
+        if (r < rows) {
+            if (interleave) {
+                int64_t i = r / 2;
+                rw = (r % 2 ? w1 : w0) + i * (k / 8);
+                rs = (r % 2 ? s1 : s0) + i * G;
+            } else {
+                rw = w0 + r * (k / 8);
+                rs = s0 + r * G;
+            }
+        }
+        for (int64_t g = 0; g < (int64_t)P * L * CG; ++g) {
+            if (rw && g < G)
+                place(dst, r, g, L, CG, TR, TB, rw + 4 * g, rs[g]);
+            else
+                place(dst, r, g, L, CG, TR, TB, NULL, 0);
+        }
+    }
+    return 0;
+}
+
+/* plain row layout of words [n][k/8], scales [n][k/32] */
+int q4o_encode_rows(const uint32_t *words, const uint16_t *scales, int64_t n,
+                    int64_t k, uint8_t *dst)
+{
+    return encode(words, scales, NULL, NULL, n, k, 0, dst);
+}
+
+/* gate/up interleaved layout: 2n logical rows */
+int q4o_encode_gate_up(const uint32_t *gw, const uint16_t *gs,
+                       const uint32_t *uw, const uint16_t *us, int64_t n,
+                       int64_t k, uint8_t *dst)
+{
+    return encode(gw, gs, uw, us, 2 * n, k, 1, dst);
+}

@@ -1,0 +1,369 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each ``pin_*`` function takes a loaded ``oracle.Oracle`` and raises
+AssertionError when the oracle disagrees with what mathematics or the format
+definition fixes.  ``tests/test_oracle_pins.py`` runs them on the real oracle;
+``tests/test_oracle_mutants.py`` runs them on deliberately broken copies of the
+oracle's C source and requires every copy to fail at least one pin.
+
+What pins what:
+  * f16 decode    : all 65,536 patterns vs numpy and vs Python's struct codec.
+  * f16 encode    : random doubles, exact ties, subnormals and overflow vs
+                    numpy's correctly rounded conversion.
+  * matmul        : exact rational brute force (fractions) on tiny shapes with
+                    every code value, within the f64 summation error bound and
+                    bit-exact where the exact sum is representable; closed
+                    forms (constant codes); one-hot x across word and group
+                    boundaries; linearity identities.
+  * SiLU / FFN    : silu(0)=0, silu(ln 3)=(3/4)ln 3, silu(-g)=silu(g)-g, the
+                    gate (not up) is the one gated.
+  * argmax        : planted maximum, ties go to the lowest index.
+  * device layout : hand-derived geometry table (tests/golden), a byte-level
+                    hand example, and a decoder written in the opposite
+                    direction (destination -> logical) over random shapes.
+"""
+from __future__ import annotations
+
+import math
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+
+import seeded_inputs as si
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+U64 = 2.0 ** -53   # unit roundoff of f64
+
+
+def half_fraction(bits: int) -> Fraction:
+    """Exact value of an f16 pattern via Python's own binary16 codec."""
+    return Fraction(struct.unpack("<e", struct.pack("<H", int(bits)))[0])
+
+
+def exact_gemv(codes: np.ndarray, scales: np.ndarray, x: np.ndarray):
+    """Exact rational y and sum|terms| for codes [n][k] (integers 0..15)."""
+    n, k = codes.shape
+    xs = [half_fraction(b) for b in x]
+    ys, as_ = [], []
+    for r in range(n):
+        s_row = [half_fraction(b) for b in scales[r]]
+        tot = Fraction(0)
+        mag = Fraction(0)
+        for kk in range(k):
+            t = xs[kk] * (int(codes[r, kk]) - 8) * s_row[kk // 32]
+            tot += t
+            mag += abs(t)
+        ys.append(tot)
+        as_.append(mag)
+    return ys, as_
+
+
+# ---------------------------------------------------------------- f16 codec
+def pin_half_decode_all_patterns(orc, quick=False):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = orc.halves_to_doubles(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signs of zeros and the struct codec as a second reference
+    assert math.copysign(1.0, orc.half_to_double(0x8000)) == -1.0
+    step = 97 if quick else 7
+    for b in range(0, 65536, step):
+        if (b & 0x7C00) != 0x7C00:
+            assert orc.half_to_double(b) == float(half_fraction(b)), hex(b)
+
+
+def pin_half_encode_rne(orc, quick=False):
+    rng = np.random.default_rng(1234)
+    cnt = 20000 if quick else 300000
+    parts = [
+        rng.standard_normal(cnt // 4) * 10.0 ** rng.integers(-9, 6, cnt // 4),
+        rng.uniform(-70000, 70000, cnt // 8),
+        rng.uniform(-1e-4, 1e-4, cnt // 8),      # around the subnormal range
+    ]
+    # exact midpoints between neighbouring f16 values: ties must go to even
+    b = rng.integers(0, 0x7bff, cnt // 4, dtype=np.int64).astype(np.uint16)
+    lo = b.view(np.float16).astype(np.float64)
+    hi = (b + 1).astype(np.uint16).view(np.float16).astype(np.float64)
+    mids = (lo + hi) / 2.0
+    parts += [mids, -mids,
+              np.array([65504.0, 65519.99, 65520.0, 1e6, -1e6, 2.0 ** -25,
+                        2.0 ** -25 * 3, 2.0 ** -24 * 1.5, 0.0, -0.0,
+                        2.0 ** -14 - 2.0 ** -25, 6.1e-5])]
+    v = np.concatenate(parts)
+    ref = v.astype(np.float16).view(np.uint16)
+    got = orc.doubles_to_halves(v)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(v[i], hex(ref[i]), hex(got[i])) for i in bad[:5]]
+    assert orc.double_to_half(float("inf")) == 0x7C00
+    assert orc.double_to_half(float("-inf")) == 0xFC00
+    assert (orc.double_to_half(float("nan")) & 0x7C00) == 0x7C00
+
+
+# ------------------------------------------------------------------ matmul
+def _tiny_cases(quick):
+    shapes = [(1, 32), (2, 64), (3, 96), (17, 32)] if not quick else \
+             [(1, 32), (3, 96), (17, 32)]
+    rng = np.random.default_rng(77)
+    for n, k in shapes:
+        codes = rng.integers(0, 16, (n, k), dtype=np.uint8)
+        codes.ravel()[:16] = np.arange(16)          # every code value appears
+        scales = si.f16_bits(rng.uniform(-0.05, 0.05, (n, k // 32)))
+        x = si.f16_bits(rng.standard_normal(k) * 2.0)
+        yield codes, scales, x
+
+
+def pin_gemv_rational(orc, quick=False):
+    for codes, scales, x in _tiny_cases(quick):
+        words = si.pack_codes(codes)
+        y, a = orc.gemv(words, scales, x)
+        ey, ea = exact_gemv(codes, scales, x)
+        k = codes.shape[1]
+        for r in range(codes.shape[0]):
+            bound = (k * U64 / (1 - k * U64)) * float(ea[r])
+            assert abs(Fraction(y[r]) - ey[r]) <= Fraction(bound), (r, y[r], float(ey[r]))
+            assert abs(Fraction(a[r]) - ea[r]) <= Fraction(bound), (r, a[r], float(ea[r]))
+
+
+def pin_gemv_exactly_representable(orc, quick=False):
+    """x in {-4..4}/4, scales in {2^-7, 2^-8}: every term and partial sum is a
+    multiple of 2^-10 well inside 53 bits, so f64 must be exact."""
+    rng = np.random.default_rng(5)
+    n, k = (5, 256) if quick else (9, 1024)
+    codes = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    scales = si.f16_bits(2.0 ** -rng.integers(7, 9, (n, k // 32)))
+    x = si.f16_bits(rng.integers(-4, 5, k) / 4.0)
+    y, a = orc.gemv(si.pack_codes(codes), scales, x)
+    ey, ea = exact_gemv(codes, scales, x)
+    assert [Fraction(v) for v in y] == ey
+    assert [Fraction(v) for v in a] == ea
+
+
+def pin_gemv_closed_forms(orc, quick=False):
+    k = 3072
+    x = si.f16_bits(np.ones(k))
+    # c = 15, s = 2^-6, x = 1: y = 7 * 2^-6 * 3072 = 336 exactly
+    words = si.pack_codes(np.full((2, k), 15, np.uint8))
+    scales = si.f16_bits(np.full((2, k // 32), 2.0 ** -6))
+    y, a = orc.gemv(words, scales, x)
+    assert list(y) == [336.0, 336.0] and list(a) == [336.0, 336.0]
+    # constant code c, scale s, random x: y = (c - 8) * s * sum(x), exactly
+    rng = np.random.default_rng(9)
+    xr = si.f16_bits(rng.standard_normal(256))
+    sx = sum(half_fraction(b) for b in xr)
+    for c in (0, 3, 8, 12, 15):
+        words = si.pack_codes(np.full((1, 256), c, np.uint8))
+        s = si.f16_bits(np.full((1, 8), 0.0126953125))
+        y, _ = orc.gemv(words, s, xr)
+        exact = (c - 8) * Fraction(0.0126953125) * sx
+        mag = abs(c - 8) * Fraction(0.0126953125) * sum(abs(half_fraction(b)) for b in xr)
+        assert abs(Fraction(y[0]) - exact) <= Fraction(2 * 256 * U64) * mag, \
+            (c, y[0], float(exact))
+        if c == 8:
+            assert y[0] == 0.0 and math.copysign(1.0, y[0]) == 1.0
+
+
+def pin_gemv_one_hot(orc, quick=False):
+    rng = np.random.default_rng(11)
+    n, k = 7, 128
+    codes = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    scales = si.f16_bits(rng.uniform(0.005, 0.02, (n, k // 32)))
+    words = si.pack_codes(codes)
+    positions = [0, 1, 7, 8, 15, 31, 32, 33, 63, 64, 95, 100, 127]
+    for kk in positions:
+        x = np.zeros(k, np.uint16)
+        x[kk] = 0x3C00          # 1.0
+        y, _ = orc.gemv(words, scales, x)
+        for r in range(n):
+            want = (int(codes[r, kk]) - 8) * half_fraction(scales[r, kk // 32])
+            assert Fraction(y[r]) == want, (kk, r)
+
+
+def pin_gemv_linearity(orc, quick=False):
+    rng = np.random.default_rng(13)
+    w, s = si.draw_weight(rng, 6, 96)
+    x = si.draw_x(rng, 96)
+    y, a = orc.gemv(w, s, x)
+    x2 = si.f16_bits(x.view(np.float16).astype(np.float64) * 2.0)
+    xn = x ^ np.uint16(0x8000)
+    y2, a2 = orc.gemv(w, s, x2)
+    yn, an = orc.gemv(w, s, xn)
+    assert np.array_equal(y2, 2.0 * y) and np.array_equal(a2, 2.0 * a)
+    assert np.array_equal(yn, -y) and np.array_equal(an, a)
+
+
+def pin_gemm_rows(orc, quick=False):
+    """each row of the batched form is the single-vector form; and a closed
+    form: X row i all (i+1)/4, constant code 12, scale 2^-5 -> 4*(i+1)/4*2^-5*k."""
+    rng = np.random.default_rng(17)
+    w, s = si.draw_weight(rng, 5, 64)
+    X = si.draw_X(rng, 3, 64)
+    Y, A = orc.gemm(w, s, X)
+    for i in range(3):
+        y, a = orc.gemv(w, s, X[i])
+        assert np.array_equal(Y[i], y) and np.array_equal(A[i], a)
+    k = 96
+    words = si.pack_codes(np.full((4, k), 12, np.uint8))
+    scales = si.f16_bits(np.full((4, k // 32), 2.0 ** -5))
+    X = si.f16_bits(np.repeat((np.arange(3)[:, None] + 1) / 4.0, k, axis=1))
+    Y, _ = orc.gemm(words, scales, X)
+    for i in range(3):
+        assert np.all(Y[i] == 4 * (i + 1) / 4.0 * 2.0 ** -5 * k)
+
+
+# -------------------------------------------------------------- SiLU / FFN
+def pin_silu(orc, quick=False):
+    assert orc.silu(0.0) == 0.0
+    ln3 = math.log(3.0)
+    assert abs(orc.silu(ln3) - 0.75 * ln3) <= 4 * U64 * ln3
+    for g in (0.1, 0.5, 1.0, 2.5, 7.0, 20.0):
+        assert abs(orc.silu(-g) - (orc.silu(g) - g)) <= 8 * U64 * max(1.0, g)
+    assert orc.silu(40.0) == 40.0
+    assert -1e-12 < orc.silu(-40.0) < 0.0
+
+
+def pin_ffn(orc, quick=False):
+    """gate codes c_g, up codes c_u, x = 1: g = (c_g-8) s_g k, u = (c_u-8) s_u k;
+    h = g * sigmoid(g) * u.  Gate 8 -> h = 0; up 8 -> h = 0; the gate is the
+    gated half (silu applied to g, not to u)."""
+    k, n = 64, 3
+    x = si.f16_bits(np.ones(k))
+    def w_const(c, s):
+        return (si.pack_codes(np.full((n, k), c, np.uint8)),
+                si.f16_bits(np.full((n, k // 32), s)))
+    for cg, cu, sg, su in ((10, 13, 2.0 ** -5, 2.0 ** -6), (5, 14, 2.0 ** -4, 2.0 ** -3),
+                           (8, 13, 2.0 ** -5, 2.0 ** -6), (12, 8, 2.0 ** -5, 2.0 ** -6)):
+        gw, gs = w_const(cg, sg)
+        uw, us = w_const(cu, su)
+        out = orc.ffn_gate_up_silu(gw, gs, uw, us, x)
+        g = (cg - 8) * sg * k
+        u = (cu - 8) * su * k
+        want = g / (1.0 + math.exp(-g)) * u
+        assert np.all(np.abs(out["h"] - want) <= 8 * U64 * abs(want)), (cg, cu, out["h"], want)
+        assert np.all(out["g"] == g) and np.all(out["u"] == u)
+        assert np.all(out["ag"] == abs(g)) and np.all(out["au"] == abs(u))
+
+
+# ------------------------------------------------------------------ argmax
+def pin_argmax(orc, quick=False):
+    assert orc.argmax(np.array([1.0, 3.0, 2.0])) == 1
+    assert orc.argmax(np.array([5.0, 5.0, 5.0])) == 0
+    assert orc.argmax(np.array([-3.0, -1.0, -1.0, -2.0])) == 1
+    v = np.random.default_rng(3).standard_normal(1000)
+    v[417] = 10.0
+    v[901] = 10.0
+    assert orc.argmax(v) == 417
+
+
+def pin_lmhead(orc, quick=False):
+    """planted winner (all codes 15, x = 1) and a planted exact tie (two equal
+    rows) resolve to the lowest index; logits are the matmul."""
+    rng = np.random.default_rng(23)
+    n, k = 40, 96
+    codes = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    codes[29] = 15
+    codes[33] = 15
+    scales = si.f16_bits(rng.uniform(0.005, 0.02, (n, k // 32)))
+    scales[33] = scales[29]
+    words = si.pack_codes(codes)
+    x = si.f16_bits(np.ones(k))
+    logits, a, idx = orc.lmhead(words, scales, x)
+    y, _ = orc.gemv(words, scales, x)
+    assert np.array_equal(logits, y) and idx == 29
+
+
+# ----------------------------------------------------------- device layout
+def load_geometry_golden():
+    rows = []
+    with open(os.path.join(GOLDEN, "layout_geometry.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append([int(t) for t in line.split()])
+    return rows
+
+
+def pin_layout_geometry(orc, quick=False):
+    for rows, k, L, CG, P, TR, tiles, tb in load_geometry_golden():
+        got = orc.layout_geometry(rows, k)
+        assert got == dict(L=L, CG=CG, P=P, TR=TR, tiles=tiles, tile_bytes=tb), \
+            (rows, k, got)
+        assert orc.layout_bytes(rows, k) == tiles * tb
+
+
+def pin_layout_hand_example(orc, quick=False):
+    """rows = 1, k = 32: one tile of 2304 bytes with L = 1, CG = 1.  Logical row r
+    sits in lane r // 2, half r % 2; only (row 0, group 0) is real data."""
+    words = np.array([[0x76543210, 0xFEDCBA98, 0x01234567, 0x89ABCDEF]], np.uint32)
+    scales = np.array([[0x2A3B]], np.uint16)
+    got = orc.encode_rows(words, scales)
+    want = bytearray()
+    for u in range(2):
+        for lane in range(64):
+            if (lane, u) == (0, 0):
+                want += words[0].tobytes()
+            else:
+                want += b"\x88" * 16
+    for lane in range(64):
+        for u in range(2):
+            want += scales[0].tobytes() if (lane, u) == (0, 0) else b"\x00\x00"
+    assert got.tobytes() == bytes(want)
+
+
+def decode_layout(buf: np.ndarray, rows: int, k: int, L, CG, P, TR, tiles, tile_bytes):
+    """Walk the device buffer unit by unit (destination -> logical) and rebuild
+    words, scales; also return the padding units seen."""
+    G = k // 32
+    words = np.zeros((tiles * TR, P * L * CG * 4), np.uint32)
+    scales = np.zeros((tiles * TR, P * L * CG), np.uint16)
+    for t in range(tiles):
+        for p in range(P):
+            base = t * tile_bytes + p * CG * 2304
+            for lane in range(64):
+                s, c = divmod(lane, L)
+                for u in range(2):
+                    r = t * TR + 2 * s + u
+                    for j in range(CG):
+                        g = p * L * CG + c * CG + j
+                        off = base + (u * CG + j) * 1024 + lane * 16
+                        words[r, 4 * g:4 * g + 4] = buf[off:off + 16].view(np.uint32)
+                        soff = base + 2 * CG * 1024 + lane * 4 * CG + (u * CG + j) * 2
+                        scales[r, g] = buf[soff:soff + 2].view(np.uint16)[0]
+    return words, scales
+
+
+def pin_layout_roundtrip(orc, quick=False):
+    rng = np.random.default_rng(29)
+    shapes = [(5, 96), (3, 8192 + 32 * 5), (130, 64)] if quick else \
+             [(5, 96), (3, 8192 + 32 * 5), (130, 64), (9, 3072), (4, 16384 + 32 * 3), (33, 32 * 7)]
+    for n, k in shapes:
+        w, s = si.draw_weight(rng, n, k)
+        geo = orc.layout_geometry(n, k)
+        buf = orc.encode_rows(w, s)
+        dw, ds = decode_layout(buf, n, k, **geo)
+        G = k // 32
+        assert np.array_equal(dw[:n, :k // 8], w) and np.array_equal(ds[:n, :G], s)
+        assert np.all(dw[n:] == 0x88888888) and np.all(dw[:, k // 8:] == 0x88888888)
+        assert np.all(ds[n:] == 0) and np.all(ds[:, G:] == 0)
+    # gate/up: logical row 2i is gate i, 2i + 1 is up i
+    n, k = 7, 96
+    gw, gs = si.draw_weight(rng, n, k)
+    uw, us = si.draw_weight(rng, n, k)
+    buf = orc.encode_gate_up(gw, gs, uw, us)
+    geo = orc.layout_geometry(2 * n, k)
+    dw, ds = decode_layout(buf, 2 * n, k, **geo)
+    assert np.array_equal(dw[0:2 * n:2, :k // 8], gw) and np.array_equal(dw[1:2 * n:2, :k // 8], uw)
+    assert np.array_equal(ds[0:2 * n:2, :3], gs) and np.array_equal(ds[1:2 * n:2, :3], us)
+
+
+ALL_PINS = [
+    pin_half_decode_all_patterns, pin_half_encode_rne,
+    pin_gemv_rational, pin_gemv_exactly_representable, pin_gemv_closed_forms,
+    pin_gemv_one_hot, pin_gemv_linearity, pin_gemm_rows,
+    pin_silu, pin_ffn, pin_argmax, pin_lmhead,
+    pin_layout_geometry, pin_layout_hand_example, pin_layout_roundtrip,
+]

@@ -1,0 +1,57 @@
+"""Mutation gate for the oracle (CPU only).
+
+Each mutant plants one plausible slip in a copy of the oracle's C source
+(never in the library), builds it with gcc into a temporary directory, and
+runs the pins.  A mutant that passes every pin would mean the pins cannot see
+that kind of mistake, so each one must fail at least one pin.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+# (name, text in q4_oracle.c, replacement)
+MUTANTS = [
+    ("nibble_order_reversed", "4 * (kk % 8)", "4 * (7 - kk % 8)"),
+    ("zero_point_7", "(double)(q - 8) * s", "(double)(q - 7) * s"),
+    ("group_of_64", "scales[r * (k / 32) + kk / 32]", "scales[r * (k / 32) + kk / 64]"),
+    ("row_stride_halved", "words[r * (k / 8) + kk / 8]", "words[r * (k / 16) + kk / 8]"),
+    ("half_exponent_bias", "(double)(1024 + m), e - 25", "(double)(1024 + m), e - 24"),
+    ("half_subnormal_scale", "ldexp((double)m, -24)", "ldexp((double)m, -25)"),
+    ("rne_ties_up", "(fmod(f, 2.0) == 0.0) ? f : f + 1.0", "f + 1.0"),
+    ("half_encode_no_overflow", "if (E > 15)", "if (E > 16)"),
+    ("silu_sign", "g / (1.0 + exp(-g))", "g / (1.0 + exp(g))"),
+    ("silu_on_up", "h[r] = q4o_silu(gv) * uv;", "h[r] = q4o_silu(uv) * gv;"),
+    ("argmax_last_tie", "if (v[i] > v[best])", "if (v[i] >= v[best])"),
+    ("abs_sum_signed", "asum += fabs(term);", "asum += term;"),
+    ("last_k_dropped", "for (int64_t kk = 0; kk < k; ++kk) {", "for (int64_t kk = 0; kk < k - 1; ++kk) {"),
+    ("gemm_row_stride", "X + i * k, n, k", "X + i * 32, n, k"),
+    ("layout_lanes_transposed", "int64_t lane = s * L + c;", "int64_t lane = c * (64 / L) + s;"),
+    ("layout_scale_offset", "(u * CG + j) * 2;", "(j * 2 + u) * 2;"),
+    ("layout_pad_scale", "place(dst, r, g, L, CG, TR, TB, NULL, 0);",
+     "place(dst, r, g, L, CG, TR, TB, NULL, 0x3c00);"),
+    ("layout_tie_smaller_L", "cover < bestCover", "cover <= bestCover"),
+    ("layout_gate_up_swapped", "rw = (r % 2 ? w1 : w0)", "rw = (r % 2 ? w0 : w1)"),
+    ("layout_tile_rows", "int64_t TR = 2 * (64 / L);", "int64_t TR = 64 / L;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/present"
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new))
+    lib = oracle.build(out=str(tmp_path / "libmutant.so"), source=str(path))
+    orc = oracle.load(lib)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc, quick=True)
+        except AssertionError:
+            failed.append(pin.__name__)
+        except Exception as e:  # a crash inside a pin also counts as caught
+            failed.append(f"{pin.__name__}:{type(e).__name__}")
+    assert failed, f"mutant {name} passed every pin"

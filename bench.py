@@ -1,0 +1,377 @@
+#!/usr/bin/env python3
+"""Benchmark of the int4-dequantizing GEMV on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is the matmul set of one Phi-3-mini decode layer at batch 1, run
+back to back through the C ABI: QKV [9216x3072], O-proj [3072x3072], gate_up
+[16384x3072] and down [3072x8192] GEMVs, int4 codes + one f16 scale per 32
+weights, x f16 ~ N(0,1), f16 out (synthetic seeded inputs of those shapes).
+Weights are rotated over enough distinct device copies (>= 1 GiB) that every
+step streams them from HBM rather than from the 256 MB Infinity Cache.
+
+Printed (one JSON line): effective GB/s over the step (algorithmic bytes:
+codes + scales + x + y, divided by the wall time of K steps), the per-kernel
+roofline of the dominant kernel (gate_up) from HIP events around each of its
+launches, the oracle's own rate on the host, and the other variants of the
+matmul (single 3072^2 GEMV, fused gate/up SiLU FFN + down, f32 LM head with
+argmax, skinny GEMM at M = 16/64/256) as sub-objects.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+PEAK_F16_TFLOPS = 2500.0       # MI355X dense f16 MFMA, published
+ROTATE_BYTES = 1 << 30         # distinct weight bytes cycled through (4x the MALL)
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def weight_bytes(n: int, k: int) -> int:
+    return n * k // 2 + n * (k // 32) * 2
+
+
+def gemv_bytes(n: int, k: int, out_bytes: int = 2) -> int:
+    return weight_bytes(n, k) + 2 * k + out_bytes * n
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only", choices=["all", "layer", "variants"], default="all",
+                    help="layer: the headline step only (for profiling)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate host time budget of the oracle baseline")
+    ap.add_argument("--summarize", metavar="RESULTS_DB",
+                    help="print per-kernel duration statistics of a rocprofv3 "
+                         "--kernel-trace database (grouped by kernel and grid) and exit")
+    return ap.parse_args()
+
+
+def summarize(db_path: str) -> int:
+    """Kernel-trace statistics from a rocprofv3 results database: one row per
+    (kernel, grid size), durations in microseconds."""
+    import sqlite3
+    import statistics
+    db = sqlite3.connect(db_path)
+    rows = db.execute("select name, grid_x, workgroup_x, vgpr_count, accum_vgpr_count, "
+                      "sgpr_count, lds_size, duration from kernels").fetchall()
+    groups = {}
+    for name, gx, wx, vg, ag, sg, lds, dur in rows:
+        groups.setdefault((name, gx, wx, vg, ag, sg, lds), []).append(dur / 1000.0)
+    print(f"# rocprofv3 kernel trace: {db_path}")
+    print("# calls  avg_us  median_us  min_us  p90_us  grid  block  vgpr  agpr  sgpr  lds  kernel")
+    for key, d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        name, gx, wx, vg, ag, sg, lds = key
+        d.sort()
+        p90 = d[min(len(d) - 1, int(0.9 * len(d)))]
+        print(f"{len(d):6d} {statistics.fmean(d):8.3f} {statistics.median(d):8.3f} {d[0]:8.3f} "
+              f"{p90:8.3f} {gx:8d} {wx:5d} {vg:4d} {ag:4d} {sg:4d} {lds:6d}  {name[:110]}")
+    return 0
+
+
+def kernels_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "int4_quantized_decode_q4_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel_tag: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{kernel_tag}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, _, v = line.partition(":")
+                vals[key.strip()] = v.strip()
+    if vals.get("kernel_sources_sha256_16") != kernels_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Rotation:
+    """C distinct device copies of a packed weight (same bytes, different
+    addresses): the first is packed from the seeded inputs, the rest are
+    device-side clones."""
+
+    def __init__(self, q4, pw, copies: int):
+        self.items = [pw]
+        for _ in range(copies - 1):
+            buf = pw.buf.clone()
+            desc = q4.q4_weight()
+            desc.n, desc.k, desc.layout, desc.version = pw.desc.n, pw.desc.k, pw.desc.layout, pw.desc.version
+            desc.data, desc.bytes = buf.data_ptr(), pw.desc.bytes
+            self.items.append(q4.PackedWeight(buf, desc))
+
+    def __getitem__(self, i):
+        return self.items[i % len(self.items)]
+
+
+def dev_f16(a):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.float16)).cuda()
+
+
+def dev_u16(a):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).cuda()
+
+
+def dev_u32(a):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint32).view(np.int32)).cuda()
+
+
+def copies_for(nbytes: int) -> int:
+    return max(2, -(-ROTATE_BYTES // nbytes))
+
+
+def timed(torch, fn, steps: int, warmup: int):
+    """Wall time of `steps` calls of fn(i) (ms per call), bracketed by
+    synchronisation on both sides, after `warmup` untimed calls."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def per_kernel(torch, launches, steps: int, warmup: int):
+    """Average device duration (us) of each launch of a step, from HIP events
+    recorded on the launching (current) stream around every launch."""
+    for i in range(warmup):
+        for fn in launches.values():
+            fn(i)
+    torch.cuda.synchronize()
+    ev = {name: [] for name in launches}
+    for i in range(steps):
+        for name, fn in launches.items():
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn(warmup + i)
+            b.record()
+            ev[name].append((a, b))
+    torch.cuda.synchronize()
+    return {name: 1000.0 * sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+            for name, pairs in ev.items()}
+
+
+def main():
+    args = parse()
+    if args.summarize:
+        return summarize(args.summarize)
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the int4 GEMV path has no multi-GPU part in this "
+              "library (run with --gpus 1)", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import int4_quantized_decode_q4_amd as q4
+    import seeded_inputs as si
+
+    torch.cuda.set_device(0)
+    K, W = args.steps, args.warmup
+    result = {}
+
+    # ---------------------------------------------------------------- layer
+    inp = si.workload(si.LAYER_SET, seed=0)
+    x3, x8 = dev_f16(inp["x3072"]), dev_f16(inp["x8192"])
+    set_bytes = sum(weight_bytes(n, k) for n, k in si.LAYER_SHAPES.values())
+    C = copies_for(set_bytes)
+    rot = {}
+    outs = {}
+    for key, (n, k) in si.LAYER_SHAPES.items():
+        w, s = inp[key]
+        rot[key] = Rotation(q4, q4.pack(dev_u32(w), dev_u16(s)), C)
+        outs[key] = torch.empty(n, dtype=torch.float16, device="cuda")
+    xin = {"qkv": x3, "o_proj": x3, "gate_up": x3, "down": x8}
+
+    def launch(key):
+        return lambda i: q4.gemv(rot[key][i], xin[key], outs[key])
+
+    launches = {key: launch(key) for key in si.LAYER_SHAPES}
+
+    def step(i):
+        for fn in launches.values():
+            fn(i)
+
+    step_bytes = sum(gemv_bytes(n, k) for n, k in si.LAYER_SHAPES.values())
+    ms = timed(torch, step, K, W)
+    kus = per_kernel(torch, launches, K, W)
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    dom = "gate_up"
+    dn, dk = si.LAYER_SHAPES[dom]
+    dom_bytes = gemv_bytes(dn, dk)
+    achieved = dom_bytes / (kus[dom] * 1e-6) / 1e9
+    traffic = committed_traffic("gemv_16384x3072")
+    result.update({
+        "metric": "int4 GEMV effective HBM GB/s (% of peak) + us per Phi-3-mini decode layer",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "phi3_mini_layer_set",
+            "matrices": {k: list(v) for k, v in si.LAYER_SHAPES.items()},
+            "batch": 1, "group": 32, "weights": "int4 codes + f16 scale per 32 (q4f16_1)",
+            "accumulate": "f32", "rotation_copies": C,
+            "bytes_per_step": step_bytes,
+        },
+        "us_per_layer_wall": round(ms * 1000, 3),
+        "us_per_layer_kernel_sum": round(sum(kus.values()), 3),
+        "pct_of_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "per_kernel_us": {k: round(v, 3) for k, v in kus.items()},
+        "per_kernel_gbs": {k: round(gemv_bytes(*si.LAYER_SHAPES[k]) / (kus[k] * 1e-6) / 1e9, 1)
+                           for k in kus},
+        "roofline": {
+            "kernel": "q4 GEMV gate_up 16384x3072 (gemv_family_kernel<32,3,f16>)",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": dom_bytes,
+        },
+    })
+
+    if args.only in ("all", "variants"):
+        result["variants"] = variants(torch, q4, si, np, K, W)
+
+    if not args.no_cpu_baseline and args.only == "all":
+        result["cpu_baseline"] = cpu_baseline(si, inp, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def variants(torch, q4, si, np, K, W):
+    out = {}
+    # single GEMV 3072^2
+    inp = si.workload(si.GEMV_3072, seed=0)
+    nb = gemv_bytes(3072, 3072)
+    rot = Rotation(q4, q4.pack(dev_u32(inp["words"]), dev_u16(inp["scales"])),
+                   copies_for(weight_bytes(3072, 3072)))
+    x = dev_f16(inp["x"])
+    y = torch.empty(3072, dtype=torch.float16, device="cuda")
+    us = per_kernel(torch, {"g": lambda i: q4.gemv(rot[i], x, y)}, K, W)["g"]
+    out["gemv_3072x3072"] = {"us": round(us, 3), "gbs": round(nb / us / 1e3, 1),
+                             "frac": round(nb / us / 1e3 / PEAK_HBM_GBS, 4), "bytes": nb}
+    del rot
+
+    # fused gate/up + SiLU, then down
+    inp = si.workload(si.FFN, seed=0)
+    g, u, d = inp["gate"], inp["up"], inp["down"]
+    gu_bytes = 2 * weight_bytes(8192, 3072) + 2 * 3072 + 2 * 8192
+    rot_gu = Rotation(q4, q4.pack_gate_up(dev_u32(g[0]), dev_u16(g[1]), dev_u32(u[0]),
+                                          dev_u16(u[1])), copies_for(gu_bytes))
+    rot_d = Rotation(q4, q4.pack(dev_u32(d[0]), dev_u16(d[1])), copies_for(weight_bytes(3072, 8192)))
+    x = dev_f16(inp["x"])
+    h = torch.empty(8192, dtype=torch.float16, device="cuda")
+    yd = torch.empty(3072, dtype=torch.float16, device="cuda")
+    kus = per_kernel(torch, {"ffn": lambda i: q4.ffn_gate_up_silu(rot_gu[i], x, h),
+                             "down": lambda i: q4.gemv(rot_d[i], h, yd)}, K, W)
+    dbytes = gemv_bytes(3072, 8192)
+    out["ffn_fused_8192x3072_plus_down"] = {
+        "ffn_us": round(kus["ffn"], 3), "ffn_gbs": round(gu_bytes / kus["ffn"] / 1e3, 1),
+        "ffn_frac": round(gu_bytes / kus["ffn"] / 1e3 / PEAK_HBM_GBS, 4),
+        "down_us": round(kus["down"], 3), "down_gbs": round(dbytes / kus["down"] / 1e3, 1),
+        "bytes": [gu_bytes, dbytes]}
+    del rot_gu, rot_d
+
+    # LM head, f32 logits + argmax
+    inp = si.workload(si.LM_HEAD, seed=0)
+    nb = gemv_bytes(32064, 3072, out_bytes=4) + 4
+    rot = Rotation(q4, q4.pack(dev_u32(inp["words"]), dev_u16(inp["scales"])),
+                   copies_for(weight_bytes(32064, 3072)))
+    x = dev_f16(inp["x"])
+    logits = torch.empty(32064, dtype=torch.float32, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    us = per_kernel(torch, {"lm": lambda i: q4.lmhead_f32(rot[i], x, logits, am)}, K, W)["lm"]
+    out["lm_head_32064x3072_f32_argmax"] = {"us": round(us, 3), "gbs": round(nb / us / 1e3, 1),
+                                            "frac": round(nb / us / 1e3 / PEAK_HBM_GBS, 4),
+                                            "bytes": nb}
+    del rot
+
+    # skinny GEMM
+    gm = {}
+    inp = si.workload(si.GEMM, seed=0, m=256)
+    rot = Rotation(q4, q4.pack(dev_u32(inp["words"]), dev_u16(inp["scales"])),
+                   copies_for(weight_bytes(16384, 3072)))
+    for m in (16, 64, 256):
+        X = dev_f16(np.ascontiguousarray(inp["X"][:m]))
+        Y = torch.empty((m, 16384), dtype=torch.float16, device="cuda")
+        steps = max(20, K // 4)
+        us = per_kernel(torch, {"g": lambda i: q4.gemm(rot[i], X, Y)}, steps, min(W, 5))["g"]
+        nb = weight_bytes(16384, 3072) + 2 * m * 3072 + 2 * m * 16384
+        fl = 2.0 * m * 16384 * 3072
+        gm[str(m)] = {"us": round(us, 3), "gbs": round(nb / us / 1e3, 1),
+                      "hbm_frac": round(nb / us / 1e3 / PEAK_HBM_GBS, 4),
+                      "tflops": round(fl / us / 1e6, 2),
+                      "mfma_frac": round(fl / us / 1e6 / PEAK_F16_TFLOPS, 4)}
+    out["gemm_16384x3072"] = gm
+    return out
+
+
+def cpu_baseline(si, inp, budget_s: float):
+    """The oracle (plain C, f64, one thread) on the host: whole layer-set
+    GEMVs, as many matrices as fit the time budget; rate in the metric's unit
+    (effective GB/s of the same algorithmic bytes)."""
+    import oracle
+    orc = oracle.load()
+    done_bytes, t_total, mats = 0, 0.0, []
+    keys = list(si.LAYER_SHAPES)
+    i = 0
+    while t_total < budget_s and i < 4 * len(keys):
+        key = keys[i % len(keys)]
+        w, s = inp[key]
+        x = inp["x8192"] if key == "down" else inp["x3072"]
+        t = time.perf_counter()
+        orc.gemv(w, s, x)
+        t_total += time.perf_counter() - t
+        done_bytes += gemv_bytes(*si.LAYER_SHAPES[key])
+        mats.append(key)
+        i += 1
+    return {"value": round(done_bytes / t_total / 1e9, 5), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{len(mats)} full GEMVs of the layer set ({','.join(mats)}), "
+                      f"{t_total:.1f} s of single-thread f64 oracle work",
+            "us_per_layer_equiv": round(1e6 * t_total * 63799296 / done_bytes / 1e0, 1)}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

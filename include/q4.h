@@ -1,0 +1,197 @@
+/*
+ * q4.h -- C ABI of libq4: the int4-dequantizing matrix multiply of LLM decode
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [P1] "Zero-TVM：手写 WGSL 着色器在浏览器中运行 Phi-3-mini，挑战编译器霸权"
+ *        (zingnex.cn forum article).
+ *        - section 完整的推理流水线: the int4 dequantizing matmul is the core of
+ *          the decoder, in several variants (baseline, subgroup reduction, tiled
+ *          rows x4 / x8) plus an f32-output version for the LM head; decoding is
+ *          a greedy argmax dispatch.
+ *        - section 内核融合: gate, up and the SiLU activation fused in one pass.
+ *        - section 性能基准: matmul and int4 dequant are where the cost is.
+ *        - section 技术限制与诚实声明: batched-prefill shaders exist (the
+ *          batched form of the matmul, q4_gemm here).
+ *        - sections 技术栈对比 / 性能基准: the weights are Phi-3-mini "q4f16_1".
+ *   [P4] the Zero-TVM README: repacking of weights is tested byte for byte.
+ *
+ * The pages name the weight format but do not define it.  Canonical form, as
+ * this library defines it (host or device arrays handed to q4_pack):
+ *   words  uint32 [n][k/8]: code k = 8*j + i of a row is bits 4*i..4*i+3 of
+ *                            the row's word j (low nibble first), codes 0..15;
+ *   scales f16    [n][k/32]: one IEEE binary16 scale per 32 consecutive k;
+ *   weight w[r][k] = (code - 8) * scale;   y[r] = sum_k x[k] * w[r][k].
+ * f16 values cross the ABI as uint16_t bit patterns.
+ *
+ * Conventions for every call:
+ *   - all buffer pointers are DEVICE pointers (hipMalloc or equivalent) unless
+ *     stated; the caller owns all memory; the library never allocates, frees
+ *     or synchronises;
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream); the
+ *     work is enqueued there and the call returns at once; device faults
+ *     surface at the caller's next synchronisation;
+ *   - every argument is validated on the host BEFORE anything is enqueued;
+ *     on error nothing is launched and nothing is written;
+ *   - buffers must stay alive until the stream has passed the call.
+ *
+ * Device layout, version 1 (what q4_pack writes; opaque to callers but
+ * specified here so that it can be checked byte for byte):
+ *   G = k/32 groups per row.  P = ceil(G/256) passes, Gp = ceil(G/P).
+ *   (L, CG) = lanes per row L in {64,32,16,8,4,2,1} and groups per lane CG in
+ *   {1,2,3,4} with L*CG >= Gp; least L*CG wins, ties go to the larger L.
+ *   A tile holds TR = 2*64/L rows; tiles = ceil(rows/TR); each tile is P
+ *   passes of PB = CG*2304 bytes.  Logical (row r, group g) lives at
+ *     t = r / TR, s = (r % TR) / 2, u = r % 2, p = g / (L*CG),
+ *     c = (g % (L*CG)) / CG, j = g % CG, lane = s*L + c, base = t*P*PB + p*PB:
+ *     its 4 canonical words at base + (u*CG + j)*1024 + lane*16,
+ *     its scale             at base + 2*CG*1024 + lane*4*CG + (u*CG + j)*2.
+ *   Padding rows (r >= rows) and groups (g >= G): words 0x88888888, scale 0.
+ *   So each 64-lane wavefront reads every 128-bit unit of a pass with one
+ *   fully contiguous 1 KiB load per (u, j), and each lane's 2*CG scales with
+ *   one load.  Gate/up layout: logical row 2i is gate row i, row 2i+1 is up
+ *   row i, so both land in the same lane after the cross-lane reduction.
+ */
+#ifndef Q4_H
+#define Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define Q4_OK             0
+#define Q4_ERR_NULL      -1  /* a required pointer is NULL */
+#define Q4_ERR_SHAPE     -2  /* n < 1, k < 32, k % 32 != 0, m < 1, or a size overflows */
+#define Q4_ERR_ALIGN     -3  /* a pointer is not aligned as documented */
+#define Q4_ERR_LAYOUT    -4  /* weight layout/version does not suit the call */
+#define Q4_ERR_WORKSPACE -5  /* workspace NULL or smaller than q4_workspace_bytes */
+#define Q4_ERR_ALIAS     -6  /* an output range overlaps an input range */
+#define Q4_ERR_HIP       -7  /* the HIP runtime refused the launch (q4_last_hip_error) */
+#define Q4_ERR_SIZE      -8  /* a destination buffer is smaller than required */
+
+/* weight layouts */
+#define Q4_LAYOUT_ROWS    1  /* plain rows: q4_gemv, q4_gemm, q4_lmhead_f32 */
+#define Q4_LAYOUT_GATE_UP 2  /* interleaved gate/up rows: q4_ffn_gate_up_silu */
+#define Q4_LAYOUT_VERSION 1
+
+/* operations, for q4_workspace_bytes */
+#define Q4_OP_GEMV    1
+#define Q4_OP_GEMM    2
+#define Q4_OP_FFN     3
+#define Q4_OP_LMHEAD  4
+
+/*
+ * Host-side descriptor of a packed weight, filled by q4_pack*; only `data`
+ * points to device memory.  The descriptor is read on the host by every op
+ * and never on the device.
+ */
+typedef struct q4_weight {
+    int32_t n;        /* output rows (gate/up: rows of EACH half) */
+    int32_t k;        /* input columns, k % 32 == 0 */
+    int32_t layout;   /* Q4_LAYOUT_ROWS or Q4_LAYOUT_GATE_UP */
+    int32_t version;  /* Q4_LAYOUT_VERSION */
+    void   *data;     /* device, 256-byte aligned, `bytes` long */
+    int64_t bytes;    /* q4_packed_bytes(n, k, layout) */
+} q4_weight;
+
+/* Bytes of the packed layout; 0 for an invalid shape or layout. */
+int64_t q4_packed_bytes(int32_t n, int32_t k, int32_t layout);
+
+/* Bytes of device workspace an op needs (0 = none).  The LM-head argmax needs
+ * one; its first 256 bytes hold a counter that must be zero before the first
+ * call on that workspace (allocate it zero-filled); every completed call
+ * leaves it at zero again.  Two calls that share a workspace must be ordered
+ * on one stream. */
+int64_t q4_workspace_bytes(int32_t op, int32_t m, int32_t n, int32_t k);
+
+/*
+ * Repack canonical weights into the device layout ([P4]: repacking is a pure
+ * permutation, checked byte for byte).
+ *   words  : device, uint32 [n][k/8], 16-byte aligned
+ *   scales : device, f16 bits [n][k/32], 2-byte aligned
+ *   dst    : device, >= q4_packed_bytes(n, k, Q4_LAYOUT_ROWS) bytes, 256-byte aligned
+ *   out    : host descriptor written on success
+ * Errors: NULL, SHAPE, ALIGN, SIZE (dst_bytes too small), ALIAS, HIP.
+ */
+int q4_pack(const uint32_t *words, const uint16_t *scales, int32_t n, int32_t k,
+            void *dst, int64_t dst_bytes, q4_weight *out, void *stream);
+
+/*
+ * Repack the gate and up halves of an FFN ([P1] 内核融合) into one
+ * interleaved layout for q4_ffn_gate_up_silu.  Each of gw/gs and uw/us is a
+ * canonical [n][k/8] / [n][k/32] pair as in q4_pack; dst needs
+ * q4_packed_bytes(n, k, Q4_LAYOUT_GATE_UP) bytes.
+ */
+int q4_pack_gate_up(const uint32_t *gw, const uint16_t *gs, const uint32_t *uw,
+                    const uint16_t *us, int32_t n, int32_t k, void *dst,
+                    int64_t dst_bytes, q4_weight *out, void *stream);
+
+/*
+ * Inverse of q4_pack / q4_pack_gate_up (for round-trip checks): writes the
+ * canonical words [rows][k/8] and scales [rows][k/32] of the packed weight,
+ * rows = n (plain) or 2n (gate/up, interleaved order: gate 0, up 0, gate 1 ...).
+ */
+int q4_unpack(const q4_weight *w, uint32_t *words, uint16_t *scales, void *stream);
+
+/*
+ * y = x . dequant(W)^T, batch 1 ([P1] 完整的推理流水线: the int4 dequantizing
+ * matmul; the rows-per-invocation and subgroup-reduction variants there are
+ * the two-rows-per-lane tiles and the cross-lane reduction here).
+ *   w : Q4_LAYOUT_ROWS
+ *   x : device f16 [k], 16-byte aligned
+ *   y : device f16 [n], 4-byte aligned; f32 accumulation, rounded to nearest
+ *       even once at the end
+ * Errors: NULL, SHAPE, ALIGN, LAYOUT, ALIAS, HIP.
+ */
+int q4_gemv(const q4_weight *w, const uint16_t *x, uint16_t *y, void *stream);
+
+/*
+ * Y = X . dequant(W)^T for m activation rows ([P1] 技术限制与诚实声明: the
+ * batched-prefill form).  m < 16 runs a VALU path that reads W once for all
+ * rows; m >= 16 dequantizes tiles of W to f16 in LDS and runs MFMA.
+ *   X : device f16 [m][k] row-major, 16-byte aligned
+ *   Y : device f16 [m][n] row-major, 4-byte aligned
+ *   ws: unused (pass NULL, 0)
+ */
+int q4_gemm(const q4_weight *w, const uint16_t *X, int32_t m, uint16_t *Y,
+            void *ws, int64_t ws_bytes, void *stream);
+
+/*
+ * h = SiLU(x . Wg^T) * (x . Wu^T) in one kernel ([P1] 内核融合, fused_ffn),
+ * SiLU(g) = g / (1 + e^-g) in f32, h rounded to f16.
+ *   w : Q4_LAYOUT_GATE_UP with n rows per half; x : f16 [k]; h : f16 [n]
+ */
+int q4_ffn_gate_up_silu(const q4_weight *w, const uint16_t *x, uint16_t *h,
+                        void *stream);
+
+/*
+ * LM head with f32 logits and greedy argmax ([P1] 完整的推理流水线: the f32
+ * output variant for sampling stability, and the argmax dispatch).
+ *   logits : device f32 [n], 8-byte aligned
+ *   argmax : device int32 [1] or NULL; the lowest index holding the maximum
+ *            logit (as computed in f32)
+ *   ws     : >= q4_workspace_bytes(Q4_OP_LMHEAD, 1, n, k) bytes when argmax is
+ *            not NULL (see q4_workspace_bytes for its zero-counter contract)
+ */
+int q4_lmhead_f32(const q4_weight *w, const uint16_t *x, float *logits,
+                  int32_t *argmax, void *ws, int64_t ws_bytes, void *stream);
+
+/* Static text for a return code. */
+const char *q4_strerror(int code);
+
+/* hipError_t behind the last Q4_ERR_HIP returned on this thread (0 if none). */
+int q4_last_hip_error(void);
+
+/* Layout geometry for a weight of `rows` logical rows: out[0..5] = L, CG, P,
+ * TR, tiles, tile bytes.  Returns Q4_OK or Q4_ERR_SHAPE/Q4_ERR_NULL. */
+int q4_layout_geometry(int32_t rows, int32_t k, int64_t *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4_H */

@@ -1,0 +1,257 @@
+"""int4_quantized_decode_q4_amd -- Python binding of libq4.
+
+libq4 is the int4-dequantizing matrix multiply of LLM decode for AMD
+Instinct MI355X (gfx950): ``y = x . dequant(W)^T`` with W as 4-bit codes and
+one f16 scale per 32 weights along k (the "q4f16_1" weights of the Zero-TVM
+article "Zero-TVM：手写 WGSL 着色器在浏览器中运行 Phi-3-mini，挑战编译器霸权",
+section 完整的推理流水线; the fused FFN of its section 内核融合).
+
+This module only marshals arguments: torch tensors provide device memory and
+the current stream, and every step runs in the HIP kernels of ``libq4.so``.
+There is no fallback: importing fails if the library is not built
+(``python -m int4_quantized_decode_q4_amd.build``), and every call raises
+``Q4Error`` with the library's return code on failure.
+
+Tensor conventions: f16 data as ``torch.float16`` (or 16-bit integer views);
+canonical words as 32-bit integers [n][k/8]; scales as 16-bit [n][k/32]; all on
+one CUDA (HIP) device, contiguous.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq4.so")
+if not os.path.exists(LIBRARY):
+    raise ImportError(
+        f"{LIBRARY} is not built; run `python -m int4_quantized_decode_q4_amd.build`")
+
+_lib = ctypes.CDLL(LIBRARY)
+
+OK = 0
+ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_LAYOUT = -1, -2, -3, -4
+ERR_WORKSPACE, ERR_ALIAS, ERR_HIP, ERR_SIZE = -5, -6, -7, -8
+LAYOUT_ROWS, LAYOUT_GATE_UP, LAYOUT_VERSION = 1, 2, 1
+OP_GEMV, OP_GEMM, OP_FFN, OP_LMHEAD = 1, 2, 3, 4
+
+
+class q4_weight(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("layout", ctypes.c_int32), ("version", ctypes.c_int32),
+                ("data", ctypes.c_void_p), ("bytes", ctypes.c_int64)]
+
+
+_P = ctypes.c_void_p
+_I32, _I64 = ctypes.c_int32, ctypes.c_int64
+_W = ctypes.POINTER(q4_weight)
+
+_SIGNATURES = {
+    "q4_packed_bytes": (_I64, [_I32, _I32, _I32]),
+    "q4_workspace_bytes": (_I64, [_I32, _I32, _I32, _I32]),
+    "q4_pack": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _I64, _W, _P]),
+    "q4_pack_gate_up": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _P, _I64, _W, _P]),
+    "q4_unpack": (ctypes.c_int, [_W, _P, _P, _P]),
+    "q4_gemv": (ctypes.c_int, [_W, _P, _P, _P]),
+    "q4_gemm": (ctypes.c_int, [_W, _P, _I32, _P, _P, _I64, _P]),
+    "q4_ffn_gate_up_silu": (ctypes.c_int, [_W, _P, _P, _P]),
+    "q4_lmhead_f32": (ctypes.c_int, [_W, _P, _P, _P, _P, _I64, _P]),
+    "q4_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "q4_last_hip_error": (ctypes.c_int, []),
+    "q4_layout_geometry": (ctypes.c_int, [_I32, _I32, _P]),
+}
+for _name, (_res, _args) in _SIGNATURES.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+lib = _lib   # the raw ctypes handle, for callers that want the C ABI itself
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = _lib.q4_strerror(code).decode()
+        if code == ERR_HIP:
+            msg += f" (hipError {_lib.q4_last_hip_error()})"
+        super().__init__(f"{where}: {msg} [{code}]")
+
+
+def _check(code: int, where: str) -> None:
+    if code != OK:
+        raise Q4Error(code, where)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, itemsize: int, shape=None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.element_size() != itemsize:
+        raise TypeError(f"{name} must have {itemsize}-byte elements, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+class PackedWeight:
+    """A weight in the device layout: the owning byte tensor plus the C
+    descriptor that every op takes."""
+
+    def __init__(self, buf: torch.Tensor, desc: q4_weight):
+        self.buf = buf
+        self.desc = desc
+
+    @property
+    def n(self) -> int:
+        return self.desc.n
+
+    @property
+    def k(self) -> int:
+        return self.desc.k
+
+    @property
+    def layout(self) -> int:
+        return self.desc.layout
+
+    @property
+    def nbytes(self) -> int:
+        return self.desc.bytes
+
+    @property
+    def device(self) -> torch.device:
+        return self.buf.device
+
+
+def packed_bytes(n: int, k: int, layout: int = LAYOUT_ROWS) -> int:
+    return int(_lib.q4_packed_bytes(n, k, layout))
+
+
+def layout_geometry(rows: int, k: int) -> dict:
+    out = (ctypes.c_int64 * 6)()
+    _check(_lib.q4_layout_geometry(rows, k, ctypes.cast(out, _P)), "q4_layout_geometry")
+    return dict(zip(("L", "CG", "P", "TR", "tiles", "tile_bytes"), (int(v) for v in out)))
+
+
+def _alloc_packed(n: int, k: int, layout: int, device) -> torch.Tensor:
+    nb = packed_bytes(n, k, layout)
+    if nb <= 0:
+        raise Q4Error(ERR_SHAPE, "packed_bytes")
+    buf = torch.empty(nb, dtype=torch.uint8, device=device)
+    if buf.data_ptr() % 256:
+        raise RuntimeError("allocator returned a buffer that is not 256-byte aligned")
+    return buf
+
+
+def pack(words: torch.Tensor, scales: torch.Tensor) -> PackedWeight:
+    """Canonical words [n][k/8] (32-bit) and scales [n][k/32] (16-bit) ->
+    device layout (q4_pack)."""
+    n, kw = words.shape
+    k = kw * 8
+    pw = _dev(words, "words", 4, (n, kw))
+    ps = _dev(scales, "scales", 2, (n, k // 32))
+    buf = _alloc_packed(n, k, LAYOUT_ROWS, words.device)
+    desc = q4_weight()
+    _check(_lib.q4_pack(pw, ps, n, k, buf.data_ptr(), buf.numel(), ctypes.byref(desc),
+                        _stream(words)), "q4_pack")
+    return PackedWeight(buf, desc)
+
+
+def pack_gate_up(gw, gs, uw, us) -> PackedWeight:
+    """Gate and up halves, each canonical [n][k/8] / [n][k/32] -> one
+    interleaved layout for ffn_gate_up_silu (q4_pack_gate_up)."""
+    n, kw = gw.shape
+    k = kw * 8
+    ptrs = [_dev(gw, "gate words", 4, (n, kw)), _dev(gs, "gate scales", 2, (n, k // 32)),
+            _dev(uw, "up words", 4, (n, kw)), _dev(us, "up scales", 2, (n, k // 32))]
+    buf = _alloc_packed(n, k, LAYOUT_GATE_UP, gw.device)
+    desc = q4_weight()
+    _check(_lib.q4_pack_gate_up(*ptrs, n, k, buf.data_ptr(), buf.numel(), ctypes.byref(desc),
+                                _stream(gw)), "q4_pack_gate_up")
+    return PackedWeight(buf, desc)
+
+
+def unpack(w: PackedWeight) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Device layout -> canonical (words int32 [rows][k/8], scales int16
+    [rows][k/32]); rows = 2n for a gate/up weight (gate 0, up 0, gate 1, ...)."""
+    rows = w.n * (2 if w.layout == LAYOUT_GATE_UP else 1)
+    words = torch.empty((rows, w.k // 8), dtype=torch.int32, device=w.device)
+    scales = torch.empty((rows, w.k // 32), dtype=torch.int16, device=w.device)
+    _check(_lib.q4_unpack(ctypes.byref(w.desc), words.data_ptr(), scales.data_ptr(),
+                          _stream(words)), "q4_unpack")
+    return words, scales
+
+
+def gemv(w: PackedWeight, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y f16 [n] = x f16 [k] . dequant(W)^T (q4_gemv)."""
+    px = _dev(x, "x", 2, (w.k,))
+    if out is None:
+        out = torch.empty(w.n, dtype=torch.float16, device=x.device)
+    py = _dev(out, "out", 2, (w.n,))
+    _check(_lib.q4_gemv(ctypes.byref(w.desc), px, py, _stream(x)), "q4_gemv")
+    return out
+
+
+def gemm(w: PackedWeight, X: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y f16 [m][n] = X f16 [m][k] . dequant(W)^T (q4_gemm)."""
+    m = X.shape[0]
+    px = _dev(X, "X", 2, (m, w.k))
+    if out is None:
+        out = torch.empty((m, w.n), dtype=torch.float16, device=X.device)
+    py = _dev(out, "out", 2, (m, w.n))
+    _check(_lib.q4_gemm(ctypes.byref(w.desc), px, m, py, None, 0, _stream(X)), "q4_gemm")
+    return out
+
+
+def ffn_gate_up_silu(w: PackedWeight, x: torch.Tensor,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """h f16 [n] = SiLU(x.Wg^T) * (x.Wu^T) in one kernel (q4_ffn_gate_up_silu)."""
+    px = _dev(x, "x", 2, (w.k,))
+    if out is None:
+        out = torch.empty(w.n, dtype=torch.float16, device=x.device)
+    ph = _dev(out, "out", 2, (w.n,))
+    _check(_lib.q4_ffn_gate_up_silu(ctypes.byref(w.desc), px, ph, _stream(x)),
+           "q4_ffn_gate_up_silu")
+    return out
+
+
+_workspaces: dict = {}
+
+
+def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    """A zero-filled workspace of at least nbytes on `device`, kept per device
+    (the LM-head argmax leaves its counter at zero after every call)."""
+    key = (device.type, device.index)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def lmhead_f32(w: PackedWeight, x: torch.Tensor, logits: Optional[torch.Tensor] = None,
+               argmax: Optional[torch.Tensor] = None, with_argmax: bool = True,
+               ws: Optional[torch.Tensor] = None):
+    """(logits f32 [n], argmax int32 [1] or None) (q4_lmhead_f32)."""
+    px = _dev(x, "x", 2, (w.k,))
+    if logits is None:
+        logits = torch.empty(w.n, dtype=torch.float32, device=x.device)
+    pl = _dev(logits, "logits", 4, (w.n,))
+    pa, pws, nws = None, None, 0
+    if with_argmax or argmax is not None:
+        if argmax is None:
+            argmax = torch.empty(1, dtype=torch.int32, device=x.device)
+        pa = _dev(argmax, "argmax", 4, (1,))
+        need = int(_lib.q4_workspace_bytes(OP_LMHEAD, 1, w.n, w.k))
+        if ws is None:
+            ws = workspace(x.device, need)
+        pws, nws = _dev(ws, "ws", 1), ws.numel()
+    _check(_lib.q4_lmhead_f32(ctypes.byref(w.desc), px, pl, pa, pws, nws, _stream(x)),
+           "q4_lmhead_f32")
+    return logits, argmax

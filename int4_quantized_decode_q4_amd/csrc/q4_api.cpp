@@ -1,0 +1,299 @@
+// q4_api.cpp -- the extern "C" entry points of libq4 (declared in
+// include/q4.h): host-side validation, then one launch on the caller's
+// stream.  Validation never touches the HIP runtime, so every error path can
+// be exercised on a machine without a GPU.
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/q4.h"
+#include "q4_geometry.h"
+#include "q4_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Do [a, a + an) and [b, b + bn) share a byte?
+bool overlap(const void *a, int64_t an, const void *b, int64_t bn)
+{
+    if (!a || !b || an <= 0 || bn <= 0)
+        return false;
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + (uintptr_t)bn && pb < pa + (uintptr_t)an;
+}
+
+bool valid_shape(int64_t n, int64_t k)
+{
+    // sizes stay far inside int64 (n, k < 2^31); the GEMV family indexes rows
+    // as int32 in its argmax, so a layout must have fewer than 2^31 rows.
+    return n >= 1 && k >= 32 && (k % 32) == 0 && n <= (int64_t)INT32_MAX / 2;
+}
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess)
+        return Q4_OK;
+    g_last_hip_error = (int)e;
+    return Q4_ERR_HIP;
+}
+
+// Checks shared by every op that reads a packed weight; returns the logical
+// row count of the layout through `rows`.
+int check_weight(const q4_weight *w, int32_t want_layout, q4::Geometry *geo, int64_t *rows)
+{
+    if (!w || !w->data)
+        return Q4_ERR_NULL;
+    if (!valid_shape(w->n, w->k))
+        return Q4_ERR_SHAPE;
+    if (w->layout != want_layout || w->version != Q4_LAYOUT_VERSION)
+        return Q4_ERR_LAYOUT;
+    if (!aligned(w->data, 256))
+        return Q4_ERR_ALIGN;
+    *rows = (want_layout == Q4_LAYOUT_GATE_UP) ? 2 * (int64_t)w->n : (int64_t)w->n;
+    if (!q4::layout_geometry(*rows, w->k, geo))
+        return Q4_ERR_SHAPE;
+    if (w->bytes < geo->tiles * geo->tile_bytes)
+        return Q4_ERR_SIZE;
+    return Q4_OK;
+}
+
+int pack_common(const uint32_t *w0, const uint16_t *s0, const uint32_t *w1, const uint16_t *s1,
+                int32_t n, int32_t k, bool gate_up, void *dst, int64_t dst_bytes, q4_weight *out,
+                void *stream)
+{
+    if (!w0 || !s0 || !dst || !out || (gate_up && (!w1 || !s1)))
+        return Q4_ERR_NULL;
+    if (!valid_shape(n, k))
+        return Q4_ERR_SHAPE;
+    if (!aligned(w0, 16) || !aligned(s0, 2) || !aligned(dst, 256) ||
+        (gate_up && (!aligned(w1, 16) || !aligned(s1, 2))))
+        return Q4_ERR_ALIGN;
+    const int64_t rows = gate_up ? 2 * (int64_t)n : (int64_t)n;
+    q4::Geometry geo;
+    if (!q4::layout_geometry(rows, k, &geo))
+        return Q4_ERR_SHAPE;
+    const int64_t need = geo.tiles * geo.tile_bytes;
+    if (dst_bytes < need)
+        return Q4_ERR_SIZE;
+    const int64_t wbytes = (int64_t)n * k / 2, sbytes = (int64_t)n * (k / 32) * 2;
+    if (overlap(dst, need, w0, wbytes) || overlap(dst, need, s0, sbytes) ||
+        (gate_up && (overlap(dst, need, w1, wbytes) || overlap(dst, need, s1, sbytes))))
+        return Q4_ERR_ALIAS;
+    (void)hipGetLastError();
+    const int rc = hip_status(q4::launch_pack(w0, s0, w1, s1, rows, k, gate_up, geo, dst,
+                                              static_cast<hipStream_t>(stream)));
+    if (rc != Q4_OK)
+        return rc;
+    out->n = n;
+    out->k = k;
+    out->layout = gate_up ? Q4_LAYOUT_GATE_UP : Q4_LAYOUT_ROWS;
+    out->version = Q4_LAYOUT_VERSION;
+    out->data = dst;
+    out->bytes = need;
+    return Q4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t q4_packed_bytes(int32_t n, int32_t k, int32_t layout)
+{
+    if (!valid_shape(n, k) || (layout != Q4_LAYOUT_ROWS && layout != Q4_LAYOUT_GATE_UP))
+        return 0;
+    q4::Geometry geo;
+    const int64_t rows = layout == Q4_LAYOUT_GATE_UP ? 2 * (int64_t)n : (int64_t)n;
+    if (!q4::layout_geometry(rows, k, &geo))
+        return 0;
+    return geo.tiles * geo.tile_bytes;
+}
+
+int64_t q4_workspace_bytes(int32_t op, int32_t m, int32_t n, int32_t k)
+{
+    if (m < 1 || !valid_shape(n, k))
+        return 0;
+    if (op == Q4_OP_LMHEAD) {
+        q4::Geometry geo;
+        if (!q4::layout_geometry(n, k, &geo))
+            return 0;
+        return q4::argmax_workspace_bytes(geo.tiles);
+    }
+    return 0;
+}
+
+int q4_layout_geometry(int32_t rows, int32_t k, int64_t *out)
+{
+    if (!out)
+        return Q4_ERR_NULL;
+    q4::Geometry geo;
+    if (!valid_shape(rows, k) || !q4::layout_geometry(rows, k, &geo))
+        return Q4_ERR_SHAPE;
+    out[0] = geo.L;
+    out[1] = geo.CG;
+    out[2] = geo.P;
+    out[3] = geo.TR;
+    out[4] = geo.tiles;
+    out[5] = geo.tile_bytes;
+    return Q4_OK;
+}
+
+int q4_pack(const uint32_t *words, const uint16_t *scales, int32_t n, int32_t k, void *dst,
+            int64_t dst_bytes, q4_weight *out, void *stream)
+{
+    return pack_common(words, scales, nullptr, nullptr, n, k, false, dst, dst_bytes, out, stream);
+}
+
+int q4_pack_gate_up(const uint32_t *gw, const uint16_t *gs, const uint32_t *uw,
+                    const uint16_t *us, int32_t n, int32_t k, void *dst, int64_t dst_bytes,
+                    q4_weight *out, void *stream)
+{
+    return pack_common(gw, gs, uw, us, n, k, true, dst, dst_bytes, out, stream);
+}
+
+int q4_unpack(const q4_weight *w, uint32_t *words, uint16_t *scales, void *stream)
+{
+    if (!w || !words || !scales)
+        return Q4_ERR_NULL;
+    if (w->layout != Q4_LAYOUT_ROWS && w->layout != Q4_LAYOUT_GATE_UP)
+        return Q4_ERR_LAYOUT;
+    q4::Geometry geo;
+    int64_t rows = 0;
+    const int rc = check_weight(w, w->layout, &geo, &rows);
+    if (rc != Q4_OK)
+        return rc;
+    if (!aligned(words, 16) || !aligned(scales, 2))
+        return Q4_ERR_ALIGN;
+    const int64_t wbytes = rows * w->k / 2, sbytes = rows * (w->k / 32) * 2;
+    if (overlap(words, wbytes, w->data, w->bytes) || overlap(scales, sbytes, w->data, w->bytes) ||
+        overlap(words, wbytes, scales, sbytes))
+        return Q4_ERR_ALIAS;
+    (void)hipGetLastError();
+    return hip_status(q4::launch_unpack(w->data, rows, w->k, geo, words, scales,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int q4_gemv(const q4_weight *w, const uint16_t *x, uint16_t *y, void *stream)
+{
+    q4::Geometry geo;
+    int64_t rows = 0;
+    if (!w || !x || !y)
+        return Q4_ERR_NULL;
+    int rc = check_weight(w, Q4_LAYOUT_ROWS, &geo, &rows);
+    if (rc != Q4_OK)
+        return rc;
+    if (!aligned(x, 16) || !aligned(y, 4))
+        return Q4_ERR_ALIGN;
+    if (overlap(y, 2 * (int64_t)w->n, x, 2 * (int64_t)w->k) ||
+        overlap(y, 2 * (int64_t)w->n, w->data, w->bytes))
+        return Q4_ERR_ALIAS;
+    (void)hipGetLastError();
+    return hip_status(q4::launch_gemv_family(geo, q4::EPI_F16, w->data, x, y, rows, w->k, w->n,
+                                             q4::ArgmaxScratch{nullptr, nullptr, nullptr},
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int q4_gemm(const q4_weight *w, const uint16_t *X, int32_t m, uint16_t *Y, void *ws,
+            int64_t ws_bytes, void *stream)
+{
+    (void)ws;
+    (void)ws_bytes;
+    q4::Geometry geo;
+    int64_t rows = 0;
+    if (!w || !X || !Y)
+        return Q4_ERR_NULL;
+    int rc = check_weight(w, Q4_LAYOUT_ROWS, &geo, &rows);
+    if (rc != Q4_OK)
+        return rc;
+    if (m < 1)
+        return Q4_ERR_SHAPE;
+    if (!aligned(X, 16) || !aligned(Y, 4))
+        return Q4_ERR_ALIGN;
+    const int64_t ybytes = 2 * (int64_t)m * w->n, xbytes = 2 * (int64_t)m * w->k;
+    if (overlap(Y, ybytes, X, xbytes) || overlap(Y, ybytes, w->data, w->bytes))
+        return Q4_ERR_ALIAS;
+    (void)hipGetLastError();
+    return hip_status(q4::launch_gemm(geo, w->data, X, m, w->n, w->k, Y,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int q4_ffn_gate_up_silu(const q4_weight *w, const uint16_t *x, uint16_t *h, void *stream)
+{
+    q4::Geometry geo;
+    int64_t rows = 0;
+    if (!w || !x || !h)
+        return Q4_ERR_NULL;
+    int rc = check_weight(w, Q4_LAYOUT_GATE_UP, &geo, &rows);
+    if (rc != Q4_OK)
+        return rc;
+    if (!aligned(x, 16) || !aligned(h, 2))
+        return Q4_ERR_ALIGN;
+    if (overlap(h, 2 * (int64_t)w->n, x, 2 * (int64_t)w->k) ||
+        overlap(h, 2 * (int64_t)w->n, w->data, w->bytes))
+        return Q4_ERR_ALIAS;
+    (void)hipGetLastError();
+    return hip_status(q4::launch_gemv_family(geo, q4::EPI_SILU, w->data, x, h, rows, w->k, w->n,
+                                             q4::ArgmaxScratch{nullptr, nullptr, nullptr},
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int q4_lmhead_f32(const q4_weight *w, const uint16_t *x, float *logits, int32_t *argmax,
+                  void *ws, int64_t ws_bytes, void *stream)
+{
+    q4::Geometry geo;
+    int64_t rows = 0;
+    if (!w || !x || !logits)
+        return Q4_ERR_NULL;
+    int rc = check_weight(w, Q4_LAYOUT_ROWS, &geo, &rows);
+    if (rc != Q4_OK)
+        return rc;
+    if (!aligned(x, 16) || !aligned(logits, 8) || (argmax && !aligned(argmax, 4)))
+        return Q4_ERR_ALIGN;
+    const int64_t lbytes = 4 * (int64_t)w->n;
+    q4::ArgmaxScratch am{nullptr, nullptr, nullptr};
+    if (argmax) {
+        const int64_t need = q4::argmax_workspace_bytes(geo.tiles);
+        if (!ws || ws_bytes < need)
+            return Q4_ERR_WORKSPACE;
+        if (!aligned(ws, 256))
+            return Q4_ERR_ALIGN;
+        if (overlap(ws, need, x, 2 * (int64_t)w->k) || overlap(ws, need, w->data, w->bytes) ||
+            overlap(ws, need, logits, lbytes) || overlap(ws, need, argmax, 4) ||
+            overlap(argmax, 4, x, 2 * (int64_t)w->k) || overlap(argmax, 4, w->data, w->bytes) ||
+            overlap(argmax, 4, logits, lbytes))
+            return Q4_ERR_ALIAS;
+        am.counter = static_cast<unsigned int *>(ws);
+        am.partials = reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) +
+                                                             q4::kArgmaxHeader);
+        am.result = argmax;
+    }
+    if (overlap(logits, lbytes, x, 2 * (int64_t)w->k) ||
+        overlap(logits, lbytes, w->data, w->bytes))
+        return Q4_ERR_ALIAS;
+    (void)hipGetLastError();
+    return hip_status(q4::launch_gemv_family(geo, q4::EPI_F32, w->data, x, logits, rows, w->k,
+                                             w->n, am, static_cast<hipStream_t>(stream)));
+}
+
+const char *q4_strerror(int code)
+{
+    switch (code) {
+    case Q4_OK: return "ok";
+    case Q4_ERR_NULL: return "a required pointer is NULL";
+    case Q4_ERR_SHAPE: return "invalid shape (n < 1, k < 32, k % 32 != 0, m < 1 or too large)";
+    case Q4_ERR_ALIGN: return "a pointer is not aligned as documented";
+    case Q4_ERR_LAYOUT: return "weight layout or layout version does not suit this call";
+    case Q4_ERR_WORKSPACE: return "workspace missing or smaller than q4_workspace_bytes";
+    case Q4_ERR_ALIAS: return "an output range overlaps an input range";
+    case Q4_ERR_HIP: return "the HIP runtime refused the launch (see q4_last_hip_error)";
+    case Q4_ERR_SIZE: return "a destination buffer is smaller than required";
+    }
+    return "unknown q4 error code";
+}
+
+int q4_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

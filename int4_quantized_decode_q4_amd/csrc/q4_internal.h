@@ -1,0 +1,49 @@
+// q4_internal.h -- launchers shared by the host API (q4_api.cpp) and the
+// kernels (q4_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "q4_geometry.h"
+
+namespace q4 {
+
+enum Epilogue {
+    EPI_F16 = 0,   // y f16, rounded to nearest even
+    EPI_F32 = 1,   // f32 logits, optional argmax
+    EPI_SILU = 2,  // interleaved gate/up rows -> SiLU(g) * u, f16
+};
+
+// Scratch of the LM-head argmax inside the caller's workspace.
+struct ArgmaxScratch {
+    unsigned int *counter;        // zero between calls
+    unsigned long long *partials; // one (f32 bits | index << 32) per block
+    int32_t *result;              // device int32 [1]
+};
+
+constexpr int64_t kArgmaxHeader = 256;   // counter area at the head of ws
+
+// Blocks of 256 threads (4 wavefronts) the GEMV family launches for a weight
+// with `tiles` tiles.
+int64_t gemv_blocks(int64_t tiles);
+
+// Bytes of workspace the argmax needs for `tiles` tiles.
+int64_t argmax_workspace_bytes(int64_t tiles);
+
+hipError_t launch_pack(const uint32_t *w0, const uint16_t *s0, const uint32_t *w1,
+                       const uint16_t *s1, int64_t rows, int64_t k, bool gate_up,
+                       const Geometry &geo, void *dst, hipStream_t stream);
+
+hipError_t launch_unpack(const void *src, int64_t rows, int64_t k, const Geometry &geo,
+                         uint32_t *words, uint16_t *scales, hipStream_t stream);
+
+hipError_t launch_gemv_family(const Geometry &geo, Epilogue epi, const void *wdata,
+                              const uint16_t *x, void *out, int64_t rows, int64_t k,
+                              int64_t n_out, ArgmaxScratch am, hipStream_t stream);
+
+hipError_t launch_gemm(const Geometry &geo, const void *wdata, const uint16_t *X,
+                       int64_t m, int64_t n, int64_t k, uint16_t *Y, hipStream_t stream);
+
+}  // namespace q4

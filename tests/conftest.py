@@ -24,3 +24,19 @@ def pytest_configure(config):
 def orc():
     import oracle
     return oracle.load()
+
+
+@pytest.fixture(scope="session")
+def q4():
+    """The HIP library binding; GPU tests fail (not skip) without a GPU or
+    without the built library."""
+    import torch
+    assert torch.cuda.is_available(), "gpu tests need a visible MI355X"
+    import int4_quantized_decode_q4_amd as q4mod
+    return q4mod
+
+
+def pytest_runtest_setup(item):
+    # name the case before any GPU work, so a fault still leaves a trace
+    if item.get_closest_marker("gpu") is not None:
+        print(f"\n[gpu-case] {item.nodeid}", flush=True)

@@ -1,0 +1,143 @@
+"""The C ABI on the CPU (no GPU needed, nothing is launched): the library
+loads and exports every function include/q4.h declares; the host geometry
+agrees with the oracle's; every documented error code comes back, from the
+host-side validation, before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4.h")
+
+
+@pytest.fixture(scope="module")
+def q4():
+    import int4_quantized_decode_q4_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(q4_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_function(q4):
+    names = declared_functions()
+    assert len(names) >= 12, names
+    lib = ctypes.CDLL(q4.LIBRARY)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+SHAPES = [(3072, 3072), (3072, 8192), (32064, 3072), (1, 32), (17, 96), (130, 64), (33, 224),
+          (7, 160), (6, 192), (3, 3200), (5, 16384), (3, 8352), (4, 16480), (999, 544),
+          (2, 2048), (10, 12288), (1, 65536)]
+
+
+@pytest.mark.parametrize("n,k", SHAPES)
+def test_host_geometry_matches_oracle(q4, orc, n, k):
+    assert q4.layout_geometry(n, k) == orc.layout_geometry(n, k)
+    assert q4.packed_bytes(n, k) == orc.layout_bytes(n, k)
+    assert q4.packed_bytes(n, k, q4.LAYOUT_GATE_UP) == orc.layout_bytes(2 * n, k)
+
+
+def test_packed_bytes_invalid(q4):
+    assert q4.packed_bytes(0, 32) == 0
+    assert q4.packed_bytes(1, 48) == 0
+    assert q4.packed_bytes(1, 16) == 0
+    assert q4.packed_bytes(-5, 64) == 0
+    assert q4.packed_bytes(4, 64, 7) == 0
+
+
+# fake device addresses: validation rejects the call before anything uses them
+A = 0x7f0000000000
+
+
+def weight(q4, n=64, k=96, layout=1, version=1, data=A + 0x100000, nbytes=None):
+    w = q4.q4_weight()
+    w.n, w.k, w.layout, w.version = n, k, layout, version
+    w.data = data
+    w.bytes = q4.packed_bytes(n, k, layout) if nbytes is None else nbytes
+    return w
+
+
+def test_pack_errors(q4):
+    lib = q4.lib
+    out = q4.q4_weight()
+    nb = q4.packed_bytes(64, 96)
+    r = ctypes.byref(out)
+    W, S, D = A, A + 0x10000, A + 0x100000
+    assert lib.q4_pack(None, S, 64, 96, D, nb, r, None) == q4.ERR_NULL
+    assert lib.q4_pack(W, S, 64, 96, D, nb, None, None) == q4.ERR_NULL
+    assert lib.q4_pack(W, S, 0, 96, D, nb, r, None) == q4.ERR_SHAPE
+    assert lib.q4_pack(W, S, 64, 100, D, nb, r, None) == q4.ERR_SHAPE
+    assert lib.q4_pack(W, S, 64, 16, D, nb, r, None) == q4.ERR_SHAPE
+    assert lib.q4_pack(W + 4, S, 64, 96, D, nb, r, None) == q4.ERR_ALIGN
+    assert lib.q4_pack(W, S + 1, 64, 96, D, nb, r, None) == q4.ERR_ALIGN
+    assert lib.q4_pack(W, S, 64, 96, D + 16, nb, r, None) == q4.ERR_ALIGN
+    assert lib.q4_pack(W, S, 64, 96, D, nb - 1, r, None) == q4.ERR_SIZE
+    assert lib.q4_pack(W, S, 64, 96, W, nb, r, None) == q4.ERR_ALIAS
+    assert lib.q4_pack_gate_up(W, S, None, S, 64, 96, D, 10 ** 9, r, None) == q4.ERR_NULL
+    nb3 = q4.packed_bytes(64, 3072)
+    assert lib.q4_pack_gate_up(W, S, W, S, 64, 3072, D, nb3, r, None) == q4.ERR_SIZE
+    assert out.data is None   # nothing was written to the descriptor
+
+
+def test_gemv_family_errors(q4):
+    lib = q4.lib
+    X, Y = A + 0x200000, A + 0x300000
+    w = weight(q4)
+    r = ctypes.byref(w)
+    assert lib.q4_gemv(None, X, Y, None) == q4.ERR_NULL
+    assert lib.q4_gemv(r, None, Y, None) == q4.ERR_NULL
+    assert lib.q4_gemv(r, X, None, None) == q4.ERR_NULL
+    assert lib.q4_gemv(ctypes.byref(weight(q4, data=None)), X, Y, None) == q4.ERR_NULL
+    assert lib.q4_gemv(ctypes.byref(weight(q4, k=100)), X, Y, None) == q4.ERR_SHAPE
+    assert lib.q4_gemv(ctypes.byref(weight(q4, n=0)), X, Y, None) == q4.ERR_SHAPE
+    assert lib.q4_gemv(ctypes.byref(weight(q4, layout=2)), X, Y, None) == q4.ERR_LAYOUT
+    assert lib.q4_gemv(ctypes.byref(weight(q4, version=2)), X, Y, None) == q4.ERR_LAYOUT
+    assert lib.q4_gemv(ctypes.byref(weight(q4, data=A + 0x100010)), X, Y, None) == q4.ERR_ALIGN
+    assert lib.q4_gemv(ctypes.byref(weight(q4, nbytes=100)), X, Y, None) == q4.ERR_SIZE
+    assert lib.q4_gemv(r, X + 8, Y, None) == q4.ERR_ALIGN
+    assert lib.q4_gemv(r, X, Y + 2, None) == q4.ERR_ALIGN
+    assert lib.q4_gemv(r, X, X + 64, None) == q4.ERR_ALIAS
+    assert lib.q4_gemv(r, X, A + 0x100000 + 512, None) == q4.ERR_ALIAS
+    # gemm
+    assert lib.q4_gemm(r, X, 0, Y, None, 0, None) == q4.ERR_SHAPE
+    assert lib.q4_gemm(r, X, 4, X + 256, None, 0, None) == q4.ERR_ALIAS
+    assert lib.q4_gemm(r, X + 2, 4, Y, None, 0, None) == q4.ERR_ALIGN
+    # fused FFN wants the gate/up layout
+    assert lib.q4_ffn_gate_up_silu(r, X, Y, None) == q4.ERR_LAYOUT
+    gu = weight(q4, layout=2)
+    assert lib.q4_ffn_gate_up_silu(ctypes.byref(gu), X, X, None) == q4.ERR_ALIAS
+    assert lib.q4_ffn_gate_up_silu(ctypes.byref(gu), X, Y + 1, None) == q4.ERR_ALIGN
+
+
+def test_lmhead_errors(q4):
+    lib = q4.lib
+    X, L, I, WS = A + 0x200000, A + 0x300000, A + 0x400000, A + 0x500000
+    w = weight(q4, n=32064, k=3072)
+    r = ctypes.byref(w)
+    need = lib.q4_workspace_bytes(q4.OP_LMHEAD, 1, 32064, 3072)
+    assert need > 256
+    assert lib.q4_workspace_bytes(q4.OP_GEMV, 1, 32064, 3072) == 0
+    assert lib.q4_lmhead_f32(r, X, None, I, WS, need, None) == q4.ERR_NULL
+    assert lib.q4_lmhead_f32(r, X, L, I, None, 0, None) == q4.ERR_WORKSPACE
+    assert lib.q4_lmhead_f32(r, X, L, I, WS, need - 1, None) == q4.ERR_WORKSPACE
+    assert lib.q4_lmhead_f32(r, X, L, I, WS + 8, need, None) == q4.ERR_ALIGN
+    assert lib.q4_lmhead_f32(r, X, L + 4, I, WS, need, None) == q4.ERR_ALIGN
+    assert lib.q4_lmhead_f32(r, X, L, I + 2, WS, need, None) == q4.ERR_ALIGN
+    assert lib.q4_lmhead_f32(r, X, L, WS + 512, WS, need, None) == q4.ERR_ALIAS
+    assert lib.q4_lmhead_f32(r, X, L, L + 64, WS, need, None) == q4.ERR_ALIAS
+    assert lib.q4_lmhead_f32(r, X, X, None, None, 0, None) == q4.ERR_ALIAS
+
+
+def test_strerror_and_last_error(q4):
+    lib = q4.lib
+    texts = {c: lib.q4_strerror(c).decode() for c in range(-8, 1)}
+    assert len(set(texts.values())) == 9 and all(texts.values())
+    assert "unknown" in lib.q4_strerror(-99).decode()
+    assert lib.q4_last_hip_error() == 0

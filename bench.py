@@ -150,39 +150,44 @@ def copies_for(nbytes: int) -> int:
     return max(2, -(-ROTATE_BYTES // nbytes))
 
 
+def capture(torch, fn, first: int, count: int):
+    """A HIP graph of fn(first), ..., fn(first + count - 1), captured on a side
+    stream (the library launches on torch's current stream, which is the
+    capture stream inside the block)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(first)                       # one eager call before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(first, first + count):
+            fn(i)
+    return g
+
+
 def timed(torch, fn, steps: int, warmup: int):
-    """Wall time of `steps` calls of fn(i) (ms per call), bracketed by
-    synchronisation on both sides, after `warmup` untimed calls."""
-    for i in range(warmup):
-        fn(i)
+    """Wall time per call (ms) of exactly `steps` calls fn(warmup), ...,
+    replayed from one HIP graph and bracketed by synchronisation on both
+    sides, after `warmup` untimed calls (their own graph)."""
+    gw = capture(torch, fn, 0, max(1, warmup))
+    gt = capture(torch, fn, warmup, steps)
+    gw.replay()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for i in range(steps):
-        fn(warmup + i)
+    gt.replay()
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
 
 
-def per_kernel(torch, launches, steps: int, warmup: int):
-    """Average device duration (us) of each launch of a step, from HIP events
-    recorded on the launching (current) stream around every launch."""
-    for i in range(warmup):
-        for fn in launches.values():
-            fn(i)
-    torch.cuda.synchronize()
-    ev = {name: [] for name in launches}
-    for i in range(steps):
-        for name, fn in launches.items():
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn(warmup + i)
-            b.record()
-            ev[name].append((a, b))
-    torch.cuda.synchronize()
-    return {name: 1000.0 * sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
-            for name, pairs in ev.items()}
+def per_launch_us(torch, fn, launches: int = 200, warmup: int = 20):
+    """Average device time (us) of one launch of fn: `launches` back-to-back
+    launches (rotating weight copies) replayed from a HIP graph, bracketed by
+    HIP events on the launching stream."""
+    return 1000.0 * timed(torch, fn, launches, warmup)
 
 
 def main():
@@ -227,7 +232,7 @@ def main():
 
     step_bytes = sum(gemv_bytes(n, k) for n, k in si.LAYER_SHAPES.values())
     ms = timed(torch, step, K, W)
-    kus = per_kernel(torch, launches, K, W)
+    kus = {key: per_launch_us(torch, fn, K, W) for key, fn in launches.items()}
     gbs = step_bytes / (ms * 1e-3) / 1e9
     dom = "gate_up"
     dn, dk = si.LAYER_SHAPES[dom]
@@ -288,7 +293,7 @@ def variants(torch, q4, si, np, K, W):
                    copies_for(weight_bytes(3072, 3072)))
     x = dev_f16(inp["x"])
     y = torch.empty(3072, dtype=torch.float16, device="cuda")
-    us = per_kernel(torch, {"g": lambda i: q4.gemv(rot[i], x, y)}, K, W)["g"]
+    us = per_launch_us(torch, lambda i: q4.gemv(rot[i], x, y), K, W)
     out["gemv_3072x3072"] = {"us": round(us, 3), "gbs": round(nb / us / 1e3, 1),
                              "frac": round(nb / us / 1e3 / PEAK_HBM_GBS, 4), "bytes": nb}
     del rot
@@ -303,8 +308,8 @@ def variants(torch, q4, si, np, K, W):
     x = dev_f16(inp["x"])
     h = torch.empty(8192, dtype=torch.float16, device="cuda")
     yd = torch.empty(3072, dtype=torch.float16, device="cuda")
-    kus = per_kernel(torch, {"ffn": lambda i: q4.ffn_gate_up_silu(rot_gu[i], x, h),
-                             "down": lambda i: q4.gemv(rot_d[i], h, yd)}, K, W)
+    kus = {"ffn": per_launch_us(torch, lambda i: q4.ffn_gate_up_silu(rot_gu[i], x, h), K, W),
+           "down": per_launch_us(torch, lambda i: q4.gemv(rot_d[i], h, yd), K, W)}
     dbytes = gemv_bytes(3072, 8192)
     out["ffn_fused_8192x3072_plus_down"] = {
         "ffn_us": round(kus["ffn"], 3), "ffn_gbs": round(gu_bytes / kus["ffn"] / 1e3, 1),
@@ -321,7 +326,7 @@ def variants(torch, q4, si, np, K, W):
     x = dev_f16(inp["x"])
     logits = torch.empty(32064, dtype=torch.float32, device="cuda")
     am = torch.empty(1, dtype=torch.int32, device="cuda")
-    us = per_kernel(torch, {"lm": lambda i: q4.lmhead_f32(rot[i], x, logits, am)}, K, W)["lm"]
+    us = per_launch_us(torch, lambda i: q4.lmhead_f32(rot[i], x, logits, am), K, W)
     out["lm_head_32064x3072_f32_argmax"] = {"us": round(us, 3), "gbs": round(nb / us / 1e3, 1),
                                             "frac": round(nb / us / 1e3 / PEAK_HBM_GBS, 4),
                                             "bytes": nb}
@@ -336,7 +341,7 @@ def variants(torch, q4, si, np, K, W):
         X = dev_f16(np.ascontiguousarray(inp["X"][:m]))
         Y = torch.empty((m, 16384), dtype=torch.float16, device="cuda")
         steps = max(20, K // 4)
-        us = per_kernel(torch, {"g": lambda i: q4.gemm(rot[i], X, Y)}, steps, min(W, 5))["g"]
+        us = per_launch_us(torch, lambda i: q4.gemm(rot[i], X, Y), steps, min(W, 5))
         nb = weight_bytes(16384, 3072) + 2 * m * 3072 + 2 * m * 16384
         fl = 2.0 * m * 16384 * 3072
         gm[str(m)] = {"us": round(us, 3), "gbs": round(nb / us / 1e3, 1),

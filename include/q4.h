@@ -102,10 +102,8 @@ typedef struct q4_weight {
 int64_t q4_packed_bytes(int32_t n, int32_t k, int32_t layout);
 
 /* Bytes of device workspace an op needs (0 = none).  The LM-head argmax needs
- * one; its first 256 bytes hold a counter that must be zero before the first
- * call on that workspace (allocate it zero-filled); every completed call
- * leaves it at zero again.  Two calls that share a workspace must be ordered
- * on one stream. */
+ * one (per-block candidates; contents need no initialisation).  Two calls
+ * that share a workspace must be ordered on one stream. */
 int64_t q4_workspace_bytes(int32_t op, int32_t m, int32_t n, int32_t k);
 
 /*
@@ -174,8 +172,9 @@ int q4_ffn_gate_up_silu(const q4_weight *w, const uint16_t *x, uint16_t *h,
  *   logits : device f32 [n], 8-byte aligned
  *   argmax : device int32 [1] or NULL; the lowest index holding the maximum
  *            logit (as computed in f32)
- *   ws     : >= q4_workspace_bytes(Q4_OP_LMHEAD, 1, n, k) bytes when argmax is
- *            not NULL (see q4_workspace_bytes for its zero-counter contract)
+ *   ws     : >= q4_workspace_bytes(Q4_OP_LMHEAD, 1, n, k) bytes, 256-byte
+ *            aligned, when argmax is not NULL; the argmax then takes a second
+ *            small launch on the same stream
  */
 int q4_lmhead_f32(const q4_weight *w, const uint16_t *x, float *logits,
                   int32_t *argmax, void *ws, int64_t ws_bytes, void *stream);

@@ -225,8 +225,7 @@ _workspaces: dict = {}
 
 
 def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    """A zero-filled workspace of at least nbytes on `device`, kept per device
-    (the LM-head argmax leaves its counter at zero after every call)."""
+    """A workspace of at least nbytes on `device`, kept per device."""
     key = (device.type, device.index)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:

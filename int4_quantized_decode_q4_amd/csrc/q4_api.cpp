@@ -120,7 +120,7 @@ int64_t q4_workspace_bytes(int32_t op, int32_t m, int32_t n, int32_t k)
         q4::Geometry geo;
         if (!q4::layout_geometry(n, k, &geo))
             return 0;
-        return q4::argmax_workspace_bytes(geo.tiles);
+        return q4::argmax_workspace_bytes(geo);
     }
     return 0;
 }
@@ -192,7 +192,7 @@ int q4_gemv(const q4_weight *w, const uint16_t *x, uint16_t *y, void *stream)
         return Q4_ERR_ALIAS;
     (void)hipGetLastError();
     return hip_status(q4::launch_gemv_family(geo, q4::EPI_F16, w->data, x, y, rows, w->k, w->n,
-                                             q4::ArgmaxScratch{nullptr, nullptr, nullptr},
+                                             q4::ArgmaxScratch{nullptr, nullptr},
                                              static_cast<hipStream_t>(stream)));
 }
 
@@ -236,7 +236,7 @@ int q4_ffn_gate_up_silu(const q4_weight *w, const uint16_t *x, uint16_t *h, void
         return Q4_ERR_ALIAS;
     (void)hipGetLastError();
     return hip_status(q4::launch_gemv_family(geo, q4::EPI_SILU, w->data, x, h, rows, w->k, w->n,
-                                             q4::ArgmaxScratch{nullptr, nullptr, nullptr},
+                                             q4::ArgmaxScratch{nullptr, nullptr},
                                              static_cast<hipStream_t>(stream)));
 }
 
@@ -253,9 +253,9 @@ int q4_lmhead_f32(const q4_weight *w, const uint16_t *x, float *logits, int32_t 
     if (!aligned(x, 16) || !aligned(logits, 8) || (argmax && !aligned(argmax, 4)))
         return Q4_ERR_ALIGN;
     const int64_t lbytes = 4 * (int64_t)w->n;
-    q4::ArgmaxScratch am{nullptr, nullptr, nullptr};
+    q4::ArgmaxScratch am{nullptr, nullptr};
     if (argmax) {
-        const int64_t need = q4::argmax_workspace_bytes(geo.tiles);
+        const int64_t need = q4::argmax_workspace_bytes(geo);
         if (!ws || ws_bytes < need)
             return Q4_ERR_WORKSPACE;
         if (!aligned(ws, 256))
@@ -265,9 +265,7 @@ int q4_lmhead_f32(const q4_weight *w, const uint16_t *x, float *logits, int32_t 
             overlap(argmax, 4, x, 2 * (int64_t)w->k) || overlap(argmax, 4, w->data, w->bytes) ||
             overlap(argmax, 4, logits, lbytes))
             return Q4_ERR_ALIAS;
-        am.counter = static_cast<unsigned int *>(ws);
-        am.partials = reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) +
-                                                             q4::kArgmaxHeader);
+        am.partials = static_cast<unsigned long long *>(ws);
         am.result = argmax;
     }
     if (overlap(logits, lbytes, x, 2 * (int64_t)w->k) ||

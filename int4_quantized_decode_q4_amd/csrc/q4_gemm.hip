@@ -14,7 +14,7 @@ hipError_t launch_gemm(const Geometry &geo, const void *wdata, const uint16_t *X
     // VALU multi-vector and MFMA kernels)
     for (int64_t i = 0; i < m; ++i) {
         const hipError_t e = launch_gemv_family(geo, EPI_F16, wdata, X + i * k, Y + i * n, n, k, n,
-                                                ArgmaxScratch{nullptr, nullptr, nullptr}, stream);
+                                                ArgmaxScratch{nullptr, nullptr}, stream);
         if (e != hipSuccess)
             return e;
     }

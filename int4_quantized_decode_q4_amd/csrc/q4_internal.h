@@ -18,19 +18,13 @@ enum Epilogue {
 
 // Scratch of the LM-head argmax inside the caller's workspace.
 struct ArgmaxScratch {
-    unsigned int *counter;        // zero between calls
     unsigned long long *partials; // one (f32 bits | index << 32) per block
     int32_t *result;              // device int32 [1]
 };
 
-constexpr int64_t kArgmaxHeader = 256;   // counter area at the head of ws
-
-// Blocks of 256 threads (4 wavefronts) the GEMV family launches for a weight
-// with `tiles` tiles.
-int64_t gemv_blocks(int64_t tiles);
-
-// Bytes of workspace the argmax needs for `tiles` tiles.
-int64_t argmax_workspace_bytes(int64_t tiles);
+// Bytes of workspace the LM-head argmax needs for a weight of this geometry
+// (one 8-byte candidate per launched block; no initialisation needed).
+int64_t argmax_workspace_bytes(const Geometry &geo);
 
 hipError_t launch_pack(const uint32_t *w0, const uint16_t *s0, const uint32_t *w1,
                        const uint16_t *s1, int64_t rows, int64_t k, bool gate_up,

@@ -140,16 +140,34 @@ __device__ __forceinline__ void load_x_group(uint32_t *xp, const uint16_t *__res
     }
 }
 
+// The dequant masks and the f16 exponent pattern, held in VGPRs.  gfx9 VOP3
+// instructions take no literal operands and read at most one SGPR, so with
+// plain constants the compiler splits (w & mask) | magic into a VOP2 and and
+// a VOP2 or (two instructions); from registers it is one v_and_or_b32.
+struct DequantConsts {
+    uint32_t lo, hi, magic;
+};
+
+__device__ __forceinline__ DequantConsts dequant_consts()
+{
+    DequantConsts k;
+    asm("v_mov_b32 %0, 0x000F000F" : "=v"(k.lo));
+    asm("v_mov_b32 %0, 0x00F000F0" : "=v"(k.hi));
+    asm("v_mov_b32 %0, 0x64006400" : "=v"(k.magic));
+    return k;
+}
+
 // 8 codes (canonical nibble order) against their 4 prepared x pairs.
-__device__ __forceinline__ void dot_word(uint32_t w, const uint32_t *xp, float &p1, float &p16)
+__device__ __forceinline__ void dot_word(uint32_t w, const uint32_t *xp, float &p1, float &p16,
+                                         const DequantConsts &m)
 {
     const h2 k1 = {(_Float16)1032.0f, (_Float16)1032.0f};
     const h2 k16 = {(_Float16)1152.0f, (_Float16)1152.0f};
-    const uint32_t a0 = (w & 0x000F000Fu) | 0x64006400u;   // 1024 + q0, 1024 + q4
-    const uint32_t a1 = (w & 0x00F000F0u) | 0x64006400u;   // 1024 + 16 q1, 1024 + 16 q5
+    const uint32_t a0 = (w & m.lo) | m.magic;   // 1024 + q0, 1024 + q4
+    const uint32_t a1 = (w & m.hi) | m.magic;   // 1024 + 16 q1, 1024 + 16 q5
     const uint32_t b = w >> 8;
-    const uint32_t a2 = (b & 0x000F000Fu) | 0x64006400u;   // q2, q6
-    const uint32_t a3 = (b & 0x00F000F0u) | 0x64006400u;   // 16 q3, 16 q7
+    const uint32_t a2 = (b & m.lo) | m.magic;   // q2, q6
+    const uint32_t a3 = (b & m.hi) | m.magic;   // 16 q3, 16 q7
     p1 = __builtin_amdgcn_fdot2(as_h2(a0) - k1, as_h2(xp[0]), p1, false);
     p16 = __builtin_amdgcn_fdot2(as_h2(a1) - k16, as_h2(xp[1]), p16, false);
     p1 = __builtin_amdgcn_fdot2(as_h2(a2) - k1, as_h2(xp[2]), p1, false);
@@ -230,143 +248,514 @@ __device__ __forceinline__ unsigned long long pack_vi(float v, int i)
            ((unsigned long long)(unsigned int)i << 32);
 }
 
-// Argmax across blocks: each block publishes its candidate, the last block
-// to arrive combines all of them in index order and resets the counter.
+// Argmax across blocks, step 1: each block publishes its candidate (plain
+// store; the reduce kernel that follows on the stream sees it at the kernel
+// boundary, so no fence or atomic is needed).
 __device__ void grid_argmax(float bv, int bi, ArgmaxScratch am)
 {
     __shared__ float sv[16];
     __shared__ int si[16];
-    __shared__ int is_last;
     block_argmax(bv, bi, sv, si);
-    if (threadIdx.x == 0) {
-        __hip_atomic_store(am.partials + blockIdx.x, pack_vi(bv, bi), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        __threadfence();
-        const unsigned prev = atomicAdd(am.counter, 1u);
-        is_last = (prev == gridDim.x - 1);
-    }
-    __syncthreads();
-    if (!is_last)
-        return;
-    __threadfence();
+    if (threadIdx.x == 0)
+        am.partials[blockIdx.x] = pack_vi(bv, bi);
+}
+
+// Step 2: one block combines the candidates (max value, then lowest index;
+// the result does not depend on the order they are visited in).
+__global__ __launch_bounds__(1024) void argmax_reduce_kernel(const unsigned long long *__restrict__ partials,
+                                                             int64_t count, int32_t *__restrict__ result)
+{
+    __shared__ float sv[16];
+    __shared__ int si[16];
     float v = -INFINITY;
     int i = 0x7fffffff;
-    for (unsigned b = threadIdx.x; b < gridDim.x; b += blockDim.x) {
-        const unsigned long long pv =
-            __hip_atomic_load(am.partials + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int64_t b = threadIdx.x; b < count; b += blockDim.x) {
+        const unsigned long long pv = partials[b];
         better(v, i, __builtin_bit_cast(float, (unsigned int)(pv & 0xFFFFFFFFull)),
                (int)(unsigned int)(pv >> 32));
     }
     block_argmax(v, i, sv, si);
-    if (threadIdx.x == 0) {
-        *am.result = i;
-        __hip_atomic_store(am.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0)
+        *result = i;
+}
+
+// Registers of one pass of one tile: 2*CG code units and 2*CG scales.
+template <int CG>
+struct TileRegs {
+    uint4 c[2][CG];
+    uint32_t s[CG];
+};
+
+template <int CG>
+__device__ __forceinline__ void load_tile(TileRegs<CG> &r, const uint8_t *__restrict__ base, int lane)
+{
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < CG; ++j)
+            r.c[u][j] = *reinterpret_cast<const uint4 *>(base + (u * CG + j) * 1024 + lane * 16);
+    const uint32_t *sp = reinterpret_cast<const uint32_t *>(base + 2 * CG * 1024 + lane * 4 * CG);
+#pragma unroll
+    for (int j = 0; j < CG; ++j)
+        r.s[j] = sp[j];
+}
+
+// acc[u] += sum over the lane's CG groups of scale * sum_k x_k (q_k - 8)
+template <int CG>
+__device__ __forceinline__ void compute_tile(const TileRegs<CG> &r, const uint32_t (&xp)[CG][16],
+                                             float (&acc)[2], const DequantConsts &m)
+{
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < CG; ++j) {
+            float p1 = 0.f, p16 = 0.f;
+            dot_word(r.c[u][j].x, &xp[j][0], p1, p16, m);
+            dot_word(r.c[u][j].y, &xp[j][4], p1, p16, m);
+            dot_word(r.c[u][j].z, &xp[j][8], p1, p16, m);
+            dot_word(r.c[u][j].w, &xp[j][12], p1, p16, m);
+            const int e = u * CG + j;
+            const float sv = f16_value((uint16_t)(r.s[e >> 1] >> ((e & 1) * 16)));
+            acc[u] = fmaf(sv, fmaf(p16, 0.0625f, p1), acc[u]);
+        }
+}
+
+// Cross-lane reduction of a finished tile and its epilogue.
+template <int L, int EPI>
+__device__ __forceinline__ void finish_tile(const float (&acc)[2], int64_t t, int s, int c,
+                                            void *__restrict__ out, int64_t rows, int64_t n_out,
+                                            float &bv, int &bi)
+{
+    constexpr int TR = 128 / L;
+    const float y0 = reduce_lanes<L>(acc[0]);
+    const float y1 = reduce_lanes<L>(acc[1]);
+    const int64_t r0 = t * TR + 2 * s;   // even
+    if (c != 0)
+        return;
+    if (EPI == EPI_F16) {
+        uint16_t *y = static_cast<uint16_t *>(out);
+        if (r0 + 1 < rows)
+            *reinterpret_cast<uint32_t *>(y + r0) =
+                (uint32_t)f16_bits(y0) | ((uint32_t)f16_bits(y1) << 16);
+        else if (r0 < rows)
+            y[r0] = f16_bits(y0);
+    } else if (EPI == EPI_F32) {
+        float *y = static_cast<float *>(out);
+        if (r0 + 1 < rows) {
+            *reinterpret_cast<float2 *>(y + r0) = make_float2(y0, y1);
+            better(bv, bi, y0, (int)r0);
+            better(bv, bi, y1, (int)r0 + 1);
+        } else if (r0 < rows) {
+            y[r0] = y0;
+            better(bv, bi, y0, (int)r0);
+        }
+    } else {  // EPI_SILU: logical rows (2i, 2i+1) = (gate i, up i)
+        const int64_t i = r0 >> 1;
+        if (i < n_out) {
+            const float h = y0 / (1.0f + expf(-y0)) * y1;
+            static_cast<uint16_t *>(out)[i] = f16_bits(h);
+        }
     }
 }
 
+// ------------------------------------------------------------ GEMV kernels --
+//
 // rows: logical rows of the layout (gate/up: 2 * n_out); n_out: output length.
+// All three kernels share the tile arithmetic above and differ in how tiles
+// are assigned and how many are kept in flight.
+
+#ifndef Q4_RING_DEPTH_CG4
+#define Q4_RING_DEPTH_CG4 2
+#endif
+#ifndef Q4_RING_DEPTH
+#define Q4_RING_DEPTH 3
+#endif
+// Tiles of registers a ring wavefront keeps loaded ahead (x slice: 16*CG
+// VGPRs; one tile: 9*CG VGPRs).
+template <int CG>
+constexpr int ring_depth() { return CG >= 4 ? Q4_RING_DEPTH_CG4 : Q4_RING_DEPTH; }
+
+#ifndef Q4_RING_STRIDED
+#define Q4_RING_STRIDED 1
+#endif
+
+// Ring kernel (single-pass weights, many tiles): each wavefront loads its x
+// slice once and walks its tiles keeping D tiles of codes and scales loaded
+// ahead in registers: the buffer it has just computed is refilled with the
+// tile D further on.  With Q4_RING_STRIDED the wavefront's j-th tile is
+// wave + j * nwaves (all wavefronts sweep the matrix together, so requests in
+// flight at any moment cover one contiguous stretch of HBM); otherwise it owns
+// a contiguous chunk.
 template <int L, int CG, int EPI>
-__global__ __launch_bounds__(256) void gemv_family_kernel(
+__global__ __launch_bounds__(256) void gemv_ring_kernel(
     const uint8_t *__restrict__ wd, const uint16_t *__restrict__ x, void *__restrict__ out,
-    int64_t rows, int64_t k, int passes, int64_t tiles, int64_t n_out, ArgmaxScratch am)
+    int64_t rows, int64_t k, int64_t tiles, int64_t n_out, ArgmaxScratch am)
 {
-    constexpr int TR = 128 / L;
+    constexpr int D = ring_depth<CG>();
     constexpr int64_t PB = (int64_t)CG * 2304;
     const int lane = threadIdx.x & 63;
     const int s = lane / L, c = lane % L;
-    const int64_t G = k >> 5;
     const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
-    const int64_t wave0 = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-
-    uint32_t xp[CG][16];
-    int have_pass = -1;
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+#if Q4_RING_STRIDED
+    const int64_t first = wave, step = nwaves;
+    const int64_t count = wave < tiles ? (tiles - wave + nwaves - 1) / nwaves : 0;
+#else
+    const int64_t per = (tiles + nwaves - 1) / nwaves;
+    const int64_t first = wave * per, step = 1;
+    const int64_t count = first < tiles ? (first + per < tiles ? per : tiles - first) : 0;
+#endif
     float bv = -INFINITY;
     int bi = 0x7fffffff;
+    const DequantConsts m = dequant_consts();
 
-    for (int64_t t = wave0; t < tiles; t += nwaves) {
-        float acc[2] = {0.f, 0.f};
-        for (int p = 0; p < passes; ++p) {
-            if (p != have_pass) {
+    if (count > 0) {
+        TileRegs<CG> r[D];
 #pragma unroll
-                for (int j = 0; j < CG; ++j)
-                    load_x_group(xp[j], x, (int64_t)p * L * CG + (int64_t)c * CG + j, G);
-                have_pass = p;
+        for (int i = 0; i < D; ++i)
+            if (i < count)
+                load_tile(r[i], wd + (first + i * step) * PB, lane);
+        uint32_t xp[CG][16];
+#pragma unroll
+        for (int j = 0; j < CG; ++j)
+            load_x_group(xp[j], x, (int64_t)c * CG + j, k >> 5);
+        int64_t q = 0;   // index of the tile in r[0]
+        // steady state: every refill is a real tile
+        while (q + 2 * D <= count) {
+#pragma unroll
+            for (int i = 0; i < D; ++i) {
+                float acc[2] = {0.f, 0.f};
+                compute_tile(r[i], xp, acc, m);
+                load_tile(r[i], wd + (first + (q + i + D) * step) * PB, lane);
+                finish_tile<L, EPI>(acc, first + (q + i) * step, s, c, out, rows, n_out, bv, bi);
             }
-            const uint8_t *base = wd + (t * passes + p) * PB;
-            uint4 cu[2][CG];
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int j = 0; j < CG; ++j)
-                    cu[u][j] = *reinterpret_cast<const uint4 *>(base + (u * CG + j) * 1024 + lane * 16);
-            uint32_t sc[CG];
-            const uint32_t *sp = reinterpret_cast<const uint32_t *>(base + 2 * CG * 1024 + lane * 4 * CG);
-#pragma unroll
-            for (int j = 0; j < CG; ++j)
-                sc[j] = sp[j];
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int j = 0; j < CG; ++j) {
-                    float p1 = 0.f, p16 = 0.f;
-                    dot_word(cu[u][j].x, &xp[j][0], p1, p16);
-                    dot_word(cu[u][j].y, &xp[j][4], p1, p16);
-                    dot_word(cu[u][j].z, &xp[j][8], p1, p16);
-                    dot_word(cu[u][j].w, &xp[j][12], p1, p16);
-                    const int e = u * CG + j;
-                    const float sv = f16_value((uint16_t)(sc[e >> 1] >> ((e & 1) * 16)));
-                    acc[u] = fmaf(sv, fmaf(p16, 0.0625f, p1), acc[u]);
-                }
+            q += D;
         }
-        const float y0 = reduce_lanes<L>(acc[0]);
-        const float y1 = reduce_lanes<L>(acc[1]);
-        const int64_t r0 = t * TR + 2 * s;   // even
-        if (c == 0) {
-            if (EPI == EPI_F16) {
-                uint16_t *y = static_cast<uint16_t *>(out);
-                if (r0 + 1 < rows)
-                    *reinterpret_cast<uint32_t *>(y + r0) =
-                        (uint32_t)f16_bits(y0) | ((uint32_t)f16_bits(y1) << 16);
-                else if (r0 < rows)
-                    y[r0] = f16_bits(y0);
-            } else if (EPI == EPI_F32) {
-                float *y = static_cast<float *>(out);
-                if (r0 + 1 < rows) {
-                    *reinterpret_cast<float2 *>(y + r0) = make_float2(y0, y1);
-                    better(bv, bi, y0, (int)r0);
-                    better(bv, bi, y1, (int)r0 + 1);
-                } else if (r0 < rows) {
-                    y[r0] = y0;
-                    better(bv, bi, y0, (int)r0);
-                }
-            } else {  // EPI_SILU: logical rows (2i, 2i+1) = (gate i, up i)
-                const int64_t i = r0 >> 1;
-                if (i < n_out) {
-                    const float h = y0 / (1.0f + expf(-y0)) * y1;
-                    static_cast<uint16_t *>(out)[i] = f16_bits(h);
-                }
+        // drain: fewer than 2D tiles left, the first D of them in r[]
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            if (q + i < count) {
+                float acc[2] = {0.f, 0.f};
+                compute_tile(r[i], xp, acc, m);
+                if (q + i + D < count)
+                    load_tile(r[i], wd + (first + (q + i + D) * step) * PB, lane);
+                finish_tile<L, EPI>(acc, first + (q + i) * step, s, c, out, rows, n_out, bv, bi);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            if (q + D + i < count) {
+                float acc[2] = {0.f, 0.f};
+                compute_tile(r[i], xp, acc, m);
+                finish_tile<L, EPI>(acc, first + (q + D + i) * step, s, c, out, rows, n_out, bv,
+                                    bi);
             }
         }
     }
-    if (EPI == EPI_F32 && am.counter != nullptr)
+    if (EPI == EPI_F32 && am.partials != nullptr)
+        grid_argmax(bv, bi, am);
+}
+
+#ifndef Q4_STREAM_DEPTH
+#define Q4_STREAM_DEPTH 3
+#endif
+
+// Buffer resources: a tile (one pass) is addressed through a V# whose
+// num_records is the tile's byte size, or 0 when the wavefront has no such
+// tile; buffer loads past num_records return zeros without touching memory,
+// so prefetches need no branch and the compiler's vmcnt waits stay exact.
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+constexpr int kBufferWord3 = 0x00020000;   // gfx9-family raw buffer format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, bytes,
+                                             kBufferWord3);
+}
+
+// Load unit i (u = i / CG, j = i % CG) of a tile into its register slot.
+template <int CG>
+__device__ __forceinline__ void load_unit(TileRegs<CG> &r, __amdgpu_buffer_rsrc_t rs, int lane, int i)
+{
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, i * 1024, 0);
+    r.c[i / CG][i % CG] = make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int CG>
+__device__ __forceinline__ void load_scales(TileRegs<CG> &r, __amdgpu_buffer_rsrc_t rs, int lane)
+{
+#pragma unroll
+    for (int j = 0; j < CG; ++j)
+        r.s[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4 * CG + 4 * j, 2 * CG * 1024, 0);
+}
+
+// One tile, unit by unit: compute unit i of `cur`, then issue the load that
+// keeps PD units in flight: unit i + PD of `cur`, or past its end a unit of
+// `nxt`, the wavefront's next tile (a zero-size resource when there is none).
+template <int CG, int PD>
+__device__ __forceinline__ void stream_tile(TileRegs<CG> &cur, TileRegs<CG> &nxt,
+                                            __amdgpu_buffer_rsrc_t cur_rs,
+                                            __amdgpu_buffer_rsrc_t nxt_rs, int lane,
+                                            const uint32_t (&xp)[CG][16], float (&acc)[2],
+                                            const DequantConsts &m)
+{
+    constexpr int NU = 2 * CG;
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+        const int u = i / CG, j = i % CG;
+        float p1 = 0.f, p16 = 0.f;
+        dot_word(cur.c[u][j].x, &xp[j][0], p1, p16, m);
+        dot_word(cur.c[u][j].y, &xp[j][4], p1, p16, m);
+        dot_word(cur.c[u][j].z, &xp[j][8], p1, p16, m);
+        dot_word(cur.c[u][j].w, &xp[j][12], p1, p16, m);
+        const int e = u * CG + j;
+        const float sv = f16_value((uint16_t)(cur.s[e >> 1] >> ((e & 1) * 16)));
+        acc[u] = fmaf(sv, fmaf(p16, 0.0625f, p1), acc[u]);
+        // the unit's arithmetic must be issued before the next load: the
+        // compiler would otherwise hoist every load of the tile to its top
+        // (and sink the arithmetic below them), defeating the pipeline
+        asm volatile("" ::"v"(acc[u]) : "memory");
+        const int pi = i + PD;
+        if (pi < NU) {
+            load_unit(cur, cur_rs, lane, pi);
+        } else {
+            if (pi == NU)
+                load_scales(nxt, nxt_rs, lane);
+            load_unit(nxt, nxt_rs, lane, pi - NU);
+        }
+    }
+}
+
+// Block kernel (single-pass weights): a block of 4 wavefronts takes 4
+// consecutive tiles at a time, one per wavefront, and strides over the
+// matrix by the grid.  The block stages x in LDS once; each wavefront then
+// builds its x pairs from LDS, so x costs one L2 read per block instead of
+// one per wavefront.  Each wavefront streams its tiles unit by unit (one
+// 1 KiB load per 16-byte lane unit) with Q4_STREAM_DEPTH units in flight, so
+// the dequant work of a unit overlaps the loads of the next ones and the
+// memory system sees a steady stream instead of the whole matrix requested
+// at once.
+constexpr int kBlockXHalves = 8192;   // largest single-pass k
+
+__device__ __forceinline__ void lds_x_group(uint32_t *xp, const uint4 *xs, int64_t g, int64_t G)
+{
+    if (g >= G) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            xp[i] = 0u;
+        return;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint4 n = xs[g * 4 + q];
+        xp[4 * q + 0] = (n.x & 0xFFFFu) | (n.z << 16);
+        xp[4 * q + 1] = (n.x >> 16) | (n.z & 0xFFFF0000u);
+        xp[4 * q + 2] = (n.y & 0xFFFFu) | (n.w << 16);
+        xp[4 * q + 3] = (n.y >> 16) | (n.w & 0xFFFF0000u);
+    }
+}
+
+template <int L, int CG, int EPI>
+__global__ __launch_bounds__(256) void gemv_block_kernel(
+    const uint8_t *__restrict__ wd, const uint16_t *__restrict__ x, void *__restrict__ out,
+    int64_t rows, int64_t k, int64_t tiles, int64_t n_out, ArgmaxScratch am)
+{
+    constexpr int PD = Q4_STREAM_DEPTH < 2 * CG ? Q4_STREAM_DEPTH : 2 * CG;
+    constexpr int64_t PB = (int64_t)CG * 2304;
+    __shared__ uint4 xs[kBlockXHalves / 8];
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int s = lane / L, c = lane % L;
+    const int64_t G = k >> 5;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    const DequantConsts m = dequant_consts();
+
+    // x first (L2 hits after the first blocks), then the head of the stream
+    const uint4 *x4 = reinterpret_cast<const uint4 *>(x);
+    for (int64_t i = threadIdx.x; i < k / 8; i += 256)
+        xs[i] = x4[i];
+    int64_t t = (int64_t)blockIdx.x * 4 + w;
+    const int64_t step = (int64_t)gridDim.x * 4;
+    auto rs_of = [&](int64_t tt) {
+        return tt < tiles ? tile_rsrc(wd + tt * PB, (int)PB) : tile_rsrc(wd, 0);
+    };
+    TileRegs<CG> ra, rb;
+    {
+        const __amdgpu_buffer_rsrc_t r0 = rs_of(t);
+        load_scales(ra, r0, lane);
+#pragma unroll
+        for (int i = 0; i < PD; ++i)
+            load_unit(ra, r0, lane, i);
+    }
+    __syncthreads();
+    uint32_t xp[CG][16];
+#pragma unroll
+    for (int j = 0; j < CG; ++j)
+        lds_x_group(xp[j], xs, (int64_t)c * CG + j, G);
+    while (t < tiles) {
+        {
+            const int64_t nt = t + step;
+            float acc[2] = {0.f, 0.f};
+            stream_tile<CG, PD>(ra, rb, rs_of(t), rs_of(nt), lane, xp, acc, m);
+            finish_tile<L, EPI>(acc, t, s, c, out, rows, n_out, bv, bi);
+            t = nt;
+        }
+        if (t >= tiles)
+            break;
+        {
+            const int64_t nt = t + step;
+            float acc[2] = {0.f, 0.f};
+            stream_tile<CG, PD>(rb, ra, rs_of(t), rs_of(nt), lane, xp, acc, m);
+            finish_tile<L, EPI>(acc, t, s, c, out, rows, n_out, bv, bi);
+            t = nt;
+        }
+    }
+    if (EPI == EPI_F32 && am.partials != nullptr)
+        grid_argmax(bv, bi, am);
+}
+
+// Split kernel (single-pass weights, few tiles): CG wavefronts share a tile;
+// wavefront j takes group slot j of every lane (2 code units, x for one
+// group), so there are CG times more wavefronts in flight, each with a
+// quarter to a third of the x traffic.  The CG partial sums of a row are
+// added in LDS in slot order (deterministic), then wavefront 0 finishes.
+template <int L, int CG, int EPI>
+__global__ __launch_bounds__(256) void gemv_split_kernel(
+    const uint8_t *__restrict__ wd, const uint16_t *__restrict__ x, void *__restrict__ out,
+    int64_t rows, int64_t k, int64_t tiles, int64_t n_out, ArgmaxScratch am)
+{
+    constexpr int64_t PB = (int64_t)CG * 2304;
+    __shared__ float part[CG][64][2];
+    const int lane = threadIdx.x & 63;
+    const int j = threadIdx.x >> 6;   // group slot of this wavefront
+    const int s = lane / L, c = lane % L;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    uint32_t xp[16];
+    load_x_group(xp, x, (int64_t)c * CG + j, k >> 5);
+    const DequantConsts m = dequant_consts();
+    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        const uint8_t *base = wd + t * PB;
+        const uint4 c0 = *reinterpret_cast<const uint4 *>(base + j * 1024 + lane * 16);
+        const uint4 c1 = *reinterpret_cast<const uint4 *>(base + (CG + j) * 1024 + lane * 16);
+        const uint16_t *sp = reinterpret_cast<const uint16_t *>(base + 2 * CG * 1024 + lane * 4 * CG);
+        const float s0 = f16_value(sp[j]), s1 = f16_value(sp[CG + j]);
+        float acc[2];
+        {
+            float p1 = 0.f, p16 = 0.f;
+            dot_word(c0.x, &xp[0], p1, p16, m);
+            dot_word(c0.y, &xp[4], p1, p16, m);
+            dot_word(c0.z, &xp[8], p1, p16, m);
+            dot_word(c0.w, &xp[12], p1, p16, m);
+            acc[0] = s0 * fmaf(p16, 0.0625f, p1);
+        }
+        {
+            float p1 = 0.f, p16 = 0.f;
+            dot_word(c1.x, &xp[0], p1, p16, m);
+            dot_word(c1.y, &xp[4], p1, p16, m);
+            dot_word(c1.z, &xp[8], p1, p16, m);
+            dot_word(c1.w, &xp[12], p1, p16, m);
+            acc[1] = s1 * fmaf(p16, 0.0625f, p1);
+        }
+        part[j][lane][0] = acc[0];
+        part[j][lane][1] = acc[1];
+        __syncthreads();
+        if (j == 0) {
+            float tot[2] = {part[0][lane][0], part[0][lane][1]};
+#pragma unroll
+            for (int q = 1; q < CG; ++q) {
+                tot[0] += part[q][lane][0];
+                tot[1] += part[q][lane][1];
+            }
+            finish_tile<L, EPI>(tot, t, s, c, out, rows, n_out, bv, bi);
+        }
+        __syncthreads();
+    }
+    if (EPI == EPI_F32 && am.partials != nullptr)
+        grid_argmax(bv, bi, am);
+}
+
+// Multi-pass kernel (k > 8192): a grid-stride loop over tiles that reloads
+// the x slice for every pass.
+template <int L, int CG, int EPI>
+__global__ __launch_bounds__(256) void gemv_multipass_kernel(
+    const uint8_t *__restrict__ wd, const uint16_t *__restrict__ x, void *__restrict__ out,
+    int64_t rows, int64_t k, int passes, int64_t tiles, int64_t n_out, ArgmaxScratch am)
+{
+    constexpr int64_t PB = (int64_t)CG * 2304;
+    const int lane = threadIdx.x & 63;
+    const int s = lane / L, c = lane % L;
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    const DequantConsts m = dequant_consts();
+    for (int64_t t = wave; t < tiles; t += nwaves) {
+        float acc[2] = {0.f, 0.f};
+        for (int p = 0; p < passes; ++p) {
+            TileRegs<CG> r;
+            load_tile(r, wd + (t * passes + p) * PB, lane);
+            uint32_t xp[CG][16];
+#pragma unroll
+            for (int j = 0; j < CG; ++j)
+                load_x_group(xp[j], x, (int64_t)p * L * CG + (int64_t)c * CG + j, k >> 5);
+            compute_tile(r, xp, acc, m);
+        }
+        finish_tile<L, EPI>(acc, t, s, c, out, rows, n_out, bv, bi);
+    }
+    if (EPI == EPI_F32 && am.partials != nullptr)
         grid_argmax(bv, bi, am);
 }
 
 // ----------------------------------------------------------------- launch --
 
-// One wavefront per tile up to this many wavefronts; beyond it wavefronts
-// loop over tiles with a grid stride.
-constexpr int64_t kMaxWaves = 256 * 32;
+#ifndef Q4_WAVES_PER_CU
+#define Q4_WAVES_PER_CU 4
+#endif
+#ifndef Q4_SPLIT_BELOW_TILES
+#define Q4_SPLIT_BELOW_TILES 2000
+#endif
+#ifndef Q4_USE_RING
+#define Q4_USE_RING 0
+#endif
+#ifndef Q4_BLOCKS_PER_CU
+#define Q4_BLOCKS_PER_CU 8
+#endif
+constexpr int64_t kCUs = 256;   // MI355X compute units; plans depend on shape only
 
-int64_t gemv_blocks(int64_t tiles)
+enum Mode { MODE_RING = 0, MODE_SPLIT = 1, MODE_MULTIPASS = 2, MODE_BLOCK = 3 };
+
+struct GemvPlan {
+    Mode mode;
+    int64_t blocks;
+    int threads;
+};
+
+// The launch plan depends only on the weight's geometry, so a given shape
+// always runs the same kernel and gives the same bits.
+static GemvPlan plan_gemv(const Geometry &geo)
 {
-    const int64_t waves = tiles < kMaxWaves ? tiles : kMaxWaves;
-    return (waves + 3) / 4;
+    if (geo.P > 1) {
+        const int64_t waves = geo.tiles < kCUs * 8 ? geo.tiles : kCUs * 8;
+        return {MODE_MULTIPASS, (waves + 3) / 4, 256};
+    }
+    if (geo.CG > 1 && geo.tiles < Q4_SPLIT_BELOW_TILES)
+        return {MODE_SPLIT, geo.tiles, 64 * geo.CG};
+#if Q4_USE_RING
+    const int64_t cap = kCUs * Q4_WAVES_PER_CU;
+    const int64_t waves = geo.tiles < cap ? geo.tiles : cap;
+    return {MODE_RING, (waves + 3) / 4, 256};
+#else
+    const int64_t groups = (geo.tiles + 3) / 4;
+    const int64_t cap = kCUs * Q4_BLOCKS_PER_CU;
+    return {MODE_BLOCK, groups < cap ? groups : cap, 256};
+#endif
 }
 
-int64_t argmax_workspace_bytes(int64_t tiles)
+int64_t argmax_workspace_bytes(const Geometry &geo)
 {
-    return kArgmaxHeader + 8 * gemv_blocks(tiles);
+    return 8 * plan_gemv(geo).blocks;
 }
 
 hipError_t launch_pack(const uint32_t *w0, const uint16_t *s0, const uint32_t *w1,
@@ -392,37 +781,57 @@ hipError_t launch_unpack(const void *src, int64_t rows, int64_t k, const Geometr
     return hipGetLastError();
 }
 
-template <int L, int CG>
-static void launch_lcg(Epilogue epi, dim3 grid, hipStream_t stream, const uint8_t *wd,
-                       const uint16_t *x, void *out, int64_t rows, int64_t k, int passes,
-                       int64_t tiles, int64_t n_out, ArgmaxScratch am)
+struct GemvArgs {
+    const uint8_t *wd;
+    const uint16_t *x;
+    void *out;
+    int64_t rows, k, n_out;
+    const Geometry *geo;
+    ArgmaxScratch am;
+};
+
+template <int L, int CG, int EPI>
+static void launch_lce(const GemvPlan &plan, const GemvArgs &a, hipStream_t stream)
 {
-    switch (epi) {
-    case EPI_F16:
-        hipLaunchKernelGGL((gemv_family_kernel<L, CG, EPI_F16>), grid, dim3(256), 0, stream, wd, x,
-                           out, rows, k, passes, tiles, n_out, am);
+    const dim3 grid((unsigned)plan.blocks), block((unsigned)plan.threads);
+    switch (plan.mode) {
+    case MODE_RING:
+        hipLaunchKernelGGL((gemv_ring_kernel<L, CG, EPI>), grid, block, 0, stream, a.wd, a.x, a.out,
+                           a.rows, a.k, a.geo->tiles, a.n_out, a.am);
         break;
-    case EPI_F32:
-        hipLaunchKernelGGL((gemv_family_kernel<L, CG, EPI_F32>), grid, dim3(256), 0, stream, wd, x,
-                           out, rows, k, passes, tiles, n_out, am);
+    case MODE_SPLIT:
+        hipLaunchKernelGGL((gemv_split_kernel<L, CG, EPI>), grid, block, 0, stream, a.wd, a.x, a.out,
+                           a.rows, a.k, a.geo->tiles, a.n_out, a.am);
         break;
-    case EPI_SILU:
-        hipLaunchKernelGGL((gemv_family_kernel<L, CG, EPI_SILU>), grid, dim3(256), 0, stream, wd,
-                           x, out, rows, k, passes, tiles, n_out, am);
+    case MODE_MULTIPASS:
+        hipLaunchKernelGGL((gemv_multipass_kernel<L, CG, EPI>), grid, block, 0, stream, a.wd, a.x,
+                           a.out, a.rows, a.k, a.geo->P, a.geo->tiles, a.n_out, a.am);
+        break;
+    case MODE_BLOCK:
+        hipLaunchKernelGGL((gemv_block_kernel<L, CG, EPI>), grid, block, 0, stream, a.wd, a.x, a.out,
+                           a.rows, a.k, a.geo->tiles, a.n_out, a.am);
         break;
     }
 }
 
-template <int L>
-static bool launch_l(int CG, Epilogue epi, dim3 grid, hipStream_t stream, const uint8_t *wd,
-                     const uint16_t *x, void *out, int64_t rows, int64_t k, int passes,
-                     int64_t tiles, int64_t n_out, ArgmaxScratch am)
+template <int L, int CG>
+static void launch_lc(Epilogue epi, const GemvPlan &plan, const GemvArgs &a, hipStream_t stream)
 {
-    switch (CG) {
-    case 1: launch_lcg<L, 1>(epi, grid, stream, wd, x, out, rows, k, passes, tiles, n_out, am); return true;
-    case 2: launch_lcg<L, 2>(epi, grid, stream, wd, x, out, rows, k, passes, tiles, n_out, am); return true;
-    case 3: launch_lcg<L, 3>(epi, grid, stream, wd, x, out, rows, k, passes, tiles, n_out, am); return true;
-    case 4: launch_lcg<L, 4>(epi, grid, stream, wd, x, out, rows, k, passes, tiles, n_out, am); return true;
+    switch (epi) {
+    case EPI_F16: launch_lce<L, CG, EPI_F16>(plan, a, stream); break;
+    case EPI_F32: launch_lce<L, CG, EPI_F32>(plan, a, stream); break;
+    case EPI_SILU: launch_lce<L, CG, EPI_SILU>(plan, a, stream); break;
+    }
+}
+
+template <int L>
+static bool launch_l(Epilogue epi, const GemvPlan &plan, const GemvArgs &a, hipStream_t stream)
+{
+    switch (a.geo->CG) {
+    case 1: launch_lc<L, 1>(epi, plan, a, stream); return true;
+    case 2: launch_lc<L, 2>(epi, plan, a, stream); return true;
+    case 3: launch_lc<L, 3>(epi, plan, a, stream); return true;
+    case 4: launch_lc<L, 4>(epi, plan, a, stream); return true;
     }
     return false;
 }
@@ -431,20 +840,27 @@ hipError_t launch_gemv_family(const Geometry &geo, Epilogue epi, const void *wda
                               const uint16_t *x, void *out, int64_t rows, int64_t k,
                               int64_t n_out, ArgmaxScratch am, hipStream_t stream)
 {
-    const dim3 grid((unsigned)gemv_blocks(geo.tiles));
-    const uint8_t *wd = static_cast<const uint8_t *>(wdata);
+    const GemvPlan plan = plan_gemv(geo);
+    const GemvArgs a{static_cast<const uint8_t *>(wdata), x, out, rows, k, n_out, &geo, am};
     bool ok = false;
     switch (geo.L) {
-    case 64: ok = launch_l<64>(geo.CG, epi, grid, stream, wd, x, out, rows, k, geo.P, geo.tiles, n_out, am); break;
-    case 32: ok = launch_l<32>(geo.CG, epi, grid, stream, wd, x, out, rows, k, geo.P, geo.tiles, n_out, am); break;
-    case 16: ok = launch_l<16>(geo.CG, epi, grid, stream, wd, x, out, rows, k, geo.P, geo.tiles, n_out, am); break;
-    case 8: ok = launch_l<8>(geo.CG, epi, grid, stream, wd, x, out, rows, k, geo.P, geo.tiles, n_out, am); break;
-    case 4: ok = launch_l<4>(geo.CG, epi, grid, stream, wd, x, out, rows, k, geo.P, geo.tiles, n_out, am); break;
-    case 2: ok = launch_l<2>(geo.CG, epi, grid, stream, wd, x, out, rows, k, geo.P, geo.tiles, n_out, am); break;
-    case 1: ok = launch_l<1>(geo.CG, epi, grid, stream, wd, x, out, rows, k, geo.P, geo.tiles, n_out, am); break;
+    case 64: ok = launch_l<64>(epi, plan, a, stream); break;
+    case 32: ok = launch_l<32>(epi, plan, a, stream); break;
+    case 16: ok = launch_l<16>(epi, plan, a, stream); break;
+    case 8: ok = launch_l<8>(epi, plan, a, stream); break;
+    case 4: ok = launch_l<4>(epi, plan, a, stream); break;
+    case 2: ok = launch_l<2>(epi, plan, a, stream); break;
+    case 1: ok = launch_l<1>(epi, plan, a, stream); break;
     }
     if (!ok)
         return hipErrorInvalidValue;
+    if (epi == EPI_F32 && am.partials != nullptr) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(argmax_reduce_kernel, dim3(1), dim3(1024), 0, stream, am.partials,
+                           plan.blocks, am.result);
+    }
     return hipGetLastError();
 }
 

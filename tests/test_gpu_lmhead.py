@@ -27,7 +27,7 @@ def test_lmhead_phi3_parity(q4, orc):
 def test_lmhead_planted_argmax_and_ties(q4, orc, n):
     """A planted winner (codes 15, x = 1) and an exact tie with a later copy of
     the same row: the lowest index wins, across blocks; repeated calls with
-    different n reuse the workspace (its counter returns to zero)."""
+    different n reuse the same workspace."""
     k = 3072
     rng = np.random.default_rng(n)
     codes = rng.integers(0, 16, (n, k), dtype=np.uint8)

@@ -332,22 +332,32 @@ def variants(torch, q4, si, np, K, W):
                                             "bytes": nb}
     del rot
 
-    # skinny GEMM
+    # skinny GEMM (prefill): M = 16, 64, 256 on the default path, and the
+    # VALU-vs-MFMA crossover over small M
     gm = {}
     inp = si.workload(si.GEMM, seed=0, m=256)
     rot = Rotation(q4, q4.pack(dev_u32(inp["words"]), dev_u16(inp["scales"])),
                    copies_for(weight_bytes(16384, 3072)))
-    for m in (16, 64, 256):
+
+    def gemm_us(m, path, steps):
         X = dev_f16(np.ascontiguousarray(inp["X"][:m]))
         Y = torch.empty((m, 16384), dtype=torch.float16, device="cuda")
-        steps = max(20, K // 4)
-        us = per_launch_us(torch, lambda i: q4.gemm(rot[i], X, Y), steps, min(W, 5))
+        return per_launch_us(torch, lambda i: q4.gemm(rot[i], X, Y, path=path), steps, 5)
+
+    for m in (16, 64, 256):
+        us = gemm_us(m, q4.GEMM_AUTO, max(20, K // 4))
         nb = weight_bytes(16384, 3072) + 2 * m * 3072 + 2 * m * 16384
         fl = 2.0 * m * 16384 * 3072
         gm[str(m)] = {"us": round(us, 3), "gbs": round(nb / us / 1e3, 1),
                       "hbm_frac": round(nb / us / 1e3 / PEAK_HBM_GBS, 4),
                       "tflops": round(fl / us / 1e6, 2),
                       "mfma_frac": round(fl / us / 1e6 / PEAK_F16_TFLOPS, 4)}
+    cross = {}
+    for m in (1, 2, 4, 8, 12, 16, 24, 32):
+        cross[str(m)] = {"valu_us": round(gemm_us(m, q4.GEMM_VALU, 20), 3),
+                         "mfma_us": round(gemm_us(m, q4.GEMM_MFMA, 20), 3)}
+    faster = [int(m) for m, v in cross.items() if v["mfma_us"] < v["valu_us"]]
+    gm["crossover"] = {"per_m": cross, "smallest_m_mfma_faster": min(faster) if faster else None}
     out["gemm_16384x3072"] = gm
     return out
 

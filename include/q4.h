@@ -149,14 +149,31 @@ int q4_gemv(const q4_weight *w, const uint16_t *x, uint16_t *y, void *stream);
 
 /*
  * Y = X . dequant(W)^T for m activation rows ([P1] 技术限制与诚实声明: the
- * batched-prefill form).  m < 16 runs a VALU path that reads W once for all
- * rows; m >= 16 dequantizes tiles of W to f16 in LDS and runs MFMA.
+ * batched-prefill form).  m < 16 runs a VALU kernel that reads W once per 8
+ * activation rows with exact dequant; m >= 16 dequantizes W to f16
+ * (q - 8) * s in LDS (one rounding, relative error <= 2^-11) and contracts
+ * with v_mfma_f32_16x16x32_f16, f32 accumulation.
  *   X : device f16 [m][k] row-major, 16-byte aligned
- *   Y : device f16 [m][n] row-major, 4-byte aligned
+ *   Y : device f16 [m][n] row-major, 2-byte aligned
  *   ws: unused (pass NULL, 0)
  */
 int q4_gemm(const q4_weight *w, const uint16_t *X, int32_t m, uint16_t *Y,
             void *ws, int64_t ws_bytes, void *stream);
+
+/* GEMM kernel choice for q4_gemm_path. */
+#define Q4_GEMM_AUTO 0   /* what q4_gemm does: MFMA for m >= 16, VALU below */
+#define Q4_GEMM_VALU 1   /* VALU kernel for any m */
+#define Q4_GEMM_MFMA 2   /* MFMA kernel for any m (falls back to VALU for
+                            layouts it does not take: k > 8192 or k < 256) */
+
+/*
+ * q4_gemm with the kernel chosen by the caller (for measuring where the MFMA
+ * kernel overtakes the VALU one); same arguments and results as q4_gemm up
+ * to the rounding differences of the two kernels.  Errors as q4_gemm, and
+ * Q4_ERR_SHAPE for an unknown path.
+ */
+int q4_gemm_path(const q4_weight *w, const uint16_t *X, int32_t m, uint16_t *Y, int32_t path,
+                 void *stream);
 
 /*
  * h = SiLU(x . Wg^T) * (x . Wu^T) in one kernel ([P1] 内核融合, fused_ffn),

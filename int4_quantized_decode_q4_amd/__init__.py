@@ -35,6 +35,7 @@ OK = 0
 ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_LAYOUT = -1, -2, -3, -4
 ERR_WORKSPACE, ERR_ALIAS, ERR_HIP, ERR_SIZE = -5, -6, -7, -8
 LAYOUT_ROWS, LAYOUT_GATE_UP, LAYOUT_VERSION = 1, 2, 1
+GEMM_AUTO, GEMM_VALU, GEMM_MFMA = 0, 1, 2
 OP_GEMV, OP_GEMM, OP_FFN, OP_LMHEAD = 1, 2, 3, 4
 
 
@@ -56,6 +57,7 @@ _SIGNATURES = {
     "q4_unpack": (ctypes.c_int, [_W, _P, _P, _P]),
     "q4_gemv": (ctypes.c_int, [_W, _P, _P, _P]),
     "q4_gemm": (ctypes.c_int, [_W, _P, _I32, _P, _P, _I64, _P]),
+    "q4_gemm_path": (ctypes.c_int, [_W, _P, _I32, _P, _I32, _P]),
     "q4_ffn_gate_up_silu": (ctypes.c_int, [_W, _P, _P, _P]),
     "q4_lmhead_f32": (ctypes.c_int, [_W, _P, _P, _P, _P, _I64, _P]),
     "q4_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -198,14 +200,20 @@ def gemv(w: PackedWeight, x: torch.Tensor, out: Optional[torch.Tensor] = None) -
     return out
 
 
-def gemm(w: PackedWeight, X: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y f16 [m][n] = X f16 [m][k] . dequant(W)^T (q4_gemm)."""
+def gemm(w: PackedWeight, X: torch.Tensor, out: Optional[torch.Tensor] = None,
+         path: int = GEMM_AUTO) -> torch.Tensor:
+    """Y f16 [m][n] = X f16 [m][k] . dequant(W)^T (q4_gemm; q4_gemm_path when a
+    kernel is forced: GEMM_VALU or GEMM_MFMA)."""
     m = X.shape[0]
     px = _dev(X, "X", 2, (m, w.k))
     if out is None:
         out = torch.empty((m, w.n), dtype=torch.float16, device=X.device)
     py = _dev(out, "out", 2, (m, w.n))
-    _check(_lib.q4_gemm(ctypes.byref(w.desc), px, m, py, None, 0, _stream(X)), "q4_gemm")
+    if path == GEMM_AUTO:
+        _check(_lib.q4_gemm(ctypes.byref(w.desc), px, m, py, None, 0, _stream(X)), "q4_gemm")
+    else:
+        _check(_lib.q4_gemm_path(ctypes.byref(w.desc), px, m, py, path, _stream(X)),
+               "q4_gemm_path")
     return out
 
 

@@ -196,11 +196,9 @@ int q4_gemv(const q4_weight *w, const uint16_t *x, uint16_t *y, void *stream)
                                              static_cast<hipStream_t>(stream)));
 }
 
-int q4_gemm(const q4_weight *w, const uint16_t *X, int32_t m, uint16_t *Y, void *ws,
-            int64_t ws_bytes, void *stream)
+int q4_gemm_path(const q4_weight *w, const uint16_t *X, int32_t m, uint16_t *Y, int32_t path,
+                 void *stream)
 {
-    (void)ws;
-    (void)ws_bytes;
     q4::Geometry geo;
     int64_t rows = 0;
     if (!w || !X || !Y)
@@ -210,14 +208,24 @@ int q4_gemm(const q4_weight *w, const uint16_t *X, int32_t m, uint16_t *Y, void 
         return rc;
     if (m < 1)
         return Q4_ERR_SHAPE;
-    if (!aligned(X, 16) || !aligned(Y, 4))
+    if (path != Q4_GEMM_AUTO && path != Q4_GEMM_VALU && path != Q4_GEMM_MFMA)
+        return Q4_ERR_SHAPE;
+    if (!aligned(X, 16) || !aligned(Y, 2))
         return Q4_ERR_ALIGN;
     const int64_t ybytes = 2 * (int64_t)m * w->n, xbytes = 2 * (int64_t)m * w->k;
     if (overlap(Y, ybytes, X, xbytes) || overlap(Y, ybytes, w->data, w->bytes))
         return Q4_ERR_ALIAS;
     (void)hipGetLastError();
-    return hip_status(q4::launch_gemm(geo, w->data, X, m, w->n, w->k, Y,
+    return hip_status(q4::launch_gemm(geo, w->data, X, m, w->n, w->k, Y, path,
                                       static_cast<hipStream_t>(stream)));
+}
+
+int q4_gemm(const q4_weight *w, const uint16_t *X, int32_t m, uint16_t *Y, void *ws,
+            int64_t ws_bytes, void *stream)
+{
+    (void)ws;
+    (void)ws_bytes;
+    return q4_gemm_path(w, X, m, Y, Q4_GEMM_AUTO, stream);
 }
 
 int q4_ffn_gate_up_silu(const q4_weight *w, const uint16_t *x, uint16_t *h, void *stream)

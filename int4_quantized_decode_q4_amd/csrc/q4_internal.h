@@ -37,7 +37,14 @@ hipError_t launch_gemv_family(const Geometry &geo, Epilogue epi, const void *wda
                               const uint16_t *x, void *out, int64_t rows, int64_t k,
                               int64_t n_out, ArgmaxScratch am, hipStream_t stream);
 
+enum GemmPath { GEMM_PATH_AUTO = 0, GEMM_PATH_VALU = 1, GEMM_PATH_MFMA = 2 };
+
+// Whether the MFMA GEMM kernel takes weights of this geometry (single pass,
+// at least 8 lanes per row); others always run the VALU kernel.
+bool gemm_mfma_eligible(const Geometry &geo);
+
 hipError_t launch_gemm(const Geometry &geo, const void *wdata, const uint16_t *X,
-                       int64_t m, int64_t n, int64_t k, uint16_t *Y, hipStream_t stream);
+                       int64_t m, int64_t n, int64_t k, uint16_t *Y, int path,
+                       hipStream_t stream);
 
 }  // namespace q4

@@ -56,7 +56,69 @@ def parse():
     ap.add_argument("--summarize", metavar="RESULTS_DB",
                     help="print per-kernel duration statistics of a rocprofv3 "
                          "--kernel-trace database (grouped by kernel and grid) and exit")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="print the HBM traffic summary of the gate_up GEMV from two "
+                         "rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of --only layer, "
+                         "calibrated on the 256 MiB copy that run makes, and exit")
     return ap.parse_args()
+
+
+CALIBRATION_BYTES = 256 << 20   # device-to-device copy made in --only layer runs
+
+
+def pmc_medians(db_path: str, counter: str):
+    """{(kernel name, grid): median value per dispatch} of one counter."""
+    import sqlite3
+    import statistics
+    db = sqlite3.connect(db_path)
+    rows = db.execute("select dispatch_id, kernel_name, grid_size, sum(value) from "
+                      "counters_collection where counter_name = ? group by dispatch_id",
+                      (counter,)).fetchall()
+    groups = {}
+    for _, name, grid, v in rows:
+        groups.setdefault((name, grid), []).append(v)
+    return {key: statistics.median(v) for key, v in groups.items()}
+
+
+def pmc_max_dispatch(db_path: str, counter: str):
+    """(kernel name, value) of the single dispatch with the largest value."""
+    import sqlite3
+    db = sqlite3.connect(db_path)
+    rows = db.execute("select kernel_name, sum(value) as v from counters_collection where "
+                      "counter_name = ? group by dispatch_id order by v desc limit 1",
+                      (counter,)).fetchall()
+    return rows[0]
+
+
+def traffic_summary(fetch_db: str, write_db: str) -> int:
+    fetch = pmc_medians(fetch_db, "FETCH_SIZE")
+    write = pmc_medians(write_db, "WRITE_SIZE")
+    # the calibration copy is the single dispatch that moves by far the most bytes
+    cal_f = pmc_max_dispatch(fetch_db, "FETCH_SIZE")
+    cal_w = pmc_max_dispatch(write_db, "WRITE_SIZE")
+    kf = CALIBRATION_BYTES / (cal_f[1] * 1024.0)
+    kw = CALIBRATION_BYTES / (cal_w[1] * 1024.0)
+    gate = [key for key in fetch if "gemv_block_kernel<32, 3, 0>" in key[0]]
+    gate = max(gate, key=lambda key: key[1])          # the 16384-row launch: largest grid
+    f_bytes = fetch[gate] * 1024.0 * kf
+    w_bytes = write.get(gate, 0.0) * 1024.0 * kw
+    print("# HBM traffic of the gate_up GEMV (16384 x 3072) per launch, from rocprofv3 PMC")
+    print(f"# FETCH_SIZE run: {fetch_db}")
+    print(f"# WRITE_SIZE run: {write_db}")
+    print(f"# calibration: {cal_f[0][:40]} copying {CALIBRATION_BYTES} B reads "
+          f"FETCH_SIZE {cal_f[1]:.1f} KiB and WRITE_SIZE {cal_w[1]:.1f} KiB")
+    print(f"kernel: {gate[0][:90]}")
+    print(f"grid: {gate[1]}")
+    print(f"fetch_size_kib_median: {fetch[gate]:.1f}")
+    print(f"write_size_kib_median: {write.get(gate, 0.0):.1f}")
+    print(f"fetch_scale: {kf:.4f}")
+    print(f"write_scale: {kw:.4f}")
+    print(f"hbm_read_bytes_per_launch: {f_bytes:.0f}")
+    print(f"hbm_write_bytes_per_launch: {w_bytes:.0f}")
+    print(f"hbm_bytes_per_launch: {f_bytes + w_bytes:.0f}")
+    print(f"algorithmic_bytes_per_launch: {gemv_bytes(16384, 3072)}")
+    print(f"kernel_sources_sha256_16: {kernels_hash()}")
+    return 0
 
 
 def summarize(db_path: str) -> int:
@@ -194,6 +256,8 @@ def main():
     args = parse()
     if args.summarize:
         return summarize(args.summarize)
+    if args.traffic:
+        return traffic_summary(*args.traffic)
     if args.gpus != 1:
         print("bench.py measures one GPU: the int4 GEMV path has no multi-GPU part in this "
               "library (run with --gpus 1)", file=sys.stderr)
@@ -231,6 +295,12 @@ def main():
             fn(i)
 
     step_bytes = sum(gemv_bytes(n, k) for n, k in si.LAYER_SHAPES.values())
+    if args.only == "layer":
+        # a device copy of known size, for calibrating HBM byte counters
+        src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device="cuda")
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
     ms = timed(torch, step, K, W)
     kus = {key: per_launch_us(torch, fn, K, W) for key, fn in launches.items()}
     gbs = step_bytes / (ms * 1e-3) / 1e9
@@ -266,7 +336,7 @@ def main():
         "per_kernel_gbs": {k: round(gemv_bytes(*si.LAYER_SHAPES[k]) / (kus[k] * 1e-6) / 1e9, 1)
                            for k in kus},
         "roofline": {
-            "kernel": "q4 GEMV gate_up 16384x3072 (gemv_family_kernel<32,3,f16>)",
+            "kernel": "q4 GEMV gate_up 16384x3072 (gemv_block_kernel<32,3,f16>)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,

@@ -5,27 +5,34 @@
 // (zingnex.cn), section 技术限制与诚实声明: batched-prefill shaders exist for
 // prompt processing; the pages give no design for them.
 //
-// Two paths:
-//  * m < 16 (or a layout the MFMA kernel does not take): a VALU kernel in
-//    the shape of the split GEMV -- CG wavefronts share a tile, each lane
-//    holds the x slices of one group for up to 8 activation rows in VGPRs, so
-//    one pass over W serves 8 rows; codes are dequantized once per word and
-//    reused for every row.  Exact dequant as in the GEMV.
-//  * m >= 16: an MFMA kernel.  A block owns 64 weight rows and BM activation
-//    rows; K is walked in steps of 8 groups (256 k) in the order the layout
-//    stores them, so each step reads, per weight row, 8 consecutive 16-byte
-//    units (128 contiguous bytes).  Each unit is dequantized to f16
-//    (q - 8) * s (one rounding, relative error <= 2^-11) into LDS; the X slab
-//    of the same 256 k is staged in LDS; v_mfma_f32_16x16x32_f16 contracts
-//    them with f32 accumulation.  Inside each 8-k word the k order in LDS is
-//    (0,4,1,5,2,6,3,7) for both operands -- the order the nibble masks
-//    produce -- which leaves the contraction unchanged.
+// Kernels:
+//  * VALU, m < 16 (or a layout the MFMA kernels do not take): the streaming
+//    kernel -- CG wavefronts per block walk tiles, wavefront j takes group
+//    slot j of every lane, so each lane keeps that group's x slices for up to
+//    8 activation rows in VGPRs for the whole launch and one pass over W
+//    serves 8 rows; codes are dequantized once per word (exact q - 8) and
+//    reused for every row.  Multi-pass layouts (k > 8192) use a per-tile
+//    variant that re-reads the x slices of each pass.
+//  * MFMA, small m (m <= 16, or m <= 32 with n < 8192): a block owns 16
+//    weight rows and its 4 wavefronts split the K steps, each an independent
+//    pipeline with its own LDS slice (no block barrier until the final
+//    in-order sum of the 4 partial tiles).
+//  * MFMA, larger m: a block owns 64 or 128 weight rows and BM activation
+//    rows; K is walked in steps of 4 groups (128 k) with a register ring of
+//    steps in flight.
+// In both MFMA kernels each 16-byte unit of codes is dequantized to f16
+// (q - 8) * s (one rounding, relative error <= 2^-11) into LDS, the X slab of
+// the same k range is staged in LDS, and v_mfma_f32_16x16x32_f16 contracts
+// them with f32 accumulation.  Inside each 8-k word the k order in LDS is
+// (0,4,1,5,2,6,3,7) for both operands -- the order the nibble masks produce
+// -- which leaves the contraction unchanged.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
 #include "q4_geometry.h"
 #include "q4_internal.h"
+#include "q4_lanes.h"
 
 namespace q4 {
 
@@ -102,28 +109,135 @@ __device__ __forceinline__ uint4 pair_word(uint4 n)
 
 constexpr int kValuRows = 8;   // activation rows per pass over W
 
-template <int L>
-__device__ __forceinline__ float reduce_lanes(float v)
+// Single-pass layouts: the streaming VALU kernel.  A block of CG wavefronts
+// walks tiles blockIdx.x, + gridDim.x, ...; wavefront j takes group slot j
+// of every lane, so a lane meets the same group of 32 k in every tile and
+// keeps that group's x slices for all MC activation rows in VGPRs for the
+// whole launch.  PT tiles of codes and scales are in flight per wavefront.
+// Each code word is dequantized once (exact q - 8) and reused for every
+// row; per tile the lane sums of a row are reduced across its L lanes, and
+// the CG slot sums are added in slot order through LDS (one barrier per
+// tile, double-buffered).
+#ifndef Q4_VALU_TILES_IN_FLIGHT
+#define Q4_VALU_TILES_IN_FLIGHT 2
+#endif
+#ifndef Q4_VALU_BLOCKS_PER_CU
+#define Q4_VALU_BLOCKS_PER_CU 2
+#endif
+
+template <int L, int CG, int MC, int PT>
+__global__ __launch_bounds__(64 * CG) void gemm_valu_stream_kernel(
+    const uint8_t *__restrict__ wd, const uint16_t *__restrict__ X, uint16_t *__restrict__ Y,
+    int64_t m0, int64_t n, int64_t k, int64_t tiles)
 {
-    if (L >= 2)
-        v += __shfl_xor(v, 1);
-    if (L >= 4)
-        v += __shfl_xor(v, 2);
-    if (L >= 8)
-        v += __shfl_xor(v, 4);
-    if (L >= 16)
-        v += __shfl_xor(v, 8);
-    if (L >= 32)
-        v += __shfl_xor(v, 16);
-    if (L >= 64)
-        v += __shfl_xor(v, 32);
-    return v;
+    constexpr int TR = 128 / L;
+    constexpr int HP = 64 / L;   // row pairs per tile
+    constexpr int PB = CG * 2304;
+    __shared__ float part[2][CG][HP][MC][2];
+    const int lane = threadIdx.x & 63;
+    const int j = threadIdx.x >> 6;
+    const int s = lane / L, c = lane % L;
+    const int64_t G = k >> 5;
+    const int64_t g = (int64_t)c * CG + j;
+    const Masks mk = masks();
+
+    uint4 xq[MC][4];
+#pragma unroll
+    for (int r = 0; r < MC; ++r) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(X + (m0 + r) * k + g * 32);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            xq[r][q] = g < G ? pair_word(src[q]) : make_uint4(0, 0, 0, 0);
+    }
+
+    // this lane's two units and two scales inside a tile
+    const int wo0 = j * 1024 + lane * 16, wo1 = (CG + j) * 1024 + lane * 16;
+    const int so0 = 2 * CG * 1024 + lane * 4 * CG + j * 2, so1 = so0 + CG * 2;
+    struct Regs {
+        v4u w0, w1;
+        uint32_t s0, s1;
+    };
+    auto load = [&](Regs &r, int64_t t) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(wd + (t < tiles ? t : 0) * PB), (short)0, t < tiles ? PB : 0,
+            0x00020000);
+        r.w0 = __builtin_amdgcn_raw_buffer_load_b128(rs, wo0, 0, 0);
+        r.w1 = __builtin_amdgcn_raw_buffer_load_b128(rs, wo1, 0, 0);
+        r.s0 = __builtin_amdgcn_raw_buffer_load_b32(rs, so0 & ~3, 0, 0);
+        r.s1 = __builtin_amdgcn_raw_buffer_load_b32(rs, so1 & ~3, 0, 0);
+    };
+
+    const int64_t stride = gridDim.x;
+    Regs ring[PT];
+#pragma unroll
+    for (int q = 0; q < PT; ++q)
+        load(ring[q], (int64_t)blockIdx.x + q * stride);
+    int buf = 0;
+    for (int64_t t = blockIdx.x; t < tiles; t += PT * stride) {
+#pragma unroll
+        for (int q = 0; q < PT; ++q) {
+            const int64_t tt = t + q * stride;
+            if (tt >= tiles)
+                break;
+            float p[MC][2];
+#pragma unroll
+            for (int r = 0; r < MC; ++r)
+                p[r][0] = p[r][1] = 0.f;
+            const uint32_t w0[4] = {ring[q].w0.x, ring[q].w0.y, ring[q].w0.z, ring[q].w0.w};
+            const uint32_t w1[4] = {ring[q].w1.x, ring[q].w1.y, ring[q].w1.z, ring[q].w1.w};
+#pragma unroll
+            for (int wq = 0; wq < 4; ++wq) {
+                h2 a0, a1, a2, a3, b0, b1, b2, b3;
+                dequant_word_unit(w0[wq], mk, a0, a1, a2, a3);
+                dequant_word_unit(w1[wq], mk, b0, b1, b2, b3);
+#pragma unroll
+                for (int r = 0; r < MC; ++r) {
+                    p[r][0] = __builtin_amdgcn_fdot2(a0, as_h2(xq[r][wq].x), p[r][0], false);
+                    p[r][1] = __builtin_amdgcn_fdot2(b0, as_h2(xq[r][wq].x), p[r][1], false);
+                    p[r][0] = __builtin_amdgcn_fdot2(a1, as_h2(xq[r][wq].y), p[r][0], false);
+                    p[r][1] = __builtin_amdgcn_fdot2(b1, as_h2(xq[r][wq].y), p[r][1], false);
+                    p[r][0] = __builtin_amdgcn_fdot2(a2, as_h2(xq[r][wq].z), p[r][0], false);
+                    p[r][1] = __builtin_amdgcn_fdot2(b2, as_h2(xq[r][wq].z), p[r][1], false);
+                    p[r][0] = __builtin_amdgcn_fdot2(a3, as_h2(xq[r][wq].w), p[r][0], false);
+                    p[r][1] = __builtin_amdgcn_fdot2(b3, as_h2(xq[r][wq].w), p[r][1], false);
+                }
+            }
+            const float sc0 = f16_value((uint16_t)(ring[q].s0 >> ((so0 & 2) * 8)));
+            const float sc1 = f16_value((uint16_t)(ring[q].s1 >> ((so1 & 2) * 8)));
+            // the tile's arithmetic is issued before its registers are refilled
+            asm volatile("" ::"v"(p[0][0]), "v"(p[0][1]) : "memory");
+            load(ring[q], tt + PT * stride);   // past the end: a zero-size resource
+#pragma unroll
+            for (int r = 0; r < MC; ++r) {
+                const float v0 = lanes::reduce<L>(sc0 * p[r][0]);
+                const float v1 = lanes::reduce<L>(sc1 * p[r][1]);
+                if (c == 0) {
+                    part[buf][j][s][r][0] = v0;
+                    part[buf][j][s][r][1] = v1;
+                }
+            }
+            __syncthreads();
+            for (int o = threadIdx.x; o < MC * TR; o += 64 * CG) {
+                const int r = o / TR, row = o % TR;
+                float y = part[buf][0][row >> 1][r][row & 1];
+#pragma unroll
+                for (int jj = 1; jj < CG; ++jj)
+                    y += part[buf][jj][row >> 1][r][row & 1];
+                const int64_t nn = tt * TR + row;
+                if (nn < n)
+                    Y[(m0 + r) * n + nn] = f16_bits(y);
+            }
+            buf ^= 1;
+        }
+    }
 }
 
-// Block = CG wavefronts; wavefront j takes group slot j of every lane of a
-// tile.  Rows m0 .. m0 + MC - 1 of X (MC <= kValuRows) per launch.
+// Multi-pass layouts (k > 8192): block = CG wavefronts on one tile at a
+// time; wavefront j takes group slot j of every lane, and the x slices of
+// each pass are read again for every tile.  Rows m0 .. m0 + MC - 1 of X
+// (MC <= kValuRows) per launch.
 template <int L, int CG, int MC>
-__global__ __launch_bounds__(256) void gemm_valu_kernel(const uint8_t *__restrict__ wd,
+__global__ __launch_bounds__(256) void gemm_valu_multipass_kernel(const uint8_t *__restrict__ wd,
                                                         const uint16_t *__restrict__ X,
                                                         uint16_t *__restrict__ Y, int64_t m0,
                                                         int64_t n, int64_t k, int passes,
@@ -199,8 +313,8 @@ __global__ __launch_bounds__(256) void gemm_valu_kernel(const uint8_t *__restric
                     y0 += part[q][lane][2 * r];
                     y1 += part[q][lane][2 * r + 1];
                 }
-                y0 = reduce_lanes<L>(y0);
-                y1 = reduce_lanes<L>(y1);
+                y0 = lanes::reduce<L>(y0);
+                y1 = lanes::reduce<L>(y1);
                 if (c == 0) {
                     uint16_t *yr = Y + (m0 + r) * n;
                     if (r0 < n)
@@ -216,14 +330,20 @@ __global__ __launch_bounds__(256) void gemm_valu_kernel(const uint8_t *__restric
 
 // ------------------------------------------------------------ MFMA path --
 
-constexpr int kBN = 64;          // weight rows per block
-constexpr int kStepK = 256;      // k per step (8 groups)
-constexpr int kLdsRow = kStepK + 8;   // halves per LDS row (padding against bank conflicts)
+#ifndef Q4_GEMM_DEPTH_LARGE
+#define Q4_GEMM_DEPTH_LARGE 2
+#endif
+constexpr int kGroupsPerStep = 4;                 // K step: 4 groups = 128 k
+constexpr int kStepK = 32 * kGroupsPerStep;
+constexpr int kLdsRow = kStepK + 8;               // halves per LDS row (+16 B against bank conflicts)
 
-// One block: weight rows n0 .. n0+63 x activation rows mb*BM .. +BM-1.
-// 4 wavefronts; wavefront w computes the 16 x BM output slab of rows
-// n0 + 16w .. n0 + 16w + 15.
-template <int L, int CG, int BM>
+// Block tile BN x BM = (16 NT WN) x (16 MT WM): 4 wavefronts in a WN x WM
+// grid, each owning NT x MT MFMA tiles of 16 x 16.  K steps of 4 groups in
+// layout order (for a row: 4 consecutive 16-byte units, 64 contiguous
+// bytes).  The next step's units, scales and X chunks are loaded into
+// registers while the current step's MFMAs run; dequant and the LDS stores
+// happen between two barriers.
+template <int L, int CG, int NT, int MT, int WN, int WM>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint8_t *__restrict__ wd,
                                                         int64_t wbytes,
                                                         const uint16_t *__restrict__ X,
@@ -231,114 +351,326 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint8_t *__restric
                                                         int64_t n, int64_t k, int64_t nblocks_n,
                                                         int64_t padded_nblocks_n)
 {
+    static_assert(WN * WM == 4, "four wavefronts");
+    constexpr int BN = 16 * NT * WN, BM = 16 * MT * WM;
     constexpr int TR = 128 / L;
     constexpr int PB = CG * 2304;
-    constexpr int MT = BM / 16;
-    __shared__ _Float16 Ws[kBN][kLdsRow];
+    constexpr int WU = BN * kGroupsPerStep / 256;     // weight units per thread per step
+    constexpr int XC = BM * kGroupsPerStep * 4 / 256; // 16-byte X chunks per thread per step
+    static_assert(WU >= 1 && XC >= 1, "tile too small for 256 threads");
+    constexpr int CBLOCKS = L / kGroupsPerStep;
+    constexpr int STEPS = CG * CBLOCKS;
+    constexpr int D = BM <= 32 ? 4 : (BM <= 64 ? 2 : Q4_GEMM_DEPTH_LARGE);   // steps in flight
+    __shared__ _Float16 Ws[BN][kLdsRow];
     __shared__ _Float16 Xs[BM][kLdsRow];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
+    const int wn = wv % WN, wm = wv / WN;
     const int64_t G = k >> 5;
 
-    // XCD-aware order: consecutive block ids go to different XCDs, so the
-    // M-blocks of one weight slab are spread by a stride of 8 block ids and
-    // land on the same XCD (sharing that XCD's L2 for the slab).
+    // XCD-aware order: block ids b, b + 8, b + 16, ... go to the same XCD,
+    // so the M-blocks of one weight slab are spread by a stride of 8 and
+    // share that XCD's L2 for the slab.
     const int64_t mblocks = gridDim.x / padded_nblocks_n;
     const int64_t b = blockIdx.x;
-    const int64_t group = b / (8 * mblocks), within = b % (8 * mblocks);
-    const int64_t nb = group * 8 + within % 8;
+    const int64_t grp = b / (8 * mblocks), within = b % (8 * mblocks);
+    const int64_t nb = grp * 8 + within % 8;
     const int64_t mb = within / 8;
     if (nb >= nblocks_n)
         return;
-    const int64_t n0 = nb * kBN, mrow0 = mb * BM;
+    const int64_t n0 = nb * BN, mrow0 = mb * BM;
     const int64_t t0 = n0 / TR;
 
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(wd), (short)0, (int)wbytes, 0x00020000);
     const Masks mk = masks();
 
-    f4 acc[MT];
+    // per-thread fixed parts of the weight unit addresses
+    int64_t ubase[WU];   // tile byte offset + lane' * 16 without the (u, j) unit term
+    int64_t sbase[WU];   // tile byte offset of the lane's scale block
+    int urow[WU], ucl[WU], uu[WU];
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
-        acc[i] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < WU; ++h) {
+        const int q = tid + 256 * h;
+        const int rr = q / kGroupsPerStep, cl = q % kGroupsPerStep;
+        const int64_t tile = t0 + rr / TR;
+        const int sl = (rr % TR) >> 1;
+        urow[h] = rr;
+        ucl[h] = cl;
+        uu[h] = rr & 1;
+        ubase[h] = tile * PB + (int64_t)(sl * L + cl) * 16;
+        sbase[h] = tile * PB + 2 * CG * 1024 + (int64_t)(sl * L + cl) * 4 * CG;
+    }
 
-    for (int j = 0; j < CG; ++j) {
-        for (int cb = 0; cb < L / 8; ++cb) {
-            // W: 64 rows x 8 units; thread takes units q = tid and tid + 256
+    // X through a buffer resource too: chunks outside X (rows past m, groups
+    // past k, steps past the end) read as zero without touching memory
+    const int xbytes = (int)(m * k * 2);
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(X), (short)0, xbytes, 0x00020000);
+
+    // D steps of operands kept in flight in registers
+    struct StepRegs {
+        v4u w[WU];
+        uint32_t s[WU];
+        v4u x[XC];
+    };
+    StepRegs ring[D];
+    auto load_step = [&](StepRegs &r, int st) {
+        const bool live = st < STEPS;
+        const int j = st / CBLOCKS, cb = st % CBLOCKS;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int q = tid + 256 * h;
-                const int rr = q >> 3, cc = q & 7;
-                const int64_t tile = t0 + rr / TR;
-                const int sl = (rr % TR) >> 1, u = rr & 1;
-                const int lanep = sl * L + cb * 8 + cc;
-                const int64_t tb = tile * PB;
-                // a tile past the end of the weight reads as zero (buffer bounds)
-                const int64_t off = tb + (u * CG + j) * 1024 + lanep * 16;
-                const int64_t soff = tb + 2 * CG * 1024 + lanep * 4 * CG + (u * CG + j) * 2;
-                const bool inb = tb < wbytes;
-                v4u cw = {0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-                uint32_t sw = 0;
-                if (inb) {
-                    cw = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
-                    sw = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(soff & ~3ll), 0, 0);
-                }
-                const uint16_t sb = (uint16_t)(sw >> ((soff & 2) * 8));
-                const h2 sc = {__builtin_bit_cast(_Float16, sb), __builtin_bit_cast(_Float16, sb)};
-                uint32_t outw[16];
-                const uint32_t ws4[4] = {cw.x, cw.y, cw.z, cw.w};
+        for (int h = 0; h < WU; ++h) {
+            const int64_t off = ubase[h] + (int64_t)(uu[h] * CG + j) * 1024 + cb * kGroupsPerStep * 16;
+            const int64_t soff = sbase[h] + (int64_t)cb * kGroupsPerStep * 4 * CG + (uu[h] * CG + j) * 2;
+            // rows past the end of the weight read as zero through the buffer bounds
+            const int wo = (int)(live && off < wbytes ? off : wbytes);
+            const int so = (int)(live && (soff & ~3ll) < wbytes ? (soff & ~3ll) : wbytes);
+            r.w[h] = __builtin_amdgcn_raw_buffer_load_b128(rs, wo, 0, 0);
+            r.s[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, so, 0, 0) >> ((soff & 2) * 8);
+        }
 #pragma unroll
-                for (int wq = 0; wq < 4; ++wq) {
-                    h2 a0, a1, a2, a3;
-                    dequant_word_unit(ws4[wq], mk, a0, a1, a2, a3);
-                    // one f16 rounding of (q - 8) * s
-                    outw[4 * wq + 0] = as_u32(a0 * sc);
-                    outw[4 * wq + 1] = as_u32(a1 * sc);
-                    outw[4 * wq + 2] = as_u32(a2 * sc);
-                    outw[4 * wq + 3] = as_u32(a3 * sc);
-                }
-                uint4 *dst = reinterpret_cast<uint4 *>(&Ws[rr][cc * 32]);
+        for (int h = 0; h < XC; ++h) {
+            const int q = tid + 256 * h;
+            const int mr = q / (kGroupsPerStep * 4), rest = q % (kGroupsPerStep * 4);
+            const int cl = rest >> 2, wq = rest & 3;
+            const int64_t g = (int64_t)(cb * kGroupsPerStep + cl) * CG + j;
+            const int64_t mm = mrow0 + mr;
+            const int xo = (live && mm < m && g < G) ? (int)((mm * k + g * 32 + wq * 8) * 2) : xbytes;
+            r.x[h] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo, 0, 0);
+        }
+    };
+    auto store_step = [&](const StepRegs &r) {
 #pragma unroll
-                for (int z = 0; z < 4; ++z)
-                    dst[z] = make_uint4(outw[4 * z], outw[4 * z + 1], outw[4 * z + 2], outw[4 * z + 3]);
+        for (int h = 0; h < WU; ++h) {
+            const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(r.s[h] & 0xFFFFu));
+            const h2 sc = {sv, sv};
+            const uint32_t ws4[4] = {r.w[h].x, r.w[h].y, r.w[h].z, r.w[h].w};
+            uint4 *dst = reinterpret_cast<uint4 *>(&Ws[urow[h]][ucl[h] * 32]);
+#pragma unroll
+            for (int wq = 0; wq < 4; ++wq) {
+                h2 a0, a1, a2, a3;
+                dequant_word_unit(ws4[wq], mk, a0, a1, a2, a3);
+                // one f16 rounding of (q - 8) * s
+                dst[wq] = make_uint4(as_u32(a0 * sc), as_u32(a1 * sc), as_u32(a2 * sc), as_u32(a3 * sc));
             }
-            // X: BM rows x 8 groups x 4 words of 8 halves
-            for (int q = tid; q < BM * 32; q += 256) {
-                const int mr = q >> 5, rest = q & 31, cc = rest >> 2, wq = rest & 3;
-                const int64_t g = (int64_t)(cb * 8 + cc) * CG + j;
-                const int64_t mm = mrow0 + mr;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (mm < m && g < G)
-                    v = pair_word(*reinterpret_cast<const uint4 *>(X + mm * k + g * 32 + wq * 8));
-                *reinterpret_cast<uint4 *>(&Xs[mr][cc * 32 + wq * 8]) = v;
-            }
-            __syncthreads();
+        }
 #pragma unroll
-            for (int ss = 0; ss < kStepK / 32; ++ss) {
-                const int kk = ss * 32 + 8 * (lane >> 4);
-                const h8 a = *reinterpret_cast<const h8 *>(&Ws[16 * wv + (lane & 15)][kk]);
+        for (int h = 0; h < XC; ++h) {
+            const int q = tid + 256 * h;
+            const int mr = q / (kGroupsPerStep * 4), rest = q % (kGroupsPerStep * 4);
+            const int cl = rest >> 2, wq = rest & 3;
+            *reinterpret_cast<uint4 *>(&Xs[mr][cl * 32 + wq * 8]) =
+                pair_word(make_uint4(r.x[h].x, r.x[h].y, r.x[h].z, r.x[h].w));
+        }
+    };
+    auto mfma_step = [&](f4 (&acc)[NT][MT]) {
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const h8 bx = *reinterpret_cast<const h8 *>(&Xs[16 * mt + (lane & 15)][kk]);
-                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bx, acc[mt], 0, 0, 0);
-                }
+        for (int ss = 0; ss < kGroupsPerStep; ++ss) {
+            const int kk = ss * 32 + 8 * (lane >> 4);
+            h8 af[NT], bf[MT];
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+                af[i] = *reinterpret_cast<const h8 *>(&Ws[(wn * NT + i) * 16 + (lane & 15)][kk]);
+#pragma unroll
+            for (int jj = 0; jj < MT; ++jj)
+                bf[jj] = *reinterpret_cast<const h8 *>(&Xs[(wm * MT + jj) * 16 + (lane & 15)][kk]);
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+#pragma unroll
+                for (int jj = 0; jj < MT; ++jj)
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[jj], acc[i][jj], 0, 0, 0);
+        }
+    };
+
+    f4 acc[NT][MT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int jj = 0; jj < MT; ++jj)
+            acc[i][jj] = f4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        load_step(ring[i], i);
+    for (int st = 0; st < STEPS; st += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            if (st + i < STEPS) {
+                __syncthreads();          // the previous step's fragments have been read
+                store_step(ring[i]);
+                __syncthreads();
+                load_step(ring[i], st + i + D);   // D steps ahead; past the end reads nothing
+                mfma_step(acc);
             }
-            __syncthreads();
         }
     }
     // D[i][j]: lane holds rows i = 4 (lane / 16) + r (weight rows), column
     // j = lane % 16 (activation row)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int64_t mm = mrow0 + 16 * mt + (lane & 15);
+    for (int jj = 0; jj < MT; ++jj) {
+        const int64_t mm = mrow0 + (wm * MT + jj) * 16 + (lane & 15);
         if (mm >= m)
             continue;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t nn = n0 + 16 * wv + 4 * (lane >> 4) + r;
-            if (nn < n)
-                Y[mm * n + nn] = f16_bits(acc[mt][r]);
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t nn = n0 + (wn * NT + i) * 16 + 4 * (lane >> 4) + r;
+                if (nn < n)
+                    Y[mm * n + nn] = f16_bits(acc[i][jj][r]);
+            }
+    }
+}
+
+// Small-m MFMA kernel (m <= 32): a block owns 16 weight rows x BM = 16 MT
+// activation rows, and its 4 wavefronts split the K steps (wavefront w takes
+// steps w, w + 4, ...).  Each wavefront is an independent pipeline -- up to
+// six steps of operands in flight in registers, a private LDS slice, no
+// block barrier -- and the four partial sums are added in wavefront order at the
+// end (deterministic).  Many small blocks keep enough weight bytes in flight
+// for the HBM-bound regime.
+template <int L, int CG, int MT>
+__global__ __launch_bounds__(256) void gemm_mfma_small_kernel(const uint8_t *__restrict__ wd,
+                                                              int64_t wbytes,
+                                                              const uint16_t *__restrict__ X,
+                                                              uint16_t *__restrict__ Y, int64_t m,
+                                                              int64_t n, int64_t k)
+{
+    constexpr int BM = 16 * MT;
+    constexpr int TR = 128 / L;
+    constexpr int PB = CG * 2304;
+    constexpr int XC = BM * kGroupsPerStep * 4 / 64;   // X chunks per lane per step
+    constexpr int CBLOCKS = L / kGroupsPerStep;
+    constexpr int STEPS = CG * CBLOCKS;
+    // a wavefront with at most 6 steps keeps all of them in flight; longer
+    // K streams 3 steps deep (measured best for k = 3072 and 8192)
+    constexpr int WSTEPS = (STEPS + 3) / 4;
+    constexpr int D = WSTEPS <= 6 ? (WSTEPS > 0 ? WSTEPS : 1) : 3;
+    static_assert(TR <= 16, "16-row blocks need at least 8 lanes per row");
+    __shared__ _Float16 Ws[4][16][kLdsRow];
+    __shared__ _Float16 Xs[4][BM][kLdsRow];
+    __shared__ float red[4][MT][4][64];
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int64_t G = k >> 5;
+    const int64_t mblocks = (m + BM - 1) / BM;
+    const int64_t nb = blockIdx.x / mblocks, mb = blockIdx.x % mblocks;
+    const int64_t n0 = nb * 16, mrow0 = mb * BM;
+
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(wd), (short)0, (int)wbytes, 0x00020000);
+    const int xbytes = (int)(m * k * 2);
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(X), (short)0, xbytes, 0x00020000);
+    const Masks mk = masks();
+
+    // this lane's weight unit in every step: row lane / 4, group slot lane % 4
+    const int rr = lane >> 2, cl = lane & 3;
+    const int64_t row = n0 + rr;
+    const int64_t tile = row / TR;
+    const int sl = (int)((row % TR) >> 1), uu = (int)(row & 1);
+    const int64_t ubase = tile * PB + (int64_t)(sl * L + cl) * 16;
+    const int64_t sbase = tile * PB + 2 * CG * 1024 + (int64_t)(sl * L + cl) * 4 * CG;
+
+    struct StepRegs {
+        v4u w;
+        uint32_t s;
+        v4u x[XC];
+    };
+    auto load_step = [&](StepRegs &r, int st) {
+        const bool live = st < STEPS;
+        const int j = st / CBLOCKS, cb = st % CBLOCKS;
+        const int64_t off = ubase + (int64_t)(uu * CG + j) * 1024 + cb * kGroupsPerStep * 16;
+        const int64_t soff = sbase + (int64_t)cb * kGroupsPerStep * 4 * CG + (uu * CG + j) * 2;
+        const int wo = (int)(live && off < wbytes ? off : wbytes);
+        const int so = (int)(live && (soff & ~3ll) < wbytes ? (soff & ~3ll) : wbytes);
+        r.w = __builtin_amdgcn_raw_buffer_load_b128(rs, wo, 0, 0);
+        r.s = __builtin_amdgcn_raw_buffer_load_b32(rs, so, 0, 0) >> ((soff & 2) * 8);
+#pragma unroll
+        for (int h = 0; h < XC; ++h) {
+            const int q = lane + 64 * h;
+            const int mr = q / (kGroupsPerStep * 4), rest = q % (kGroupsPerStep * 4);
+            const int xcl = rest >> 2, wq = rest & 3;
+            const int64_t g = (int64_t)(cb * kGroupsPerStep + xcl) * CG + j;
+            const int64_t mm = mrow0 + mr;
+            const int xo = (live && mm < m && g < G) ? (int)((mm * k + g * 32 + wq * 8) * 2) : xbytes;
+            r.x[h] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo, 0, 0);
+        }
+    };
+    auto run_step = [&](const StepRegs &r, f4 (&acc)[MT]) {
+        {
+            const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(r.s & 0xFFFFu));
+            const h2 sc = {sv, sv};
+            const uint32_t ws4[4] = {r.w.x, r.w.y, r.w.z, r.w.w};
+            uint4 *dst = reinterpret_cast<uint4 *>(&Ws[wv][rr][cl * 32]);
+#pragma unroll
+            for (int wq = 0; wq < 4; ++wq) {
+                h2 a0, a1, a2, a3;
+                dequant_word_unit(ws4[wq], mk, a0, a1, a2, a3);
+                dst[wq] = make_uint4(as_u32(a0 * sc), as_u32(a1 * sc), as_u32(a2 * sc), as_u32(a3 * sc));
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < XC; ++h) {
+            const int q = lane + 64 * h;
+            const int mr = q / (kGroupsPerStep * 4), rest = q % (kGroupsPerStep * 4);
+            const int xcl = rest >> 2, wq = rest & 3;
+            *reinterpret_cast<uint4 *>(&Xs[wv][mr][xcl * 32 + wq * 8]) =
+                pair_word(make_uint4(r.x[h].x, r.x[h].y, r.x[h].z, r.x[h].w));
+        }
+        // the wavefront's own LDS slice: its writes must land before its reads
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int ss = 0; ss < kGroupsPerStep; ++ss) {
+            const int kk = ss * 32 + 8 * (lane >> 4);
+            const h8 a = *reinterpret_cast<const h8 *>(&Ws[wv][lane & 15][kk]);
+#pragma unroll
+            for (int jj = 0; jj < MT; ++jj) {
+                const h8 bx = *reinterpret_cast<const h8 *>(&Xs[wv][jj * 16 + (lane & 15)][kk]);
+                acc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bx, acc[jj], 0, 0, 0);
+            }
+        }
+        // fragments read before the next step overwrites the slice
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    };
+
+    f4 acc[MT];
+#pragma unroll
+    for (int jj = 0; jj < MT; ++jj)
+        acc[jj] = f4{0.f, 0.f, 0.f, 0.f};
+    StepRegs ring[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        load_step(ring[i], wv + 4 * i);
+    for (int st = wv; st < STEPS; st += 4 * D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            const int cur = st + 4 * i;
+            if (cur < STEPS) {
+                run_step(ring[i], acc);
+                load_step(ring[i], cur + 4 * D);   // past the end reads nothing
+            }
+        }
+    }
+#pragma unroll
+    for (int jj = 0; jj < MT; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            red[wv][jj][r][lane] = acc[jj][r];
+    __syncthreads();
+    if (wv == 0) {
+#pragma unroll
+        for (int jj = 0; jj < MT; ++jj) {
+            const int64_t mm = mrow0 + jj * 16 + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float v = ((red[0][jj][r][lane] + red[1][jj][r][lane]) + red[2][jj][r][lane]) +
+                                red[3][jj][r][lane];
+                const int64_t nn = n0 + 4 * (lane >> 4) + r;
+                if (mm < m && nn < n)
+                    Y[mm * n + nn] = f16_bits(v);
+            }
         }
     }
 }
@@ -347,15 +679,21 @@ template <int L, int CG>
 hipError_t launch_valu_lc(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
                           int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
 {
-    const int64_t cap = 256 * 8;
+    constexpr int PT = Q4_VALU_TILES_IN_FLIGHT;
+    const bool single = geo.P == 1;
+    const int64_t cap = single ? 256 * Q4_VALU_BLOCKS_PER_CU : 256 * 8;
     const dim3 grid((unsigned)(geo.tiles < cap ? geo.tiles : cap)), block(64 * CG);
     for (int64_t m0 = 0; m0 < m; m0 += kValuRows) {
         const int64_t mc = m - m0 < kValuRows ? m - m0 : kValuRows;
         switch (mc) {
-#define Q4_VALU_CASE(R)                                                                           \
-    case R:                                                                                       \
-        hipLaunchKernelGGL((gemm_valu_kernel<L, CG, R>), grid, block, 0, stream, wd, X, Y, m0, n, \
-                           k, geo.P, geo.tiles);                                                  \
+#define Q4_VALU_CASE(R)                                                                            \
+    case R:                                                                                        \
+        if (single)                                                                                \
+            hipLaunchKernelGGL((gemm_valu_stream_kernel<L, CG, R, PT>), grid, block, 0, stream, wd, \
+                               X, Y, m0, n, k, geo.tiles);                                         \
+        else                                                                                       \
+            hipLaunchKernelGGL((gemm_valu_multipass_kernel<L, CG, R>), grid, block, 0, stream, wd, \
+                               X, Y, m0, n, k, geo.P, geo.tiles);                                  \
         break;
             Q4_VALU_CASE(1)
             Q4_VALU_CASE(2)
@@ -374,27 +712,48 @@ hipError_t launch_valu_lc(const Geometry &geo, const uint8_t *wd, const uint16_t
     return hipSuccess;
 }
 
+template <int L, int CG, int NT, int MT, int WN, int WM>
+hipError_t launch_mfma_cfg(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
+                           int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
+{
+    constexpr int BN = 16 * NT * WN, BM = 16 * MT * WM;
+    const int64_t nbn = (n + BN - 1) / BN;
+    const int64_t padded = (nbn + 7) / 8 * 8;   // whole groups of 8 for the XCD order
+    const int64_t wbytes = geo.tiles * geo.tile_bytes;
+    const dim3 grid((unsigned)(padded * ((m + BM - 1) / BM)));
+    hipLaunchKernelGGL((gemm_mfma_kernel<L, CG, NT, MT, WN, WM>), grid, dim3(256), 0, stream, wd,
+                       wbytes, X, Y, m, n, k, nbn, padded);
+    return hipGetLastError();
+}
+
+template <int L, int CG, int MT>
+hipError_t launch_mfma_small(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
+                             int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
+{
+    const int64_t wbytes = geo.tiles * geo.tile_bytes;
+    const dim3 grid((unsigned)(((n + 15) / 16) * ((m + 16 * MT - 1) / (16 * MT))));
+    hipLaunchKernelGGL((gemm_mfma_small_kernel<L, CG, MT>), grid, dim3(256), 0, stream, wd, wbytes,
+                       X, Y, m, n, k);
+    return hipGetLastError();
+}
+
 template <int L, int CG>
 hipError_t launch_mfma_lc(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
                           int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
 {
-    const int64_t nbn = (n + kBN - 1) / kBN;
-    const int64_t padded_nbn = (nbn + 7) / 8 * 8;   // whole groups of 8 for the XCD order
-    const int64_t wbytes = geo.tiles * geo.tile_bytes;
-    if (m <= 16) {
-        const dim3 grid((unsigned)(padded_nbn * ((m + 15) / 16)));
-        hipLaunchKernelGGL((gemm_mfma_kernel<L, CG, 16>), grid, dim3(256), 0, stream, wd, wbytes, X,
-                           Y, m, n, k, nbn, padded_nbn);
-    } else if (m <= 32) {
-        const dim3 grid((unsigned)(padded_nbn * ((m + 31) / 32)));
-        hipLaunchKernelGGL((gemm_mfma_kernel<L, CG, 32>), grid, dim3(256), 0, stream, wd, wbytes, X,
-                           Y, m, n, k, nbn, padded_nbn);
-    } else {
-        const dim3 grid((unsigned)(padded_nbn * ((m + 63) / 64)));
-        hipLaunchKernelGGL((gemm_mfma_kernel<L, CG, 64>), grid, dim3(256), 0, stream, wd, wbytes, X,
-                           Y, m, n, k, nbn, padded_nbn);
-    }
-    return hipGetLastError();
+    // m <= 16: the small kernel always; m <= 32: only while the 64-row tile
+    // kernel would have too few blocks (n < 8192) to stream the weights
+    if (L >= 8 && m <= 16)
+        return launch_mfma_small<L >= 8 ? L : 8, CG, 1>(geo, wd, X, m, n, k, Y, stream);
+    if (L >= 8 && m <= 32 && n < 8192)
+        return launch_mfma_small<L >= 8 ? L : 8, CG, 2>(geo, wd, X, m, n, k, Y, stream);
+    if (m <= 16)
+        return launch_mfma_cfg<L, CG, 1, 1, 4, 1>(geo, wd, X, m, n, k, Y, stream);  // 64 x 16
+    if (m <= 32)
+        return launch_mfma_cfg<L, CG, 2, 1, 2, 2>(geo, wd, X, m, n, k, Y, stream);  // 64 x 32
+    if (m <= 64)
+        return launch_mfma_cfg<L, CG, 2, 2, 2, 2>(geo, wd, X, m, n, k, Y, stream);  // 64 x 64
+    return launch_mfma_cfg<L, CG, 4, 4, 2, 2>(geo, wd, X, m, n, k, Y, stream);      // 128 x 128
 }
 
 template <int L>
@@ -418,7 +777,7 @@ hipError_t launch_l(bool mfma, const Geometry &geo, const uint8_t *wd, const uin
 
 }  // namespace
 
-bool gemm_mfma_eligible(const Geometry &geo) { return geo.P == 1 && geo.L >= 8; }
+bool gemm_mfma_eligible(const Geometry &geo) { return geo.P == 1 && geo.L >= 4; }
 
 hipError_t launch_gemm(const Geometry &geo, const void *wdata, const uint16_t *X, int64_t m,
                        int64_t n, int64_t k, uint16_t *Y, int path, hipStream_t stream)
@@ -427,15 +786,15 @@ hipError_t launch_gemm(const Geometry &geo, const void *wdata, const uint16_t *X
     bool mfma = (path == GEMM_PATH_MFMA) || (path == GEMM_PATH_AUTO && m >= 16);
     if (mfma && !gemm_mfma_eligible(geo))
         mfma = false;
-    // the MFMA kernel addresses the weight through 32-bit buffer offsets
-    if (mfma && geo.tiles * geo.tile_bytes >= ((int64_t)1 << 31))
+    // the MFMA kernel addresses the weight and X through 32-bit buffer offsets
+    if (mfma && (geo.tiles * geo.tile_bytes >= ((int64_t)1 << 31) || m * k * 2 >= ((int64_t)1 << 31)))
         mfma = false;
     switch (geo.L) {
     case 64: return launch_l<64>(mfma, geo, wd, X, m, n, k, Y, stream);
     case 32: return launch_l<32>(mfma, geo, wd, X, m, n, k, Y, stream);
     case 16: return launch_l<16>(mfma, geo, wd, X, m, n, k, Y, stream);
     case 8: return launch_l<8>(mfma, geo, wd, X, m, n, k, Y, stream);
-    case 4: return launch_l<4>(false, geo, wd, X, m, n, k, Y, stream);
+    case 4: return launch_l<4>(mfma, geo, wd, X, m, n, k, Y, stream);
     case 2: return launch_l<2>(false, geo, wd, X, m, n, k, Y, stream);
     case 1: return launch_l<1>(false, geo, wd, X, m, n, k, Y, stream);
     }

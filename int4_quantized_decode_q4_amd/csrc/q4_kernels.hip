@@ -31,6 +31,7 @@
 
 #include "q4_geometry.h"
 #include "q4_internal.h"
+#include "q4_lanes.h"
 
 namespace q4 {
 
@@ -174,38 +175,10 @@ __device__ __forceinline__ void dot_word(uint32_t w, const uint32_t *xp, float &
     p16 = __builtin_amdgcn_fdot2(as_h2(a3) - k16, as_h2(xp[3]), p16, false);
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
-                                                              0xF, 0xF, false));
-}
-
-template <int XOR>
-__device__ __forceinline__ float swizzle_xor(float v)
-{
-    // ds_swizzle bit-mask mode inside 32-lane halves: and 0x1F, or 0, xor XOR
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
-                                                                 (XOR << 10) | 0x1F));
-}
-
-// Sum over aligned groups of L lanes; every lane of a group gets the sum.
 template <int L>
 __device__ __forceinline__ float reduce_lanes(float v)
 {
-    if (L >= 2)
-        v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]: xor 1
-    if (L >= 4)
-        v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]: xor 2
-    if (L >= 8)
-        v += swizzle_xor<4>(v);
-    if (L >= 16)
-        v += swizzle_xor<8>(v);
-    if (L >= 32)
-        v += swizzle_xor<16>(v);
-    if (L >= 64)
-        v += __shfl_xor(v, 32);
-    return v;
+    return lanes::reduce<L>(v);
 }
 
 __device__ __forceinline__ void better(float &bv, int &bi, float ov, int oi)
@@ -260,21 +233,29 @@ __device__ void grid_argmax(float bv, int bi, ArgmaxScratch am)
         am.partials[blockIdx.x] = pack_vi(bv, bi);
 }
 
-// Step 2: one block combines the candidates (max value, then lowest index;
-// the result does not depend on the order they are visited in).
-__global__ __launch_bounds__(1024) void argmax_reduce_kernel(const unsigned long long *__restrict__ partials,
-                                                             int64_t count, int32_t *__restrict__ result)
+// Step 2: one wavefront combines the candidates (max value, then lowest
+// index; the result does not depend on the order they are visited in).  All
+// of a lane's loads in a round are issued before any is used, so the kernel
+// costs about one memory round trip.
+__global__ __launch_bounds__(64) void argmax_reduce_kernel(const unsigned long long *__restrict__ partials,
+                                                           int64_t count, int32_t *__restrict__ result)
 {
-    __shared__ float sv[16];
-    __shared__ int si[16];
+    constexpr int kPerLane = 8;
     float v = -INFINITY;
     int i = 0x7fffffff;
-    for (int64_t b = threadIdx.x; b < count; b += blockDim.x) {
-        const unsigned long long pv = partials[b];
-        better(v, i, __builtin_bit_cast(float, (unsigned int)(pv & 0xFFFFFFFFull)),
-               (int)(unsigned int)(pv >> 32));
+    for (int64_t base = 0; base < count; base += 64 * kPerLane) {
+        unsigned long long pv[kPerLane];
+#pragma unroll
+        for (int q = 0; q < kPerLane; ++q) {
+            const int64_t b = base + q * 64 + threadIdx.x;
+            pv[q] = b < count ? partials[b] : 0x7FFFFFFFFF800000ull;  // (-inf, INT32_MAX)
+        }
+#pragma unroll
+        for (int q = 0; q < kPerLane; ++q)
+            better(v, i, __builtin_bit_cast(float, (unsigned int)(pv[q] & 0xFFFFFFFFull)),
+                   (int)(unsigned int)(pv[q] >> 32));
     }
-    block_argmax(v, i, sv, si);
+    wave_argmax(v, i);
     if (threadIdx.x == 0)
         *result = i;
 }
@@ -320,18 +301,11 @@ __device__ __forceinline__ void compute_tile(const TileRegs<CG> &r, const uint32
         }
 }
 
-// Cross-lane reduction of a finished tile and its epilogue.
-template <int L, int EPI>
-__device__ __forceinline__ void finish_tile(const float (&acc)[2], int64_t t, int s, int c,
-                                            void *__restrict__ out, int64_t rows, int64_t n_out,
-                                            float &bv, int &bi)
+// Epilogue of the finished sums y0, y1 of logical rows r0 (even) and r0 + 1.
+template <int EPI>
+__device__ __forceinline__ void store_rows(float y0, float y1, int64_t r0, void *__restrict__ out,
+                                           int64_t rows, int64_t n_out, float &bv, int &bi)
 {
-    constexpr int TR = 128 / L;
-    const float y0 = reduce_lanes<L>(acc[0]);
-    const float y1 = reduce_lanes<L>(acc[1]);
-    const int64_t r0 = t * TR + 2 * s;   // even
-    if (c != 0)
-        return;
     if (EPI == EPI_F16) {
         uint16_t *y = static_cast<uint16_t *>(out);
         if (r0 + 1 < rows)
@@ -358,107 +332,32 @@ __device__ __forceinline__ void finish_tile(const float (&acc)[2], int64_t t, in
     }
 }
 
+// Cross-lane reduction of a finished tile and its epilogue.
+template <int L, int EPI>
+__device__ __forceinline__ void finish_tile(const float (&acc)[2], int64_t t, int s, int c,
+                                            void *__restrict__ out, int64_t rows, int64_t n_out,
+                                            float &bv, int &bi)
+{
+    constexpr int TR = 128 / L;
+    const float y0 = reduce_lanes<L>(acc[0]);
+    const float y1 = reduce_lanes<L>(acc[1]);
+    if (c == 0)
+        store_rows<EPI>(y0, y1, t * TR + 2 * s, out, rows, n_out, bv, bi);
+}
+
 // ------------------------------------------------------------ GEMV kernels --
 //
 // rows: logical rows of the layout (gate/up: 2 * n_out); n_out: output length.
-// All three kernels share the tile arithmetic above and differ in how tiles
-// are assigned and how many are kept in flight.
-
-#ifndef Q4_RING_DEPTH_CG4
-#define Q4_RING_DEPTH_CG4 2
-#endif
-#ifndef Q4_RING_DEPTH
-#define Q4_RING_DEPTH 3
-#endif
-// Tiles of registers a ring wavefront keeps loaded ahead (x slice: 16*CG
-// VGPRs; one tile: 9*CG VGPRs).
-template <int CG>
-constexpr int ring_depth() { return CG >= 4 ? Q4_RING_DEPTH_CG4 : Q4_RING_DEPTH; }
-
-#ifndef Q4_RING_STRIDED
-#define Q4_RING_STRIDED 1
-#endif
-
-// Ring kernel (single-pass weights, many tiles): each wavefront loads its x
-// slice once and walks its tiles keeping D tiles of codes and scales loaded
-// ahead in registers: the buffer it has just computed is refilled with the
-// tile D further on.  With Q4_RING_STRIDED the wavefront's j-th tile is
-// wave + j * nwaves (all wavefronts sweep the matrix together, so requests in
-// flight at any moment cover one contiguous stretch of HBM); otherwise it owns
-// a contiguous chunk.
-template <int L, int CG, int EPI>
-__global__ __launch_bounds__(256) void gemv_ring_kernel(
-    const uint8_t *__restrict__ wd, const uint16_t *__restrict__ x, void *__restrict__ out,
-    int64_t rows, int64_t k, int64_t tiles, int64_t n_out, ArgmaxScratch am)
-{
-    constexpr int D = ring_depth<CG>();
-    constexpr int64_t PB = (int64_t)CG * 2304;
-    const int lane = threadIdx.x & 63;
-    const int s = lane / L, c = lane % L;
-    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
-    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-#if Q4_RING_STRIDED
-    const int64_t first = wave, step = nwaves;
-    const int64_t count = wave < tiles ? (tiles - wave + nwaves - 1) / nwaves : 0;
-#else
-    const int64_t per = (tiles + nwaves - 1) / nwaves;
-    const int64_t first = wave * per, step = 1;
-    const int64_t count = first < tiles ? (first + per < tiles ? per : tiles - first) : 0;
-#endif
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    const DequantConsts m = dequant_consts();
-
-    if (count > 0) {
-        TileRegs<CG> r[D];
-#pragma unroll
-        for (int i = 0; i < D; ++i)
-            if (i < count)
-                load_tile(r[i], wd + (first + i * step) * PB, lane);
-        uint32_t xp[CG][16];
-#pragma unroll
-        for (int j = 0; j < CG; ++j)
-            load_x_group(xp[j], x, (int64_t)c * CG + j, k >> 5);
-        int64_t q = 0;   // index of the tile in r[0]
-        // steady state: every refill is a real tile
-        while (q + 2 * D <= count) {
-#pragma unroll
-            for (int i = 0; i < D; ++i) {
-                float acc[2] = {0.f, 0.f};
-                compute_tile(r[i], xp, acc, m);
-                load_tile(r[i], wd + (first + (q + i + D) * step) * PB, lane);
-                finish_tile<L, EPI>(acc, first + (q + i) * step, s, c, out, rows, n_out, bv, bi);
-            }
-            q += D;
-        }
-        // drain: fewer than 2D tiles left, the first D of them in r[]
-#pragma unroll
-        for (int i = 0; i < D; ++i) {
-            if (q + i < count) {
-                float acc[2] = {0.f, 0.f};
-                compute_tile(r[i], xp, acc, m);
-                if (q + i + D < count)
-                    load_tile(r[i], wd + (first + (q + i + D) * step) * PB, lane);
-                finish_tile<L, EPI>(acc, first + (q + i) * step, s, c, out, rows, n_out, bv, bi);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < D; ++i) {
-            if (q + D + i < count) {
-                float acc[2] = {0.f, 0.f};
-                compute_tile(r[i], xp, acc, m);
-                finish_tile<L, EPI>(acc, first + (q + D + i) * step, s, c, out, rows, n_out, bv,
-                                    bi);
-            }
-        }
-    }
-    if (EPI == EPI_F32 && am.partials != nullptr)
-        grid_argmax(bv, bi, am);
-}
+// The three kernels (block, split, multi-pass) share the unit arithmetic
+// above and differ in how tiles are assigned and how many are kept in flight.
 
 #ifndef Q4_STREAM_DEPTH
-#define Q4_STREAM_DEPTH 3
+#define Q4_STREAM_DEPTH 6
 #endif
+#ifndef Q4_BLOCK_WAVES
+#define Q4_BLOCK_WAVES 4
+#endif
+constexpr int kBlockWaves = Q4_BLOCK_WAVES;
 
 // Buffer resources: a tile (one pass) is addressed through a V# whose
 // num_records is the tile's byte size, or 0 when the wavefront has no such
@@ -526,15 +425,15 @@ __device__ __forceinline__ void stream_tile(TileRegs<CG> &cur, TileRegs<CG> &nxt
     }
 }
 
-// Block kernel (single-pass weights): a block of 4 wavefronts takes 4
-// consecutive tiles at a time, one per wavefront, and strides over the
-// matrix by the grid.  The block stages x in LDS once; each wavefront then
-// builds its x pairs from LDS, so x costs one L2 read per block instead of
-// one per wavefront.  Each wavefront streams its tiles unit by unit (one
-// 1 KiB load per 16-byte lane unit) with Q4_STREAM_DEPTH units in flight, so
-// the dequant work of a unit overlaps the loads of the next ones and the
-// memory system sees a steady stream instead of the whole matrix requested
-// at once.
+// Block kernel (single-pass weights): a block of kBlockWaves wavefronts
+// takes that many consecutive tiles at a time, one per wavefront, and
+// strides over the matrix by the grid (about two blocks per CU, so each
+// wavefront streams a few tiles).  The block stages x in LDS once; each
+// wavefront then builds its x pairs from LDS, so x costs one L2 read per
+// block instead of one per wavefront, and few blocks keep that cost small.
+// Each wavefront streams its tiles unit by unit (one 1 KiB load per 16-byte
+// lane unit) with Q4_STREAM_DEPTH units in flight -- by default a whole
+// tile, so while a tile is reduced the next one is already on its way.
 constexpr int kBlockXHalves = 8192;   // largest single-pass k
 
 __device__ __forceinline__ void lds_x_group(uint32_t *xp, const uint4 *xs, int64_t g, int64_t G)
@@ -556,7 +455,7 @@ __device__ __forceinline__ void lds_x_group(uint32_t *xp, const uint4 *xs, int64
 }
 
 template <int L, int CG, int EPI>
-__global__ __launch_bounds__(256) void gemv_block_kernel(
+__global__ __launch_bounds__(64 * kBlockWaves) void gemv_block_kernel(
     const uint8_t *__restrict__ wd, const uint16_t *__restrict__ x, void *__restrict__ out,
     int64_t rows, int64_t k, int64_t tiles, int64_t n_out, ArgmaxScratch am)
 {
@@ -564,19 +463,30 @@ __global__ __launch_bounds__(256) void gemv_block_kernel(
     constexpr int64_t PB = (int64_t)CG * 2304;
     __shared__ uint4 xs[kBlockXHalves / 8];
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    // wave-uniform by construction; said explicitly so that the tile index and
+    // its buffer resource live in SGPRs (no waterfall loop around each load)
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int s = lane / L, c = lane % L;
     const int64_t G = k >> 5;
     float bv = -INFINITY;
     int bi = 0x7fffffff;
     const DequantConsts m = dequant_consts();
 
-    // x first (L2 hits after the first blocks), then the head of the stream
-    const uint4 *x4 = reinterpret_cast<const uint4 *>(x);
-    for (int64_t i = threadIdx.x; i < k / 8; i += 256)
-        xs[i] = x4[i];
-    int64_t t = (int64_t)blockIdx.x * 4 + w;
-    const int64_t step = (int64_t)gridDim.x * 4;
+    // x and the head of the weight stream are requested together: x through
+    // a resource of k halves (loads past it return zeros), up to 4 x 16 bytes
+    // per thread (the largest single-pass k; only the rounds k needs are
+    // issued), written to LDS once both are in flight
+    const __amdgpu_buffer_rsrc_t xrs = tile_rsrc(reinterpret_cast<const uint8_t *>(x), (int)(k * 2));
+    constexpr int kThreads = 64 * kBlockWaves;
+    constexpr int kXRounds = kBlockXHalves / 8 / kThreads;
+    const int xrounds = (int)((k / 8 + kThreads - 1) / kThreads);
+    v4u xv[kXRounds];
+#pragma unroll
+    for (int q = 0; q < kXRounds; ++q)
+        if (q < xrounds)
+            xv[q] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (threadIdx.x + kThreads * q) * 16, 0, 0);
+    int64_t t = (int64_t)blockIdx.x * kBlockWaves + w;
+    const int64_t step = (int64_t)gridDim.x * kBlockWaves;
     auto rs_of = [&](int64_t tt) {
         return tt < tiles ? tile_rsrc(wd + tt * PB, (int)PB) : tile_rsrc(wd, 0);
     };
@@ -588,6 +498,10 @@ __global__ __launch_bounds__(256) void gemv_block_kernel(
         for (int i = 0; i < PD; ++i)
             load_unit(ra, r0, lane, i);
     }
+#pragma unroll
+    for (int q = 0; q < kXRounds; ++q)
+        if (q < xrounds)
+            xs[threadIdx.x + kThreads * q] = make_uint4(xv[q].x, xv[q].y, xv[q].z, xv[q].w);
     __syncthreads();
     uint32_t xp[CG][16];
 #pragma unroll
@@ -615,62 +529,100 @@ __global__ __launch_bounds__(256) void gemv_block_kernel(
         grid_argmax(bv, bi, am);
 }
 
-// Split kernel (single-pass weights, few tiles): CG wavefronts share a tile;
-// wavefront j takes group slot j of every lane (2 code units, x for one
-// group), so there are CG times more wavefronts in flight, each with a
-// quarter to a third of the x traffic.  The CG partial sums of a row are
-// added in LDS in slot order (deterministic), then wavefront 0 finishes.
+// Split kernel (single-pass weights, long k, few tiles): a block of CG
+// wavefronts owns the tiles blockIdx.x, + gridDim.x, ... (at most
+// kSplitMaxTiles of them); wavefront j takes group slot j of every lane in
+// all of them, so a lane keeps the x slice of one group in VGPRs for the
+// whole launch and streams 2 code units per tile, with the next
+// Q4_SPLIT_DEPTH - 1 tiles already in flight.  Each tile's row sums are
+// reduced across lanes inside the wavefront and parked in LDS; after one
+// barrier at the end the CG slot sums of a row are added in slot order
+// (deterministic) and the epilogue runs.
+constexpr int kSplitMaxTiles = 8;
+#ifndef Q4_SPLIT_DEPTH
+#define Q4_SPLIT_DEPTH 2
+#endif
+
 template <int L, int CG, int EPI>
-__global__ __launch_bounds__(256) void gemv_split_kernel(
+__global__ __launch_bounds__(64 * CG) void gemv_split_kernel(
     const uint8_t *__restrict__ wd, const uint16_t *__restrict__ x, void *__restrict__ out,
     int64_t rows, int64_t k, int64_t tiles, int64_t n_out, ArgmaxScratch am)
 {
-    constexpr int64_t PB = (int64_t)CG * 2304;
-    __shared__ float part[CG][64][2];
+    constexpr int HP = 64 / L;   // row pairs per tile
+    constexpr int TR = 128 / L;
+    constexpr int PB = CG * 2304;
+    constexpr int D = Q4_SPLIT_DEPTH;
+    __shared__ float part[kSplitMaxTiles][CG][HP][2];
     const int lane = threadIdx.x & 63;
-    const int j = threadIdx.x >> 6;   // group slot of this wavefront
+    const int j = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int s = lane / L, c = lane % L;
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
     uint32_t xp[16];
     load_x_group(xp, x, (int64_t)c * CG + j, k >> 5);
     const DequantConsts m = dequant_consts();
-    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
-        const uint8_t *base = wd + t * PB;
-        const uint4 c0 = *reinterpret_cast<const uint4 *>(base + j * 1024 + lane * 16);
-        const uint4 c1 = *reinterpret_cast<const uint4 *>(base + (CG + j) * 1024 + lane * 16);
-        const uint16_t *sp = reinterpret_cast<const uint16_t *>(base + 2 * CG * 1024 + lane * 4 * CG);
-        const float s0 = f16_value(sp[j]), s1 = f16_value(sp[CG + j]);
-        float acc[2];
-        {
-            float p1 = 0.f, p16 = 0.f;
-            dot_word(c0.x, &xp[0], p1, p16, m);
-            dot_word(c0.y, &xp[4], p1, p16, m);
-            dot_word(c0.z, &xp[8], p1, p16, m);
-            dot_word(c0.w, &xp[12], p1, p16, m);
-            acc[0] = s0 * fmaf(p16, 0.0625f, p1);
-        }
-        {
-            float p1 = 0.f, p16 = 0.f;
-            dot_word(c1.x, &xp[0], p1, p16, m);
-            dot_word(c1.y, &xp[4], p1, p16, m);
-            dot_word(c1.z, &xp[8], p1, p16, m);
-            dot_word(c1.w, &xp[12], p1, p16, m);
-            acc[1] = s1 * fmaf(p16, 0.0625f, p1);
-        }
-        part[j][lane][0] = acc[0];
-        part[j][lane][1] = acc[1];
-        __syncthreads();
-        if (j == 0) {
-            float tot[2] = {part[0][lane][0], part[0][lane][1]};
+    const int64_t count =
+        (int64_t)blockIdx.x < tiles ? (tiles - 1 - (int64_t)blockIdx.x) / gridDim.x + 1 : 0;
+
+    // this wavefront's two units and two scales inside a tile
+    const int wo0 = j * 1024 + lane * 16, wo1 = (CG + j) * 1024 + lane * 16;
+    const int so0 = 2 * CG * 1024 + lane * 4 * CG + j * 2, so1 = so0 + CG * 2;
+    struct Regs {
+        v4u w0, w1;
+        uint16_t s0, s1;
+    };
+    auto load = [&](Regs &r, int64_t i) {   // the block's i-th tile; none past count
+        const bool live = i < count;
+        const __amdgpu_buffer_rsrc_t rs =
+            tile_rsrc(wd + (live ? (int64_t)blockIdx.x + i * gridDim.x : 0) * PB, live ? PB : 0);
+        r.w0 = __builtin_amdgcn_raw_buffer_load_b128(rs, wo0, 0, 0);
+        r.w1 = __builtin_amdgcn_raw_buffer_load_b128(rs, wo1, 0, 0);
+        r.s0 = __builtin_amdgcn_raw_buffer_load_b16(rs, so0, 0, 0);
+        r.s1 = __builtin_amdgcn_raw_buffer_load_b16(rs, so1, 0, 0);
+    };
+    Regs ring[D];
 #pragma unroll
-            for (int q = 1; q < CG; ++q) {
-                tot[0] += part[q][lane][0];
-                tot[1] += part[q][lane][1];
+    for (int q = 0; q < D; ++q)
+        load(ring[q], q);
+    for (int64_t i0 = 0; i0 < count; i0 += D) {
+#pragma unroll
+        for (int q = 0; q < D; ++q) {
+            const int64_t i = i0 + q;
+            if (i >= count)
+                break;
+            float a1 = 0.f, a16 = 0.f, b1 = 0.f, b16 = 0.f;
+            dot_word(ring[q].w0.x, &xp[0], a1, a16, m);
+            dot_word(ring[q].w0.y, &xp[4], a1, a16, m);
+            dot_word(ring[q].w0.z, &xp[8], a1, a16, m);
+            dot_word(ring[q].w0.w, &xp[12], a1, a16, m);
+            dot_word(ring[q].w1.x, &xp[0], b1, b16, m);
+            dot_word(ring[q].w1.y, &xp[4], b1, b16, m);
+            dot_word(ring[q].w1.z, &xp[8], b1, b16, m);
+            dot_word(ring[q].w1.w, &xp[12], b1, b16, m);
+            const float acc0 = f16_value(ring[q].s0) * fmaf(a16, 0.0625f, a1);
+            const float acc1 = f16_value(ring[q].s1) * fmaf(b16, 0.0625f, b1);
+            // the tile's arithmetic is issued before its registers are refilled
+            asm volatile("" ::"v"(acc0), "v"(acc1) : "memory");
+            load(ring[q], i + D);
+            const float y0 = reduce_lanes<L>(acc0);
+            const float y1 = reduce_lanes<L>(acc1);
+            if (c == 0) {
+                part[i][j][s][0] = y0;
+                part[i][j][s][1] = y1;
             }
-            finish_tile<L, EPI>(tot, t, s, c, out, rows, n_out, bv, bi);
         }
-        __syncthreads();
+    }
+    __syncthreads();
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int o = threadIdx.x; o < count * HP; o += 64 * CG) {
+        const int i = o / HP, ss = o % HP;
+        float y0 = part[i][0][ss][0], y1 = part[i][0][ss][1];
+#pragma unroll
+        for (int jj = 1; jj < CG; ++jj) {
+            y0 += part[i][jj][ss][0];
+            y1 += part[i][jj][ss][1];
+        }
+        const int64_t t = (int64_t)blockIdx.x + (int64_t)i * gridDim.x;
+        store_rows<EPI>(y0, y1, t * TR + 2 * ss, out, rows, n_out, bv, bi);
     }
     if (EPI == EPI_F32 && am.partials != nullptr)
         grid_argmax(bv, bi, am);
@@ -710,21 +662,21 @@ __global__ __launch_bounds__(256) void gemv_multipass_kernel(
 
 // ----------------------------------------------------------------- launch --
 
-#ifndef Q4_WAVES_PER_CU
-#define Q4_WAVES_PER_CU 4
-#endif
 #ifndef Q4_SPLIT_BELOW_TILES
 #define Q4_SPLIT_BELOW_TILES 2000
 #endif
-#ifndef Q4_USE_RING
-#define Q4_USE_RING 0
-#endif
 #ifndef Q4_BLOCKS_PER_CU
-#define Q4_BLOCKS_PER_CU 8
+#define Q4_BLOCKS_PER_CU 2
+#endif
+#ifndef Q4_SPLIT_MIN_CG
+#define Q4_SPLIT_MIN_CG 4
+#endif
+#ifndef Q4_SPLIT_BLOCKS_PER_CU
+#define Q4_SPLIT_BLOCKS_PER_CU 2
 #endif
 constexpr int64_t kCUs = 256;   // MI355X compute units; plans depend on shape only
 
-enum Mode { MODE_RING = 0, MODE_SPLIT = 1, MODE_MULTIPASS = 2, MODE_BLOCK = 3 };
+enum Mode { MODE_SPLIT = 1, MODE_MULTIPASS = 2, MODE_BLOCK = 3 };
 
 struct GemvPlan {
     Mode mode;
@@ -740,17 +692,20 @@ static GemvPlan plan_gemv(const Geometry &geo)
         const int64_t waves = geo.tiles < kCUs * 8 ? geo.tiles : kCUs * 8;
         return {MODE_MULTIPASS, (waves + 3) / 4, 256};
     }
-    if (geo.CG > 1 && geo.tiles < Q4_SPLIT_BELOW_TILES)
-        return {MODE_SPLIT, geo.tiles, 64 * geo.CG};
-#if Q4_USE_RING
-    const int64_t cap = kCUs * Q4_WAVES_PER_CU;
-    const int64_t waves = geo.tiles < cap ? geo.tiles : cap;
-    return {MODE_RING, (waves + 3) / 4, 256};
-#else
-    const int64_t groups = (geo.tiles + 3) / 4;
+    // long k (4 groups per lane) and few tiles: one wavefront per tile would
+    // leave the GPU short of wavefronts and each with a long serial chain, so
+    // the group slots of a tile go to separate wavefronts
+    if (geo.CG >= Q4_SPLIT_MIN_CG && geo.tiles < Q4_SPLIT_BELOW_TILES) {
+        int64_t blocks = kCUs * Q4_SPLIT_BLOCKS_PER_CU;
+        if (blocks > geo.tiles)
+            blocks = geo.tiles;
+        if (blocks * kSplitMaxTiles < geo.tiles)
+            blocks = (geo.tiles + kSplitMaxTiles - 1) / kSplitMaxTiles;
+        return {MODE_SPLIT, blocks, 64 * geo.CG};
+    }
+    const int64_t groups = (geo.tiles + kBlockWaves - 1) / kBlockWaves;
     const int64_t cap = kCUs * Q4_BLOCKS_PER_CU;
-    return {MODE_BLOCK, groups < cap ? groups : cap, 256};
-#endif
+    return {MODE_BLOCK, groups < cap ? groups : cap, 64 * kBlockWaves};
 }
 
 int64_t argmax_workspace_bytes(const Geometry &geo)
@@ -795,10 +750,6 @@ static void launch_lce(const GemvPlan &plan, const GemvArgs &a, hipStream_t stre
 {
     const dim3 grid((unsigned)plan.blocks), block((unsigned)plan.threads);
     switch (plan.mode) {
-    case MODE_RING:
-        hipLaunchKernelGGL((gemv_ring_kernel<L, CG, EPI>), grid, block, 0, stream, a.wd, a.x, a.out,
-                           a.rows, a.k, a.geo->tiles, a.n_out, a.am);
-        break;
     case MODE_SPLIT:
         hipLaunchKernelGGL((gemv_split_kernel<L, CG, EPI>), grid, block, 0, stream, a.wd, a.x, a.out,
                            a.rows, a.k, a.geo->tiles, a.n_out, a.am);
@@ -858,7 +809,7 @@ hipError_t launch_gemv_family(const Geometry &geo, Epilogue epi, const void *wda
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
-        hipLaunchKernelGGL(argmax_reduce_kernel, dim3(1), dim3(1024), 0, stream, am.partials,
+        hipLaunchKernelGGL(argmax_reduce_kernel, dim3(1), dim3(64), 0, stream, am.partials,
                            plan.blocks, am.result);
     }
     return hipGetLastError();

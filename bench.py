@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--summarize", metavar="RESULTS_DB",
                     help="print per-kernel duration statistics of a rocprofv3 "
                          "--kernel-trace database (grouped by kernel and grid) and exit")
+    ap.add_argument("--roles", metavar="NAMES",
+                    help="with --summarize: comma-separated names of the GEMVs one step "
+                         "launches, in order (a --only layer run: qkv,o_proj,gate_up,down)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="print the HBM traffic summary of the gate_up GEMV from two "
                          "rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of --only layer, "
@@ -66,17 +69,41 @@ def parse():
 CALIBRATION_BYTES = 256 << 20   # device-to-device copy made in --only layer runs
 
 
+LAYER_ROLES = ("qkv", "o_proj", "gate_up", "down")   # launch order of one layer step
+
+
+def label_roles(seq, roles):
+    """Roles of the q4 GEMV dispatches of a profiled run, in dispatch order:
+    a dispatch with the same (kernel, grid) as the previous GEMV dispatch keeps
+    its role (a loop over one GEMV), any other takes the next role in step
+    order.  This matches the launch order of bench.py's layer part: the timed
+    steps, then one timing loop per GEMV in step order.  Non-GEMV dispatches
+    get None."""
+    out, ri, prev = [], -1, None
+    for name, grid in seq:
+        if not name.startswith("void q4::gemv_"):
+            out.append(None)
+            continue
+        if (name, grid) != prev:
+            ri = (ri + 1) % len(roles)
+            prev = (name, grid)
+        out.append(roles[ri])
+    return out
+
+
 def pmc_medians(db_path: str, counter: str):
-    """{(kernel name, grid): median value per dispatch} of one counter."""
+    """{role or (kernel name, grid): median value per dispatch} of one counter;
+    layer GEMV dispatches are keyed by their role."""
     import sqlite3
     import statistics
     db = sqlite3.connect(db_path)
     rows = db.execute("select dispatch_id, kernel_name, grid_size, sum(value) from "
-                      "counters_collection where counter_name = ? group by dispatch_id",
-                      (counter,)).fetchall()
+                      "counters_collection where counter_name = ? group by dispatch_id "
+                      "order by dispatch_id", (counter,)).fetchall()
+    labels = label_roles([(name, grid) for _, name, grid, _ in rows], LAYER_ROLES)
     groups = {}
-    for _, name, grid, v in rows:
-        groups.setdefault((name, grid), []).append(v)
+    for (_, name, grid, v), role in zip(rows, labels):
+        groups.setdefault(role or (name, grid), []).append(v)
     return {key: statistics.median(v) for key, v in groups.items()}
 
 
@@ -98,48 +125,53 @@ def traffic_summary(fetch_db: str, write_db: str) -> int:
     cal_w = pmc_max_dispatch(write_db, "WRITE_SIZE")
     kf = CALIBRATION_BYTES / (cal_f[1] * 1024.0)
     kw = CALIBRATION_BYTES / (cal_w[1] * 1024.0)
-    gate = [key for key in fetch if "gemv_block_kernel<32, 3, 0>" in key[0]]
-    gate = max(gate, key=lambda key: key[1])          # the 16384-row launch: largest grid
-    f_bytes = fetch[gate] * 1024.0 * kf
-    w_bytes = write.get(gate, 0.0) * 1024.0 * kw
-    print("# HBM traffic of the gate_up GEMV (16384 x 3072) per launch, from rocprofv3 PMC")
+    import seeded_inputs as si
+    print("# HBM traffic per launch of the layer-set GEMVs, from rocprofv3 PMC; the gate_up")
+    print("# GEMV (16384 x 3072) is the kernel bench.py reports in its roofline object")
     print(f"# FETCH_SIZE run: {fetch_db}")
     print(f"# WRITE_SIZE run: {write_db}")
     print(f"# calibration: {cal_f[0][:40]} copying {CALIBRATION_BYTES} B reads "
           f"FETCH_SIZE {cal_f[1]:.1f} KiB and WRITE_SIZE {cal_w[1]:.1f} KiB")
-    print(f"kernel: {gate[0][:90]}")
-    print(f"grid: {gate[1]}")
-    print(f"fetch_size_kib_median: {fetch[gate]:.1f}")
-    print(f"write_size_kib_median: {write.get(gate, 0.0):.1f}")
     print(f"fetch_scale: {kf:.4f}")
     print(f"write_scale: {kw:.4f}")
-    print(f"hbm_read_bytes_per_launch: {f_bytes:.0f}")
-    print(f"hbm_write_bytes_per_launch: {w_bytes:.0f}")
-    print(f"hbm_bytes_per_launch: {f_bytes + w_bytes:.0f}")
-    print(f"algorithmic_bytes_per_launch: {gemv_bytes(16384, 3072)}")
+    for role in LAYER_ROLES:
+        n, k = si.LAYER_SHAPES[role]
+        f_bytes = fetch[role] * 1024.0 * kf
+        w_bytes = write.get(role, 0.0) * 1024.0 * kw
+        tag = "" if role == "gate_up" else f"{role}."
+        print(f"# {role} {n} x {k}: FETCH_SIZE median {fetch[role]:.1f} KiB, "
+              f"WRITE_SIZE median {write.get(role, 0.0):.1f} KiB")
+        print(f"{tag}hbm_read_bytes_per_launch: {f_bytes:.0f}")
+        print(f"{tag}hbm_write_bytes_per_launch: {w_bytes:.0f}")
+        print(f"{tag}hbm_bytes_per_launch: {f_bytes + w_bytes:.0f}")
+        print(f"{tag}algorithmic_bytes_per_launch: {gemv_bytes(n, k)}")
     print(f"kernel_sources_sha256_16: {kernels_hash()}")
     return 0
 
 
-def summarize(db_path: str) -> int:
+def summarize(db_path: str, roles=None) -> int:
     """Kernel-trace statistics from a rocprofv3 results database: one row per
-    (kernel, grid size), durations in microseconds."""
+    (kernel, grid size), durations in microseconds.  With `roles` (the names
+    of the GEMVs one step launches, in launch order) the q4 GEMV dispatches
+    are labelled by label_roles, so two layers that run the same kernel with
+    the same grid get separate rows."""
     import sqlite3
     import statistics
     db = sqlite3.connect(db_path)
     rows = db.execute("select name, grid_x, workgroup_x, vgpr_count, accum_vgpr_count, "
-                      "sgpr_count, lds_size, duration from kernels").fetchall()
+                      "sgpr_count, lds_size, duration from kernels order by start").fetchall()
+    labels = label_roles([(r[0], r[1]) for r in rows], roles) if roles else [None] * len(rows)
     groups = {}
-    for name, gx, wx, vg, ag, sg, lds, dur in rows:
-        groups.setdefault((name, gx, wx, vg, ag, sg, lds), []).append(dur / 1000.0)
+    for (name, gx, wx, vg, ag, sg, lds, dur), role in zip(rows, labels):
+        groups.setdefault((role or "-", name, gx, wx, vg, ag, sg, lds), []).append(dur / 1000.0)
     print(f"# rocprofv3 kernel trace: {db_path}")
-    print("# calls  avg_us  median_us  min_us  p90_us  grid  block  vgpr  agpr  sgpr  lds  kernel")
+    print("# calls  avg_us  median_us  min_us  p90_us  grid  block  vgpr  agpr  sgpr  lds  role  kernel")
     for key, d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
-        name, gx, wx, vg, ag, sg, lds = key
+        role, name, gx, wx, vg, ag, sg, lds = key
         d.sort()
         p90 = d[min(len(d) - 1, int(0.9 * len(d)))]
         print(f"{len(d):6d} {statistics.fmean(d):8.3f} {statistics.median(d):8.3f} {d[0]:8.3f} "
-              f"{p90:8.3f} {gx:8d} {wx:5d} {vg:4d} {ag:4d} {sg:4d} {lds:6d}  {name[:110]}")
+              f"{p90:8.3f} {gx:8d} {wx:5d} {vg:4d} {ag:4d} {sg:4d} {lds:6d}  {role:8s} {name[:100]}")
     return 0
 
 
@@ -255,7 +287,7 @@ def per_launch_us(torch, fn, launches: int = 200, warmup: int = 20):
 def main():
     args = parse()
     if args.summarize:
-        return summarize(args.summarize)
+        return summarize(args.summarize, args.roles.split(",") if args.roles else None)
     if args.traffic:
         return traffic_summary(*args.traffic)
     if args.gpus != 1:
@@ -308,7 +340,7 @@ def main():
     dn, dk = si.LAYER_SHAPES[dom]
     dom_bytes = gemv_bytes(dn, dk)
     achieved = dom_bytes / (kus[dom] * 1e-6) / 1e9
-    traffic = committed_traffic("gemv_16384x3072")
+    traffic = committed_traffic("phi3_layer_set")
     result.update({
         "metric": "int4 GEMV effective HBM GB/s (% of peak) + us per Phi-3-mini decode layer",
         "value": round(gbs, 2),

@@ -59,7 +59,8 @@ def test_ffn_closed_forms(q4):
     assert np.all((h & 0x7FFF) == 0)
 
 
-@pytest.mark.parametrize("n,k", [(1, 32), (7, 96), (129, 3072), (300, 8192 + 32 * 3)])
+@pytest.mark.parametrize("n,k", [(1, 32), (7, 96), (129, 3072), (300, 8192 + 32 * 3),
+                                 (129, 8192), (1000, 7168)])
 def test_ffn_ragged(q4, orc, n, k):
     rng = np.random.default_rng(n + 3 * k)
     x = si.draw_x(rng, k)

@@ -29,7 +29,7 @@ def test_gemm_parity_auto(q4, orc, m):
 
 
 @pytest.mark.parametrize("path", ["valu", "mfma"])
-@pytest.mark.parametrize("m", [1, 3, 16, 40])
+@pytest.mark.parametrize("m", [1, 3, 16, 24, 40])
 def test_gemm_forced_paths(q4, orc, path, m):
     rng = np.random.default_rng(7 * m + len(path))
     n, k = 777, 8192
@@ -89,7 +89,7 @@ def test_gemm_one_hot_rows(q4, orc, path):
     assert np.array_equal(host_u16(Y), want)
 
 
-@pytest.mark.parametrize("m", [16, 64, 256])
+@pytest.mark.parametrize("m", [16, 24, 64, 256])
 def test_gemm_prefill_full_shape_sampled(q4, orc, m):
     """The full prefill shape (W 16384 x 3072): every output computed on the
     GPU, 96 weight rows x all m rows checked against the oracle."""

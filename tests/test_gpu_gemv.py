@@ -35,9 +35,12 @@ def test_layer_set_parity(q4, orc, key):
     print(f"{key}: max err/tol {ratio:.3g}")
 
 
+# includes the long-k split kernel with several tiles per block and an odd
+# last tile (3001 x 8192) and with padded groups (777 x 7168: 224 of 256
+# group slots real)
 RAGGED = [(1, 32), (2, 32), (17, 96), (130, 64), (33, 224), (7, 160), (6, 192), (1, 768),
           (3, 3200), (5, 16384), (3, 8352), (4, 16480), (1001, 3072), (9, 8192), (64, 4096),
-          (3, 3072)]
+          (3, 3072), (3001, 8192), (777, 7168)]
 
 
 @pytest.mark.parametrize("n,k", RAGGED)

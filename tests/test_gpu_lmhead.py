@@ -23,13 +23,14 @@ def test_lmhead_phi3_parity(q4, orc):
     assert int(idx.item()) == int(np.argmax(got))
 
 
-@pytest.mark.parametrize("n", [32064, 1001, 5, 1])
-def test_lmhead_planted_argmax_and_ties(q4, orc, n):
+@pytest.mark.parametrize("n,k", [(32064, 3072), (1001, 3072), (5, 3072), (1, 3072),
+                                 (1001, 8192), (5003, 8192)])
+def test_lmhead_planted_argmax_and_ties(q4, orc, n, k):
     """A planted winner (codes 15, x = 1) and an exact tie with a later copy of
     the same row: the lowest index wins, across blocks; repeated calls with
-    different n reuse the same workspace."""
-    k = 3072
-    rng = np.random.default_rng(n)
+    different n reuse the same workspace.  k = 8192 takes the long-k split
+    kernel (1001 rows) and the block kernel with 4 groups per lane (5003)."""
+    rng = np.random.default_rng(n + k)
     codes = rng.integers(0, 16, (n, k), dtype=np.uint8)
     scales = si.f16_bits(rng.uniform(0.005, 0.02, (n, k // 32)))
     win = (n * 5) // 7

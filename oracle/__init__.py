@@ -67,6 +67,8 @@ class Oracle:
         lib.q4o_ffn_gate_up_silu.argtypes = [_P, _P, _P, _P, _P, _I64, _I64,
                                              _P, _P, _P, _P, _P]
         lib.q4o_ffn_gate_up_silu.restype = ctypes.c_int
+        lib.q4o_add_rmsnorm.argtypes = [_P, _P, _P, _I64, ctypes.c_double, _P, _P]
+        lib.q4o_add_rmsnorm.restype = ctypes.c_int
         lib.q4o_argmax.argtypes = [_P, _I64]
         lib.q4o_argmax.restype = ctypes.c_int64
         lib.q4o_lmhead.argtypes = [_P, _P, _P, _I64, _I64, _P, _P]
@@ -150,6 +152,24 @@ class Oracle:
             *[_ptr(out[name]) for name in ("h", "g", "u", "ag", "au")])
         assert rc == 0
         return out
+
+    def add_rmsnorm(self, x, r, gamma, eps: float):
+        """(h, xn) f16 bits [k]: the new residual f16(x + r) (x when r is None)
+        and the normalised activation f16(h * gamma / sqrt(mean(h^2) + eps))."""
+        k = x.shape[0]
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        gamma = np.ascontiguousarray(gamma, dtype=np.uint16)
+        assert gamma.shape == (k,)
+        rp = None
+        if r is not None:
+            r = np.ascontiguousarray(r, dtype=np.uint16)
+            assert r.shape == (k,)
+            rp = _ptr(r)
+        h = np.empty(k, np.uint16)
+        xn = np.empty(k, np.uint16)
+        rc = self.lib.q4o_add_rmsnorm(_ptr(x), rp, _ptr(gamma), k, float(eps), _ptr(h), _ptr(xn))
+        assert rc == 0
+        return h, xn
 
     def argmax(self, v) -> int:
         v = np.ascontiguousarray(v, dtype=np.float64)

@@ -193,6 +193,44 @@ int q4o_ffn_gate_up_silu(const uint32_t *gw, const uint16_t *gs,
     return 0;
 }
 
+/*
+ * Residual add + RMSNorm ([P1] 内核融合: add_norm merges the residual
+ * connection and RMSNorm), the step in front of the QKV and gate/up matmuls.
+ * The pages give neither epsilon nor where results are rounded; the reading
+ * here: epsilon is a parameter, and the two vectors a separate kernel would
+ * store are f16:
+ *   h_i  = f16(x_i + r_i)                 (r NULL: h_i = x_i) -- new residual
+ *   ms   = (1/k) * sum_i h_i^2            (f64, over the f16 values h_i)
+ *   xn_i = f16(h_i * gamma_i / sqrt(ms + eps))
+ * x, r, gamma, h, xn are f16 bits [k]; h may be NULL.  Returns 0, or -1 for
+ * k < 1 or eps < 0.
+ */
+int q4o_add_rmsnorm(const uint16_t *x, const uint16_t *r, const uint16_t *gamma,
+                    int64_t k, double eps, uint16_t *h, uint16_t *xn)
+{
+    if (k < 1 || eps < 0)
+        return -1;
+    double ss = 0.0;
+    for (int64_t i = 0; i < k; ++i) {
+        double v = q4o_half_to_double(x[i]);
+        if (r)
+            v += q4o_half_to_double(r[i]);   /* exact: two f16 */
+        const double hv = q4o_half_to_double(q4o_double_to_half(v));
+        ss += hv * hv;
+    }
+    const double rms = sqrt(ss / (double)k + eps);
+    for (int64_t i = 0; i < k; ++i) {
+        double v = q4o_half_to_double(x[i]);
+        if (r)
+            v += q4o_half_to_double(r[i]);
+        const uint16_t hb = q4o_double_to_half(v);
+        if (h)
+            h[i] = hb;
+        xn[i] = q4o_double_to_half(q4o_half_to_double(hb) * q4o_half_to_double(gamma[i]) / rms);
+    }
+    return 0;
+}
+
 /* greedy argmax ([P1] 完整的推理流水线, 贪婪解码采样): the lowest index that
  * holds the maximum.  Returns -1 for n < 1. */
 int64_t q4o_argmax(const double *v, int64_t n)

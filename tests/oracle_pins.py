@@ -18,6 +18,9 @@ What pins what:
   * SiLU / FFN    : silu(0)=0, silu(ln 3)=(3/4)ln 3, silu(-g)=silu(g)-g, the
                     gate (not up) is the one gated.
   * argmax        : planted maximum, ties go to the lowest index.
+  * add + RMSNorm : a hand example (x = (3, 4)), the residual against numpy's
+                    f16 addition, constant inputs (+-1, and 1/sqrt(2) with
+                    eps = mean square), scale invariance, exact gamma scaling.
   * device layout : hand-derived geometry table (tests/golden), a byte-level
                     hand example, and a decoder written in the opposite
                     direction (destination -> logical) over random shapes.
@@ -277,6 +280,51 @@ def pin_lmhead(orc, quick=False):
 
 
 # ----------------------------------------------------------- device layout
+def pin_add_rmsnorm(orc, quick=False):
+    """Residual add + RMSNorm: a hand example, the residual against numpy's
+    f16 addition, closed forms and exact invariances."""
+    f16 = si.f16_bits
+    one = f16(np.ones(2))
+    # hand example: x = (3, 4), k = 2, eps = 0: mean of squares 12.5, root
+    # 3.5355339...; 3 / 3.5355339 = 0.8485281 lies 1737.79 f16 steps of 2^-11
+    # above 0 -> 1738 * 2^-11 = 0.8486328125; 4 / 3.5355339 = 1.1313708 is
+    # 1158.52 steps of 2^-10 -> 1159 * 2^-10 = 1.1318359375
+    h, xn = orc.add_rmsnorm(f16(np.array([3.0, 4.0])), None, one, 0.0)
+    assert np.array_equal(h, f16(np.array([3.0, 4.0])))
+    assert np.array_equal(xn, f16(np.array([0.8486328125, 1.1318359375])))
+    # the residual is f16(x + r), as numpy's correctly rounded f16 addition
+    rng = np.random.default_rng(31)
+    k = 256 if quick else 3072
+    x = rng.normal(0, 1, k).astype(np.float16)
+    r = rng.normal(0, 4, k).astype(np.float16)
+    g = rng.uniform(0.5, 2.0, k).astype(np.float16)
+    h, xn = orc.add_rmsnorm(x.view(np.uint16), r.view(np.uint16), g.view(np.uint16), 1e-5)
+    assert np.array_equal(h, (x + r).view(np.uint16))
+    # adding first is the same as normalising the stored residual
+    h2, xn2 = orc.add_rmsnorm(h, None, g.view(np.uint16), 1e-5)
+    assert np.array_equal(h2, h) and np.array_equal(xn2, xn)
+    # constant input: each element is +-1 exactly (mean over k, not the sum)
+    for c in (2.0, -0.375):
+        _, xn = orc.add_rmsnorm(f16(np.full(k, c)), None, f16(np.ones(k)), 0.0)
+        assert np.array_equal(xn, f16(np.full(k, math.copysign(1.0, c))))
+        # eps = c^2 doubles the mean square: 1 / sqrt(2) -> 1448 * 2^-11
+        _, xn = orc.add_rmsnorm(f16(np.full(k, c)), None, f16(np.ones(k)), c * c)
+        assert np.array_equal(xn, f16(np.full(k, math.copysign(0.70703125, c))))
+    # eps = 0: scaling x by 2 changes nothing; gamma scales the output exactly
+    _, a = orc.add_rmsnorm(x.view(np.uint16), None, g.view(np.uint16), 0.0)
+    _, b = orc.add_rmsnorm((x * np.float16(2)).view(np.uint16), None, g.view(np.uint16), 0.0)
+    assert np.array_equal(a, b)
+    _, c2 = orc.add_rmsnorm(x.view(np.uint16), None, (g * np.float16(2)).view(np.uint16), 0.0)
+    av = a.view(np.float16).astype(np.float64)
+    normal = np.abs(av) >= 2.0 ** -13
+    assert np.array_equal(c2.view(np.float16).astype(np.float64)[normal], 2 * av[normal])
+    # against the plain formula evaluated in numpy f64 (one rounding to f16)
+    hv = (x + r).astype(np.float64)
+    want = (hv * g.astype(np.float64) / np.sqrt(np.mean(hv * hv) + 1e-5)).astype(np.float16)
+    _, xn = orc.add_rmsnorm(x.view(np.uint16), r.view(np.uint16), g.view(np.uint16), 1e-5)
+    assert np.array_equal(xn, want.view(np.uint16))
+
+
 def load_geometry_golden():
     rows = []
     with open(os.path.join(GOLDEN, "layout_geometry.txt")) as f:
@@ -364,6 +412,6 @@ ALL_PINS = [
     pin_half_decode_all_patterns, pin_half_encode_rne,
     pin_gemv_rational, pin_gemv_exactly_representable, pin_gemv_closed_forms,
     pin_gemv_one_hot, pin_gemv_linearity, pin_gemm_rows,
-    pin_silu, pin_ffn, pin_argmax, pin_lmhead,
+    pin_silu, pin_ffn, pin_argmax, pin_lmhead, pin_add_rmsnorm,
     pin_layout_geometry, pin_layout_hand_example, pin_layout_roundtrip,
 ]

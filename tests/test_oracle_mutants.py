@@ -35,6 +35,14 @@ MUTANTS = [
     ("layout_tie_smaller_L", "cover < bestCover", "cover <= bestCover"),
     ("layout_gate_up_swapped", "rw = (r % 2 ? w1 : w0)", "rw = (r % 2 ? w0 : w1)"),
     ("layout_tile_rows", "int64_t TR = 2 * (64 / L);", "int64_t TR = 64 / L;"),
+    ("norm_sum_not_mean", "sqrt(ss / (double)k + eps)", "sqrt(ss + eps)"),
+    ("norm_eps_dropped", "sqrt(ss / (double)k + eps)", "sqrt(ss / (double)k)"),
+    ("norm_residual_dropped", "            v += q4o_half_to_double(r[i]);   /* exact: two f16 */",
+     "            v += 0.0;"),
+    ("norm_gamma_dropped", "q4o_half_to_double(hb) * q4o_half_to_double(gamma[i]) / rms",
+     "q4o_half_to_double(hb) / rms"),
+    ("norm_unrounded_residual", "const double hv = q4o_half_to_double(q4o_double_to_half(v));",
+     "const double hv = v;"),
 ]
 
 

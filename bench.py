@@ -420,6 +420,26 @@ def variants(torch, q4, si, np, K, W):
         "bytes": [gu_bytes, dbytes]}
     del rot_gu, rot_d
 
+    # residual add + RMSNorm fused into the QKV GEMV (9216 x 3072), next to
+    # the plain GEMV on the same weights: the prologue's cost inside the launch
+    inp = si.workload(si.LAYER_SET, seed=0)
+    w, s_ = inp["qkv"]
+    rng = np.random.default_rng(11)
+    rot = Rotation(q4, q4.pack(dev_u32(w), dev_u16(s_)), copies_for(weight_bytes(9216, 3072)))
+    x = dev_f16(inp["x3072"])
+    res = dev_f16(si.f16_bits(rng.normal(0.0, 2.0, 3072)))
+    gam = dev_f16(si.f16_bits(rng.uniform(0.5, 1.5, 3072)))
+    hout = torch.empty(3072, dtype=torch.float16, device="cuda")
+    y = torch.empty(9216, dtype=torch.float16, device="cuda")
+    nb = gemv_bytes(9216, 3072) + 4 * 2 * 3072   # + residual, gamma, residual out
+    us_n = per_launch_us(torch, lambda i: q4.add_rmsnorm_gemv(rot[i], x, res, gam, 1e-5, hout, y), K, W)
+    us_p = per_launch_us(torch, lambda i: q4.gemv(rot[i], x, y), K, W)
+    out["add_rmsnorm_qkv_9216x3072"] = {"us": round(us_n, 3), "plain_gemv_us": round(us_p, 3),
+                                        "gbs": round(nb / us_n / 1e3, 1),
+                                        "frac": round(nb / us_n / 1e3 / PEAK_HBM_GBS, 4),
+                                        "bytes": nb}
+    del rot
+
     # LM head, f32 logits + argmax
     inp = si.workload(si.LM_HEAD, seed=0)
     nb = gemv_bytes(32064, 3072, out_bytes=4) + 4

@@ -196,6 +196,36 @@ int q4_ffn_gate_up_silu(const q4_weight *w, const uint16_t *x, uint16_t *h,
 int q4_lmhead_f32(const q4_weight *w, const uint16_t *x, float *logits,
                   int32_t *argmax, void *ws, int64_t ws_bytes, void *stream);
 
+/*
+ * Residual add + RMSNorm in front of the matmul, fused into its activation
+ * staging ([P1] 内核融合: add_norm merges the residual connection and
+ * RMSNorm; here that step also runs inside the QKV or gate/up matmul that
+ * consumes it, saving its launch and its round trip through memory):
+ *   h_i  = f16(x_i + residual_i)          (residual NULL: h_i = x_i)
+ *   xn_i = f16(h_i * gamma_i / sqrt(mean_k(h^2) + eps))   (f32 arithmetic)
+ *   y    = xn . dequant(W)^T, exactly as q4_gemv computes it from xn
+ *   x, residual, gamma : device f16 [k], 16-byte aligned; residual may be NULL
+ *   eps                : finite, >= 0 (the pages do not give it)
+ *   residual_out       : device f16 [k], 16-byte aligned, or NULL; receives h
+ *                        (the updated residual stream)
+ *   y                  : device f16 [n], 4-byte aligned
+ * No output may overlap an input or the other output (in particular
+ * residual_out != residual: every block reads the residual).
+ * Errors: NULL, SHAPE (also eps < 0 or not finite), ALIGN, LAYOUT, ALIAS, HIP.
+ */
+int q4_add_rmsnorm_gemv(const q4_weight *w, const uint16_t *x, const uint16_t *residual,
+                        const uint16_t *gamma, float eps, uint16_t *residual_out, uint16_t *y,
+                        void *stream);
+
+/*
+ * The same prologue in front of the fused gate/up + SiLU
+ * (q4_ffn_gate_up_silu): h_ffn = SiLU(xn . Wg^T) * (xn . Wu^T), f16 [n],
+ * 2-byte aligned; other arguments as q4_add_rmsnorm_gemv.
+ */
+int q4_add_rmsnorm_ffn_gate_up_silu(const q4_weight *w, const uint16_t *x,
+                                    const uint16_t *residual, const uint16_t *gamma, float eps,
+                                    uint16_t *residual_out, uint16_t *h, void *stream);
+
 /* Static text for a return code. */
 const char *q4_strerror(int code);
 

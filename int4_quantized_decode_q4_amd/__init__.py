@@ -59,6 +59,8 @@ _SIGNATURES = {
     "q4_gemm": (ctypes.c_int, [_W, _P, _I32, _P, _P, _I64, _P]),
     "q4_gemm_path": (ctypes.c_int, [_W, _P, _I32, _P, _I32, _P]),
     "q4_ffn_gate_up_silu": (ctypes.c_int, [_W, _P, _P, _P]),
+    "q4_add_rmsnorm_gemv": (ctypes.c_int, [_W, _P, _P, _P, ctypes.c_float, _P, _P, _P]),
+    "q4_add_rmsnorm_ffn_gate_up_silu": (ctypes.c_int, [_W, _P, _P, _P, ctypes.c_float, _P, _P, _P]),
     "q4_lmhead_f32": (ctypes.c_int, [_W, _P, _P, _P, _P, _I64, _P]),
     "q4_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "q4_last_hip_error": (ctypes.c_int, []),
@@ -226,6 +228,45 @@ def ffn_gate_up_silu(w: PackedWeight, x: torch.Tensor,
     ph = _dev(out, "out", 2, (w.n,))
     _check(_lib.q4_ffn_gate_up_silu(ctypes.byref(w.desc), px, ph, _stream(x)),
            "q4_ffn_gate_up_silu")
+    return out
+
+
+def _norm_args(w: PackedWeight, x, residual, gamma, residual_out):
+    px = _dev(x, "x", 2, (w.k,))
+    pr = None if residual is None else _dev(residual, "residual", 2, (w.k,))
+    pg = _dev(gamma, "gamma", 2, (w.k,))
+    pro = None if residual_out is None else _dev(residual_out, "residual_out", 2, (w.k,))
+    return px, pr, pg, pro
+
+
+def add_rmsnorm_gemv(w: PackedWeight, x: torch.Tensor, residual: Optional[torch.Tensor],
+                     gamma: torch.Tensor, eps: float, residual_out: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y f16 [n] = f16(h * gamma / sqrt(mean(h^2) + eps)) . dequant(W)^T with
+    h = f16(x + residual) (x when residual is None) written to residual_out
+    when given (q4_add_rmsnorm_gemv)."""
+    px, pr, pg, pro = _norm_args(w, x, residual, gamma, residual_out)
+    if out is None:
+        out = torch.empty(w.n, dtype=torch.float16, device=x.device)
+    py = _dev(out, "out", 2, (w.n,))
+    _check(_lib.q4_add_rmsnorm_gemv(ctypes.byref(w.desc), px, pr, pg, float(eps), pro, py,
+                                    _stream(x)), "q4_add_rmsnorm_gemv")
+    return out
+
+
+def add_rmsnorm_ffn_gate_up_silu(w: PackedWeight, x: torch.Tensor,
+                                 residual: Optional[torch.Tensor], gamma: torch.Tensor,
+                                 eps: float, residual_out: Optional[torch.Tensor] = None,
+                                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The same add + RMSNorm prologue in front of the fused gate/up SiLU
+    (q4_add_rmsnorm_ffn_gate_up_silu)."""
+    px, pr, pg, pro = _norm_args(w, x, residual, gamma, residual_out)
+    if out is None:
+        out = torch.empty(w.n, dtype=torch.float16, device=x.device)
+    ph = _dev(out, "out", 2, (w.n,))
+    _check(_lib.q4_add_rmsnorm_ffn_gate_up_silu(ctypes.byref(w.desc), px, pr, pg, float(eps),
+                                                pro, ph, _stream(x)),
+           "q4_add_rmsnorm_ffn_gate_up_silu")
     return out
 
 

@@ -3,6 +3,7 @@
 // stream.  Validation never touches the HIP runtime, so every error path can
 // be exercised on a machine without a GPU.
 #include <stdint.h>
+#include <cmath>
 #include <string.h>
 
 #include <hip/hip_runtime.h>
@@ -192,7 +193,7 @@ int q4_gemv(const q4_weight *w, const uint16_t *x, uint16_t *y, void *stream)
         return Q4_ERR_ALIAS;
     (void)hipGetLastError();
     return hip_status(q4::launch_gemv_family(geo, q4::EPI_F16, w->data, x, y, rows, w->k, w->n,
-                                             q4::ArgmaxScratch{nullptr, nullptr},
+                                             q4::ArgmaxScratch{nullptr, nullptr}, nullptr,
                                              static_cast<hipStream_t>(stream)));
 }
 
@@ -244,7 +245,7 @@ int q4_ffn_gate_up_silu(const q4_weight *w, const uint16_t *x, uint16_t *h, void
         return Q4_ERR_ALIAS;
     (void)hipGetLastError();
     return hip_status(q4::launch_gemv_family(geo, q4::EPI_SILU, w->data, x, h, rows, w->k, w->n,
-                                             q4::ArgmaxScratch{nullptr, nullptr},
+                                             q4::ArgmaxScratch{nullptr, nullptr}, nullptr,
                                              static_cast<hipStream_t>(stream)));
 }
 
@@ -281,7 +282,80 @@ int q4_lmhead_f32(const q4_weight *w, const uint16_t *x, float *logits, int32_t 
         return Q4_ERR_ALIAS;
     (void)hipGetLastError();
     return hip_status(q4::launch_gemv_family(geo, q4::EPI_F32, w->data, x, logits, rows, w->k,
-                                             w->n, am, static_cast<hipStream_t>(stream)));
+                                             w->n, am, nullptr, static_cast<hipStream_t>(stream)));
+}
+
+// Shared checks of the add + RMSNorm entry points; out is y (gemv) or h
+// (ffn), n of them.
+static int check_norm_args(const q4_weight *w, const uint16_t *x, const uint16_t *residual,
+                           const uint16_t *gamma, float eps, const uint16_t *residual_out,
+                           const void *out, int64_t out_bytes)
+{
+    if (!(eps >= 0.f) || !std::isfinite(eps))
+        return Q4_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(gamma, 16) || (residual && !aligned(residual, 16)) ||
+        (residual_out && !aligned(residual_out, 16)))
+        return Q4_ERR_ALIGN;
+    const int64_t kb = 2 * (int64_t)w->k;
+    // outputs overlap no input and not each other
+    const void *ins[4] = {x, residual, gamma, w->data};
+    const int64_t inb[4] = {kb, kb, kb, w->bytes};
+    for (int i = 0; i < 4; ++i) {
+        if (!ins[i])
+            continue;
+        if (overlap(out, out_bytes, ins[i], inb[i]) ||
+            (residual_out && overlap(residual_out, kb, ins[i], inb[i])))
+            return Q4_ERR_ALIAS;
+    }
+    if (residual_out && overlap(residual_out, kb, out, out_bytes))
+        return Q4_ERR_ALIAS;
+    return Q4_OK;
+}
+
+int q4_add_rmsnorm_gemv(const q4_weight *w, const uint16_t *x, const uint16_t *residual,
+                        const uint16_t *gamma, float eps, uint16_t *residual_out, uint16_t *y,
+                        void *stream)
+{
+    q4::Geometry geo;
+    int64_t rows = 0;
+    if (!w || !x || !gamma || !y)
+        return Q4_ERR_NULL;
+    int rc = check_weight(w, Q4_LAYOUT_ROWS, &geo, &rows);
+    if (rc != Q4_OK)
+        return rc;
+    if (!aligned(y, 4))
+        return Q4_ERR_ALIGN;
+    rc = check_norm_args(w, x, residual, gamma, eps, residual_out, y, 2 * (int64_t)w->n);
+    if (rc != Q4_OK)
+        return rc;
+    const q4::NormArgs nm{residual, gamma, residual_out, eps};
+    (void)hipGetLastError();
+    return hip_status(q4::launch_gemv_family(geo, q4::EPI_F16, w->data, x, y, rows, w->k, w->n,
+                                             q4::ArgmaxScratch{nullptr, nullptr}, &nm,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int q4_add_rmsnorm_ffn_gate_up_silu(const q4_weight *w, const uint16_t *x,
+                                    const uint16_t *residual, const uint16_t *gamma, float eps,
+                                    uint16_t *residual_out, uint16_t *h, void *stream)
+{
+    q4::Geometry geo;
+    int64_t rows = 0;
+    if (!w || !x || !gamma || !h)
+        return Q4_ERR_NULL;
+    int rc = check_weight(w, Q4_LAYOUT_GATE_UP, &geo, &rows);
+    if (rc != Q4_OK)
+        return rc;
+    if (!aligned(h, 2))
+        return Q4_ERR_ALIGN;
+    rc = check_norm_args(w, x, residual, gamma, eps, residual_out, h, 2 * (int64_t)w->n);
+    if (rc != Q4_OK)
+        return rc;
+    const q4::NormArgs nm{residual, gamma, residual_out, eps};
+    (void)hipGetLastError();
+    return hip_status(q4::launch_gemv_family(geo, q4::EPI_SILU, w->data, x, h, rows, w->k, w->n,
+                                             q4::ArgmaxScratch{nullptr, nullptr}, &nm,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 const char *q4_strerror(int code)

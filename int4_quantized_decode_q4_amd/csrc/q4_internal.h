@@ -33,9 +33,20 @@ hipError_t launch_pack(const uint32_t *w0, const uint16_t *s0, const uint32_t *w
 hipError_t launch_unpack(const void *src, int64_t rows, int64_t k, const Geometry &geo,
                          uint32_t *words, uint16_t *scales, hipStream_t stream);
 
+// Residual add + RMSNorm applied to x inside a GEMV launch (EPI_F16 and
+// EPI_SILU only): h = f16(x + r) (r may be null), the matmul sees
+// f16(h * gamma / sqrt(mean(h^2) + eps)); h_out (may be null) receives h.
+struct NormArgs {
+    const uint16_t *r;
+    const uint16_t *gamma;
+    uint16_t *h_out;
+    float eps;
+};
+
 hipError_t launch_gemv_family(const Geometry &geo, Epilogue epi, const void *wdata,
                               const uint16_t *x, void *out, int64_t rows, int64_t k,
-                              int64_t n_out, ArgmaxScratch am, hipStream_t stream);
+                              int64_t n_out, ArgmaxScratch am, const NormArgs *norm,
+                              hipStream_t stream);
 
 enum GemmPath { GEMM_PATH_AUTO = 0, GEMM_PATH_VALU = 1, GEMM_PATH_MFMA = 2 };
 

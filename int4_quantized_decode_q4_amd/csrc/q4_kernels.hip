@@ -36,6 +36,7 @@
 namespace q4 {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 
@@ -121,6 +122,16 @@ __global__ void unpack_kernel(const uint8_t *__restrict__ src, int64_t rows, int
 
 // x pairs for one group of 32 k, ordered per word of codes as
 // (x0,x4) (x1,x5) (x2,x6) (x3,x7) to match dot_word's nibble pairs.
+// natural x pairs (x0,x1) (x2,x3) (x4,x5) (x6,x7) of one 8-k word ->
+// (x0,x4) (x1,x5) (x2,x6) (x3,x7), the order the dequant produces
+__device__ __forceinline__ void pair_into(uint32_t *xp, uint4 n)
+{
+    xp[0] = (n.x & 0xFFFFu) | (n.z << 16);
+    xp[1] = (n.x >> 16) | (n.z & 0xFFFF0000u);
+    xp[2] = (n.y & 0xFFFFu) | (n.w << 16);
+    xp[3] = (n.y >> 16) | (n.w & 0xFFFF0000u);
+}
+
 __device__ __forceinline__ void load_x_group(uint32_t *xp, const uint16_t *__restrict__ x,
                                              int64_t g, int64_t G)
 {
@@ -132,12 +143,124 @@ __device__ __forceinline__ void load_x_group(uint32_t *xp, const uint16_t *__res
     }
     const uint4 *src = reinterpret_cast<const uint4 *>(x + g * 32);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {  // q = word of codes, 8 k each
-        const uint4 n = src[q];    // natural pairs (x0,x1) (x2,x3) (x4,x5) (x6,x7)
-        xp[4 * q + 0] = (n.x & 0xFFFFu) | (n.z << 16);
-        xp[4 * q + 1] = (n.x >> 16) | (n.z & 0xFFFF0000u);
-        xp[4 * q + 2] = (n.y & 0xFFFFu) | (n.w << 16);
-        xp[4 * q + 3] = (n.y >> 16) | (n.w & 0xFFFF0000u);
+    for (int q = 0; q < 4; ++q)   // q = word of codes, 8 k each
+        pair_into(xp + 4 * q, src[q]);
+}
+
+// ------------------------------------------------ residual add + RMSNorm --
+// The add_norm step ([P1] 内核融合) run inside the matmul that consumes it:
+// h = f16(x + r), the matmul sees f16(h * gamma / sqrt(mean(h^2) + eps)),
+// all in f32.  Every block computes the mean square over all of k itself
+// (k <= a few thousand halves, from L2), so no launch or grid barrier is
+// needed; block 0 stores h when the caller asks for it.
+
+__device__ __forceinline__ uint4 residual_add8(uint4 xv, uint4 rv)
+{
+    const uint32_t a[4] = {xv.x, xv.y, xv.z, xv.w}, b[4] = {rv.x, rv.y, rv.z, rv.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const h2 p = as_h2(a[i]), q = as_h2(b[i]);
+        // the f32 sum of two f16 is exact: one rounding, to f16
+        const _Float16 lo = (_Float16)((float)p.x + (float)q.x);
+        const _Float16 hi = (_Float16)((float)p.y + (float)q.y);
+        o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__device__ __forceinline__ float sumsq8(uint4 v)
+{
+    const uint32_t a[4] = {v.x, v.y, v.z, v.w};
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const h2 p = as_h2(a[i]);
+        s += (float)p.x * (float)p.x;
+        s += (float)p.y * (float)p.y;
+    }
+    return s;
+}
+
+// f16(h * gamma * inv) of 8 halves; h * gamma is exact in f32
+__device__ __forceinline__ uint4 norm8(uint4 hv, uint4 gv, float inv)
+{
+    const uint32_t a[4] = {hv.x, hv.y, hv.z, hv.w}, b[4] = {gv.x, gv.y, gv.z, gv.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const h2 p = as_h2(a[i]), q = as_h2(b[i]);
+        const _Float16 lo = (_Float16)((float)p.x * (float)q.x * inv);
+        const _Float16 hi = (_Float16)((float)p.y * (float)q.y * inv);
+        o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__device__ __forceinline__ uint4 as_uint4(v4u v) { return make_uint4(v.x, v.y, v.z, v.w); }
+
+__device__ __forceinline__ float inv_rms(float sumsq, int64_t k, float eps)
+{
+    return 1.0f / sqrtf(sumsq / (float)k + eps);
+}
+
+// Sum of one value per thread over the block, in a fixed order (every thread
+// gets the same bits).  scratch: 16 floats of LDS.
+__device__ float block_sum(float v, float *scratch)
+{
+    v = lanes::reduce<64>(v);
+    const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    __syncthreads();   // a previous use of scratch has been read
+    if ((threadIdx.x & 63) == 0)
+        scratch[w] = v;
+    __syncthreads();
+    float t = 0.f;
+    for (int i = 0; i < nw; ++i)
+        t += scratch[i];
+    return t;
+}
+
+// 1 / sqrt(mean(h^2) + eps) over all of k, by the whole block from global
+// memory; block 0 also stores h when asked.
+__device__ float norm_prepass(const uint16_t *__restrict__ x, const NormArgs &nm, int64_t k,
+                              float *scratch)
+{
+    const uint4 *x4 = reinterpret_cast<const uint4 *>(x);
+    const uint4 *r4 = reinterpret_cast<const uint4 *>(nm.r);
+    uint4 *h4 = reinterpret_cast<uint4 *>(nm.h_out);
+    float ss = 0.f;
+    for (int64_t i = threadIdx.x; i < k / 8; i += blockDim.x) {
+        uint4 h = x4[i];
+        if (r4 != nullptr)
+            h = residual_add8(h, r4[i]);
+        ss += sumsq8(h);
+        if (h4 != nullptr && blockIdx.x == 0)
+            h4[i] = h;
+    }
+    return inv_rms(block_sum(ss, scratch), k, nm.eps);
+}
+
+// The normalised x pairs of group g (zeros past the end).
+__device__ __forceinline__ void norm_x_group(uint32_t *xp, const uint16_t *__restrict__ x,
+                                             const NormArgs &nm, float inv, int64_t g, int64_t G)
+{
+    if (g >= G) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            xp[i] = 0u;
+        return;
+    }
+    const uint4 *x4 = reinterpret_cast<const uint4 *>(x + g * 32);
+    const uint4 *r4 = reinterpret_cast<const uint4 *>(nm.r + g * 32);
+    const uint4 *g4 = reinterpret_cast<const uint4 *>(nm.gamma + g * 32);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint4 h = x4[q];
+        if (nm.r != nullptr)
+            h = residual_add8(h, r4[q]);
+        pair_into(xp + 4 * q, norm8(h, g4[q], inv));
     }
 }
 
@@ -363,7 +486,6 @@ constexpr int kBlockWaves = Q4_BLOCK_WAVES;
 // num_records is the tile's byte size, or 0 when the wavefront has no such
 // tile; buffer loads past num_records return zeros without touching memory,
 // so prefetches need no branch and the compiler's vmcnt waits stay exact.
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
 constexpr int kBufferWord3 = 0x00020000;   // gfx9-family raw buffer format
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base, int bytes)
@@ -445,19 +567,14 @@ __device__ __forceinline__ void lds_x_group(uint32_t *xp, const uint4 *xs, int64
         return;
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint4 n = xs[g * 4 + q];
-        xp[4 * q + 0] = (n.x & 0xFFFFu) | (n.z << 16);
-        xp[4 * q + 1] = (n.x >> 16) | (n.z & 0xFFFF0000u);
-        xp[4 * q + 2] = (n.y & 0xFFFFu) | (n.w << 16);
-        xp[4 * q + 3] = (n.y >> 16) | (n.w & 0xFFFF0000u);
-    }
+    for (int q = 0; q < 4; ++q)
+        pair_into(xp + 4 * q, xs[g * 4 + q]);
 }
 
-template <int L, int CG, int EPI>
+template <int L, int CG, int EPI, bool NORM>
 __global__ __launch_bounds__(64 * kBlockWaves) void gemv_block_kernel(
     const uint8_t *__restrict__ wd, const uint16_t *__restrict__ x, void *__restrict__ out,
-    int64_t rows, int64_t k, int64_t tiles, int64_t n_out, ArgmaxScratch am)
+    int64_t rows, int64_t k, int64_t tiles, int64_t n_out, ArgmaxScratch am, NormArgs nm)
 {
     constexpr int PD = Q4_STREAM_DEPTH < 2 * CG ? Q4_STREAM_DEPTH : 2 * CG;
     constexpr int64_t PB = (int64_t)CG * 2304;
@@ -485,6 +602,20 @@ __global__ __launch_bounds__(64 * kBlockWaves) void gemv_block_kernel(
     for (int q = 0; q < kXRounds; ++q)
         if (q < xrounds)
             xv[q] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (threadIdx.x + kThreads * q) * 16, 0, 0);
+    // with the norm: the residual (a zero-size resource when there is none)
+    // and gamma, requested with x
+    v4u rv[NORM ? kXRounds : 1], gv[NORM ? kXRounds : 1];
+    if constexpr (NORM) {
+        const __amdgpu_buffer_rsrc_t rrs =
+            tile_rsrc(reinterpret_cast<const uint8_t *>(nm.r), nm.r != nullptr ? (int)(k * 2) : 0);
+        const __amdgpu_buffer_rsrc_t grs = tile_rsrc(reinterpret_cast<const uint8_t *>(nm.gamma), (int)(k * 2));
+#pragma unroll
+        for (int q = 0; q < kXRounds; ++q)
+            if (q < xrounds) {
+                rv[q] = __builtin_amdgcn_raw_buffer_load_b128(rrs, (threadIdx.x + kThreads * q) * 16, 0, 0);
+                gv[q] = __builtin_amdgcn_raw_buffer_load_b128(grs, (threadIdx.x + kThreads * q) * 16, 0, 0);
+            }
+    }
     int64_t t = (int64_t)blockIdx.x * kBlockWaves + w;
     const int64_t step = (int64_t)gridDim.x * kBlockWaves;
     auto rs_of = [&](int64_t tt) {
@@ -498,10 +629,44 @@ __global__ __launch_bounds__(64 * kBlockWaves) void gemv_block_kernel(
         for (int i = 0; i < PD; ++i)
             load_unit(ra, r0, lane, i);
     }
+    // with the norm: each thread keeps its chunks of h in registers and
+    // parks its wavefront's part of the sum of squares in LDS; after one
+    // barrier every thread has the block's sum, normalises its own chunks
+    // into LDS, and the staging barrier below publishes them
+    if constexpr (NORM) {
+        __shared__ float nss[kBlockWaves];
+        uint4 hv[kXRounds];
+        float ss = 0.f;
 #pragma unroll
-    for (int q = 0; q < kXRounds; ++q)
-        if (q < xrounds)
-            xs[threadIdx.x + kThreads * q] = make_uint4(xv[q].x, xv[q].y, xv[q].z, xv[q].w);
+        for (int q = 0; q < kXRounds; ++q)
+            if (q < xrounds) {   // chunks past k read as zero and add nothing
+                hv[q] = as_uint4(xv[q]);
+                if (nm.r != nullptr)
+                    hv[q] = residual_add8(hv[q], as_uint4(rv[q]));
+                ss += sumsq8(hv[q]);
+                const int64_t ci = threadIdx.x + kThreads * q;
+                if (nm.h_out != nullptr && blockIdx.x == 0 && ci < k / 8)
+                    reinterpret_cast<uint4 *>(nm.h_out)[ci] = hv[q];
+            }
+        ss = lanes::reduce<64>(ss);
+        if (lane == 0)
+            nss[w] = ss;
+        __syncthreads();
+        float tot = 0.f;
+#pragma unroll
+        for (int i = 0; i < kBlockWaves; ++i)
+            tot += nss[i];
+        const float inv = inv_rms(tot, k, nm.eps);
+#pragma unroll
+        for (int q = 0; q < kXRounds; ++q)
+            if (q < xrounds)
+                xs[threadIdx.x + kThreads * q] = norm8(hv[q], as_uint4(gv[q]), inv);
+    } else {
+#pragma unroll
+        for (int q = 0; q < kXRounds; ++q)
+            if (q < xrounds)
+                xs[threadIdx.x + kThreads * q] = as_uint4(xv[q]);
+    }
     __syncthreads();
     uint32_t xp[CG][16];
 #pragma unroll
@@ -543,10 +708,10 @@ constexpr int kSplitMaxTiles = 8;
 #define Q4_SPLIT_DEPTH 2
 #endif
 
-template <int L, int CG, int EPI>
+template <int L, int CG, int EPI, bool NORM>
 __global__ __launch_bounds__(64 * CG) void gemv_split_kernel(
     const uint8_t *__restrict__ wd, const uint16_t *__restrict__ x, void *__restrict__ out,
-    int64_t rows, int64_t k, int64_t tiles, int64_t n_out, ArgmaxScratch am)
+    int64_t rows, int64_t k, int64_t tiles, int64_t n_out, ArgmaxScratch am, NormArgs nm)
 {
     constexpr int HP = 64 / L;   // row pairs per tile
     constexpr int TR = 128 / L;
@@ -557,7 +722,8 @@ __global__ __launch_bounds__(64 * CG) void gemv_split_kernel(
     const int j = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int s = lane / L, c = lane % L;
     uint32_t xp[16];
-    load_x_group(xp, x, (int64_t)c * CG + j, k >> 5);
+    if constexpr (!NORM)
+        load_x_group(xp, x, (int64_t)c * CG + j, k >> 5);
     const DequantConsts m = dequant_consts();
     const int64_t count =
         (int64_t)blockIdx.x < tiles ? (tiles - 1 - (int64_t)blockIdx.x) / gridDim.x + 1 : 0;
@@ -582,6 +748,13 @@ __global__ __launch_bounds__(64 * CG) void gemv_split_kernel(
 #pragma unroll
     for (int q = 0; q < D; ++q)
         load(ring[q], q);
+    if constexpr (NORM) {
+        // after the first tiles are requested: the block's pass over x for
+        // the mean square, then this lane's group, normalised
+        __shared__ float nscr[16];
+        const float inv = norm_prepass(x, nm, k, nscr);
+        norm_x_group(xp, x, nm, inv, (int64_t)c * CG + j, k >> 5);
+    }
     for (int64_t i0 = 0; i0 < count; i0 += D) {
 #pragma unroll
         for (int q = 0; q < D; ++q) {
@@ -630,10 +803,11 @@ __global__ __launch_bounds__(64 * CG) void gemv_split_kernel(
 
 // Multi-pass kernel (k > 8192): a grid-stride loop over tiles that reloads
 // the x slice for every pass.
-template <int L, int CG, int EPI>
+template <int L, int CG, int EPI, bool NORM>
 __global__ __launch_bounds__(256) void gemv_multipass_kernel(
     const uint8_t *__restrict__ wd, const uint16_t *__restrict__ x, void *__restrict__ out,
-    int64_t rows, int64_t k, int passes, int64_t tiles, int64_t n_out, ArgmaxScratch am)
+    int64_t rows, int64_t k, int passes, int64_t tiles, int64_t n_out, ArgmaxScratch am,
+    NormArgs nm)
 {
     constexpr int64_t PB = (int64_t)CG * 2304;
     const int lane = threadIdx.x & 63;
@@ -643,6 +817,11 @@ __global__ __launch_bounds__(256) void gemv_multipass_kernel(
     float bv = -INFINITY;
     int bi = 0x7fffffff;
     const DequantConsts m = dequant_consts();
+    float inv = 0.f;
+    if constexpr (NORM) {
+        __shared__ float nscr[16];
+        inv = norm_prepass(x, nm, k, nscr);
+    }
     for (int64_t t = wave; t < tiles; t += nwaves) {
         float acc[2] = {0.f, 0.f};
         for (int p = 0; p < passes; ++p) {
@@ -650,8 +829,13 @@ __global__ __launch_bounds__(256) void gemv_multipass_kernel(
             load_tile(r, wd + (t * passes + p) * PB, lane);
             uint32_t xp[CG][16];
 #pragma unroll
-            for (int j = 0; j < CG; ++j)
-                load_x_group(xp[j], x, (int64_t)p * L * CG + (int64_t)c * CG + j, k >> 5);
+            for (int j = 0; j < CG; ++j) {
+                const int64_t g = (int64_t)p * L * CG + (int64_t)c * CG + j;
+                if constexpr (NORM)
+                    norm_x_group(xp[j], x, nm, inv, g, k >> 5);
+                else
+                    load_x_group(xp[j], x, g, k >> 5);
+            }
             compute_tile(r, xp, acc, m);
         }
         finish_tile<L, EPI>(acc, t, s, c, out, rows, n_out, bv, bi);
@@ -743,65 +927,83 @@ struct GemvArgs {
     int64_t rows, k, n_out;
     const Geometry *geo;
     ArgmaxScratch am;
+    NormArgs nm;
 };
 
-template <int L, int CG, int EPI>
-static void launch_lce(const GemvPlan &plan, const GemvArgs &a, hipStream_t stream)
+template <int L, int CG, int EPI, bool NORM>
+static void launch_lcen(const GemvPlan &plan, const GemvArgs &a, hipStream_t stream)
 {
     const dim3 grid((unsigned)plan.blocks), block((unsigned)plan.threads);
     switch (plan.mode) {
     case MODE_SPLIT:
-        hipLaunchKernelGGL((gemv_split_kernel<L, CG, EPI>), grid, block, 0, stream, a.wd, a.x, a.out,
-                           a.rows, a.k, a.geo->tiles, a.n_out, a.am);
+        hipLaunchKernelGGL((gemv_split_kernel<L, CG, EPI, NORM>), grid, block, 0, stream, a.wd, a.x,
+                           a.out, a.rows, a.k, a.geo->tiles, a.n_out, a.am, a.nm);
         break;
     case MODE_MULTIPASS:
-        hipLaunchKernelGGL((gemv_multipass_kernel<L, CG, EPI>), grid, block, 0, stream, a.wd, a.x,
-                           a.out, a.rows, a.k, a.geo->P, a.geo->tiles, a.n_out, a.am);
+        hipLaunchKernelGGL((gemv_multipass_kernel<L, CG, EPI, NORM>), grid, block, 0, stream, a.wd,
+                           a.x, a.out, a.rows, a.k, a.geo->P, a.geo->tiles, a.n_out, a.am, a.nm);
         break;
     case MODE_BLOCK:
-        hipLaunchKernelGGL((gemv_block_kernel<L, CG, EPI>), grid, block, 0, stream, a.wd, a.x, a.out,
-                           a.rows, a.k, a.geo->tiles, a.n_out, a.am);
+        hipLaunchKernelGGL((gemv_block_kernel<L, CG, EPI, NORM>), grid, block, 0, stream, a.wd, a.x,
+                           a.out, a.rows, a.k, a.geo->tiles, a.n_out, a.am, a.nm);
         break;
     }
 }
 
 template <int L, int CG>
-static void launch_lc(Epilogue epi, const GemvPlan &plan, const GemvArgs &a, hipStream_t stream)
+static void launch_lc(Epilogue epi, bool norm, const GemvPlan &plan, const GemvArgs &a,
+                      hipStream_t stream)
 {
     switch (epi) {
-    case EPI_F16: launch_lce<L, CG, EPI_F16>(plan, a, stream); break;
-    case EPI_F32: launch_lce<L, CG, EPI_F32>(plan, a, stream); break;
-    case EPI_SILU: launch_lce<L, CG, EPI_SILU>(plan, a, stream); break;
+    case EPI_F16:
+        if (norm)
+            launch_lcen<L, CG, EPI_F16, true>(plan, a, stream);
+        else
+            launch_lcen<L, CG, EPI_F16, false>(plan, a, stream);
+        break;
+    case EPI_F32: launch_lcen<L, CG, EPI_F32, false>(plan, a, stream); break;
+    case EPI_SILU:
+        if (norm)
+            launch_lcen<L, CG, EPI_SILU, true>(plan, a, stream);
+        else
+            launch_lcen<L, CG, EPI_SILU, false>(plan, a, stream);
+        break;
     }
 }
 
 template <int L>
-static bool launch_l(Epilogue epi, const GemvPlan &plan, const GemvArgs &a, hipStream_t stream)
+static bool launch_l(Epilogue epi, bool norm, const GemvPlan &plan, const GemvArgs &a,
+                     hipStream_t stream)
 {
     switch (a.geo->CG) {
-    case 1: launch_lc<L, 1>(epi, plan, a, stream); return true;
-    case 2: launch_lc<L, 2>(epi, plan, a, stream); return true;
-    case 3: launch_lc<L, 3>(epi, plan, a, stream); return true;
-    case 4: launch_lc<L, 4>(epi, plan, a, stream); return true;
+    case 1: launch_lc<L, 1>(epi, norm, plan, a, stream); return true;
+    case 2: launch_lc<L, 2>(epi, norm, plan, a, stream); return true;
+    case 3: launch_lc<L, 3>(epi, norm, plan, a, stream); return true;
+    case 4: launch_lc<L, 4>(epi, norm, plan, a, stream); return true;
     }
     return false;
 }
 
 hipError_t launch_gemv_family(const Geometry &geo, Epilogue epi, const void *wdata,
                               const uint16_t *x, void *out, int64_t rows, int64_t k,
-                              int64_t n_out, ArgmaxScratch am, hipStream_t stream)
+                              int64_t n_out, ArgmaxScratch am, const NormArgs *norm,
+                              hipStream_t stream)
 {
+    if (norm != nullptr && epi == EPI_F32)
+        return hipErrorInvalidValue;   // the LM head takes no norm prologue
     const GemvPlan plan = plan_gemv(geo);
-    const GemvArgs a{static_cast<const uint8_t *>(wdata), x, out, rows, k, n_out, &geo, am};
+    const GemvArgs a{static_cast<const uint8_t *>(wdata), x, out, rows, k, n_out, &geo, am,
+                     norm != nullptr ? *norm : NormArgs{nullptr, nullptr, nullptr, 0.f}};
+    const bool nrm = norm != nullptr;
     bool ok = false;
     switch (geo.L) {
-    case 64: ok = launch_l<64>(epi, plan, a, stream); break;
-    case 32: ok = launch_l<32>(epi, plan, a, stream); break;
-    case 16: ok = launch_l<16>(epi, plan, a, stream); break;
-    case 8: ok = launch_l<8>(epi, plan, a, stream); break;
-    case 4: ok = launch_l<4>(epi, plan, a, stream); break;
-    case 2: ok = launch_l<2>(epi, plan, a, stream); break;
-    case 1: ok = launch_l<1>(epi, plan, a, stream); break;
+    case 64: ok = launch_l<64>(epi, nrm, plan, a, stream); break;
+    case 32: ok = launch_l<32>(epi, nrm, plan, a, stream); break;
+    case 16: ok = launch_l<16>(epi, nrm, plan, a, stream); break;
+    case 8: ok = launch_l<8>(epi, nrm, plan, a, stream); break;
+    case 4: ok = launch_l<4>(epi, nrm, plan, a, stream); break;
+    case 2: ok = launch_l<2>(epi, nrm, plan, a, stream); break;
+    case 1: ok = launch_l<1>(epi, nrm, plan, a, stream); break;
     }
     if (!ok)
         return hipErrorInvalidValue;

@@ -116,6 +116,37 @@ def test_gemv_family_errors(q4):
     assert lib.q4_ffn_gate_up_silu(ctypes.byref(gu), X, Y + 1, None) == q4.ERR_ALIGN
 
 
+def test_add_rmsnorm_errors(q4):
+    lib = q4.lib
+    X, R, Gm, H, Y = A + 0x200000, A + 0x210000, A + 0x220000, A + 0x230000, A + 0x300000
+    w = weight(q4)
+    r = ctypes.byref(w)
+    f = lib.q4_add_rmsnorm_gemv
+    assert f(None, X, R, Gm, 1e-5, H, Y, None) == q4.ERR_NULL
+    assert f(r, None, R, Gm, 1e-5, H, Y, None) == q4.ERR_NULL
+    assert f(r, X, R, None, 1e-5, H, Y, None) == q4.ERR_NULL
+    assert f(r, X, R, Gm, 1e-5, H, None, None) == q4.ERR_NULL
+    assert f(r, X, R, Gm, -1.0, H, Y, None) == q4.ERR_SHAPE
+    assert f(r, X, R, Gm, float("nan"), H, Y, None) == q4.ERR_SHAPE
+    assert f(r, X, R, Gm, float("inf"), H, Y, None) == q4.ERR_SHAPE
+    assert f(r, X + 8, R, Gm, 1e-5, H, Y, None) == q4.ERR_ALIGN
+    assert f(r, X, R + 8, Gm, 1e-5, H, Y, None) == q4.ERR_ALIGN
+    assert f(r, X, R, Gm + 2, 1e-5, H, Y, None) == q4.ERR_ALIGN
+    assert f(r, X, R, Gm, 1e-5, H + 8, Y, None) == q4.ERR_ALIGN
+    assert f(r, X, R, Gm, 1e-5, H, Y + 2, None) == q4.ERR_ALIGN
+    assert f(r, X, R, Gm, 1e-5, R, Y, None) == q4.ERR_ALIAS        # residual updated in place
+    assert f(r, X, R, Gm, 1e-5, H, Gm + 64, None) == q4.ERR_ALIAS  # y over gamma
+    assert f(r, X, R, Gm, 1e-5, H, H + 64, None) == q4.ERR_ALIAS   # the two outputs
+    assert f(r, X, R, Gm, 1e-5, X + 32, Y, None) == q4.ERR_ALIAS   # residual_out over x
+    assert f(ctypes.byref(weight(q4, layout=2)), X, R, Gm, 1e-5, H, Y, None) == q4.ERR_LAYOUT
+    g = lib.q4_add_rmsnorm_ffn_gate_up_silu
+    gu = ctypes.byref(weight(q4, layout=2))
+    assert g(r, X, R, Gm, 1e-5, H, Y, None) == q4.ERR_LAYOUT
+    assert g(gu, X, R, Gm, -0.5, H, Y, None) == q4.ERR_SHAPE
+    assert g(gu, X, R, Gm, 1e-5, H, Y + 1, None) == q4.ERR_ALIGN
+    assert g(gu, X, R, Gm, 1e-5, H, X, None) == q4.ERR_ALIAS
+
+
 def test_lmhead_errors(q4):
     lib = q4.lib
     X, L, I, WS = A + 0x200000, A + 0x300000, A + 0x400000, A + 0x500000

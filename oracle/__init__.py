@@ -69,6 +69,14 @@ class Oracle:
         lib.q4o_ffn_gate_up_silu.restype = ctypes.c_int
         lib.q4o_add_rmsnorm.argtypes = [_P, _P, _P, _I64, ctypes.c_double, _P, _P]
         lib.q4o_add_rmsnorm.restype = ctypes.c_int
+        lib.q4o_rope_pair.argtypes = [ctypes.c_double, ctypes.c_double, _I64, _I64, _I64,
+                                      ctypes.c_double, _P, _P]
+        lib.q4o_rope_pair.restype = None
+        lib.q4o_qkv_rope.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, ctypes.c_double,
+                                     _P, _P]
+        lib.q4o_qkv_rope.restype = ctypes.c_int
+        lib.q4o_encode_rope.argtypes = [_P, _P, _I64, _I64, _I64, _P]
+        lib.q4o_encode_rope.restype = ctypes.c_int
         lib.q4o_argmax.argtypes = [_P, _I64]
         lib.q4o_argmax.restype = ctypes.c_int64
         lib.q4o_lmhead.argtypes = [_P, _P, _P, _I64, _I64, _P, _P]
@@ -171,6 +179,26 @@ class Oracle:
         assert rc == 0
         return h, xn
 
+    def rope_pair(self, yi: float, yj: float, i: int, d: int, pos: int, base: float):
+        oi, oj = ctypes.c_double(), ctypes.c_double()
+        self.lib.q4o_rope_pair(float(yi), float(yj), i, d, pos, float(base),
+                               ctypes.addressof(oi), ctypes.addressof(oj))
+        return oi.value, oj.value
+
+    def qkv_rope(self, words, scales, x, d: int, nq: int, pos: int, base: float):
+        """(y f64 [n] with RoPE on the q and k heads, a f64 [n])."""
+        n = words.shape[0]
+        k = x.shape[0]
+        self._check_w(words, scales, n, k)
+        words, scales = np.ascontiguousarray(words), np.ascontiguousarray(scales)
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        y = np.empty(n, np.float64)
+        a = np.empty(n, np.float64)
+        rc = self.lib.q4o_qkv_rope(_ptr(words), _ptr(scales), _ptr(x), n, k, d, nq, pos,
+                                   float(base), _ptr(y), _ptr(a))
+        assert rc == 0
+        return y, a
+
     def argmax(self, v) -> int:
         v = np.ascontiguousarray(v, dtype=np.float64)
         return int(self.lib.q4o_argmax(_ptr(v), v.size))
@@ -205,6 +233,15 @@ class Oracle:
         words, scales = np.ascontiguousarray(words), np.ascontiguousarray(scales)
         dst = np.full(self.layout_bytes(n, k), 0xA5, np.uint8)
         rc = self.lib.q4o_encode_rows(_ptr(words), _ptr(scales), n, k, _ptr(dst))
+        assert rc == 0
+        return dst
+
+    def encode_rope(self, words, scales, d: int) -> np.ndarray:
+        n, k = words.shape[0], words.shape[1] * 8
+        self._check_w(words, scales, n, k)
+        words, scales = np.ascontiguousarray(words), np.ascontiguousarray(scales)
+        dst = np.full(self.layout_bytes(n, k), 0xA5, np.uint8)
+        rc = self.lib.q4o_encode_rope(_ptr(words), _ptr(scales), n, k, d, _ptr(dst))
         assert rc == 0
         return dst
 

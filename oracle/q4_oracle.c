@@ -231,6 +231,51 @@ int q4o_add_rmsnorm(const uint16_t *x, const uint16_t *r, const uint16_t *gamma,
     return 0;
 }
 
+/*
+ * Rotary position embedding of one pair of head dims ([P1] 完整的推理流水线:
+ * RoPE is computed in place inside the fused QKV kernel).  The pages give
+ * neither the pairing nor the base; the reading is Phi-3's: dim i of a head
+ * d wide is paired with dim i + d/2 ("rotate half"), angle
+ * pos * base^(-2i/d), and
+ *   out_i = y_i cos - y_j sin,   out_j = y_j cos + y_i sin   (j = i + d/2).
+ */
+void q4o_rope_pair(double yi, double yj, int64_t i, int64_t d, int64_t pos,
+                   double base, double *oi, double *oj)
+{
+    const double ang = (double)pos * pow(base, -2.0 * (double)i / (double)d);
+    const double c = cos(ang), s = sin(ang);
+    *oi = yi * c - yj * s;
+    *oj = yj * c + yi * s;
+}
+
+/*
+ * The fused QKV step ([P1] 内核融合: qkv_fused merges the Q/K/V projection,
+ * RoPE and the paged KV-cache append): y = x . dequant(W)^T over rows
+ * [nq q heads | nkv k heads | nkv v heads], each head d rows, then RoPE on
+ * the q and k heads; v is left as is.  nkv = (n/d - nq) / 2.  y, a: f64 [n];
+ * a[r] is row r's magnitude sum before the rotation.  Returns 0 or -1.
+ */
+int q4o_qkv_rope(const uint32_t *words, const uint16_t *scales, const uint16_t *x,
+                 int64_t n, int64_t k, int64_t d, int64_t nq, int64_t pos, double base,
+                 double *y, double *a)
+{
+    if (d < 2 || d % 2 || n % d || nq < 0)
+        return -1;
+    const int64_t heads = n / d, nkv = (heads - nq) / 2;
+    if (nkv < 0 || nq + 2 * nkv != heads)
+        return -1;
+    if (q4o_gemv(words, scales, x, n, k, y, a))
+        return -1;
+    for (int64_t h = 0; h < nq + nkv; ++h)   /* q heads, then k heads */
+        for (int64_t i = 0; i < d / 2; ++i) {
+            double oi, oj;
+            q4o_rope_pair(y[h * d + i], y[h * d + i + d / 2], i, d, pos, base, &oi, &oj);
+            y[h * d + i] = oi;
+            y[h * d + i + d / 2] = oj;
+        }
+    return 0;
+}
+
 /* greedy argmax ([P1] 完整的推理流水线, 贪婪解码采样): the lowest index that
  * holds the maximum.  Returns -1 for n < 1. */
 int64_t q4o_argmax(const double *v, int64_t n)
@@ -347,11 +392,13 @@ static void place(uint8_t *dst, int64_t r, int64_t g, int L, int CG,
     memcpy(scale_dst, &src_scale, 2);
 }
 
-/* shared walk: logical row r is produced by `pick` (gate/up interleave or
- * plain rows) */
+/* shared walk over the logical rows r of the layout; the canonical row
+ * behind r: plain (mode 0), gate/up interleave (mode 1: 2i = gate i, 2i+1 =
+ * up i), or rotary pairs (mode 2, heads d wide: 2p + u = dim p % (d/2) +
+ * u d/2 of head p / (d/2)) */
 static int encode(const uint32_t *w0, const uint16_t *s0, const uint32_t *w1,
                   const uint16_t *s1, int64_t rows, int64_t k, int interleave,
-                  uint8_t *dst)
+                  int64_t d, uint8_t *dst)
 {
     int64_t geo[6];
     if (q4o_layout_geometry(rows, k, geo))
@@ -363,10 +410,15 @@ static int encode(const uint32_t *w0, const uint16_t *s0, const uint32_t *w1,
         const uint32_t *rw = NULL;
         const uint16_t *rs = NULL;
         if (r < rows) {
-            if (interleave) {
+            if (interleave == 1) {
                 int64_t i = r / 2;
                 rw = (r % 2 ? w1 : w0) + i * (k / 8);
                 rs = (r % 2 ? s1 : s0) + i * G;
+            } else if (interleave == 2) {
+                int64_t pr = r / 2, u = r % 2;
+                int64_t src = (pr / (d / 2)) * d + pr % (d / 2) + u * (d / 2);
+                rw = w0 + src * (k / 8);
+                rs = s0 + src * G;
             } else {
                 rw = w0 + r * (k / 8);
                 rs = s0 + r * G;
@@ -386,7 +438,7 @@ static int encode(const uint32_t *w0, const uint16_t *s0, const uint32_t *w1,
 int q4o_encode_rows(const uint32_t *words, const uint16_t *scales, int64_t n,
                     int64_t k, uint8_t *dst)
 {
-    return encode(words, scales, NULL, NULL, n, k, 0, dst);
+    return encode(words, scales, NULL, NULL, n, k, 0, 0, dst);
 }
 
 /* gate/up interleaved layout: 2n logical rows */
@@ -394,5 +446,15 @@ int q4o_encode_gate_up(const uint32_t *gw, const uint16_t *gs,
                        const uint32_t *uw, const uint16_t *us, int64_t n,
                        int64_t k, uint8_t *dst)
 {
-    return encode(gw, gs, uw, us, 2 * n, k, 1, dst);
+    return encode(gw, gs, uw, us, 2 * n, k, 1, 0, dst);
+}
+
+/* rotary-pair layout of words [n][k/8], scales [n][k/32]: heads of d rows
+ * (d even, n % d == 0), dims i and i + d/2 of a head on logical rows 2p, 2p+1 */
+int q4o_encode_rope(const uint32_t *words, const uint16_t *scales, int64_t n,
+                    int64_t k, int64_t d, uint8_t *dst)
+{
+    if (d < 2 || d % 2 || n % d)
+        return -1;
+    return encode(words, scales, NULL, NULL, n, k, 2, d, dst);
 }

@@ -18,6 +18,10 @@ What pins what:
   * SiLU / FFN    : silu(0)=0, silu(ln 3)=(3/4)ln 3, silu(-g)=silu(g)-g, the
                     gate (not up) is the one gated.
   * argmax        : planted maximum, ties go to the lowest index.
+  * RoPE          : a hand example (pairing and frequency), identity at 0,
+                    norm preservation, q.k depends on the position difference
+                    only, only q and k heads of the fused QKV rotate; the
+                    rotary-pair layout decoded in the opposite direction.
   * add + RMSNorm : a hand example (x = (3, 4)), the residual against numpy's
                     f16 addition, constant inputs (+-1, and 1/sqrt(2) with
                     eps = mean square), scale invariance, exact gamma scaling.
@@ -325,6 +329,65 @@ def pin_add_rmsnorm(orc, quick=False):
     assert np.array_equal(xn, want.view(np.uint16))
 
 
+def pin_rope(orc, quick=False):
+    """RoPE: a hand example (which dims pair, which frequency), identity at
+    position 0, norm preservation, the relative-position property of q.k, and
+    which heads of the fused QKV output rotate."""
+    base = 10000.0
+    # head of 4 dims, position 1: pair (0, 2) turns by 1 rad, pair (1, 3) by
+    # 10000^(-2/4) = 0.01 rad; a unit vector on dim 0 lands on (cos 1, sin 1)
+    assert orc.rope_pair(1.0, 0.0, 0, 4, 1, base) == (math.cos(1.0), math.sin(1.0))
+    oi, oj = orc.rope_pair(0.0, 1.0, 1, 4, 1, base)
+    assert abs(oi + math.sin(0.01)) < 1e-15 and abs(oj - math.cos(0.01)) < 1e-15
+    rng = np.random.default_rng(37)
+    for _ in range(20):
+        yi, yj = rng.normal(size=2)
+        i, pos = int(rng.integers(0, 48)), int(rng.integers(0, 4096))
+        assert orc.rope_pair(yi, yj, i, 96, 0, base) == (yi, yj)
+        oi, oj = orc.rope_pair(yi, yj, i, 96, pos, base)
+        assert abs((oi * oi + oj * oj) - (yi * yi + yj * yj)) <= 1e-12 * (yi * yi + yj * yj)
+
+    def rot(v, pos):
+        out = np.empty_like(v)
+        for i in range(48):
+            out[i], out[i + 48] = orc.rope_pair(v[i], v[i + 48], i, 96, pos, base)
+        return out
+
+    q, kk = rng.normal(size=96), rng.normal(size=96)
+    for p1, p2, t in ((5, 3, 100), (0, 77, 1000), (2000, 1999, 17)):
+        d0 = float(rot(q, p1) @ rot(kk, p2))
+        d1 = float(rot(q, p1 + t) @ rot(kk, p2 + t))
+        assert abs(d0 - d1) <= 1e-9 * (abs(d0) + 1.0)
+    # fused QKV: 2 q heads, 1 k head, 1 v head of 8 dims; position 0 is the
+    # plain matmul; elsewhere v is untouched and q, k are the rotated rows
+    d, nq = 8, 2
+    n, k = 4 * d, 64
+    w, s = si.draw_weight(rng, n, k)
+    x = si.draw_x(rng, k)
+    y_plain, a_plain = orc.gemv(w, s, x)
+    y0, a0 = orc.qkv_rope(w, s, x, d, nq, 0, base)
+    assert np.array_equal(y0, y_plain) and np.array_equal(a0, a_plain)
+    y5, _ = orc.qkv_rope(w, s, x, d, nq, 5, base)
+    assert np.array_equal(y5[3 * d:], y_plain[3 * d:])
+    for h in range(3):
+        for i in range(d // 2):
+            want = orc.rope_pair(y_plain[h * d + i], y_plain[h * d + i + d // 2], i, d, 5, base)
+            assert (y5[h * d + i], y5[h * d + i + d // 2]) == want
+
+
+def pin_rope_layout(orc, quick=False):
+    """Rotary-pair layout: decoded in the opposite direction, logical row
+    2p + u holds dim p % (d/2) + u d/2 of head p / (d/2)."""
+    rng = np.random.default_rng(41)
+    for n, k, d in ((96, 64, 96), (48, 3072, 8), (24, 96, 12)):
+        w, s = si.draw_weight(rng, n, k)
+        geo = orc.layout_geometry(n, k)
+        dw, ds = decode_layout(orc.encode_rope(w, s, d), n, k, **geo)
+        src = np.array([(r // 2 // (d // 2)) * d + (r // 2) % (d // 2) + (r % 2) * (d // 2)
+                        for r in range(n)])
+        assert np.array_equal(dw[:n, :k // 8], w[src]) and np.array_equal(ds[:n, :k // 32], s[src])
+
+
 def load_geometry_golden():
     rows = []
     with open(os.path.join(GOLDEN, "layout_geometry.txt")) as f:
@@ -412,6 +475,6 @@ ALL_PINS = [
     pin_half_decode_all_patterns, pin_half_encode_rne,
     pin_gemv_rational, pin_gemv_exactly_representable, pin_gemv_closed_forms,
     pin_gemv_one_hot, pin_gemv_linearity, pin_gemm_rows,
-    pin_silu, pin_ffn, pin_argmax, pin_lmhead, pin_add_rmsnorm,
-    pin_layout_geometry, pin_layout_hand_example, pin_layout_roundtrip,
+    pin_silu, pin_ffn, pin_argmax, pin_lmhead, pin_add_rmsnorm, pin_rope,
+    pin_layout_geometry, pin_layout_hand_example, pin_layout_roundtrip, pin_rope_layout,
 ]

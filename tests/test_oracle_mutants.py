@@ -41,6 +41,13 @@ MUTANTS = [
      "            v += 0.0;"),
     ("norm_gamma_dropped", "q4o_half_to_double(hb) * q4o_half_to_double(gamma[i]) / rms",
      "q4o_half_to_double(hb) / rms"),
+    ("rope_adjacent_pair", "q4o_rope_pair(y[h * d + i], y[h * d + i + d / 2], i, d, pos, base, &oi, &oj);",
+     "q4o_rope_pair(y[h * d + i], y[h * d + i + 1], i, d, pos, base, &oi, &oj);"),
+    ("rope_frequency", "pow(base, -2.0 * (double)i / (double)d)", "pow(base, -1.0 * (double)i / (double)d)"),
+    ("rope_sign", "*oi = yi * c - yj * s;", "*oi = yi * c + yj * s;"),
+    ("rope_rotates_v", "for (int64_t h = 0; h < nq + nkv; ++h)", "for (int64_t h = 0; h < nq + 2 * nkv; ++h)"),
+    ("rope_layout_adjacent", "int64_t src = (pr / (d / 2)) * d + pr % (d / 2) + u * (d / 2);",
+     "int64_t src = (pr / (d / 2)) * d + 2 * (pr % (d / 2)) + u;"),
     ("norm_unrounded_residual", "const double hv = q4o_half_to_double(q4o_double_to_half(v));",
      "const double hv = v;"),
 ]

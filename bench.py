@@ -212,11 +212,7 @@ class Rotation:
     def __init__(self, q4, pw, copies: int):
         self.items = [pw]
         for _ in range(copies - 1):
-            buf = pw.buf.clone()
-            desc = q4.q4_weight()
-            desc.n, desc.k, desc.layout, desc.version = pw.desc.n, pw.desc.k, pw.desc.layout, pw.desc.version
-            desc.data, desc.bytes = buf.data_ptr(), pw.desc.bytes
-            self.items.append(q4.PackedWeight(buf, desc))
+            self.items.append(pw.clone())
 
     def __getitem__(self, i):
         return self.items[i % len(self.items)]
@@ -439,6 +435,21 @@ def variants(torch, q4, si, np, K, W):
                                         "frac": round(nb / us_n / 1e3 / PEAK_HBM_GBS, 4),
                                         "bytes": nb}
     del rot
+    # the fused QKV step: RoPE on the 32 q and 32 k heads (96 dims) at
+    # position 1000 and the K/V append into a 64-page cache, with and without
+    # the add + RMSNorm prologue
+    rot = Rotation(q4, q4.pack_rope(dev_u32(w), dev_u16(s_), 96), copies_for(weight_bytes(9216, 3072)))
+    cache = torch.zeros((64, 2, 16, 32, 96), dtype=torch.float16, device="cuda")
+    pt = torch.arange(64, dtype=torch.int32, device="cuda")
+    us_r = per_launch_us(torch, lambda i: q4.qkv_rope_append(rot[i], x, 32, 1000, 10000.0, cache, pt, out=y), K, W)
+    us_rn = per_launch_us(torch, lambda i: q4.qkv_rope_append(rot[i], x, 32, 1000, 10000.0, cache, pt, out=y,
+                                                              norm=(res, gam, 1e-5, hout)), K, W)
+    nb = gemv_bytes(9216, 3072) + 2 * 2 * 3072   # + the K and V rows appended
+    out["qkv_rope_append_9216x3072"] = {"us": round(us_r, 3), "with_norm_us": round(us_rn, 3),
+                                        "gbs": round(nb / us_r / 1e3, 1),
+                                        "frac": round(nb / us_r / 1e3 / PEAK_HBM_GBS, 4),
+                                        "bytes": nb}
+    del rot, cache
 
     # LM head, f32 logits + argmax
     inp = si.workload(si.LM_HEAD, seed=0)

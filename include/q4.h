@@ -76,6 +76,7 @@ extern "C" {
 /* weight layouts */
 #define Q4_LAYOUT_ROWS    1  /* plain rows: q4_gemv, q4_gemm, q4_lmhead_f32 */
 #define Q4_LAYOUT_GATE_UP 2  /* interleaved gate/up rows: q4_ffn_gate_up_silu */
+#define Q4_LAYOUT_ROPE    3  /* rotary-paired head rows: q4_qkv_rope_append */
 #define Q4_LAYOUT_VERSION 1
 
 /* operations, for q4_workspace_bytes */
@@ -92,10 +93,12 @@ extern "C" {
 typedef struct q4_weight {
     int32_t n;        /* output rows (gate/up: rows of EACH half) */
     int32_t k;        /* input columns, k % 32 == 0 */
-    int32_t layout;   /* Q4_LAYOUT_ROWS or Q4_LAYOUT_GATE_UP */
+    int32_t layout;   /* Q4_LAYOUT_ROWS, Q4_LAYOUT_GATE_UP or Q4_LAYOUT_ROPE */
     int32_t version;  /* Q4_LAYOUT_VERSION */
     void   *data;     /* device, 256-byte aligned, `bytes` long */
     int64_t bytes;    /* q4_packed_bytes(n, k, layout) */
+    int32_t head_dim; /* Q4_LAYOUT_ROPE: rows per head (even, divides n); else 0 */
+    int32_t reserved; /* 0 */
 } q4_weight;
 
 /* Bytes of the packed layout; 0 for an invalid shape or layout. */
@@ -129,9 +132,22 @@ int q4_pack_gate_up(const uint32_t *gw, const uint16_t *gs, const uint32_t *uw,
                     int64_t dst_bytes, q4_weight *out, void *stream);
 
 /*
- * Inverse of q4_pack / q4_pack_gate_up (for round-trip checks): writes the
- * canonical words [rows][k/8] and scales [rows][k/32] of the packed weight,
- * rows = n (plain) or 2n (gate/up, interleaved order: gate 0, up 0, gate 1 ...).
+ * Rotary-paired layout for the fused QKV step ([P1] 内核融合: qkv_fused
+ * applies RoPE inside the projection): the n rows are heads of head_dim
+ * rows; the device layout is the plain one over a row permutation that puts
+ * dims i and i + head_dim/2 of a head on logical rows 2p and 2p + 1 (p =
+ * head * head_dim/2 + i), so both halves of a rotation pair meet in one lane.
+ * Arguments as q4_pack, plus head_dim (even, >= 2, dividing n); the
+ * descriptor records it.  Errors as q4_pack.
+ */
+int q4_pack_rope(const uint32_t *words, const uint16_t *scales, int32_t n, int32_t k,
+                 int32_t head_dim, void *dst, int64_t dst_bytes, q4_weight *out, void *stream);
+
+/*
+ * Inverse of q4_pack / q4_pack_gate_up / q4_pack_rope (for round-trip
+ * checks): writes the canonical words [rows][k/8] and scales [rows][k/32] of
+ * the packed weight, rows = n (plain and rotary-paired: original row order)
+ * or 2n (gate/up, interleaved order: gate 0, up 0, gate 1 ...).
  */
 int q4_unpack(const q4_weight *w, uint32_t *words, uint16_t *scales, void *stream);
 
@@ -225,6 +241,44 @@ int q4_add_rmsnorm_gemv(const q4_weight *w, const uint16_t *x, const uint16_t *r
 int q4_add_rmsnorm_ffn_gate_up_silu(const q4_weight *w, const uint16_t *x,
                                     const uint16_t *residual, const uint16_t *gamma, float eps,
                                     uint16_t *residual_out, uint16_t *h, void *stream);
+
+/*
+ * The fused QKV step ([P1] 内核融合: qkv_fused merges the Q/K/V projection,
+ * RoPE and the paged KV-cache append into one dispatch; 完整的推理流水线:
+ * vLLM-style page table, RoPE computed in place):
+ *   y = x . dequant(W)^T over rows [nq q heads | nkv k heads | nkv v heads]
+ *   (each head d = w->head_dim rows, nkv = (n/d - nq) / 2); dims i and
+ *   i + d/2 of every q and k head are rotated by pos * rope_base^(-2i/d)
+ *   (y_i' = y_i cos - y_j sin, y_j' = y_j cos + y_i sin, angle in f64,
+ *   rotation in f32); v is left as is.
+ *   w          : Q4_LAYOUT_ROPE (q4_pack_rope)
+ *   x          : device f16 [k], 16-byte aligned
+ *   qkv        : device f16 [n], 4-byte aligned: y after RoPE
+ *   kv_cache   : device f16 [n_pages][2][16][nkv][d] or NULL (no append):
+ *                page, then K (0) / V (1), then the 16 token slots of the
+ *                page, then head, then dim; the k and v heads of y (k after
+ *                RoPE) are written to slot pos % 16 of page
+ *                page_table[pos / 16]; nothing else is written
+ *   page_table : device int32, at least pos / 16 + 1 entries (needed with a
+ *                cache); an entry outside [0, n_pages) appends nothing
+ *   pos        : >= 0;  rope_base : finite, > 0;  head_dim <= 512
+ * Errors: NULL, SHAPE (nq, pos, rope_base, n_pages out of range), ALIGN,
+ * LAYOUT, ALIAS, HIP.
+ */
+int q4_qkv_rope_append(const q4_weight *w, const uint16_t *x, int32_t n_q_heads, int32_t pos,
+                       double rope_base, uint16_t *qkv, uint16_t *kv_cache,
+                       const int32_t *page_table, int32_t n_pages, void *stream);
+
+/*
+ * q4_qkv_rope_append behind the residual add + RMSNorm prologue of
+ * q4_add_rmsnorm_gemv (the whole add_norm + qkv_fused pair of [P1] 内核融合
+ * in one launch); arguments as the two calls.
+ */
+int q4_add_rmsnorm_qkv_rope_append(const q4_weight *w, const uint16_t *x,
+                                   const uint16_t *residual, const uint16_t *gamma, float eps,
+                                   uint16_t *residual_out, int32_t n_q_heads, int32_t pos,
+                                   double rope_base, uint16_t *qkv, uint16_t *kv_cache,
+                                   const int32_t *page_table, int32_t n_pages, void *stream);
 
 /* Static text for a return code. */
 const char *q4_strerror(int code);

@@ -34,7 +34,7 @@ _lib = ctypes.CDLL(LIBRARY)
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_LAYOUT = -1, -2, -3, -4
 ERR_WORKSPACE, ERR_ALIAS, ERR_HIP, ERR_SIZE = -5, -6, -7, -8
-LAYOUT_ROWS, LAYOUT_GATE_UP, LAYOUT_VERSION = 1, 2, 1
+LAYOUT_ROWS, LAYOUT_GATE_UP, LAYOUT_ROPE, LAYOUT_VERSION = 1, 2, 3, 1
 GEMM_AUTO, GEMM_VALU, GEMM_MFMA = 0, 1, 2
 OP_GEMV, OP_GEMM, OP_FFN, OP_LMHEAD = 1, 2, 3, 4
 
@@ -42,7 +42,8 @@ OP_GEMV, OP_GEMM, OP_FFN, OP_LMHEAD = 1, 2, 3, 4
 class q4_weight(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("layout", ctypes.c_int32), ("version", ctypes.c_int32),
-                ("data", ctypes.c_void_p), ("bytes", ctypes.c_int64)]
+                ("data", ctypes.c_void_p), ("bytes", ctypes.c_int64),
+                ("head_dim", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -54,7 +55,13 @@ _SIGNATURES = {
     "q4_workspace_bytes": (_I64, [_I32, _I32, _I32, _I32]),
     "q4_pack": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _I64, _W, _P]),
     "q4_pack_gate_up": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _P, _I64, _W, _P]),
+    "q4_pack_rope": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _I64, _W, _P]),
     "q4_unpack": (ctypes.c_int, [_W, _P, _P, _P]),
+    "q4_qkv_rope_append": (ctypes.c_int, [_W, _P, _I32, _I32, ctypes.c_double, _P, _P, _P, _I32,
+                                          _P]),
+    "q4_add_rmsnorm_qkv_rope_append": (ctypes.c_int, [_W, _P, _P, _P, ctypes.c_float, _P, _I32,
+                                                      _I32, ctypes.c_double, _P, _P, _P, _I32,
+                                                      _P]),
     "q4_gemv": (ctypes.c_int, [_W, _P, _P, _P]),
     "q4_gemm": (ctypes.c_int, [_W, _P, _I32, _P, _P, _I64, _P]),
     "q4_gemm_path": (ctypes.c_int, [_W, _P, _I32, _P, _I32, _P]),
@@ -132,6 +139,16 @@ class PackedWeight:
     def device(self) -> torch.device:
         return self.buf.device
 
+    def clone(self) -> "PackedWeight":
+        """A copy in new device memory (same bytes, every descriptor field)."""
+        buf = self.buf.clone()
+        if buf.data_ptr() % 256:
+            raise RuntimeError("allocator returned a buffer that is not 256-byte aligned")
+        desc = q4_weight()
+        ctypes.memmove(ctypes.byref(desc), ctypes.byref(self.desc), ctypes.sizeof(q4_weight))
+        desc.data = buf.data_ptr()
+        return PackedWeight(buf, desc)
+
 
 def packed_bytes(n: int, k: int, layout: int = LAYOUT_ROWS) -> int:
     return int(_lib.q4_packed_bytes(n, k, layout))
@@ -178,6 +195,20 @@ def pack_gate_up(gw, gs, uw, us) -> PackedWeight:
     desc = q4_weight()
     _check(_lib.q4_pack_gate_up(*ptrs, n, k, buf.data_ptr(), buf.numel(), ctypes.byref(desc),
                                 _stream(gw)), "q4_pack_gate_up")
+    return PackedWeight(buf, desc)
+
+
+def pack_rope(words: torch.Tensor, scales: torch.Tensor, head_dim: int) -> PackedWeight:
+    """Canonical [n][k/8] / [n][k/32] of the concatenated q, k, v head rows
+    -> the rotary-paired layout for qkv_rope_append (q4_pack_rope)."""
+    n, kw = words.shape
+    k = kw * 8
+    pw = _dev(words, "words", 4, (n, kw))
+    ps = _dev(scales, "scales", 2, (n, k // 32))
+    buf = _alloc_packed(n, k, LAYOUT_ROPE, words.device)
+    desc = q4_weight()
+    _check(_lib.q4_pack_rope(pw, ps, n, k, head_dim, buf.data_ptr(), buf.numel(),
+                             ctypes.byref(desc), _stream(words)), "q4_pack_rope")
     return PackedWeight(buf, desc)
 
 
@@ -267,6 +298,41 @@ def add_rmsnorm_ffn_gate_up_silu(w: PackedWeight, x: torch.Tensor,
     _check(_lib.q4_add_rmsnorm_ffn_gate_up_silu(ctypes.byref(w.desc), px, pr, pg, float(eps),
                                                 pro, ph, _stream(x)),
            "q4_add_rmsnorm_ffn_gate_up_silu")
+    return out
+
+
+def qkv_rope_append(w: PackedWeight, x: torch.Tensor, n_q_heads: int, pos: int,
+                    rope_base: float, kv_cache: Optional[torch.Tensor] = None,
+                    page_table: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, norm=None) -> torch.Tensor:
+    """qkv f16 [n]: the fused QKV projection with RoPE on the q and k heads,
+    the k and v heads appended to kv_cache f16 [pages][2][16][n_kv][d] at
+    slot pos % 16 of page page_table[pos // 16] (q4_qkv_rope_append).
+    norm = (residual or None, gamma, eps, residual_out or None) runs the add
+    + RMSNorm prologue first (q4_add_rmsnorm_qkv_rope_append)."""
+    px = _dev(x, "x", 2, (w.k,))
+    if out is None:
+        out = torch.empty(w.n, dtype=torch.float16, device=x.device)
+    py = _dev(out, "out", 2, (w.n,))
+    pc, pt, npages = None, None, 0
+    if kv_cache is not None:
+        if kv_cache.element_size() != 2 or not kv_cache.is_contiguous() or kv_cache.dim() != 5:
+            raise ValueError("kv_cache must be a contiguous 16-bit [pages][2][16][n_kv][d] tensor")
+        pc = kv_cache.data_ptr()
+        npages = kv_cache.shape[0]
+        if page_table is None:
+            raise ValueError("a page table is needed with a cache")
+        pt = _dev(page_table, "page_table", 4)
+    if norm is None:
+        _check(_lib.q4_qkv_rope_append(ctypes.byref(w.desc), px, n_q_heads, pos, float(rope_base),
+                                       py, pc, pt, npages, _stream(x)), "q4_qkv_rope_append")
+    else:
+        residual, gamma, eps, residual_out = norm
+        _, pr, pg, pro = _norm_args(w, x, residual, gamma, residual_out)
+        _check(_lib.q4_add_rmsnorm_qkv_rope_append(ctypes.byref(w.desc), px, pr, pg, float(eps),
+                                                   pro, n_q_heads, pos, float(rope_base), py, pc,
+                                                   pt, npages, _stream(x)),
+               "q4_add_rmsnorm_qkv_rope_append")
     return out
 
 

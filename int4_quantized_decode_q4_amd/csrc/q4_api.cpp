@@ -54,6 +54,9 @@ int check_weight(const q4_weight *w, int32_t want_layout, q4::Geometry *geo, int
         return Q4_ERR_LAYOUT;
     if (!aligned(w->data, 256))
         return Q4_ERR_ALIGN;
+    if (w->layout == Q4_LAYOUT_ROPE &&
+        (w->head_dim < 2 || w->head_dim % 2 != 0 || w->n % w->head_dim != 0))
+        return Q4_ERR_SHAPE;
     *rows = (want_layout == Q4_LAYOUT_GATE_UP) ? 2 * (int64_t)w->n : (int64_t)w->n;
     if (!q4::layout_geometry(*rows, w->k, geo))
         return Q4_ERR_SHAPE;
@@ -63,12 +66,15 @@ int check_weight(const q4_weight *w, int32_t want_layout, q4::Geometry *geo, int
 }
 
 int pack_common(const uint32_t *w0, const uint16_t *s0, const uint32_t *w1, const uint16_t *s1,
-                int32_t n, int32_t k, bool gate_up, void *dst, int64_t dst_bytes, q4_weight *out,
-                void *stream)
+                int32_t n, int32_t k, q4::PackMode mode, int32_t d, void *dst, int64_t dst_bytes,
+                q4_weight *out, void *stream)
 {
+    const bool gate_up = mode == q4::PACK_GATE_UP;
     if (!w0 || !s0 || !dst || !out || (gate_up && (!w1 || !s1)))
         return Q4_ERR_NULL;
     if (!valid_shape(n, k))
+        return Q4_ERR_SHAPE;
+    if (mode == q4::PACK_ROPE && (d < 2 || d % 2 != 0 || n % d != 0))
         return Q4_ERR_SHAPE;
     if (!aligned(w0, 16) || !aligned(s0, 2) || !aligned(dst, 256) ||
         (gate_up && (!aligned(w1, 16) || !aligned(s1, 2))))
@@ -85,16 +91,19 @@ int pack_common(const uint32_t *w0, const uint16_t *s0, const uint32_t *w1, cons
         (gate_up && (overlap(dst, need, w1, wbytes) || overlap(dst, need, s1, sbytes))))
         return Q4_ERR_ALIAS;
     (void)hipGetLastError();
-    const int rc = hip_status(q4::launch_pack(w0, s0, w1, s1, rows, k, gate_up, geo, dst,
+    const int rc = hip_status(q4::launch_pack(w0, s0, w1, s1, rows, k, mode, d, geo, dst,
                                               static_cast<hipStream_t>(stream)));
     if (rc != Q4_OK)
         return rc;
     out->n = n;
     out->k = k;
-    out->layout = gate_up ? Q4_LAYOUT_GATE_UP : Q4_LAYOUT_ROWS;
+    out->layout = gate_up ? Q4_LAYOUT_GATE_UP
+                          : (mode == q4::PACK_ROPE ? Q4_LAYOUT_ROPE : Q4_LAYOUT_ROWS);
     out->version = Q4_LAYOUT_VERSION;
     out->data = dst;
     out->bytes = need;
+    out->head_dim = mode == q4::PACK_ROPE ? d : 0;
+    out->reserved = 0;
     return Q4_OK;
 }
 
@@ -104,7 +113,8 @@ extern "C" {
 
 int64_t q4_packed_bytes(int32_t n, int32_t k, int32_t layout)
 {
-    if (!valid_shape(n, k) || (layout != Q4_LAYOUT_ROWS && layout != Q4_LAYOUT_GATE_UP))
+    if (!valid_shape(n, k) ||
+        (layout != Q4_LAYOUT_ROWS && layout != Q4_LAYOUT_GATE_UP && layout != Q4_LAYOUT_ROPE))
         return 0;
     q4::Geometry geo;
     const int64_t rows = layout == Q4_LAYOUT_GATE_UP ? 2 * (int64_t)n : (int64_t)n;
@@ -145,21 +155,30 @@ int q4_layout_geometry(int32_t rows, int32_t k, int64_t *out)
 int q4_pack(const uint32_t *words, const uint16_t *scales, int32_t n, int32_t k, void *dst,
             int64_t dst_bytes, q4_weight *out, void *stream)
 {
-    return pack_common(words, scales, nullptr, nullptr, n, k, false, dst, dst_bytes, out, stream);
+    return pack_common(words, scales, nullptr, nullptr, n, k, q4::PACK_ROWS, 0, dst, dst_bytes,
+                       out, stream);
+}
+
+int q4_pack_rope(const uint32_t *words, const uint16_t *scales, int32_t n, int32_t k,
+                 int32_t head_dim, void *dst, int64_t dst_bytes, q4_weight *out, void *stream)
+{
+    return pack_common(words, scales, nullptr, nullptr, n, k, q4::PACK_ROPE, head_dim, dst,
+                       dst_bytes, out, stream);
 }
 
 int q4_pack_gate_up(const uint32_t *gw, const uint16_t *gs, const uint32_t *uw,
                     const uint16_t *us, int32_t n, int32_t k, void *dst, int64_t dst_bytes,
                     q4_weight *out, void *stream)
 {
-    return pack_common(gw, gs, uw, us, n, k, true, dst, dst_bytes, out, stream);
+    return pack_common(gw, gs, uw, us, n, k, q4::PACK_GATE_UP, 0, dst, dst_bytes, out, stream);
 }
 
 int q4_unpack(const q4_weight *w, uint32_t *words, uint16_t *scales, void *stream)
 {
     if (!w || !words || !scales)
         return Q4_ERR_NULL;
-    if (w->layout != Q4_LAYOUT_ROWS && w->layout != Q4_LAYOUT_GATE_UP)
+    if (w->layout != Q4_LAYOUT_ROWS && w->layout != Q4_LAYOUT_GATE_UP &&
+        w->layout != Q4_LAYOUT_ROPE)
         return Q4_ERR_LAYOUT;
     q4::Geometry geo;
     int64_t rows = 0;
@@ -173,7 +192,9 @@ int q4_unpack(const q4_weight *w, uint32_t *words, uint16_t *scales, void *strea
         overlap(words, wbytes, scales, sbytes))
         return Q4_ERR_ALIAS;
     (void)hipGetLastError();
-    return hip_status(q4::launch_unpack(w->data, rows, w->k, geo, words, scales,
+    const q4::PackMode mode = w->layout == Q4_LAYOUT_GATE_UP ? q4::PACK_GATE_UP
+                              : (w->layout == Q4_LAYOUT_ROPE ? q4::PACK_ROPE : q4::PACK_ROWS);
+    return hip_status(q4::launch_unpack(w->data, rows, w->k, mode, w->head_dim, geo, words, scales,
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -193,7 +214,7 @@ int q4_gemv(const q4_weight *w, const uint16_t *x, uint16_t *y, void *stream)
         return Q4_ERR_ALIAS;
     (void)hipGetLastError();
     return hip_status(q4::launch_gemv_family(geo, q4::EPI_F16, w->data, x, y, rows, w->k, w->n,
-                                             q4::ArgmaxScratch{nullptr, nullptr}, nullptr,
+                                             q4::ArgmaxScratch{nullptr, nullptr}, nullptr, nullptr,
                                              static_cast<hipStream_t>(stream)));
 }
 
@@ -245,7 +266,7 @@ int q4_ffn_gate_up_silu(const q4_weight *w, const uint16_t *x, uint16_t *h, void
         return Q4_ERR_ALIAS;
     (void)hipGetLastError();
     return hip_status(q4::launch_gemv_family(geo, q4::EPI_SILU, w->data, x, h, rows, w->k, w->n,
-                                             q4::ArgmaxScratch{nullptr, nullptr}, nullptr,
+                                             q4::ArgmaxScratch{nullptr, nullptr}, nullptr, nullptr,
                                              static_cast<hipStream_t>(stream)));
 }
 
@@ -282,7 +303,7 @@ int q4_lmhead_f32(const q4_weight *w, const uint16_t *x, float *logits, int32_t 
         return Q4_ERR_ALIAS;
     (void)hipGetLastError();
     return hip_status(q4::launch_gemv_family(geo, q4::EPI_F32, w->data, x, logits, rows, w->k,
-                                             w->n, am, nullptr, static_cast<hipStream_t>(stream)));
+                                             w->n, am, nullptr, nullptr, static_cast<hipStream_t>(stream)));
 }
 
 // Shared checks of the add + RMSNorm entry points; out is y (gemv) or h
@@ -331,7 +352,7 @@ int q4_add_rmsnorm_gemv(const q4_weight *w, const uint16_t *x, const uint16_t *r
     const q4::NormArgs nm{residual, gamma, residual_out, eps};
     (void)hipGetLastError();
     return hip_status(q4::launch_gemv_family(geo, q4::EPI_F16, w->data, x, y, rows, w->k, w->n,
-                                             q4::ArgmaxScratch{nullptr, nullptr}, &nm,
+                                             q4::ArgmaxScratch{nullptr, nullptr}, &nm, nullptr,
                                              static_cast<hipStream_t>(stream)));
 }
 
@@ -354,8 +375,80 @@ int q4_add_rmsnorm_ffn_gate_up_silu(const q4_weight *w, const uint16_t *x,
     const q4::NormArgs nm{residual, gamma, residual_out, eps};
     (void)hipGetLastError();
     return hip_status(q4::launch_gemv_family(geo, q4::EPI_SILU, w->data, x, h, rows, w->k, w->n,
-                                             q4::ArgmaxScratch{nullptr, nullptr}, &nm,
+                                             q4::ArgmaxScratch{nullptr, nullptr}, &nm, nullptr,
                                              static_cast<hipStream_t>(stream)));
+}
+
+// The fused QKV step with an optional add + RMSNorm prologue (nm null: none).
+static int qkv_rope_common(const q4_weight *w, const uint16_t *x, const q4::NormArgs *nm,
+                           int32_t n_q_heads, int32_t pos, double rope_base, uint16_t *qkv,
+                           uint16_t *kv_cache, const int32_t *page_table, int32_t n_pages,
+                           void *stream)
+{
+    q4::Geometry geo;
+    int64_t rows = 0;
+    if (!w || !x || !qkv || (kv_cache && !page_table))
+        return Q4_ERR_NULL;
+    int rc = check_weight(w, Q4_LAYOUT_ROPE, &geo, &rows);
+    if (rc != Q4_OK)
+        return rc;
+    const int64_t d = w->head_dim, heads = (int64_t)w->n / d;
+    if (d > 512)   // the kernels keep d/2 RoPE twiddles in LDS
+        return Q4_ERR_SHAPE;
+    const int64_t nkv2 = heads - n_q_heads;
+    if (n_q_heads < 0 || nkv2 < 0 || nkv2 % 2 != 0 || pos < 0 || !(rope_base > 0.0) ||
+        !std::isfinite(rope_base) || (kv_cache && n_pages < 1))
+        return Q4_ERR_SHAPE;
+    const int64_t nkv = nkv2 / 2;
+    if (!aligned(x, 16) || !aligned(qkv, 4) || (kv_cache && !aligned(kv_cache, 4)) ||
+        (page_table && !aligned(page_table, 4)))
+        return Q4_ERR_ALIGN;
+    const int64_t kb = 2 * (int64_t)w->k, yb = 2 * (int64_t)w->n;
+    const int64_t cb = (int64_t)n_pages * 2 * 16 * nkv * d * 2;
+    const int64_t ptb = 4 * ((int64_t)pos / 16 + 1);
+    if (overlap(qkv, yb, x, kb) || overlap(qkv, yb, w->data, w->bytes))
+        return Q4_ERR_ALIAS;
+    if (kv_cache && (overlap(kv_cache, cb, x, kb) || overlap(kv_cache, cb, w->data, w->bytes) ||
+                     overlap(kv_cache, cb, qkv, yb) || overlap(kv_cache, cb, page_table, ptb)))
+        return Q4_ERR_ALIAS;
+    if (page_table && overlap(qkv, yb, page_table, ptb))
+        return Q4_ERR_ALIAS;
+    if (nm) {
+        rc = check_norm_args(w, x, nm->r, nm->gamma, nm->eps, nm->h_out, qkv, yb);
+        if (rc != Q4_OK)
+            return rc;
+        if (kv_cache && ((nm->r && overlap(kv_cache, cb, nm->r, kb)) ||
+                         overlap(kv_cache, cb, nm->gamma, kb) ||
+                         (nm->h_out && overlap(kv_cache, cb, nm->h_out, kb))))
+            return Q4_ERR_ALIAS;
+    }
+    const q4::RopeArgs rp{(int32_t)d, n_q_heads, (int32_t)nkv, pos, rope_base, kv_cache,
+                          page_table, n_pages};
+    (void)hipGetLastError();
+    return hip_status(q4::launch_gemv_family(geo, q4::EPI_ROPE, w->data, x, qkv, rows, w->k, w->n,
+                                             q4::ArgmaxScratch{nullptr, nullptr}, nm, &rp,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int q4_qkv_rope_append(const q4_weight *w, const uint16_t *x, int32_t n_q_heads, int32_t pos,
+                       double rope_base, uint16_t *qkv, uint16_t *kv_cache,
+                       const int32_t *page_table, int32_t n_pages, void *stream)
+{
+    return qkv_rope_common(w, x, nullptr, n_q_heads, pos, rope_base, qkv, kv_cache, page_table,
+                           n_pages, stream);
+}
+
+int q4_add_rmsnorm_qkv_rope_append(const q4_weight *w, const uint16_t *x,
+                                   const uint16_t *residual, const uint16_t *gamma, float eps,
+                                   uint16_t *residual_out, int32_t n_q_heads, int32_t pos,
+                                   double rope_base, uint16_t *qkv, uint16_t *kv_cache,
+                                   const int32_t *page_table, int32_t n_pages, void *stream)
+{
+    if (!gamma)
+        return Q4_ERR_NULL;
+    const q4::NormArgs nm{residual, gamma, residual_out, eps};
+    return qkv_rope_common(w, x, &nm, n_q_heads, pos, rope_base, qkv, kv_cache, page_table,
+                           n_pages, stream);
 }
 
 const char *q4_strerror(int code)

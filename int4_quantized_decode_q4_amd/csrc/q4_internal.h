@@ -14,7 +14,44 @@ enum Epilogue {
     EPI_F16 = 0,   // y f16, rounded to nearest even
     EPI_F32 = 1,   // f32 logits, optional argmax
     EPI_SILU = 2,  // interleaved gate/up rows -> SiLU(g) * u, f16
+    EPI_ROPE = 3,  // rotary-paired head rows -> RoPE on q and k, f16, KV append
 };
+
+// The fused QKV epilogue: heads of d rows, nq q heads then nkv k heads then
+// nkv v heads; RoPE at position pos on q and k; k and v appended to the
+// paged cache [n_pages][2][16][nkv][d] (cache may be null).
+struct RopeArgs {
+    int32_t d, nq, nkv, pos;
+    double base;
+    uint16_t *cache;
+    const int32_t *page_table;
+    int32_t n_pages;
+};
+
+// What the RoPE epilogue's kernels receive: RopeArgs plus the launch's
+// twiddles (cos, sin of pos * base^(-2i/d), i < d/2), computed on the host
+// in f64 and passed in the kernel arguments.  Other epilogues get NoRope.
+constexpr int kRopeMaxHalf = 256;   // head_dim <= 512
+struct RopeTab {
+    int32_t d, nq, nkv, pos;
+    uint16_t *cache;
+    const int32_t *page_table;
+    int32_t n_pages;
+    float cs[kRopeMaxHalf][2];
+};
+struct NoRope {
+};
+template <int EPI>
+struct RopeParam {
+    using type = NoRope;
+};
+template <>
+struct RopeParam<EPI_ROPE> {
+    using type = RopeTab;
+};
+
+// Row order of a packed layout: plain, gate/up interleave, rotary pairs.
+enum PackMode { PACK_ROWS = 0, PACK_GATE_UP = 1, PACK_ROPE = 2 };
 
 // Scratch of the LM-head argmax inside the caller's workspace.
 struct ArgmaxScratch {
@@ -27,11 +64,12 @@ struct ArgmaxScratch {
 int64_t argmax_workspace_bytes(const Geometry &geo);
 
 hipError_t launch_pack(const uint32_t *w0, const uint16_t *s0, const uint32_t *w1,
-                       const uint16_t *s1, int64_t rows, int64_t k, bool gate_up,
+                       const uint16_t *s1, int64_t rows, int64_t k, PackMode mode, int64_t d,
                        const Geometry &geo, void *dst, hipStream_t stream);
 
-hipError_t launch_unpack(const void *src, int64_t rows, int64_t k, const Geometry &geo,
-                         uint32_t *words, uint16_t *scales, hipStream_t stream);
+hipError_t launch_unpack(const void *src, int64_t rows, int64_t k, PackMode mode, int64_t d,
+                         const Geometry &geo, uint32_t *words, uint16_t *scales,
+                         hipStream_t stream);
 
 // Residual add + RMSNorm applied to x inside a GEMV launch (EPI_F16 and
 // EPI_SILU only): h = f16(x + r) (r may be null), the matmul sees
@@ -46,7 +84,7 @@ struct NormArgs {
 hipError_t launch_gemv_family(const Geometry &geo, Epilogue epi, const void *wdata,
                               const uint16_t *x, void *out, int64_t rows, int64_t k,
                               int64_t n_out, ArgmaxScratch am, const NormArgs *norm,
-                              hipStream_t stream);
+                              const RopeArgs *rope, hipStream_t stream);
 
 enum GemmPath { GEMM_PATH_AUTO = 0, GEMM_PATH_VALU = 1, GEMM_PATH_MFMA = 2 };
 

@@ -55,9 +55,17 @@ __device__ __forceinline__ float f16_value(uint16_t b)
 // One thread per destination 16-byte code unit (and the scale beside it):
 // a pure permutation of the canonical words, padding where the logical
 // (row, group) lies outside the matrix.
+// Canonical row behind logical row r of a rotary-paired layout with heads of
+// d rows: logical rows 2p, 2p + 1 hold dims i, i + d/2 of head p / (d/2).
+__host__ __device__ __forceinline__ int64_t rope_source_row(int64_t r, int64_t d)
+{
+    const int64_t p = r >> 1, half = d >> 1;
+    return (p / half) * d + p % half + (r & 1) * half;
+}
+
 __global__ void pack_kernel(const uint32_t *__restrict__ w0, const uint16_t *__restrict__ s0,
                             const uint32_t *__restrict__ w1, const uint16_t *__restrict__ s1,
-                            int64_t rows, int64_t k, int gate_up, int L, int CG, int P,
+                            int64_t rows, int64_t k, int mode, int64_t d, int L, int CG, int P,
                             int64_t units, uint8_t *__restrict__ dst)
 {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -82,10 +90,12 @@ __global__ void pack_kernel(const uint32_t *__restrict__ w0, const uint16_t *__r
         const uint32_t *sw = w0;
         const uint16_t *ss = s0;
         int64_t row = r;
-        if (gate_up) {
+        if (mode == PACK_GATE_UP) {
             row = r >> 1;
             sw = (r & 1) ? w1 : w0;
             ss = (r & 1) ? s1 : s0;
+        } else if (mode == PACK_ROPE) {
+            row = rope_source_row(r, d);
         }
         words = *reinterpret_cast<const uint4 *>(sw + row * (k / 8) + 4 * g);
         scale = ss[row * G + g];
@@ -97,8 +107,8 @@ __global__ void pack_kernel(const uint32_t *__restrict__ w0, const uint16_t *__r
 
 // One thread per logical (row, group) of the real matrix.
 __global__ void unpack_kernel(const uint8_t *__restrict__ src, int64_t rows, int64_t k,
-                              int L, int CG, int P, uint32_t *__restrict__ words,
-                              uint16_t *__restrict__ scales)
+                              int mode, int64_t d, int L, int CG, int P,
+                              uint32_t *__restrict__ words, uint16_t *__restrict__ scales)
 {
     const int64_t G = k / 32;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -113,8 +123,10 @@ __global__ void unpack_kernel(const uint8_t *__restrict__ src, int64_t rows, int
     const int lane = s * L + c;
     const uint8_t *base = src + (t * P + p) * (int64_t)CG * 2304;
     const uint4 v = *reinterpret_cast<const uint4 *>(base + (int64_t)(u * CG + j) * 1024 + lane * 16);
-    *reinterpret_cast<uint4 *>(words + r * (k / 8) + 4 * g) = v;
-    scales[r * G + g] =
+    // rotary pairs come back in the original row order
+    const int64_t row = mode == PACK_ROPE ? rope_source_row(r, d) : r;
+    *reinterpret_cast<uint4 *>(words + row * (k / 8) + 4 * g) = v;
+    scales[row * G + g] =
         *reinterpret_cast<const uint16_t *>(base + (int64_t)2 * CG * 1024 + lane * 4 * CG + (u * CG + j) * 2);
 }
 
@@ -427,16 +439,17 @@ __device__ __forceinline__ void compute_tile(const TileRegs<CG> &r, const uint32
 // Epilogue of the finished sums y0, y1 of logical rows r0 (even) and r0 + 1.
 template <int EPI>
 __device__ __forceinline__ void store_rows(float y0, float y1, int64_t r0, void *__restrict__ out,
-                                           int64_t rows, int64_t n_out, float &bv, int &bi)
+                                           int64_t rows, int64_t n_out, float &bv, int &bi,
+                                           const typename RopeParam<EPI>::type &rp)
 {
-    if (EPI == EPI_F16) {
+    if constexpr (EPI == EPI_F16) {
         uint16_t *y = static_cast<uint16_t *>(out);
         if (r0 + 1 < rows)
             *reinterpret_cast<uint32_t *>(y + r0) =
                 (uint32_t)f16_bits(y0) | ((uint32_t)f16_bits(y1) << 16);
         else if (r0 < rows)
             y[r0] = f16_bits(y0);
-    } else if (EPI == EPI_F32) {
+    } else if constexpr (EPI == EPI_F32) {
         float *y = static_cast<float *>(out);
         if (r0 + 1 < rows) {
             *reinterpret_cast<float2 *>(y + r0) = make_float2(y0, y1);
@@ -446,11 +459,38 @@ __device__ __forceinline__ void store_rows(float y0, float y1, int64_t r0, void 
             y[r0] = y0;
             better(bv, bi, y0, (int)r0);
         }
-    } else {  // EPI_SILU: logical rows (2i, 2i+1) = (gate i, up i)
+    } else if constexpr (EPI == EPI_SILU) {  // logical rows (2i, 2i+1) = (gate i, up i)
         const int64_t i = r0 >> 1;
         if (i < n_out) {
             const float h = y0 / (1.0f + expf(-y0)) * y1;
             static_cast<uint16_t *>(out)[i] = f16_bits(h);
+        }
+    } else if constexpr (EPI == EPI_ROPE) {
+        // logical rows (2p, 2p+1) = dims (i, i + d/2) of head p / (d/2)
+        if (r0 >= rows)
+            return;
+        const int64_t p = r0 >> 1, half = rp.d >> 1;
+        const int64_t blk = p / half, i = p % half;
+        float a = y0, b = y1;
+        if (blk < rp.nq + rp.nkv) {   // q and k heads turn
+            const float cs = rp.cs[i][0], sn = rp.cs[i][1];
+            a = y0 * cs - y1 * sn;
+            b = y1 * cs + y0 * sn;
+        }
+        const uint16_t ha = f16_bits(a), hb = f16_bits(b);
+        uint16_t *y = static_cast<uint16_t *>(out);
+        y[blk * rp.d + i] = ha;
+        y[blk * rp.d + i + half] = hb;
+        if (rp.cache != nullptr && blk >= rp.nq) {   // k and v heads: the page slot of pos
+            const int64_t kv = blk >= rp.nq + rp.nkv ? 1 : 0;
+            const int64_t head = blk - rp.nq - kv * rp.nkv;
+            const int32_t page = rp.page_table[rp.pos >> 4];
+            if (page >= 0 && page < rp.n_pages) {
+                uint16_t *dst = rp.cache + (((int64_t)page * 2 + kv) * 16 + (rp.pos & 15)) * rp.nkv * rp.d +
+                                head * rp.d + i;
+                dst[0] = ha;
+                dst[half] = hb;
+            }
         }
     }
 }
@@ -459,13 +499,14 @@ __device__ __forceinline__ void store_rows(float y0, float y1, int64_t r0, void 
 template <int L, int EPI>
 __device__ __forceinline__ void finish_tile(const float (&acc)[2], int64_t t, int s, int c,
                                             void *__restrict__ out, int64_t rows, int64_t n_out,
-                                            float &bv, int &bi)
+                                            float &bv, int &bi,
+                                            const typename RopeParam<EPI>::type &rp)
 {
     constexpr int TR = 128 / L;
     const float y0 = reduce_lanes<L>(acc[0]);
     const float y1 = reduce_lanes<L>(acc[1]);
     if (c == 0)
-        store_rows<EPI>(y0, y1, t * TR + 2 * s, out, rows, n_out, bv, bi);
+        store_rows<EPI>(y0, y1, t * TR + 2 * s, out, rows, n_out, bv, bi, rp);
 }
 
 // ------------------------------------------------------------ GEMV kernels --
@@ -574,7 +615,8 @@ __device__ __forceinline__ void lds_x_group(uint32_t *xp, const uint4 *xs, int64
 template <int L, int CG, int EPI, bool NORM>
 __global__ __launch_bounds__(64 * kBlockWaves) void gemv_block_kernel(
     const uint8_t *__restrict__ wd, const uint16_t *__restrict__ x, void *__restrict__ out,
-    int64_t rows, int64_t k, int64_t tiles, int64_t n_out, ArgmaxScratch am, NormArgs nm)
+    int64_t rows, int64_t k, int64_t tiles, int64_t n_out, ArgmaxScratch am, NormArgs nm,
+    typename RopeParam<EPI>::type rp)
 {
     constexpr int PD = Q4_STREAM_DEPTH < 2 * CG ? Q4_STREAM_DEPTH : 2 * CG;
     constexpr int64_t PB = (int64_t)CG * 2304;
@@ -677,7 +719,7 @@ __global__ __launch_bounds__(64 * kBlockWaves) void gemv_block_kernel(
             const int64_t nt = t + step;
             float acc[2] = {0.f, 0.f};
             stream_tile<CG, PD>(ra, rb, rs_of(t), rs_of(nt), lane, xp, acc, m);
-            finish_tile<L, EPI>(acc, t, s, c, out, rows, n_out, bv, bi);
+            finish_tile<L, EPI>(acc, t, s, c, out, rows, n_out, bv, bi, rp);
             t = nt;
         }
         if (t >= tiles)
@@ -686,7 +728,7 @@ __global__ __launch_bounds__(64 * kBlockWaves) void gemv_block_kernel(
             const int64_t nt = t + step;
             float acc[2] = {0.f, 0.f};
             stream_tile<CG, PD>(rb, ra, rs_of(t), rs_of(nt), lane, xp, acc, m);
-            finish_tile<L, EPI>(acc, t, s, c, out, rows, n_out, bv, bi);
+            finish_tile<L, EPI>(acc, t, s, c, out, rows, n_out, bv, bi, rp);
             t = nt;
         }
     }
@@ -711,7 +753,8 @@ constexpr int kSplitMaxTiles = 8;
 template <int L, int CG, int EPI, bool NORM>
 __global__ __launch_bounds__(64 * CG) void gemv_split_kernel(
     const uint8_t *__restrict__ wd, const uint16_t *__restrict__ x, void *__restrict__ out,
-    int64_t rows, int64_t k, int64_t tiles, int64_t n_out, ArgmaxScratch am, NormArgs nm)
+    int64_t rows, int64_t k, int64_t tiles, int64_t n_out, ArgmaxScratch am, NormArgs nm,
+    typename RopeParam<EPI>::type rp)
 {
     constexpr int HP = 64 / L;   // row pairs per tile
     constexpr int TR = 128 / L;
@@ -795,7 +838,7 @@ __global__ __launch_bounds__(64 * CG) void gemv_split_kernel(
             y1 += part[i][jj][ss][1];
         }
         const int64_t t = (int64_t)blockIdx.x + (int64_t)i * gridDim.x;
-        store_rows<EPI>(y0, y1, t * TR + 2 * ss, out, rows, n_out, bv, bi);
+        store_rows<EPI>(y0, y1, t * TR + 2 * ss, out, rows, n_out, bv, bi, rp);
     }
     if (EPI == EPI_F32 && am.partials != nullptr)
         grid_argmax(bv, bi, am);
@@ -807,7 +850,7 @@ template <int L, int CG, int EPI, bool NORM>
 __global__ __launch_bounds__(256) void gemv_multipass_kernel(
     const uint8_t *__restrict__ wd, const uint16_t *__restrict__ x, void *__restrict__ out,
     int64_t rows, int64_t k, int passes, int64_t tiles, int64_t n_out, ArgmaxScratch am,
-    NormArgs nm)
+    NormArgs nm, typename RopeParam<EPI>::type rp)
 {
     constexpr int64_t PB = (int64_t)CG * 2304;
     const int lane = threadIdx.x & 63;
@@ -838,7 +881,7 @@ __global__ __launch_bounds__(256) void gemv_multipass_kernel(
             }
             compute_tile(r, xp, acc, m);
         }
-        finish_tile<L, EPI>(acc, t, s, c, out, rows, n_out, bv, bi);
+        finish_tile<L, EPI>(acc, t, s, c, out, rows, n_out, bv, bi, rp);
     }
     if (EPI == EPI_F32 && am.partials != nullptr)
         grid_argmax(bv, bi, am);
@@ -898,25 +941,26 @@ int64_t argmax_workspace_bytes(const Geometry &geo)
 }
 
 hipError_t launch_pack(const uint32_t *w0, const uint16_t *s0, const uint32_t *w1,
-                       const uint16_t *s1, int64_t rows, int64_t k, bool gate_up,
+                       const uint16_t *s1, int64_t rows, int64_t k, PackMode mode, int64_t d,
                        const Geometry &geo, void *dst, hipStream_t stream)
 {
     const int64_t units = geo.tiles * geo.P * 2 * geo.CG * 64;
     const int64_t blocks = (units + 255) / 256;
     hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w0, s0, w1, s1,
-                       rows, k, gate_up ? 1 : 0, geo.L, geo.CG, geo.P, units,
+                       rows, k, (int)mode, d, geo.L, geo.CG, geo.P, units,
                        static_cast<uint8_t *>(dst));
     return hipGetLastError();
 }
 
-hipError_t launch_unpack(const void *src, int64_t rows, int64_t k, const Geometry &geo,
-                         uint32_t *words, uint16_t *scales, hipStream_t stream)
+hipError_t launch_unpack(const void *src, int64_t rows, int64_t k, PackMode mode, int64_t d,
+                         const Geometry &geo, uint32_t *words, uint16_t *scales,
+                         hipStream_t stream)
 {
     const int64_t items = rows * (k / 32);
     const int64_t blocks = (items + 255) / 256;
     hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       static_cast<const uint8_t *>(src), rows, k, geo.L, geo.CG, geo.P, words,
-                       scales);
+                       static_cast<const uint8_t *>(src), rows, k, (int)mode, d, geo.L, geo.CG,
+                       geo.P, words, scales);
     return hipGetLastError();
 }
 
@@ -928,7 +972,17 @@ struct GemvArgs {
     const Geometry *geo;
     ArgmaxScratch am;
     NormArgs nm;
+    const RopeTab *rp;   // EPI_ROPE only
 };
+
+template <int EPI>
+static typename RopeParam<EPI>::type rope_param(const GemvArgs &a)
+{
+    if constexpr (EPI == EPI_ROPE)
+        return *a.rp;
+    else
+        return NoRope{};
+}
 
 template <int L, int CG, int EPI, bool NORM>
 static void launch_lcen(const GemvPlan &plan, const GemvArgs &a, hipStream_t stream)
@@ -937,15 +991,15 @@ static void launch_lcen(const GemvPlan &plan, const GemvArgs &a, hipStream_t str
     switch (plan.mode) {
     case MODE_SPLIT:
         hipLaunchKernelGGL((gemv_split_kernel<L, CG, EPI, NORM>), grid, block, 0, stream, a.wd, a.x,
-                           a.out, a.rows, a.k, a.geo->tiles, a.n_out, a.am, a.nm);
+                           a.out, a.rows, a.k, a.geo->tiles, a.n_out, a.am, a.nm, rope_param<EPI>(a));
         break;
     case MODE_MULTIPASS:
         hipLaunchKernelGGL((gemv_multipass_kernel<L, CG, EPI, NORM>), grid, block, 0, stream, a.wd,
-                           a.x, a.out, a.rows, a.k, a.geo->P, a.geo->tiles, a.n_out, a.am, a.nm);
+                           a.x, a.out, a.rows, a.k, a.geo->P, a.geo->tiles, a.n_out, a.am, a.nm, rope_param<EPI>(a));
         break;
     case MODE_BLOCK:
         hipLaunchKernelGGL((gemv_block_kernel<L, CG, EPI, NORM>), grid, block, 0, stream, a.wd, a.x,
-                           a.out, a.rows, a.k, a.geo->tiles, a.n_out, a.am, a.nm);
+                           a.out, a.rows, a.k, a.geo->tiles, a.n_out, a.am, a.nm, rope_param<EPI>(a));
         break;
     }
 }
@@ -968,6 +1022,12 @@ static void launch_lc(Epilogue epi, bool norm, const GemvPlan &plan, const GemvA
         else
             launch_lcen<L, CG, EPI_SILU, false>(plan, a, stream);
         break;
+    case EPI_ROPE:
+        if (norm)
+            launch_lcen<L, CG, EPI_ROPE, true>(plan, a, stream);
+        else
+            launch_lcen<L, CG, EPI_ROPE, false>(plan, a, stream);
+        break;
     }
 }
 
@@ -987,13 +1047,33 @@ static bool launch_l(Epilogue epi, bool norm, const GemvPlan &plan, const GemvAr
 hipError_t launch_gemv_family(const Geometry &geo, Epilogue epi, const void *wdata,
                               const uint16_t *x, void *out, int64_t rows, int64_t k,
                               int64_t n_out, ArgmaxScratch am, const NormArgs *norm,
-                              hipStream_t stream)
+                              const RopeArgs *rope, hipStream_t stream)
 {
     if (norm != nullptr && epi == EPI_F32)
         return hipErrorInvalidValue;   // the LM head takes no norm prologue
+    if ((epi == EPI_ROPE) != (rope != nullptr))
+        return hipErrorInvalidValue;
+    if (rope != nullptr && (rope->d < 2 || rope->d / 2 > kRopeMaxHalf))
+        return hipErrorInvalidValue;
     const GemvPlan plan = plan_gemv(geo);
+    RopeTab tab{};
+    if (rope != nullptr) {
+        // the twiddles in f64 on the host, passed to the kernel as f32
+        tab.d = rope->d;
+        tab.nq = rope->nq;
+        tab.nkv = rope->nkv;
+        tab.pos = rope->pos;
+        tab.cache = rope->cache;
+        tab.page_table = rope->page_table;
+        tab.n_pages = rope->n_pages;
+        for (int i = 0; i < rope->d / 2; ++i) {
+            const double ang = (double)rope->pos * pow(rope->base, -2.0 * (double)i / (double)rope->d);
+            tab.cs[i][0] = (float)cos(ang);
+            tab.cs[i][1] = (float)sin(ang);
+        }
+    }
     const GemvArgs a{static_cast<const uint8_t *>(wdata), x, out, rows, k, n_out, &geo, am,
-                     norm != nullptr ? *norm : NormArgs{nullptr, nullptr, nullptr, 0.f}};
+                     norm != nullptr ? *norm : NormArgs{nullptr, nullptr, nullptr, 0.f}, &tab};
     const bool nrm = norm != nullptr;
     bool ok = false;
     switch (geo.L) {

@@ -147,6 +147,57 @@ def test_add_rmsnorm_errors(q4):
     assert g(gu, X, R, Gm, 1e-5, H, X, None) == q4.ERR_ALIAS
 
 
+def rope_weight(q4, n=96, k=96, head_dim=8, **kw):
+    w = weight(q4, n=n, k=k, layout=3, **kw)
+    w.head_dim = head_dim
+    return w
+
+
+def test_rope_errors(q4):
+    lib = q4.lib
+    X, Y, C, T = A + 0x200000, A + 0x300000, A + 0x400000, A + 0x500000
+    W0, S0, D = A + 0x600000, A + 0x700000, A + 0x800000
+    out = q4.q4_weight()
+    pr = lib.q4_pack_rope
+    nb = q4.packed_bytes(96, 96, q4.LAYOUT_ROPE)
+    assert nb == q4.packed_bytes(96, 96)
+    assert pr(W0, S0, 96, 96, 7, D, nb, ctypes.byref(out), None) == q4.ERR_SHAPE   # odd
+    assert pr(W0, S0, 96, 96, 0, D, nb, ctypes.byref(out), None) == q4.ERR_SHAPE
+    assert pr(W0, S0, 96, 96, 64, D, nb, ctypes.byref(out), None) == q4.ERR_SHAPE  # 64 !| 96
+    assert pr(None, S0, 96, 96, 8, D, nb, ctypes.byref(out), None) == q4.ERR_NULL
+    assert pr(W0, S0, 96, 96, 8, D, nb - 1, ctypes.byref(out), None) == q4.ERR_SIZE
+    w = rope_weight(q4)
+    r = ctypes.byref(w)
+    f = lib.q4_qkv_rope_append
+    # 96 rows = 12 heads of 8: 4 q + 4 k + 4 v
+    assert f(ctypes.byref(weight(q4, n=96)), X, 4, 0, 1e4, Y, C, T, 2, None) == q4.ERR_LAYOUT
+    assert f(ctypes.byref(rope_weight(q4, head_dim=7)), X, 4, 0, 1e4, Y, C, T, 2, None) == q4.ERR_SHAPE
+    assert f(ctypes.byref(rope_weight(q4, head_dim=64)), X, 4, 0, 1e4, Y, C, T, 2, None) == q4.ERR_SHAPE
+    assert f(r, X, 5, 0, 1e4, Y, C, T, 2, None) == q4.ERR_SHAPE      # 7 k/v heads: odd
+    assert f(r, X, 13, 0, 1e4, Y, C, T, 2, None) == q4.ERR_SHAPE     # more q heads than heads
+    assert f(r, X, -1, 0, 1e4, Y, C, T, 2, None) == q4.ERR_SHAPE
+    assert f(r, X, 4, -1, 1e4, Y, C, T, 2, None) == q4.ERR_SHAPE
+    assert f(r, X, 4, 0, 0.0, Y, C, T, 2, None) == q4.ERR_SHAPE
+    assert f(r, X, 4, 0, float("nan"), Y, C, T, 2, None) == q4.ERR_SHAPE
+    assert f(r, X, 4, 0, 1e4, Y, C, T, 0, None) == q4.ERR_SHAPE      # a cache of no pages
+    assert f(r, X, 4, 0, 1e4, Y, C, None, 2, None) == q4.ERR_NULL    # a cache needs a table
+    assert f(r, None, 4, 0, 1e4, Y, C, T, 2, None) == q4.ERR_NULL
+    assert f(r, X, 4, 0, 1e4, None, C, T, 2, None) == q4.ERR_NULL
+    assert f(r, X + 8, 4, 0, 1e4, Y, C, T, 2, None) == q4.ERR_ALIGN
+    assert f(r, X, 4, 0, 1e4, Y + 2, C, T, 2, None) == q4.ERR_ALIGN
+    assert f(r, X, 4, 0, 1e4, Y, C + 2, T, 2, None) == q4.ERR_ALIGN
+    assert f(r, X, 4, 0, 1e4, X + 64, C, T, 2, None) == q4.ERR_ALIAS     # qkv over x
+    assert f(r, X, 4, 0, 1e4, Y, Y + 64, T, 2, None) == q4.ERR_ALIAS     # cache over qkv
+    assert f(r, X, 4, 0, 1e4, Y, C, C + 64, 2, None) == q4.ERR_ALIAS     # table inside cache
+    g = lib.q4_add_rmsnorm_qkv_rope_append
+    Gm = A + 0x220000
+    assert g(r, X, None, None, 1e-5, None, 4, 0, 1e4, Y, C, T, 2, None) == q4.ERR_NULL
+    assert g(r, X, None, Gm, -1.0, None, 4, 0, 1e4, Y, C, T, 2, None) == q4.ERR_SHAPE
+    assert g(r, X, None, Gm, 1e-5, None, 4, 0, 1e4, Y, Gm + 32, T, 2, None) == q4.ERR_ALIAS
+    # the other ops refuse the rotary-paired layout
+    assert lib.q4_gemv(r, X, Y, None) == q4.ERR_LAYOUT
+
+
 def test_lmhead_errors(q4):
     lib = q4.lib
     X, L, I, WS = A + 0x200000, A + 0x300000, A + 0x400000, A + 0x500000

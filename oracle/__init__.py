@@ -77,6 +77,9 @@ class Oracle:
         lib.q4o_qkv_rope.restype = ctypes.c_int
         lib.q4o_encode_rope.argtypes = [_P, _P, _I64, _I64, _I64, _P]
         lib.q4o_encode_rope.restype = ctypes.c_int
+        lib.q4o_attention_decode.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _I64,
+                                             ctypes.c_double, _P, _P]
+        lib.q4o_attention_decode.restype = ctypes.c_int
         lib.q4o_argmax.argtypes = [_P, _I64]
         lib.q4o_argmax.restype = ctypes.c_int64
         lib.q4o_lmhead.argtypes = [_P, _P, _P, _I64, _I64, _P, _P]
@@ -198,6 +201,22 @@ class Oracle:
                                    float(base), _ptr(y), _ptr(a))
         assert rc == 0
         return y, a
+
+    def attention_decode(self, q, cache, page_table, ctx: int, nq: int, nkv: int, d: int,
+                         scale: float):
+        """(out f64 [nq][d], a f64 [nq][d]) of one decode token over positions
+        0 .. ctx-1 of the paged cache f16 bits [pages][2][16][nkv][d]."""
+        q = np.ascontiguousarray(q, dtype=np.uint16).reshape(nq * d)
+        cache = np.ascontiguousarray(cache, dtype=np.uint16)
+        assert cache.ndim == 5 and cache.shape[1:] == (2, 16, nkv, d)
+        pt = np.ascontiguousarray(page_table, dtype=np.int32)
+        assert pt.size >= (ctx + 15) // 16
+        out = np.empty((nq, d), np.float64)
+        a = np.empty((nq, d), np.float64)
+        rc = self.lib.q4o_attention_decode(_ptr(q), _ptr(cache), _ptr(pt), cache.shape[0], ctx,
+                                           nq, nkv, d, float(scale), _ptr(out), _ptr(a))
+        assert rc == 0
+        return out, a
 
     def argmax(self, v) -> int:
         v = np.ascontiguousarray(v, dtype=np.float64)

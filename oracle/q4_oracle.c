@@ -33,6 +33,7 @@
  * computing each destination address.
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
@@ -273,6 +274,63 @@ int q4o_qkv_rope(const uint32_t *words, const uint16_t *scales, const uint16_t *
             y[h * d + i] = oi;
             y[h * d + i + d / 2] = oj;
         }
+    return 0;
+}
+
+/*
+ * Paged-attention decode for one token ([P1] 内核融合: attention merges paged
+ * attention with the page-table reads; 完整的推理流水线: vLLM-style page
+ * table).  Cache layout as the fused QKV step writes it:
+ * cache[page][K=0|V=1][16 slots][nkv heads][d], position t in slot t % 16 of
+ * page page_table[t / 16].  Query head h reads kv head h / (nq / nkv).
+ *   s_t = scale * sum_i q[h][i] K_t[i],  p_t = e^(s_t - max s) / sum_u e^(s_u - max s)
+ *   out[h][i] = sum_t p_t V_t[i],        a[h][i] = sum_t p_t |V_t[i]|
+ * over t = 0 .. ctx-1.  q [nq][d], cache f16 bits; out, a f64 [nq][d].
+ * Returns 0, or -1 for a bad shape or a page entry outside [0, n_pages).
+ */
+int q4o_attention_decode(const uint16_t *q, const uint16_t *cache, const int32_t *page_table,
+                         int64_t n_pages, int64_t ctx, int64_t nq, int64_t nkv, int64_t d,
+                         double scale, double *out, double *a)
+{
+    if (ctx < 1 || nq < 1 || nkv < 1 || nq % nkv || d < 1)
+        return -1;
+    for (int64_t t = 0; t < ctx; ++t)
+        if (page_table[t / 16] < 0 || page_table[t / 16] >= n_pages)
+            return -1;
+    double *sc = (double *)malloc(sizeof(double) * (size_t)ctx);
+    if (!sc)
+        return -1;
+    for (int64_t h = 0; h < nq; ++h) {
+        const int64_t g = h / (nq / nkv);
+        double mx = -INFINITY;
+        for (int64_t t = 0; t < ctx; ++t) {
+            const uint16_t *kr = cache + (((int64_t)page_table[t / 16] * 2 + 0) * 16 + t % 16) * nkv * d + g * d;
+            double dot = 0.0;
+            for (int64_t i = 0; i < d; ++i)
+                dot += q4o_half_to_double(q[h * d + i]) * q4o_half_to_double(kr[i]);
+            sc[t] = scale * dot;
+            if (sc[t] > mx)
+                mx = sc[t];
+        }
+        double den = 0.0;
+        for (int64_t t = 0; t < ctx; ++t) {
+            sc[t] = exp(sc[t] - mx);
+            den += sc[t];
+        }
+        for (int64_t i = 0; i < d; ++i) {
+            double o = 0.0, m = 0.0;
+            for (int64_t t = 0; t < ctx; ++t) {
+                const uint16_t *vr = cache + (((int64_t)page_table[t / 16] * 2 + 1) * 16 + t % 16) * nkv * d + g * d;
+                const double v = q4o_half_to_double(vr[i]);
+                o += sc[t] * v;
+                m += sc[t] * fabs(v);
+            }
+            out[h * d + i] = o / den;
+            if (a)
+                a[h * d + i] = m / den;
+        }
+    }
+    free(sc);
     return 0;
 }
 

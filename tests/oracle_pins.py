@@ -18,6 +18,9 @@ What pins what:
   * SiLU / FFN    : silu(0)=0, silu(ln 3)=(3/4)ln 3, silu(-g)=silu(g)-g, the
                     gate (not up) is the one gated.
   * argmax        : planted maximum, ties go to the lowest index.
+  * attention     : one position returns its V row, equal scores the mean of
+                    V, a dominant key its V row, grouped-query heads, page
+                    order invariance.
   * RoPE          : a hand example (pairing and frequency), identity at 0,
                     norm preservation, q.k depends on the position difference
                     only, only q and k heads of the fused QKV rotate; the
@@ -388,6 +391,61 @@ def pin_rope_layout(orc, quick=False):
         assert np.array_equal(dw[:n, :k // 8], w[src]) and np.array_equal(ds[:n, :k // 32], s[src])
 
 
+def _cache(rng, pages, nkv, d, scale=1.0):
+    return si.f16_bits(rng.normal(0.0, scale, (pages, 2, 16, nkv, d)))
+
+
+def pin_attention(orc, quick=False):
+    """Paged-attention decode: one position returns its V row, equal scores
+    return the mean of V, a dominant key selects its V row, the grouped-query
+    head mapping, and the physical page order does not matter."""
+    rng = np.random.default_rng(43)
+    nq, nkv, d = 4, 2, 32
+    pages = 4
+    cache = _cache(rng, pages, nkv, d)
+    q = si.f16_bits(rng.normal(0.0, 1.0, (nq, d)))
+    table = np.array([2, 0, 3, 1], np.int32)
+    V = lambda t, g: cache[table[t // 16], 1, t % 16, g].view(np.float16).astype(np.float64)
+    # a single position: its V row, exactly
+    out, _ = orc.attention_decode(q, cache, table, 1, nq, nkv, d, 0.125)
+    for h in range(nq):
+        assert np.array_equal(out[h], V(0, h // 2))
+    # scale 0 (and equal keys): every weight 1/ctx -> the mean of V
+    ctx = 37
+    out, _ = orc.attention_decode(q, cache, table, ctx, nq, nkv, d, 0.0)
+    for h in range(nq):
+        want = np.mean([V(t, h // 2) for t in range(ctx)], axis=0)
+        assert np.allclose(out[h], want, rtol=1e-12, atol=1e-12)
+    eq = cache.copy()
+    eq[:, 0] = eq[0, 0, 0]            # every key the same row
+    out, _ = orc.attention_decode(q, eq, table, ctx, nq, nkv, d, 0.3)
+    for h in range(nq):
+        want = np.mean([eq[table[t // 16], 1, t % 16, h // 2].view(np.float16).astype(np.float64)
+                        for t in range(ctx)], axis=0)
+        assert np.allclose(out[h], want, rtol=1e-12, atol=1e-12)
+    # a dominant key: position 21 of kv head 1 matches query heads 2 and 3
+    big = cache.copy()
+    big[table[21 // 16], 0, 21 % 16, 1] = si.f16_bits(np.full(d, 4.0))
+    qq = si.f16_bits(np.full((nq, d), 4.0))
+    out, _ = orc.attention_decode(qq, big, table, ctx, nq, nkv, d, 1.0)
+    for h in (2, 3):
+        assert np.allclose(out[h], V(21, 1), rtol=0, atol=1e-12)
+    # grouped heads: constant V per kv head -> each query head returns its group's value
+    grp = cache.copy()
+    for g in range(nkv):
+        grp[:, 1, :, g] = si.f16_bits(np.full(d, g + 1.5))
+    out, _ = orc.attention_decode(q, grp, table, ctx, nq, nkv, d, 0.2)
+    for h in range(nq):
+        assert np.allclose(out[h], h // 2 + 1.5, rtol=1e-14)
+    # the physical page order does not matter
+    perm = np.array([1, 3, 0, 2])
+    moved = np.empty_like(cache)
+    moved[perm] = cache
+    a1, _ = orc.attention_decode(q, cache, table, ctx, nq, nkv, d, 0.17)
+    a2, _ = orc.attention_decode(q, moved, perm[table].astype(np.int32), ctx, nq, nkv, d, 0.17)
+    assert np.array_equal(a1, a2)
+
+
 def load_geometry_golden():
     rows = []
     with open(os.path.join(GOLDEN, "layout_geometry.txt")) as f:
@@ -475,6 +533,6 @@ ALL_PINS = [
     pin_half_decode_all_patterns, pin_half_encode_rne,
     pin_gemv_rational, pin_gemv_exactly_representable, pin_gemv_closed_forms,
     pin_gemv_one_hot, pin_gemv_linearity, pin_gemm_rows,
-    pin_silu, pin_ffn, pin_argmax, pin_lmhead, pin_add_rmsnorm, pin_rope,
+    pin_silu, pin_ffn, pin_argmax, pin_lmhead, pin_add_rmsnorm, pin_rope, pin_attention,
     pin_layout_geometry, pin_layout_hand_example, pin_layout_roundtrip, pin_rope_layout,
 ]

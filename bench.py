@@ -382,6 +382,60 @@ def main():
     return 0
 
 
+def decode_layer(torch, q4, si, np, K, W, ctx):
+    """One whole Phi-3-mini decoder layer per step, in 5 launches (+1 to
+    combine the attention chunks): add + RMSNorm + QKV + RoPE + K/V append,
+    paged attention over ctx positions, O-proj, add + RMSNorm + gate/up +
+    SiLU, down-proj.  Layer copies (weights and cache) rotated over >= 1 GiB."""
+    inp = si.workload(si.LAYER_SET, seed=0)
+    rng = np.random.default_rng(13)
+    (qw, qs), (ow, os_), (dw, ds) = inp["qkv"], inp["o_proj"], inp["down"]
+    fi = si.workload(si.FFN, seed=0)
+    (gw, gs), (uw, us_) = fi["gate"], fi["up"]
+    pages = ctx // 16 + 1
+    layer_bytes = (weight_bytes(9216, 3072) + weight_bytes(3072, 3072) +
+                   2 * weight_bytes(8192, 3072) + weight_bytes(3072, 8192))
+    kv_read = ctx * 2 * 3072 * 2
+    copies = copies_for(layer_bytes + pages * 2 * 16 * 3072 * 2)
+    base = {"qkv": q4.pack_rope(dev_u32(qw), dev_u16(qs), 96),
+            "o": q4.pack(dev_u32(ow), dev_u16(os_)),
+            "gu": q4.pack_gate_up(dev_u32(gw), dev_u16(gs), dev_u32(uw), dev_u16(us_)),
+            "down": q4.pack(dev_u32(dw), dev_u16(ds))}
+    layers = []
+    for c in range(copies):
+        lw = {key: (pw if c == 0 else pw.clone()) for key, pw in base.items()}
+        lw["cache"] = torch.empty((pages, 2, 16, 32, 96), dtype=torch.float16,
+                                  device="cuda").normal_()
+        layers.append(lw)
+    pt = torch.arange(pages, dtype=torch.int32, device="cuda")
+    g1 = dev_f16(si.f16_bits(rng.uniform(0.5, 1.5, 3072)))
+    g2 = dev_f16(si.f16_bits(rng.uniform(0.5, 1.5, 3072)))
+    f16 = dict(dtype=torch.float16, device="cuda")
+    x = dev_f16(inp["x3072"])                     # the previous layer's down-proj output
+    res = [dev_f16(si.f16_bits(rng.normal(0.0, 2.0, 3072))), torch.empty(3072, **f16)]
+    res2 = torch.empty(3072, **f16)
+    qkv, att = torch.empty(9216, **f16), torch.empty((32, 96), **f16)
+    o, h, y = torch.empty(3072, **f16), torch.empty(8192, **f16), torch.empty(3072, **f16)
+    ws = q4.workspace(x.device, int(q4.lib.q4_workspace_bytes(q4.OP_ATTENTION, ctx, 32, 96)))
+
+    def step(i):
+        L = layers[i % copies]
+        pos = ctx - 1
+        q4.qkv_rope_append(L["qkv"], x, 32, pos, 10000.0, L["cache"], pt, out=qkv,
+                           norm=(res[0], g1, 1e-5, res[1]))
+        q4.attention_decode(qkv[:3072], L["cache"], pt, ctx, 32, 96 ** -0.5, out=att, ws=ws)
+        q4.gemv(L["o"], att.view(-1), out=o)
+        q4.add_rmsnorm_ffn_gate_up_silu(L["gu"], o, res[1], g2, 1e-5, residual_out=res2, out=h)
+        q4.gemv(L["down"], h, out=y)
+
+    ms = timed(torch, step, K, W)
+    nb = layer_bytes + kv_read
+    return {"us": round(ms * 1000, 3), "ctx": ctx, "launches": 6 if ctx > 256 else 5,
+            "weight_bytes": layer_bytes, "kv_bytes_read": kv_read,
+            "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
+            "frac": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "layer_copies": copies}
+
+
 def variants(torch, q4, si, np, K, W):
     out = {}
     # single GEMV 3072^2
@@ -450,6 +504,27 @@ def variants(torch, q4, si, np, K, W):
                                         "frac": round(nb / us_r / 1e3 / PEAK_HBM_GBS, 4),
                                         "bytes": nb}
     del rot, cache
+
+    # paged-attention decode, Phi-3 heads (32 x 96), 4096 positions; caches
+    # rotated over >= 1 GiB so the K/V rows come from HBM
+    ctx = 4096
+    pages = ctx // 16
+    kv_bytes = pages * 2 * 16 * 3072 * 2
+    ncache = copies_for(kv_bytes)
+    caches = [torch.empty((pages, 2, 16, 32, 96), dtype=torch.float16, device="cuda").normal_()
+              for _ in range(ncache)]
+    pt = torch.randperm(pages, device="cuda").to(torch.int32)
+    qv = torch.randn(32 * 96, device="cuda").to(torch.float16)
+    ao = torch.empty((32, 96), dtype=torch.float16, device="cuda")
+    ws = q4.workspace(qv.device, int(q4.lib.q4_workspace_bytes(q4.OP_ATTENTION, ctx, 32, 96)))
+    us = per_launch_us(torch, lambda i: q4.attention_decode(qv, caches[i % ncache], pt, ctx, 32,
+                                                            96 ** -0.5, out=ao, ws=ws), K, W)
+    nb = kv_bytes + 2 * 2 * 3072 + 4 * pages
+    out["attention_decode_32x96_ctx4096"] = {"us": round(us, 3), "gbs": round(nb / us / 1e3, 1),
+                                             "frac": round(nb / us / 1e3 / PEAK_HBM_GBS, 4),
+                                             "bytes": nb, "launches": 2}
+    del caches
+    out["decode_layer_phi3_ctx1024"] = decode_layer(torch, q4, si, np, K, W, 1024)
 
     # LM head, f32 logits + argmax
     inp = si.workload(si.LM_HEAD, seed=0)

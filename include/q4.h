@@ -84,6 +84,7 @@ extern "C" {
 #define Q4_OP_GEMM    2
 #define Q4_OP_FFN     3
 #define Q4_OP_LMHEAD  4
+#define Q4_OP_ATTENTION 5  /* q4_workspace_bytes(Q4_OP_ATTENTION, ctx, n_q_heads, head_dim) */
 
 /*
  * Host-side descriptor of a packed weight, filled by q4_pack*; only `data`
@@ -279,6 +280,29 @@ int q4_add_rmsnorm_qkv_rope_append(const q4_weight *w, const uint16_t *x,
                                    uint16_t *residual_out, int32_t n_q_heads, int32_t pos,
                                    double rope_base, uint16_t *qkv, uint16_t *kv_cache,
                                    const int32_t *page_table, int32_t n_pages, void *stream);
+
+/*
+ * Paged-attention decode for one token ([P1] 内核融合: attention merges paged
+ * attention with the page-table reads), over the cache q4_qkv_rope_append
+ * fills:  for query head h (kv head g = h / (nq / nkv)) and positions
+ * t = 0 .. ctx-1 (slot t % 16 of page page_table[t / 16]):
+ *   s_t = scale * q_h . K_t,   p = softmax(s),   out_h = sum_t p_t V_t
+ * (f32 arithmetic, f16 out).
+ *   q          : device f16 [nq][d], 16-byte aligned (the roped q heads)
+ *   kv_cache   : device f16 [n_pages][2][16][nkv][d], 16-byte aligned
+ *   page_table : device int32, (ctx + 15) / 16 entries in [0, n_pages); an
+ *                entry outside that range makes its 16 positions count as
+ *                absent (a head with every position absent gives NaN)
+ *   d          : 32 .. 256, a multiple of 32;  nq % nkv == 0;  ctx >= 1
+ *   out        : device f16 [nq][d], 4-byte aligned
+ *   ws         : q4_workspace_bytes(Q4_OP_ATTENTION, ctx, nq, d) bytes, 16-byte
+ *                aligned (NULL when that is 0: contexts of <= 256 positions
+ *                need none; longer ones take a second, combining launch)
+ * Errors: NULL, SHAPE, ALIGN, WORKSPACE, ALIAS, HIP.
+ */
+int q4_attention_decode(const uint16_t *q, const uint16_t *kv_cache, const int32_t *page_table,
+                        int32_t n_pages, int32_t ctx, int32_t nq, int32_t nkv, int32_t d,
+                        float scale, uint16_t *out, void *ws, int64_t ws_bytes, void *stream);
 
 /* Static text for a return code. */
 const char *q4_strerror(int code);

@@ -9,7 +9,7 @@ section 完整的推理流水线; the fused FFN of its section 内核融合).
 This module only marshals arguments: torch tensors provide device memory and
 the current stream, and every step runs in the HIP kernels of ``libq4.so``.
 There is no fallback: importing fails if the library is not built
-(``python -m int4_quantized_decode_q4_amd.build``), and every call raises
+(``python int4_quantized_decode_q4_amd/build.py``), and every call raises
 ``Q4Error`` with the library's return code on failure.
 
 Tensor conventions: f16 data as ``torch.float16`` (or 16-bit integer views);
@@ -27,7 +27,7 @@ import torch
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq4.so")
 if not os.path.exists(LIBRARY):
     raise ImportError(
-        f"{LIBRARY} is not built; run `python -m int4_quantized_decode_q4_amd.build`")
+        f"{LIBRARY} is not built; run `python int4_quantized_decode_q4_amd/build.py`")
 
 _lib = ctypes.CDLL(LIBRARY)
 
@@ -36,7 +36,7 @@ ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_LAYOUT = -1, -2, -3, -4
 ERR_WORKSPACE, ERR_ALIAS, ERR_HIP, ERR_SIZE = -5, -6, -7, -8
 LAYOUT_ROWS, LAYOUT_GATE_UP, LAYOUT_ROPE, LAYOUT_VERSION = 1, 2, 3, 1
 GEMM_AUTO, GEMM_VALU, GEMM_MFMA = 0, 1, 2
-OP_GEMV, OP_GEMM, OP_FFN, OP_LMHEAD = 1, 2, 3, 4
+OP_GEMV, OP_GEMM, OP_FFN, OP_LMHEAD, OP_ATTENTION = 1, 2, 3, 4, 5
 
 
 class q4_weight(ctypes.Structure):
@@ -69,6 +69,8 @@ _SIGNATURES = {
     "q4_add_rmsnorm_gemv": (ctypes.c_int, [_W, _P, _P, _P, ctypes.c_float, _P, _P, _P]),
     "q4_add_rmsnorm_ffn_gate_up_silu": (ctypes.c_int, [_W, _P, _P, _P, ctypes.c_float, _P, _P, _P]),
     "q4_lmhead_f32": (ctypes.c_int, [_W, _P, _P, _P, _P, _I64, _P]),
+    "q4_attention_decode": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                           ctypes.c_float, _P, _P, _I64, _P]),
     "q4_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "q4_last_hip_error": (ctypes.c_int, []),
     "q4_layout_geometry": (ctypes.c_int, [_I32, _I32, _P]),
@@ -333,6 +335,33 @@ def qkv_rope_append(w: PackedWeight, x: torch.Tensor, n_q_heads: int, pos: int,
                                                    pro, n_q_heads, pos, float(rope_base), py, pc,
                                                    pt, npages, _stream(x)),
                "q4_add_rmsnorm_qkv_rope_append")
+    return out
+
+
+def attention_decode(q: torch.Tensor, kv_cache: torch.Tensor, page_table: torch.Tensor, ctx: int,
+                     n_q_heads: int, scale: float, out: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out f16 [nq][d]: one decode token's attention over positions 0..ctx-1
+    of the paged cache f16 [pages][2][16][n_kv][d] (q4_attention_decode)."""
+    if kv_cache.dim() != 5 or kv_cache.element_size() != 2 or not kv_cache.is_contiguous():
+        raise ValueError("kv_cache must be a contiguous 16-bit [pages][2][16][n_kv][d] tensor")
+    pages, _, _, nkv, d = kv_cache.shape
+    pq = _dev(q, "q", 2)
+    if q.numel() != n_q_heads * d:
+        raise ValueError(f"q has {q.numel()} elements, expected {n_q_heads * d}")
+    pt = _dev(page_table, "page_table", 4)
+    if out is None:
+        out = torch.empty((n_q_heads, d), dtype=torch.float16, device=q.device)
+    po = _dev(out, "out", 2)
+    need = int(_lib.q4_workspace_bytes(OP_ATTENTION, ctx, n_q_heads, d))
+    pws = None
+    if need > 0:
+        if ws is None:
+            ws = workspace(q.device, need)
+        pws = ws.data_ptr()
+    _check(_lib.q4_attention_decode(pq, kv_cache.data_ptr(), pt, pages, ctx, n_q_heads, nkv, d,
+                                    float(scale), po, pws, need if need > 0 else 0, _stream(q)),
+           "q4_attention_decode")
     return out
 
 

@@ -1,6 +1,9 @@
 """Build libq4.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m int4_quantized_decode_q4_amd.build
+    python int4_quantized_decode_q4_amd/build.py
+
+This file is loaded by path, never through the package: importing the
+package needs a built (and current) libq4.so, which is what this makes.
 
 Each source is compiled by hipcc to an object under ``_build/`` (in
 parallel), then linked into ``int4_quantized_decode_q4_amd/libq4.so``.
@@ -17,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libq4.so")
-SOURCES = ["q4_kernels.hip", "q4_gemm.hip", "q4_api.cpp"]
+SOURCES = ["q4_kernels.hip", "q4_gemm.hip", "q4_attention.hip", "q4_api.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -127,6 +127,8 @@ int64_t q4_workspace_bytes(int32_t op, int32_t m, int32_t n, int32_t k)
 {
     if (m < 1 || !valid_shape(n, k))
         return 0;
+    if (op == Q4_OP_ATTENTION)   // m = ctx, n = query heads, k = head dim
+        return (k % 32 == 0 && k <= 256) ? q4::attention_workspace_bytes(m, n, k) : 0;
     if (op == Q4_OP_LMHEAD) {
         q4::Geometry geo;
         if (!q4::layout_geometry(n, k, &geo))
@@ -449,6 +451,34 @@ int q4_add_rmsnorm_qkv_rope_append(const q4_weight *w, const uint16_t *x,
     const q4::NormArgs nm{residual, gamma, residual_out, eps};
     return qkv_rope_common(w, x, &nm, n_q_heads, pos, rope_base, qkv, kv_cache, page_table,
                            n_pages, stream);
+}
+
+int q4_attention_decode(const uint16_t *q, const uint16_t *kv_cache, const int32_t *page_table,
+                        int32_t n_pages, int32_t ctx, int32_t nq, int32_t nkv, int32_t d,
+                        float scale, uint16_t *out, void *ws, int64_t ws_bytes, void *stream)
+{
+    if (!q || !kv_cache || !page_table || !out)
+        return Q4_ERR_NULL;
+    if (ctx < 1 || n_pages < 1 || nq < 1 || nkv < 1 || nq % nkv != 0 || d < 32 || d > 256 ||
+        d % 32 != 0 || !std::isfinite(scale))
+        return Q4_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(page_table, 4) || !aligned(out, 4) ||
+        (ws && !aligned(ws, 16)))
+        return Q4_ERR_ALIGN;
+    const int64_t need = q4::attention_workspace_bytes(ctx, nq, d);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return Q4_ERR_WORKSPACE;
+    const int64_t qb = 2 * (int64_t)nq * d, cb = (int64_t)n_pages * 2 * 16 * nkv * d * 2;
+    const int64_t tb = 4 * (((int64_t)ctx + 15) / 16);
+    if (overlap(out, qb, q, qb) || overlap(out, qb, kv_cache, cb) || overlap(out, qb, page_table, tb))
+        return Q4_ERR_ALIAS;
+    if (need > 0 && (overlap(ws, need, q, qb) || overlap(ws, need, kv_cache, cb) ||
+                     overlap(ws, need, page_table, tb) || overlap(ws, need, out, qb)))
+        return Q4_ERR_ALIAS;
+    (void)hipGetLastError();
+    return hip_status(q4::launch_attention(q, kv_cache, page_table, n_pages, ctx, nq, nkv, d, scale,
+                                           out, need > 0 ? ws : nullptr,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 const char *q4_strerror(int code)

@@ -86,6 +86,13 @@ hipError_t launch_gemv_family(const Geometry &geo, Epilogue epi, const void *wda
                               int64_t n_out, ArgmaxScratch am, const NormArgs *norm,
                               const RopeArgs *rope, hipStream_t stream);
 
+// Paged-attention decode (q4_attention.hip): workspace bytes (0 when the
+// context fits one chunk) and the launch.
+int64_t attention_workspace_bytes(int64_t ctx, int64_t nq, int64_t d);
+hipError_t launch_attention(const uint16_t *q, const uint16_t *cache, const int32_t *page_table,
+                            int32_t n_pages, int32_t ctx, int32_t nq, int32_t nkv, int32_t d,
+                            float scale, uint16_t *out, void *ws, hipStream_t stream);
+
 enum GemmPath { GEMM_PATH_AUTO = 0, GEMM_PATH_VALU = 1, GEMM_PATH_MFMA = 2 };
 
 // Whether the MFMA GEMM kernel takes weights of this geometry (single pass,

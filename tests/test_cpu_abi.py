@@ -198,6 +198,39 @@ def test_rope_errors(q4):
     assert lib.q4_gemv(r, X, Y, None) == q4.ERR_LAYOUT
 
 
+def test_attention_errors(q4):
+    lib = q4.lib
+    Q, C, T, O, Wk = A + 0x200000, A + 0x1000000, A + 0x300000, A + 0x400000, A + 0x500000
+    f = lib.q4_attention_decode
+    need = lib.q4_workspace_bytes(q4.OP_ATTENTION, 4096, 32, 96)
+    assert need == 32 * 16 * (96 + 2) * 4
+    assert lib.q4_workspace_bytes(q4.OP_ATTENTION, 256, 32, 96) == 0   # one chunk: none
+    ok = (Q, C, T, 300, 4096, 32, 32, 96, 0.1, O, Wk, need, None)
+    def call(**kw):
+        names = ("q", "c", "t", "pages", "ctx", "nq", "nkv", "d", "scale", "o", "ws", "wsb", "s")
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return f(*[args[n] for n in names])
+    assert call(q=None) == q4.ERR_NULL
+    assert call(c=None) == q4.ERR_NULL
+    assert call(t=None) == q4.ERR_NULL
+    assert call(o=None) == q4.ERR_NULL
+    assert call(ctx=0) == q4.ERR_SHAPE
+    assert call(pages=0) == q4.ERR_SHAPE
+    assert call(nq=30, nkv=4) == q4.ERR_SHAPE        # nq % nkv
+    assert call(d=80) == q4.ERR_SHAPE                # not a multiple of 32
+    assert call(d=288) == q4.ERR_SHAPE
+    assert call(scale=float("inf")) == q4.ERR_SHAPE
+    assert call(q=Q + 8) == q4.ERR_ALIGN
+    assert call(c=C + 8) == q4.ERR_ALIGN
+    assert call(o=O + 2) == q4.ERR_ALIGN
+    assert call(ws=None) == q4.ERR_WORKSPACE
+    assert call(wsb=need - 4) == q4.ERR_WORKSPACE
+    assert call(o=Q + 64) == q4.ERR_ALIAS            # out over q
+    assert call(o=C + 4096) == q4.ERR_ALIAS          # out inside the cache
+    assert call(ws=O) == q4.ERR_ALIAS                # workspace over out
+
+
 def test_lmhead_errors(q4):
     lib = q4.lib
     X, L, I, WS = A + 0x200000, A + 0x300000, A + 0x400000, A + 0x500000

@@ -404,7 +404,7 @@ def decode_layer(torch, q4, si, np, K, W, ctx):
     layers = []
     for c in range(copies):
         lw = {key: (pw if c == 0 else pw.clone()) for key, pw in base.items()}
-        lw["cache"] = torch.empty((pages, 2, 16, 32, 96), dtype=torch.float16,
+        lw["cache"] = torch.empty((pages, 2, 32, 16, 96), dtype=torch.float16,
                                   device="cuda").normal_()
         layers.append(lw)
     pt = torch.arange(pages, dtype=torch.int32, device="cuda")
@@ -493,7 +493,7 @@ def variants(torch, q4, si, np, K, W):
     # position 1000 and the K/V append into a 64-page cache, with and without
     # the add + RMSNorm prologue
     rot = Rotation(q4, q4.pack_rope(dev_u32(w), dev_u16(s_), 96), copies_for(weight_bytes(9216, 3072)))
-    cache = torch.zeros((64, 2, 16, 32, 96), dtype=torch.float16, device="cuda")
+    cache = torch.zeros((64, 2, 32, 16, 96), dtype=torch.float16, device="cuda")
     pt = torch.arange(64, dtype=torch.int32, device="cuda")
     us_r = per_launch_us(torch, lambda i: q4.qkv_rope_append(rot[i], x, 32, 1000, 10000.0, cache, pt, out=y), K, W)
     us_rn = per_launch_us(torch, lambda i: q4.qkv_rope_append(rot[i], x, 32, 1000, 10000.0, cache, pt, out=y,
@@ -511,7 +511,7 @@ def variants(torch, q4, si, np, K, W):
     pages = ctx // 16
     kv_bytes = pages * 2 * 16 * 3072 * 2
     ncache = copies_for(kv_bytes)
-    caches = [torch.empty((pages, 2, 16, 32, 96), dtype=torch.float16, device="cuda").normal_()
+    caches = [torch.empty((pages, 2, 32, 16, 96), dtype=torch.float16, device="cuda").normal_()
               for _ in range(ncache)]
     pt = torch.randperm(pages, device="cuda").to(torch.int32)
     qv = torch.randn(32 * 96, device="cuda").to(torch.float16)

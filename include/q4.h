@@ -106,8 +106,9 @@ typedef struct q4_weight {
 int64_t q4_packed_bytes(int32_t n, int32_t k, int32_t layout);
 
 /* Bytes of device workspace an op needs (0 = none).  The LM-head argmax needs
- * one (per-block candidates; contents need no initialisation).  Two calls
- * that share a workspace must be ordered on one stream. */
+ * one (per-block candidates), and so does q4_attention_decode over a context
+ * split into chunks (per-chunk records); contents need no initialisation.
+ * Two calls that share a workspace must be ordered on one stream. */
 int64_t q4_workspace_bytes(int32_t op, int32_t m, int32_t n, int32_t k);
 
 /*
@@ -255,9 +256,10 @@ int q4_add_rmsnorm_ffn_gate_up_silu(const q4_weight *w, const uint16_t *x,
  *   w          : Q4_LAYOUT_ROPE (q4_pack_rope)
  *   x          : device f16 [k], 16-byte aligned
  *   qkv        : device f16 [n], 4-byte aligned: y after RoPE
- *   kv_cache   : device f16 [n_pages][2][16][nkv][d] or NULL (no append):
- *                page, then K (0) / V (1), then the 16 token slots of the
- *                page, then head, then dim; the k and v heads of y (k after
+ *   kv_cache   : device f16 [n_pages][2][nkv][16][d] or NULL (no append):
+ *                page, then K (0) / V (1), then head, then the 16 token
+ *                slots of the page, then dim (one head's 16 rows of a page
+ *                are contiguous); the k and v heads of y (k after
  *                RoPE) are written to slot pos % 16 of page
  *                page_table[pos / 16]; nothing else is written
  *   page_table : device int32, at least pos / 16 + 1 entries (needed with a
@@ -289,15 +291,18 @@ int q4_add_rmsnorm_qkv_rope_append(const q4_weight *w, const uint16_t *x,
  *   s_t = scale * q_h . K_t,   p = softmax(s),   out_h = sum_t p_t V_t
  * (f32 arithmetic, f16 out).
  *   q          : device f16 [nq][d], 16-byte aligned (the roped q heads)
- *   kv_cache   : device f16 [n_pages][2][16][nkv][d], 16-byte aligned
+ *   kv_cache   : device f16 [n_pages][2][nkv][16][d], 16-byte aligned
  *   page_table : device int32, (ctx + 15) / 16 entries in [0, n_pages); an
  *                entry outside that range makes its 16 positions count as
  *                absent (a head with every position absent gives NaN)
- *   d          : 32 .. 256, a multiple of 32;  nq % nkv == 0;  ctx >= 1
+ *   d          : 32 .. 256, a multiple of 32;  nq % nkv == 0;  ctx >= 1;
+ *                one page (2 * nkv * 16 * d halves) under 2 GiB
  *   out        : device f16 [nq][d], 4-byte aligned
  *   ws         : q4_workspace_bytes(Q4_OP_ATTENTION, ctx, nq, d) bytes, 16-byte
- *                aligned (NULL when that is 0: contexts of <= 256 positions
- *                need none; longer ones take a second, combining launch)
+ *                aligned (NULL when that is 0: a context short enough for
+ *                one block per head needs none; a longer one is split into
+ *                chunks whose f32 records a second launch merges; contents
+ *                need no initialisation)
  * Errors: NULL, SHAPE, ALIGN, WORKSPACE, ALIAS, HIP.
  */
 int q4_attention_decode(const uint16_t *q, const uint16_t *kv_cache, const int32_t *page_table,

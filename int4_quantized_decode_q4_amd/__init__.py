@@ -308,7 +308,7 @@ def qkv_rope_append(w: PackedWeight, x: torch.Tensor, n_q_heads: int, pos: int,
                     page_table: Optional[torch.Tensor] = None,
                     out: Optional[torch.Tensor] = None, norm=None) -> torch.Tensor:
     """qkv f16 [n]: the fused QKV projection with RoPE on the q and k heads,
-    the k and v heads appended to kv_cache f16 [pages][2][16][n_kv][d] at
+    the k and v heads appended to kv_cache f16 [pages][2][n_kv][16][d] at
     slot pos % 16 of page page_table[pos // 16] (q4_qkv_rope_append).
     norm = (residual or None, gamma, eps, residual_out or None) runs the add
     + RMSNorm prologue first (q4_add_rmsnorm_qkv_rope_append)."""
@@ -319,7 +319,7 @@ def qkv_rope_append(w: PackedWeight, x: torch.Tensor, n_q_heads: int, pos: int,
     pc, pt, npages = None, None, 0
     if kv_cache is not None:
         if kv_cache.element_size() != 2 or not kv_cache.is_contiguous() or kv_cache.dim() != 5:
-            raise ValueError("kv_cache must be a contiguous 16-bit [pages][2][16][n_kv][d] tensor")
+            raise ValueError("kv_cache must be a contiguous 16-bit [pages][2][n_kv][16][d] tensor")
         pc = kv_cache.data_ptr()
         npages = kv_cache.shape[0]
         if page_table is None:
@@ -342,10 +342,10 @@ def attention_decode(q: torch.Tensor, kv_cache: torch.Tensor, page_table: torch.
                      n_q_heads: int, scale: float, out: Optional[torch.Tensor] = None,
                      ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out f16 [nq][d]: one decode token's attention over positions 0..ctx-1
-    of the paged cache f16 [pages][2][16][n_kv][d] (q4_attention_decode)."""
+    of the paged cache f16 [pages][2][n_kv][16][d] (q4_attention_decode)."""
     if kv_cache.dim() != 5 or kv_cache.element_size() != 2 or not kv_cache.is_contiguous():
-        raise ValueError("kv_cache must be a contiguous 16-bit [pages][2][16][n_kv][d] tensor")
-    pages, _, _, nkv, d = kv_cache.shape
+        raise ValueError("kv_cache must be a contiguous 16-bit [pages][2][n_kv][16][d] tensor")
+    pages, _, nkv, _, d = kv_cache.shape
     pq = _dev(q, "q", 2)
     if q.numel() != n_q_heads * d:
         raise ValueError(f"q has {q.numel()} elements, expected {n_q_heads * d}")

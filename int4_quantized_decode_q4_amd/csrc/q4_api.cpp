@@ -459,8 +459,9 @@ int q4_attention_decode(const uint16_t *q, const uint16_t *kv_cache, const int32
 {
     if (!q || !kv_cache || !page_table || !out)
         return Q4_ERR_NULL;
+    // one page of the cache (K and V halves) is addressed with 32-bit offsets
     if (ctx < 1 || n_pages < 1 || nq < 1 || nkv < 1 || nq % nkv != 0 || d < 32 || d > 256 ||
-        d % 32 != 0 || !std::isfinite(scale))
+        d % 32 != 0 || !std::isfinite(scale) || (int64_t)nkv * 16 * d * 2 * 2 > INT32_MAX)
         return Q4_ERR_SHAPE;
     if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(page_table, 4) || !aligned(out, 4) ||
         (ws && !aligned(ws, 16)))

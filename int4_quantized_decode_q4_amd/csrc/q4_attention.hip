@@ -7,18 +7,36 @@
 // page-table reads) and section 完整的推理流水线 (vLLM-style page table).
 //
 // Design (split over the context, as flash-decoding does for one query):
-//  * a block owns one query head and a chunk of 256 positions (16 pages); its
-//    4 wavefronts take 64 positions each, 16 at a time: 4 lanes per
-//    position, each lane d/4 dims, so one step reads 16 whole K rows and 16
-//    whole V rows of one page (the page index is uniform over the step);
-//  * the next step's rows are requested before the current one is used;
+//  * the cache is head-major inside a page ([page][K|V][head][slot][dim]),
+//    so the 16 K rows (and the 16 V rows) one head takes from a page are one
+//    contiguous run of 32 d bytes;
+//  * a block owns one query head and a chunk of positions, sized from the
+//    context so the grid holds about one block per compute unit (measured
+//    best: more, shorter blocks and more wavefronts per block were slower);
+//    its 4 wavefronts take a quarter each, 16 positions (one page) at a
+//    time: 4 lanes per
+//    position, each lane d/4 dims interleaved in 16-byte pieces, so every
+//    load instruction reads 16 whole 64-byte spans; the wavefront's page
+//    indices are read once, one per lane;
+//  * the next step's rows are requested before the current one is used, by
+//    buffer loads through a resource that spans the head's K and V runs of
+//    the step's page; a step past the wavefront's end or on an absent page
+//    gets a resource of size 0, whose loads return zeros without touching
+//    memory, so every load is issued unconditionally and the compiler's
+//    vmcnt waits stay exact (a branch around the loads makes it wait for
+//    all of them);
 //  * scores: f16 pairs through v_dot2_f32_f16, summed over the 4 lanes of a
-//    position with DPP, times the caller's scale; an online softmax per
-//    wavefront (running max and sum, the accumulator rescaled when the max
-//    grows), exp in f32;
+//    position with DPP, times scale * log2(e), so the softmax runs in base 2
+//    (e^(s - m) = 2^((s - m) log2 e); one v_exp_f32 per exponential); every
+//    lane runs its own online softmax (running max and sum, the accumulator
+//    rescaled when the max grows) and the lanes of a dim slice merge their
+//    states once at the end, so a step has no wavefront-wide exchange;
 //  * the 4 wavefronts are combined in LDS; with one chunk the block writes
 //    the f16 output, otherwise it writes (max, sum, weighted V) to the
-//    workspace and a second launch combines the chunks.
+//    workspace and a second launch merges the chunks of each head (merging
+//    in the last block of a head instead needs an agent-scope release per
+//    block and an acquire in the last one, which write back and invalidate
+//    the L2; measured slower than the second launch).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -31,19 +49,21 @@ namespace q4 {
 namespace {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+constexpr int kBufferWord3 = 0x00020000;   // gfx9-family raw buffer format
 
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 
-constexpr int kChunk = 256;   // positions per block
-constexpr int kStep = 16;     // positions per wavefront step
-
-__device__ __forceinline__ float wave_max(float v)
-{
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1)
-        v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
+#ifndef Q4_ATT_DEPTH
+#define Q4_ATT_DEPTH 2
+#endif
+#ifndef Q4_ATT_WAVES
+#define Q4_ATT_WAVES 4
+#endif
+constexpr int kWaves = Q4_ATT_WAVES;              // wavefronts per block
+constexpr int kStep = 16;                         // positions per wavefront step (one page)
+constexpr int kMinChunk = kStep * kWaves;         // positions per block: one step per wavefront ..
+constexpr int kMaxChunk = 64 * kStep * kWaves;    // .. up to 64 pages per wavefront
 
 __device__ __forceinline__ float dot8(uint4 a, uint4 b, float acc)
 {
@@ -65,52 +85,84 @@ __device__ __forceinline__ void axpy8(float p, uint4 v, float *acc)
     }
 }
 
-// DL = d / 32: 16-byte loads per lane per row (each lane d/4 dims).
+// 2^x in f32 (v_exp_f32; 2^-inf = 0).
+__device__ __forceinline__ float exp2_f32(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Merge two online-softmax states (max m, sum l, accumulator acc; scores in
+// base-2 units): the result is the state of the union of their positions.
+template <int LD>
+__device__ __forceinline__ void merge_state(float &m, float &l, float *acc, float mo, float lo,
+                                            const float *acco)
+{
+    const float mn = fmaxf(m, mo);
+    const float e1 = m == -INFINITY ? 0.f : exp2_f32(m - mn);
+    const float e2 = mo == -INFINITY ? 0.f : exp2_f32(mo - mn);
+    l = l * e1 + lo * e2;
+#pragma unroll
+    for (int i = 0; i < LD; ++i)
+        acc[i] = acc[i] * e1 + acco[i] * e2;
+    m = mn;
+}
+
+// DL = d / 32: 16-byte loads per lane per row (each lane d/4 dims).  Every
+// lane keeps its own online softmax over the positions it meets (no
+// cross-lane work per step beyond the 4-lane score sum); the 16 lanes of a
+// dim slice merge their states once at the end.
 template <int DL>
-__global__ __launch_bounds__(256) void attention_decode_kernel(
+__global__ __launch_bounds__(64 * kWaves) void attention_decode_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ cache,
     const int32_t *__restrict__ page_table, int32_t n_pages, int32_t ctx, int32_t nq,
-    int32_t nkv, float scale, uint16_t *__restrict__ out, float *__restrict__ partial)
+    int32_t nkv, int32_t chunk_len, float scale, uint16_t *__restrict__ out,
+    float *__restrict__ partial)
 {
     constexpr int D = 32 * DL;
     constexpr int LD = 8 * DL;   // dims per lane
-    __shared__ float wm[4], wl[4];
-    __shared__ float wacc[4][D];
+    constexpr int R = Q4_ATT_DEPTH;   // steps in flight
+    __shared__ float wm[kWaves], wl[kWaves];
+    __shared__ float wacc[kWaves][D];
     const int lane = threadIdx.x & 63;
+    const float scale2 = scale * 1.44269504088896340736f;   // scores in base-2 units
     const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int h = blockIdx.x % nq, chunk = blockIdx.x / nq;
     const int g = h / (nq / nkv);
     const int sub = lane & 3, slot = lane >> 2;
-    const int64_t row_stride = (int64_t)nkv * D;   // halves between slots of a page
+    const int64_t half_page = (int64_t)nkv * 16 * D;   // halves of the K (or V) half of a page
+    // byte offsets inside a step's resource: this lane's pieces of its row in
+    // the K run, and the V run half a page further on
+    const int k_off = slot * D * 2 + sub * 16;
+    const int v_off = k_off + (int)(half_page * 2);
+    const int span = (int)(half_page * 2) + 32 * D;
 
+    // lane `sub` holds the 16-byte pieces sub, sub + 4, ... of a row, so the
+    // 4 lanes of a position read 64 contiguous bytes per load instruction
     uint4 qv[DL];
 #pragma unroll
     for (int j = 0; j < DL; ++j)
-        qv[j] = reinterpret_cast<const uint4 *>(q + (int64_t)h * D + sub * LD)[j];
+        qv[j] = reinterpret_cast<const uint4 *>(q + (int64_t)h * D)[4 * j + sub];
 
-    const int t_begin = chunk * kChunk + w * (kChunk / 4);
-    const int t_end = min(t_begin + kChunk / 4, ctx);
+    const int t_begin = chunk * chunk_len + w * (chunk_len / kWaves);
+    const int t_end = min(t_begin + chunk_len / kWaves, ctx);
+    // the wavefront's page indices (at most 64), one per lane, read once: a
+    // step's K/V addresses then never wait on the table
+    const int npg = t_begin < t_end ? (t_end - t_begin + kStep - 1) / kStep : 0;
+    const int32_t my_page = lane < npg ? page_table[(t_begin >> 4) + lane] : -1;
     struct Rows {
         uint4 k[DL], v[DL];
         bool ok;
     };
     auto load = [&](Rows &r, int t0) {
-        // t0 % 16 == 0: the step is one page; entries outside the cache read nothing
-        r.ok = false;
-        if (t0 < t_end) {
-            const int32_t page = page_table[t0 >> 4];
-            if (page >= 0 && page < n_pages) {
-                r.ok = true;
-                const uint16_t *base = cache + ((int64_t)page * 2 * 16 + slot) * row_stride +
-                                       (int64_t)g * D + sub * LD;
-                const uint4 *kp = reinterpret_cast<const uint4 *>(base);
-                const uint4 *vp = reinterpret_cast<const uint4 *>(base + 16 * row_stride);
+        // t0 % 16 == 0: the step is one page (uniform over the wavefront)
+        const int32_t page = t0 < t_end ? __builtin_amdgcn_readlane(my_page, (t0 - t_begin) >> 4) : -1;
+        r.ok = page >= 0 && page < n_pages;
+        const uint16_t *base = cache + (r.ok ? (int64_t)page * 2 * half_page + (int64_t)g * 16 * D : 0);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(base), (short)0, r.ok ? span : 0, kBufferWord3);
 #pragma unroll
-                for (int j = 0; j < DL; ++j) {
-                    r.k[j] = kp[j];
-                    r.v[j] = vp[j];
-                }
-            }
+        for (int j = 0; j < DL; ++j) {
+            const v4u k = __builtin_amdgcn_raw_buffer_load_b128(rs, k_off + 64 * j, 0, 0);
+            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, v_off + 64 * j, 0, 0);
+            r.k[j] = make_uint4(k.x, k.y, k.z, k.w);
+            r.v[j] = make_uint4(v.x, v.y, v.z, v.w);
         }
     };
 
@@ -118,81 +170,86 @@ __global__ __launch_bounds__(256) void attention_decode_kernel(
 #pragma unroll
     for (int i = 0; i < LD; ++i)
         acc[i] = 0.f;
-    float m = -INFINITY, l = 0.f;
-    Rows ra, rb;
-    load(ra, t_begin);
-    for (int t0 = t_begin; t0 < t_end; t0 += 2 * kStep) {
-        load(rb, t0 + kStep);
+    float m = -INFINITY, l = 0.f;   // this lane's state
+    Rows ring[R];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            Rows &r = half == 0 ? ra : rb;
-            const int ts = t0 + half * kStep;
-            if (ts >= t_end)
-                break;
+    for (int i = 0; i < R; ++i)
+        load(ring[i], t_begin + i * kStep);
+    for (int t0 = t_begin; t0 < t_end; t0 += R * kStep) {
+        // no early exit inside: a step past the end has ok == false and
+        // costs only its (zero-size) loads, and one path through the loop
+        // keeps the compiler's vmcnt waits exact
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int ts = t0 + i * kStep;
+            const Rows &r = ring[i];
             const int t = ts + slot;
             // slots past the context (or of an absent page) hold whatever the
-            // cache holds there: their score is -inf and their V row zero
+            // cache holds there: they take no part
             const bool valid = r.ok && t < t_end;
             float s = 0.f;
 #pragma unroll
             for (int j = 0; j < DL; ++j)
                 s = dot8(qv[j], r.k[j], s);
-            s = lanes::reduce<4>(s) * scale;
-            if (!valid)
-                s = -INFINITY;
-            const float smax = wave_max(s);
-            if (smax != -INFINITY) {   // a step with nothing valid changes nothing
-                const float mn = fmaxf(m, smax);
-                const float alpha = expf(m - mn);   // 0 while m is still -inf
-                const float p = valid ? expf(s - mn) : 0.f;
-                // each position's p sits in its 4 lanes: count it once
-                l = l * alpha + lanes::reduce<64>(sub == 0 ? p : 0.f);
+            s = lanes::reduce<4>(s) * scale2;
+            if (valid) {
+                const float mn = fmaxf(m, s);
+                const float alpha = exp2_f32(m - mn);   // 0 while m is still -inf
+                const float p = exp2_f32(s - mn);
+                l = l * alpha + p;
 #pragma unroll
-                for (int i = 0; i < LD; ++i)
-                    acc[i] *= alpha;
-                const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+                for (int c = 0; c < LD; ++c)
+                    acc[c] *= alpha;
 #pragma unroll
                 for (int j = 0; j < DL; ++j)
-                    axpy8(p, valid ? r.v[j] : zero, acc + 8 * j);
+                    axpy8(p, r.v[j], acc + 8 * j);
                 m = mn;
             }
-            if (half == 0)
-                load(ra, t0 + 2 * kStep);
+            // the step's registers are refilled with the step R further on
+            load(ring[i], ts + R * kStep);
         }
     }
-    // sum the 16 positions' accumulators (lanes with the same dim slice)
+    // merge the 16 lanes of each dim slice (lanes with the same `sub`)
 #pragma unroll
-    for (int i = 0; i < LD; ++i) {
-        float v = acc[i];
-        v += __shfl_xor(v, 4);
-        v += __shfl_xor(v, 8);
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        acc[i] = v;
+    for (int off = 4; off < 64; off <<= 1) {
+        float acco[LD];
+#pragma unroll
+        for (int c = 0; c < LD; ++c)
+            acco[c] = __shfl_xor(acc[c], off);
+        const float mo = __shfl_xor(m, off), lo = __shfl_xor(l, off);
+        merge_state<LD>(m, l, acc, mo, lo, acco);
     }
-    if (lane < 4) {
+    if (lane < 4) {   // acc[8 j + e] is dim (4 j + lane) * 8 + e
 #pragma unroll
-        for (int i = 0; i < LD; ++i)
-            wacc[w][lane * LD + i] = acc[i];
+        for (int j = 0; j < DL; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                wacc[w][(4 * j + lane) * 8 + e] = acc[8 * j + e];
     }
     if (lane == 0) {
         wm[w] = m;
         wl[w] = l;
     }
     __syncthreads();
-    const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
-    float e[4], L = 0.f;
+    float M = wm[0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        e[i] = wm[i] == -INFINITY ? 0.f : expf(wm[i] - M);
+    for (int i = 1; i < kWaves; ++i)
+        M = fmaxf(M, wm[i]);
+    float e[kWaves], L = 0.f;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        e[i] = wm[i] == -INFINITY ? 0.f : exp2_f32(wm[i] - M);
         L += wl[i] * e[i];
     }
     for (int i = threadIdx.x; i < D; i += blockDim.x) {
-        const float A = ((wacc[0][i] * e[0] + wacc[1][i] * e[1]) + wacc[2][i] * e[2]) + wacc[3][i] * e[3];
-        if (partial == nullptr) {
+        float A = 0.f;
+#pragma unroll
+        for (int u = 0; u < kWaves; ++u)
+            A += wacc[u][i] * e[u];
+        if (partial == nullptr) {   // the whole context in one chunk
             out[(int64_t)h * D + i] = __builtin_bit_cast(uint16_t, (_Float16)(A / L));
         } else {
-            float *rec = partial + ((int64_t)h * gridDim.x / nq + chunk) * (D + 2);
+            float *rec = partial + ((int64_t)h * (gridDim.x / nq) + chunk) * (D + 2);
             rec[2 + i] = A;
             if (i == 0) {
                 rec[0] = M;
@@ -202,43 +259,86 @@ __global__ __launch_bounds__(256) void attention_decode_kernel(
     }
 }
 
-// Combine the chunks of each head: out = sum A_s e^(M_s - M) / sum L_s e^(M_s - M).
-__global__ __launch_bounds__(256) void attention_combine_kernel(const float *__restrict__ partial,
-                                                                int32_t chunks, int32_t d,
-                                                                uint16_t *__restrict__ out)
+// Combine the chunks of each head:
+//   out = sum_c A_c 2^(M_c - Mx) / sum_c L_c 2^(M_c - Mx),  Mx = max_c M_c
+// (maxima in base-2 units).  A thread owns one dim of one head and merges the
+// chunk records online, reading 16 chunks' (M, L, A) per batch with every
+// load issued before the first use, so a context of up to 16 chunks costs
+// one round trip to memory.
+constexpr int kCombineBatch = 16;
+
+__global__ __launch_bounds__(64) void attention_combine_kernel(const float *__restrict__ partial,
+                                                               int32_t chunks, int32_t d,
+                                                               uint16_t *__restrict__ out)
 {
-    const int h = blockIdx.x;
-    const float *rec = partial + (int64_t)h * chunks * (d + 2);
-    float M = -INFINITY;
-    for (int c = 0; c < chunks; ++c)
-        M = fmaxf(M, rec[(int64_t)c * (d + 2)]);
-    for (int i = threadIdx.x; i < d; i += blockDim.x) {
-        float num = 0.f, den = 0.f;
-        for (int c = 0; c < chunks; ++c) {
-            const float *r = rec + (int64_t)c * (d + 2);
-            const float e = r[0] == -INFINITY ? 0.f : expf(r[0] - M);
-            num += r[2 + i] * e;
-            den += r[1] * e;
+    const int h = blockIdx.x, i = blockIdx.y * 64 + threadIdx.x;
+    if (i >= d)
+        return;
+    const int64_t stride = d + 2;
+    const float *rec = partial + (int64_t)h * chunks * stride;
+    float m = -INFINITY, l = 0.f, a = 0.f;
+    for (int c0 = 0; c0 < chunks; c0 += kCombineBatch) {
+        float mc[kCombineBatch], lc[kCombineBatch], ac[kCombineBatch];
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) {
+            const float *r = rec + min(c0 + u, chunks - 1) * stride;   // in bounds; extras unused
+            mc[u] = r[0];
+            lc[u] = r[1];
+            ac[u] = r[2 + i];
         }
-        out[(int64_t)h * d + i] = __builtin_bit_cast(uint16_t, (_Float16)(num / den));
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) {
+            if (c0 + u < chunks) {
+                const float mn = fmaxf(m, mc[u]);
+                const float e1 = m == -INFINITY ? 0.f : exp2_f32(m - mn);
+                const float e2 = mc[u] == -INFINITY ? 0.f : exp2_f32(mc[u] - mn);
+                l = l * e1 + lc[u] * e2;
+                a = a * e1 + ac[u] * e2;
+                m = mn;
+            }
+        }
     }
+    out[(int64_t)h * d + i] = __builtin_bit_cast(uint16_t, (_Float16)(a / l));
+}
+
+// Positions per block: the longest chunk (kMinChunk times a power of two, at
+// most kMaxChunk) that still gives the grid about one block per compute unit,
+// but never below kMinChunk.  Longer chunks spread the block's fixed cost (query,
+// page indices, the final merge, the partial record) over more rows.
+int64_t chunk_len(int64_t ctx, int64_t nq)
+{
+#ifdef Q4_ATT_FIXED_CHUNK
+    (void)ctx;
+    (void)nq;
+    return Q4_ATT_FIXED_CHUNK;
+#else
+#ifndef Q4_ATT_TARGET_BLOCKS
+#define Q4_ATT_TARGET_BLOCKS 256
+#endif
+    constexpr int64_t kTargetBlocks = Q4_ATT_TARGET_BLOCKS;
+    int64_t c = kMaxChunk;
+    while (c > kMinChunk && nq * ((ctx + c - 1) / c) < kTargetBlocks)
+        c >>= 1;
+    return c;
+#endif
 }
 
 template <int DL>
 hipError_t launch_dl(const uint16_t *q, const uint16_t *cache, const int32_t *pt, int32_t n_pages,
-                     int32_t ctx, int32_t nq, int32_t nkv, float scale, uint16_t *out, float *ws,
+                     int32_t ctx, int32_t nq, int32_t nkv, float scale, uint16_t *out, void *ws,
                      hipStream_t stream)
 {
-    const int chunks = (ctx + kChunk - 1) / kChunk;
-    float *partial = chunks > 1 ? ws : nullptr;
-    hipLaunchKernelGGL((attention_decode_kernel<DL>), dim3((unsigned)(nq * chunks)), dim3(256), 0,
-                       stream, q, cache, pt, n_pages, ctx, nq, nkv, scale, out, partial);
+    const int cl = (int)chunk_len(ctx, nq);
+    const int chunks = (ctx + cl - 1) / cl;
+    float *partial = chunks > 1 ? static_cast<float *>(ws) : nullptr;
+    hipLaunchKernelGGL((attention_decode_kernel<DL>), dim3((unsigned)(nq * chunks)), dim3(64 * kWaves), 0,
+                       stream, q, cache, pt, n_pages, ctx, nq, nkv, cl, scale, out, partial);
     if (chunks > 1) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
-        hipLaunchKernelGGL(attention_combine_kernel, dim3((unsigned)nq), dim3(128), 0, stream,
-                           ws, chunks, 32 * DL, out);
+        hipLaunchKernelGGL(attention_combine_kernel, dim3((unsigned)nq, (unsigned)(DL + 1) / 2), dim3(64),
+                           0, stream, partial, chunks, 32 * DL, out);
     }
     return hipGetLastError();
 }
@@ -247,7 +347,8 @@ hipError_t launch_dl(const uint16_t *q, const uint16_t *cache, const int32_t *pt
 
 int64_t attention_workspace_bytes(int64_t ctx, int64_t nq, int64_t d)
 {
-    const int64_t chunks = (ctx + kChunk - 1) / kChunk;
+    const int64_t cl = chunk_len(ctx, nq);
+    const int64_t chunks = (ctx + cl - 1) / cl;
     return chunks > 1 ? nq * chunks * (d + 2) * 4 : 0;
 }
 
@@ -255,7 +356,7 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *cache, const int3
                             int32_t n_pages, int32_t ctx, int32_t nq, int32_t nkv, int32_t d,
                             float scale, uint16_t *out, void *ws, hipStream_t stream)
 {
-    float *w = static_cast<float *>(ws);
+    void *w = ws;
     switch (d / 32) {
     case 1: return launch_dl<1>(q, cache, page_table, n_pages, ctx, nq, nkv, scale, out, w, stream);
     case 2: return launch_dl<2>(q, cache, page_table, n_pages, ctx, nq, nkv, scale, out, w, stream);

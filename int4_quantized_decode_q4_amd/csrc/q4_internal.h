@@ -19,7 +19,7 @@ enum Epilogue {
 
 // The fused QKV epilogue: heads of d rows, nq q heads then nkv k heads then
 // nkv v heads; RoPE at position pos on q and k; k and v appended to the
-// paged cache [n_pages][2][16][nkv][d] (cache may be null).
+// paged cache [n_pages][2][nkv][16][d] (cache may be null).
 struct RopeArgs {
     int32_t d, nq, nkv, pos;
     double base;

@@ -486,8 +486,7 @@ __device__ __forceinline__ void store_rows(float y0, float y1, int64_t r0, void 
             const int64_t head = blk - rp.nq - kv * rp.nkv;
             const int32_t page = rp.page_table[rp.pos >> 4];
             if (page >= 0 && page < rp.n_pages) {
-                uint16_t *dst = rp.cache + (((int64_t)page * 2 + kv) * 16 + (rp.pos & 15)) * rp.nkv * rp.d +
-                                head * rp.d + i;
+                uint16_t *dst = rp.cache + ((((int64_t)page * 2 + kv) * rp.nkv + head) * 16 + (rp.pos & 15)) * rp.d + i;
                 dst[0] = ha;
                 dst[half] = hb;
             }

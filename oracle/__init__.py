@@ -205,10 +205,10 @@ class Oracle:
     def attention_decode(self, q, cache, page_table, ctx: int, nq: int, nkv: int, d: int,
                          scale: float):
         """(out f64 [nq][d], a f64 [nq][d]) of one decode token over positions
-        0 .. ctx-1 of the paged cache f16 bits [pages][2][16][nkv][d]."""
+        0 .. ctx-1 of the paged cache f16 bits [pages][2][nkv][16][d]."""
         q = np.ascontiguousarray(q, dtype=np.uint16).reshape(nq * d)
         cache = np.ascontiguousarray(cache, dtype=np.uint16)
-        assert cache.ndim == 5 and cache.shape[1:] == (2, 16, nkv, d)
+        assert cache.ndim == 5 and cache.shape[1:] == (2, nkv, 16, d)
         pt = np.ascontiguousarray(page_table, dtype=np.int32)
         assert pt.size >= (ctx + 15) // 16
         out = np.empty((nq, d), np.float64)

@@ -281,8 +281,9 @@ int q4o_qkv_rope(const uint32_t *words, const uint16_t *scales, const uint16_t *
  * Paged-attention decode for one token ([P1] 内核融合: attention merges paged
  * attention with the page-table reads; 完整的推理流水线: vLLM-style page
  * table).  Cache layout as the fused QKV step writes it:
- * cache[page][K=0|V=1][16 slots][nkv heads][d], position t in slot t % 16 of
- * page page_table[t / 16].  Query head h reads kv head h / (nq / nkv).
+ * cache[page][K=0|V=1][nkv heads][16 slots][d] (head-major inside a page, as
+ * vLLM's blocks are), position t in slot t % 16 of page page_table[t / 16].
+ * Query head h reads kv head h / (nq / nkv).
  *   s_t = scale * sum_i q[h][i] K_t[i],  p_t = e^(s_t - max s) / sum_u e^(s_u - max s)
  *   out[h][i] = sum_t p_t V_t[i],        a[h][i] = sum_t p_t |V_t[i]|
  * over t = 0 .. ctx-1.  q [nq][d], cache f16 bits; out, a f64 [nq][d].
@@ -304,7 +305,7 @@ int q4o_attention_decode(const uint16_t *q, const uint16_t *cache, const int32_t
         const int64_t g = h / (nq / nkv);
         double mx = -INFINITY;
         for (int64_t t = 0; t < ctx; ++t) {
-            const uint16_t *kr = cache + (((int64_t)page_table[t / 16] * 2 + 0) * 16 + t % 16) * nkv * d + g * d;
+            const uint16_t *kr = cache + ((((int64_t)page_table[t / 16] * 2 + 0) * nkv + g) * 16 + t % 16) * d;
             double dot = 0.0;
             for (int64_t i = 0; i < d; ++i)
                 dot += q4o_half_to_double(q[h * d + i]) * q4o_half_to_double(kr[i]);
@@ -320,7 +321,7 @@ int q4o_attention_decode(const uint16_t *q, const uint16_t *cache, const int32_t
         for (int64_t i = 0; i < d; ++i) {
             double o = 0.0, m = 0.0;
             for (int64_t t = 0; t < ctx; ++t) {
-                const uint16_t *vr = cache + (((int64_t)page_table[t / 16] * 2 + 1) * 16 + t % 16) * nkv * d + g * d;
+                const uint16_t *vr = cache + ((((int64_t)page_table[t / 16] * 2 + 1) * nkv + g) * 16 + t % 16) * d;
                 const double v = q4o_half_to_double(vr[i]);
                 o += sc[t] * v;
                 m += sc[t] * fabs(v);

@@ -392,7 +392,7 @@ def pin_rope_layout(orc, quick=False):
 
 
 def _cache(rng, pages, nkv, d, scale=1.0):
-    return si.f16_bits(rng.normal(0.0, scale, (pages, 2, 16, nkv, d)))
+    return si.f16_bits(rng.normal(0.0, scale, (pages, 2, nkv, 16, d)))
 
 
 def pin_attention(orc, quick=False):
@@ -405,7 +405,7 @@ def pin_attention(orc, quick=False):
     cache = _cache(rng, pages, nkv, d)
     q = si.f16_bits(rng.normal(0.0, 1.0, (nq, d)))
     table = np.array([2, 0, 3, 1], np.int32)
-    V = lambda t, g: cache[table[t // 16], 1, t % 16, g].view(np.float16).astype(np.float64)
+    V = lambda t, g: cache[table[t // 16], 1, g, t % 16].view(np.float16).astype(np.float64)
     # a single position: its V row, exactly
     out, _ = orc.attention_decode(q, cache, table, 1, nq, nkv, d, 0.125)
     for h in range(nq):
@@ -417,15 +417,15 @@ def pin_attention(orc, quick=False):
         want = np.mean([V(t, h // 2) for t in range(ctx)], axis=0)
         assert np.allclose(out[h], want, rtol=1e-12, atol=1e-12)
     eq = cache.copy()
-    eq[:, 0] = eq[0, 0, 0]            # every key the same row
+    eq[:, 0] = eq[0, 0, 0, 0]         # every key the same row
     out, _ = orc.attention_decode(q, eq, table, ctx, nq, nkv, d, 0.3)
     for h in range(nq):
-        want = np.mean([eq[table[t // 16], 1, t % 16, h // 2].view(np.float16).astype(np.float64)
+        want = np.mean([eq[table[t // 16], 1, h // 2, t % 16].view(np.float16).astype(np.float64)
                         for t in range(ctx)], axis=0)
         assert np.allclose(out[h], want, rtol=1e-12, atol=1e-12)
     # a dominant key: position 21 of kv head 1 matches query heads 2 and 3
     big = cache.copy()
-    big[table[21 // 16], 0, 21 % 16, 1] = si.f16_bits(np.full(d, 4.0))
+    big[table[21 // 16], 0, 1, 21 % 16] = si.f16_bits(np.full(d, 4.0))
     qq = si.f16_bits(np.full((nq, d), 4.0))
     out, _ = orc.attention_decode(qq, big, table, ctx, nq, nkv, d, 1.0)
     for h in (2, 3):
@@ -433,7 +433,7 @@ def pin_attention(orc, quick=False):
     # grouped heads: constant V per kv head -> each query head returns its group's value
     grp = cache.copy()
     for g in range(nkv):
-        grp[:, 1, :, g] = si.f16_bits(np.full(d, g + 1.5))
+        grp[:, 1, g] = si.f16_bits(np.full(d, g + 1.5))
     out, _ = orc.attention_decode(q, grp, table, ctx, nq, nkv, d, 0.2)
     for h in range(nq):
         assert np.allclose(out[h], h // 2 + 1.5, rtol=1e-14)

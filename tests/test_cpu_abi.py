@@ -203,8 +203,9 @@ def test_attention_errors(q4):
     Q, C, T, O, Wk = A + 0x200000, A + 0x1000000, A + 0x300000, A + 0x400000, A + 0x500000
     f = lib.q4_attention_decode
     need = lib.q4_workspace_bytes(q4.OP_ATTENTION, 4096, 32, 96)
-    assert need == 32 * 16 * (96 + 2) * 4
-    assert lib.q4_workspace_bytes(q4.OP_ATTENTION, 256, 32, 96) == 0   # one chunk: none
+    # one (max, sum, d sums) f32 record per head and chunk, chunks of >= 64 positions
+    assert need > 0 and need % (32 * (96 + 2) * 4) == 0 and need <= 32 * 64 * (96 + 2) * 4
+    assert lib.q4_workspace_bytes(q4.OP_ATTENTION, 64, 32, 96) == 0    # one chunk: none
     ok = (Q, C, T, 300, 4096, 32, 32, 96, 0.1, O, Wk, need, None)
     def call(**kw):
         names = ("q", "c", "t", "pages", "ctx", "nq", "nkv", "d", "scale", "o", "ws", "wsb", "s")

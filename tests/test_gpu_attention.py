@@ -19,14 +19,15 @@ def tol_attn(o, a):
 
 def make(rng, ctx, nq, nkv, d, spare_pages=2):
     pages = (ctx + 15) // 16 + spare_pages
-    cache = si.f16_bits(rng.normal(0.0, 1.0, (pages, 2, 16, nkv, d)))
+    cache = si.f16_bits(rng.normal(0.0, 1.0, (pages, 2, nkv, 16, d)))
     table = rng.permutation(pages)[: (ctx + 15) // 16].astype(np.int32)
     # every slot the context does not cover holds NaN: it must never leak in
     used = np.zeros((pages, 16), bool)
     for t in range(ctx):
         used[table[t // 16], t % 16] = True
     for kv in (0, 1):
-        cache[:, kv][~used] = NAN16
+        for g in range(nkv):
+            cache[:, kv, g][~used] = NAN16
     q = si.f16_bits(rng.normal(0.0, 1.0, (nq, d)))
     return cache, table, q
 
@@ -84,6 +85,24 @@ def test_attention_deterministic(q4):
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
+def test_attention_many_chunks(q4, orc):
+    """Contexts split into many chunks per head (a single head, grouped
+    heads, long contexts) through one shared workspace, called in a row with
+    different shapes."""
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda").fill_(0xFF)
+    for i, (nq, nkv, d, ctx) in enumerate([(1, 1, 64, 5000), (4, 2, 128, 20000), (32, 32, 96, 1000),
+                                           (1, 1, 64, 300), (4, 2, 128, 20000)]):
+        rng = np.random.default_rng(900 + i)
+        need = q4.lib.q4_workspace_bytes(q4.OP_ATTENTION, ctx, nq, d)
+        assert 0 < need <= ws.numel()
+        cache, table, q = make(rng, ctx, nq, nkv, d)
+        c = torch.from_numpy(cache.view(np.float16)).cuda()
+        out = q4.attention_decode(dev_f16(q.reshape(-1)), c, torch.from_numpy(table).cuda(), ctx,
+                                  nq, 0.09, ws=ws)
+        ref, a = orc.attention_decode(q, cache, table, ctx, nq, nkv, d, 0.09)
+        assert_within(host_f16_as_f64(out), ref, tol_attn(ref, a), f"attention {nq}x{d} ctx={ctx}")
+
+
 def test_decode_steps_then_attention(q4, orc):
     """The decode pipeline: 40 fused QKV steps fill the cache through a page
     table; attention of the last step's q over the 40 positions matches the
@@ -96,7 +115,7 @@ def test_decode_steps_then_attention(q4, orc):
     pw = q4.pack_rope(dev_u32(w), dev_u16(s), d)
     pages = 5
     table = np.array([3, 0, 4], np.int32)
-    cache = torch.zeros((pages, 2, 16, nkv, d), dtype=torch.float16, device="cuda")
+    cache = torch.zeros((pages, 2, nkv, 16, d), dtype=torch.float16, device="cuda")
     pt = torch.from_numpy(table).cuda()
     steps = 40
     for pos in range(steps):

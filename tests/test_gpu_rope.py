@@ -35,7 +35,7 @@ def run_case(q4, orc, n, k, d, nq, pos, seed, norm=False):
     pw = q4.pack_rope(dev_u32(w), dev_u16(s), d)
     pages = pos // 16 + 3
     table = rng.permutation(pages).astype(np.int32)
-    cache = torch.full((pages, 2, 16, nkv, d), SENTINEL, dtype=torch.int16, device="cuda")
+    cache = torch.full((pages, 2, nkv, 16, d), SENTINEL, dtype=torch.int16, device="cuda")
     pt = torch.from_numpy(table).cuda()
     if norm:
         r = si.f16_bits(rng.normal(0.0, 2.0, k))
@@ -58,10 +58,10 @@ def run_case(q4, orc, n, k, d, nq, pos, seed, norm=False):
     page, slot = table[pos // 16], pos % 16
     kpart = yb[nq * d:(nq + nkv) * d].reshape(nkv, d)
     vpart = yb[(nq + nkv) * d:].reshape(nkv, d)
-    assert np.array_equal(c[page, 0, slot], kpart)
-    assert np.array_equal(c[page, 1, slot], vpart)
+    assert np.array_equal(c[page, 0, :, slot], kpart)
+    assert np.array_equal(c[page, 1, :, slot], vpart)
     mask = np.ones(c.shape, bool)
-    mask[page, :, slot] = False
+    mask[page, :, :, slot] = False
     assert np.all(c[mask] == SENTINEL)
     return pw, x, y
 
@@ -114,7 +114,7 @@ def test_qkv_rope_invalid_page_appends_nothing(q4, orc):
     w, s = si.draw_weight(rng, n, k)
     x = si.draw_x(rng, k)
     pw = q4.pack_rope(dev_u32(w), dev_u16(s), d)
-    cache = torch.full((2, 2, 16, 32, d), SENTINEL, dtype=torch.int16, device="cuda")
+    cache = torch.full((2, 2, 32, 16, d), SENTINEL, dtype=torch.int16, device="cuda")
     pt = torch.tensor([1, 7, -1], dtype=torch.int32, device="cuda")
     for pos in (20, 33):   # page entries 7 and -1: outside the 2 pages
         y = q4.qkv_rope_append(pw, dev_f16(x), nq, pos, 10000.0, cache, pt)

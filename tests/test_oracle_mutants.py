@@ -49,9 +49,12 @@ MUTANTS = [
     ("rope_layout_adjacent", "int64_t src = (pr / (d / 2)) * d + pr % (d / 2) + u * (d / 2);",
      "int64_t src = (pr / (d / 2)) * d + 2 * (pr % (d / 2)) + u;"),
     ("attn_group_modulo", "const int64_t g = h / (nq / nkv);", "const int64_t g = h % nkv;"),
-    ("attn_keys_from_v", "page_table[t / 16] * 2 + 0) * 16 + t % 16)",
-     "page_table[t / 16] * 2 + 1) * 16 + t % 16)"),
-    ("attn_slot", "page_table[t / 16] * 2 + 0) * 16 + t % 16)", "page_table[t / 16] * 2 + 0) * 16 + t / 16)"),
+    ("attn_keys_from_v", "page_table[t / 16] * 2 + 0) * nkv + g) * 16 + t % 16)",
+     "page_table[t / 16] * 2 + 1) * nkv + g) * 16 + t % 16)"),
+    ("attn_slot", "page_table[t / 16] * 2 + 0) * nkv + g) * 16 + t % 16)",
+     "page_table[t / 16] * 2 + 0) * nkv + g) * 16 + t / 16)"),
+    ("attn_slot_major_v", "page_table[t / 16] * 2 + 1) * nkv + g) * 16 + t % 16) * d;",
+     "page_table[t / 16] * 2 + 1) * 16 + t % 16) * nkv + g) * d;"),
     ("attn_no_scale", "sc[t] = scale * dot;", "sc[t] = dot;"),
     ("attn_unnormalised", "out[h * d + i] = o / den;", "out[h * d + i] = o;"),
     ("norm_unrounded_residual", "const double hv = q4o_half_to_double(q4o_double_to_half(v));",

@@ -60,6 +60,12 @@ class Oracle:
         lib.q4o_double_to_half.restype = ctypes.c_uint16
         lib.q4o_gemv.argtypes = [_P, _P, _P, _I64, _I64, _P, _P]
         lib.q4o_gemv.restype = ctypes.c_int
+        lib.q4o_gemv3.argtypes = [_P, _P, _P, _I64, _I64, _P, _P]
+        lib.q4o_gemv3.restype = ctypes.c_int
+        lib.q4o_encode3.argtypes = [_P, _P, _I64, _I64, _P]
+        lib.q4o_encode3.restype = ctypes.c_int
+        lib.q4o_layout3_bytes.argtypes = [_I64, _I64]
+        lib.q4o_layout3_bytes.restype = ctypes.c_int64
         lib.q4o_gemm.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P, _P]
         lib.q4o_gemm.restype = ctypes.c_int
         lib.q4o_silu.argtypes = [ctypes.c_double]
@@ -132,6 +138,33 @@ class Oracle:
                                _ptr(y), _ptr(a))
         assert rc == 0
         return y, a
+
+    def _check_w3(self, words3, scales, n, k):
+        assert words3.dtype == np.uint32 and words3.shape == (n, 3 * k // 32), words3.shape
+        assert scales.dtype == np.uint16 and scales.shape == (n, k // 32), scales.shape
+
+    def gemv3(self, words3, scales, x):
+        """(y, a) in f64 for an int3 weight: words3 uint32 [n][3k/32] (each
+        row one LSB-first stream of 3-bit codes), w = (q - 4) * scale."""
+        n, k = words3.shape[0], x.shape[0]
+        self._check_w3(words3, scales, n, k)
+        words3, scales = np.ascontiguousarray(words3), np.ascontiguousarray(scales)
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        y = np.empty(n, np.float64)
+        a = np.empty(n, np.float64)
+        rc = self.lib.q4o_gemv3(_ptr(words3), _ptr(scales), _ptr(x), n, k, _ptr(y), _ptr(a))
+        assert rc == 0
+        return y, a
+
+    def encode3(self, words3, scales) -> np.ndarray:
+        """The int3 device layout (bytes) of words3 [n][3k/32], scales [n][k/32]."""
+        n, k = words3.shape[0], words3.shape[1] * 32 // 3
+        self._check_w3(words3, scales, n, k)
+        words3, scales = np.ascontiguousarray(words3), np.ascontiguousarray(scales)
+        dst = np.full(int(self.lib.q4o_layout3_bytes(n, k)), 0xA5, np.uint8)
+        rc = self.lib.q4o_encode3(_ptr(words3), _ptr(scales), n, k, _ptr(dst))
+        assert rc == 0
+        return dst
 
     def gemm(self, words, scales, X):
         m, k = X.shape

@@ -429,21 +429,32 @@ int64_t q4o_layout_bytes(int64_t rows, int64_t k)
     return g[4] * g[5];
 }
 
+/* byte offsets of the code unit and the scale of logical (row r, group g)
+ * for lane units of UB bytes (int4: 1024 = 64 lanes x 16; int3: 768 = 64 x
+ * 12): a pass is CG * (2 UB + 256) bytes, a tile P passes (TB bytes) */
+static void unit_offsets(int64_t r, int64_t g, int L, int CG, int64_t TR, int64_t TB,
+                         int64_t UB, int64_t *code_off, int64_t *scale_off)
+{
+    int64_t PB = (int64_t)CG * (2 * UB + 256);
+    int64_t t = r / TR, s = (r % TR) / 2, u = r % 2;
+    int64_t p = g / ((int64_t)L * CG);
+    int64_t c = (g % ((int64_t)L * CG)) / CG, j = g % CG;
+    int64_t lane = s * L + c;
+    int64_t base = t * TB + p * PB;
+    *code_off = base + (u * CG + j) * UB + lane * (UB / 64);
+    *scale_off = base + (int64_t)2 * CG * UB + lane * 4 * CG + (u * CG + j) * 2;
+}
+
 /* place one logical (row, group) at its destination; src words may be NULL
  * (padding) */
 static void place(uint8_t *dst, int64_t r, int64_t g, int L, int CG,
                   int64_t TR, int64_t TB, const uint32_t *src_words,
                   uint16_t src_scale)
 {
-    int64_t PB = (int64_t)CG * 2304;
-    int64_t t = r / TR, s = (r % TR) / 2, u = r % 2;
-    int64_t p = g / ((int64_t)L * CG);
-    int64_t c = (g % ((int64_t)L * CG)) / CG, j = g % CG;
-    int64_t lane = s * L + c;
-    int64_t base = t * TB + p * PB;
-    uint8_t *code_dst = dst + base + (u * CG + j) * 1024 + lane * 16;
-    uint8_t *scale_dst = dst + base + (int64_t)2 * CG * 1024 + lane * 4 * CG +
-                         (u * CG + j) * 2;
+    int64_t co, so;
+    unit_offsets(r, g, L, CG, TR, TB, 1024, &co, &so);
+    uint8_t *code_dst = dst + co;
+    uint8_t *scale_dst = dst + so;
     for (int w = 0; w < 4; ++w) {
         uint32_t word = src_words ? src_words[w] : 0x88888888u;
         memcpy(code_dst + 4 * w, &word, 4); /* little-endian, as on the GPU */
@@ -516,4 +527,126 @@ int q4o_encode_rope(const uint32_t *words, const uint16_t *scales, int64_t n,
     if (d < 2 || d % 2 || n % d)
         return -1;
     return encode(words, scales, NULL, NULL, n, k, 2, d, dst);
+}
+
+/* ----------------------------------------------------------------- int3 -- */
+
+/*
+ * The int3 variant of the same matmul ([P4] the Zero-TVM README, where it
+ * says where the shaders live, names one generator for an int4/int3 matmul
+ * family; no page gives the int3 bit layout).  This
+ * library's definition, which the oracle follows literally:
+ *   - codes q in 0..7; a row's codes form one bit stream, LSB first, over its
+ *     little-endian uint32 words [n][3k/32]: code k sits in stream bits
+ *     3k, 3k+1, 3k+2 (bit b of the stream is bit b % 32 of word b / 32), so
+ *     each group of 32 codes fills exactly 3 words;
+ *   - one f16 scale per group of 32 consecutive k of a row; scales [N][K/32];
+ *   - weight value w = (q - 4) * scale (4 is the midpoint of 0..7);
+ *   - y[n] = sum_k x[k] * w[n][k], f64, k ascending, one term at a time.
+ */
+
+/* bit b of row r's stream */
+static int stream_bit(const uint32_t *words3, int64_t r, int64_t k, int64_t b)
+{
+    uint32_t word = words3[r * (3 * k / 32) + b / 32];
+    return (int)((word >> (b % 32)) & 1u);
+}
+
+/* code of row r at position kk: stream bits 3kk (least significant) .. 3kk+2 */
+static int code3_at(const uint32_t *words3, int64_t r, int64_t kk, int64_t k)
+{
+    int q = 0;
+    for (int t = 0; t < 3; ++t)
+        q |= stream_bit(words3, r, k, 3 * kk + t) << t;
+    return q;
+}
+
+/* y = x . dequant3(W)^T; words3 [n][3k/32], scales [n][k/32], x [k] f16 bits;
+ * a as in q4o_gemv (may be NULL).  Returns 0, or -1 on a bad shape. */
+int q4o_gemv3(const uint32_t *words3, const uint16_t *scales, const uint16_t *x,
+              int64_t n, int64_t k, double *y, double *a)
+{
+    if (n < 1 || k < 32 || k % 32 != 0)
+        return -1;
+    const int64_t G = k / 32;
+    for (int64_t r = 0; r < n; ++r) {
+        double acc = 0.0, mag = 0.0;
+        for (int64_t col = 0; col < k; ++col) {
+            int q = code3_at(words3, r, col, k);
+            double s = q4o_half_to_double(scales[r * G + col / 32]);
+            double term = q4o_half_to_double(x[col]) * ((double)(q - 4) * s);
+            acc += term;
+            mag += fabs(term);
+        }
+        y[r] = acc;
+        if (a)
+            a[r] = mag;
+    }
+    return 0;
+}
+
+/*
+ * Device layout of an int3 weight (layout Q4_LAYOUT_INT3, version 1), from
+ * its specification.  The tile geometry (L, CG, P, TR, tiles) is the int4
+ * one above; a lane unit holds one group of one row in 12 bytes (3 words)
+ * instead of 16, so a unit slot is 768 bytes and a pass PB3 = CG * 1792:
+ *   codes (3 words) at t*TB3 + p*PB3 + (u*CG + j)*768 + lane*12,
+ *   scale (f16)     at t*TB3 + p*PB3 + 2*CG*768 + lane*4*CG + (u*CG + j)*2,
+ * with TB3 = P * PB3 and (t, p, u, j, lane) from (row, group) as for int4.
+ * The 32 codes c0..c31 of a group sit in its 3 device words w0, w1, w2:
+ *   word i, bits 3m .. 3m+2       (m = 0..4): code 10i + m,
+ *   word i, bits 16+3m .. 18+3m   (m = 0..4): code 10i + 5 + m,
+ *   word i, bit 15: bit i of code 30;  word i, bit 31: bit i of code 31.
+ * Padding (rows >= n or groups >= G): every code 4, scale 0x0000.
+ */
+static void place3(uint8_t *dst, int64_t r, int64_t g, int L, int CG, int64_t TR,
+                   int64_t TB3, const int *codes, uint16_t scale)
+{
+    int64_t co, so;
+    unit_offsets(r, g, L, CG, TR, TB3, 768, &co, &so);
+    uint8_t *code_dst = dst + co;
+    uint8_t *scale_dst = dst + so;
+    for (int i = 0; i < 3; ++i) {
+        uint32_t word = 0;
+        for (int m = 0; m < 5; ++m) {
+            word |= (uint32_t)codes[10 * i + m] << (3 * m);
+            word |= (uint32_t)codes[10 * i + 5 + m] << (16 + 3 * m);
+        }
+        word |= (uint32_t)((codes[30] >> i) & 1) << 15;
+        word |= (uint32_t)((codes[31] >> i) & 1) << 31;
+        memcpy(code_dst + 4 * i, &word, 4);
+    }
+    memcpy(scale_dst, &scale, 2);
+}
+
+/* int3 device layout of words3 [n][3k/32], scales [n][k/32] */
+int q4o_encode3(const uint32_t *words3, const uint16_t *scales, int64_t n, int64_t k,
+                uint8_t *dst)
+{
+    int64_t geo[6];
+    if (q4o_layout_geometry(n, k, geo))
+        return -1;
+    int L = (int)geo[0], CG = (int)geo[1], P = (int)geo[2];
+    int64_t TR = geo[3], T = geo[4];
+    int64_t TB3 = (int64_t)P * CG * 1792;
+    int64_t G = k / 32;
+    int codes[32];
+    for (int64_t r = 0; r < T * TR; ++r) {
+        for (int64_t g = 0; g < (int64_t)P * L * CG; ++g) {
+            int real = r < n && g < G;
+            for (int i = 0; i < 32; ++i)
+                codes[i] = real ? code3_at(words3, r, 32 * g + i, k) : 4;
+            place3(dst, r, g, L, CG, TR, TB3, codes, real ? scales[r * G + g] : 0);
+        }
+    }
+    return 0;
+}
+
+/* bytes of the int3 device layout */
+int64_t q4o_layout3_bytes(int64_t n, int64_t k)
+{
+    int64_t g[6];
+    if (q4o_layout_geometry(n, k, g))
+        return 0;
+    return g[4] * g[2] * g[1] * 1792;
 }

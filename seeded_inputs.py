@@ -10,6 +10,9 @@ name the format):
   * words        : uint32 [n][k/8]; code k = 8*j + i of a row is in bits
                    4*i .. 4*i+3 of that row's word j (low nibble first)
   * scales       : f16 bits, uint16 [n][k/32], one per 32 consecutive k
+  * words3 (int3): uint32 [n][3k/32]; a row's 3-bit codes form one bit
+                   stream, LSB first over its words: code k is in stream bits
+                   3k .. 3k+2 (stream bit b = bit b % 32 of word b / 32)
 
 Distributions are those of the decode workloads the library is measured on:
 x ~ N(0, 1) rounded to f16; codes uniform in 0..15; scales uniform in
@@ -60,6 +63,18 @@ def draw_weight(rng: np.random.Generator, n: int, k: int,
     codes = rng.integers(0, 16, size=(n, k), dtype=np.uint8)
     scales = f16_bits(rng.uniform(lo, hi, size=(n, k // 32)))
     return pack_codes(codes), scales
+
+
+def draw_weight3(rng: np.random.Generator, n: int, k: int,
+                 lo: float = 0.005, hi: float = 0.02):
+    """int3 weight: (words3 uint32 [n][3k/32], scales f16 bits [n][k/32]).
+
+    Uniform random words: every bit pattern is a valid code stream, so each
+    3-bit code is uniform in 0..7.  Draw order: words, then scales."""
+    assert k % 32 == 0
+    words3 = rng.integers(0, 1 << 32, size=(n, 3 * k // 32), dtype=np.uint64).astype(np.uint32)
+    scales = f16_bits(rng.uniform(lo, hi, size=(n, k // 32)))
+    return words3, scales
 
 
 # The workloads the library is measured and tested on (shapes of a Phi-3-mini

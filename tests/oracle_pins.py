@@ -28,6 +28,10 @@ What pins what:
   * add + RMSNorm : a hand example (x = (3, 4)), the residual against numpy's
                     f16 addition, constant inputs (+-1, and 1/sqrt(2) with
                     eps = mean square), scale invariance, exact gamma scaling.
+  * int3          : one-hot x at every position (codes crossing word
+                    boundaries included) against codes written through a
+                    Python integer stream; constant codes 0, 4, 7; the device
+                    layout read back destination by destination.
   * device layout : hand-derived geometry table (tests/golden), a byte-level
                     hand example, and a decoder written in the opposite
                     direction (destination -> logical) over random shapes.
@@ -529,10 +533,117 @@ def pin_layout_roundtrip(orc, quick=False):
     assert np.array_equal(ds[0:2 * n:2, :3], gs) and np.array_equal(ds[1:2 * n:2, :3], us)
 
 
+def _stream_words3(codes) -> np.ndarray:
+    """codes [n][k] in 0..7 -> canonical words3 [n][3k/32], through one Python
+    integer per row holding sum_k codes[k] * 8^k (the stream read LSB first)."""
+    codes = np.asarray(codes)
+    n, k = codes.shape
+    out = np.zeros((n, 3 * k // 32), np.uint32)
+    for r in range(n):
+        v = 0
+        for kk in reversed(range(k)):
+            v = v * 8 + int(codes[r, kk])
+        for j in range(3 * k // 32):
+            out[r, j] = (v >> (32 * j)) & 0xFFFFFFFF
+    return out
+
+
+def pin_int3(orc, quick=False):
+    """int3 matmul: one-hot x reads back (q - 4) * s for every position (codes
+    that cross a word boundary included), constant codes give closed forms,
+    and the stream is read per row."""
+    rng = np.random.default_rng(31)
+    n, k = 3, 64
+    codes = rng.integers(0, 8, size=(n, k))
+    codes[:, 10] = 5      # stream bits 30..32: crosses from word 0 into word 1
+    codes[:, 21] = 6      # bits 63..65: word 1 into word 2
+    codes[:, 42] = 3      # bits 126..128, second group: word 3 into word 4
+    words3 = _stream_words3(codes)
+    scales = si.f16_bits(rng.uniform(0.25, 2.0, size=(n, k // 32)))
+    sv = scales.view(np.float16).astype(np.float64)
+    for kk in range(k):
+        x = np.zeros(k, np.uint16)
+        x[kk] = si.f16_bits(1.0)
+        y, a = orc.gemv3(words3, scales, x)
+        want = (codes[:, kk] - 4) * sv[:, kk // 32]
+        assert np.array_equal(y, want), (kk, y, want)
+        assert np.array_equal(a, np.abs(want))
+    # constant codes: y = (c - 4) * sum over groups of s_g * (sum of x in g)
+    x = si.draw_x(rng, k)
+    xv = x.view(np.float16).astype(np.float64)
+    gsum = xv.reshape(k // 32, 32).sum(axis=1)
+    for c in (0, 4, 7):
+        wc = _stream_words3(np.full((n, k), c))
+        y, _ = orc.gemv3(wc, scales, x)
+        want = (c - 4) * (sv * gsum).sum(axis=1)
+        assert np.allclose(y, want, rtol=1e-13, atol=0), (c, y, want)
+        if c == 4:
+            assert np.all(y == 0.0)
+
+
+def _decode3_device(buf: np.ndarray, n: int, k: int, g6):
+    """Read an int3 device layout back into codes [n][k] and scales [n][k/32],
+    and the padding slots' codes and scales, walking destinations."""
+    L, CG, P, TR, T = g6["L"], g6["CG"], g6["P"], g6["TR"], g6["tiles"]
+    PB = CG * 1792
+    G = k // 32
+    codes = np.full((n, k), -1)
+    scales = np.zeros((n, G), np.uint16)
+    pad_codes, pad_scales = set(), set()
+    w32 = buf.view(np.uint32)
+    for t in range(T):
+        for p in range(P):
+            base = (t * P + p) * PB
+            for uj in range(2 * CG):
+                u, j = divmod(uj, CG)
+                for lane in range(64):
+                    s_, c = divmod(lane, L)
+                    r = t * TR + 2 * s_ + u
+                    g = p * L * CG + c * CG + j
+                    off = base + uj * 768 + lane * 12
+                    w = [int(w32[off // 4 + i]) for i in range(3)]
+                    grp = [0] * 32
+                    for i in range(3):
+                        for m in range(5):
+                            grp[10 * i + m] = (w[i] >> (3 * m)) & 7
+                            grp[10 * i + 5 + m] = (w[i] >> (16 + 3 * m)) & 7
+                        grp[30] |= ((w[i] >> 15) & 1) << i
+                        grp[31] |= ((w[i] >> 31) & 1) << i
+                    so = base + 2 * CG * 768 + lane * 4 * CG + uj * 2
+                    sc = int(buf[so]) | (int(buf[so + 1]) << 8)
+                    if r < n and g < G:
+                        codes[r, 32 * g:32 * g + 32] = grp
+                        scales[r, g] = sc
+                    else:
+                        pad_codes.update(grp)
+                        pad_scales.add(sc)
+    return codes, scales, pad_codes, pad_scales
+
+
+def pin_int3_layout(orc, quick=False):
+    """The int3 device layout read back destination by destination: every
+    (row, group) lands once with its 32 codes and scale; padding holds code 4
+    (a zero weight) with scale 0; the size is tiles * P * CG * 1792."""
+    rng = np.random.default_rng(37)
+    shapes = [(5, 64), (3, 3072)] if quick else [(5, 64), (3, 3072), (70, 96), (2, 8192)]
+    for n, k in shapes:
+        codes = rng.integers(0, 8, size=(n, k))
+        words3 = _stream_words3(codes)
+        scales = si.f16_bits(rng.uniform(0.005, 0.02, size=(n, k // 32)))
+        buf = orc.encode3(words3, scales)
+        g6 = orc.layout_geometry(n, k)
+        assert buf.size == g6["tiles"] * g6["P"] * g6["CG"] * 1792
+        dc, ds, pc, ps = _decode3_device(buf, n, k, g6)
+        assert np.array_equal(dc, codes), (n, k)
+        assert np.array_equal(ds, scales)
+        assert pc <= {4} and ps <= {0}
+
+
 ALL_PINS = [
     pin_half_decode_all_patterns, pin_half_encode_rne,
     pin_gemv_rational, pin_gemv_exactly_representable, pin_gemv_closed_forms,
     pin_gemv_one_hot, pin_gemv_linearity, pin_gemm_rows,
     pin_silu, pin_ffn, pin_argmax, pin_lmhead, pin_add_rmsnorm, pin_rope, pin_attention,
     pin_layout_geometry, pin_layout_hand_example, pin_layout_roundtrip, pin_rope_layout,
+    pin_int3, pin_int3_layout,
 ]

@@ -57,6 +57,20 @@ MUTANTS = [
      "page_table[t / 16] * 2 + 1) * 16 + t % 16) * nkv + g) * d;"),
     ("attn_no_scale", "sc[t] = scale * dot;", "sc[t] = dot;"),
     ("attn_unnormalised", "out[h * d + i] = o / den;", "out[h * d + i] = o;"),
+    ("int3_group_of_64", "scales[r * G + col / 32]", "scales[r * G + col / 64]"),
+    ("int3_last_k_dropped", "for (int64_t col = 0; col < k; ++col) {", "for (int64_t col = 0; col < k - 1; ++col) {"),
+    ("int3_zero_point_3", "((double)(q - 4) * s)", "((double)(q - 3) * s)"),
+    ("int3_bits_msb_first", "q |= stream_bit(words3, r, k, 3 * kk + t) << t;",
+     "q |= stream_bit(words3, r, k, 3 * kk + t) << (2 - t);"),
+    ("int3_row_stride", "words3[r * (3 * k / 32) + b / 32]", "words3[r * (k / 8) + b / 32]"),
+    ("int3_no_word_carry", "uint32_t word = words3[r * (3 * k / 32) + b / 32];\n    return (int)((word >> (b % 32)) & 1u);",
+     "uint32_t word = words3[r * (3 * k / 32) + b / 32];\n    return (int)((word >> (b % 32)) & 1u) & (b % 32 < 30 || b % 3 == 0 ? 1 : 0);"),
+    ("int3_high_half_reversed", "word |= (uint32_t)codes[10 * i + 5 + m] << (16 + 3 * m);",
+     "word |= (uint32_t)codes[10 * i + 5 + m] << (16 + 3 * (4 - m));"),
+    ("int3_extra_bit_14", "word |= (uint32_t)((codes[30] >> i) & 1) << 15;",
+     "word |= (uint32_t)((codes[30] >> i) & 1) << 14;"),
+    ("int3_pad_code_0", "codes[i] = real ? code3_at(words3, r, 32 * g + i, k) : 4;",
+     "codes[i] = real ? code3_at(words3, r, 32 * g + i, k) : 0;"),
     ("norm_unrounded_residual", "const double hv = q4o_half_to_double(q4o_double_to_half(v));",
      "const double hv = v;"),
 ]

@@ -77,6 +77,7 @@ extern "C" {
 #define Q4_LAYOUT_ROWS    1  /* plain rows: q4_gemv, q4_gemm, q4_lmhead_f32 */
 #define Q4_LAYOUT_GATE_UP 2  /* interleaved gate/up rows: q4_ffn_gate_up_silu */
 #define Q4_LAYOUT_ROPE    3  /* rotary-paired head rows: q4_qkv_rope_append */
+#define Q4_LAYOUT_INT3    4  /* int3 rows (q4_pack_int3): q4_gemv */
 #define Q4_LAYOUT_VERSION 1
 
 /* operations, for q4_workspace_bytes */
@@ -146,10 +147,31 @@ int q4_pack_rope(const uint32_t *words, const uint16_t *scales, int32_t n, int32
                  int32_t head_dim, void *dst, int64_t dst_bytes, q4_weight *out, void *stream);
 
 /*
- * Inverse of q4_pack / q4_pack_gate_up / q4_pack_rope (for round-trip
- * checks): writes the canonical words [rows][k/8] and scales [rows][k/32] of
- * the packed weight, rows = n (plain and rotary-paired: original row order)
- * or 2n (gate/up, interleaved order: gate 0, up 0, gate 1 ...).
+ * int3 weights: the int3 variant of the same matmul (the Zero-TVM README,
+ * where it says where the shaders live, names one generator for an int4/int3
+ * matmul family; no page defines the int3 format).  Definition: codes q in
+ * 0..7, weight (q - 4) * scale, one f16 scale per 32 consecutive k; a row's
+ * codes form one bit stream, LSB first over its little-endian uint32 words,
+ * code k in stream bits 3k .. 3k+2 (so a group of 32 codes fills 3 words).
+ *   words3 : device, uint32 [n][3k/32], 4-byte aligned
+ *   scales : device, f16 bits [n][k/32], 2-byte aligned
+ *   k      : a multiple of 32, at most 8192 (one pass of the layout)
+ *   dst    : device, >= q4_packed_bytes(n, k, Q4_LAYOUT_INT3) bytes, 256-byte
+ *            aligned.  The device layout uses the tiles of the int4 one with
+ *            12-byte lane units (word i of a group's unit: codes 10i + m at
+ *            bits 3m and 10i + 5 + m at bits 16 + 3m, m = 0..4; bit i of
+ *            codes 30 and 31 at bits 15 and 31); padding is code 4, scale 0.
+ * The result feeds q4_gemv (and q4_unpack).  Errors as q4_pack.
+ */
+int q4_pack_int3(const uint32_t *words3, const uint16_t *scales, int32_t n, int32_t k,
+                 void *dst, int64_t dst_bytes, q4_weight *out, void *stream);
+
+/*
+ * Inverse of q4_pack / q4_pack_gate_up / q4_pack_rope / q4_pack_int3 (for
+ * round-trip checks): writes the canonical words [rows][k/8] (int3: words3
+ * [rows][3k/32], 4-byte aligned) and scales [rows][k/32] of the packed
+ * weight, rows = n (plain, rotary-paired and int3: original row order) or 2n
+ * (gate/up, interleaved order: gate 0, up 0, gate 1 ...).
  */
 int q4_unpack(const q4_weight *w, uint32_t *words, uint16_t *scales, void *stream);
 
@@ -157,7 +179,7 @@ int q4_unpack(const q4_weight *w, uint32_t *words, uint16_t *scales, void *strea
  * y = x . dequant(W)^T, batch 1 ([P1] 完整的推理流水线: the int4 dequantizing
  * matmul; the rows-per-invocation and subgroup-reduction variants there are
  * the two-rows-per-lane tiles and the cross-lane reduction here).
- *   w : Q4_LAYOUT_ROWS
+ *   w : Q4_LAYOUT_ROWS, or Q4_LAYOUT_INT3 (the int3 variant)
  *   x : device f16 [k], 16-byte aligned
  *   y : device f16 [n], 4-byte aligned; f32 accumulation, rounded to nearest
  *       even once at the end

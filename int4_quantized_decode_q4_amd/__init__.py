@@ -34,7 +34,7 @@ _lib = ctypes.CDLL(LIBRARY)
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_LAYOUT = -1, -2, -3, -4
 ERR_WORKSPACE, ERR_ALIAS, ERR_HIP, ERR_SIZE = -5, -6, -7, -8
-LAYOUT_ROWS, LAYOUT_GATE_UP, LAYOUT_ROPE, LAYOUT_VERSION = 1, 2, 3, 1
+LAYOUT_ROWS, LAYOUT_GATE_UP, LAYOUT_ROPE, LAYOUT_INT3, LAYOUT_VERSION = 1, 2, 3, 4, 1
 GEMM_AUTO, GEMM_VALU, GEMM_MFMA = 0, 1, 2
 OP_GEMV, OP_GEMM, OP_FFN, OP_LMHEAD, OP_ATTENTION = 1, 2, 3, 4, 5
 
@@ -57,6 +57,7 @@ _SIGNATURES = {
     "q4_pack_gate_up": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _P, _I64, _W, _P]),
     "q4_pack_rope": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _I64, _W, _P]),
     "q4_unpack": (ctypes.c_int, [_W, _P, _P, _P]),
+    "q4_pack_int3": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _I64, _W, _P]),
     "q4_qkv_rope_append": (ctypes.c_int, [_W, _P, _I32, _I32, ctypes.c_double, _P, _P, _P, _I32,
                                           _P]),
     "q4_add_rmsnorm_qkv_rope_append": (ctypes.c_int, [_W, _P, _P, _P, ctypes.c_float, _P, _I32,
@@ -214,11 +215,30 @@ def pack_rope(words: torch.Tensor, scales: torch.Tensor, head_dim: int) -> Packe
     return PackedWeight(buf, desc)
 
 
+def pack_int3(words3: torch.Tensor, scales: torch.Tensor) -> PackedWeight:
+    """int3 weight: canonical words3 [n][3k/32] (32-bit; each row one LSB-first
+    stream of 3-bit codes, w = (q - 4) * scale) and scales [n][k/32] (16-bit)
+    -> the int3 device layout, for gemv (q4_pack_int3)."""
+    n, kw = words3.shape
+    if kw % 3:
+        raise ValueError("words3 must have 3 words per group of 32 codes")
+    k = kw * 32 // 3
+    pw = _dev(words3, "words3", 4, (n, kw))
+    ps = _dev(scales, "scales", 2, (n, k // 32))
+    buf = _alloc_packed(n, k, LAYOUT_INT3, words3.device)
+    desc = q4_weight()
+    _check(_lib.q4_pack_int3(pw, ps, n, k, buf.data_ptr(), buf.numel(), ctypes.byref(desc),
+                             _stream(words3)), "q4_pack_int3")
+    return PackedWeight(buf, desc)
+
+
 def unpack(w: PackedWeight) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Device layout -> canonical (words int32 [rows][k/8], scales int16
-    [rows][k/32]); rows = 2n for a gate/up weight (gate 0, up 0, gate 1, ...)."""
+    """Device layout -> canonical (words int32 [rows][k/8] -- int3: [rows][3k/32]
+    --, scales int16 [rows][k/32]); rows = 2n for a gate/up weight (gate 0,
+    up 0, gate 1, ...)."""
     rows = w.n * (2 if w.layout == LAYOUT_GATE_UP else 1)
-    words = torch.empty((rows, w.k // 8), dtype=torch.int32, device=w.device)
+    wcols = 3 * w.k // 32 if w.layout == LAYOUT_INT3 else w.k // 8
+    words = torch.empty((rows, wcols), dtype=torch.int32, device=w.device)
     scales = torch.empty((rows, w.k // 32), dtype=torch.int16, device=w.device)
     _check(_lib.q4_unpack(ctypes.byref(w.desc), words.data_ptr(), scales.data_ptr(),
                           _stream(words)), "q4_unpack")
@@ -226,7 +246,7 @@ def unpack(w: PackedWeight) -> Tuple[torch.Tensor, torch.Tensor]:
 
 
 def gemv(w: PackedWeight, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """y f16 [n] = x f16 [k] . dequant(W)^T (q4_gemv)."""
+    """y f16 [n] = x f16 [k] . dequant(W)^T (q4_gemv); W int4 rows or int3."""
     px = _dev(x, "x", 2, (w.k,))
     if out is None:
         out = torch.empty(w.n, dtype=torch.float16, device=x.device)

@@ -42,6 +42,9 @@ int hip_status(hipError_t e)
     return Q4_ERR_HIP;
 }
 
+// int3 weights hold one pass (k <= 8192, the longest k of the decode shapes)
+constexpr int32_t kInt3MaxK = 8192;
+
 // Checks shared by every op that reads a packed weight; returns the logical
 // row count of the layout through `rows`.
 int check_weight(const q4_weight *w, int32_t want_layout, q4::Geometry *geo, int64_t *rows)
@@ -57,8 +60,12 @@ int check_weight(const q4_weight *w, int32_t want_layout, q4::Geometry *geo, int
     if (w->layout == Q4_LAYOUT_ROPE &&
         (w->head_dim < 2 || w->head_dim % 2 != 0 || w->n % w->head_dim != 0))
         return Q4_ERR_SHAPE;
+    if (w->layout == Q4_LAYOUT_INT3 && w->k > kInt3MaxK)
+        return Q4_ERR_SHAPE;
     *rows = (want_layout == Q4_LAYOUT_GATE_UP) ? 2 * (int64_t)w->n : (int64_t)w->n;
-    if (!q4::layout_geometry(*rows, w->k, geo))
+    const bool ok = w->layout == Q4_LAYOUT_INT3 ? q4::layout_geometry3(*rows, w->k, geo)
+                                                : q4::layout_geometry(*rows, w->k, geo);
+    if (!ok)
         return Q4_ERR_SHAPE;
     if (w->bytes < geo->tiles * geo->tile_bytes)
         return Q4_ERR_SIZE;
@@ -114,10 +121,13 @@ extern "C" {
 int64_t q4_packed_bytes(int32_t n, int32_t k, int32_t layout)
 {
     if (!valid_shape(n, k) ||
-        (layout != Q4_LAYOUT_ROWS && layout != Q4_LAYOUT_GATE_UP && layout != Q4_LAYOUT_ROPE))
+        (layout != Q4_LAYOUT_ROWS && layout != Q4_LAYOUT_GATE_UP && layout != Q4_LAYOUT_ROPE &&
+         layout != Q4_LAYOUT_INT3))
         return 0;
     q4::Geometry geo;
     const int64_t rows = layout == Q4_LAYOUT_GATE_UP ? 2 * (int64_t)n : (int64_t)n;
+    if (layout == Q4_LAYOUT_INT3)
+        return k <= kInt3MaxK && q4::layout_geometry3(rows, k, &geo) ? geo.tiles * geo.tile_bytes : 0;
     if (!q4::layout_geometry(rows, k, &geo))
         return 0;
     return geo.tiles * geo.tile_bytes;
@@ -175,25 +185,64 @@ int q4_pack_gate_up(const uint32_t *gw, const uint16_t *gs, const uint32_t *uw,
     return pack_common(gw, gs, uw, us, n, k, q4::PACK_GATE_UP, 0, dst, dst_bytes, out, stream);
 }
 
+int q4_pack_int3(const uint32_t *words3, const uint16_t *scales, int32_t n, int32_t k, void *dst,
+                 int64_t dst_bytes, q4_weight *out, void *stream)
+{
+    if (!words3 || !scales || !dst || !out)
+        return Q4_ERR_NULL;
+    if (!valid_shape(n, k) || k > kInt3MaxK)
+        return Q4_ERR_SHAPE;
+    if (!aligned(words3, 4) || !aligned(scales, 2) || !aligned(dst, 256))
+        return Q4_ERR_ALIGN;
+    q4::Geometry geo;
+    if (!q4::layout_geometry3(n, k, &geo))
+        return Q4_ERR_SHAPE;
+    const int64_t need = geo.tiles * geo.tile_bytes;
+    if (dst_bytes < need)
+        return Q4_ERR_SIZE;
+    const int64_t wbytes = (int64_t)n * (3 * (int64_t)k / 32) * 4, sbytes = (int64_t)n * (k / 32) * 2;
+    if (overlap(dst, need, words3, wbytes) || overlap(dst, need, scales, sbytes))
+        return Q4_ERR_ALIAS;
+    (void)hipGetLastError();
+    const int rc = hip_status(q4::launch_pack3(words3, scales, n, k, geo, dst,
+                                               static_cast<hipStream_t>(stream)));
+    if (rc != Q4_OK)
+        return rc;
+    out->n = n;
+    out->k = k;
+    out->layout = Q4_LAYOUT_INT3;
+    out->version = Q4_LAYOUT_VERSION;
+    out->data = dst;
+    out->bytes = need;
+    out->head_dim = 0;
+    out->reserved = 0;
+    return Q4_OK;
+}
+
 int q4_unpack(const q4_weight *w, uint32_t *words, uint16_t *scales, void *stream)
 {
     if (!w || !words || !scales)
         return Q4_ERR_NULL;
     if (w->layout != Q4_LAYOUT_ROWS && w->layout != Q4_LAYOUT_GATE_UP &&
-        w->layout != Q4_LAYOUT_ROPE)
+        w->layout != Q4_LAYOUT_ROPE && w->layout != Q4_LAYOUT_INT3)
         return Q4_ERR_LAYOUT;
     q4::Geometry geo;
     int64_t rows = 0;
     const int rc = check_weight(w, w->layout, &geo, &rows);
     if (rc != Q4_OK)
         return rc;
-    if (!aligned(words, 16) || !aligned(scales, 2))
+    const bool int3 = w->layout == Q4_LAYOUT_INT3;
+    if (!aligned(words, int3 ? 4 : 16) || !aligned(scales, 2))
         return Q4_ERR_ALIGN;
-    const int64_t wbytes = rows * w->k / 2, sbytes = rows * (w->k / 32) * 2;
+    const int64_t wbytes = int3 ? rows * (3 * (int64_t)w->k / 32) * 4 : rows * w->k / 2;
+    const int64_t sbytes = rows * (w->k / 32) * 2;
     if (overlap(words, wbytes, w->data, w->bytes) || overlap(scales, sbytes, w->data, w->bytes) ||
         overlap(words, wbytes, scales, sbytes))
         return Q4_ERR_ALIAS;
     (void)hipGetLastError();
+    if (int3)
+        return hip_status(q4::launch_unpack3(w->data, rows, w->k, geo, words, scales,
+                                             static_cast<hipStream_t>(stream)));
     const q4::PackMode mode = w->layout == Q4_LAYOUT_GATE_UP ? q4::PACK_GATE_UP
                               : (w->layout == Q4_LAYOUT_ROPE ? q4::PACK_ROPE : q4::PACK_ROWS);
     return hip_status(q4::launch_unpack(w->data, rows, w->k, mode, w->head_dim, geo, words, scales,
@@ -206,7 +255,9 @@ int q4_gemv(const q4_weight *w, const uint16_t *x, uint16_t *y, void *stream)
     int64_t rows = 0;
     if (!w || !x || !y)
         return Q4_ERR_NULL;
-    int rc = check_weight(w, Q4_LAYOUT_ROWS, &geo, &rows);
+    // int4 rows or int3 rows
+    const bool int3 = w->layout == Q4_LAYOUT_INT3;
+    int rc = check_weight(w, int3 ? Q4_LAYOUT_INT3 : Q4_LAYOUT_ROWS, &geo, &rows);
     if (rc != Q4_OK)
         return rc;
     if (!aligned(x, 16) || !aligned(y, 4))
@@ -215,6 +266,9 @@ int q4_gemv(const q4_weight *w, const uint16_t *x, uint16_t *y, void *stream)
         overlap(y, 2 * (int64_t)w->n, w->data, w->bytes))
         return Q4_ERR_ALIAS;
     (void)hipGetLastError();
+    if (int3)
+        return hip_status(q4::launch_gemv3(geo, w->data, x, y, rows, w->k,
+                                           static_cast<hipStream_t>(stream)));
     return hip_status(q4::launch_gemv_family(geo, q4::EPI_F16, w->data, x, y, rows, w->k, w->n,
                                              q4::ArgmaxScratch{nullptr, nullptr}, nullptr, nullptr,
                                              static_cast<hipStream_t>(stream)));

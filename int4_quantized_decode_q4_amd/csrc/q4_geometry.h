@@ -14,7 +14,7 @@ struct Geometry {
     int P;              // passes over k
     int TR;             // rows per tile = 2 * 64 / L
     int64_t tiles;      // ceil(rows / TR)
-    int64_t pass_bytes; // CG * 2304
+    int64_t pass_bytes; // CG * 2304 (int3: CG * 1792)
     int64_t tile_bytes; // P * pass_bytes
 };
 
@@ -46,6 +46,17 @@ __host__ __device__ inline bool layout_geometry(int64_t rows, int64_t k, Geometr
     g->tiles = (rows + g->TR - 1) / g->TR;
     g->pass_bytes = (int64_t)best_cg * 2304;
     g->tile_bytes = passes * g->pass_bytes;
+    return true;
+}
+
+// The int3 layout: the same tiles and lane mapping, with 12-byte lane units
+// (3 words of codes per group instead of 4), so a pass is CG * 1792 bytes.
+__host__ __device__ inline bool layout_geometry3(int64_t rows, int64_t k, Geometry *g)
+{
+    if (!layout_geometry(rows, k, g))
+        return false;
+    g->pass_bytes = (int64_t)g->CG * 1792;
+    g->tile_bytes = g->P * g->pass_bytes;
     return true;
 }
 

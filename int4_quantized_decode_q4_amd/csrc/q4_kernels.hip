@@ -25,7 +25,13 @@
 //     f32.  Products of f16 x and small integers are exact in f32;
 //   * the L lanes of a row are reduced with DPP (xor 1, 2), ds_swizzle (xor 4,
 //     8, 16) and one bpermute (xor 32); every lane ends with the same sum.
+//
+// The int3 variant of the same matmul (the Zero-TVM README, where it says
+// where the shaders live, names one generator for an int4/int3 family) runs
+// the block kernel with a 12-byte lane unit instead of 16; see the int3
+// dequant below for its word layout.
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <math.h>
 #include <stdint.h>
 
@@ -128,6 +134,131 @@ __global__ void unpack_kernel(const uint8_t *__restrict__ src, int64_t rows, int
     *reinterpret_cast<uint4 *>(words + row * (k / 8) + 4 * g) = v;
     scales[row * G + g] =
         *reinterpret_cast<const uint16_t *>(base + (int64_t)2 * CG * 1024 + lane * 4 * CG + (u * CG + j) * 2);
+}
+
+// ------------------------------------------------------------ int3 packing --
+//
+// Canonical int3 rows are bit streams (code k in stream bits 3k .. 3k+2, LSB
+// first over little-endian words), 3 words per group of 32 codes; the device
+// unit of a group is 3 words with code 10i + m at bits 3m and 10i + 5 + m at
+// bits 16 + 3m of word i (m = 0..4), and bit i of codes 30 / 31 at bits 15 /
+// 31 of word i.  Padding is code 4 (a zero weight) with scale 0.
+
+// code i of a group from its 3 canonical words
+__device__ __forceinline__ uint32_t canonical3_code(const uint32_t (&w)[3], int i)
+{
+    const int b = 3 * i, wi = b >> 5, sh = b & 31;
+    uint64_t v = w[wi];
+    if (wi < 2)
+        v |= (uint64_t)w[wi + 1] << 32;
+    return (uint32_t)(v >> sh) & 7u;
+}
+
+__device__ __forceinline__ void device3_words(const uint32_t (&codes)[32], uint32_t (&d)[3])
+{
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        uint32_t v = ((codes[30] >> i) & 1u) << 15 | ((codes[31] >> i) & 1u) << 31;
+#pragma unroll
+        for (int m = 0; m < 5; ++m)
+            v |= codes[10 * i + m] << (3 * m) | codes[10 * i + 5 + m] << (16 + 3 * m);
+        d[i] = v;
+    }
+}
+
+// One thread per destination 12-byte unit (and the scale beside it).
+__global__ void pack3_kernel(const uint32_t *__restrict__ w3, const uint16_t *__restrict__ sc,
+                             int64_t rows, int64_t k, int L, int CG, int P, int64_t units,
+                             uint8_t *__restrict__ dst)
+{
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= units)
+        return;
+    const int lane = (int)(idx & 63);
+    int64_t rest = idx >> 6;
+    const int uj = (int)(rest % (2 * CG));
+    rest /= 2 * CG;
+    const int p = (int)(rest % P);
+    const int64_t t = rest / P;
+    const int u = uj / CG, j = uj % CG;
+    const int s = lane / L, c = lane % L;
+    const int64_t r = t * (128 / L) + 2 * s + u;
+    const int64_t G = k / 32;
+    const int64_t g = (int64_t)p * L * CG + (int64_t)c * CG + j;
+    uint32_t codes[32];
+    uint16_t scale = 0;
+    if (r < rows && g < G) {
+        const uint32_t *src = w3 + r * (3 * G) + 3 * g;
+        const uint32_t w[3] = {src[0], src[1], src[2]};
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            codes[i] = canonical3_code(w, i);
+        scale = sc[r * G + g];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            codes[i] = 4u;
+    }
+    uint32_t d[3];
+    device3_words(codes, d);
+    uint8_t *base = dst + (t * P + p) * (int64_t)CG * 1792;
+    uint32_t *out = reinterpret_cast<uint32_t *>(base + (int64_t)uj * 768 + lane * 12);
+    out[0] = d[0];
+    out[1] = d[1];
+    out[2] = d[2];
+    *reinterpret_cast<uint16_t *>(base + (int64_t)2 * CG * 768 + lane * 4 * CG + uj * 2) = scale;
+}
+
+// One thread per logical (row, group) of the real matrix: device unit back
+// to the canonical stream.
+__global__ void unpack3_kernel(const uint8_t *__restrict__ src, int64_t rows, int64_t k, int L,
+                               int CG, int P, uint32_t *__restrict__ w3, uint16_t *__restrict__ sc)
+{
+    const int64_t G = k / 32;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= rows * G)
+        return;
+    const int64_t r = idx / G, g = idx % G;
+    const int64_t t = r / (128 / L);
+    const int s = (int)((r % (128 / L)) >> 1), u = (int)(r & 1);
+    const int64_t p = g / ((int64_t)L * CG);
+    const int c = (int)((g % ((int64_t)L * CG)) / CG), j = (int)(g % CG);
+    const int lane = s * L + c;
+    const uint8_t *base = src + (t * P + p) * (int64_t)CG * 1792;
+    const uint32_t *d = reinterpret_cast<const uint32_t *>(base + (int64_t)(u * CG + j) * 768 + lane * 12);
+    uint64_t lo = 0;   // stream bits 0..63 of the group
+    uint32_t hi = 0;   // bits 64..95
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const uint32_t v = d[i];
+#pragma unroll
+        for (int m = 0; m < 10; ++m) {
+            const int code_i = 10 * i + m;
+            const uint32_t q = (v >> (m < 5 ? 3 * m : 16 + 3 * (m - 5))) & 7u;
+            const int b = 3 * code_i;
+            if (b + 3 <= 64)
+                lo |= (uint64_t)q << b;
+            else if (b >= 64)
+                hi |= q << (b - 64);
+            else {   // code 21: bits 63..65
+                lo |= (uint64_t)q << b;
+                hi |= q >> (64 - b);
+            }
+        }
+    }
+    uint32_t q30 = 0, q31 = 0;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        q30 |= ((d[i] >> 15) & 1u) << i;
+        q31 |= ((d[i] >> 31) & 1u) << i;
+    }
+    hi |= q30 << (90 - 64) | q31 << (93 - 64);
+    uint32_t *dst = w3 + r * (3 * G) + 3 * g;
+    dst[0] = (uint32_t)lo;
+    dst[1] = (uint32_t)(lo >> 32);
+    dst[2] = hi;
+    sc[r * G + g] = *reinterpret_cast<const uint16_t *>(base + (int64_t)2 * CG * 768 + lane * 4 * CG +
+                                                        (u * CG + j) * 2);
 }
 
 // ----------------------------------------------------------- GEMV family --
@@ -309,6 +440,111 @@ __device__ __forceinline__ void dot_word(uint32_t w, const uint32_t *xp, float &
     p1 = __builtin_amdgcn_fdot2(as_h2(a2) - k1, as_h2(xp[2]), p1, false);
     p16 = __builtin_amdgcn_fdot2(as_h2(a3) - k16, as_h2(xp[3]), p16, false);
 }
+
+// The 16-byte unit of one (row, group): 4 words of 8 codes.
+__device__ __forceinline__ float dot_unit4(uint4 c, const uint32_t *xp, const DequantConsts &m)
+{
+    float p1 = 0.f, p16 = 0.f;
+    dot_word(c.x, xp + 0, p1, p16, m);
+    dot_word(c.y, xp + 4, p1, p16, m);
+    dot_word(c.z, xp + 8, p1, p16, m);
+    dot_word(c.w, xp + 12, p1, p16, m);
+    return fmaf(p16, 0.0625f, p1);
+}
+
+// int3 (codes 0..7, w = (q - 4) * s).  A group's 32 codes c0..c31 sit in 3
+// device words; word i holds codes 10i + m at bits 3m and 10i + 5 + m at bits
+// 16 + 3m (m = 0..4), and bit i of c30 / c31 at bit 15 / 31.  So each word
+// gives 5 f16 pairs (code 10i + m, code 10i + 5 + m) with the magic trick:
+// the codes at bits 0, 3, 6 of each half are masked in place, read as
+// 1024 + q, 1024 + 8q and 1024 + 64q, and offset by 1028, 1056 and 1280 to
+// q - 4 times 1, 8 and 64; the codes at bits 9 and 12 take one shift by 9
+// first.  The last pair (c30, c31) is assembled from the three top bits of
+// each half.  Per group: 3 x (1 shift + 5 and-or + 5 subtract + 5 dot) plus
+// 3 shifts, 3 and-or, 1 subtract and 1 dot -- about 56 VALU for 32 weights,
+// against 52 for int4, on 12 bytes of codes instead of 16.
+struct DequantConsts3 {
+    uint32_t m0, m3, m6, b1, b2, b4, magic;
+};
+
+__device__ __forceinline__ DequantConsts3 dequant_consts3()
+{
+    DequantConsts3 k;
+    asm("v_mov_b32 %0, 0x00070007" : "=v"(k.m0));
+    asm("v_mov_b32 %0, 0x00380038" : "=v"(k.m3));
+    asm("v_mov_b32 %0, 0x01C001C0" : "=v"(k.m6));
+    asm("v_mov_b32 %0, 0x00010001" : "=v"(k.b1));
+    asm("v_mov_b32 %0, 0x00020002" : "=v"(k.b2));
+    asm("v_mov_b32 %0, 0x00040004" : "=v"(k.b4));
+    asm("v_mov_b32 %0, 0x64006400" : "=v"(k.magic));
+    return k;
+}
+
+// x pairs of one group for dot_unit3: xp[5i + m] = (x[10i + m], x[10i + 5 + m]),
+// xp[15] = (x30, x31), from the natural pairs n[q] = (x[2q], x[2q + 1]).
+__device__ __forceinline__ void pair3_into(uint32_t *xp, const uint32_t (&n)[16])
+{
+    auto half = [&](int i) -> uint32_t { return (n[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu; };
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int m = 0; m < 5; ++m)
+            xp[5 * i + m] = half(10 * i + m) | (half(10 * i + 5 + m) << 16);
+    xp[15] = n[15];
+}
+
+__device__ __forceinline__ float dot_unit3(uint4 c, const uint32_t *xp, const DequantConsts3 &m)
+{
+    const h2 k1 = {(_Float16)1028.0f, (_Float16)1028.0f};
+    const h2 k8 = {(_Float16)1056.0f, (_Float16)1056.0f};
+    const h2 k64 = {(_Float16)1280.0f, (_Float16)1280.0f};
+    const uint32_t w[3] = {c.x, c.y, c.z};
+    float p1 = 0.f, p8 = 0.f, p64 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const uint32_t v = w[i], t = v >> 9;
+        const uint32_t a0 = (v & m.m0) | m.magic;   // 1024 + q(10i), 1024 + q(10i+5)
+        const uint32_t a1 = (v & m.m3) | m.magic;   // 1024 + 8 q(10i+1), ..
+        const uint32_t a2 = (v & m.m6) | m.magic;   // 1024 + 64 q(10i+2), ..
+        const uint32_t a3 = (t & m.m0) | m.magic;   // 1024 + q(10i+3), ..
+        const uint32_t a4 = (t & m.m3) | m.magic;   // 1024 + 8 q(10i+4), ..
+        p1 = __builtin_amdgcn_fdot2(as_h2(a0) - k1, as_h2(xp[5 * i + 0]), p1, false);
+        p8 = __builtin_amdgcn_fdot2(as_h2(a1) - k8, as_h2(xp[5 * i + 1]), p8, false);
+        p64 = __builtin_amdgcn_fdot2(as_h2(a2) - k64, as_h2(xp[5 * i + 2]), p64, false);
+        p1 = __builtin_amdgcn_fdot2(as_h2(a3) - k1, as_h2(xp[5 * i + 3]), p1, false);
+        p8 = __builtin_amdgcn_fdot2(as_h2(a4) - k8, as_h2(xp[5 * i + 4]), p8, false);
+    }
+    uint32_t e = ((w[0] >> 15) & m.b1) | m.magic;   // bit 0 of c30 and c31
+    e = ((w[1] >> 14) & m.b2) | e;                   // bit 1
+    e = ((w[2] >> 13) & m.b4) | e;                   // bit 2: 1024 + c30, 1024 + c31
+    p1 = __builtin_amdgcn_fdot2(as_h2(e) - k1, as_h2(xp[15]), p1, false);
+    return fmaf(p64, 0.015625f, fmaf(p8, 0.125f, p1));
+}
+
+// Per-format pieces of the block kernel: FMT 4 (int4, 16-byte lane units) or
+// 3 (int3, 12-byte lane units); a pass is CG * (2 * UB + 256) bytes.
+template <int FMT>
+struct Fmt;
+template <>
+struct Fmt<4> {
+    static constexpr int UB = 1024;
+    using Consts = DequantConsts;
+    static __device__ __forceinline__ Consts consts() { return dequant_consts(); }
+    static __device__ __forceinline__ float dot(uint4 c, const uint32_t *xp, const Consts &m)
+    {
+        return dot_unit4(c, xp, m);
+    }
+};
+template <>
+struct Fmt<3> {
+    static constexpr int UB = 768;
+    using Consts = DequantConsts3;
+    static __device__ __forceinline__ Consts consts() { return dequant_consts3(); }
+    static __device__ __forceinline__ float dot(uint4 c, const uint32_t *xp, const Consts &m)
+    {
+        return dot_unit3(c, xp, m);
+    }
+};
 
 template <int L>
 __device__ __forceinline__ float reduce_lanes(float v)
@@ -534,55 +770,59 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base,
                                              kBufferWord3);
 }
 
-// Load unit i (u = i / CG, j = i % CG) of a tile into its register slot.
-template <int CG>
+// Load unit i (u = i / CG, j = i % CG) of a tile into its register slot
+// (int3: 12 bytes, the fourth word unused).
+typedef unsigned v3u __attribute__((ext_vector_type(3)));
+
+template <int CG, int FMT = 4>
 __device__ __forceinline__ void load_unit(TileRegs<CG> &r, __amdgpu_buffer_rsrc_t rs, int lane, int i)
 {
-    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, i * 1024, 0);
-    r.c[i / CG][i % CG] = make_uint4(v.x, v.y, v.z, v.w);
+    if constexpr (FMT == 4) {
+        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, i * 1024, 0);
+        r.c[i / CG][i % CG] = make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+        const v3u v = __builtin_amdgcn_raw_buffer_load_b96(rs, lane * 12, i * 768, 0);
+        r.c[i / CG][i % CG] = make_uint4(v.x, v.y, v.z, 0u);
+    }
 }
 
-template <int CG>
+template <int CG, int FMT = 4>
 __device__ __forceinline__ void load_scales(TileRegs<CG> &r, __amdgpu_buffer_rsrc_t rs, int lane)
 {
 #pragma unroll
     for (int j = 0; j < CG; ++j)
-        r.s[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4 * CG + 4 * j, 2 * CG * 1024, 0);
+        r.s[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4 * CG + 4 * j, 2 * CG * Fmt<FMT>::UB, 0);
 }
 
 // One tile, unit by unit: compute unit i of `cur`, then issue the load that
 // keeps PD units in flight: unit i + PD of `cur`, or past its end a unit of
 // `nxt`, the wavefront's next tile (a zero-size resource when there is none).
-template <int CG, int PD>
+template <int FMT, int CG, int PD>
 __device__ __forceinline__ void stream_tile(TileRegs<CG> &cur, TileRegs<CG> &nxt,
                                             __amdgpu_buffer_rsrc_t cur_rs,
                                             __amdgpu_buffer_rsrc_t nxt_rs, int lane,
                                             const uint32_t (&xp)[CG][16], float (&acc)[2],
-                                            const DequantConsts &m)
+                                            const typename Fmt<FMT>::Consts &m)
 {
     constexpr int NU = 2 * CG;
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
         const int u = i / CG, j = i % CG;
-        float p1 = 0.f, p16 = 0.f;
-        dot_word(cur.c[u][j].x, &xp[j][0], p1, p16, m);
-        dot_word(cur.c[u][j].y, &xp[j][4], p1, p16, m);
-        dot_word(cur.c[u][j].z, &xp[j][8], p1, p16, m);
-        dot_word(cur.c[u][j].w, &xp[j][12], p1, p16, m);
+        const float p = Fmt<FMT>::dot(cur.c[u][j], &xp[j][0], m);
         const int e = u * CG + j;
         const float sv = f16_value((uint16_t)(cur.s[e >> 1] >> ((e & 1) * 16)));
-        acc[u] = fmaf(sv, fmaf(p16, 0.0625f, p1), acc[u]);
+        acc[u] = fmaf(sv, p, acc[u]);
         // the unit's arithmetic must be issued before the next load: the
         // compiler would otherwise hoist every load of the tile to its top
         // (and sink the arithmetic below them), defeating the pipeline
         asm volatile("" ::"v"(acc[u]) : "memory");
         const int pi = i + PD;
         if (pi < NU) {
-            load_unit(cur, cur_rs, lane, pi);
+            load_unit<CG, FMT>(cur, cur_rs, lane, pi);
         } else {
             if (pi == NU)
-                load_scales(nxt, nxt_rs, lane);
-            load_unit(nxt, nxt_rs, lane, pi - NU);
+                load_scales<CG, FMT>(nxt, nxt_rs, lane);
+            load_unit<CG, FMT>(nxt, nxt_rs, lane, pi - NU);
         }
     }
 }
@@ -598,6 +838,7 @@ __device__ __forceinline__ void stream_tile(TileRegs<CG> &cur, TileRegs<CG> &nxt
 // tile, so while a tile is reduced the next one is already on its way.
 constexpr int kBlockXHalves = 8192;   // largest single-pass k
 
+template <int FMT = 4>
 __device__ __forceinline__ void lds_x_group(uint32_t *xp, const uint4 *xs, int64_t g, int64_t G)
 {
     if (g >= G) {
@@ -606,19 +847,32 @@ __device__ __forceinline__ void lds_x_group(uint32_t *xp, const uint4 *xs, int64
             xp[i] = 0u;
         return;
     }
+    if constexpr (FMT == 4) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        pair_into(xp + 4 * q, xs[g * 4 + q]);
+        for (int q = 0; q < 4; ++q)
+            pair_into(xp + 4 * q, xs[g * 4 + q]);
+    } else {
+        uint32_t n[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint4 v = xs[g * 4 + q];
+            n[4 * q] = v.x;
+            n[4 * q + 1] = v.y;
+            n[4 * q + 2] = v.z;
+            n[4 * q + 3] = v.w;
+        }
+        pair3_into(xp, n);
+    }
 }
 
-template <int L, int CG, int EPI, bool NORM>
+template <int L, int CG, int EPI, bool NORM, int FMT = 4>
 __global__ __launch_bounds__(64 * kBlockWaves) void gemv_block_kernel(
     const uint8_t *__restrict__ wd, const uint16_t *__restrict__ x, void *__restrict__ out,
     int64_t rows, int64_t k, int64_t tiles, int64_t n_out, ArgmaxScratch am, NormArgs nm,
     typename RopeParam<EPI>::type rp)
 {
     constexpr int PD = Q4_STREAM_DEPTH < 2 * CG ? Q4_STREAM_DEPTH : 2 * CG;
-    constexpr int64_t PB = (int64_t)CG * 2304;
+    constexpr int64_t PB = (int64_t)CG * (2 * Fmt<FMT>::UB + 256);
     __shared__ uint4 xs[kBlockXHalves / 8];
     const int lane = threadIdx.x & 63;
     // wave-uniform by construction; said explicitly so that the tile index and
@@ -628,7 +882,7 @@ __global__ __launch_bounds__(64 * kBlockWaves) void gemv_block_kernel(
     const int64_t G = k >> 5;
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    const DequantConsts m = dequant_consts();
+    const typename Fmt<FMT>::Consts m = Fmt<FMT>::consts();
 
     // x and the head of the weight stream are requested together: x through
     // a resource of k halves (loads past it return zeros), up to 4 x 16 bytes
@@ -665,10 +919,10 @@ __global__ __launch_bounds__(64 * kBlockWaves) void gemv_block_kernel(
     TileRegs<CG> ra, rb;
     {
         const __amdgpu_buffer_rsrc_t r0 = rs_of(t);
-        load_scales(ra, r0, lane);
+        load_scales<CG, FMT>(ra, r0, lane);
 #pragma unroll
         for (int i = 0; i < PD; ++i)
-            load_unit(ra, r0, lane, i);
+            load_unit<CG, FMT>(ra, r0, lane, i);
     }
     // with the norm: each thread keeps its chunks of h in registers and
     // parks its wavefront's part of the sum of squares in LDS; after one
@@ -712,12 +966,12 @@ __global__ __launch_bounds__(64 * kBlockWaves) void gemv_block_kernel(
     uint32_t xp[CG][16];
 #pragma unroll
     for (int j = 0; j < CG; ++j)
-        lds_x_group(xp[j], xs, (int64_t)c * CG + j, G);
+        lds_x_group<FMT>(xp[j], xs, (int64_t)c * CG + j, G);
     while (t < tiles) {
         {
             const int64_t nt = t + step;
             float acc[2] = {0.f, 0.f};
-            stream_tile<CG, PD>(ra, rb, rs_of(t), rs_of(nt), lane, xp, acc, m);
+            stream_tile<FMT, CG, PD>(ra, rb, rs_of(t), rs_of(nt), lane, xp, acc, m);
             finish_tile<L, EPI>(acc, t, s, c, out, rows, n_out, bv, bi, rp);
             t = nt;
         }
@@ -726,7 +980,7 @@ __global__ __launch_bounds__(64 * kBlockWaves) void gemv_block_kernel(
         {
             const int64_t nt = t + step;
             float acc[2] = {0.f, 0.f};
-            stream_tile<CG, PD>(rb, ra, rs_of(t), rs_of(nt), lane, xp, acc, m);
+            stream_tile<FMT, CG, PD>(rb, ra, rs_of(t), rs_of(nt), lane, xp, acc, m);
             finish_tile<L, EPI>(acc, t, s, c, out, rows, n_out, bv, bi, rp);
             t = nt;
         }
@@ -961,6 +1215,70 @@ hipError_t launch_unpack(const void *src, int64_t rows, int64_t k, PackMode mode
                        static_cast<const uint8_t *>(src), rows, k, (int)mode, d, geo.L, geo.CG,
                        geo.P, words, scales);
     return hipGetLastError();
+}
+
+hipError_t launch_pack3(const uint32_t *w3, const uint16_t *s, int64_t rows, int64_t k,
+                        const Geometry &geo, void *dst, hipStream_t stream)
+{
+    const int64_t units = geo.tiles * geo.P * 2 * geo.CG * 64;
+    hipLaunchKernelGGL(pack3_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream,
+                       w3, s, rows, k, geo.L, geo.CG, geo.P, units, static_cast<uint8_t *>(dst));
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack3(const void *src, int64_t rows, int64_t k, const Geometry &geo,
+                          uint32_t *w3, uint16_t *s, hipStream_t stream)
+{
+    const int64_t items = rows * (k / 32);
+    hipLaunchKernelGGL(unpack3_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream,
+                       static_cast<const uint8_t *>(src), rows, k, geo.L, geo.CG, geo.P, w3, s);
+    return hipGetLastError();
+}
+
+// int3 GEMV: the block kernel with 12-byte units, single pass (k <= 8192),
+// f16 output.
+template <int L, int CG>
+static void launch_gemv3_lc(const Geometry &geo, const uint8_t *wd, const uint16_t *x, uint16_t *y,
+                            int64_t rows, int64_t k, hipStream_t stream)
+{
+    const int64_t groups = (geo.tiles + kBlockWaves - 1) / kBlockWaves;
+    const int64_t cap = kCUs * Q4_BLOCKS_PER_CU;
+    hipLaunchKernelGGL((gemv_block_kernel<L, CG, EPI_F16, false, 3>), dim3((unsigned)(groups < cap ? groups : cap)),
+                       dim3(64 * kBlockWaves), 0, stream, wd, x, static_cast<void *>(y), rows, k,
+                       geo.tiles, rows, ArgmaxScratch{nullptr, nullptr},
+                       NormArgs{nullptr, nullptr, nullptr, 0.f}, NoRope{});
+}
+
+template <int L>
+static bool launch_gemv3_l(const Geometry &geo, const uint8_t *wd, const uint16_t *x, uint16_t *y,
+                           int64_t rows, int64_t k, hipStream_t stream)
+{
+    switch (geo.CG) {
+    case 1: launch_gemv3_lc<L, 1>(geo, wd, x, y, rows, k, stream); return true;
+    case 2: launch_gemv3_lc<L, 2>(geo, wd, x, y, rows, k, stream); return true;
+    case 3: launch_gemv3_lc<L, 3>(geo, wd, x, y, rows, k, stream); return true;
+    case 4: launch_gemv3_lc<L, 4>(geo, wd, x, y, rows, k, stream); return true;
+    }
+    return false;
+}
+
+hipError_t launch_gemv3(const Geometry &geo, const void *wdata, const uint16_t *x, uint16_t *y,
+                        int64_t rows, int64_t k, hipStream_t stream)
+{
+    if (geo.P != 1 || k > kBlockXHalves)
+        return hipErrorInvalidValue;
+    const uint8_t *wd = static_cast<const uint8_t *>(wdata);
+    bool ok = false;
+    switch (geo.L) {
+    case 64: ok = launch_gemv3_l<64>(geo, wd, x, y, rows, k, stream); break;
+    case 32: ok = launch_gemv3_l<32>(geo, wd, x, y, rows, k, stream); break;
+    case 16: ok = launch_gemv3_l<16>(geo, wd, x, y, rows, k, stream); break;
+    case 8: ok = launch_gemv3_l<8>(geo, wd, x, y, rows, k, stream); break;
+    case 4: ok = launch_gemv3_l<4>(geo, wd, x, y, rows, k, stream); break;
+    case 2: ok = launch_gemv3_l<2>(geo, wd, x, y, rows, k, stream); break;
+    case 1: ok = launch_gemv3_l<1>(geo, wd, x, y, rows, k, stream); break;
+    }
+    return ok ? hipGetLastError() : hipErrorInvalidValue;
 }
 
 struct GemvArgs {

@@ -44,6 +44,45 @@ def test_host_geometry_matches_oracle(q4, orc, n, k):
     assert q4.packed_bytes(n, k, q4.LAYOUT_GATE_UP) == orc.layout_bytes(2 * n, k)
 
 
+@pytest.mark.parametrize("n,k", [(3072, 3072), (3072, 8192), (1, 32), (17, 96), (130, 64),
+                                 (33, 224), (999, 544), (5, 7168)])
+def test_int3_packed_bytes_matches_oracle(q4, orc, n, k):
+    assert q4.packed_bytes(n, k, q4.LAYOUT_INT3) == orc.lib.q4o_layout3_bytes(n, k)
+
+
+def test_int3_errors(q4):
+    lib = q4.lib
+    out = q4.q4_weight()
+    r = ctypes.byref(out)
+    W, S, D = A, A + 0x10000, A + 0x100000
+    nb = q4.packed_bytes(64, 96, q4.LAYOUT_INT3)
+    assert nb > 0 and q4.packed_bytes(64, 8224, q4.LAYOUT_INT3) == 0   # beyond one pass
+    f = lib.q4_pack_int3
+    assert f(None, S, 64, 96, D, nb, r, None) == q4.ERR_NULL
+    assert f(W, S, 64, 96, D, nb, None, None) == q4.ERR_NULL
+    assert f(W, S, 64, 100, D, nb, r, None) == q4.ERR_SHAPE
+    assert f(W, S, 64, 8224, D, 10 ** 9, r, None) == q4.ERR_SHAPE
+    assert f(W + 2, S, 64, 96, D, nb, r, None) == q4.ERR_ALIGN
+    assert f(W, S + 1, 64, 96, D, nb, r, None) == q4.ERR_ALIGN
+    assert f(W, S, 64, 96, D + 16, nb, r, None) == q4.ERR_ALIGN
+    assert f(W, S, 64, 96, D, nb - 1, r, None) == q4.ERR_SIZE
+    assert f(W, S, 64, 96, W, nb, r, None) == q4.ERR_ALIAS
+    assert out.data is None
+    X, Y = A + 0x200000, A + 0x300000
+    w3 = weight(q4, layout=q4.LAYOUT_INT3)
+    assert lib.q4_gemv(ctypes.byref(weight(q4, layout=q4.LAYOUT_INT3, k=8224, nbytes=10 ** 9)),
+                       X, Y, None) == q4.ERR_SHAPE
+    assert lib.q4_gemv(ctypes.byref(weight(q4, layout=q4.LAYOUT_INT3, nbytes=nb - 1)), X, Y,
+                       None) == q4.ERR_SIZE
+    assert lib.q4_gemv(ctypes.byref(w3), X + 8, Y, None) == q4.ERR_ALIGN
+    assert lib.q4_gemv(ctypes.byref(w3), X, X, None) == q4.ERR_ALIAS
+    # the other ops refuse int3 weights
+    assert lib.q4_gemm(ctypes.byref(w3), X, 4, Y, None, 0, None) == q4.ERR_LAYOUT
+    assert lib.q4_lmhead_f32(ctypes.byref(w3), X, Y, None, None, 0, None) == q4.ERR_LAYOUT
+    assert lib.q4_ffn_gate_up_silu(ctypes.byref(w3), X, Y, None) == q4.ERR_LAYOUT
+    assert lib.q4_unpack(ctypes.byref(w3), W + 2, S, None) == q4.ERR_ALIGN
+
+
 def test_packed_bytes_invalid(q4):
     assert q4.packed_bytes(0, 32) == 0
     assert q4.packed_bytes(1, 48) == 0

@@ -1,0 +1,129 @@
+"""The int3 variant of the matmul on the GPU against the oracle: the packed
+layout byte for byte, the unpack round trip, GEMV parity at the decode shapes
+and at ragged/edge shapes (f16 output bound as for int4), bit-exact one-hot
+reads (codes that cross a word boundary included), exactly representable
+sums, closed forms and determinism."""
+import numpy as np
+import pytest
+import torch
+
+import seeded_inputs as si
+from parity import assert_within, dev_f16, dev_u16, dev_u32, host_f16_as_f64, host_u16, tol_f16
+
+pytestmark = pytest.mark.gpu
+
+
+def stream_words3(codes) -> np.ndarray:
+    """codes [n][k] in 0..7 -> canonical words3 [n][3k/32] (code k at stream
+    bits 3k .. 3k+2, LSB first), bit by bit."""
+    codes = np.asarray(codes, dtype=np.uint64)
+    n, k = codes.shape
+    bits = np.zeros((n, 3 * k), np.uint64)
+    for t in range(3):
+        bits[:, t::3] = (codes >> np.uint64(t)) & np.uint64(1)
+    bits = bits.reshape(n, 3 * k // 32, 32)
+    return (bits << np.arange(32, dtype=np.uint64)).sum(axis=2).astype(np.uint32)
+
+
+def run(q4, w3, s, x):
+    pw = q4.pack_int3(dev_u32(w3), dev_u16(s))
+    return q4.gemv(pw, dev_f16(x)), pw
+
+
+@pytest.mark.parametrize("n,k", [(3072, 3072), (1, 32), (17, 96), (130, 64), (33, 224),
+                                 (999, 544), (5, 8192), (70, 7168)])
+def test_pack_int3_byte_exact_and_roundtrip(q4, orc, n, k):
+    rng = np.random.default_rng(n * 7 + k)
+    w3, s = si.draw_weight3(rng, n, k)
+    pw = q4.pack_int3(dev_u32(w3), dev_u16(s))
+    assert pw.layout == q4.LAYOUT_INT3
+    assert np.array_equal(pw.buf.cpu().numpy(), orc.encode3(w3, s))
+    uw, us = q4.unpack(pw)
+    assert np.array_equal(uw.cpu().numpy().view(np.uint32), w3)
+    assert np.array_equal(us.cpu().numpy().view(np.uint16), s)
+
+
+@pytest.mark.parametrize("n,k", [(3072, 3072), (9216, 3072), (16384, 3072), (3072, 8192)])
+def test_gemv_int3_decode_shapes(q4, orc, n, k):
+    rng = np.random.default_rng(n + 3 * k)
+    w3, s = si.draw_weight3(rng, n, k)
+    x = si.draw_x(rng, k)
+    y, _ = run(q4, w3, s, x)
+    ref, a = orc.gemv3(w3, s, x)
+    ratio = assert_within(host_f16_as_f64(y), ref, tol_f16(ref, a), f"int3 gemv {n}x{k}")
+    print(f"{n}x{k}: max err/tol {ratio:.3g}")
+
+
+RAGGED = [(1, 32), (2, 32), (17, 96), (130, 64), (33, 224), (7, 160), (6, 192), (1, 768),
+          (1001, 3072), (9, 8192), (64, 4096), (3001, 8192), (777, 7168), (3, 3200)]
+
+
+@pytest.mark.parametrize("n,k", RAGGED)
+def test_gemv_int3_ragged(q4, orc, n, k):
+    rng = np.random.default_rng(5000 + n * 31 + k)
+    w3, s = si.draw_weight3(rng, n, k)
+    x = si.draw_x(rng, k)
+    y, _ = run(q4, w3, s, x)
+    ref, a = orc.gemv3(w3, s, x)
+    assert_within(host_f16_as_f64(y), ref, tol_f16(ref, a), f"int3 gemv {n}x{k}")
+
+
+@pytest.mark.parametrize("n,k", [(3072, 3072), (130, 8192)])
+def test_gemv_int3_one_hot_bit_exact(q4, orc, n, k):
+    """x = e_k: y_n = (q - 4) * s exactly; the f16 output is its RNE, bit for
+    bit, at positions that cover every code slot of the device words (10 and
+    21 cross canonical word boundaries; 30 and 31 are the bit-sliced codes)."""
+    rng = np.random.default_rng(17)
+    w3, s = si.draw_weight3(rng, n, k)
+    pw = q4.pack_int3(dev_u32(w3), dev_u16(s))
+    for kk in list(range(32)) + [32 + 10, 32 + 21, 32 + 30, k // 2 + 7, k - 33, k - 2, k - 1]:
+        x = np.zeros(k, np.uint16)
+        x[kk] = 0x3C00
+        got = host_u16(q4.gemv(pw, dev_f16(x)))
+        ref, _ = orc.gemv3(w3, s, x)
+        want = orc.doubles_to_halves(ref)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, f"k={kk}: rows {bad[:5].tolist()} got {got[bad[:5]]} want {want[bad[:5]]}"
+
+
+@pytest.mark.parametrize("n,k", [(3072, 3072), (9216, 3072), (101, 8192)])
+def test_gemv_int3_exactly_representable(q4, orc, n, k):
+    """x in {-4..4}/4, scales in {2^-7, 2^-8}: exact in f32 in any order, so y
+    is the RNE of the exact sum."""
+    rng = np.random.default_rng(n + k + 1)
+    codes = rng.integers(0, 8, (n, k))
+    w3 = stream_words3(codes)
+    s = si.f16_bits(2.0 ** -rng.integers(7, 9, (n, k // 32)))
+    x = si.f16_bits(rng.integers(-4, 5, k) / 4.0)
+    y, _ = run(q4, w3, s, x)
+    ref, _ = orc.gemv3(w3, s, x)
+    want = orc.doubles_to_halves(ref)
+    bad = np.nonzero(host_u16(y) != want)[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first {bad[:5].tolist()}"
+
+
+def test_gemv_int3_closed_forms(q4):
+    k = 3072
+    x = si.f16_bits(np.ones(k))
+    # every code 7, scale 2^-6: y = 3 * 2^-6 * 3072 = 144 in every row
+    w = stream_words3(np.full((130, k), 7))
+    s = si.f16_bits(np.full((130, k // 32), 2.0 ** -6))
+    y, _ = run(q4, w, s, x)
+    assert np.all(host_u16(y) == si.f16_bits(144.0))
+    # every code 0: y = -4 * 2^-6 * 3072 = -192
+    y, _ = run(q4, stream_words3(np.zeros((130, k), np.int64)), s, x)
+    assert np.all(host_u16(y) == si.f16_bits(-192.0))
+    # code 4 is the zero weight: y = +0 whatever x is
+    rng = np.random.default_rng(4)
+    s4 = si.f16_bits(rng.uniform(0.005, 0.02, (64, k // 32)))
+    y, _ = run(q4, stream_words3(np.full((64, k), 4)), s4, si.draw_x(rng, k))
+    assert np.all(host_u16(y) == 0)
+
+
+def test_gemv_int3_deterministic(q4):
+    rng = np.random.default_rng(9)
+    w3, s = si.draw_weight3(rng, 9216, 3072)
+    pw = q4.pack_int3(dev_u32(w3), dev_u16(s))
+    x = dev_f16(si.draw_x(rng, 3072))
+    outs = [host_u16(q4.gemv(pw, x)) for _ in range(3)]
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])

@@ -43,6 +43,11 @@ def gemv_bytes(n: int, k: int, out_bytes: int = 2) -> int:
     return weight_bytes(n, k) + 2 * k + out_bytes * n
 
 
+def weight3_bytes(n: int, k: int) -> int:
+    """int3: 3-bit codes plus one f16 scale per 32."""
+    return n * k * 3 // 8 + n * (k // 32) * 2
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -449,6 +454,35 @@ def variants(torch, q4, si, np, K, W):
     out["gemv_3072x3072"] = {"us": round(us, 3), "gbs": round(nb / us / 1e3, 1),
                              "frac": round(nb / us / 1e3 / PEAK_HBM_GBS, 4), "bytes": nb}
     del rot
+
+    # the int3 variant of the matmul on the layer set's shapes (uniform random
+    # codes), one GEMV at a time and the four back to back
+    rng = np.random.default_rng(3)
+    i3 = {}
+    for key, (n, k) in si.LAYER_SHAPES.items():
+        w3, s3 = si.draw_weight3(rng, n, k)
+        i3[key] = (Rotation(q4, q4.pack_int3(dev_u32(w3), dev_u16(s3)),
+                            copies_for(weight3_bytes(n, k))),
+                   dev_f16(si.draw_x(rng, k)), torch.empty(n, dtype=torch.float16, device="cuda"))
+    rec = {}
+    tot_bytes = 0
+    for key, (n, k) in si.LAYER_SHAPES.items():
+        r3, xk, yk = i3[key]
+        nb3 = weight3_bytes(n, k) + 2 * k + 2 * n
+        tot_bytes += nb3
+        us3 = per_launch_us(torch, lambda i, r3=r3, xk=xk, yk=yk: q4.gemv(r3[i], xk, yk), K, W)
+        rec[key] = {"us": round(us3, 3), "gbs": round(nb3 / us3 / 1e3, 1),
+                    "frac": round(nb3 / us3 / 1e3 / PEAK_HBM_GBS, 4), "bytes": nb3}
+
+    def int3_step(i):
+        for r3, xk, yk in i3.values():
+            q4.gemv(r3[i], xk, yk)
+
+    us_set = per_launch_us(torch, int3_step, K, W)
+    rec["set"] = {"us": round(us_set, 3), "gbs": round(tot_bytes / us_set / 1e3, 1),
+                  "frac": round(tot_bytes / us_set / 1e3 / PEAK_HBM_GBS, 4), "bytes": tot_bytes}
+    out["int3_gemv_phi3_layer_set"] = rec
+    del i3
 
     # fused gate/up + SiLU, then down
     inp = si.workload(si.FFN, seed=0)

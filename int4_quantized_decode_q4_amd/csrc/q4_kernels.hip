@@ -275,6 +275,10 @@ __device__ __forceinline__ void pair_into(uint32_t *xp, uint4 n)
     xp[3] = (n.y >> 16) | (n.w & 0xFFFF0000u);
 }
 
+__device__ __forceinline__ void pair3_into(uint32_t *xp, const uint32_t (&n)[16]);
+
+// x pairs of one group (int4: per word of codes; int3: see pair3_into)
+template <int FMT = 4>
 __device__ __forceinline__ void load_x_group(uint32_t *xp, const uint16_t *__restrict__ x,
                                              int64_t g, int64_t G)
 {
@@ -285,9 +289,22 @@ __device__ __forceinline__ void load_x_group(uint32_t *xp, const uint16_t *__res
         return;
     }
     const uint4 *src = reinterpret_cast<const uint4 *>(x + g * 32);
+    if constexpr (FMT == 4) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)   // q = word of codes, 8 k each
-        pair_into(xp + 4 * q, src[q]);
+        for (int q = 0; q < 4; ++q)   // q = word of codes, 8 k each
+            pair_into(xp + 4 * q, src[q]);
+    } else {
+        uint32_t n[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint4 v = src[q];
+            n[4 * q] = v.x;
+            n[4 * q + 1] = v.y;
+            n[4 * q + 2] = v.z;
+            n[4 * q + 3] = v.w;
+        }
+        pair3_into(xp, n);
+    }
 }
 
 // ------------------------------------------------ residual add + RMSNorm --
@@ -1003,7 +1020,7 @@ constexpr int kSplitMaxTiles = 8;
 #define Q4_SPLIT_DEPTH 2
 #endif
 
-template <int L, int CG, int EPI, bool NORM>
+template <int L, int CG, int EPI, bool NORM, int FMT = 4>
 __global__ __launch_bounds__(64 * CG) void gemv_split_kernel(
     const uint8_t *__restrict__ wd, const uint16_t *__restrict__ x, void *__restrict__ out,
     int64_t rows, int64_t k, int64_t tiles, int64_t n_out, ArgmaxScratch am, NormArgs nm,
@@ -1011,7 +1028,8 @@ __global__ __launch_bounds__(64 * CG) void gemv_split_kernel(
 {
     constexpr int HP = 64 / L;   // row pairs per tile
     constexpr int TR = 128 / L;
-    constexpr int PB = CG * 2304;
+    constexpr int UB = Fmt<FMT>::UB;
+    constexpr int PB = CG * (2 * UB + 256);
     constexpr int D = Q4_SPLIT_DEPTH;
     __shared__ float part[kSplitMaxTiles][CG][HP][2];
     const int lane = threadIdx.x & 63;
@@ -1019,14 +1037,14 @@ __global__ __launch_bounds__(64 * CG) void gemv_split_kernel(
     const int s = lane / L, c = lane % L;
     uint32_t xp[16];
     if constexpr (!NORM)
-        load_x_group(xp, x, (int64_t)c * CG + j, k >> 5);
-    const DequantConsts m = dequant_consts();
+        load_x_group<FMT>(xp, x, (int64_t)c * CG + j, k >> 5);
+    const typename Fmt<FMT>::Consts m = Fmt<FMT>::consts();
     const int64_t count =
         (int64_t)blockIdx.x < tiles ? (tiles - 1 - (int64_t)blockIdx.x) / gridDim.x + 1 : 0;
 
     // this wavefront's two units and two scales inside a tile
-    const int wo0 = j * 1024 + lane * 16, wo1 = (CG + j) * 1024 + lane * 16;
-    const int so0 = 2 * CG * 1024 + lane * 4 * CG + j * 2, so1 = so0 + CG * 2;
+    const int wo0 = j * UB + lane * (UB / 64), wo1 = (CG + j) * UB + lane * (UB / 64);
+    const int so0 = 2 * CG * UB + lane * 4 * CG + j * 2, so1 = so0 + CG * 2;
     struct Regs {
         v4u w0, w1;
         uint16_t s0, s1;
@@ -1035,8 +1053,15 @@ __global__ __launch_bounds__(64 * CG) void gemv_split_kernel(
         const bool live = i < count;
         const __amdgpu_buffer_rsrc_t rs =
             tile_rsrc(wd + (live ? (int64_t)blockIdx.x + i * gridDim.x : 0) * PB, live ? PB : 0);
-        r.w0 = __builtin_amdgcn_raw_buffer_load_b128(rs, wo0, 0, 0);
-        r.w1 = __builtin_amdgcn_raw_buffer_load_b128(rs, wo1, 0, 0);
+        if constexpr (FMT == 4) {
+            r.w0 = __builtin_amdgcn_raw_buffer_load_b128(rs, wo0, 0, 0);
+            r.w1 = __builtin_amdgcn_raw_buffer_load_b128(rs, wo1, 0, 0);
+        } else {
+            const v3u a = __builtin_amdgcn_raw_buffer_load_b96(rs, wo0, 0, 0);
+            const v3u b = __builtin_amdgcn_raw_buffer_load_b96(rs, wo1, 0, 0);
+            r.w0 = v4u{a.x, a.y, a.z, 0u};
+            r.w1 = v4u{b.x, b.y, b.z, 0u};
+        }
         r.s0 = __builtin_amdgcn_raw_buffer_load_b16(rs, so0, 0, 0);
         r.s1 = __builtin_amdgcn_raw_buffer_load_b16(rs, so1, 0, 0);
     };
@@ -1057,17 +1082,24 @@ __global__ __launch_bounds__(64 * CG) void gemv_split_kernel(
             const int64_t i = i0 + q;
             if (i >= count)
                 break;
-            float a1 = 0.f, a16 = 0.f, b1 = 0.f, b16 = 0.f;
-            dot_word(ring[q].w0.x, &xp[0], a1, a16, m);
-            dot_word(ring[q].w0.y, &xp[4], a1, a16, m);
-            dot_word(ring[q].w0.z, &xp[8], a1, a16, m);
-            dot_word(ring[q].w0.w, &xp[12], a1, a16, m);
-            dot_word(ring[q].w1.x, &xp[0], b1, b16, m);
-            dot_word(ring[q].w1.y, &xp[4], b1, b16, m);
-            dot_word(ring[q].w1.z, &xp[8], b1, b16, m);
-            dot_word(ring[q].w1.w, &xp[12], b1, b16, m);
-            const float acc0 = f16_value(ring[q].s0) * fmaf(a16, 0.0625f, a1);
-            const float acc1 = f16_value(ring[q].s1) * fmaf(b16, 0.0625f, b1);
+            float acc0, acc1;
+            if constexpr (FMT == 4) {
+                float a1 = 0.f, a16 = 0.f, b1 = 0.f, b16 = 0.f;
+                dot_word(ring[q].w0.x, &xp[0], a1, a16, m);
+                dot_word(ring[q].w0.y, &xp[4], a1, a16, m);
+                dot_word(ring[q].w0.z, &xp[8], a1, a16, m);
+                dot_word(ring[q].w0.w, &xp[12], a1, a16, m);
+                dot_word(ring[q].w1.x, &xp[0], b1, b16, m);
+                dot_word(ring[q].w1.y, &xp[4], b1, b16, m);
+                dot_word(ring[q].w1.z, &xp[8], b1, b16, m);
+                dot_word(ring[q].w1.w, &xp[12], b1, b16, m);
+                acc0 = f16_value(ring[q].s0) * fmaf(a16, 0.0625f, a1);
+                acc1 = f16_value(ring[q].s1) * fmaf(b16, 0.0625f, b1);
+            } else {
+                const v4u a = ring[q].w0, b = ring[q].w1;
+                acc0 = f16_value(ring[q].s0) * dot_unit3(make_uint4(a.x, a.y, a.z, 0u), xp, m);
+                acc1 = f16_value(ring[q].s1) * dot_unit3(make_uint4(b.x, b.y, b.z, 0u), xp, m);
+            }
             // the tile's arithmetic is issued before its registers are refilled
             asm volatile("" ::"v"(acc0), "v"(acc1) : "memory");
             load(ring[q], i + D);
@@ -1235,18 +1267,23 @@ hipError_t launch_unpack3(const void *src, int64_t rows, int64_t k, const Geomet
     return hipGetLastError();
 }
 
-// int3 GEMV: the block kernel with 12-byte units, single pass (k <= 8192),
-// f16 output.
+// int3 GEMV: the int4 plan (block or split kernel) with 12-byte units,
+// single pass (k <= 8192), f16 output.
 template <int L, int CG>
 static void launch_gemv3_lc(const Geometry &geo, const uint8_t *wd, const uint16_t *x, uint16_t *y,
                             int64_t rows, int64_t k, hipStream_t stream)
 {
-    const int64_t groups = (geo.tiles + kBlockWaves - 1) / kBlockWaves;
-    const int64_t cap = kCUs * Q4_BLOCKS_PER_CU;
-    hipLaunchKernelGGL((gemv_block_kernel<L, CG, EPI_F16, false, 3>), dim3((unsigned)(groups < cap ? groups : cap)),
-                       dim3(64 * kBlockWaves), 0, stream, wd, x, static_cast<void *>(y), rows, k,
-                       geo.tiles, rows, ArgmaxScratch{nullptr, nullptr},
-                       NormArgs{nullptr, nullptr, nullptr, 0.f}, NoRope{});
+    const GemvPlan plan = plan_gemv(geo);
+    const dim3 grid((unsigned)plan.blocks), block((unsigned)plan.threads);
+    void *out = static_cast<void *>(y);
+    const ArgmaxScratch am{nullptr, nullptr};
+    const NormArgs nm{nullptr, nullptr, nullptr, 0.f};
+    if (plan.mode == MODE_SPLIT)
+        hipLaunchKernelGGL((gemv_split_kernel<L, CG, EPI_F16, false, 3>), grid, block, 0, stream, wd, x,
+                           out, rows, k, geo.tiles, rows, am, nm, NoRope{});
+    else
+        hipLaunchKernelGGL((gemv_block_kernel<L, CG, EPI_F16, false, 3>), grid, block, 0, stream, wd, x,
+                           out, rows, k, geo.tiles, rows, am, nm, NoRope{});
 }
 
 template <int L>

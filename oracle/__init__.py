@@ -60,6 +60,15 @@ class Oracle:
         lib.q4o_double_to_half.restype = ctypes.c_uint16
         lib.q4o_gemv.argtypes = [_P, _P, _P, _I64, _I64, _P, _P]
         lib.q4o_gemv.restype = ctypes.c_int
+        lib.q4o_kv_quant_row.argtypes = [_P, _I64, _P, _P]
+        lib.q4o_kv_quant_row.restype = None
+        lib.q4o_kv8_page_bytes.argtypes = [_I64, _I64]
+        lib.q4o_kv8_page_bytes.restype = ctypes.c_int64
+        lib.q4o_kv_append_int8.argtypes = [_P, _I64, _I64, _I64, _I64, _P, _P, _I64]
+        lib.q4o_kv_append_int8.restype = ctypes.c_int
+        lib.q4o_attention_decode_int8.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _I64,
+                                                  ctypes.c_double, _P, _P]
+        lib.q4o_attention_decode_int8.restype = ctypes.c_int
         lib.q4o_gemv3.argtypes = [_P, _P, _P, _I64, _I64, _P, _P]
         lib.q4o_gemv3.restype = ctypes.c_int
         lib.q4o_encode3.argtypes = [_P, _P, _I64, _I64, _P]
@@ -155,6 +164,43 @@ class Oracle:
         rc = self.lib.q4o_gemv3(_ptr(words3), _ptr(scales), _ptr(x), n, k, _ptr(y), _ptr(a))
         assert rc == 0
         return y, a
+
+    def kv_quant_row(self, x):
+        """(codes int8 [d], scale f32) of one f16 row (symmetric, per row)."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        q = np.empty(x.size, np.int8)
+        sc = np.zeros(1, np.float32)
+        self.lib.q4o_kv_quant_row(_ptr(x), x.size, _ptr(q), _ptr(sc))
+        return q, sc[0]
+
+    def kv8_page_bytes(self, nkv: int, d: int) -> int:
+        return int(self.lib.q4o_kv8_page_bytes(nkv, d))
+
+    def kv_append_int8(self, qkv, nq: int, nkv: int, d: int, pos: int, cache8, page_table):
+        """Quantise and append the k, v heads of qkv f16 [(nq + 2 nkv) d] into
+        cache8 (uint8 [pages][page bytes], modified in place)."""
+        qkv = np.ascontiguousarray(qkv, dtype=np.uint16)
+        assert qkv.size == (nq + 2 * nkv) * d
+        assert cache8.dtype == np.uint8 and cache8.flags["C_CONTIGUOUS"]
+        assert cache8.shape[1] == self.kv8_page_bytes(nkv, d)
+        pt = np.ascontiguousarray(page_table, dtype=np.int32)
+        rc = self.lib.q4o_kv_append_int8(_ptr(qkv), nq, nkv, d, pos, _ptr(cache8), _ptr(pt),
+                                         cache8.shape[0])
+        assert rc == 0
+
+    def attention_decode_int8(self, q, cache8, page_table, ctx: int, nq: int, nkv: int, d: int,
+                              scale: float):
+        """(out, a) f64 [nq][d] over the int8 cache (uint8 [pages][page bytes])."""
+        q = np.ascontiguousarray(q, dtype=np.uint16).reshape(nq * d)
+        assert cache8.dtype == np.uint8 and cache8.shape[1] == self.kv8_page_bytes(nkv, d)
+        cache8 = np.ascontiguousarray(cache8)
+        pt = np.ascontiguousarray(page_table, dtype=np.int32)
+        out = np.empty((nq, d), np.float64)
+        a = np.empty((nq, d), np.float64)
+        rc = self.lib.q4o_attention_decode_int8(_ptr(q), _ptr(cache8), _ptr(pt), cache8.shape[0],
+                                                ctx, nq, nkv, d, float(scale), _ptr(out), _ptr(a))
+        assert rc == 0
+        return out, a
 
     def encode3(self, words3, scales) -> np.ndarray:
         """The int3 device layout (bytes) of words3 [n][3k/32], scales [n][k/32]."""

@@ -288,15 +288,44 @@ int q4o_qkv_rope(const uint32_t *words, const uint16_t *scales, const uint16_t *
  *   out[h][i] = sum_t p_t V_t[i],        a[h][i] = sum_t p_t |V_t[i]|
  * over t = 0 .. ctx-1.  q [nq][d], cache f16 bits; out, a f64 [nq][d].
  * Returns 0, or -1 for a bad shape or a page entry outside [0, n_pages).
+ * The same definition serves the int8 cache (q4o_attention_decode_int8);
+ * kv_at reads either.
  */
-int q4o_attention_decode(const uint16_t *q, const uint16_t *cache, const int32_t *page_table,
-                         int64_t n_pages, int64_t ctx, int64_t nq, int64_t nkv, int64_t d,
-                         double scale, double *out, double *a)
+
+/* where one decode step reads its keys and values: the f16 cache, or the
+ * int8 cache (the int8 KV section below) */
+struct kv_source {
+    const uint16_t *f16;     /* [pages][2][nkv][16][d] f16 bits, or NULL */
+    const uint8_t *i8;       /* int8 pages (16 d codes + 16 f32 scales per block) */
+    const int32_t *table;
+    int64_t nkv, d;
+};
+
+int64_t q4o_kv8_page_bytes(int64_t nkv, int64_t d);
+
+/* element i of the key (kv = 0) or value (kv = 1) row of kv head g at
+ * position t, exact in f64 */
+static double kv_at(const struct kv_source *src, int kv, int64_t g, int64_t t, int64_t i)
 {
+    const int64_t page = src->table[t / 16], d = src->d;
+    if (src->f16)
+        return q4o_half_to_double(src->f16[(((page * 2 + kv) * src->nkv + g) * 16 + t % 16) * d + i]);
+    const uint8_t *blk = src->i8 + page * q4o_kv8_page_bytes(src->nkv, d) +
+                         (kv * src->nkv + g) * (16 * d + 64);
+    float s;
+    memcpy(&s, blk + 16 * d + 4 * (t % 16), 4);
+    return (double)(int8_t)blk[(t % 16) * d + i] * (double)s;
+}
+
+/* the attention definition over either cache (see q4o_attention_decode) */
+static int attend(const uint16_t *q, const struct kv_source *src, int64_t n_pages, int64_t ctx,
+                  int64_t nq, double scale, double *out, double *a)
+{
+    const int64_t nkv = src->nkv, d = src->d;
     if (ctx < 1 || nq < 1 || nkv < 1 || nq % nkv || d < 1)
         return -1;
     for (int64_t t = 0; t < ctx; ++t)
-        if (page_table[t / 16] < 0 || page_table[t / 16] >= n_pages)
+        if (src->table[t / 16] < 0 || src->table[t / 16] >= n_pages)
             return -1;
     double *sc = (double *)malloc(sizeof(double) * (size_t)ctx);
     if (!sc)
@@ -305,10 +334,9 @@ int q4o_attention_decode(const uint16_t *q, const uint16_t *cache, const int32_t
         const int64_t g = h / (nq / nkv);
         double mx = -INFINITY;
         for (int64_t t = 0; t < ctx; ++t) {
-            const uint16_t *kr = cache + ((((int64_t)page_table[t / 16] * 2 + 0) * nkv + g) * 16 + t % 16) * d;
             double dot = 0.0;
             for (int64_t i = 0; i < d; ++i)
-                dot += q4o_half_to_double(q[h * d + i]) * q4o_half_to_double(kr[i]);
+                dot += q4o_half_to_double(q[h * d + i]) * kv_at(src, 0, g, t, i);
             sc[t] = scale * dot;
             if (sc[t] > mx)
                 mx = sc[t];
@@ -321,8 +349,7 @@ int q4o_attention_decode(const uint16_t *q, const uint16_t *cache, const int32_t
         for (int64_t i = 0; i < d; ++i) {
             double o = 0.0, m = 0.0;
             for (int64_t t = 0; t < ctx; ++t) {
-                const uint16_t *vr = cache + ((((int64_t)page_table[t / 16] * 2 + 1) * nkv + g) * 16 + t % 16) * d;
-                const double v = q4o_half_to_double(vr[i]);
+                const double v = kv_at(src, 1, g, t, i);
                 o += sc[t] * v;
                 m += sc[t] * fabs(v);
             }
@@ -333,6 +360,14 @@ int q4o_attention_decode(const uint16_t *q, const uint16_t *cache, const int32_t
     }
     free(sc);
     return 0;
+}
+
+int q4o_attention_decode(const uint16_t *q, const uint16_t *cache, const int32_t *page_table,
+                         int64_t n_pages, int64_t ctx, int64_t nq, int64_t nkv, int64_t d,
+                         double scale, double *out, double *a)
+{
+    const struct kv_source src = {cache, NULL, page_table, nkv, d};
+    return attend(q, &src, n_pages, ctx, nq, scale, out, a);
 }
 
 /* greedy argmax ([P1] 完整的推理流水线, 贪婪解码采样): the lowest index that
@@ -649,4 +684,83 @@ int64_t q4o_layout3_bytes(int64_t n, int64_t k)
     if (q4o_layout_geometry(n, k, g))
         return 0;
     return g[4] * g[2] * g[1] * 1792;
+}
+
+/* ------------------------------------------------------------ int8 KV -- */
+
+/*
+ * The optional int8 KV cache ([P1] 完整的推理流水线: the paged KV cache has an
+ * int8 quantisation path that halves its memory; no page gives the scheme).
+ * Reading: symmetric quantisation per (token, kv head) row of d values:
+ *   m = max_i |x_i|  (over the f16 values, exact in f32),
+ *   scale = m / 127  (f32, correctly rounded),  scale = 0 when m = 0,
+ *   q_i = rint(x_i / scale)  (f32 quotient, ties to even; 0 when scale = 0),
+ * so |q_i| <= 127 and x_i ~ q_i * scale.  The codes are decided in f32, the
+ * kernel's precision, as the oracle must decide them the same way.
+ * Cache layout: [page][K=0|V=1][kv head] blocks of 16 * d int8 codes (slot
+ * major) followed by 16 f32 scales, i.e. 16 d + 64 bytes per block.
+ */
+void q4o_kv_quant_row(const uint16_t *x, int64_t d, int8_t *q, float *scale)
+{
+    float m = 0.0f;
+    for (int64_t i = 0; i < d; ++i) {
+        float a = (float)fabs(q4o_half_to_double(x[i]));
+        if (a > m)
+            m = a;
+    }
+    float s = m / 127.0f;   /* f32 division, rounded once */
+    *scale = s;
+    for (int64_t i = 0; i < d; ++i) {
+        if (s == 0.0f) {
+            q[i] = 0;
+            continue;
+        }
+        float t = (float)q4o_half_to_double(x[i]) / s;
+        q[i] = (int8_t)rintf(t);
+    }
+}
+
+/* bytes of one int8 page: 2 * nkv blocks of 16 d codes + 16 f32 scales */
+int64_t q4o_kv8_page_bytes(int64_t nkv, int64_t d)
+{
+    return 2 * nkv * (16 * d + 64);
+}
+
+/*
+ * Append the k and v heads of a fused QKV output (f16 [nq + 2 nkv][d], k heads
+ * after RoPE) at position pos: each head row quantised by q4o_kv_quant_row
+ * into slot pos % 16 of page page_table[pos / 16].  An entry outside
+ * [0, n_pages) appends nothing.  Returns 0, or -1 on a bad shape.
+ */
+int q4o_kv_append_int8(const uint16_t *qkv, int64_t nq, int64_t nkv, int64_t d, int64_t pos,
+                       uint8_t *cache8, const int32_t *page_table, int64_t n_pages)
+{
+    if (nq < 1 || nkv < 1 || d < 1 || pos < 0)
+        return -1;
+    int64_t page = page_table[pos / 16];
+    if (page < 0 || page >= n_pages)
+        return 0;
+    int64_t block = 16 * d + 64;
+    for (int64_t kv = 0; kv < 2; ++kv)
+        for (int64_t g = 0; g < nkv; ++g) {
+            const uint16_t *row = qkv + (nq + kv * nkv + g) * d;
+            uint8_t *blk = cache8 + page * q4o_kv8_page_bytes(nkv, d) + (kv * nkv + g) * block;
+            float s;
+            q4o_kv_quant_row(row, d, (int8_t *)(blk + (pos % 16) * d), &s);
+            memcpy(blk + 16 * d + 4 * (pos % 16), &s, 4);
+        }
+    return 0;
+}
+
+/*
+ * Paged-attention decode over the int8 cache: the definition of
+ * q4o_attention_decode with K_t[i] = q * scale and V_t[i] = q * scale
+ * (the dequantised values, exact in f64).
+ */
+int q4o_attention_decode_int8(const uint16_t *q, const uint8_t *cache8, const int32_t *page_table,
+                              int64_t n_pages, int64_t ctx, int64_t nq, int64_t nkv, int64_t d,
+                              double scale, double *out, double *a)
+{
+    const struct kv_source src = {NULL, cache8, page_table, nkv, d};
+    return attend(q, &src, n_pages, ctx, nq, scale, out, a);
 }

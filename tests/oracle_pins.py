@@ -32,6 +32,11 @@ What pins what:
                     boundaries included) against codes written through a
                     Python integer stream; constant codes 0, 4, 7; the device
                     layout read back destination by destination.
+  * int8 KV       : a hand-quantised row away from ties, the +-127 maximum,
+                    reconstruction within half a step, power-of-two scaling,
+                    the zero row; the append's bytes against blocks located in
+                    Python; int8 attention equal bit for bit to the f16
+                    attention over the exactly dequantised cache.
   * device layout : hand-derived geometry table (tests/golden), a byte-level
                     hand example, and a decoder written in the opposite
                     direction (destination -> logical) over random shapes.
@@ -639,11 +644,96 @@ def pin_int3_layout(orc, quick=False):
         assert pc <= {4} and ps <= {0}
 
 
+def pin_kv_quant(orc, quick=False):
+    """int8 KV rows: a hand example away from rounding ties, |q| <= 127 with
+    the largest element at +-127, the reconstruction within half a step,
+    power-of-two scaling of the row, and the zero row."""
+    q, sc = orc.kv_quant_row(si.f16_bits([2.0, -1.5, 0.25, 0.0]))
+    # scale = 2/127; x / scale = 127, -95.25, 15.875, 0
+    assert np.array_equal(q, np.array([127, -95, 16, 0], np.int8)), q
+    assert sc == np.float32(2.0) / np.float32(127.0)
+    rng = np.random.default_rng(41)
+    for d in (32, 96, 256):
+        x = si.f16_bits(rng.normal(0, 1.5, d))
+        q, sc = orc.kv_quant_row(x)
+        xv = x.view(np.float16).astype(np.float64)
+        assert np.abs(q.astype(np.int64)).max() == 127
+        assert np.abs(q[np.argmax(np.abs(xv))]) == 127
+        assert np.all(np.abs(q.astype(np.float64) * float(sc) - xv) <= float(sc) * (0.5 + 1e-6))
+        q2, sc2 = orc.kv_quant_row(si.f16_bits(xv * 4.0))
+        assert np.array_equal(q2, q) and sc2 == np.float32(sc) * np.float32(4.0)
+    q, sc = orc.kv_quant_row(np.zeros(64, np.uint16))
+    assert sc == 0 and np.all(q == 0)
+
+
+def _kv8_block(orc, nkv, d, page, kv, g):
+    """byte offset of the (page, K|V, kv head) block of an int8 cache"""
+    return page * 2 * nkv * (16 * d + 64) + (kv * nkv + g) * (16 * d + 64)
+
+
+def pin_kv_append_int8(orc, quick=False):
+    """The int8 append writes each k / v head's quantised row into its block's
+    slot and its scale into the block's scale array, nothing else; an absent
+    page writes nothing."""
+    rng = np.random.default_rng(43)
+    nq, nkv, d = 4, 2, 32
+    pages = 3
+    pb = orc.kv8_page_bytes(nkv, d)
+    assert pb == 2 * nkv * (16 * d + 64)
+    table = np.array([2, 0], np.int32)
+    qkv = si.f16_bits(rng.normal(0, 1, (nq + 2 * nkv) * d))
+    for pos in (0, 5, 21):
+        cache = np.full((pages, pb), 0xA5, np.uint8)
+        orc.kv_append_int8(qkv, nq, nkv, d, pos, cache, table)
+        flat = cache.reshape(-1)
+        want = np.full(flat.size, 0xA5, np.uint8)
+        for kv in (0, 1):
+            for g in range(nkv):
+                row = qkv[(nq + kv * nkv + g) * d:(nq + kv * nkv + g + 1) * d]
+                q, sc = orc.kv_quant_row(row)
+                o = _kv8_block(orc, nkv, d, table[pos // 16], kv, g)
+                want[o + (pos % 16) * d:o + (pos % 16 + 1) * d] = q.view(np.uint8)
+                so = o + 16 * d + 4 * (pos % 16)
+                want[so:so + 4] = np.array([sc], np.float32).view(np.uint8)
+        assert np.array_equal(flat, want), pos
+    cache = np.full((pages, pb), 0xA5, np.uint8)
+    orc.kv_append_int8(qkv, nq, nkv, d, 3, cache, np.array([7], np.int32))
+    assert np.all(cache == 0xA5)
+
+
+def pin_attention_int8(orc, quick=False):
+    """Attention over an int8 cache equals the (pinned) f16 attention over the
+    cache of its dequantised values, bit for bit, when those values are exact
+    in f16 (power-of-two scales): pins the block layout, the slot, the scale
+    placement and K vs V."""
+    rng = np.random.default_rng(47)
+    nq, nkv, d = 4, 2, 64
+    ctx = 45
+    pages = 4
+    table = np.array([3, 1, 0], np.int32)
+    pb = orc.kv8_page_bytes(nkv, d)
+    cache8 = np.zeros((pages, pb), np.uint8)
+    cache16 = np.zeros((pages, 2, nkv, 16, d), np.uint16)
+    for p in range(pages):
+        for kv in (0, 1):
+            for g in range(nkv):
+                codes = rng.integers(-127, 128, (16, d)).astype(np.int8)
+                scales = (2.0 ** -rng.integers(5, 9, 16)).astype(np.float32)
+                o = _kv8_block(orc, nkv, d, p, kv, g) - p * pb
+                cache8[p, o:o + 16 * d] = codes.view(np.uint8).reshape(-1)
+                cache8[p, o + 16 * d:o + 16 * d + 64] = scales.view(np.uint8)
+                cache16[p, kv, g] = si.f16_bits(codes.astype(np.float64) * scales[:, None])
+    q = si.f16_bits(rng.normal(0, 1, (nq, d)))
+    out8, a8 = orc.attention_decode_int8(q, cache8, table, ctx, nq, nkv, d, 0.11)
+    out16, a16 = orc.attention_decode(q, cache16, table, ctx, nq, nkv, d, 0.11)
+    assert np.array_equal(out8, out16) and np.array_equal(a8, a16)
+
+
 ALL_PINS = [
     pin_half_decode_all_patterns, pin_half_encode_rne,
     pin_gemv_rational, pin_gemv_exactly_representable, pin_gemv_closed_forms,
     pin_gemv_one_hot, pin_gemv_linearity, pin_gemm_rows,
     pin_silu, pin_ffn, pin_argmax, pin_lmhead, pin_add_rmsnorm, pin_rope, pin_attention,
     pin_layout_geometry, pin_layout_hand_example, pin_layout_roundtrip, pin_rope_layout,
-    pin_int3, pin_int3_layout,
+    pin_int3, pin_int3_layout, pin_kv_quant, pin_kv_append_int8, pin_attention_int8,
 ]

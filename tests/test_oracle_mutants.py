@@ -49,12 +49,12 @@ MUTANTS = [
     ("rope_layout_adjacent", "int64_t src = (pr / (d / 2)) * d + pr % (d / 2) + u * (d / 2);",
      "int64_t src = (pr / (d / 2)) * d + 2 * (pr % (d / 2)) + u;"),
     ("attn_group_modulo", "const int64_t g = h / (nq / nkv);", "const int64_t g = h % nkv;"),
-    ("attn_keys_from_v", "page_table[t / 16] * 2 + 0) * nkv + g) * 16 + t % 16)",
-     "page_table[t / 16] * 2 + 1) * nkv + g) * 16 + t % 16)"),
-    ("attn_slot", "page_table[t / 16] * 2 + 0) * nkv + g) * 16 + t % 16)",
-     "page_table[t / 16] * 2 + 0) * nkv + g) * 16 + t / 16)"),
-    ("attn_slot_major_v", "page_table[t / 16] * 2 + 1) * nkv + g) * 16 + t % 16) * d;",
-     "page_table[t / 16] * 2 + 1) * 16 + t % 16) * nkv + g) * d;"),
+    ("attn_keys_from_v", "q4o_half_to_double(q[h * d + i]) * kv_at(src, 0, g, t, i);",
+     "q4o_half_to_double(q[h * d + i]) * kv_at(src, 1, g, t, i);"),
+    ("attn_slot", "[(((page * 2 + kv) * src->nkv + g) * 16 + t % 16) * d + i]",
+     "[(((page * 2 + kv) * src->nkv + g) * 16 + t / 16) * d + i]"),
+    ("attn_slot_major", "[(((page * 2 + kv) * src->nkv + g) * 16 + t % 16) * d + i]",
+     "[(((page * 2 + kv) * 16 + t % 16) * src->nkv + g) * d + i]"),
     ("attn_no_scale", "sc[t] = scale * dot;", "sc[t] = dot;"),
     ("attn_unnormalised", "out[h * d + i] = o / den;", "out[h * d + i] = o;"),
     ("int3_group_of_64", "scales[r * G + col / 32]", "scales[r * G + col / 64]"),
@@ -71,6 +71,13 @@ MUTANTS = [
      "word |= (uint32_t)((codes[30] >> i) & 1) << 14;"),
     ("int3_pad_code_0", "codes[i] = real ? code3_at(words3, r, 32 * g + i, k) : 4;",
      "codes[i] = real ? code3_at(words3, r, 32 * g + i, k) : 0;"),
+    ("kv8_scale_128", "float s = m / 127.0f;", "float s = m / 128.0f;"),
+    ("kv8_truncate", "q[i] = (int8_t)rintf(t);", "q[i] = (int8_t)t;"),
+    ("kv8_append_slot", "q4o_kv_quant_row(row, d, (int8_t *)(blk + (pos % 16) * d), &s);",
+     "q4o_kv_quant_row(row, d, (int8_t *)(blk + (pos / 16) * d), &s);"),
+    ("kv8_scale_of_slot0", "memcpy(&s, blk + 16 * d + 4 * (t % 16), 4);", "memcpy(&s, blk + 16 * d, 4);"),
+    ("kv8_block_size", "(kv * src->nkv + g) * (16 * d + 64);", "(kv * src->nkv + g) * (16 * d);"),
+    ("kv8_code_slot", "(double)(int8_t)blk[(t % 16) * d + i]", "(double)(int8_t)blk[(t % 16) + i * 16]"),
     ("norm_unrounded_residual", "const double hv = q4o_half_to_double(q4o_double_to_half(v));",
      "const double hv = v;"),
 ]

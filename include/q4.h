@@ -331,6 +331,46 @@ int q4_attention_decode(const uint16_t *q, const uint16_t *kv_cache, const int32
                         int32_t n_pages, int32_t ctx, int32_t nq, int32_t nkv, int32_t d,
                         float scale, uint16_t *out, void *ws, int64_t ws_bytes, void *stream);
 
+/*
+ * The int8 KV cache ([P1] 完整的推理流水线: the paged KV cache has an optional
+ * int8 quantisation path that halves its memory; the pages give no scheme).
+ * Each (token, kv head) row of d values is stored as d int8 codes and one f32
+ * scale: scale = max_i |x_i| / 127 and code_i = rint(x_i / scale) (f32,
+ * correctly rounded division, ties to even; all codes 0 when the row is 0),
+ * so x_i ~ code_i * scale.  Page layout: [page][K=0|V=1][kv head] blocks of
+ * 16 rows of d codes (slot order) followed by the 16 rows' f32 scales, i.e.
+ * q4_kv_int8_page_bytes(nkv, d) = 2 * nkv * (16 d + 64) bytes per page
+ * (Phi-3-mini: 102,400 B against 196,608 B in f16).
+ * Returns 0 for an invalid shape (d not in 32 .. 256 step 32, nkv < 1, or a
+ * page of 2 GiB or more).
+ */
+int64_t q4_kv_int8_page_bytes(int32_t n_kv_heads, int32_t head_dim);
+
+/*
+ * Quantise the k and v heads of one fused QKV output into the int8 cache at
+ * position pos (slot pos % 16 of page page_table[pos / 16]); run it after
+ * q4_qkv_rope_append (whose own f16 append may be skipped with a NULL cache).
+ *   qkv        : device f16 [(n_q_heads + 2 n_kv_heads) * head_dim], 2-byte
+ *                aligned: q heads, k heads (roped), v heads
+ *   cache8     : device, n_pages * q4_kv_int8_page_bytes(..) bytes, 16-byte aligned
+ *   page_table : device int32, at least pos / 16 + 1 entries; an entry outside
+ *                [0, n_pages) appends nothing
+ * Errors: NULL, SHAPE, ALIGN, ALIAS, HIP.
+ */
+int q4_kv_append_int8(const uint16_t *qkv, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                      int32_t pos, void *cache8, const int32_t *page_table, int32_t n_pages,
+                      void *stream);
+
+/*
+ * q4_attention_decode over the int8 cache: K_t = code * scale, V_t = code *
+ * scale of each row, otherwise the same definition, arguments (cache8 as
+ * above, 16-byte aligned) and workspace (q4_workspace_bytes(Q4_OP_ATTENTION,
+ * ctx, nq, d)).  Errors as q4_attention_decode.
+ */
+int q4_attention_decode_int8(const uint16_t *q, const void *cache8, const int32_t *page_table,
+                             int32_t n_pages, int32_t ctx, int32_t nq, int32_t nkv, int32_t d,
+                             float scale, uint16_t *out, void *ws, int64_t ws_bytes, void *stream);
+
 /* Static text for a return code. */
 const char *q4_strerror(int code);
 

@@ -58,6 +58,10 @@ _SIGNATURES = {
     "q4_pack_rope": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _I64, _W, _P]),
     "q4_unpack": (ctypes.c_int, [_W, _P, _P, _P]),
     "q4_pack_int3": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _I64, _W, _P]),
+    "q4_kv_int8_page_bytes": (ctypes.c_int64, [_I32, _I32]),
+    "q4_kv_append_int8": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _I32, _P]),
+    "q4_attention_decode_int8": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                                ctypes.c_float, _P, _P, _I64, _P]),
     "q4_qkv_rope_append": (ctypes.c_int, [_W, _P, _I32, _I32, ctypes.c_double, _P, _P, _P, _I32,
                                           _P]),
     "q4_add_rmsnorm_qkv_rope_append": (ctypes.c_int, [_W, _P, _P, _P, ctypes.c_float, _P, _I32,
@@ -382,6 +386,55 @@ def attention_decode(q: torch.Tensor, kv_cache: torch.Tensor, page_table: torch.
     _check(_lib.q4_attention_decode(pq, kv_cache.data_ptr(), pt, pages, ctx, n_q_heads, nkv, d,
                                     float(scale), po, pws, need if need > 0 else 0, _stream(q)),
            "q4_attention_decode")
+    return out
+
+
+def kv_int8_page_bytes(n_kv_heads: int, head_dim: int) -> int:
+    return int(_lib.q4_kv_int8_page_bytes(n_kv_heads, head_dim))
+
+
+def kv_append_int8(qkv: torch.Tensor, n_q_heads: int, n_kv_heads: int, head_dim: int, pos: int,
+                   cache8: torch.Tensor, page_table: torch.Tensor) -> None:
+    """Quantise the k and v heads of a fused QKV output into the int8 cache
+    (uint8 [pages][q4_kv_int8_page_bytes]) at position pos (q4_kv_append_int8)."""
+    pq = _dev(qkv, "qkv", 2)
+    if qkv.numel() != (n_q_heads + 2 * n_kv_heads) * head_dim:
+        raise ValueError("qkv does not hold n_q_heads + 2 n_kv_heads heads of head_dim")
+    pb = kv_int8_page_bytes(n_kv_heads, head_dim)
+    if cache8.dim() != 2 or cache8.shape[1] != pb:
+        raise ValueError(f"cache8 must be [pages][{pb}] bytes")
+    pc = _dev(cache8, "cache8", 1)
+    pt = _dev(page_table, "page_table", 4)
+    _check(_lib.q4_kv_append_int8(pq, n_q_heads, n_kv_heads, head_dim, pos, pc, pt,
+                                  cache8.shape[0], _stream(qkv)), "q4_kv_append_int8")
+
+
+def attention_decode_int8(q: torch.Tensor, cache8: torch.Tensor, page_table: torch.Tensor,
+                          ctx: int, n_q_heads: int, n_kv_heads: int, head_dim: int, scale: float,
+                          out: Optional[torch.Tensor] = None,
+                          ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out f16 [nq][d]: attention of one decode token over the int8 cache
+    (q4_attention_decode_int8)."""
+    pb = kv_int8_page_bytes(n_kv_heads, head_dim)
+    if cache8.dim() != 2 or cache8.shape[1] != pb:
+        raise ValueError(f"cache8 must be [pages][{pb}] bytes")
+    pq = _dev(q, "q", 2)
+    if q.numel() != n_q_heads * head_dim:
+        raise ValueError(f"q has {q.numel()} elements, expected {n_q_heads * head_dim}")
+    pt = _dev(page_table, "page_table", 4)
+    if out is None:
+        out = torch.empty((n_q_heads, head_dim), dtype=torch.float16, device=q.device)
+    po = _dev(out, "out", 2)
+    need = int(_lib.q4_workspace_bytes(OP_ATTENTION, ctx, n_q_heads, head_dim))
+    pws = None
+    if need > 0:
+        if ws is None:
+            ws = workspace(q.device, need)
+        pws = ws.data_ptr()
+    _check(_lib.q4_attention_decode_int8(pq, _dev(cache8, "cache8", 1), pt, cache8.shape[0], ctx,
+                                         n_q_heads, n_kv_heads, head_dim, float(scale), po, pws,
+                                         need if need > 0 else 0, _stream(q)),
+           "q4_attention_decode_int8")
     return out
 
 

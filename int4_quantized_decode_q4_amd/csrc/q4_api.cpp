@@ -536,6 +536,64 @@ int q4_attention_decode(const uint16_t *q, const uint16_t *kv_cache, const int32
                                            static_cast<hipStream_t>(stream)));
 }
 
+int64_t q4_kv_int8_page_bytes(int32_t n_kv_heads, int32_t head_dim)
+{
+    if (n_kv_heads < 1 || head_dim < 32 || head_dim > 256 || head_dim % 32 != 0)
+        return 0;
+    const int64_t b = q4::kv_int8_page_bytes(n_kv_heads, head_dim);
+    return b <= INT32_MAX ? b : 0;
+}
+
+int q4_kv_append_int8(const uint16_t *qkv, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                      int32_t pos, void *cache8, const int32_t *page_table, int32_t n_pages,
+                      void *stream)
+{
+    if (!qkv || !cache8 || !page_table)
+        return Q4_ERR_NULL;
+    const int64_t pb = q4_kv_int8_page_bytes(n_kv_heads, head_dim);
+    if (pb == 0 || n_q_heads < 1 || pos < 0 || n_pages < 1)
+        return Q4_ERR_SHAPE;
+    if (!aligned(qkv, 2) || !aligned(cache8, 16) || !aligned(page_table, 4))
+        return Q4_ERR_ALIGN;
+    const int64_t qb = 2 * ((int64_t)n_q_heads + 2 * (int64_t)n_kv_heads) * head_dim;
+    const int64_t cb = (int64_t)n_pages * pb, tb = 4 * ((int64_t)pos / 16 + 1);
+    if (overlap(cache8, cb, qkv, qb) || overlap(cache8, cb, page_table, tb))
+        return Q4_ERR_ALIAS;
+    (void)hipGetLastError();
+    return hip_status(q4::launch_kv_append_int8(qkv, n_q_heads, n_kv_heads, head_dim, pos,
+                                                static_cast<uint8_t *>(cache8), page_table, n_pages,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int q4_attention_decode_int8(const uint16_t *q, const void *cache8, const int32_t *page_table,
+                             int32_t n_pages, int32_t ctx, int32_t nq, int32_t nkv, int32_t d,
+                             float scale, uint16_t *out, void *ws, int64_t ws_bytes, void *stream)
+{
+    if (!q || !cache8 || !page_table || !out)
+        return Q4_ERR_NULL;
+    const int64_t pb = q4_kv_int8_page_bytes(nkv, d);
+    if (pb == 0 || ctx < 1 || n_pages < 1 || nq < 1 || nq % nkv != 0 || !std::isfinite(scale))
+        return Q4_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(cache8, 16) || !aligned(page_table, 4) || !aligned(out, 4) ||
+        (ws && !aligned(ws, 16)))
+        return Q4_ERR_ALIGN;
+    const int64_t need = q4::attention_workspace_bytes(ctx, nq, d);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return Q4_ERR_WORKSPACE;
+    const int64_t qb = 2 * (int64_t)nq * d, cb = (int64_t)n_pages * pb;
+    const int64_t tb = 4 * (((int64_t)ctx + 15) / 16);
+    if (overlap(out, qb, q, qb) || overlap(out, qb, cache8, cb) || overlap(out, qb, page_table, tb))
+        return Q4_ERR_ALIAS;
+    if (need > 0 && (overlap(ws, need, q, qb) || overlap(ws, need, cache8, cb) ||
+                     overlap(ws, need, page_table, tb) || overlap(ws, need, out, qb)))
+        return Q4_ERR_ALIAS;
+    (void)hipGetLastError();
+    return hip_status(q4::launch_attention_int8(q, static_cast<const uint8_t *>(cache8), page_table,
+                                                n_pages, ctx, nq, nkv, d, scale, out,
+                                                need > 0 ? ws : nullptr,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 const char *q4_strerror(int code)
 {
     switch (code) {

@@ -101,6 +101,15 @@ int64_t attention_workspace_bytes(int64_t ctx, int64_t nq, int64_t d);
 hipError_t launch_attention(const uint16_t *q, const uint16_t *cache, const int32_t *page_table,
                             int32_t n_pages, int32_t ctx, int32_t nq, int32_t nkv, int32_t d,
                             float scale, uint16_t *out, void *ws, hipStream_t stream);
+// the int8 cache: page bytes, the attention over it (same workspace), and the
+// quantise-and-append of one fused QKV output
+int64_t kv_int8_page_bytes(int64_t nkv, int64_t d);
+hipError_t launch_attention_int8(const uint16_t *q, const uint8_t *cache8, const int32_t *page_table,
+                                 int32_t n_pages, int32_t ctx, int32_t nq, int32_t nkv, int32_t d,
+                                 float scale, uint16_t *out, void *ws, hipStream_t stream);
+hipError_t launch_kv_append_int8(const uint16_t *qkv, int32_t nq, int32_t nkv, int32_t d, int32_t pos,
+                                 uint8_t *cache8, const int32_t *page_table, int32_t n_pages,
+                                 hipStream_t stream);
 
 enum GemmPath { GEMM_PATH_AUTO = 0, GEMM_PATH_VALU = 1, GEMM_PATH_MFMA = 2 };
 

@@ -271,6 +271,47 @@ def test_attention_errors(q4):
     assert call(ws=O) == q4.ERR_ALIAS                # workspace over out
 
 
+def test_kv_int8_errors(q4, orc):
+    lib = q4.lib
+    assert lib.q4_kv_int8_page_bytes(32, 96) == orc.kv8_page_bytes(32, 96) == 102400
+    for nkv, d in ((0, 96), (32, 100), (32, 288), (32, 16)):
+        assert lib.q4_kv_int8_page_bytes(nkv, d) == 0
+    QKV, C, T = A + 0x200000, A + 0x1000000, A + 0x300000
+    f = lib.q4_kv_append_int8
+    assert f(None, 32, 32, 96, 0, C, T, 4, None) == q4.ERR_NULL
+    assert f(QKV, 32, 32, 96, 0, None, T, 4, None) == q4.ERR_NULL
+    assert f(QKV, 32, 32, 96, 0, C, None, 4, None) == q4.ERR_NULL
+    assert f(QKV, 32, 32, 100, 0, C, T, 4, None) == q4.ERR_SHAPE
+    assert f(QKV, 0, 32, 96, 0, C, T, 4, None) == q4.ERR_SHAPE
+    assert f(QKV, 32, 32, 96, -1, C, T, 4, None) == q4.ERR_SHAPE
+    assert f(QKV, 32, 32, 96, 0, C, T, 0, None) == q4.ERR_SHAPE
+    assert f(QKV + 1, 32, 32, 96, 0, C, T, 4, None) == q4.ERR_ALIGN
+    assert f(QKV, 32, 32, 96, 0, C + 8, T, 4, None) == q4.ERR_ALIGN
+    assert f(QKV, 32, 32, 96, 0, C, T + 2, 4, None) == q4.ERR_ALIGN
+    assert f(QKV, 32, 32, 96, 0, QKV, T, 4, None) == q4.ERR_ALIAS        # cache over qkv
+    assert f(QKV, 32, 32, 96, 0, C, C + 64, 4, None) == q4.ERR_ALIAS     # table inside cache
+    g = lib.q4_attention_decode_int8
+    Q, O, Wk = A + 0x200000, A + 0x400000, A + 0x500000
+    need = lib.q4_workspace_bytes(q4.OP_ATTENTION, 4096, 32, 96)
+    ok = (Q, C, T, 300, 4096, 32, 32, 96, 0.1, O, Wk, need, None)
+    def call(**kw):
+        names = ("q", "c", "t", "pages", "ctx", "nq", "nkv", "d", "scale", "o", "ws", "wsb", "s")
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return g(*[args[n] for n in names])
+    assert call(c=None) == q4.ERR_NULL
+    assert call(o=None) == q4.ERR_NULL
+    assert call(ctx=0) == q4.ERR_SHAPE
+    assert call(d=80) == q4.ERR_SHAPE
+    assert call(nq=30, nkv=4) == q4.ERR_SHAPE
+    assert call(scale=float("nan")) == q4.ERR_SHAPE
+    assert call(c=C + 8) == q4.ERR_ALIGN
+    assert call(q=Q + 8) == q4.ERR_ALIGN
+    assert call(ws=None) == q4.ERR_WORKSPACE
+    assert call(o=C + 4096) == q4.ERR_ALIAS          # out inside the cache
+    assert call(ws=O) == q4.ERR_ALIAS
+
+
 def test_lmhead_errors(q4):
     lib = q4.lib
     X, L, I, WS = A + 0x200000, A + 0x300000, A + 0x400000, A + 0x500000

@@ -558,6 +558,28 @@ def variants(torch, q4, si, np, K, W):
                                              "frac": round(nb / us / 1e3 / PEAK_HBM_GBS, 4),
                                              "bytes": nb, "launches": 2}
     del caches
+
+    # the same attention over the int8 cache (codes + one f32 scale per row),
+    # and the quantise-and-append of one token's k and v heads
+    pb8 = q4.kv_int8_page_bytes(32, 96)
+    kv8_bytes = pages * pb8
+    n8 = copies_for(kv8_bytes)
+    caches8 = []
+    for _ in range(n8):
+        c8 = torch.randint(-127, 128, (pages, pb8), dtype=torch.int8, device="cuda").view(torch.uint8)
+        sc = c8.view(pages, 2, 32, 16 * 96 + 64)[:, :, :, 16 * 96:]
+        sc.copy_(torch.full((pages, 2, 32, 16), 0.01, device="cuda").view(torch.uint8).view(pages, 2, 32, 64))
+        caches8.append(c8)
+    us8 = per_launch_us(torch, lambda i: q4.attention_decode_int8(qv, caches8[i % n8], pt, ctx, 32, 32, 96,
+                                                                   96 ** -0.5, out=ao, ws=ws), K, W)
+    nb8 = kv8_bytes + 2 * 2 * 3072 + 4 * pages
+    out["attention_decode_int8_32x96_ctx4096"] = {"us": round(us8, 3), "gbs": round(nb8 / us8 / 1e3, 1),
+                                                  "frac": round(nb8 / us8 / 1e3 / PEAK_HBM_GBS, 4),
+                                                  "bytes": nb8, "launches": 2}
+    qkv = torch.randn(9216, device="cuda").to(torch.float16)
+    usa = per_launch_us(torch, lambda i: q4.kv_append_int8(qkv, 32, 32, 96, 1000, caches8[i % n8], pt), K, W)
+    out["kv_append_int8_32x96"] = {"us": round(usa, 3)}
+    del caches8
     out["decode_layer_phi3_ctx1024"] = decode_layer(torch, q4, si, np, K, W, 1024)
 
     # LM head, f32 logits + argmax

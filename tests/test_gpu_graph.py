@@ -52,3 +52,73 @@ def test_graph_replays_match_eager(q4):
         torch.cuda.synchronize()
         for name, a, b in zip(("y", "h", "down", "logits", "argmax"), eager, (y, h, yd, logits, am)):
             assert torch.equal(a, b), f"replay {rep}: {name} differs from eager"
+
+
+def test_graph_replays_decode_layer_ops(q4):
+    """The decode-step ops around the matmul replayed from one graph: add +
+    RMSNorm + QKV + RoPE + f16 append, the int8 append, attention over both
+    caches (two launches each), an int3 GEMV; every replay equal to eager,
+    with the caches reset between replays."""
+    rng = np.random.default_rng(13)
+    nq = nkv = 32
+    d, k, ctx = 96, 3072, 700
+    n = (nq + 2 * nkv) * d
+    w, s = si.draw_weight(rng, n, k)
+    pw = q4.pack_rope(dev_u32(w), dev_u16(s), d)
+    w3, s3 = si.draw_weight3(rng, 3072, 3072)
+    p3 = q4.pack_int3(dev_u32(w3), dev_u16(s3))
+    x = dev_f16(si.draw_x(rng, k))
+    r = dev_f16(si.draw_x(rng, k))
+    gamma = dev_f16(si.f16_bits(rng.uniform(0.5, 1.5, k)))
+    pages = (ctx + 15) // 16 + 1
+    pt = torch.from_numpy(rng.permutation(pages)[: pages - 1].astype(np.int32)).cuda()
+    cache0 = torch.randn((pages, 2, nkv, 16, d), device="cuda").to(torch.float16)
+    pb8 = q4.kv_int8_page_bytes(nkv, d)
+    cache80 = torch.randint(0, 256, (pages, pb8), dtype=torch.uint8, device="cuda")
+    cache80.view(pages, 2, nkv, 16 * d + 64)[:, :, :, 16 * d:].copy_(
+        torch.full((pages, 2, nkv, 16), 0.01, device="cuda").view(torch.uint8))
+    cache, cache8 = cache0.clone(), cache80.clone()
+    qkv = torch.empty(n, dtype=torch.float16, device="cuda")
+    hres = torch.empty(k, dtype=torch.float16, device="cuda")
+    att = torch.empty((nq, d), dtype=torch.float16, device="cuda")
+    att8 = torch.empty((nq, d), dtype=torch.float16, device="cuda")
+    y3 = torch.empty(3072, dtype=torch.float16, device="cuda")
+    ws = torch.zeros(q4.lib.q4_workspace_bytes(q4.OP_ATTENTION, ctx, nq, d), dtype=torch.uint8,
+                     device="cuda")
+    ws8 = torch.zeros_like(ws)
+    pos = ctx - 1
+
+    def run():
+        q4.qkv_rope_append(pw, x, nq, pos, 10000.0, cache, pt, out=qkv,
+                           norm=(r, gamma, 1e-5, hres))
+        q4.kv_append_int8(qkv, nq, nkv, d, pos, cache8, pt)
+        q4.attention_decode(qkv[: nq * d], cache, pt, ctx, nq, d ** -0.5, out=att, ws=ws)
+        q4.attention_decode_int8(qkv[: nq * d], cache8, pt, ctx, nq, nkv, d, d ** -0.5, out=att8,
+                                 ws=ws8)
+        q4.gemv(p3, x, y3)
+
+    outs = (qkv, hres, att, att8, y3, cache, cache8)
+    run()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    cache.copy_(cache0)
+    cache8.copy_(cache80)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    names = ("qkv", "residual", "attention", "attention int8", "int3 gemv", "cache", "int8 cache")
+    for rep in range(4):
+        for t in outs[:5]:
+            t.zero_()                      # eager work between replays
+        cache.copy_(cache0)
+        cache8.copy_(cache80)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(names, eager, outs):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from eager"

@@ -14,10 +14,9 @@
 //    context so the grid holds about one block per compute unit (measured
 //    best: more, shorter blocks and more wavefronts per block were slower);
 //    its 4 wavefronts take a quarter each, 16 positions (one page) at a
-//    time: 4 lanes per
-//    position, each lane d/4 dims interleaved in 16-byte pieces, so every
-//    load instruction reads 16 whole 64-byte spans; the wavefront's page
-//    indices are read once, one per lane;
+//    time: 4 lanes per position, each lane d/4 dims interleaved in 16-byte
+//    pieces, so every load instruction reads 16 whole 64-byte spans; the
+//    wavefront's page indices are read once, one per lane;
 //  * the next step's rows are requested before the current one is used, by
 //    buffer loads through a resource that spans the head's K and V runs of
 //    the step's page; a step past the wavefront's end or on an absent page
@@ -124,6 +123,10 @@ constexpr int kWaves = Q4_ATT_WAVES;              // wavefronts per block
 constexpr int kStep = 16;                         // positions per wavefront step (one page)
 constexpr int kMinChunk = kStep * kWaves;         // positions per block: one step per wavefront ..
 constexpr int kMaxChunk = 64 * kStep * kWaves;    // .. up to 64 pages per wavefront
+#ifndef Q4_ATT_TARGET_BLOCKS
+#define Q4_ATT_TARGET_BLOCKS 256
+#endif
+constexpr int64_t kTargetBlocks = Q4_ATT_TARGET_BLOCKS;   // blocks the chunking aims for
 
 __device__ __forceinline__ float dot8(uint4 a, uint4 b, float acc)
 {
@@ -442,20 +445,10 @@ __global__ __launch_bounds__(64) void attention_combine_kernel(const float *__re
 // page indices, the final merge, the partial record) over more rows.
 int64_t chunk_len(int64_t ctx, int64_t nq)
 {
-#ifdef Q4_ATT_FIXED_CHUNK
-    (void)ctx;
-    (void)nq;
-    return Q4_ATT_FIXED_CHUNK;
-#else
-#ifndef Q4_ATT_TARGET_BLOCKS
-#define Q4_ATT_TARGET_BLOCKS 256
-#endif
-    constexpr int64_t kTargetBlocks = Q4_ATT_TARGET_BLOCKS;
     int64_t c = kMaxChunk;
     while (c > kMinChunk && nq * ((ctx + c - 1) / c) < kTargetBlocks)
         c >>= 1;
     return c;
-#endif
 }
 
 template <int DL, bool I8>

@@ -72,6 +72,10 @@ class Oracle:
         lib.q4o_gemv3.argtypes = [_P, _P, _P, _I64, _I64, _P, _P]
         lib.q4o_gemv3.restype = ctypes.c_int
         lib.q4o_encode3.argtypes = [_P, _P, _I64, _I64, _P]
+        lib.q4o_encode3_gate_up.argtypes = [_P, _P, _P, _P, _I64, _I64, _P]
+        lib.q4o_encode3_gate_up.restype = ctypes.c_int
+        lib.q4o_ffn_gate_up_silu3.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P]
+        lib.q4o_ffn_gate_up_silu3.restype = ctypes.c_int
         lib.q4o_encode3.restype = ctypes.c_int
         lib.q4o_layout3_bytes.argtypes = [_I64, _I64]
         lib.q4o_layout3_bytes.restype = ctypes.c_int64
@@ -201,6 +205,31 @@ class Oracle:
                                                 ctx, nq, nkv, d, float(scale), _ptr(out), _ptr(a))
         assert rc == 0
         return out, a
+
+    def ffn_gate_up_silu3(self, gw3, gs, uw3, us, x):
+        """int3 FFN: dict with h, g, u, ag, au (all f64 [n])."""
+        n, k = gw3.shape[0], x.shape[0]
+        self._check_w3(gw3, gs, n, k)
+        self._check_w3(uw3, us, n, k)
+        arrs = [np.ascontiguousarray(a) for a in (gw3, gs, uw3, us)]
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        out = {name: np.empty(n, np.float64) for name in ("h", "g", "u", "ag", "au")}
+        rc = self.lib.q4o_ffn_gate_up_silu3(
+            *[_ptr(a) for a in arrs], _ptr(x), n, k,
+            *[_ptr(out[name]) for name in ("h", "g", "u", "ag", "au")])
+        assert rc == 0
+        return out
+
+    def encode3_gate_up(self, gw3, gs, uw3, us) -> np.ndarray:
+        """The int3 gate/up device layout (2n interleaved logical rows)."""
+        n, k = gw3.shape[0], gw3.shape[1] * 32 // 3
+        self._check_w3(gw3, gs, n, k)
+        self._check_w3(uw3, us, n, k)
+        arrs = [np.ascontiguousarray(a) for a in (gw3, gs, uw3, us)]
+        dst = np.full(int(self.lib.q4o_layout3_bytes(2 * n, k)), 0xA5, np.uint8)
+        rc = self.lib.q4o_encode3_gate_up(*[_ptr(a) for a in arrs], n, k, _ptr(dst))
+        assert rc == 0
+        return dst
 
     def encode3(self, words3, scales) -> np.ndarray:
         """The int3 device layout (bytes) of words3 [n][3k/32], scales [n][k/32]."""

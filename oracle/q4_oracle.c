@@ -165,6 +165,12 @@ double q4o_silu(double g)
     return g / (1.0 + exp(-g));
 }
 
+/* the gated product of one intermediate row: SiLU of the gate times the up */
+static double gated(double g, double u)
+{
+    return q4o_silu(g) * u;
+}
+
 /*
  * Fused gate/up + SiLU ([P1] 内核融合, fused_ffn): h = SiLU(x.Wg^T) * (x.Wu^T),
  * elementwise over the n intermediate rows.  Also returns the gate and up
@@ -181,7 +187,7 @@ int q4o_ffn_gate_up_silu(const uint32_t *gw, const uint16_t *gs,
         double gv, uv, agv, auv;
         q4o_gemv(gw + r * (k / 8), gs + r * (k / 32), x, 1, k, &gv, &agv);
         q4o_gemv(uw + r * (k / 8), us + r * (k / 32), x, 1, k, &uv, &auv);
-        h[r] = q4o_silu(gv) * uv;
+        h[r] = gated(gv, uv);
         if (g)
             g[r] = gv;
         if (u)
@@ -620,6 +626,31 @@ int q4o_gemv3(const uint32_t *words3, const uint16_t *scales, const uint16_t *x,
     return 0;
 }
 
+/* The fused gate/up + SiLU FFN over int3 weights: q4o_ffn_gate_up_silu with
+ * the int3 matmul (gate and up rows each a canonical int3 stream). */
+int q4o_ffn_gate_up_silu3(const uint32_t *gw3, const uint16_t *gs, const uint32_t *uw3,
+                          const uint16_t *us, const uint16_t *x, int64_t n, int64_t k, double *h,
+                          double *g, double *u, double *ag, double *au)
+{
+    if (n < 0 || k < 32 || k % 32 != 0)
+        return -1;
+    for (int64_t r = 0; r < n; ++r) {
+        double gv, uv, agv, auv;
+        q4o_gemv3(gw3 + r * (3 * k / 32), gs + r * (k / 32), x, 1, k, &gv, &agv);
+        q4o_gemv3(uw3 + r * (3 * k / 32), us + r * (k / 32), x, 1, k, &uv, &auv);
+        h[r] = gated(gv, uv);
+        if (g)
+            g[r] = gv;
+        if (u)
+            u[r] = uv;
+        if (ag)
+            ag[r] = agv;
+        if (au)
+            au[r] = auv;
+    }
+    return 0;
+}
+
 /*
  * Device layout of an int3 weight (layout Q4_LAYOUT_INT3, version 1), from
  * its specification.  The tile geometry (L, CG, P, TR, tiles) is the int4
@@ -633,6 +664,8 @@ int q4o_gemv3(const uint32_t *words3, const uint16_t *scales, const uint16_t *x,
  *   word i, bits 16+3m .. 18+3m   (m = 0..4): code 10i + 5 + m,
  *   word i, bit 15: bit i of code 30;  word i, bit 31: bit i of code 31.
  * Padding (rows >= n or groups >= G): every code 4, scale 0x0000.
+ * The gate/up int3 layout (Q4_LAYOUT_INT3_GATE_UP) is the same placement over
+ * 2n logical rows, row 2i = gate row i and row 2i+1 = up row i.
  */
 static void place3(uint8_t *dst, int64_t r, int64_t g, int L, int CG, int64_t TR,
                    int64_t TB3, const int *codes, uint16_t scale)
@@ -654,12 +687,14 @@ static void place3(uint8_t *dst, int64_t r, int64_t g, int L, int CG, int64_t TR
     memcpy(scale_dst, &scale, 2);
 }
 
-/* int3 device layout of words3 [n][3k/32], scales [n][k/32] */
-int q4o_encode3(const uint32_t *words3, const uint16_t *scales, int64_t n, int64_t k,
-                uint8_t *dst)
+/* int3 device layout over `rows` logical rows; logical row r reads row r of
+ * (w0, s0), or with a second source row r / 2 of (w0, s0) for even r and of
+ * (w1, s1) for odd r (gate/up) */
+static int encode3(const uint32_t *w0, const uint16_t *s0, const uint32_t *w1, const uint16_t *s1,
+                   int64_t rows, int64_t k, uint8_t *dst)
 {
     int64_t geo[6];
-    if (q4o_layout_geometry(n, k, geo))
+    if (q4o_layout_geometry(rows, k, geo))
         return -1;
     int L = (int)geo[0], CG = (int)geo[1], P = (int)geo[2];
     int64_t TR = geo[3], T = geo[4];
@@ -667,14 +702,31 @@ int q4o_encode3(const uint32_t *words3, const uint16_t *scales, int64_t n, int64
     int64_t G = k / 32;
     int codes[32];
     for (int64_t r = 0; r < T * TR; ++r) {
+        const uint32_t *rw = w1 ? (r % 2 ? w1 : w0) : w0;
+        const uint16_t *rs = w1 ? (r % 2 ? s1 : s0) : s0;
+        const int64_t src = w1 ? r / 2 : r;
         for (int64_t g = 0; g < (int64_t)P * L * CG; ++g) {
-            int real = r < n && g < G;
+            int real = r < rows && g < G;
             for (int i = 0; i < 32; ++i)
-                codes[i] = real ? code3_at(words3, r, 32 * g + i, k) : 4;
-            place3(dst, r, g, L, CG, TR, TB3, codes, real ? scales[r * G + g] : 0);
+                codes[i] = real ? code3_at(rw, src, 32 * g + i, k) : 4;
+            place3(dst, r, g, L, CG, TR, TB3, codes, real ? rs[src * G + g] : 0);
         }
     }
     return 0;
+}
+
+/* int3 device layout of words3 [n][3k/32], scales [n][k/32] */
+int q4o_encode3(const uint32_t *words3, const uint16_t *scales, int64_t n, int64_t k,
+                uint8_t *dst)
+{
+    return encode3(words3, scales, NULL, NULL, n, k, dst);
+}
+
+/* int3 gate/up layout: 2n logical rows, gate i on row 2i, up i on row 2i + 1 */
+int q4o_encode3_gate_up(const uint32_t *gw3, const uint16_t *gs, const uint32_t *uw3,
+                        const uint16_t *us, int64_t n, int64_t k, uint8_t *dst)
+{
+    return encode3(gw3, gs, uw3, us, 2 * n, k, dst);
 }
 
 /* bytes of the int3 device layout */

@@ -642,6 +642,35 @@ def pin_int3_layout(orc, quick=False):
         assert np.array_equal(dc, codes), (n, k)
         assert np.array_equal(ds, scales)
         assert pc <= {4} and ps <= {0}
+    # gate/up: 2n logical rows, even rows the gate, odd rows the up matrix
+    n, k = 5, 96
+    gc, uc = rng.integers(0, 8, size=(n, k)), rng.integers(0, 8, size=(n, k))
+    gs = si.f16_bits(rng.uniform(0.005, 0.02, size=(n, k // 32)))
+    us = si.f16_bits(rng.uniform(0.005, 0.02, size=(n, k // 32)))
+    buf = orc.encode3_gate_up(_stream_words3(gc), gs, _stream_words3(uc), us)
+    g6 = orc.layout_geometry(2 * n, k)
+    dc, ds, pc, ps = _decode3_device(buf, 2 * n, k, g6)
+    assert np.array_equal(dc[0::2], gc) and np.array_equal(dc[1::2], uc)
+    assert np.array_equal(ds[0::2], gs) and np.array_equal(ds[1::2], us)
+    assert pc <= {4} and ps <= {0}
+
+
+def pin_int3_ffn(orc, quick=False):
+    """int3 FFN: the gate (not the up) is the gated half; constant codes give
+    h = silu(cg * S) * cu * S in closed form."""
+    rng = np.random.default_rng(53)
+    n, k = 3, 64
+    x = si.draw_x(rng, k)
+    xv = x.view(np.float16).astype(np.float64)
+    s = si.f16_bits(np.full((n, k // 32), 0.0625))
+    S = 0.0625 * xv.sum()
+    for cg, cu in ((7, 5), (1, 6), (4, 7)):
+        gw, uw = _stream_words3(np.full((n, k), cg)), _stream_words3(np.full((n, k), cu))
+        r = orc.ffn_gate_up_silu3(gw, s, uw, s, x)
+        gv, uv = (cg - 4) * S, (cu - 4) * S
+        want = gv / (1.0 + math.exp(-gv)) * uv
+        assert np.allclose(r["h"], want, rtol=1e-12, atol=1e-15), (cg, cu, r["h"], want)
+        assert np.allclose(r["g"], gv, rtol=1e-13) and np.allclose(r["u"], uv, rtol=1e-13)
 
 
 def pin_kv_quant(orc, quick=False):
@@ -735,5 +764,5 @@ ALL_PINS = [
     pin_gemv_one_hot, pin_gemv_linearity, pin_gemm_rows,
     pin_silu, pin_ffn, pin_argmax, pin_lmhead, pin_add_rmsnorm, pin_rope, pin_attention,
     pin_layout_geometry, pin_layout_hand_example, pin_layout_roundtrip, pin_rope_layout,
-    pin_int3, pin_int3_layout, pin_kv_quant, pin_kv_append_int8, pin_attention_int8,
+    pin_int3, pin_int3_layout, pin_int3_ffn, pin_kv_quant, pin_kv_append_int8, pin_attention_int8,
 ]

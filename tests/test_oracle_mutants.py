@@ -23,7 +23,7 @@ MUTANTS = [
     ("rne_ties_up", "(fmod(f, 2.0) == 0.0) ? f : f + 1.0", "f + 1.0"),
     ("half_encode_no_overflow", "if (E > 15)", "if (E > 16)"),
     ("silu_sign", "g / (1.0 + exp(-g))", "g / (1.0 + exp(g))"),
-    ("silu_on_up", "h[r] = q4o_silu(gv) * uv;", "h[r] = q4o_silu(uv) * gv;"),
+    ("silu_on_up", "return q4o_silu(g) * u;", "return q4o_silu(u) * g;"),
     ("argmax_last_tie", "if (v[i] > v[best])", "if (v[i] >= v[best])"),
     ("abs_sum_signed", "asum += fabs(term);", "asum += term;"),
     ("last_k_dropped", "for (int64_t kk = 0; kk < k; ++kk) {", "for (int64_t kk = 0; kk < k - 1; ++kk) {"),
@@ -69,8 +69,12 @@ MUTANTS = [
      "word |= (uint32_t)codes[10 * i + 5 + m] << (16 + 3 * (4 - m));"),
     ("int3_extra_bit_14", "word |= (uint32_t)((codes[30] >> i) & 1) << 15;",
      "word |= (uint32_t)((codes[30] >> i) & 1) << 14;"),
-    ("int3_pad_code_0", "codes[i] = real ? code3_at(words3, r, 32 * g + i, k) : 4;",
-     "codes[i] = real ? code3_at(words3, r, 32 * g + i, k) : 0;"),
+    ("int3_pad_code_0", "codes[i] = real ? code3_at(rw, src, 32 * g + i, k) : 4;",
+     "codes[i] = real ? code3_at(rw, src, 32 * g + i, k) : 0;"),
+    ("int3_gate_up_swapped", "const uint32_t *rw = w1 ? (r % 2 ? w1 : w0) : w0;",
+     "const uint32_t *rw = w1 ? (r % 2 ? w0 : w1) : w0;"),
+    ("int3_ffn_up_rows_as_gate", "q4o_gemv3(uw3 + r * (3 * k / 32), us + r * (k / 32), x, 1, k, &uv, &auv);",
+     "q4o_gemv3(gw3 + r * (3 * k / 32), gs + r * (k / 32), x, 1, k, &uv, &auv);"),
     ("kv8_scale_128", "float s = m / 127.0f;", "float s = m / 128.0f;"),
     ("kv8_truncate", "q[i] = (int8_t)rintf(t);", "q[i] = (int8_t)t;"),
     ("kv8_append_slot", "q4o_kv_quant_row(row, d, (int8_t *)(blk + (pos % 16) * d), &s);",

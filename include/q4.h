@@ -77,7 +77,8 @@ extern "C" {
 #define Q4_LAYOUT_ROWS    1  /* plain rows: q4_gemv, q4_gemm, q4_lmhead_f32 */
 #define Q4_LAYOUT_GATE_UP 2  /* interleaved gate/up rows: q4_ffn_gate_up_silu */
 #define Q4_LAYOUT_ROPE    3  /* rotary-paired head rows: q4_qkv_rope_append */
-#define Q4_LAYOUT_INT3    4  /* int3 rows (q4_pack_int3): q4_gemv */
+#define Q4_LAYOUT_INT3    4  /* int3 rows (q4_pack_int3): q4_gemv, q4_lmhead_f32 */
+#define Q4_LAYOUT_INT3_GATE_UP 5  /* int3 gate/up rows (q4_pack_int3_gate_up): q4_ffn_gate_up_silu */
 #define Q4_LAYOUT_VERSION 1
 
 /* operations, for q4_workspace_bytes */
@@ -161,10 +162,20 @@ int q4_pack_rope(const uint32_t *words, const uint16_t *scales, int32_t n, int32
  *            12-byte lane units (word i of a group's unit: codes 10i + m at
  *            bits 3m and 10i + 5 + m at bits 16 + 3m, m = 0..4; bit i of
  *            codes 30 and 31 at bits 15 and 31); padding is code 4, scale 0.
- * The result feeds q4_gemv (and q4_unpack).  Errors as q4_pack.
+ * The result feeds q4_gemv and q4_lmhead_f32 (and q4_unpack).  Errors as q4_pack.
  */
 int q4_pack_int3(const uint32_t *words3, const uint16_t *scales, int32_t n, int32_t k,
                  void *dst, int64_t dst_bytes, q4_weight *out, void *stream);
+
+/*
+ * The gate and up halves of an FFN as int3 weights (each canonical as in
+ * q4_pack_int3) in one interleaved layout (logical row 2i = gate row i, 2i+1
+ * = up row i) for q4_ffn_gate_up_silu; dst needs q4_packed_bytes(n, k,
+ * Q4_LAYOUT_INT3_GATE_UP) bytes.  Errors as q4_pack.
+ */
+int q4_pack_int3_gate_up(const uint32_t *gw3, const uint16_t *gs, const uint32_t *uw3,
+                         const uint16_t *us, int32_t n, int32_t k, void *dst, int64_t dst_bytes,
+                         q4_weight *out, void *stream);
 
 /*
  * Inverse of q4_pack / q4_pack_gate_up / q4_pack_rope / q4_pack_int3 (for
@@ -218,7 +229,8 @@ int q4_gemm_path(const q4_weight *w, const uint16_t *X, int32_t m, uint16_t *Y, 
 /*
  * h = SiLU(x . Wg^T) * (x . Wu^T) in one kernel ([P1] 内核融合, fused_ffn),
  * SiLU(g) = g / (1 + e^-g) in f32, h rounded to f16.
- *   w : Q4_LAYOUT_GATE_UP with n rows per half; x : f16 [k]; h : f16 [n]
+ *   w : Q4_LAYOUT_GATE_UP (or Q4_LAYOUT_INT3_GATE_UP) with n rows per half;
+ *       x : f16 [k]; h : f16 [n]
  */
 int q4_ffn_gate_up_silu(const q4_weight *w, const uint16_t *x, uint16_t *h,
                         void *stream);
@@ -226,6 +238,7 @@ int q4_ffn_gate_up_silu(const q4_weight *w, const uint16_t *x, uint16_t *h,
 /*
  * LM head with f32 logits and greedy argmax ([P1] 完整的推理流水线: the f32
  * output variant for sampling stability, and the argmax dispatch).
+ *   w      : Q4_LAYOUT_ROWS, or Q4_LAYOUT_INT3
  *   logits : device f32 [n], 8-byte aligned
  *   argmax : device int32 [1] or NULL; the lowest index holding the maximum
  *            logit (as computed in f32)

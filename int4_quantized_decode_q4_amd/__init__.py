@@ -35,6 +35,7 @@ OK = 0
 ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_LAYOUT = -1, -2, -3, -4
 ERR_WORKSPACE, ERR_ALIAS, ERR_HIP, ERR_SIZE = -5, -6, -7, -8
 LAYOUT_ROWS, LAYOUT_GATE_UP, LAYOUT_ROPE, LAYOUT_INT3, LAYOUT_VERSION = 1, 2, 3, 4, 1
+LAYOUT_INT3_GATE_UP = 5
 GEMM_AUTO, GEMM_VALU, GEMM_MFMA = 0, 1, 2
 OP_GEMV, OP_GEMM, OP_FFN, OP_LMHEAD, OP_ATTENTION = 1, 2, 3, 4, 5
 
@@ -58,6 +59,7 @@ _SIGNATURES = {
     "q4_pack_rope": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _I64, _W, _P]),
     "q4_unpack": (ctypes.c_int, [_W, _P, _P, _P]),
     "q4_pack_int3": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _I64, _W, _P]),
+    "q4_pack_int3_gate_up": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _P, _I64, _W, _P]),
     "q4_kv_int8_page_bytes": (ctypes.c_int64, [_I32, _I32]),
     "q4_kv_append_int8": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _I32, _P]),
     "q4_attention_decode_int8": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32,
@@ -236,12 +238,29 @@ def pack_int3(words3: torch.Tensor, scales: torch.Tensor) -> PackedWeight:
     return PackedWeight(buf, desc)
 
 
+def pack_int3_gate_up(gw3, gs, uw3, us) -> PackedWeight:
+    """Gate and up halves as int3 weights, each canonical words3 [n][3k/32] /
+    scales [n][k/32] -> one interleaved layout for ffn_gate_up_silu
+    (q4_pack_int3_gate_up)."""
+    n, kw = gw3.shape
+    if kw % 3:
+        raise ValueError("words3 must have 3 words per group of 32 codes")
+    k = kw * 32 // 3
+    ptrs = [_dev(gw3, "gate words3", 4, (n, kw)), _dev(gs, "gate scales", 2, (n, k // 32)),
+            _dev(uw3, "up words3", 4, (n, kw)), _dev(us, "up scales", 2, (n, k // 32))]
+    buf = _alloc_packed(n, k, LAYOUT_INT3_GATE_UP, gw3.device)
+    desc = q4_weight()
+    _check(_lib.q4_pack_int3_gate_up(*ptrs, n, k, buf.data_ptr(), buf.numel(), ctypes.byref(desc),
+                                     _stream(gw3)), "q4_pack_int3_gate_up")
+    return PackedWeight(buf, desc)
+
+
 def unpack(w: PackedWeight) -> Tuple[torch.Tensor, torch.Tensor]:
     """Device layout -> canonical (words int32 [rows][k/8] -- int3: [rows][3k/32]
     --, scales int16 [rows][k/32]); rows = 2n for a gate/up weight (gate 0,
     up 0, gate 1, ...)."""
-    rows = w.n * (2 if w.layout == LAYOUT_GATE_UP else 1)
-    wcols = 3 * w.k // 32 if w.layout == LAYOUT_INT3 else w.k // 8
+    rows = w.n * (2 if w.layout in (LAYOUT_GATE_UP, LAYOUT_INT3_GATE_UP) else 1)
+    wcols = 3 * w.k // 32 if w.layout in (LAYOUT_INT3, LAYOUT_INT3_GATE_UP) else w.k // 8
     words = torch.empty((rows, wcols), dtype=torch.int32, device=w.device)
     scales = torch.empty((rows, w.k // 32), dtype=torch.int16, device=w.device)
     _check(_lib.q4_unpack(ctypes.byref(w.desc), words.data_ptr(), scales.data_ptr(),

@@ -60,11 +60,14 @@ int check_weight(const q4_weight *w, int32_t want_layout, q4::Geometry *geo, int
     if (w->layout == Q4_LAYOUT_ROPE &&
         (w->head_dim < 2 || w->head_dim % 2 != 0 || w->n % w->head_dim != 0))
         return Q4_ERR_SHAPE;
-    if (w->layout == Q4_LAYOUT_INT3 && w->k > kInt3MaxK)
+    const bool int3 = w->layout == Q4_LAYOUT_INT3 || w->layout == Q4_LAYOUT_INT3_GATE_UP;
+    if (int3 && w->k > kInt3MaxK)
         return Q4_ERR_SHAPE;
-    *rows = (want_layout == Q4_LAYOUT_GATE_UP) ? 2 * (int64_t)w->n : (int64_t)w->n;
-    const bool ok = w->layout == Q4_LAYOUT_INT3 ? q4::layout_geometry3(*rows, w->k, geo)
-                                                : q4::layout_geometry(*rows, w->k, geo);
+    *rows = (want_layout == Q4_LAYOUT_GATE_UP || want_layout == Q4_LAYOUT_INT3_GATE_UP)
+                ? 2 * (int64_t)w->n
+                : (int64_t)w->n;
+    const bool ok = int3 ? q4::layout_geometry3(*rows, w->k, geo)
+                         : q4::layout_geometry(*rows, w->k, geo);
     if (!ok)
         return Q4_ERR_SHAPE;
     if (w->bytes < geo->tiles * geo->tile_bytes)
@@ -122,11 +125,13 @@ int64_t q4_packed_bytes(int32_t n, int32_t k, int32_t layout)
 {
     if (!valid_shape(n, k) ||
         (layout != Q4_LAYOUT_ROWS && layout != Q4_LAYOUT_GATE_UP && layout != Q4_LAYOUT_ROPE &&
-         layout != Q4_LAYOUT_INT3))
+         layout != Q4_LAYOUT_INT3 && layout != Q4_LAYOUT_INT3_GATE_UP))
         return 0;
     q4::Geometry geo;
-    const int64_t rows = layout == Q4_LAYOUT_GATE_UP ? 2 * (int64_t)n : (int64_t)n;
-    if (layout == Q4_LAYOUT_INT3)
+    const int64_t rows = (layout == Q4_LAYOUT_GATE_UP || layout == Q4_LAYOUT_INT3_GATE_UP)
+                             ? 2 * (int64_t)n
+                             : (int64_t)n;
+    if (layout == Q4_LAYOUT_INT3 || layout == Q4_LAYOUT_INT3_GATE_UP)
         return k <= kInt3MaxK && q4::layout_geometry3(rows, k, &geo) ? geo.tiles * geo.tile_bytes : 0;
     if (!q4::layout_geometry(rows, k, &geo))
         return 0;
@@ -185,32 +190,38 @@ int q4_pack_gate_up(const uint32_t *gw, const uint16_t *gs, const uint32_t *uw,
     return pack_common(gw, gs, uw, us, n, k, q4::PACK_GATE_UP, 0, dst, dst_bytes, out, stream);
 }
 
-int q4_pack_int3(const uint32_t *words3, const uint16_t *scales, int32_t n, int32_t k, void *dst,
-                 int64_t dst_bytes, q4_weight *out, void *stream)
+// int3 packing; with (uw3, us) the gate/up interleave of (gw3, gs) and them
+int pack3_common(const uint32_t *gw3, const uint16_t *gs, const uint32_t *uw3, const uint16_t *us,
+                 int32_t n, int32_t k, void *dst, int64_t dst_bytes, q4_weight *out, void *stream)
 {
-    if (!words3 || !scales || !dst || !out)
+    const bool gate_up = uw3 != nullptr || us != nullptr;
+    if (!gw3 || !gs || !dst || !out || (gate_up && (!uw3 || !us)))
         return Q4_ERR_NULL;
     if (!valid_shape(n, k) || k > kInt3MaxK)
         return Q4_ERR_SHAPE;
-    if (!aligned(words3, 4) || !aligned(scales, 2) || !aligned(dst, 256))
+    if (!aligned(gw3, 4) || !aligned(gs, 2) || !aligned(dst, 256) ||
+        (gate_up && (!aligned(uw3, 4) || !aligned(us, 2))))
         return Q4_ERR_ALIGN;
+    const int64_t rows = gate_up ? 2 * (int64_t)n : (int64_t)n;
     q4::Geometry geo;
-    if (!q4::layout_geometry3(n, k, &geo))
+    if (!q4::layout_geometry3(rows, k, &geo))
         return Q4_ERR_SHAPE;
     const int64_t need = geo.tiles * geo.tile_bytes;
     if (dst_bytes < need)
         return Q4_ERR_SIZE;
     const int64_t wbytes = (int64_t)n * (3 * (int64_t)k / 32) * 4, sbytes = (int64_t)n * (k / 32) * 2;
-    if (overlap(dst, need, words3, wbytes) || overlap(dst, need, scales, sbytes))
+    if (overlap(dst, need, gw3, wbytes) || overlap(dst, need, gs, sbytes) ||
+        (gate_up && (overlap(dst, need, uw3, wbytes) || overlap(dst, need, us, sbytes))))
         return Q4_ERR_ALIAS;
     (void)hipGetLastError();
-    const int rc = hip_status(q4::launch_pack3(words3, scales, n, k, geo, dst,
+    const int rc = hip_status(q4::launch_pack3(gw3, gs, gate_up ? uw3 : nullptr,
+                                               gate_up ? us : nullptr, rows, k, geo, dst,
                                                static_cast<hipStream_t>(stream)));
     if (rc != Q4_OK)
         return rc;
     out->n = n;
     out->k = k;
-    out->layout = Q4_LAYOUT_INT3;
+    out->layout = gate_up ? Q4_LAYOUT_INT3_GATE_UP : Q4_LAYOUT_INT3;
     out->version = Q4_LAYOUT_VERSION;
     out->data = dst;
     out->bytes = need;
@@ -219,19 +230,35 @@ int q4_pack_int3(const uint32_t *words3, const uint16_t *scales, int32_t n, int3
     return Q4_OK;
 }
 
+int q4_pack_int3(const uint32_t *words3, const uint16_t *scales, int32_t n, int32_t k, void *dst,
+                 int64_t dst_bytes, q4_weight *out, void *stream)
+{
+    return pack3_common(words3, scales, nullptr, nullptr, n, k, dst, dst_bytes, out, stream);
+}
+
+int q4_pack_int3_gate_up(const uint32_t *gw3, const uint16_t *gs, const uint32_t *uw3,
+                         const uint16_t *us, int32_t n, int32_t k, void *dst, int64_t dst_bytes,
+                         q4_weight *out, void *stream)
+{
+    if (!uw3 || !us)
+        return Q4_ERR_NULL;
+    return pack3_common(gw3, gs, uw3, us, n, k, dst, dst_bytes, out, stream);
+}
+
 int q4_unpack(const q4_weight *w, uint32_t *words, uint16_t *scales, void *stream)
 {
     if (!w || !words || !scales)
         return Q4_ERR_NULL;
     if (w->layout != Q4_LAYOUT_ROWS && w->layout != Q4_LAYOUT_GATE_UP &&
-        w->layout != Q4_LAYOUT_ROPE && w->layout != Q4_LAYOUT_INT3)
+        w->layout != Q4_LAYOUT_ROPE && w->layout != Q4_LAYOUT_INT3 &&
+        w->layout != Q4_LAYOUT_INT3_GATE_UP)
         return Q4_ERR_LAYOUT;
     q4::Geometry geo;
     int64_t rows = 0;
     const int rc = check_weight(w, w->layout, &geo, &rows);
     if (rc != Q4_OK)
         return rc;
-    const bool int3 = w->layout == Q4_LAYOUT_INT3;
+    const bool int3 = w->layout == Q4_LAYOUT_INT3 || w->layout == Q4_LAYOUT_INT3_GATE_UP;
     if (!aligned(words, int3 ? 4 : 16) || !aligned(scales, 2))
         return Q4_ERR_ALIGN;
     const int64_t wbytes = int3 ? rows * (3 * (int64_t)w->k / 32) * 4 : rows * w->k / 2;
@@ -267,7 +294,8 @@ int q4_gemv(const q4_weight *w, const uint16_t *x, uint16_t *y, void *stream)
         return Q4_ERR_ALIAS;
     (void)hipGetLastError();
     if (int3)
-        return hip_status(q4::launch_gemv3(geo, w->data, x, y, rows, w->k,
+        return hip_status(q4::launch_gemv3(geo, q4::EPI_F16, w->data, x, y, rows, w->k, w->n,
+                                           q4::ArgmaxScratch{nullptr, nullptr},
                                            static_cast<hipStream_t>(stream)));
     return hip_status(q4::launch_gemv_family(geo, q4::EPI_F16, w->data, x, y, rows, w->k, w->n,
                                              q4::ArgmaxScratch{nullptr, nullptr}, nullptr, nullptr,
@@ -312,7 +340,9 @@ int q4_ffn_gate_up_silu(const q4_weight *w, const uint16_t *x, uint16_t *h, void
     int64_t rows = 0;
     if (!w || !x || !h)
         return Q4_ERR_NULL;
-    int rc = check_weight(w, Q4_LAYOUT_GATE_UP, &geo, &rows);
+    // int4 or int3 gate/up pairs
+    const bool int3 = w->layout == Q4_LAYOUT_INT3_GATE_UP;
+    int rc = check_weight(w, int3 ? Q4_LAYOUT_INT3_GATE_UP : Q4_LAYOUT_GATE_UP, &geo, &rows);
     if (rc != Q4_OK)
         return rc;
     if (!aligned(x, 16) || !aligned(h, 2))
@@ -321,6 +351,10 @@ int q4_ffn_gate_up_silu(const q4_weight *w, const uint16_t *x, uint16_t *h, void
         overlap(h, 2 * (int64_t)w->n, w->data, w->bytes))
         return Q4_ERR_ALIAS;
     (void)hipGetLastError();
+    if (int3)
+        return hip_status(q4::launch_gemv3(geo, q4::EPI_SILU, w->data, x, h, rows, w->k, w->n,
+                                           q4::ArgmaxScratch{nullptr, nullptr},
+                                           static_cast<hipStream_t>(stream)));
     return hip_status(q4::launch_gemv_family(geo, q4::EPI_SILU, w->data, x, h, rows, w->k, w->n,
                                              q4::ArgmaxScratch{nullptr, nullptr}, nullptr, nullptr,
                                              static_cast<hipStream_t>(stream)));
@@ -333,7 +367,9 @@ int q4_lmhead_f32(const q4_weight *w, const uint16_t *x, float *logits, int32_t 
     int64_t rows = 0;
     if (!w || !x || !logits)
         return Q4_ERR_NULL;
-    int rc = check_weight(w, Q4_LAYOUT_ROWS, &geo, &rows);
+    // int4 or int3 rows
+    const bool int3 = w->layout == Q4_LAYOUT_INT3;
+    int rc = check_weight(w, int3 ? Q4_LAYOUT_INT3 : Q4_LAYOUT_ROWS, &geo, &rows);
     if (rc != Q4_OK)
         return rc;
     if (!aligned(x, 16) || !aligned(logits, 8) || (argmax && !aligned(argmax, 4)))
@@ -358,6 +394,9 @@ int q4_lmhead_f32(const q4_weight *w, const uint16_t *x, float *logits, int32_t 
         overlap(logits, lbytes, w->data, w->bytes))
         return Q4_ERR_ALIAS;
     (void)hipGetLastError();
+    if (int3)
+        return hip_status(q4::launch_gemv3(geo, q4::EPI_F32, w->data, x, logits, rows, w->k, w->n, am,
+                                           static_cast<hipStream_t>(stream)));
     return hip_status(q4::launch_gemv_family(geo, q4::EPI_F32, w->data, x, logits, rows, w->k,
                                              w->n, am, nullptr, nullptr, static_cast<hipStream_t>(stream)));
 }

@@ -86,14 +86,17 @@ hipError_t launch_gemv_family(const Geometry &geo, Epilogue epi, const void *wda
                               int64_t n_out, ArgmaxScratch am, const NormArgs *norm,
                               const RopeArgs *rope, hipStream_t stream);
 
-// int3 weights (q4_kernels.hip): repacking both ways and the GEMV (single
-// pass, k <= 8192, f16 output).
-hipError_t launch_pack3(const uint32_t *w3, const uint16_t *s, int64_t rows, int64_t k,
-                        const Geometry &geo, void *dst, hipStream_t stream);
+// int3 weights (q4_kernels.hip): repacking both ways (plain rows, or gate/up
+// interleaved with a second source) and the matmuls (single pass, k <= 8192;
+// f16, f32 + argmax and SiLU epilogues).
+hipError_t launch_pack3(const uint32_t *w3, const uint16_t *s, const uint32_t *w3_up,
+                        const uint16_t *s_up, int64_t rows, int64_t k, const Geometry &geo,
+                        void *dst, hipStream_t stream);
 hipError_t launch_unpack3(const void *src, int64_t rows, int64_t k, const Geometry &geo,
                           uint32_t *w3, uint16_t *s, hipStream_t stream);
-hipError_t launch_gemv3(const Geometry &geo, const void *wdata, const uint16_t *x, uint16_t *y,
-                        int64_t rows, int64_t k, hipStream_t stream);
+hipError_t launch_gemv3(const Geometry &geo, Epilogue epi, const void *wdata, const uint16_t *x,
+                        void *out, int64_t rows, int64_t k, int64_t n_out, ArgmaxScratch am,
+                        hipStream_t stream);
 
 // Paged-attention decode (q4_attention.hip): workspace bytes (0 when the
 // context fits one chunk) and the launch.

@@ -166,8 +166,11 @@ __device__ __forceinline__ void device3_words(const uint32_t (&codes)[32], uint3
     }
 }
 
-// One thread per destination 12-byte unit (and the scale beside it).
-__global__ void pack3_kernel(const uint32_t *__restrict__ w3, const uint16_t *__restrict__ sc,
+// One thread per destination 12-byte unit (and the scale beside it).  With a
+// second source (w3b, scb: the up half of a gate/up pair) logical row r reads
+// row r / 2 of the gate (even r) or of the up matrix (odd r).
+__global__ void pack3_kernel(const uint32_t *__restrict__ w3a, const uint16_t *__restrict__ sca,
+                             const uint32_t *__restrict__ w3b, const uint16_t *__restrict__ scb,
                              int64_t rows, int64_t k, int L, int CG, int P, int64_t units,
                              uint8_t *__restrict__ dst)
 {
@@ -188,12 +191,14 @@ __global__ void pack3_kernel(const uint32_t *__restrict__ w3, const uint16_t *__
     uint32_t codes[32];
     uint16_t scale = 0;
     if (r < rows && g < G) {
-        const uint32_t *src = w3 + r * (3 * G) + 3 * g;
+        const bool up = w3b != nullptr && (r & 1);
+        const int64_t row = w3b != nullptr ? r >> 1 : r;
+        const uint32_t *src = (up ? w3b : w3a) + row * (3 * G) + 3 * g;
         const uint32_t w[3] = {src[0], src[1], src[2]};
 #pragma unroll
         for (int i = 0; i < 32; ++i)
             codes[i] = canonical3_code(w, i);
-        scale = sc[r * G + g];
+        scale = (up ? scb : sca)[row * G + g];
     } else {
 #pragma unroll
         for (int i = 0; i < 32; ++i)
@@ -1249,12 +1254,14 @@ hipError_t launch_unpack(const void *src, int64_t rows, int64_t k, PackMode mode
     return hipGetLastError();
 }
 
-hipError_t launch_pack3(const uint32_t *w3, const uint16_t *s, int64_t rows, int64_t k,
-                        const Geometry &geo, void *dst, hipStream_t stream)
+hipError_t launch_pack3(const uint32_t *w3, const uint16_t *s, const uint32_t *w3_up,
+                        const uint16_t *s_up, int64_t rows, int64_t k, const Geometry &geo,
+                        void *dst, hipStream_t stream)
 {
     const int64_t units = geo.tiles * geo.P * 2 * geo.CG * 64;
     hipLaunchKernelGGL(pack3_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream,
-                       w3, s, rows, k, geo.L, geo.CG, geo.P, units, static_cast<uint8_t *>(dst));
+                       w3, s, w3_up, s_up, rows, k, geo.L, geo.CG, geo.P, units,
+                       static_cast<uint8_t *>(dst));
     return hipGetLastError();
 }
 
@@ -1267,55 +1274,79 @@ hipError_t launch_unpack3(const void *src, int64_t rows, int64_t k, const Geomet
     return hipGetLastError();
 }
 
-// int3 GEMV: the int4 plan (block or split kernel) with 12-byte units,
-// single pass (k <= 8192), f16 output.
-template <int L, int CG>
-static void launch_gemv3_lc(const Geometry &geo, const uint8_t *wd, const uint16_t *x, uint16_t *y,
-                            int64_t rows, int64_t k, hipStream_t stream)
+// int3 matmuls: the int4 plan (block or split kernel) with 12-byte units,
+// single pass (k <= 8192); epilogues f16 (GEMV), f32 + argmax (LM head) and
+// SiLU (gate/up interleaved rows; n_out = rows / 2).
+template <int L, int CG, int EPI>
+static void launch_gemv3_lce(const GemvPlan &plan, const Geometry &geo, const uint8_t *wd,
+                             const uint16_t *x, void *out, int64_t rows, int64_t k, int64_t n_out,
+                             ArgmaxScratch am, hipStream_t stream)
 {
-    const GemvPlan plan = plan_gemv(geo);
     const dim3 grid((unsigned)plan.blocks), block((unsigned)plan.threads);
-    void *out = static_cast<void *>(y);
-    const ArgmaxScratch am{nullptr, nullptr};
     const NormArgs nm{nullptr, nullptr, nullptr, 0.f};
     if (plan.mode == MODE_SPLIT)
-        hipLaunchKernelGGL((gemv_split_kernel<L, CG, EPI_F16, false, 3>), grid, block, 0, stream, wd, x,
-                           out, rows, k, geo.tiles, rows, am, nm, NoRope{});
+        hipLaunchKernelGGL((gemv_split_kernel<L, CG, EPI, false, 3>), grid, block, 0, stream, wd, x,
+                           out, rows, k, geo.tiles, n_out, am, nm, NoRope{});
     else
-        hipLaunchKernelGGL((gemv_block_kernel<L, CG, EPI_F16, false, 3>), grid, block, 0, stream, wd, x,
-                           out, rows, k, geo.tiles, rows, am, nm, NoRope{});
+        hipLaunchKernelGGL((gemv_block_kernel<L, CG, EPI, false, 3>), grid, block, 0, stream, wd, x,
+                           out, rows, k, geo.tiles, n_out, am, nm, NoRope{});
+}
+
+template <int L, int CG>
+static bool launch_gemv3_lc(Epilogue epi, const GemvPlan &plan, const Geometry &geo,
+                            const uint8_t *wd, const uint16_t *x, void *out, int64_t rows,
+                            int64_t k, int64_t n_out, ArgmaxScratch am, hipStream_t stream)
+{
+    switch (epi) {
+    case EPI_F16: launch_gemv3_lce<L, CG, EPI_F16>(plan, geo, wd, x, out, rows, k, n_out, am, stream); return true;
+    case EPI_F32: launch_gemv3_lce<L, CG, EPI_F32>(plan, geo, wd, x, out, rows, k, n_out, am, stream); return true;
+    case EPI_SILU: launch_gemv3_lce<L, CG, EPI_SILU>(plan, geo, wd, x, out, rows, k, n_out, am, stream); return true;
+    default: return false;
+    }
 }
 
 template <int L>
-static bool launch_gemv3_l(const Geometry &geo, const uint8_t *wd, const uint16_t *x, uint16_t *y,
-                           int64_t rows, int64_t k, hipStream_t stream)
+static bool launch_gemv3_l(Epilogue epi, const GemvPlan &plan, const Geometry &geo,
+                           const uint8_t *wd, const uint16_t *x, void *out, int64_t rows, int64_t k,
+                           int64_t n_out, ArgmaxScratch am, hipStream_t stream)
 {
     switch (geo.CG) {
-    case 1: launch_gemv3_lc<L, 1>(geo, wd, x, y, rows, k, stream); return true;
-    case 2: launch_gemv3_lc<L, 2>(geo, wd, x, y, rows, k, stream); return true;
-    case 3: launch_gemv3_lc<L, 3>(geo, wd, x, y, rows, k, stream); return true;
-    case 4: launch_gemv3_lc<L, 4>(geo, wd, x, y, rows, k, stream); return true;
+    case 1: return launch_gemv3_lc<L, 1>(epi, plan, geo, wd, x, out, rows, k, n_out, am, stream);
+    case 2: return launch_gemv3_lc<L, 2>(epi, plan, geo, wd, x, out, rows, k, n_out, am, stream);
+    case 3: return launch_gemv3_lc<L, 3>(epi, plan, geo, wd, x, out, rows, k, n_out, am, stream);
+    case 4: return launch_gemv3_lc<L, 4>(epi, plan, geo, wd, x, out, rows, k, n_out, am, stream);
     }
     return false;
 }
 
-hipError_t launch_gemv3(const Geometry &geo, const void *wdata, const uint16_t *x, uint16_t *y,
-                        int64_t rows, int64_t k, hipStream_t stream)
+hipError_t launch_gemv3(const Geometry &geo, Epilogue epi, const void *wdata, const uint16_t *x,
+                        void *out, int64_t rows, int64_t k, int64_t n_out, ArgmaxScratch am,
+                        hipStream_t stream)
 {
     if (geo.P != 1 || k > kBlockXHalves)
         return hipErrorInvalidValue;
+    const GemvPlan plan = plan_gemv(geo);
     const uint8_t *wd = static_cast<const uint8_t *>(wdata);
     bool ok = false;
     switch (geo.L) {
-    case 64: ok = launch_gemv3_l<64>(geo, wd, x, y, rows, k, stream); break;
-    case 32: ok = launch_gemv3_l<32>(geo, wd, x, y, rows, k, stream); break;
-    case 16: ok = launch_gemv3_l<16>(geo, wd, x, y, rows, k, stream); break;
-    case 8: ok = launch_gemv3_l<8>(geo, wd, x, y, rows, k, stream); break;
-    case 4: ok = launch_gemv3_l<4>(geo, wd, x, y, rows, k, stream); break;
-    case 2: ok = launch_gemv3_l<2>(geo, wd, x, y, rows, k, stream); break;
-    case 1: ok = launch_gemv3_l<1>(geo, wd, x, y, rows, k, stream); break;
+    case 64: ok = launch_gemv3_l<64>(epi, plan, geo, wd, x, out, rows, k, n_out, am, stream); break;
+    case 32: ok = launch_gemv3_l<32>(epi, plan, geo, wd, x, out, rows, k, n_out, am, stream); break;
+    case 16: ok = launch_gemv3_l<16>(epi, plan, geo, wd, x, out, rows, k, n_out, am, stream); break;
+    case 8: ok = launch_gemv3_l<8>(epi, plan, geo, wd, x, out, rows, k, n_out, am, stream); break;
+    case 4: ok = launch_gemv3_l<4>(epi, plan, geo, wd, x, out, rows, k, n_out, am, stream); break;
+    case 2: ok = launch_gemv3_l<2>(epi, plan, geo, wd, x, out, rows, k, n_out, am, stream); break;
+    case 1: ok = launch_gemv3_l<1>(epi, plan, geo, wd, x, out, rows, k, n_out, am, stream); break;
     }
-    return ok ? hipGetLastError() : hipErrorInvalidValue;
+    if (!ok)
+        return hipErrorInvalidValue;
+    if (epi == EPI_F32 && am.partials != nullptr) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(argmax_reduce_kernel, dim3(1), dim3(64), 0, stream, am.partials,
+                           plan.blocks, am.result);
+    }
+    return hipGetLastError();
 }
 
 struct GemvArgs {

@@ -50,7 +50,7 @@ def test_int3_packed_bytes_matches_oracle(q4, orc, n, k):
     assert q4.packed_bytes(n, k, q4.LAYOUT_INT3) == orc.lib.q4o_layout3_bytes(n, k)
 
 
-def test_int3_errors(q4):
+def test_int3_errors(q4, orc):
     lib = q4.lib
     out = q4.q4_weight()
     r = ctypes.byref(out)
@@ -76,11 +76,28 @@ def test_int3_errors(q4):
                        None) == q4.ERR_SIZE
     assert lib.q4_gemv(ctypes.byref(w3), X + 8, Y, None) == q4.ERR_ALIGN
     assert lib.q4_gemv(ctypes.byref(w3), X, X, None) == q4.ERR_ALIAS
-    # the other ops refuse int3 weights
+    # the LM head takes int3 rows (validated like int4); GEMM, FFN and the
+    # norm / RoPE ops refuse them, and the gate/up layout is only for the FFN
+    assert lib.q4_lmhead_f32(ctypes.byref(w3), X, Y, A + 0x600000, None, 0, None) == q4.ERR_WORKSPACE
+    assert lib.q4_lmhead_f32(ctypes.byref(w3), X, Y + 4, None, None, 0, None) == q4.ERR_ALIGN
     assert lib.q4_gemm(ctypes.byref(w3), X, 4, Y, None, 0, None) == q4.ERR_LAYOUT
-    assert lib.q4_lmhead_f32(ctypes.byref(w3), X, Y, None, None, 0, None) == q4.ERR_LAYOUT
     assert lib.q4_ffn_gate_up_silu(ctypes.byref(w3), X, Y, None) == q4.ERR_LAYOUT
     assert lib.q4_unpack(ctypes.byref(w3), W + 2, S, None) == q4.ERR_ALIGN
+    g3 = weight(q4, layout=q4.LAYOUT_INT3_GATE_UP)
+    assert g3.bytes == q4.packed_bytes(64, 96, q4.LAYOUT_INT3_GATE_UP) == orc.lib.q4o_layout3_bytes(128, 96)
+    assert lib.q4_gemv(ctypes.byref(g3), X, Y, None) == q4.ERR_LAYOUT
+    assert lib.q4_lmhead_f32(ctypes.byref(g3), X, Y, None, None, 0, None) == q4.ERR_LAYOUT
+    assert lib.q4_ffn_gate_up_silu(ctypes.byref(g3), X + 8, Y, None) == q4.ERR_ALIGN
+    assert lib.q4_ffn_gate_up_silu(ctypes.byref(weight(q4, layout=q4.LAYOUT_INT3_GATE_UP,
+                                                        nbytes=g3.bytes - 1)), X, Y, None) == q4.ERR_SIZE
+    fg = lib.q4_pack_int3_gate_up
+    nbg = g3.bytes
+    assert fg(W, S, None, S, 64, 96, D, nbg, r, None) == q4.ERR_NULL
+    assert fg(W, S, W, S, 64, 8224, D, 10 ** 9, r, None) == q4.ERR_SHAPE
+    assert fg(W, S, W + 2, S, 64, 96, D, nbg, r, None) == q4.ERR_ALIGN
+    assert fg(W, S, W, S, 64, 96, D, nbg - 1, r, None) == q4.ERR_SIZE
+    assert fg(W, S, D, S, 64, 96, D, nbg, r, None) == q4.ERR_ALIAS
+    assert out.data is None
 
 
 def test_packed_bytes_invalid(q4):

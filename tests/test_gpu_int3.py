@@ -1,14 +1,16 @@
 """The int3 variant of the matmul on the GPU against the oracle: the packed
-layout byte for byte, the unpack round trip, GEMV parity at the decode shapes
-and at ragged/edge shapes (f16 output bound as for int4), bit-exact one-hot
-reads (codes that cross a word boundary included), exactly representable
-sums, closed forms and determinism."""
+layouts (plain and gate/up) byte for byte, the unpack round trip, GEMV parity
+at the decode shapes and at ragged/edge shapes (f16 output bound as for
+int4), bit-exact one-hot reads (codes that cross a word boundary included),
+exactly representable sums, closed forms and determinism; the fused FFN and
+the f32 LM head with argmax over int3 weights."""
 import numpy as np
 import pytest
 import torch
 
 import seeded_inputs as si
-from parity import assert_within, dev_f16, dev_u16, dev_u32, host_f16_as_f64, host_u16, tol_f16
+from parity import (argmax_ok, assert_within, dev_f16, dev_u16, dev_u32, host_f16_as_f64, host_u16,
+                    tol_f16, tol_f32, tol_ffn)
 
 pytestmark = pytest.mark.gpu
 
@@ -127,3 +129,39 @@ def test_gemv_int3_deterministic(q4):
     x = dev_f16(si.draw_x(rng, 3072))
     outs = [host_u16(q4.gemv(pw, x)) for _ in range(3)]
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+@pytest.mark.parametrize("n,k", [(8192, 3072), (64, 3072), (17, 96), (130, 64), (999, 544),
+                                 (40, 8192)])
+def test_pack_int3_gate_up_and_ffn(q4, orc, n, k):
+    rng = np.random.default_rng(7 * n + k)
+    gw, gs = si.draw_weight3(rng, n, k)
+    uw, us = si.draw_weight3(rng, n, k)
+    x = si.draw_x(rng, k)
+    pw = q4.pack_int3_gate_up(dev_u32(gw), dev_u16(gs), dev_u32(uw), dev_u16(us))
+    assert pw.layout == q4.LAYOUT_INT3_GATE_UP
+    if n * k <= 3072 * 1024:
+        assert np.array_equal(pw.buf.cpu().numpy(), orc.encode3_gate_up(gw, gs, uw, us))
+        ww, ss = q4.unpack(pw)
+        ww, ss = ww.cpu().numpy().view(np.uint32), ss.cpu().numpy().view(np.uint16)
+        assert np.array_equal(ww[0::2], gw) and np.array_equal(ww[1::2], uw)
+        assert np.array_equal(ss[0::2], gs) and np.array_equal(ss[1::2], us)
+    h = q4.ffn_gate_up_silu(pw, dev_f16(x))
+    ref = orc.ffn_gate_up_silu3(gw, gs, uw, us, x)
+    r = assert_within(host_f16_as_f64(h), ref["h"], tol_ffn(ref), f"int3 ffn {n}x{k}")
+    print(f"max err/tol {r:.3g}")
+
+
+@pytest.mark.parametrize("n,k", [(32064, 3072), (1001, 3072), (7, 160), (1001, 8192), (3, 8192)])
+def test_lmhead_int3(q4, orc, n, k):
+    rng = np.random.default_rng(11 * n + k)
+    w3, s3 = si.draw_weight3(rng, n, k)
+    x = si.draw_x(rng, k)
+    pw = q4.pack_int3(dev_u32(w3), dev_u16(s3))
+    for _ in range(2):   # the workspace is reused
+        logits, idx = q4.lmhead_f32(pw, dev_f16(x))
+    ref, a = orc.gemv3(w3, s3, x)
+    got = logits.cpu().numpy().astype(np.float64)
+    assert_within(got, ref, tol_f32(a), f"int3 lm head {n}x{k}")
+    assert argmax_ok(int(idx.item()), ref, a, orc.argmax(ref))
+    assert int(idx.item()) == int(np.argmax(got))

@@ -483,6 +483,28 @@ def variants(torch, q4, si, np, K, W):
                   "frac": round(tot_bytes / us_set / 1e3 / PEAK_HBM_GBS, 4), "bytes": tot_bytes}
     out["int3_gemv_phi3_layer_set"] = rec
     del i3
+    # int3 fused gate/up + SiLU (2 x 8192 x 3072) and LM head (32064 x 3072, f32 + argmax)
+    gw, gs = si.draw_weight3(rng, 8192, 3072)
+    uw, us = si.draw_weight3(rng, 8192, 3072)
+    gu3_bytes = 2 * weight3_bytes(8192, 3072) + 2 * 3072 + 2 * 8192
+    r3 = Rotation(q4, q4.pack_int3_gate_up(dev_u32(gw), dev_u16(gs), dev_u32(uw), dev_u16(us)),
+                  copies_for(gu3_bytes))
+    x3 = dev_f16(si.draw_x(rng, 3072))
+    h3 = torch.empty(8192, dtype=torch.float16, device="cuda")
+    us3 = per_launch_us(torch, lambda i: q4.ffn_gate_up_silu(r3[i], x3, h3), K, W)
+    del r3
+    lw, ls = si.draw_weight3(rng, 32064, 3072)
+    lm3_bytes = weight3_bytes(32064, 3072) + 2 * 3072 + 4 * 32064 + 4
+    r3 = Rotation(q4, q4.pack_int3(dev_u32(lw), dev_u16(ls)), copies_for(lm3_bytes))
+    lg = torch.empty(32064, dtype=torch.float32, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    ws3 = q4.workspace(x3.device, int(q4.lib.q4_workspace_bytes(q4.OP_LMHEAD, 1, 32064, 3072)))
+    usl = per_launch_us(torch, lambda i: q4.lmhead_f32(r3[i], x3, lg, am, ws=ws3), K, W)
+    del r3
+    out["int3_ffn_and_lm_head"] = {
+        "ffn_us": round(us3, 3), "ffn_gbs": round(gu3_bytes / us3 / 1e3, 1), "ffn_bytes": gu3_bytes,
+        "lm_head_us": round(usl, 3), "lm_head_gbs": round(lm3_bytes / usl / 1e3, 1),
+        "lm_head_bytes": lm3_bytes, "lm_head_launches": 2}
 
     # fused gate/up + SiLU, then down
     inp = si.workload(si.FFN, seed=0)

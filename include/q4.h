@@ -87,7 +87,6 @@ extern "C" {
 #define Q4_OP_FFN     3
 #define Q4_OP_LMHEAD  4
 #define Q4_OP_ATTENTION 5  /* q4_workspace_bytes(Q4_OP_ATTENTION, ctx, n_q_heads, head_dim) */
-#define Q4_OP_ATTENTION_OPROJ 6  /* (Q4_OP_ATTENTION_OPROJ, ctx, n_q_heads, head_dim) */
 
 /*
  * Host-side descriptor of a packed weight, filled by q4_pack*; only `data`
@@ -384,26 +383,6 @@ int q4_kv_append_int8(const uint16_t *qkv, int32_t n_q_heads, int32_t n_kv_heads
 int q4_attention_decode_int8(const uint16_t *q, const void *cache8, const int32_t *page_table,
                              int32_t n_pages, int32_t ctx, int32_t nq, int32_t nkv, int32_t d,
                              float scale, uint16_t *out, void *ws, int64_t ws_bytes, void *stream);
-
-/*
- * Attention of one decode token followed by the output projection, with the
- * merge of the context chunks done inside the projection's x staging (the
- * attention step and the matmul after it, [P1] 内核融合; 2 launches instead
- * of attention's 2 plus the matmul's 1):
- *   y = dequant(W_o) . attention(q, cache)     (attention as q4_attention_decode /
- *                                               q4_attention_decode_int8, rounded to f16)
- * The bits of y equal those of q4_attention_decode(_int8) followed by q4_gemv.
- *   kv_cache : the f16 cache (kv_int8 = 0, layout of q4_attention_decode) or the
- *              int8 cache (kv_int8 = 1, layout of q4_attention_decode_int8)
- *   w_o      : Q4_LAYOUT_ROWS, k = nq * d; y : device f16 [w_o->n], 4-byte aligned
- *   ws       : q4_workspace_bytes(Q4_OP_ATTENTION_OPROJ, ctx, nq, d) bytes,
- *              256-byte aligned (always needed; contents need no initialisation)
- * Other arguments and errors as q4_attention_decode, plus LAYOUT / SIZE for w_o.
- */
-int q4_attention_oproj(const uint16_t *q, const void *kv_cache, int32_t kv_int8,
-                       const int32_t *page_table, int32_t n_pages, int32_t ctx, int32_t nq,
-                       int32_t nkv, int32_t d, float scale, const q4_weight *w_o, uint16_t *y,
-                       void *ws, int64_t ws_bytes, void *stream);
 
 /* Static text for a return code. */
 const char *q4_strerror(int code);

@@ -37,7 +37,7 @@ ERR_WORKSPACE, ERR_ALIAS, ERR_HIP, ERR_SIZE = -5, -6, -7, -8
 LAYOUT_ROWS, LAYOUT_GATE_UP, LAYOUT_ROPE, LAYOUT_INT3, LAYOUT_VERSION = 1, 2, 3, 4, 1
 LAYOUT_INT3_GATE_UP = 5
 GEMM_AUTO, GEMM_VALU, GEMM_MFMA = 0, 1, 2
-OP_GEMV, OP_GEMM, OP_FFN, OP_LMHEAD, OP_ATTENTION, OP_ATTENTION_OPROJ = 1, 2, 3, 4, 5, 6
+OP_GEMV, OP_GEMM, OP_FFN, OP_LMHEAD, OP_ATTENTION = 1, 2, 3, 4, 5
 
 
 class q4_weight(ctypes.Structure):
@@ -61,8 +61,6 @@ _SIGNATURES = {
     "q4_pack_int3": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _I64, _W, _P]),
     "q4_pack_int3_gate_up": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _P, _I64, _W, _P]),
     "q4_kv_int8_page_bytes": (ctypes.c_int64, [_I32, _I32]),
-    "q4_attention_oproj": (ctypes.c_int, [_P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32,
-                                          ctypes.c_float, _W, _P, _P, _I64, _P]),
     "q4_kv_append_int8": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _I32, _P]),
     "q4_attention_decode_int8": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                                 ctypes.c_float, _P, _P, _I64, _P]),
@@ -456,45 +454,6 @@ def attention_decode_int8(q: torch.Tensor, cache8: torch.Tensor, page_table: tor
                                          n_q_heads, n_kv_heads, head_dim, float(scale), po, pws,
                                          need if need > 0 else 0, _stream(q)),
            "q4_attention_decode_int8")
-    return out
-
-
-def attention_oproj(q: torch.Tensor, kv_cache: torch.Tensor, page_table: torch.Tensor, ctx: int,
-                    n_q_heads: int, scale: float, w_o: PackedWeight, out: Optional[torch.Tensor] = None,
-                    ws: Optional[torch.Tensor] = None, kv_int8: bool = False,
-                    n_kv_heads: Optional[int] = None, head_dim: Optional[int] = None) -> torch.Tensor:
-    """y f16 [w_o.n] = W_o . attention(q, cache), the chunk merge inside the
-    projection (q4_attention_oproj).  The f16 cache gives n_kv_heads and
-    head_dim by its shape; the int8 cache (kv_int8=True, uint8 [pages][page
-    bytes]) needs them passed."""
-    if kv_int8:
-        nkv, d = n_kv_heads, head_dim
-        if nkv is None or d is None:
-            raise ValueError("the int8 cache needs n_kv_heads and head_dim")
-        pb = kv_int8_page_bytes(nkv, d)
-        if kv_cache.dim() != 2 or kv_cache.shape[1] != pb:
-            raise ValueError(f"cache must be [pages][{pb}] bytes")
-        pages = kv_cache.shape[0]
-        pc = _dev(kv_cache, "kv_cache", 1)
-    else:
-        if kv_cache.dim() != 5 or kv_cache.element_size() != 2 or not kv_cache.is_contiguous():
-            raise ValueError("kv_cache must be a contiguous 16-bit [pages][2][n_kv][16][d] tensor")
-        pages, _, nkv, _, d = kv_cache.shape
-        pc = kv_cache.data_ptr()
-    pq = _dev(q, "q", 2)
-    if q.numel() != n_q_heads * d:
-        raise ValueError(f"q has {q.numel()} elements, expected {n_q_heads * d}")
-    pt = _dev(page_table, "page_table", 4)
-    if out is None:
-        out = torch.empty(w_o.n, dtype=torch.float16, device=q.device)
-    py = _dev(out, "out", 2, (w_o.n,))
-    need = int(_lib.q4_workspace_bytes(OP_ATTENTION_OPROJ, ctx, n_q_heads, d))
-    if ws is None:
-        ws = workspace(q.device, need)
-    _check(_lib.q4_attention_oproj(pq, pc, 1 if kv_int8 else 0, pt, pages, ctx, n_q_heads, nkv, d,
-                                   float(scale), ctypes.byref(w_o.desc), py, ws.data_ptr(),
-                                   ws.numel() * ws.element_size(), _stream(q)),
-           "q4_attention_oproj")
     return out
 
 

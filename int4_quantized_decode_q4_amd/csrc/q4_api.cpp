@@ -42,14 +42,6 @@ int hip_status(hipError_t e)
     return Q4_ERR_HIP;
 }
 
-// q4_attention_oproj's workspace: the chunk records, then room for the f16
-// attention output (used only when the O-projection cannot merge itself)
-int64_t oproj_workspace_bytes(int64_t ctx, int64_t nq, int64_t d)
-{
-    const int64_t rec = (q4::attention_records_bytes(ctx, nq, d) + 255) / 256 * 256;
-    return rec + (2 * nq * d + 255) / 256 * 256;
-}
-
 // int3 weights hold one pass (k <= 8192, the longest k of the decode shapes)
 constexpr int32_t kInt3MaxK = 8192;
 
@@ -150,8 +142,6 @@ int64_t q4_workspace_bytes(int32_t op, int32_t m, int32_t n, int32_t k)
 {
     if (m < 1 || !valid_shape(n, k))
         return 0;
-    if (op == Q4_OP_ATTENTION_OPROJ)   // m = ctx, n = query heads, k = head dim
-        return (k % 32 == 0 && k <= 256) ? oproj_workspace_bytes(m, n, k) : 0;
     if (op == Q4_OP_ATTENTION)   // m = ctx, n = query heads, k = head dim
         return (k % 32 == 0 && k <= 256) ? q4::attention_workspace_bytes(m, n, k) : 0;
     if (op == Q4_OP_LMHEAD) {
@@ -641,63 +631,6 @@ int q4_attention_decode_int8(const uint16_t *q, const void *cache8, const int32_
                                                 n_pages, ctx, nq, nkv, d, scale, out,
                                                 need > 0 ? ws : nullptr,
                                                 static_cast<hipStream_t>(stream)));
-}
-
-int q4_attention_oproj(const uint16_t *q, const void *kv_cache, int32_t kv_int8,
-                       const int32_t *page_table, int32_t n_pages, int32_t ctx, int32_t nq,
-                       int32_t nkv, int32_t d, float scale, const q4_weight *w_o, uint16_t *y,
-                       void *ws, int64_t ws_bytes, void *stream)
-{
-    if (!q || !kv_cache || !page_table || !w_o || !y || !ws)
-        return Q4_ERR_NULL;
-    if (kv_int8 != 0 && kv_int8 != 1)
-        return Q4_ERR_SHAPE;
-    const int64_t pb = kv_int8 ? q4_kv_int8_page_bytes(nkv, d)
-                               : ((nkv >= 1 && d >= 32 && d <= 256 && d % 32 == 0)
-                                      ? (int64_t)nkv * 16 * d * 2 * 2 : 0);
-    if (pb == 0 || pb > INT32_MAX || ctx < 1 || n_pages < 1 || nq < 1 || nq % nkv != 0 ||
-        !std::isfinite(scale))
-        return Q4_ERR_SHAPE;
-    q4::Geometry geo;
-    int64_t rows = 0;
-    const int rc = check_weight(w_o, Q4_LAYOUT_ROWS, &geo, &rows);
-    if (rc != Q4_OK)
-        return rc;
-    if ((int64_t)w_o->k != (int64_t)nq * d)
-        return Q4_ERR_SHAPE;
-    if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(page_table, 4) || !aligned(y, 4) ||
-        !aligned(ws, 256))
-        return Q4_ERR_ALIGN;
-    const int64_t need = oproj_workspace_bytes(ctx, nq, d);
-    if (ws_bytes < need)
-        return Q4_ERR_WORKSPACE;
-    const int64_t qb = 2 * (int64_t)nq * d, cb = (int64_t)n_pages * pb, yb = 2 * (int64_t)w_o->n;
-    const int64_t tb = 4 * (((int64_t)ctx + 15) / 16);
-    if (overlap(y, yb, q, qb) || overlap(y, yb, kv_cache, cb) || overlap(y, yb, page_table, tb) ||
-        overlap(y, yb, w_o->data, w_o->bytes) || overlap(y, yb, ws, need))
-        return Q4_ERR_ALIAS;
-    if (overlap(ws, need, q, qb) || overlap(ws, need, kv_cache, cb) ||
-        overlap(ws, need, page_table, tb) || overlap(ws, need, w_o->data, w_o->bytes))
-        return Q4_ERR_ALIAS;
-    (void)hipGetLastError();
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    float *rec = static_cast<float *>(ws);
-    int r2 = hip_status(q4::launch_attention_records(q, static_cast<const uint8_t *>(kv_cache),
-                                                     kv_int8 != 0, page_table, n_pages, ctx, nq, nkv,
-                                                     d, scale, rec, s));
-    if (r2 != Q4_OK)
-        return r2;
-    const q4::MergeArgs mg{rec, q4::attention_records_chunks(ctx, nq), d};
-    if (q4::gemv_merge_supported(geo))
-        return hip_status(q4::launch_gemv_merge(geo, w_o->data, mg, y, rows, w_o->k, s));
-    // shapes the merging kernel does not take: merge into the workspace, then the plain GEMV
-    uint16_t *att = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) +
-                                                 (q4::attention_records_bytes(ctx, nq, d) + 255) / 256 * 256);
-    r2 = hip_status(q4::launch_attention_combine(rec, mg.chunks, nq, d, att, s));
-    if (r2 != Q4_OK)
-        return r2;
-    return hip_status(q4::launch_gemv_family(geo, q4::EPI_F16, w_o->data, att, y, rows, w_o->k, w_o->n,
-                                             q4::ArgmaxScratch{nullptr, nullptr}, nullptr, nullptr, s));
 }
 
 const char *q4_strerror(int code)

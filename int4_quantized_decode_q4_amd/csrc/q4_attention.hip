@@ -53,7 +53,6 @@
 
 #include "q4_internal.h"
 #include "q4_lanes.h"
-#include "q4_merge.h"
 
 namespace q4 {
 
@@ -148,6 +147,9 @@ __device__ __forceinline__ void axpy8(float p, uint4 v, float *acc)
         acc[2 * i + 1] = fmaf(p, (float)h.y, acc[2 * i + 1]);
     }
 }
+
+// 2^x in f32 (v_exp_f32; 2^-inf = 0).
+__device__ __forceinline__ float exp2_f32(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Merge two online-softmax states (max m, sum l, accumulator acc; scores in
 // base-2 units): the result is the state of the union of their positions.
@@ -423,11 +425,18 @@ __global__ __launch_bounds__(64) void attention_combine_kernel(const float *__re
             ac[u] = r[2 + i];
         }
 #pragma unroll
-        for (int u = 0; u < kCombineBatch; ++u)
-            if (c0 + u < chunks)
-                merge_record(m, l, a, mc[u], lc[u], ac[u]);
+        for (int u = 0; u < kCombineBatch; ++u) {
+            if (c0 + u < chunks) {
+                const float mn = fmaxf(m, mc[u]);
+                const float e1 = m == -INFINITY ? 0.f : exp2_f32(m - mn);
+                const float e2 = mc[u] == -INFINITY ? 0.f : exp2_f32(mc[u] - mn);
+                l = l * e1 + lc[u] * e2;
+                a = a * e1 + ac[u] * e2;
+                m = mn;
+            }
+        }
     }
-    out[(int64_t)h * d + i] = merged_f16(l, a);
+    out[(int64_t)h * d + i] = __builtin_bit_cast(uint16_t, (_Float16)(a / l));
 }
 
 // Positions per block: the longest chunk (kMinChunk times a power of two, at
@@ -505,63 +514,6 @@ hipError_t launch_attention_int8(const uint16_t *q, const uint8_t *cache8, const
 }
 
 int64_t kv_int8_page_bytes(int64_t nkv, int64_t d) { return 2 * nkv * kv8_block_bytes(d); }
-
-// The fused attention + O-projection: the decode kernel always writes chunk
-// records (even for a single chunk); the matmul merges them.
-int32_t attention_records_chunks(int64_t ctx, int64_t nq)
-{
-    const int64_t cl = chunk_len(ctx, nq);
-    return (int32_t)((ctx + cl - 1) / cl);
-}
-
-int64_t attention_records_bytes(int64_t ctx, int64_t nq, int64_t d)
-{
-    return nq * attention_records_chunks(ctx, nq) * (d + 2) * 4;
-}
-
-template <bool I8>
-static hipError_t launch_records(const uint16_t *q, const uint8_t *cache, const int32_t *pt,
-                                 int32_t n_pages, int32_t ctx, int32_t nq, int32_t nkv, int32_t d,
-                                 float scale, float *records, hipStream_t stream)
-{
-    const int cl = (int)chunk_len(ctx, nq);
-    const int chunks = (ctx + cl - 1) / cl;
-    const dim3 grid((unsigned)(nq * chunks)), block(64 * kWaves);
-    switch (d / 32) {
-#define Q4_REC_CASE(DL)                                                                             \
-    case DL:                                                                                        \
-        hipLaunchKernelGGL((attention_decode_kernel<DL, I8>), grid, block, 0, stream, q, cache, pt, \
-                           n_pages, ctx, nq, nkv, cl, scale, nullptr, records);                     \
-        return hipGetLastError();
-        Q4_REC_CASE(1)
-        Q4_REC_CASE(2)
-        Q4_REC_CASE(3)
-        Q4_REC_CASE(4)
-        Q4_REC_CASE(5)
-        Q4_REC_CASE(6)
-        Q4_REC_CASE(7)
-        Q4_REC_CASE(8)
-#undef Q4_REC_CASE
-    }
-    return hipErrorInvalidValue;
-}
-
-hipError_t launch_attention_records(const uint16_t *q, const uint8_t *cache, bool int8,
-                                    const int32_t *page_table, int32_t n_pages, int32_t ctx,
-                                    int32_t nq, int32_t nkv, int32_t d, float scale, float *records,
-                                    hipStream_t stream)
-{
-    return int8 ? launch_records<true>(q, cache, page_table, n_pages, ctx, nq, nkv, d, scale, records, stream)
-                : launch_records<false>(q, cache, page_table, n_pages, ctx, nq, nkv, d, scale, records, stream);
-}
-
-hipError_t launch_attention_combine(const float *records, int32_t chunks, int32_t nq, int32_t d,
-                                    uint16_t *out, hipStream_t stream)
-{
-    hipLaunchKernelGGL(attention_combine_kernel, dim3((unsigned)nq, (unsigned)((d / 32 + 1) / 2)), dim3(64),
-                       0, stream, records, chunks, d, out);
-    return hipGetLastError();
-}
 
 hipError_t launch_kv_append_int8(const uint16_t *qkv, int32_t nq, int32_t nkv, int32_t d, int32_t pos,
                                  uint8_t *cache8, const int32_t *page_table, int32_t n_pages,

@@ -81,15 +81,6 @@ struct NormArgs {
     float eps;
 };
 
-// x of a matmul taken as the merged paged-attention output: the chunk
-// records [head][chunk][d + 2] f32 of q4_attention.hip, heads of d dims
-// (k = heads * d).
-struct MergeArgs {
-    const float *rec;
-    int32_t chunks;
-    int32_t d;
-};
-
 hipError_t launch_gemv_family(const Geometry &geo, Epilogue epi, const void *wdata,
                               const uint16_t *x, void *out, int64_t rows, int64_t k,
                               int64_t n_out, ArgmaxScratch am, const NormArgs *norm,
@@ -108,10 +99,7 @@ hipError_t launch_gemv3(const Geometry &geo, Epilogue epi, const void *wdata, co
                         hipStream_t stream);
 
 // Paged-attention decode (q4_attention.hip): workspace bytes (0 when the
-// context fits one chunk) and the launch.  The fused form writes the chunk
-// records for every context (attention_records_bytes, records_chunks) and
-// leaves the merge to the matmul that consumes the output (launch_gemv_merge
-// in q4_kernels.hip).
+// context fits one chunk) and the launch.
 int64_t attention_workspace_bytes(int64_t ctx, int64_t nq, int64_t d);
 hipError_t launch_attention(const uint16_t *q, const uint16_t *cache, const int32_t *page_table,
                             int32_t n_pages, int32_t ctx, int32_t nq, int32_t nkv, int32_t d,
@@ -122,20 +110,6 @@ int64_t kv_int8_page_bytes(int64_t nkv, int64_t d);
 hipError_t launch_attention_int8(const uint16_t *q, const uint8_t *cache8, const int32_t *page_table,
                                  int32_t n_pages, int32_t ctx, int32_t nq, int32_t nkv, int32_t d,
                                  float scale, uint16_t *out, void *ws, hipStream_t stream);
-int64_t attention_records_bytes(int64_t ctx, int64_t nq, int64_t d);
-int32_t attention_records_chunks(int64_t ctx, int64_t nq);
-hipError_t launch_attention_records(const uint16_t *q, const uint8_t *cache, bool int8,
-                                    const int32_t *page_table, int32_t n_pages, int32_t ctx,
-                                    int32_t nq, int32_t nkv, int32_t d, float scale, float *records,
-                                    hipStream_t stream);
-// y = f16 GEMV (int4 rows) of x = the merged attention records; false when
-// the shape would not run the single-pass block kernel (the caller then
-// merges with the combine kernel and runs the plain GEMV).
-bool gemv_merge_supported(const Geometry &geo);
-hipError_t launch_gemv_merge(const Geometry &geo, const void *wdata, const MergeArgs &mg,
-                             uint16_t *y, int64_t rows, int64_t k, hipStream_t stream);
-hipError_t launch_attention_combine(const float *records, int32_t chunks, int32_t nq, int32_t d,
-                                    uint16_t *out, hipStream_t stream);
 hipError_t launch_kv_append_int8(const uint16_t *qkv, int32_t nq, int32_t nkv, int32_t d, int32_t pos,
                                  uint8_t *cache8, const int32_t *page_table, int32_t n_pages,
                                  hipStream_t stream);

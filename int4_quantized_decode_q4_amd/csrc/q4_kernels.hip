@@ -38,7 +38,6 @@
 #include "q4_geometry.h"
 #include "q4_internal.h"
 #include "q4_lanes.h"
-#include "q4_merge.h"
 
 namespace q4 {
 
@@ -888,11 +887,11 @@ __device__ __forceinline__ void lds_x_group(uint32_t *xp, const uint4 *xs, int64
     }
 }
 
-template <int L, int CG, int EPI, bool NORM, int FMT = 4, bool MERGE = false>
+template <int L, int CG, int EPI, bool NORM, int FMT = 4>
 __global__ __launch_bounds__(64 * kBlockWaves) void gemv_block_kernel(
     const uint8_t *__restrict__ wd, const uint16_t *__restrict__ x, void *__restrict__ out,
     int64_t rows, int64_t k, int64_t tiles, int64_t n_out, ArgmaxScratch am, NormArgs nm,
-    typename RopeParam<EPI>::type rp, MergeArgs mg)
+    typename RopeParam<EPI>::type rp)
 {
     constexpr int PD = Q4_STREAM_DEPTH < 2 * CG ? Q4_STREAM_DEPTH : 2 * CG;
     constexpr int64_t PB = (int64_t)CG * (2 * Fmt<FMT>::UB + 256);
@@ -918,7 +917,7 @@ __global__ __launch_bounds__(64 * kBlockWaves) void gemv_block_kernel(
     v4u xv[kXRounds];
 #pragma unroll
     for (int q = 0; q < kXRounds; ++q)
-        if (!MERGE && q < xrounds)
+        if (q < xrounds)
             xv[q] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (threadIdx.x + kThreads * q) * 16, 0, 0);
     // with the norm: the residual (a zero-size resource when there is none)
     // and gamma, requested with x
@@ -947,53 +946,11 @@ __global__ __launch_bounds__(64 * kBlockWaves) void gemv_block_kernel(
         for (int i = 0; i < PD; ++i)
             load_unit<CG, FMT>(ra, r0, lane, i);
     }
-    // with the merge: x is the paged-attention output, formed here from the
-    // chunk records (8 consecutive elements -- dims of one head -- per thread
-    // and round) with the combine kernel's arithmetic, so the bits are those
-    // of the separate combine launch; the first weight units are in flight
-    // meanwhile
-    if constexpr (MERGE) {
-#pragma unroll
-        for (int q = 0; q < kXRounds; ++q) {
-            const int64_t e0 = (int64_t)(threadIdx.x + kThreads * q) * 8;
-            if (q >= xrounds || e0 >= k)
-                continue;
-            const int64_t h = e0 / mg.d, i0 = e0 % mg.d;
-            const float *rec = mg.rec + h * mg.chunks * (int64_t)(mg.d + 2);
-            float mm[8], ll[8], aa[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                mm[e] = -INFINITY;
-                ll[e] = 0.f;
-                aa[e] = 0.f;
-            }
-            for (int cc = 0; cc < mg.chunks; ++cc) {
-                const float *r = rec + cc * (int64_t)(mg.d + 2);
-                const float mc = r[0], lc = r[1];
-                const float2 *ap = reinterpret_cast<const float2 *>(r + 2 + i0);   // 8-byte aligned
-                float ac[8];
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    const float2 v = ap[e2];
-                    ac[2 * e2] = v.x;
-                    ac[2 * e2 + 1] = v.y;
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    merge_record(mm[e], ll[e], aa[e], mc, lc, ac[e]);
-            }
-            uint32_t pk[4];
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2)
-                pk[e2] = (uint32_t)merged_f16(ll[2 * e2], aa[2 * e2]) |
-                         ((uint32_t)merged_f16(ll[2 * e2 + 1], aa[2 * e2 + 1]) << 16);
-            xs[threadIdx.x + kThreads * q] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-        }
-    } else if constexpr (NORM) {
     // with the norm: each thread keeps its chunks of h in registers and
     // parks its wavefront's part of the sum of squares in LDS; after one
     // barrier every thread has the block's sum, normalises its own chunks
     // into LDS, and the staging barrier below publishes them
+    if constexpr (NORM) {
         __shared__ float nss[kBlockWaves];
         uint4 hv[kXRounds];
         float ss = 0.f;
@@ -1332,7 +1289,7 @@ static void launch_gemv3_lce(const GemvPlan &plan, const Geometry &geo, const ui
                            out, rows, k, geo.tiles, n_out, am, nm, NoRope{});
     else
         hipLaunchKernelGGL((gemv_block_kernel<L, CG, EPI, false, 3>), grid, block, 0, stream, wd, x,
-                           out, rows, k, geo.tiles, n_out, am, nm, NoRope{}, MergeArgs{});
+                           out, rows, k, geo.tiles, n_out, am, nm, NoRope{});
 }
 
 template <int L, int CG>
@@ -1392,55 +1349,6 @@ hipError_t launch_gemv3(const Geometry &geo, Epilogue epi, const void *wdata, co
     return hipGetLastError();
 }
 
-// The O-projection GEMV over the merged attention output (int4 rows, f16 out,
-// block kernel only).
-bool gemv_merge_supported(const Geometry &geo) { return plan_gemv(geo).mode == MODE_BLOCK; }
-
-template <int L, int CG>
-static void launch_merge_lc(const GemvPlan &plan, const Geometry &geo, const uint8_t *wd,
-                            const MergeArgs &mg, uint16_t *y, int64_t rows, int64_t k,
-                            hipStream_t stream)
-{
-    hipLaunchKernelGGL((gemv_block_kernel<L, CG, EPI_F16, false, 4, true>), dim3((unsigned)plan.blocks),
-                       dim3((unsigned)plan.threads), 0, stream, wd, nullptr, static_cast<void *>(y), rows,
-                       k, geo.tiles, rows, ArgmaxScratch{nullptr, nullptr},
-                       NormArgs{nullptr, nullptr, nullptr, 0.f}, NoRope{}, mg);
-}
-
-template <int L>
-static bool launch_merge_l(const GemvPlan &plan, const Geometry &geo, const uint8_t *wd,
-                           const MergeArgs &mg, uint16_t *y, int64_t rows, int64_t k,
-                           hipStream_t stream)
-{
-    switch (geo.CG) {
-    case 1: launch_merge_lc<L, 1>(plan, geo, wd, mg, y, rows, k, stream); return true;
-    case 2: launch_merge_lc<L, 2>(plan, geo, wd, mg, y, rows, k, stream); return true;
-    case 3: launch_merge_lc<L, 3>(plan, geo, wd, mg, y, rows, k, stream); return true;
-    case 4: launch_merge_lc<L, 4>(plan, geo, wd, mg, y, rows, k, stream); return true;
-    }
-    return false;
-}
-
-hipError_t launch_gemv_merge(const Geometry &geo, const void *wdata, const MergeArgs &mg,
-                             uint16_t *y, int64_t rows, int64_t k, hipStream_t stream)
-{
-    const GemvPlan plan = plan_gemv(geo);
-    if (plan.mode != MODE_BLOCK || k > kBlockXHalves || mg.d < 8 || mg.d % 8 != 0 || k % mg.d != 0)
-        return hipErrorInvalidValue;
-    const uint8_t *wd = static_cast<const uint8_t *>(wdata);
-    bool ok = false;
-    switch (geo.L) {
-    case 64: ok = launch_merge_l<64>(plan, geo, wd, mg, y, rows, k, stream); break;
-    case 32: ok = launch_merge_l<32>(plan, geo, wd, mg, y, rows, k, stream); break;
-    case 16: ok = launch_merge_l<16>(plan, geo, wd, mg, y, rows, k, stream); break;
-    case 8: ok = launch_merge_l<8>(plan, geo, wd, mg, y, rows, k, stream); break;
-    case 4: ok = launch_merge_l<4>(plan, geo, wd, mg, y, rows, k, stream); break;
-    case 2: ok = launch_merge_l<2>(plan, geo, wd, mg, y, rows, k, stream); break;
-    case 1: ok = launch_merge_l<1>(plan, geo, wd, mg, y, rows, k, stream); break;
-    }
-    return ok ? hipGetLastError() : hipErrorInvalidValue;
-}
-
 struct GemvArgs {
     const uint8_t *wd;
     const uint16_t *x;
@@ -1476,8 +1384,7 @@ static void launch_lcen(const GemvPlan &plan, const GemvArgs &a, hipStream_t str
         break;
     case MODE_BLOCK:
         hipLaunchKernelGGL((gemv_block_kernel<L, CG, EPI, NORM>), grid, block, 0, stream, a.wd, a.x,
-                           a.out, a.rows, a.k, a.geo->tiles, a.n_out, a.am, a.nm, rope_param<EPI>(a),
-                           MergeArgs{});
+                           a.out, a.rows, a.k, a.geo->tiles, a.n_out, a.am, a.nm, rope_param<EPI>(a));
         break;
     }
 }

@@ -329,35 +329,6 @@ def test_kv_int8_errors(q4, orc):
     assert call(ws=O) == q4.ERR_ALIAS
 
 
-def test_attention_oproj_errors(q4):
-    lib = q4.lib
-    f = lib.q4_attention_oproj
-    Q, C, T, Y, Wk = A + 0x200000, A + 0x1000000, A + 0x300000, A + 0x400000, A + 0x500000
-    need = lib.q4_workspace_bytes(q4.OP_ATTENTION_OPROJ, 4096, 32, 96)
-    assert need >= lib.q4_workspace_bytes(q4.OP_ATTENTION, 4096, 32, 96) + 2 * 32 * 96
-    assert lib.q4_workspace_bytes(q4.OP_ATTENTION_OPROJ, 1, 32, 96) >= 32 * 98 * 4   # records even for one chunk
-    wo = weight(q4, n=3072, k=3072)
-    r = ctypes.byref(wo)
-    ok = (Q, C, 0, T, 300, 4096, 32, 32, 96, 0.1, r, Y, Wk, need, None)
-    names = ("q", "c", "i8", "t", "pages", "ctx", "nq", "nkv", "d", "scale", "w", "y", "ws", "wsb", "s")
-    def call(**kw):
-        args = dict(zip(names, ok))
-        args.update(kw)
-        return f(*[args[n] for n in names])
-    assert call(ws=None) == q4.ERR_NULL
-    assert call(w=None) == q4.ERR_NULL
-    assert call(i8=2) == q4.ERR_SHAPE
-    assert call(d=80) == q4.ERR_SHAPE
-    assert call(ctx=0) == q4.ERR_SHAPE
-    assert call(w=ctypes.byref(weight(q4, n=3072, k=3104))) == q4.ERR_SHAPE      # k != nq * d
-    assert call(w=ctypes.byref(weight(q4, n=3072, k=3072, layout=2))) == q4.ERR_LAYOUT
-    assert call(ws=Wk + 16) == q4.ERR_ALIGN
-    assert call(c=C + 8) == q4.ERR_ALIGN
-    assert call(wsb=need - 1) == q4.ERR_WORKSPACE
-    assert call(y=Q + 64) == q4.ERR_ALIAS
-    assert call(ws=C) == q4.ERR_ALIAS
-
-
 def test_lmhead_errors(q4):
     lib = q4.lib
     X, L, I, WS = A + 0x200000, A + 0x300000, A + 0x400000, A + 0x500000

@@ -103,6 +103,19 @@ def test_attention_many_chunks(q4, orc):
         assert_within(host_f16_as_f64(out), ref, tol_attn(ref, a), f"attention {nq}x{d} ctx={ctx}")
 
 
+def test_attention_long_context_many_chunks(q4, orc):
+    """70,000 positions over 2 query heads on one kv head: 137 chunks per
+    head, so the combine kernel merges its records in several batches of 16
+    (the last one partial)."""
+    rng = np.random.default_rng(70000)
+    nq, nkv, d, ctx = 2, 1, 128, 70000
+    assert q4.lib.q4_workspace_bytes(q4.OP_ATTENTION, ctx, nq, d) > nq * 32 * (d + 2) * 4
+    cache, table, q = make(rng, ctx, nq, nkv, d)
+    out = run(q4, cache, table, q, ctx, nq, 0.08)
+    ref, a = orc.attention_decode(q, cache, table, ctx, nq, nkv, d, 0.08)
+    assert_within(host_f16_as_f64(out), ref, tol_attn(ref, a), "attention ctx 70000")
+
+
 def test_decode_steps_then_attention(q4, orc):
     """The decode pipeline: 40 fused QKV steps fill the cache through a page
     table; attention of the last step's q over the 40 positions matches the

@@ -63,6 +63,17 @@ def test_attention_int8_parity(q4, orc, nq, nkv, d, ctx):
     print(f"max err/tol {r:.3g}")
 
 
+def test_attention_int8_long_context(q4, orc):
+    """70,000 positions, 2 query heads: many chunks through the combine kernel."""
+    rng = np.random.default_rng(70001)
+    nq, nkv, d, ctx = 2, 1, 128, 70000
+    cache, table = make_cache8(rng, ctx, nkv, d)
+    q = si.f16_bits(rng.normal(0.0, 1.0, (nq, d)))
+    out = run8(q4, cache, table, q, ctx, nq, nkv, d, 0.08)
+    ref, a = orc.attention_decode_int8(q, cache, table, ctx, nq, nkv, d, 0.08)
+    assert_within(host_f16_as_f64(out), ref, tol_attn(ref, a), "int8 attention ctx 70000")
+
+
 def test_kv_append_int8_bit_exact(q4, orc):
     rng = np.random.default_rng(61)
     nq, nkv, d = 32, 32, 96

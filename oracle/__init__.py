@@ -72,6 +72,8 @@ class Oracle:
         lib.q4o_gemv3.argtypes = [_P, _P, _P, _I64, _I64, _P, _P]
         lib.q4o_gemv3.restype = ctypes.c_int
         lib.q4o_encode3.argtypes = [_P, _P, _I64, _I64, _P]
+        lib.q4o_gemm3.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P, _P]
+        lib.q4o_gemm3.restype = ctypes.c_int
         lib.q4o_encode3_gate_up.argtypes = [_P, _P, _P, _P, _I64, _I64, _P]
         lib.q4o_encode3_gate_up.restype = ctypes.c_int
         lib.q4o_ffn_gate_up_silu3.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P]
@@ -205,6 +207,19 @@ class Oracle:
                                                 ctx, nq, nkv, d, float(scale), _ptr(out), _ptr(a))
         assert rc == 0
         return out, a
+
+    def gemm3(self, words3, scales, X):
+        """(Y, A) f64 [m][n] for an int3 weight and activation rows X [m][k]."""
+        m, k = X.shape
+        n = words3.shape[0]
+        self._check_w3(words3, scales, n, k)
+        words3, scales = np.ascontiguousarray(words3), np.ascontiguousarray(scales)
+        X = np.ascontiguousarray(X, dtype=np.uint16)
+        Y = np.empty((m, n), np.float64)
+        A = np.empty((m, n), np.float64)
+        rc = self.lib.q4o_gemm3(_ptr(words3), _ptr(scales), _ptr(X), m, n, k, _ptr(Y), _ptr(A))
+        assert rc == 0
+        return Y, A
 
     def ffn_gate_up_silu3(self, gw3, gs, uw3, us, x):
         """int3 FFN: dict with h, g, u, ag, au (all f64 [n])."""

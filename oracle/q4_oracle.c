@@ -626,6 +626,21 @@ int q4o_gemv3(const uint32_t *words3, const uint16_t *scales, const uint16_t *x,
     return 0;
 }
 
+/* Y = X . dequant3(W)^T for m activation rows (the int3 form of q4o_gemm):
+ * X [m][k] f16 bits, Y, A [m][n] (A may be NULL). */
+int q4o_gemm3(const uint32_t *words3, const uint16_t *scales, const uint16_t *X, int64_t m,
+              int64_t n, int64_t k, double *Y, double *A)
+{
+    if (m < 1)
+        return -1;
+    for (int64_t r = 0; r < m; ++r) {
+        const int rc = q4o_gemv3(words3, scales, X + r * k, n, k, Y + r * n, A ? A + r * n : NULL);
+        if (rc)
+            return rc;
+    }
+    return 0;
+}
+
 /* The fused gate/up + SiLU FFN over int3 weights: q4o_ffn_gate_up_silu with
  * the int3 matmul (gate and up rows each a canonical int3 stream). */
 int q4o_ffn_gate_up_silu3(const uint32_t *gw3, const uint16_t *gs, const uint32_t *uw3,

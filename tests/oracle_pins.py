@@ -655,6 +655,18 @@ def pin_int3_layout(orc, quick=False):
     assert pc <= {4} and ps <= {0}
 
 
+def pin_int3_gemm(orc, quick=False):
+    """int3 GEMM: row r of Y is the int3 GEMV of row r of X, exactly."""
+    rng = np.random.default_rng(59)
+    m, n, k = 5, 7, 96
+    w3, s3 = si.draw_weight3(rng, n, k)
+    X = si.f16_bits(rng.normal(0, 1, (m, k)))
+    Y, A = orc.gemm3(w3, s3, X)
+    for r in range(m):
+        y, a = orc.gemv3(w3, s3, X[r])
+        assert np.array_equal(Y[r], y) and np.array_equal(A[r], a), r
+
+
 def pin_int3_ffn(orc, quick=False):
     """int3 FFN: the gate (not the up) is the gated half; constant codes give
     h = silu(cg * S) * cu * S in closed form."""
@@ -764,5 +776,5 @@ ALL_PINS = [
     pin_gemv_one_hot, pin_gemv_linearity, pin_gemm_rows,
     pin_silu, pin_ffn, pin_argmax, pin_lmhead, pin_add_rmsnorm, pin_rope, pin_attention,
     pin_layout_geometry, pin_layout_hand_example, pin_layout_roundtrip, pin_rope_layout,
-    pin_int3, pin_int3_layout, pin_int3_ffn, pin_kv_quant, pin_kv_append_int8, pin_attention_int8,
+    pin_int3, pin_int3_layout, pin_int3_gemm, pin_int3_ffn, pin_kv_quant, pin_kv_append_int8, pin_attention_int8,
 ]

@@ -71,6 +71,7 @@ MUTANTS = [
      "word |= (uint32_t)((codes[30] >> i) & 1) << 14;"),
     ("int3_pad_code_0", "codes[i] = real ? code3_at(rw, src, 32 * g + i, k) : 4;",
      "codes[i] = real ? code3_at(rw, src, 32 * g + i, k) : 0;"),
+    ("int3_gemm_row_stride", "X + r * k, n, k, Y + r * n", "X + r * 32, n, k, Y + r * n"),
     ("int3_gate_up_swapped", "const uint32_t *rw = w1 ? (r % 2 ? w1 : w0) : w0;",
      "const uint32_t *rw = w1 ? (r % 2 ? w0 : w1) : w0;"),
     ("int3_ffn_up_rows_as_gate", "q4o_gemv3(uw3 + r * (3 * k / 32), us + r * (k / 32), x, 1, k, &uv, &auv);",

@@ -77,7 +77,7 @@ extern "C" {
 #define Q4_LAYOUT_ROWS    1  /* plain rows: q4_gemv, q4_gemm, q4_lmhead_f32 */
 #define Q4_LAYOUT_GATE_UP 2  /* interleaved gate/up rows: q4_ffn_gate_up_silu */
 #define Q4_LAYOUT_ROPE    3  /* rotary-paired head rows: q4_qkv_rope_append */
-#define Q4_LAYOUT_INT3    4  /* int3 rows (q4_pack_int3): q4_gemv, q4_lmhead_f32 */
+#define Q4_LAYOUT_INT3    4  /* int3 rows (q4_pack_int3): q4_gemv, q4_gemm, q4_lmhead_f32 */
 #define Q4_LAYOUT_INT3_GATE_UP 5  /* int3 gate/up rows (q4_pack_int3_gate_up): q4_ffn_gate_up_silu */
 #define Q4_LAYOUT_VERSION 1
 
@@ -162,7 +162,7 @@ int q4_pack_rope(const uint32_t *words, const uint16_t *scales, int32_t n, int32
  *            12-byte lane units (word i of a group's unit: codes 10i + m at
  *            bits 3m and 10i + 5 + m at bits 16 + 3m, m = 0..4; bit i of
  *            codes 30 and 31 at bits 15 and 31); padding is code 4, scale 0.
- * The result feeds q4_gemv and q4_lmhead_f32 (and q4_unpack).  Errors as q4_pack.
+ * The result feeds q4_gemv, q4_gemm and q4_lmhead_f32 (and q4_unpack).  Errors as q4_pack.
  */
 int q4_pack_int3(const uint32_t *words3, const uint16_t *scales, int32_t n, int32_t k,
                  void *dst, int64_t dst_bytes, q4_weight *out, void *stream);
@@ -204,6 +204,7 @@ int q4_gemv(const q4_weight *w, const uint16_t *x, uint16_t *y, void *stream);
  * activation rows with exact dequant; m >= 16 dequantizes W to f16
  * (q - 8) * s in LDS (one rounding, relative error <= 2^-11) and contracts
  * with v_mfma_f32_16x16x32_f16, f32 accumulation.
+ *   w : Q4_LAYOUT_ROWS, or Q4_LAYOUT_INT3 ((q - 4) * s on the same paths)
  *   X : device f16 [m][k] row-major, 16-byte aligned
  *   Y : device f16 [m][n] row-major, 2-byte aligned
  *   ws: unused (pass NULL, 0)

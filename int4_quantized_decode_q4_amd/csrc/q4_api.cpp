@@ -309,7 +309,9 @@ int q4_gemm_path(const q4_weight *w, const uint16_t *X, int32_t m, uint16_t *Y, 
     int64_t rows = 0;
     if (!w || !X || !Y)
         return Q4_ERR_NULL;
-    int rc = check_weight(w, Q4_LAYOUT_ROWS, &geo, &rows);
+    // int4 or int3 rows
+    const bool int3 = w->layout == Q4_LAYOUT_INT3;
+    int rc = check_weight(w, int3 ? Q4_LAYOUT_INT3 : Q4_LAYOUT_ROWS, &geo, &rows);
     if (rc != Q4_OK)
         return rc;
     if (m < 1)
@@ -323,7 +325,7 @@ int q4_gemm_path(const q4_weight *w, const uint16_t *X, int32_t m, uint16_t *Y, 
         return Q4_ERR_ALIAS;
     (void)hipGetLastError();
     return hip_status(q4::launch_gemm(geo, w->data, X, m, w->n, w->k, Y, path,
-                                      static_cast<hipStream_t>(stream)));
+                                      static_cast<hipStream_t>(stream), int3));
 }
 
 int q4_gemm(const q4_weight *w, const uint16_t *X, int32_t m, uint16_t *Y, void *ws,

@@ -94,6 +94,112 @@ __device__ __forceinline__ void dequant_word(uint32_t w, const Masks &m, h2 &a0,
     a3 = as_h2((b & m.hi) | m.magic) - k16;
 }
 
+// ------------------------------------------------------------ int3 units --
+//
+// An int3 lane unit is 12 bytes (3 words) for one group of 32 codes: word i
+// holds codes 10i + m at bits 3m and 10i + 5 + m at bits 16 + 3m (m = 0..4),
+// bit i of codes 30 / 31 at bits 15 / 31.  Dequantised here to exact
+// (q - 4) f16 pairs P[5i + m] = (c(10i+m), c(10i+5+m)), P[15] = (c30, c31):
+// a code masked in place at bits 0, 3 or 6 of a half reads as 1024 + q,
+// 128 + q or 16 + q under the exponents 0x6400, 0x5800, 0x4C00 (f16 ulp 1,
+// 1/8, 1/64), and 1028, 132 or 20 is subtracted.
+struct Masks3 {
+    uint32_t m0, m3, m6, b1, b2, b4, e1024, e128, e16;
+};
+
+__device__ __forceinline__ Masks3 masks3()
+{
+    Masks3 k;
+    asm("v_mov_b32 %0, 0x00070007" : "=v"(k.m0));
+    asm("v_mov_b32 %0, 0x00380038" : "=v"(k.m3));
+    asm("v_mov_b32 %0, 0x01C001C0" : "=v"(k.m6));
+    asm("v_mov_b32 %0, 0x00010001" : "=v"(k.b1));
+    asm("v_mov_b32 %0, 0x00020002" : "=v"(k.b2));
+    asm("v_mov_b32 %0, 0x00040004" : "=v"(k.b4));
+    asm("v_mov_b32 %0, 0x64006400" : "=v"(k.e1024));
+    asm("v_mov_b32 %0, 0x58005800" : "=v"(k.e128));
+    asm("v_mov_b32 %0, 0x4C004C00" : "=v"(k.e16));
+    return k;
+}
+
+__device__ __forceinline__ void dequant_unit3(uint32_t w0, uint32_t w1, uint32_t w2, const Masks3 &k,
+                                              h2 (&P)[16])
+{
+    const h2 o1 = {(_Float16)1028.0f, (_Float16)1028.0f};
+    const h2 o8 = {(_Float16)132.0f, (_Float16)132.0f};
+    const h2 o64 = {(_Float16)20.0f, (_Float16)20.0f};
+    const uint32_t w[3] = {w0, w1, w2};
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const uint32_t v = w[i], t = v >> 9;
+        P[5 * i + 0] = as_h2((v & k.m0) | k.e1024) - o1;
+        P[5 * i + 1] = as_h2((v & k.m3) | k.e128) - o8;
+        P[5 * i + 2] = as_h2((v & k.m6) | k.e16) - o64;
+        P[5 * i + 3] = as_h2((t & k.m0) | k.e1024) - o1;
+        P[5 * i + 4] = as_h2((t & k.m3) | k.e128) - o8;
+    }
+    uint32_t e = ((w0 >> 15) & k.b1) | k.e1024;
+    e = ((w1 >> 14) & k.b2) | e;
+    e = ((w2 >> 13) & k.b4) | e;
+    P[15] = as_h2(e) - o1;
+}
+
+// the 32 values of a unit's pairs back in k order, 8 halves per uint4
+__device__ __forceinline__ void pairs3_to_k(const h2 (&P)[16], uint4 (&out)[4])
+{
+    auto half = [&](int kk) -> uint32_t {
+        const int pi = kk == 30 ? 15 : kk == 31 ? 15 : 5 * (kk / 10) + (kk % 10) % 5;
+        const int hi = kk == 30 ? 0 : kk == 31 ? 1 : (kk % 10) >= 5;
+        return (as_u32(P[pi]) >> (16 * hi)) & 0xFFFFu;
+    };
+    uint32_t d[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+        d[q] = half(2 * q) | (half(2 * q + 1) << 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        out[q] = make_uint4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);
+}
+
+// x of one group (32 halves in k order, 4 uint4) -> the pairs matching P
+__device__ __forceinline__ void pair3_x(const uint4 (&n)[4], uint4 (&xp)[4])
+{
+    const uint32_t nn[16] = {n[0].x, n[0].y, n[0].z, n[0].w, n[1].x, n[1].y, n[1].z, n[1].w,
+                             n[2].x, n[2].y, n[2].z, n[2].w, n[3].x, n[3].y, n[3].z, n[3].w};
+    auto half = [&](int kk) -> uint32_t { return (nn[kk >> 1] >> ((kk & 1) * 16)) & 0xFFFFu; };
+    uint32_t d[16];
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int mm = 0; mm < 5; ++mm)
+            d[5 * i + mm] = half(10 * i + mm) | (half(10 * i + 5 + mm) << 16);
+    d[15] = nn[15];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        xp[q] = make_uint4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);
+}
+
+// Per-format sizes: lane unit bytes US and unit slot bytes UB (64 lanes).
+template <int FMT>
+struct GFmt {
+    static constexpr int US = FMT == 4 ? 16 : 12;
+    static constexpr int UB = 64 * US;
+    static constexpr int PASS = 2 * UB + 256;   // bytes per group slot per pass (x CG)
+};
+
+typedef unsigned v3u __attribute__((ext_vector_type(3)));
+
+template <int FMT>
+__device__ __forceinline__ v4u load_unit_g(__amdgpu_buffer_rsrc_t rs, int off)
+{
+    if constexpr (FMT == 4) {
+        return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    } else {
+        const v3u v = __builtin_amdgcn_raw_buffer_load_b96(rs, off, 0, 0);
+        return v4u{v.x, v.y, v.z, 0u};
+    }
+}
+
 // natural x pairs of one word (x0,x1)(x2,x3)(x4,x5)(x6,x7) -> (x0,x4)(x1,x5)(x2,x6)(x3,x7)
 __device__ __forceinline__ uint4 pair_word(uint4 n)
 {
@@ -125,34 +231,46 @@ constexpr int kValuRows = 8;   // activation rows per pass over W
 #define Q4_VALU_BLOCKS_PER_CU 2
 #endif
 
-template <int L, int CG, int MC, int PT>
+template <int L, int CG, int MC, int PT, int FMT = 4>
 __global__ __launch_bounds__(64 * CG) void gemm_valu_stream_kernel(
     const uint8_t *__restrict__ wd, const uint16_t *__restrict__ X, uint16_t *__restrict__ Y,
     int64_t m0, int64_t n, int64_t k, int64_t tiles)
 {
     constexpr int TR = 128 / L;
     constexpr int HP = 64 / L;   // row pairs per tile
-    constexpr int PB = CG * 2304;
+    constexpr int PB = CG * GFmt<FMT>::PASS;
+    constexpr int UB = GFmt<FMT>::UB, US = GFmt<FMT>::US;
     __shared__ float part[2][CG][HP][MC][2];
     const int lane = threadIdx.x & 63;
     const int j = threadIdx.x >> 6;
     const int s = lane / L, c = lane % L;
     const int64_t G = k >> 5;
     const int64_t g = (int64_t)c * CG + j;
-    const Masks mk = masks();
+    const Masks mk = FMT == 4 ? masks() : Masks{};
+    const Masks3 mk3 = FMT == 3 ? masks3() : Masks3{};
 
+    // x pairs of this lane's group for every row: int4 per word (pair_word),
+    // int3 for the whole unit (pair3_x)
     uint4 xq[MC][4];
 #pragma unroll
     for (int r = 0; r < MC; ++r) {
         const uint4 *src = reinterpret_cast<const uint4 *>(X + (m0 + r) * k + g * 32);
+        if constexpr (FMT == 4) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            xq[r][q] = g < G ? pair_word(src[q]) : make_uint4(0, 0, 0, 0);
+            for (int q = 0; q < 4; ++q)
+                xq[r][q] = g < G ? pair_word(src[q]) : make_uint4(0, 0, 0, 0);
+        } else {
+            uint4 nat[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                nat[q] = g < G ? src[q] : make_uint4(0, 0, 0, 0);
+            pair3_x(nat, xq[r]);
+        }
     }
 
     // this lane's two units and two scales inside a tile
-    const int wo0 = j * 1024 + lane * 16, wo1 = (CG + j) * 1024 + lane * 16;
-    const int so0 = 2 * CG * 1024 + lane * 4 * CG + j * 2, so1 = so0 + CG * 2;
+    const int wo0 = j * UB + lane * US, wo1 = (CG + j) * UB + lane * US;
+    const int so0 = 2 * CG * UB + lane * 4 * CG + j * 2, so1 = so0 + CG * 2;
     struct Regs {
         v4u w0, w1;
         uint32_t s0, s1;
@@ -161,8 +279,8 @@ __global__ __launch_bounds__(64 * CG) void gemm_valu_stream_kernel(
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t *>(wd + (t < tiles ? t : 0) * PB), (short)0, t < tiles ? PB : 0,
             0x00020000);
-        r.w0 = __builtin_amdgcn_raw_buffer_load_b128(rs, wo0, 0, 0);
-        r.w1 = __builtin_amdgcn_raw_buffer_load_b128(rs, wo1, 0, 0);
+        r.w0 = load_unit_g<FMT>(rs, wo0);
+        r.w1 = load_unit_g<FMT>(rs, wo1);
         r.s0 = __builtin_amdgcn_raw_buffer_load_b32(rs, so0 & ~3, 0, 0);
         r.s1 = __builtin_amdgcn_raw_buffer_load_b32(rs, so1 & ~3, 0, 0);
     };
@@ -183,23 +301,41 @@ __global__ __launch_bounds__(64 * CG) void gemm_valu_stream_kernel(
 #pragma unroll
             for (int r = 0; r < MC; ++r)
                 p[r][0] = p[r][1] = 0.f;
-            const uint32_t w0[4] = {ring[q].w0.x, ring[q].w0.y, ring[q].w0.z, ring[q].w0.w};
-            const uint32_t w1[4] = {ring[q].w1.x, ring[q].w1.y, ring[q].w1.z, ring[q].w1.w};
+            if constexpr (FMT == 4) {
+                const uint32_t w0[4] = {ring[q].w0.x, ring[q].w0.y, ring[q].w0.z, ring[q].w0.w};
+                const uint32_t w1[4] = {ring[q].w1.x, ring[q].w1.y, ring[q].w1.z, ring[q].w1.w};
 #pragma unroll
-            for (int wq = 0; wq < 4; ++wq) {
-                h2 a0, a1, a2, a3, b0, b1, b2, b3;
-                dequant_word_unit(w0[wq], mk, a0, a1, a2, a3);
-                dequant_word_unit(w1[wq], mk, b0, b1, b2, b3);
+                for (int wq = 0; wq < 4; ++wq) {
+                    h2 a0, a1, a2, a3, b0, b1, b2, b3;
+                    dequant_word_unit(w0[wq], mk, a0, a1, a2, a3);
+                    dequant_word_unit(w1[wq], mk, b0, b1, b2, b3);
+#pragma unroll
+                    for (int r = 0; r < MC; ++r) {
+                        p[r][0] = __builtin_amdgcn_fdot2(a0, as_h2(xq[r][wq].x), p[r][0], false);
+                        p[r][1] = __builtin_amdgcn_fdot2(b0, as_h2(xq[r][wq].x), p[r][1], false);
+                        p[r][0] = __builtin_amdgcn_fdot2(a1, as_h2(xq[r][wq].y), p[r][0], false);
+                        p[r][1] = __builtin_amdgcn_fdot2(b1, as_h2(xq[r][wq].y), p[r][1], false);
+                        p[r][0] = __builtin_amdgcn_fdot2(a2, as_h2(xq[r][wq].z), p[r][0], false);
+                        p[r][1] = __builtin_amdgcn_fdot2(b2, as_h2(xq[r][wq].z), p[r][1], false);
+                        p[r][0] = __builtin_amdgcn_fdot2(a3, as_h2(xq[r][wq].w), p[r][0], false);
+                        p[r][1] = __builtin_amdgcn_fdot2(b3, as_h2(xq[r][wq].w), p[r][1], false);
+                    }
+                }
+            } else {
+                h2 A[16], B[16];
+                dequant_unit3(ring[q].w0.x, ring[q].w0.y, ring[q].w0.z, mk3, A);
+                dequant_unit3(ring[q].w1.x, ring[q].w1.y, ring[q].w1.z, mk3, B);
 #pragma unroll
                 for (int r = 0; r < MC; ++r) {
-                    p[r][0] = __builtin_amdgcn_fdot2(a0, as_h2(xq[r][wq].x), p[r][0], false);
-                    p[r][1] = __builtin_amdgcn_fdot2(b0, as_h2(xq[r][wq].x), p[r][1], false);
-                    p[r][0] = __builtin_amdgcn_fdot2(a1, as_h2(xq[r][wq].y), p[r][0], false);
-                    p[r][1] = __builtin_amdgcn_fdot2(b1, as_h2(xq[r][wq].y), p[r][1], false);
-                    p[r][0] = __builtin_amdgcn_fdot2(a2, as_h2(xq[r][wq].z), p[r][0], false);
-                    p[r][1] = __builtin_amdgcn_fdot2(b2, as_h2(xq[r][wq].z), p[r][1], false);
-                    p[r][0] = __builtin_amdgcn_fdot2(a3, as_h2(xq[r][wq].w), p[r][0], false);
-                    p[r][1] = __builtin_amdgcn_fdot2(b3, as_h2(xq[r][wq].w), p[r][1], false);
+                    const uint32_t xr[16] = {xq[r][0].x, xq[r][0].y, xq[r][0].z, xq[r][0].w,
+                                             xq[r][1].x, xq[r][1].y, xq[r][1].z, xq[r][1].w,
+                                             xq[r][2].x, xq[r][2].y, xq[r][2].z, xq[r][2].w,
+                                             xq[r][3].x, xq[r][3].y, xq[r][3].z, xq[r][3].w};
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        p[r][0] = __builtin_amdgcn_fdot2(A[i], as_h2(xr[i]), p[r][0], false);
+                        p[r][1] = __builtin_amdgcn_fdot2(B[i], as_h2(xr[i]), p[r][1], false);
+                    }
                 }
             }
             const float sc0 = f16_value((uint16_t)(ring[q].s0 >> ((so0 & 2) * 8)));
@@ -343,7 +479,7 @@ constexpr int kLdsRow = kStepK + 8;               // halves per LDS row (+16 B a
 // bytes).  The next step's units, scales and X chunks are loaded into
 // registers while the current step's MFMAs run; dequant and the LDS stores
 // happen between two barriers.
-template <int L, int CG, int NT, int MT, int WN, int WM>
+template <int L, int CG, int NT, int MT, int WN, int WM, int FMT = 4>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint8_t *__restrict__ wd,
                                                         int64_t wbytes,
                                                         const uint16_t *__restrict__ X,
@@ -354,7 +490,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint8_t *__restric
     static_assert(WN * WM == 4, "four wavefronts");
     constexpr int BN = 16 * NT * WN, BM = 16 * MT * WM;
     constexpr int TR = 128 / L;
-    constexpr int PB = CG * 2304;
+    constexpr int PB = CG * GFmt<FMT>::PASS;
+    constexpr int UB = GFmt<FMT>::UB, US = GFmt<FMT>::US;
     constexpr int WU = BN * kGroupsPerStep / 256;     // weight units per thread per step
     constexpr int XC = BM * kGroupsPerStep * 4 / 256; // 16-byte X chunks per thread per step
     static_assert(WU >= 1 && XC >= 1, "tile too small for 256 threads");
@@ -384,10 +521,11 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint8_t *__restric
 
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(wd), (short)0, (int)wbytes, 0x00020000);
-    const Masks mk = masks();
+    const Masks mk = FMT == 4 ? masks() : Masks{};
+    const Masks3 mk3 = FMT == 3 ? masks3() : Masks3{};
 
     // per-thread fixed parts of the weight unit addresses
-    int64_t ubase[WU];   // tile byte offset + lane' * 16 without the (u, j) unit term
+    int64_t ubase[WU];   // tile byte offset + lane' * US without the (u, j) unit term
     int64_t sbase[WU];   // tile byte offset of the lane's scale block
     int urow[WU], ucl[WU], uu[WU];
 #pragma unroll
@@ -399,8 +537,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint8_t *__restric
         urow[h] = rr;
         ucl[h] = cl;
         uu[h] = rr & 1;
-        ubase[h] = tile * PB + (int64_t)(sl * L + cl) * 16;
-        sbase[h] = tile * PB + 2 * CG * 1024 + (int64_t)(sl * L + cl) * 4 * CG;
+        ubase[h] = tile * PB + (int64_t)(sl * L + cl) * US;
+        sbase[h] = tile * PB + 2 * CG * UB + (int64_t)(sl * L + cl) * 4 * CG;
     }
 
     // X through a buffer resource too: chunks outside X (rows past m, groups
@@ -421,12 +559,12 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint8_t *__restric
         const int j = st / CBLOCKS, cb = st % CBLOCKS;
 #pragma unroll
         for (int h = 0; h < WU; ++h) {
-            const int64_t off = ubase[h] + (int64_t)(uu[h] * CG + j) * 1024 + cb * kGroupsPerStep * 16;
+            const int64_t off = ubase[h] + (int64_t)(uu[h] * CG + j) * UB + cb * kGroupsPerStep * US;
             const int64_t soff = sbase[h] + (int64_t)cb * kGroupsPerStep * 4 * CG + (uu[h] * CG + j) * 2;
             // rows past the end of the weight read as zero through the buffer bounds
             const int wo = (int)(live && off < wbytes ? off : wbytes);
             const int so = (int)(live && (soff & ~3ll) < wbytes ? (soff & ~3ll) : wbytes);
-            r.w[h] = __builtin_amdgcn_raw_buffer_load_b128(rs, wo, 0, 0);
+            r.w[h] = load_unit_g<FMT>(rs, wo);
             r.s[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, so, 0, 0) >> ((soff & 2) * 8);
         }
 #pragma unroll
@@ -445,14 +583,28 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint8_t *__restric
         for (int h = 0; h < WU; ++h) {
             const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(r.s[h] & 0xFFFFu));
             const h2 sc = {sv, sv};
-            const uint32_t ws4[4] = {r.w[h].x, r.w[h].y, r.w[h].z, r.w[h].w};
             uint4 *dst = reinterpret_cast<uint4 *>(&Ws[urow[h]][ucl[h] * 32]);
+            if constexpr (FMT == 4) {
+                const uint32_t ws4[4] = {r.w[h].x, r.w[h].y, r.w[h].z, r.w[h].w};
 #pragma unroll
-            for (int wq = 0; wq < 4; ++wq) {
-                h2 a0, a1, a2, a3;
-                dequant_word_unit(ws4[wq], mk, a0, a1, a2, a3);
-                // one f16 rounding of (q - 8) * s
-                dst[wq] = make_uint4(as_u32(a0 * sc), as_u32(a1 * sc), as_u32(a2 * sc), as_u32(a3 * sc));
+                for (int wq = 0; wq < 4; ++wq) {
+                    h2 a0, a1, a2, a3;
+                    dequant_word_unit(ws4[wq], mk, a0, a1, a2, a3);
+                    // one f16 rounding of (q - 8) * s
+                    dst[wq] = make_uint4(as_u32(a0 * sc), as_u32(a1 * sc), as_u32(a2 * sc), as_u32(a3 * sc));
+                }
+            } else {
+                // one f16 rounding of (q - 4) * s, then back to k order (X stays natural)
+                h2 P[16];
+                dequant_unit3(r.w[h].x, r.w[h].y, r.w[h].z, mk3, P);
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    P[i] = P[i] * sc;
+                uint4 o[4];
+                pairs3_to_k(P, o);
+#pragma unroll
+                for (int wq = 0; wq < 4; ++wq)
+                    dst[wq] = o[wq];
             }
         }
 #pragma unroll
@@ -460,8 +612,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint8_t *__restric
             const int q = tid + 256 * h;
             const int mr = q / (kGroupsPerStep * 4), rest = q % (kGroupsPerStep * 4);
             const int cl = rest >> 2, wq = rest & 3;
-            *reinterpret_cast<uint4 *>(&Xs[mr][cl * 32 + wq * 8]) =
-                pair_word(make_uint4(r.x[h].x, r.x[h].y, r.x[h].z, r.x[h].w));
+            const uint4 xv = make_uint4(r.x[h].x, r.x[h].y, r.x[h].z, r.x[h].w);
+            *reinterpret_cast<uint4 *>(&Xs[mr][cl * 32 + wq * 8]) = FMT == 4 ? pair_word(xv) : xv;
         }
     };
     auto mfma_step = [&](f4 (&acc)[NT][MT]) {
@@ -530,7 +682,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint8_t *__restric
 // block barrier -- and the four partial sums are added in wavefront order at the
 // end (deterministic).  Many small blocks keep enough weight bytes in flight
 // for the HBM-bound regime.
-template <int L, int CG, int MT>
+template <int L, int CG, int MT, int FMT = 4>
 __global__ __launch_bounds__(256) void gemm_mfma_small_kernel(const uint8_t *__restrict__ wd,
                                                               int64_t wbytes,
                                                               const uint16_t *__restrict__ X,
@@ -539,7 +691,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_small_kernel(const uint8_t *__r
 {
     constexpr int BM = 16 * MT;
     constexpr int TR = 128 / L;
-    constexpr int PB = CG * 2304;
+    constexpr int PB = CG * GFmt<FMT>::PASS;
+    constexpr int UB = GFmt<FMT>::UB, US = GFmt<FMT>::US;
     constexpr int XC = BM * kGroupsPerStep * 4 / 64;   // X chunks per lane per step
     constexpr int CBLOCKS = L / kGroupsPerStep;
     constexpr int STEPS = CG * CBLOCKS;
@@ -563,15 +716,16 @@ __global__ __launch_bounds__(256) void gemm_mfma_small_kernel(const uint8_t *__r
     const int xbytes = (int)(m * k * 2);
     const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(X), (short)0, xbytes, 0x00020000);
-    const Masks mk = masks();
+    const Masks mk = FMT == 4 ? masks() : Masks{};
+    const Masks3 mk3 = FMT == 3 ? masks3() : Masks3{};
 
     // this lane's weight unit in every step: row lane / 4, group slot lane % 4
     const int rr = lane >> 2, cl = lane & 3;
     const int64_t row = n0 + rr;
     const int64_t tile = row / TR;
     const int sl = (int)((row % TR) >> 1), uu = (int)(row & 1);
-    const int64_t ubase = tile * PB + (int64_t)(sl * L + cl) * 16;
-    const int64_t sbase = tile * PB + 2 * CG * 1024 + (int64_t)(sl * L + cl) * 4 * CG;
+    const int64_t ubase = tile * PB + (int64_t)(sl * L + cl) * US;
+    const int64_t sbase = tile * PB + 2 * CG * UB + (int64_t)(sl * L + cl) * 4 * CG;
 
     struct StepRegs {
         v4u w;
@@ -581,11 +735,11 @@ __global__ __launch_bounds__(256) void gemm_mfma_small_kernel(const uint8_t *__r
     auto load_step = [&](StepRegs &r, int st) {
         const bool live = st < STEPS;
         const int j = st / CBLOCKS, cb = st % CBLOCKS;
-        const int64_t off = ubase + (int64_t)(uu * CG + j) * 1024 + cb * kGroupsPerStep * 16;
+        const int64_t off = ubase + (int64_t)(uu * CG + j) * UB + cb * kGroupsPerStep * US;
         const int64_t soff = sbase + (int64_t)cb * kGroupsPerStep * 4 * CG + (uu * CG + j) * 2;
         const int wo = (int)(live && off < wbytes ? off : wbytes);
         const int so = (int)(live && (soff & ~3ll) < wbytes ? (soff & ~3ll) : wbytes);
-        r.w = __builtin_amdgcn_raw_buffer_load_b128(rs, wo, 0, 0);
+        r.w = load_unit_g<FMT>(rs, wo);
         r.s = __builtin_amdgcn_raw_buffer_load_b32(rs, so, 0, 0) >> ((soff & 2) * 8);
 #pragma unroll
         for (int h = 0; h < XC; ++h) {
@@ -602,13 +756,26 @@ __global__ __launch_bounds__(256) void gemm_mfma_small_kernel(const uint8_t *__r
         {
             const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(r.s & 0xFFFFu));
             const h2 sc = {sv, sv};
-            const uint32_t ws4[4] = {r.w.x, r.w.y, r.w.z, r.w.w};
             uint4 *dst = reinterpret_cast<uint4 *>(&Ws[wv][rr][cl * 32]);
+            if constexpr (FMT == 4) {
+                const uint32_t ws4[4] = {r.w.x, r.w.y, r.w.z, r.w.w};
 #pragma unroll
-            for (int wq = 0; wq < 4; ++wq) {
-                h2 a0, a1, a2, a3;
-                dequant_word_unit(ws4[wq], mk, a0, a1, a2, a3);
-                dst[wq] = make_uint4(as_u32(a0 * sc), as_u32(a1 * sc), as_u32(a2 * sc), as_u32(a3 * sc));
+                for (int wq = 0; wq < 4; ++wq) {
+                    h2 a0, a1, a2, a3;
+                    dequant_word_unit(ws4[wq], mk, a0, a1, a2, a3);
+                    dst[wq] = make_uint4(as_u32(a0 * sc), as_u32(a1 * sc), as_u32(a2 * sc), as_u32(a3 * sc));
+                }
+            } else {
+                h2 P[16];
+                dequant_unit3(r.w.x, r.w.y, r.w.z, mk3, P);
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    P[i] = P[i] * sc;
+                uint4 o[4];
+                pairs3_to_k(P, o);
+#pragma unroll
+                for (int wq = 0; wq < 4; ++wq)
+                    dst[wq] = o[wq];
             }
         }
 #pragma unroll
@@ -616,8 +783,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_small_kernel(const uint8_t *__r
             const int q = lane + 64 * h;
             const int mr = q / (kGroupsPerStep * 4), rest = q % (kGroupsPerStep * 4);
             const int xcl = rest >> 2, wq = rest & 3;
-            *reinterpret_cast<uint4 *>(&Xs[wv][mr][xcl * 32 + wq * 8]) =
-                pair_word(make_uint4(r.x[h].x, r.x[h].y, r.x[h].z, r.x[h].w));
+            const uint4 xv = make_uint4(r.x[h].x, r.x[h].y, r.x[h].z, r.x[h].w);
+            *reinterpret_cast<uint4 *>(&Xs[wv][mr][xcl * 32 + wq * 8]) = FMT == 4 ? pair_word(xv) : xv;
         }
         // the wavefront's own LDS slice: its writes must land before its reads
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -675,7 +842,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_small_kernel(const uint8_t *__r
     }
 }
 
-template <int L, int CG>
+template <int L, int CG, int FMT>
 hipError_t launch_valu_lc(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
                           int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
 {
@@ -689,9 +856,9 @@ hipError_t launch_valu_lc(const Geometry &geo, const uint8_t *wd, const uint16_t
 #define Q4_VALU_CASE(R)                                                                            \
     case R:                                                                                        \
         if (single)                                                                                \
-            hipLaunchKernelGGL((gemm_valu_stream_kernel<L, CG, R, PT>), grid, block, 0, stream, wd, \
-                               X, Y, m0, n, k, geo.tiles);                                         \
-        else                                                                                       \
+            hipLaunchKernelGGL((gemm_valu_stream_kernel<L, CG, R, PT, FMT>), grid, block, 0, stream, \
+                               wd, X, Y, m0, n, k, geo.tiles);                                     \
+        else if constexpr (FMT == 4)                                                               \
             hipLaunchKernelGGL((gemm_valu_multipass_kernel<L, CG, R>), grid, block, 0, stream, wd, \
                                X, Y, m0, n, k, geo.P, geo.tiles);                                  \
         break;
@@ -712,7 +879,7 @@ hipError_t launch_valu_lc(const Geometry &geo, const uint8_t *wd, const uint16_t
     return hipSuccess;
 }
 
-template <int L, int CG, int NT, int MT, int WN, int WM>
+template <int L, int CG, int NT, int MT, int WN, int WM, int FMT>
 hipError_t launch_mfma_cfg(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
                            int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
 {
@@ -721,42 +888,42 @@ hipError_t launch_mfma_cfg(const Geometry &geo, const uint8_t *wd, const uint16_
     const int64_t padded = (nbn + 7) / 8 * 8;   // whole groups of 8 for the XCD order
     const int64_t wbytes = geo.tiles * geo.tile_bytes;
     const dim3 grid((unsigned)(padded * ((m + BM - 1) / BM)));
-    hipLaunchKernelGGL((gemm_mfma_kernel<L, CG, NT, MT, WN, WM>), grid, dim3(256), 0, stream, wd,
+    hipLaunchKernelGGL((gemm_mfma_kernel<L, CG, NT, MT, WN, WM, FMT>), grid, dim3(256), 0, stream, wd,
                        wbytes, X, Y, m, n, k, nbn, padded);
     return hipGetLastError();
 }
 
-template <int L, int CG, int MT>
+template <int L, int CG, int MT, int FMT>
 hipError_t launch_mfma_small(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
                              int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
 {
     const int64_t wbytes = geo.tiles * geo.tile_bytes;
     const dim3 grid((unsigned)(((n + 15) / 16) * ((m + 16 * MT - 1) / (16 * MT))));
-    hipLaunchKernelGGL((gemm_mfma_small_kernel<L, CG, MT>), grid, dim3(256), 0, stream, wd, wbytes,
+    hipLaunchKernelGGL((gemm_mfma_small_kernel<L, CG, MT, FMT>), grid, dim3(256), 0, stream, wd, wbytes,
                        X, Y, m, n, k);
     return hipGetLastError();
 }
 
-template <int L, int CG>
+template <int L, int CG, int FMT>
 hipError_t launch_mfma_lc(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
                           int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
 {
     // m <= 16: the small kernel always; m <= 32: only while the 64-row tile
     // kernel would have too few blocks (n < 8192) to stream the weights
     if (L >= 8 && m <= 16)
-        return launch_mfma_small<L >= 8 ? L : 8, CG, 1>(geo, wd, X, m, n, k, Y, stream);
+        return launch_mfma_small<L >= 8 ? L : 8, CG, 1, FMT>(geo, wd, X, m, n, k, Y, stream);
     if (L >= 8 && m <= 32 && n < 8192)
-        return launch_mfma_small<L >= 8 ? L : 8, CG, 2>(geo, wd, X, m, n, k, Y, stream);
+        return launch_mfma_small<L >= 8 ? L : 8, CG, 2, FMT>(geo, wd, X, m, n, k, Y, stream);
     if (m <= 16)
-        return launch_mfma_cfg<L, CG, 1, 1, 4, 1>(geo, wd, X, m, n, k, Y, stream);  // 64 x 16
+        return launch_mfma_cfg<L, CG, 1, 1, 4, 1, FMT>(geo, wd, X, m, n, k, Y, stream);  // 64 x 16
     if (m <= 32)
-        return launch_mfma_cfg<L, CG, 2, 1, 2, 2>(geo, wd, X, m, n, k, Y, stream);  // 64 x 32
+        return launch_mfma_cfg<L, CG, 2, 1, 2, 2, FMT>(geo, wd, X, m, n, k, Y, stream);  // 64 x 32
     if (m <= 64)
-        return launch_mfma_cfg<L, CG, 2, 2, 2, 2>(geo, wd, X, m, n, k, Y, stream);  // 64 x 64
-    return launch_mfma_cfg<L, CG, 4, 4, 2, 2>(geo, wd, X, m, n, k, Y, stream);      // 128 x 128
+        return launch_mfma_cfg<L, CG, 2, 2, 2, 2, FMT>(geo, wd, X, m, n, k, Y, stream);  // 64 x 64
+    return launch_mfma_cfg<L, CG, 4, 4, 2, 2, FMT>(geo, wd, X, m, n, k, Y, stream);      // 128 x 128
 }
 
-template <int L>
+template <int L, int FMT>
 hipError_t launch_l(bool mfma, const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
                     int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
 {
@@ -764,8 +931,8 @@ hipError_t launch_l(bool mfma, const Geometry &geo, const uint8_t *wd, const uin
 #define Q4_CG_CASE(C)                                                                 \
     case C:                                                                           \
         if (mfma)                                                                     \
-            return launch_mfma_lc<L, C>(geo, wd, X, m, n, k, Y, stream);              \
-        return launch_valu_lc<L, C>(geo, wd, X, m, n, k, Y, stream);
+            return launch_mfma_lc<L, C, FMT>(geo, wd, X, m, n, k, Y, stream);         \
+        return launch_valu_lc<L, C, FMT>(geo, wd, X, m, n, k, Y, stream);
         Q4_CG_CASE(1)
         Q4_CG_CASE(2)
         Q4_CG_CASE(3)
@@ -779,8 +946,24 @@ hipError_t launch_l(bool mfma, const Geometry &geo, const uint8_t *wd, const uin
 
 bool gemm_mfma_eligible(const Geometry &geo) { return geo.P == 1 && geo.L >= 4; }
 
+template <int FMT>
+static hipError_t launch_gemm_fmt(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
+                                  int64_t n, int64_t k, uint16_t *Y, bool mfma, hipStream_t stream)
+{
+    switch (geo.L) {
+    case 64: return launch_l<64, FMT>(mfma, geo, wd, X, m, n, k, Y, stream);
+    case 32: return launch_l<32, FMT>(mfma, geo, wd, X, m, n, k, Y, stream);
+    case 16: return launch_l<16, FMT>(mfma, geo, wd, X, m, n, k, Y, stream);
+    case 8: return launch_l<8, FMT>(mfma, geo, wd, X, m, n, k, Y, stream);
+    case 4: return launch_l<4, FMT>(mfma, geo, wd, X, m, n, k, Y, stream);
+    case 2: return launch_l<2, FMT>(false, geo, wd, X, m, n, k, Y, stream);
+    case 1: return launch_l<1, FMT>(false, geo, wd, X, m, n, k, Y, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemm(const Geometry &geo, const void *wdata, const uint16_t *X, int64_t m,
-                       int64_t n, int64_t k, uint16_t *Y, int path, hipStream_t stream)
+                       int64_t n, int64_t k, uint16_t *Y, int path, hipStream_t stream, bool int3)
 {
     const uint8_t *wd = static_cast<const uint8_t *>(wdata);
     bool mfma = (path == GEMM_PATH_MFMA) || (path == GEMM_PATH_AUTO && m >= 16);
@@ -789,16 +972,9 @@ hipError_t launch_gemm(const Geometry &geo, const void *wdata, const uint16_t *X
     // the MFMA kernel addresses the weight and X through 32-bit buffer offsets
     if (mfma && (geo.tiles * geo.tile_bytes >= ((int64_t)1 << 31) || m * k * 2 >= ((int64_t)1 << 31)))
         mfma = false;
-    switch (geo.L) {
-    case 64: return launch_l<64>(mfma, geo, wd, X, m, n, k, Y, stream);
-    case 32: return launch_l<32>(mfma, geo, wd, X, m, n, k, Y, stream);
-    case 16: return launch_l<16>(mfma, geo, wd, X, m, n, k, Y, stream);
-    case 8: return launch_l<8>(mfma, geo, wd, X, m, n, k, Y, stream);
-    case 4: return launch_l<4>(mfma, geo, wd, X, m, n, k, Y, stream);
-    case 2: return launch_l<2>(false, geo, wd, X, m, n, k, Y, stream);
-    case 1: return launch_l<1>(false, geo, wd, X, m, n, k, Y, stream);
-    }
-    return hipErrorInvalidValue;
+    if (int3)   // one pass (k <= 8192, checked by the caller)
+        return geo.P == 1 ? launch_gemm_fmt<3>(geo, wd, X, m, n, k, Y, mfma, stream) : hipErrorInvalidValue;
+    return launch_gemm_fmt<4>(geo, wd, X, m, n, k, Y, mfma, stream);
 }
 
 }  // namespace q4

@@ -122,6 +122,6 @@ bool gemm_mfma_eligible(const Geometry &geo);
 
 hipError_t launch_gemm(const Geometry &geo, const void *wdata, const uint16_t *X,
                        int64_t m, int64_t n, int64_t k, uint16_t *Y, int path,
-                       hipStream_t stream);
+                       hipStream_t stream, bool int3 = false);
 
 }  // namespace q4

@@ -76,11 +76,17 @@ def test_int3_errors(q4, orc):
                        None) == q4.ERR_SIZE
     assert lib.q4_gemv(ctypes.byref(w3), X + 8, Y, None) == q4.ERR_ALIGN
     assert lib.q4_gemv(ctypes.byref(w3), X, X, None) == q4.ERR_ALIAS
-    # the LM head takes int3 rows (validated like int4); GEMM, FFN and the
-    # norm / RoPE ops refuse them, and the gate/up layout is only for the FFN
+    # the LM head and the GEMM take int3 rows (validated like int4); the FFN
+    # and the norm / RoPE ops refuse them, and the gate/up layout is only for
+    # the FFN
     assert lib.q4_lmhead_f32(ctypes.byref(w3), X, Y, A + 0x600000, None, 0, None) == q4.ERR_WORKSPACE
     assert lib.q4_lmhead_f32(ctypes.byref(w3), X, Y + 4, None, None, 0, None) == q4.ERR_ALIGN
-    assert lib.q4_gemm(ctypes.byref(w3), X, 4, Y, None, 0, None) == q4.ERR_LAYOUT
+    assert lib.q4_gemm(ctypes.byref(w3), X, 0, Y, None, 0, None) == q4.ERR_SHAPE
+    assert lib.q4_gemm(ctypes.byref(w3), X + 8, 4, Y, None, 0, None) == q4.ERR_ALIGN
+    assert lib.q4_gemm(ctypes.byref(weight(q4, layout=q4.LAYOUT_INT3, k=8224, nbytes=10 ** 9)), X, 4, Y,
+                       None, 0, None) == q4.ERR_SHAPE
+    assert lib.q4_add_rmsnorm_gemv(ctypes.byref(w3), X, None, A + 0x700000, 1e-5, None, Y,
+                                   None) == q4.ERR_LAYOUT
     assert lib.q4_ffn_gate_up_silu(ctypes.byref(w3), X, Y, None) == q4.ERR_LAYOUT
     assert lib.q4_unpack(ctypes.byref(w3), W + 2, S, None) == q4.ERR_ALIGN
     g3 = weight(q4, layout=q4.LAYOUT_INT3_GATE_UP)

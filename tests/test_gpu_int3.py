@@ -3,7 +3,9 @@ layouts (plain and gate/up) byte for byte, the unpack round trip, GEMV parity
 at the decode shapes and at ragged/edge shapes (f16 output bound as for
 int4), bit-exact one-hot reads (codes that cross a word boundary included),
 exactly representable sums, closed forms and determinism; the fused FFN and
-the f32 LM head with argmax over int3 weights."""
+the f32 LM head with argmax over int3 weights; the int3 GEMM on the VALU and
+MFMA paths (full parity, forced paths, ragged shapes, bit-exact cases, and
+sampled rows at the full prefill shape)."""
 import numpy as np
 import pytest
 import torch
@@ -165,3 +167,114 @@ def test_lmhead_int3(q4, orc, n, k):
     assert_within(got, ref, tol_f32(a), f"int3 lm head {n}x{k}")
     assert argmax_ok(int(idx.item()), ref, a, orc.argmax(ref))
     assert int(idx.item()) == int(np.argmax(got))
+
+
+
+GEMM_PATHS = {"auto": 0, "valu": 1, "mfma": 2}
+
+
+def run_gemm3(q4, w3, s, X, path=0):
+    pw = q4.pack_int3(dev_u32(w3), dev_u16(s))
+    return q4.gemm(pw, dev_f16(X), path=path), pw
+
+
+@pytest.mark.parametrize("m", [1, 2, 5, 8, 9, 15, 16, 17, 31, 33, 64, 65])
+def test_gemm_int3_parity_auto(q4, orc, m):
+    rng = np.random.default_rng(300 + m)
+    n, k = 1001, 3072
+    w3, s = si.draw_weight3(rng, n, k)
+    X = si.draw_X(rng, m, k)
+    Y, _ = run_gemm3(q4, w3, s, X)
+    ref, a = orc.gemm3(w3, s, X)
+    assert_within(host_f16_as_f64(Y), ref, tol_f16(ref, a), f"int3 gemm m={m}")
+
+
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("m", [1, 3, 16, 24, 40])
+def test_gemm_int3_forced_paths(q4, orc, path, m):
+    rng = np.random.default_rng(11 * m + len(path))
+    n, k = 777, 8192
+    w3, s = si.draw_weight3(rng, n, k)
+    X = si.draw_X(rng, m, k)
+    Y, _ = run_gemm3(q4, w3, s, X, GEMM_PATHS[path])
+    ref, a = orc.gemm3(w3, s, X)
+    assert_within(host_f16_as_f64(Y), ref, tol_f16(ref, a), f"int3 gemm {path} m={m}")
+
+
+@pytest.mark.parametrize("n,k", [(33, 96), (130, 224), (9, 3200), (70, 8160), (1, 32), (64, 256)])
+@pytest.mark.parametrize("m", [1, 6, 16, 20])
+def test_gemm_int3_ragged_shapes(q4, orc, n, k, m):
+    rng = np.random.default_rng(7 * n * k + m)
+    w3, s = si.draw_weight3(rng, n, k)
+    X = si.draw_X(rng, m, k)
+    ref, a = orc.gemm3(w3, s, X)
+    for path in (0, 1, 2):
+        Y, _ = run_gemm3(q4, w3, s, X, path)
+        assert_within(host_f16_as_f64(Y), ref, tol_f16(ref, a), f"int3 gemm {n}x{k} m={m} path={path}")
+
+
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("m", [3, 16, 64])
+def test_gemm_int3_exactly_representable_bit_exact(q4, orc, path, m):
+    """x in {-4..4}/4, scales in {2^-7, 2^-8}: every product and partial sum
+    is exact in f32 and (q - 4) * s is exact in f16, so both kernels must give
+    the round-to-nearest-even of the exact result."""
+    rng = np.random.default_rng(40 + m)
+    n, k = 512, 3072
+    w3 = stream_words3(rng.integers(0, 8, (n, k)))
+    s = si.f16_bits(2.0 ** -rng.integers(7, 9, (n, k // 32)))
+    X = si.f16_bits(rng.integers(-4, 5, (m, k)) / 4.0)
+    Y, _ = run_gemm3(q4, w3, s, X, GEMM_PATHS[path])
+    ref, _ = orc.gemm3(w3, s, X)
+    want = orc.doubles_to_halves(ref.ravel()).reshape(ref.shape)
+    bad = np.argwhere(host_u16(Y) != want)
+    assert bad.size == 0, f"{len(bad)} entries differ, first {bad[:4].tolist()}"
+
+
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_gemm_int3_one_hot_rows(q4, orc, path):
+    """row i of X is e_{k_i}: Y[i][r] = (q[r][k_i] - 4) * s exactly (one f16
+    rounding); the positions cover every code slot of a 32-group (10 and 21
+    cross canonical word boundaries, 30 and 31 are the bit-sliced codes) and
+    pin the k order and output layout of both kernels."""
+    rng = np.random.default_rng(23)
+    n, k = 300, 3072
+    w3, s = si.draw_weight3(rng, n, k)
+    ks = list(range(32)) + [32, 42, 53, 62, 63, 255, 256, 1000, 2047, 3061, 3070, 3071, 1536]
+    X = np.zeros((len(ks), k), np.uint16)
+    for i, kk in enumerate(ks):
+        X[i, kk] = 0x3C00
+    Y, _ = run_gemm3(q4, w3, s, X, GEMM_PATHS[path])
+    ref, _ = orc.gemm3(w3, s, X)
+    want = orc.doubles_to_halves(ref.ravel()).reshape(ref.shape)
+    assert np.array_equal(host_u16(Y), want)
+
+
+@pytest.mark.parametrize("m", [4, 16, 24, 64, 256])
+def test_gemm_int3_prefill_full_shape_sampled(q4, orc, m):
+    """The full prefill shape (W 16384 x 3072, int3): every output computed on
+    the GPU, 96 weight rows x all m rows checked against the oracle."""
+    rng = np.random.default_rng(900 + m)
+    w3, s = si.draw_weight3(rng, 16384, 3072)
+    X = si.draw_X(rng, m, 3072)
+    Y, _ = run_gemm3(q4, w3, s, X)
+    Yh = host_f16_as_f64(Y)
+    rows = np.sort(np.random.default_rng(m).choice(16384, 96, replace=False))
+    ref, a = orc.gemm3(np.ascontiguousarray(w3[rows]), np.ascontiguousarray(s[rows]), X)
+    assert_within(Yh[:, rows], ref, tol_f16(ref, a), f"int3 prefill m={m}")
+    assert np.all(np.isfinite(Yh))
+
+
+def test_gemm_int3_row_matches_gemv(q4, orc):
+    """m = 1 through the GEMM and the GEMV read the same packed buffer and both
+    sit within the bound of the oracle."""
+    rng = np.random.default_rng(61)
+    n, k = 3072, 3072
+    w3, s = si.draw_weight3(rng, n, k)
+    X = si.draw_X(rng, 1, k)
+    Y, pw = run_gemm3(q4, w3, s, X, 1)
+    y = q4.gemv(pw, dev_f16(X[0]))
+    ref, a = orc.gemm3(w3, s, X)
+    t = tol_f16(ref, a)
+    assert_within(host_f16_as_f64(Y), ref, t, "gemm m=1")
+    assert_within(host_f16_as_f64(y)[None, :], ref, t, "gemv")

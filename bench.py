@@ -645,6 +645,21 @@ def variants(torch, q4, si, np, K, W):
     faster = [int(m) for m, v in cross.items() if v["mfma_us"] < v["valu_us"]]
     gm["crossover"] = {"per_m": cross, "smallest_m_mfma_faster": min(faster) if faster else None}
     out["gemm_16384x3072"] = gm
+    del rot
+
+    # the same prefill GEMM over int3 weights (uniform random codes)
+    w3, s3 = si.draw_weight3(np.random.default_rng(5), 16384, 3072)
+    rot = Rotation(q4, q4.pack_int3(dev_u32(w3), dev_u16(s3)), copies_for(weight3_bytes(16384, 3072)))
+    g3 = {}
+    for m in (1, 8, 16, 64, 256):
+        us = gemm_us(m, q4.GEMM_AUTO, max(20, K // 4))
+        nb = weight3_bytes(16384, 3072) + 2 * m * 3072 + 2 * m * 16384
+        fl = 2.0 * m * 16384 * 3072
+        g3[str(m)] = {"us": round(us, 3), "gbs": round(nb / us / 1e3, 1),
+                      "hbm_frac": round(nb / us / 1e3 / PEAK_HBM_GBS, 4),
+                      "tflops": round(fl / us / 1e6, 2),
+                      "mfma_frac": round(fl / us / 1e6 / PEAK_F16_TFLOPS, 4)}
+    out["int3_gemm_16384x3072"] = g3
     return out
 
 

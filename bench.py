@@ -618,8 +618,8 @@ def variants(torch, q4, si, np, K, W):
                                             "bytes": nb}
     del rot
 
-    # skinny GEMM (prefill): M = 16, 64, 256 on the default path, and the
-    # VALU-vs-MFMA crossover over small M
+    # skinny GEMM (prefill, batched decode): M = 1, 8, 16, 64, 256 on the
+    # default path, and the VALU-vs-MFMA crossover over small M
     gm = {}
     inp = si.workload(si.GEMM, seed=0, m=256)
     rot = Rotation(q4, q4.pack(dev_u32(inp["words"]), dev_u16(inp["scales"])),
@@ -630,7 +630,7 @@ def variants(torch, q4, si, np, K, W):
         Y = torch.empty((m, 16384), dtype=torch.float16, device="cuda")
         return per_launch_us(torch, lambda i: q4.gemm(rot[i], X, Y, path=path), steps, 5)
 
-    for m in (16, 64, 256):
+    for m in (1, 8, 16, 64, 256):
         us = gemm_us(m, q4.GEMM_AUTO, max(20, K // 4))
         nb = weight_bytes(16384, 3072) + 2 * m * 3072 + 2 * m * 16384
         fl = 2.0 * m * 16384 * 3072

@@ -324,6 +324,16 @@ int q4_gemm_path(const q4_weight *w, const uint16_t *X, int32_t m, uint16_t *Y, 
     if (overlap(Y, ybytes, X, xbytes) || overlap(Y, ybytes, w->data, w->bytes))
         return Q4_ERR_ALIAS;
     (void)hipGetLastError();
+    // one activation row is the GEMV: its kernels stream W faster than the
+    // GEMM's single-row VALU pass (they need y 4-byte aligned)
+    if (path == Q4_GEMM_AUTO && m == 1 && aligned(Y, 4)) {
+        const q4::ArgmaxScratch none{nullptr, nullptr};
+        const hipStream_t st = static_cast<hipStream_t>(stream);
+        if (int3)
+            return hip_status(q4::launch_gemv3(geo, q4::EPI_F16, w->data, X, Y, rows, w->k, w->n, none, st));
+        return hip_status(q4::launch_gemv_family(geo, q4::EPI_F16, w->data, X, Y, rows, w->k, w->n, none,
+                                                 nullptr, nullptr, st));
+    }
     return hip_status(q4::launch_gemm(geo, w->data, X, m, w->n, w->k, Y, path,
                                       static_cast<hipStream_t>(stream), int3));
 }

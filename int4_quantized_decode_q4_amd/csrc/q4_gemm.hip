@@ -6,7 +6,7 @@
 // prompt processing; the pages give no design for them.
 //
 // Kernels:
-//  * VALU, m < 16 (or a layout the MFMA kernels do not take): the streaming
+//  * VALU, m < 4 (or a layout the MFMA kernels do not take): the streaming
 //    kernel -- CG wavefronts per block walk tiles, wavefront j takes group
 //    slot j of every lane, so each lane keeps that group's x slices for up to
 //    8 activation rows in VGPRs for the whole launch and one pass over W
@@ -26,6 +26,9 @@
 // them with f32 accumulation.  Inside each 8-k word the k order in LDS is
 // (0,4,1,5,2,6,3,7) for both operands -- the order the nibble masks produce
 // -- which leaves the contraction unchanged.
+// int3 weights (12-byte units of 32 codes, one pass) run through the same
+// kernels with their own dequant: exact (q - 4) pairs on the VALU path, f16
+// (q - 4) * s put back in k order for the MFMA kernels (X is not re-paired).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -966,7 +969,10 @@ hipError_t launch_gemm(const Geometry &geo, const void *wdata, const uint16_t *X
                        int64_t n, int64_t k, uint16_t *Y, int path, hipStream_t stream, bool int3)
 {
     const uint8_t *wd = static_cast<const uint8_t *>(wdata);
-    bool mfma = (path == GEMM_PATH_MFMA) || (path == GEMM_PATH_AUTO && m >= 16);
+    // from 4 rows on the MFMA kernels are faster (16384 x 3072: 13.7 against
+    // 17.4 us at m = 4, 17.4 against 44 us at m = 12); at 1-2 rows the VALU
+    // kernel's single exact pass over W wins
+    bool mfma = (path == GEMM_PATH_MFMA) || (path == GEMM_PATH_AUTO && m >= 4);
     if (mfma && !gemm_mfma_eligible(geo))
         mfma = false;
     // the MFMA kernel addresses the weight and X through 32-bit buffer offsets

@@ -1,5 +1,5 @@
 """q4_gemm / q4_gemm_path on the GPU against the oracle: the VALU kernel
-(m < 16, exact dequant) and the MFMA kernel (m >= 16, f16 dequant), full
+(m < 4, exact dequant) and the MFMA kernels (m >= 4, f16 dequant), full
 checks at moderate sizes and sampled checks at the full prefill shape."""
 import numpy as np
 import pytest
@@ -117,3 +117,31 @@ def test_gemm_mfma_matches_valu_within_tolerance(q4, orc):
     assert_within(host_f16_as_f64(Yv), ref, t, "valu")
     assert_within(host_f16_as_f64(Ym), ref, t, "mfma")
     assert_within(host_f16_as_f64(Ym), host_f16_as_f64(Yv), 2 * t, "mfma vs valu")
+
+
+@pytest.mark.parametrize("int3", [False, True])
+def test_gemm_one_row_is_the_gemv(q4, orc, int3):
+    """m = 1 on the default path runs the GEMV kernels: the output equals
+    q4_gemv's bit for bit and sits within the oracle's bound.  With Y only
+    2-byte aligned it takes the VALU GEMM kernel instead, also within the
+    bound."""
+    import torch
+    rng = np.random.default_rng(77 + int3)
+    n, k = 1001, 3072
+    if int3:
+        w, s = si.draw_weight3(rng, n, k)
+        pw = q4.pack_int3(dev_u32(w), dev_u16(s))
+        ref, a = orc.gemm3(w, s, si.draw_X(np.random.default_rng(5), 1, k))
+    else:
+        w, s = si.draw_weight(rng, n, k)
+        pw = q4.pack(dev_u32(w), dev_u16(s))
+        ref, a = orc.gemm(w, s, si.draw_X(np.random.default_rng(5), 1, k))
+    X = si.draw_X(np.random.default_rng(5), 1, k)
+    Y = q4.gemm(pw, dev_f16(X))
+    y = q4.gemv(pw, dev_f16(X[0]))
+    assert np.array_equal(host_u16(Y).reshape(-1), host_u16(y))
+    assert_within(host_f16_as_f64(Y), ref, tol_f16(ref, a), "gemm m=1 (gemv kernels)")
+    buf = torch.empty(n + 1, dtype=torch.float16, device="cuda")
+    Ym = buf[1:].view(1, n)
+    q4.gemm(pw, dev_f16(X), out=Ym)
+    assert_within(host_f16_as_f64(Ym), ref, tol_f16(ref, a), "gemm m=1, Y 2-byte aligned (VALU kernel)")

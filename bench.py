@@ -53,8 +53,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", choices=["all", "layer", "variants"], default="all",
-                    help="layer: the headline step only (for profiling)")
+    ap.add_argument("--only", choices=["all", "layer", "variants", "gemm"], default="all",
+                    help="layer: the headline step only; gemm: the prefill GEMM at --gemm-m "
+                         "only (both for profiling)")
+    ap.add_argument("--gemm-m", type=int, default=256,
+                    help="with --only gemm: activation rows of the 16384x3072 GEMM")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate host time budget of the oracle baseline")
@@ -64,6 +67,9 @@ def parse():
     ap.add_argument("--roles", metavar="NAMES",
                     help="with --summarize: comma-separated names of the GEMVs one step "
                          "launches, in order (a --only layer run: qkv,o_proj,gate_up,down)")
+    ap.add_argument("--counters", nargs="+", metavar="PMC_DB",
+                    help="print the median per dispatch of every counter in rocprofv3 --pmc "
+                         "databases, per q4 kernel and grid, and exit")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="print the HBM traffic summary of the gate_up GEMV from two "
                          "rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of --only layer, "
@@ -120,6 +126,34 @@ def pmc_max_dispatch(db_path: str, counter: str):
                       "counter_name = ? group by dispatch_id order by v desc limit 1",
                       (counter,)).fetchall()
     return rows[0]
+
+
+def counters_summary(db_paths) -> int:
+    """Median per dispatch of every counter of the library's kernels in one or
+    more rocprofv3 --pmc databases (one pass each), grouped by kernel and grid."""
+    import sqlite3
+    import statistics
+    groups = {}
+    for path in db_paths:
+        db = sqlite3.connect(path)
+        rows = db.execute("select dispatch_id, kernel_name, grid_size, counter_name, sum(value) from "
+                          "counters_collection group by dispatch_id, counter_name").fetchall()
+        for _, name, grid, counter, v in rows:
+            if "q4::" in name:
+                groups.setdefault((name, grid), {}).setdefault(counter, []).append(v)
+        print(f"# rocprofv3 --pmc: {path}")
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            if any(c == counter for *_, c, _ in rows):
+                # the run's calibration copy moves by far the most bytes
+                cal = pmc_max_dispatch(path, counter)
+                print(f"# calibration: {cal[0][:40]} copying {CALIBRATION_BYTES} B reads {counter} "
+                      f"{cal[1]:.1f} KiB -> {counter.lower()}_scale "
+                      f"{CALIBRATION_BYTES / (cal[1] * 1024.0):.4f}")
+    for (name, grid), cs in sorted(groups.items()):
+        print(f"# kernel {name[:110]}  grid {grid}")
+        for counter, v in sorted(cs.items()):
+            print(f"{counter}: {statistics.median(v):.6g}   (dispatches: {len(v)})")
+    return 0
 
 
 def traffic_summary(fetch_db: str, write_db: str) -> int:
@@ -291,6 +325,8 @@ def main():
         return summarize(args.summarize, args.roles.split(",") if args.roles else None)
     if args.traffic:
         return traffic_summary(*args.traffic)
+    if args.counters:
+        return counters_summary(args.counters)
     if args.gpus != 1:
         print("bench.py measures one GPU: the int4 GEMV path has no multi-GPU part in this "
               "library (run with --gpus 1)", file=sys.stderr)
@@ -304,6 +340,8 @@ def main():
     torch.cuda.set_device(0)
     K, W = args.steps, args.warmup
     result = {}
+    if args.only == "gemm":
+        return gemm_only(torch, q4, si, np, K, W, args.gemm_m)
 
     # ---------------------------------------------------------------- layer
     inp = si.workload(si.LAYER_SET, seed=0)
@@ -618,7 +656,7 @@ def variants(torch, q4, si, np, K, W):
                                             "bytes": nb}
     del rot
 
-    # skinny GEMM (prefill, batched decode): M = 1, 8, 16, 64, 256 on the
+    # skinny GEMM (prefill, batched decode): M = 1, 8, 16, 64, 128, 256 on the
     # default path, and the VALU-vs-MFMA crossover over small M
     gm = {}
     inp = si.workload(si.GEMM, seed=0, m=256)
@@ -630,7 +668,7 @@ def variants(torch, q4, si, np, K, W):
         Y = torch.empty((m, 16384), dtype=torch.float16, device="cuda")
         return per_launch_us(torch, lambda i: q4.gemm(rot[i], X, Y, path=path), steps, 5)
 
-    for m in (1, 8, 16, 64, 256):
+    for m in (1, 8, 16, 64, 128, 256):
         us = gemm_us(m, q4.GEMM_AUTO, max(20, K // 4))
         nb = weight_bytes(16384, 3072) + 2 * m * 3072 + 2 * m * 16384
         fl = 2.0 * m * 16384 * 3072
@@ -651,7 +689,7 @@ def variants(torch, q4, si, np, K, W):
     w3, s3 = si.draw_weight3(np.random.default_rng(5), 16384, 3072)
     rot = Rotation(q4, q4.pack_int3(dev_u32(w3), dev_u16(s3)), copies_for(weight3_bytes(16384, 3072)))
     g3 = {}
-    for m in (1, 8, 16, 64, 256):
+    for m in (1, 8, 16, 64, 128, 256):
         us = gemm_us(m, q4.GEMM_AUTO, max(20, K // 4))
         nb = weight3_bytes(16384, 3072) + 2 * m * 3072 + 2 * m * 16384
         fl = 2.0 * m * 16384 * 3072
@@ -661,6 +699,31 @@ def variants(torch, q4, si, np, K, W):
                       "mfma_frac": round(fl / us / 1e6 / PEAK_F16_TFLOPS, 4)}
     out["int3_gemm_16384x3072"] = g3
     return out
+
+
+def gemm_only(torch, q4, si, np, K, W, m: int) -> int:
+    """The prefill GEMM (W 16384 x 3072, X [m][3072], default path) alone, for
+    rocprofv3 counter runs; prints one JSON line.  Makes the same calibration
+    copy as --only layer."""
+    if not 1 <= m <= 256:
+        print("--gemm-m must be in 1..256", file=sys.stderr)
+        return 2
+    src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device="cuda")
+    torch.empty_like(src).copy_(src)
+    torch.cuda.synchronize()
+    del src
+    inp = si.workload(si.GEMM, seed=0, m=256)
+    rot = Rotation(q4, q4.pack(dev_u32(inp["words"]), dev_u16(inp["scales"])),
+                   copies_for(weight_bytes(16384, 3072)))
+    X = dev_f16(np.ascontiguousarray(inp["X"][:m]))
+    Y = torch.empty((m, 16384), dtype=torch.float16, device="cuda")
+    us = per_launch_us(torch, lambda i: q4.gemm(rot[i], X, Y), K, W)
+    nb = weight_bytes(16384, 3072) + 2 * m * 3072 + 2 * m * 16384
+    fl = 2.0 * m * 16384 * 3072
+    print(json.dumps({"workload": "gemm_16384x3072", "m": m, "steps": K, "us": round(us, 3),
+                      "gbs": round(nb / us / 1e3, 1), "tflops": round(fl / us / 1e6, 2),
+                      "mfma_frac": round(fl / us / 1e6 / PEAK_F16_TFLOPS, 4)}), flush=True)
+    return 0
 
 
 def cpu_baseline(si, inp, budget_s: float):

@@ -923,6 +923,12 @@ hipError_t launch_mfma_lc(const Geometry &geo, const uint8_t *wd, const uint16_t
         return launch_mfma_cfg<L, CG, 2, 1, 2, 2, FMT>(geo, wd, X, m, n, k, Y, stream);  // 64 x 32
     if (m <= 64)
         return launch_mfma_cfg<L, CG, 2, 2, 2, 2, FMT>(geo, wd, X, m, n, k, Y, stream);  // 64 x 64
+    // up to 128 rows a 128 x 128 tile would leave half the compute units of a
+    // 16384-row weight idle (128 blocks): 128 x 64 takes m = 128 from 57.5 to
+    // 40.3 us; above, 128 x 128 is the faster of the two (60.0 against 63.5 us
+    // at m = 256)
+    if (m <= 128)
+        return launch_mfma_cfg<L, CG, 4, 2, 2, 2, FMT>(geo, wd, X, m, n, k, Y, stream);  // 128 x 64
     return launch_mfma_cfg<L, CG, 4, 4, 2, 2, FMT>(geo, wd, X, m, n, k, Y, stream);      // 128 x 128
 }
 

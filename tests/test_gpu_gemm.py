@@ -17,7 +17,7 @@ def run(q4, w, s, X, path=0):
     return q4.gemm(pw, dev_f16(X), path=path), pw
 
 
-@pytest.mark.parametrize("m", [1, 2, 5, 8, 9, 15, 16, 17, 31, 33, 64, 65])
+@pytest.mark.parametrize("m", [1, 2, 5, 8, 9, 15, 16, 17, 31, 33, 64, 65, 97, 128, 129])
 def test_gemm_parity_auto(q4, orc, m):
     rng = np.random.default_rng(100 + m)
     n, k = 1000, 3072
@@ -89,7 +89,7 @@ def test_gemm_one_hot_rows(q4, orc, path):
     assert np.array_equal(host_u16(Y), want)
 
 
-@pytest.mark.parametrize("m", [16, 24, 64, 256])
+@pytest.mark.parametrize("m", [16, 24, 64, 100, 128, 256])
 def test_gemm_prefill_full_shape_sampled(q4, orc, m):
     """The full prefill shape (W 16384 x 3072): every output computed on the
     GPU, 96 weight rows x all m rows checked against the oracle."""

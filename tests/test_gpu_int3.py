@@ -178,7 +178,7 @@ def run_gemm3(q4, w3, s, X, path=0):
     return q4.gemm(pw, dev_f16(X), path=path), pw
 
 
-@pytest.mark.parametrize("m", [1, 2, 5, 8, 9, 15, 16, 17, 31, 33, 64, 65])
+@pytest.mark.parametrize("m", [1, 2, 5, 8, 9, 15, 16, 17, 31, 33, 64, 65, 97, 128, 129])
 def test_gemm_int3_parity_auto(q4, orc, m):
     rng = np.random.default_rng(300 + m)
     n, k = 1001, 3072
@@ -250,7 +250,7 @@ def test_gemm_int3_one_hot_rows(q4, orc, path):
     assert np.array_equal(host_u16(Y), want)
 
 
-@pytest.mark.parametrize("m", [4, 16, 24, 64, 256])
+@pytest.mark.parametrize("m", [4, 16, 24, 64, 128, 256])
 def test_gemm_int3_prefill_full_shape_sampled(q4, orc, m):
     """The full prefill shape (W 16384 x 3072, int3): every output computed on
     the GPU, 96 weight rows x all m rows checked against the oracle."""

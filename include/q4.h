@@ -156,10 +156,10 @@ int q4_pack_rope(const uint32_t *words, const uint16_t *scales, int32_t n, int32
  * code k in stream bits 3k .. 3k+2 (so a group of 32 codes fills 3 words).
  *   words3 : device, uint32 [n][3k/32], 4-byte aligned
  *   scales : device, f16 bits [n][k/32], 2-byte aligned
- *   k      : a multiple of 32, at most 8192 (one pass of the layout)
+ *   k      : a multiple of 32 (k > 8192 takes several passes, as for int4)
  *   dst    : device, >= q4_packed_bytes(n, k, Q4_LAYOUT_INT3) bytes, 256-byte
- *            aligned.  The device layout uses the tiles of the int4 one with
- *            12-byte lane units (word i of a group's unit: codes 10i + m at
+ *            aligned.  The device layout uses the tiles and passes of the int4
+ *            one with 12-byte lane units (word i of a group's unit: codes 10i + m at
  *            bits 3m and 10i + 5 + m at bits 16 + 3m, m = 0..4; bit i of
  *            codes 30 and 31 at bits 15 and 31); padding is code 4, scale 0.
  * The result feeds q4_gemv, q4_gemm and q4_lmhead_f32 (and q4_unpack).  Errors as q4_pack.

@@ -42,9 +42,6 @@ int hip_status(hipError_t e)
     return Q4_ERR_HIP;
 }
 
-// int3 weights hold one pass (k <= 8192, the longest k of the decode shapes)
-constexpr int32_t kInt3MaxK = 8192;
-
 // Checks shared by every op that reads a packed weight; returns the logical
 // row count of the layout through `rows`.
 int check_weight(const q4_weight *w, int32_t want_layout, q4::Geometry *geo, int64_t *rows)
@@ -61,8 +58,6 @@ int check_weight(const q4_weight *w, int32_t want_layout, q4::Geometry *geo, int
         (w->head_dim < 2 || w->head_dim % 2 != 0 || w->n % w->head_dim != 0))
         return Q4_ERR_SHAPE;
     const bool int3 = w->layout == Q4_LAYOUT_INT3 || w->layout == Q4_LAYOUT_INT3_GATE_UP;
-    if (int3 && w->k > kInt3MaxK)
-        return Q4_ERR_SHAPE;
     *rows = (want_layout == Q4_LAYOUT_GATE_UP || want_layout == Q4_LAYOUT_INT3_GATE_UP)
                 ? 2 * (int64_t)w->n
                 : (int64_t)w->n;
@@ -132,7 +127,7 @@ int64_t q4_packed_bytes(int32_t n, int32_t k, int32_t layout)
                              ? 2 * (int64_t)n
                              : (int64_t)n;
     if (layout == Q4_LAYOUT_INT3 || layout == Q4_LAYOUT_INT3_GATE_UP)
-        return k <= kInt3MaxK && q4::layout_geometry3(rows, k, &geo) ? geo.tiles * geo.tile_bytes : 0;
+        return q4::layout_geometry3(rows, k, &geo) ? geo.tiles * geo.tile_bytes : 0;
     if (!q4::layout_geometry(rows, k, &geo))
         return 0;
     return geo.tiles * geo.tile_bytes;
@@ -197,7 +192,7 @@ int pack3_common(const uint32_t *gw3, const uint16_t *gs, const uint32_t *uw3, c
     const bool gate_up = uw3 != nullptr || us != nullptr;
     if (!gw3 || !gs || !dst || !out || (gate_up && (!uw3 || !us)))
         return Q4_ERR_NULL;
-    if (!valid_shape(n, k) || k > kInt3MaxK)
+    if (!valid_shape(n, k))
         return Q4_ERR_SHAPE;
     if (!aligned(gw3, 4) || !aligned(gs, 2) || !aligned(dst, 256) ||
         (gate_up && (!aligned(uw3, 4) || !aligned(us, 2))))

@@ -375,7 +375,7 @@ __global__ __launch_bounds__(64 * CG) void gemm_valu_stream_kernel(
 // time; wavefront j takes group slot j of every lane, and the x slices of
 // each pass are read again for every tile.  Rows m0 .. m0 + MC - 1 of X
 // (MC <= kValuRows) per launch.
-template <int L, int CG, int MC>
+template <int L, int CG, int MC, int FMT = 4>
 __global__ __launch_bounds__(256) void gemm_valu_multipass_kernel(const uint8_t *__restrict__ wd,
                                                         const uint16_t *__restrict__ X,
                                                         uint16_t *__restrict__ Y, int64_t m0,
@@ -383,13 +383,14 @@ __global__ __launch_bounds__(256) void gemm_valu_multipass_kernel(const uint8_t 
                                                         int64_t tiles)
 {
     constexpr int TR = 128 / L;
-    const int64_t PB = (int64_t)CG * 2304;
+    const int64_t PB = (int64_t)CG * GFmt<FMT>::PASS;
     __shared__ float part[CG][64][2 * MC];
     const int lane = threadIdx.x & 63;
     const int j = threadIdx.x >> 6;
     const int s = lane / L, c = lane % L;
     const int64_t G = k >> 5;
-    const Masks mk = masks();
+    const Masks mk = FMT == 4 ? masks() : Masks{};
+    const Masks3 mk3 = FMT == 3 ? masks3() : Masks3{};
     for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
         float acc[MC][2];
 #pragma unroll
@@ -398,6 +399,42 @@ __global__ __launch_bounds__(256) void gemm_valu_multipass_kernel(const uint8_t 
         for (int p = 0; p < passes; ++p) {
             const int64_t g = (int64_t)p * L * CG + (int64_t)c * CG + j;
             const uint8_t *base = wd + (t * passes + p) * PB;
+            if constexpr (FMT == 3) {
+                // exact (q - 4) pairs of the lane's two units; x re-paired to match
+                constexpr int UB = GFmt<3>::UB;
+                const uint32_t *u0 = reinterpret_cast<const uint32_t *>(base + j * UB + lane * 12);
+                const uint32_t *u1 = reinterpret_cast<const uint32_t *>(base + (CG + j) * UB + lane * 12);
+                const uint16_t *sp = reinterpret_cast<const uint16_t *>(base + 2 * CG * UB + lane * 4 * CG);
+                const float s0 = f16_value(sp[j]), s1 = f16_value(sp[CG + j]);
+                h2 A[16], B[16];
+                dequant_unit3(u0[0], u0[1], u0[2], mk3, A);
+                dequant_unit3(u1[0], u1[1], u1[2], mk3, B);
+#pragma unroll
+                for (int r = 0; r < MC; ++r) {
+                    uint4 nat[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
+                                    make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+                    if (g < G) {
+                        const uint4 *src = reinterpret_cast<const uint4 *>(X + (m0 + r) * k + g * 32);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            nat[q] = src[q];
+                    }
+                    uint4 xp[4];
+                    pair3_x(nat, xp);
+                    const uint32_t xr[16] = {xp[0].x, xp[0].y, xp[0].z, xp[0].w, xp[1].x, xp[1].y,
+                                             xp[1].z, xp[1].w, xp[2].x, xp[2].y, xp[2].z, xp[2].w,
+                                             xp[3].x, xp[3].y, xp[3].z, xp[3].w};
+                    float a = 0.f, b = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        a = __builtin_amdgcn_fdot2(A[i], as_h2(xr[i]), a, false);
+                        b = __builtin_amdgcn_fdot2(B[i], as_h2(xr[i]), b, false);
+                    }
+                    acc[r][0] = fmaf(s0, a, acc[r][0]);
+                    acc[r][1] = fmaf(s1, b, acc[r][1]);
+                }
+                continue;
+            }
             const uint4 c0 = *reinterpret_cast<const uint4 *>(base + j * 1024 + lane * 16);
             const uint4 c1 = *reinterpret_cast<const uint4 *>(base + (CG + j) * 1024 + lane * 16);
             const uint16_t *sp =
@@ -861,8 +898,8 @@ hipError_t launch_valu_lc(const Geometry &geo, const uint8_t *wd, const uint16_t
         if (single)                                                                                \
             hipLaunchKernelGGL((gemm_valu_stream_kernel<L, CG, R, PT, FMT>), grid, block, 0, stream, \
                                wd, X, Y, m0, n, k, geo.tiles);                                     \
-        else if constexpr (FMT == 4)                                                               \
-            hipLaunchKernelGGL((gemm_valu_multipass_kernel<L, CG, R>), grid, block, 0, stream, wd, \
+        else                                                                                       \
+            hipLaunchKernelGGL((gemm_valu_multipass_kernel<L, CG, R, FMT>), grid, block, 0, stream, wd, \
                                X, Y, m0, n, k, geo.P, geo.tiles);                                  \
         break;
             Q4_VALU_CASE(1)
@@ -984,8 +1021,8 @@ hipError_t launch_gemm(const Geometry &geo, const void *wdata, const uint16_t *X
     // the MFMA kernel addresses the weight and X through 32-bit buffer offsets
     if (mfma && (geo.tiles * geo.tile_bytes >= ((int64_t)1 << 31) || m * k * 2 >= ((int64_t)1 << 31)))
         mfma = false;
-    if (int3)   // one pass (k <= 8192, checked by the caller)
-        return geo.P == 1 ? launch_gemm_fmt<3>(geo, wd, X, m, n, k, Y, mfma, stream) : hipErrorInvalidValue;
+    if (int3)
+        return launch_gemm_fmt<3>(geo, wd, X, m, n, k, Y, mfma, stream);
     return launch_gemm_fmt<4>(geo, wd, X, m, n, k, Y, mfma, stream);
 }
 

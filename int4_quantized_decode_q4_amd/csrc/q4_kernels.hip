@@ -1135,21 +1135,24 @@ __global__ __launch_bounds__(64 * CG) void gemv_split_kernel(
 }
 
 // Multi-pass kernel (k > 8192): a grid-stride loop over tiles that reloads
-// the x slice for every pass.
-template <int L, int CG, int EPI, bool NORM>
+// the x slice for every pass.  int3 (FMT 3, no norm prologue) reads its
+// 12-byte units through a buffer resource per pass and takes the block
+// kernel's unit arithmetic.
+template <int L, int CG, int EPI, bool NORM, int FMT = 4>
 __global__ __launch_bounds__(256) void gemv_multipass_kernel(
     const uint8_t *__restrict__ wd, const uint16_t *__restrict__ x, void *__restrict__ out,
     int64_t rows, int64_t k, int passes, int64_t tiles, int64_t n_out, ArgmaxScratch am,
     NormArgs nm, typename RopeParam<EPI>::type rp)
 {
-    constexpr int64_t PB = (int64_t)CG * 2304;
+    static_assert(FMT == 4 || !NORM, "the int3 kernels have no norm prologue");
+    constexpr int64_t PB = (int64_t)CG * (2 * Fmt<FMT>::UB + 256);
     const int lane = threadIdx.x & 63;
     const int s = lane / L, c = lane % L;
     const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
     const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    const DequantConsts m = dequant_consts();
+    const typename Fmt<FMT>::Consts m = Fmt<FMT>::consts();
     float inv = 0.f;
     if constexpr (NORM) {
         __shared__ float nscr[16];
@@ -1159,7 +1162,15 @@ __global__ __launch_bounds__(256) void gemv_multipass_kernel(
         float acc[2] = {0.f, 0.f};
         for (int p = 0; p < passes; ++p) {
             TileRegs<CG> r;
-            load_tile(r, wd + (t * passes + p) * PB, lane);
+            if constexpr (FMT == 4) {
+                load_tile(r, wd + (t * passes + p) * PB, lane);
+            } else {
+                const __amdgpu_buffer_rsrc_t rs = tile_rsrc(wd + (t * passes + p) * PB, (int)PB);
+#pragma unroll
+                for (int i = 0; i < 2 * CG; ++i)
+                    load_unit<CG, 3>(r, rs, lane, i);
+                load_scales<CG, 3>(r, rs, lane);
+            }
             uint32_t xp[CG][16];
 #pragma unroll
             for (int j = 0; j < CG; ++j) {
@@ -1167,9 +1178,21 @@ __global__ __launch_bounds__(256) void gemv_multipass_kernel(
                 if constexpr (NORM)
                     norm_x_group(xp[j], x, nm, inv, g, k >> 5);
                 else
-                    load_x_group(xp[j], x, g, k >> 5);
+                    load_x_group<FMT>(xp[j], x, g, k >> 5);
             }
-            compute_tile(r, xp, acc, m);
+            if constexpr (FMT == 4) {
+                compute_tile(r, xp, acc, m);
+            } else {
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int j = 0; j < CG; ++j) {
+                        const float d = Fmt<3>::dot(r.c[u][j], &xp[j][0], m);
+                        const int e = u * CG + j;
+                        const float sv = f16_value((uint16_t)(r.s[e >> 1] >> ((e & 1) * 16)));
+                        acc[u] = fmaf(sv, d, acc[u]);
+                    }
+            }
         }
         finish_tile<L, EPI>(acc, t, s, c, out, rows, n_out, bv, bi, rp);
     }
@@ -1274,9 +1297,9 @@ hipError_t launch_unpack3(const void *src, int64_t rows, int64_t k, const Geomet
     return hipGetLastError();
 }
 
-// int3 matmuls: the int4 plan (block or split kernel) with 12-byte units,
-// single pass (k <= 8192); epilogues f16 (GEMV), f32 + argmax (LM head) and
-// SiLU (gate/up interleaved rows; n_out = rows / 2).
+// int3 matmuls: the int4 plan (block, split or multi-pass kernel) with
+// 12-byte units; epilogues f16 (GEMV), f32 + argmax (LM head) and SiLU
+// (gate/up interleaved rows; n_out = rows / 2).
 template <int L, int CG, int EPI>
 static void launch_gemv3_lce(const GemvPlan &plan, const Geometry &geo, const uint8_t *wd,
                              const uint16_t *x, void *out, int64_t rows, int64_t k, int64_t n_out,
@@ -1287,6 +1310,9 @@ static void launch_gemv3_lce(const GemvPlan &plan, const Geometry &geo, const ui
     if (plan.mode == MODE_SPLIT)
         hipLaunchKernelGGL((gemv_split_kernel<L, CG, EPI, false, 3>), grid, block, 0, stream, wd, x,
                            out, rows, k, geo.tiles, n_out, am, nm, NoRope{});
+    else if (plan.mode == MODE_MULTIPASS)
+        hipLaunchKernelGGL((gemv_multipass_kernel<L, CG, EPI, false, 3>), grid, block, 0, stream, wd, x,
+                           out, rows, k, geo.P, geo.tiles, n_out, am, nm, NoRope{});
     else
         hipLaunchKernelGGL((gemv_block_kernel<L, CG, EPI, false, 3>), grid, block, 0, stream, wd, x,
                            out, rows, k, geo.tiles, n_out, am, nm, NoRope{});
@@ -1323,7 +1349,7 @@ hipError_t launch_gemv3(const Geometry &geo, Epilogue epi, const void *wdata, co
                         void *out, int64_t rows, int64_t k, int64_t n_out, ArgmaxScratch am,
                         hipStream_t stream)
 {
-    if (geo.P != 1 || k > kBlockXHalves)
+    if (geo.P == 1 && k > kBlockXHalves)
         return hipErrorInvalidValue;
     const GemvPlan plan = plan_gemv(geo);
     const uint8_t *wd = static_cast<const uint8_t *>(wdata);

@@ -628,9 +628,11 @@ def _decode3_device(buf: np.ndarray, n: int, k: int, g6):
 def pin_int3_layout(orc, quick=False):
     """The int3 device layout read back destination by destination: every
     (row, group) lands once with its 32 codes and scale; padding holds code 4
-    (a zero weight) with scale 0; the size is tiles * P * CG * 1792."""
+    (a zero weight) with scale 0; the size is tiles * P * CG * 1792 (one and
+    two passes)."""
     rng = np.random.default_rng(37)
-    shapes = [(5, 64), (3, 3072)] if quick else [(5, 64), (3, 3072), (70, 96), (2, 8192)]
+    shapes = [(5, 64), (3, 3072)] if quick else [(5, 64), (3, 3072), (70, 96), (2, 8192), (2, 8224),
+                                                 (3, 16384)]
     for n, k in shapes:
         codes = rng.integers(0, 8, size=(n, k))
         words3 = _stream_words3(codes)

@@ -45,7 +45,8 @@ def test_host_geometry_matches_oracle(q4, orc, n, k):
 
 
 @pytest.mark.parametrize("n,k", [(3072, 3072), (3072, 8192), (1, 32), (17, 96), (130, 64),
-                                 (33, 224), (999, 544), (5, 7168)])
+                                 (33, 224), (999, 544), (5, 7168), (64, 8224), (3, 16384),
+                                 (5, 24608)])
 def test_int3_packed_bytes_matches_oracle(q4, orc, n, k):
     assert q4.packed_bytes(n, k, q4.LAYOUT_INT3) == orc.lib.q4o_layout3_bytes(n, k)
 
@@ -56,12 +57,13 @@ def test_int3_errors(q4, orc):
     r = ctypes.byref(out)
     W, S, D = A, A + 0x10000, A + 0x100000
     nb = q4.packed_bytes(64, 96, q4.LAYOUT_INT3)
-    assert nb > 0 and q4.packed_bytes(64, 8224, q4.LAYOUT_INT3) == 0   # beyond one pass
+    nb2 = q4.packed_bytes(64, 8224, q4.LAYOUT_INT3)   # two passes
+    assert nb > 0 and nb2 == orc.lib.q4o_layout3_bytes(64, 8224) > nb
     f = lib.q4_pack_int3
     assert f(None, S, 64, 96, D, nb, r, None) == q4.ERR_NULL
     assert f(W, S, 64, 96, D, nb, None, None) == q4.ERR_NULL
     assert f(W, S, 64, 100, D, nb, r, None) == q4.ERR_SHAPE
-    assert f(W, S, 64, 8224, D, 10 ** 9, r, None) == q4.ERR_SHAPE
+    assert f(W, S, 64, 8224, D, nb2 - 1, r, None) == q4.ERR_SIZE
     assert f(W + 2, S, 64, 96, D, nb, r, None) == q4.ERR_ALIGN
     assert f(W, S + 1, 64, 96, D, nb, r, None) == q4.ERR_ALIGN
     assert f(W, S, 64, 96, D + 16, nb, r, None) == q4.ERR_ALIGN
@@ -70,8 +72,8 @@ def test_int3_errors(q4, orc):
     assert out.data is None
     X, Y = A + 0x200000, A + 0x300000
     w3 = weight(q4, layout=q4.LAYOUT_INT3)
-    assert lib.q4_gemv(ctypes.byref(weight(q4, layout=q4.LAYOUT_INT3, k=8224, nbytes=10 ** 9)),
-                       X, Y, None) == q4.ERR_SHAPE
+    assert lib.q4_gemv(ctypes.byref(weight(q4, layout=q4.LAYOUT_INT3, k=8224, nbytes=nb2 - 1)),
+                       X, Y, None) == q4.ERR_SIZE
     assert lib.q4_gemv(ctypes.byref(weight(q4, layout=q4.LAYOUT_INT3, nbytes=nb - 1)), X, Y,
                        None) == q4.ERR_SIZE
     assert lib.q4_gemv(ctypes.byref(w3), X + 8, Y, None) == q4.ERR_ALIGN
@@ -83,8 +85,8 @@ def test_int3_errors(q4, orc):
     assert lib.q4_lmhead_f32(ctypes.byref(w3), X, Y + 4, None, None, 0, None) == q4.ERR_ALIGN
     assert lib.q4_gemm(ctypes.byref(w3), X, 0, Y, None, 0, None) == q4.ERR_SHAPE
     assert lib.q4_gemm(ctypes.byref(w3), X + 8, 4, Y, None, 0, None) == q4.ERR_ALIGN
-    assert lib.q4_gemm(ctypes.byref(weight(q4, layout=q4.LAYOUT_INT3, k=8224, nbytes=10 ** 9)), X, 4, Y,
-                       None, 0, None) == q4.ERR_SHAPE
+    assert lib.q4_gemm(ctypes.byref(weight(q4, layout=q4.LAYOUT_INT3, k=8224, nbytes=nb2 - 1)), X, 4, Y,
+                       None, 0, None) == q4.ERR_SIZE
     assert lib.q4_add_rmsnorm_gemv(ctypes.byref(w3), X, None, A + 0x700000, 1e-5, None, Y,
                                    None) == q4.ERR_LAYOUT
     assert lib.q4_ffn_gate_up_silu(ctypes.byref(w3), X, Y, None) == q4.ERR_LAYOUT
@@ -99,7 +101,8 @@ def test_int3_errors(q4, orc):
     fg = lib.q4_pack_int3_gate_up
     nbg = g3.bytes
     assert fg(W, S, None, S, 64, 96, D, nbg, r, None) == q4.ERR_NULL
-    assert fg(W, S, W, S, 64, 8224, D, 10 ** 9, r, None) == q4.ERR_SHAPE
+    assert fg(W, S, W, S, 64, 8224, D, q4.packed_bytes(64, 8224, q4.LAYOUT_INT3_GATE_UP) - 1, r,
+              None) == q4.ERR_SIZE
     assert fg(W, S, W + 2, S, 64, 96, D, nbg, r, None) == q4.ERR_ALIGN
     assert fg(W, S, W, S, 64, 96, D, nbg - 1, r, None) == q4.ERR_SIZE
     assert fg(W, S, D, S, 64, 96, D, nbg, r, None) == q4.ERR_ALIAS

@@ -2,8 +2,9 @@
 layouts (plain and gate/up) byte for byte, the unpack round trip, GEMV parity
 at the decode shapes and at ragged/edge shapes (f16 output bound as for
 int4), bit-exact one-hot reads (codes that cross a word boundary included),
-exactly representable sums, closed forms and determinism; the fused FFN and
-the f32 LM head with argmax over int3 weights; the int3 GEMM on the VALU and
+exactly representable sums, closed forms and determinism, at one and at
+several passes (k > 8192); the fused FFN and the f32 LM head with argmax over
+int3 weights; the int3 GEMM on the VALU and
 MFMA paths (full parity, forced paths, ragged shapes, bit-exact cases, and
 sampled rows at the full prefill shape)."""
 import numpy as np
@@ -35,7 +36,8 @@ def run(q4, w3, s, x):
 
 
 @pytest.mark.parametrize("n,k", [(3072, 3072), (1, 32), (17, 96), (130, 64), (33, 224),
-                                 (999, 544), (5, 8192), (70, 7168)])
+                                 (999, 544), (5, 8192), (70, 7168), (64, 8224), (3, 16384),
+                                 (130, 24608)])
 def test_pack_int3_byte_exact_and_roundtrip(q4, orc, n, k):
     rng = np.random.default_rng(n * 7 + k)
     w3, s = si.draw_weight3(rng, n, k)
@@ -59,7 +61,8 @@ def test_gemv_int3_decode_shapes(q4, orc, n, k):
 
 
 RAGGED = [(1, 32), (2, 32), (17, 96), (130, 64), (33, 224), (7, 160), (6, 192), (1, 768),
-          (1001, 3072), (9, 8192), (64, 4096), (3001, 8192), (777, 7168), (3, 3200)]
+          (1001, 3072), (9, 8192), (64, 4096), (3001, 8192), (777, 7168), (3, 3200),
+          (3072, 16384), (130, 8224), (17, 24608), (1, 16384), (999, 8448)]
 
 
 @pytest.mark.parametrize("n,k", RAGGED)
@@ -72,7 +75,7 @@ def test_gemv_int3_ragged(q4, orc, n, k):
     assert_within(host_f16_as_f64(y), ref, tol_f16(ref, a), f"int3 gemv {n}x{k}")
 
 
-@pytest.mark.parametrize("n,k", [(3072, 3072), (130, 8192)])
+@pytest.mark.parametrize("n,k", [(3072, 3072), (130, 8192), (130, 16384)])
 def test_gemv_int3_one_hot_bit_exact(q4, orc, n, k):
     """x = e_k: y_n = (q - 4) * s exactly; the f16 output is its RNE, bit for
     bit, at positions that cover every code slot of the device words (10 and
@@ -90,7 +93,7 @@ def test_gemv_int3_one_hot_bit_exact(q4, orc, n, k):
         assert bad.size == 0, f"k={kk}: rows {bad[:5].tolist()} got {got[bad[:5]]} want {want[bad[:5]]}"
 
 
-@pytest.mark.parametrize("n,k", [(3072, 3072), (9216, 3072), (101, 8192)])
+@pytest.mark.parametrize("n,k", [(3072, 3072), (9216, 3072), (101, 8192), (101, 16384)])
 def test_gemv_int3_exactly_representable(q4, orc, n, k):
     """x in {-4..4}/4, scales in {2^-7, 2^-8}: exact in f32 in any order, so y
     is the RNE of the exact sum."""
@@ -134,7 +137,7 @@ def test_gemv_int3_deterministic(q4):
 
 
 @pytest.mark.parametrize("n,k", [(8192, 3072), (64, 3072), (17, 96), (130, 64), (999, 544),
-                                 (40, 8192)])
+                                 (40, 8192), (40, 8224), (256, 16384)])
 def test_pack_int3_gate_up_and_ffn(q4, orc, n, k):
     rng = np.random.default_rng(7 * n + k)
     gw, gs = si.draw_weight3(rng, n, k)
@@ -154,7 +157,8 @@ def test_pack_int3_gate_up_and_ffn(q4, orc, n, k):
     print(f"max err/tol {r:.3g}")
 
 
-@pytest.mark.parametrize("n,k", [(32064, 3072), (1001, 3072), (7, 160), (1001, 8192), (3, 8192)])
+@pytest.mark.parametrize("n,k", [(32064, 3072), (1001, 3072), (7, 160), (1001, 8192), (3, 8192),
+                                 (1001, 16384), (5, 8224)])
 def test_lmhead_int3(q4, orc, n, k):
     rng = np.random.default_rng(11 * n + k)
     w3, s3 = si.draw_weight3(rng, n, k)
@@ -201,7 +205,8 @@ def test_gemm_int3_forced_paths(q4, orc, path, m):
     assert_within(host_f16_as_f64(Y), ref, tol_f16(ref, a), f"int3 gemm {path} m={m}")
 
 
-@pytest.mark.parametrize("n,k", [(33, 96), (130, 224), (9, 3200), (70, 8160), (1, 32), (64, 256)])
+@pytest.mark.parametrize("n,k", [(33, 96), (130, 224), (9, 3200), (70, 8160), (1, 32), (64, 256),
+                                 (70, 8224), (33, 16384)])
 @pytest.mark.parametrize("m", [1, 6, 16, 20])
 def test_gemm_int3_ragged_shapes(q4, orc, n, k, m):
     rng = np.random.default_rng(7 * n * k + m)

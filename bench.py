@@ -677,7 +677,7 @@ def variants(torch, q4, si, np, K, W):
                       "tflops": round(fl / us / 1e6, 2),
                       "mfma_frac": round(fl / us / 1e6 / PEAK_F16_TFLOPS, 4)}
     cross = {}
-    for m in (1, 2, 4, 8, 12, 16, 24, 32):
+    for m in (1, 2, 4, 8, 12, 16, 24, 32, 64, 128, 256):
         cross[str(m)] = {"valu_us": round(gemm_us(m, q4.GEMM_VALU, 20), 3),
                          "mfma_us": round(gemm_us(m, q4.GEMM_MFMA, 20), 3)}
     faster = [int(m) for m, v in cross.items() if v["mfma_us"] < v["valu_us"]]

@@ -1,6 +1,7 @@
 """Replaying the ops from a HIP graph: every replay must equal the eager
 result bit for bit, with eager work and synchronisation between replays
-(including the LM-head argmax's second launch)."""
+(including the LM-head argmax's second launch); the GEMV family, the decode
+step's ops, and the GEMM kernels and int3 ops."""
 import numpy as np
 import pytest
 import torch
@@ -117,6 +118,68 @@ def test_graph_replays_decode_layer_ops(q4):
             t.zero_()                      # eager work between replays
         cache.copy_(cache0)
         cache8.copy_(cache80)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(names, eager, outs):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from eager"
+
+
+def test_graph_replays_gemm_and_int3(q4):
+    """The GEMM on each of its kernels (GEMV at m = 1, VALU at m = 3, small
+    and tiled MFMA at m = 8, 100, 256), int4 and int3, and the int3 FFN, LM
+    head (two launches) and multi-pass GEMV, replayed from one graph: every
+    replay equal to eager."""
+    rng = np.random.default_rng(14)
+    k = 3072
+    w, s = si.draw_weight(rng, 4096, k)
+    pw = q4.pack(dev_u32(w), dev_u16(s))
+    w3, s3 = si.draw_weight3(rng, 4096, k)
+    p3 = q4.pack_int3(dev_u32(w3), dev_u16(s3))
+    g3, gs3 = si.draw_weight3(rng, 2048, k)
+    u3, us3 = si.draw_weight3(rng, 2048, k)
+    gu3 = q4.pack_int3_gate_up(dev_u32(g3), dev_u16(gs3), dev_u32(u3), dev_u16(us3))
+    l3, ls3 = si.draw_weight3(rng, 5003, k)
+    lm3 = q4.pack_int3(dev_u32(l3), dev_u16(ls3))
+    mp3w, mp3s = si.draw_weight3(rng, 777, 16384)
+    mp3 = q4.pack_int3(dev_u32(mp3w), dev_u16(mp3s))
+    X = dev_f16(si.draw_X(rng, 256, k))
+    x = X[0].contiguous()
+    xl = dev_f16(si.draw_x(rng, 16384))
+    ms = (1, 3, 8, 100, 256)
+    Ys = {(m, f): torch.empty((m, 4096), dtype=torch.float16, device="cuda") for m in ms for f in (4, 3)}
+    h3 = torch.empty(2048, dtype=torch.float16, device="cuda")
+    logits = torch.empty(5003, dtype=torch.float32, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(q4.lib.q4_workspace_bytes(q4.OP_LMHEAD, 1, 5003, k), dtype=torch.uint8,
+                     device="cuda")
+    ymp = torch.empty(777, dtype=torch.float16, device="cuda")
+
+    def run():
+        for m in ms:
+            q4.gemm(pw, X[:m], Ys[(m, 4)])
+            q4.gemm(p3, X[:m], Ys[(m, 3)])
+        q4.ffn_gate_up_silu(gu3, x, h3)
+        q4.lmhead_f32(lm3, x, logits, am, ws=ws)
+        q4.gemv(mp3, xl, ymp)
+
+    outs = list(Ys.values()) + [h3, logits, am, ymp]
+    run()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    names = [f"gemm m={m} int{f}" for (m, f) in Ys] + ["int3 ffn", "int3 logits", "int3 argmax",
+                                                      "int3 multi-pass gemv"]
+    for rep in range(4):
+        for t in outs:
+            t.zero_()                      # eager work between replays
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()

@@ -65,7 +65,7 @@ def parse():
                     help="print per-kernel duration statistics of a rocprofv3 "
                          "--kernel-trace database (grouped by kernel and grid) and exit")
     ap.add_argument("--roles", metavar="NAMES",
-                    help="with --summarize: comma-separated names of the GEMVs one step "
+                    help="with --summarize or --counters: comma-separated names of the GEMVs one step "
                          "launches, in order (a --only layer run: qkv,o_proj,gate_up,down)")
     ap.add_argument("--counters", nargs="+", metavar="PMC_DB",
                     help="print the median per dispatch of every counter in rocprofv3 --pmc "
@@ -128,19 +128,30 @@ def pmc_max_dispatch(db_path: str, counter: str):
     return rows[0]
 
 
-def counters_summary(db_paths) -> int:
+def counters_summary(db_paths, roles=None) -> int:
     """Median per dispatch of every counter of the library's kernels in one or
-    more rocprofv3 --pmc databases (one pass each), grouped by kernel and grid."""
+    more rocprofv3 --pmc databases (one pass each), grouped by kernel and grid;
+    with `roles` the layer GEMV dispatches are grouped by role (label_roles)."""
     import sqlite3
     import statistics
     groups = {}
     for path in db_paths:
         db = sqlite3.connect(path)
         rows = db.execute("select dispatch_id, kernel_name, grid_size, counter_name, sum(value) from "
-                          "counters_collection group by dispatch_id, counter_name").fetchall()
-        for _, name, grid, counter, v in rows:
+                          "counters_collection group by dispatch_id, counter_name "
+                          "order by dispatch_id").fetchall()
+        role_of = {}
+        if roles:
+            order = []
+            for d, name, grid, _, _ in rows:
+                if not order or order[-1][0] != d:
+                    order.append((d, name, grid))
+            labels = label_roles([(name, grid) for _, name, grid in order], roles)
+            role_of = {d: lab for (d, _, _), lab in zip(order, labels)}
+        for d, name, grid, counter, v in rows:
             if "q4::" in name:
-                groups.setdefault((name, grid), {}).setdefault(counter, []).append(v)
+                key = (f"{role_of[d]}: {name}", grid) if role_of.get(d) else (name, grid)
+                groups.setdefault(key, {}).setdefault(counter, []).append(v)
         print(f"# rocprofv3 --pmc: {path}")
         for counter in ("FETCH_SIZE", "WRITE_SIZE"):
             if any(c == counter for *_, c, _ in rows):
@@ -326,7 +337,7 @@ def main():
     if args.traffic:
         return traffic_summary(*args.traffic)
     if args.counters:
-        return counters_summary(args.counters)
+        return counters_summary(args.counters, args.roles.split(",") if args.roles else None)
     if args.gpus != 1:
         print("bench.py measures one GPU: the int4 GEMV path has no multi-GPU part in this "
               "library (run with --gpus 1)", file=sys.stderr)

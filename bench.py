@@ -215,13 +215,14 @@ def summarize(db_path: str, roles=None) -> int:
     for (name, gx, wx, vg, ag, sg, lds, dur), role in zip(rows, labels):
         groups.setdefault((role or "-", name, gx, wx, vg, ag, sg, lds), []).append(dur / 1000.0)
     print(f"# rocprofv3 kernel trace: {db_path}")
-    print("# calls  avg_us  median_us  min_us  p90_us  grid  block  vgpr  agpr  sgpr  lds  role  kernel")
+    print("# calls  avg_us  median_us  min_us  p10_us  p90_us  grid  block  vgpr  agpr  sgpr  lds  role  kernel")
     for key, d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         role, name, gx, wx, vg, ag, sg, lds = key
         d.sort()
+        p10 = d[int(0.1 * (len(d) - 1))]
         p90 = d[min(len(d) - 1, int(0.9 * len(d)))]
         print(f"{len(d):6d} {statistics.fmean(d):8.3f} {statistics.median(d):8.3f} {d[0]:8.3f} "
-              f"{p90:8.3f} {gx:8d} {wx:5d} {vg:4d} {ag:4d} {sg:4d} {lds:6d}  {role:8s} {name[:100]}")
+              f"{p10:8.3f} {p90:8.3f} {gx:8d} {wx:5d} {vg:4d} {ag:4d} {sg:4d} {lds:6d}  {role:8s} {name[:100]}")
     return 0
 
 

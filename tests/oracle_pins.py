@@ -20,7 +20,10 @@ What pins what:
   * argmax        : planted maximum, ties go to the lowest index.
   * attention     : one position returns its V row, equal scores the mean of
                     V, a dominant key its V row, grouped-query heads, page
-                    order invariance.
+                    order invariance; the softmax weights in closed form at
+                    known score gaps and several temperatures (base e, one
+                    scaling), and the magnitude sum sum_t p_t |V_t| with V of
+                    both signs.
   * RoPE          : a hand example (pairing and frequency), identity at 0,
                     norm preservation, q.k depends on the position difference
                     only, only q and k heads of the fused QKV rotate; the
@@ -32,7 +35,8 @@ What pins what:
                     boundaries included) against codes written through a
                     Python integer stream; constant codes 0, 4, 7; the device
                     layout read back destination by destination.
-  * int8 KV       : a hand-quantised row away from ties, the +-127 maximum,
+  * int8 KV       : a hand-quantised row away from ties, the +-127 maximum
+                    (placed at every index of the row, the last included),
                     reconstruction within half a step, power-of-two scaling,
                     the zero row; the append's bytes against blocks located in
                     Python; int8 attention equal bit for bit to the f16
@@ -455,6 +459,47 @@ def pin_attention(orc, quick=False):
     assert np.array_equal(a1, a2)
 
 
+def pin_attention_softmax(orc, quick=False):
+    """The softmax weighting and its temperature in closed form, and the
+    magnitude sum a = sum_t p_t |V_t| that sizes every attention tolerance.
+
+    One query head, q = 1 at dimension 0 and 0 elsewhere; key t holds c_t at
+    dimension 0 and 0 elsewhere, so the raw score of position t is exactly
+    c_t and the scaled one is scale * c_t (power-of-two scales: exact).  With
+    position 0 at score 0 the weights are e^(scale c_t) / sum_u e^(scale c_u),
+    which fixes the exponent base (e, not 2), that the score is scaled once by
+    `scale` (no hidden 1/sqrt(d)), the normalisation, and, with V of mixed
+    signs, a = sum_t p_t |V_t| (not the un-normalised sum, not |out|)."""
+    nkv, nq = 1, 1
+    for d in (32, 96):
+        for scale, cs in ((0.5, (0.0, 2.0)), (0.125, (0.0, 2.0)), (0.25, (0.0, 3.0, -1.5))):
+            ctx = len(cs)
+            pages = 1
+            cache = np.zeros((pages, 2, nkv, 16, d), np.uint16)
+            q = np.zeros((nq, d), np.uint16)
+            q[0, 0] = si.f16_bits([1.0])[0]
+            vals = []
+            for t, c in enumerate(cs):
+                cache[0, 0, 0, t, 0] = si.f16_bits([c])[0]
+                # V rows of both signs, element by element: +/- (t + 1) * 0.75, alternating
+                v = np.array([(t + 1) * 0.75 * (1 if (i + t) % 2 == 0 else -1) for i in range(d)])
+                cache[0, 1, 0, t] = si.f16_bits(v)
+                vals.append(v)
+            table = np.array([0], np.int32)
+            out, a = orc.attention_decode(q, cache, table, ctx, nq, nkv, d, scale)
+            w = np.array([math.exp(scale * c) for c in cs])
+            p = w / w.sum()
+            want = sum(p[t] * vals[t] for t in range(ctx))
+            want_a = sum(p[t] * np.abs(vals[t]) for t in range(ctx))
+            assert np.allclose(out[0], want, rtol=1e-13, atol=0), (d, scale, out[0][:4], want[:4])
+            assert np.allclose(a[0], want_a, rtol=1e-13, atol=0), (d, scale, a[0][:4], want_a[:4])
+            # the two-position form the weights reduce to: (V0 + e^D V1) / (1 + e^D)
+            if ctx == 2:
+                D = scale * cs[1]
+                two = (vals[0] + math.exp(D) * vals[1]) / (1.0 + math.exp(D))
+                assert np.allclose(out[0], two, rtol=1e-13, atol=0)
+
+
 def load_geometry_golden():
     rows = []
     with open(os.path.join(GOLDEN, "layout_geometry.txt")) as f:
@@ -707,6 +752,19 @@ def pin_kv_quant(orc, quick=False):
         assert np.array_equal(q2, q) and sc2 == np.float32(sc) * np.float32(4.0)
     q, sc = orc.kv_quant_row(np.zeros(64, np.uint16))
     assert sc == 0 and np.all(q == 0)
+    # the row maximum at every index, the first and the last included: the
+    # element of largest magnitude (3 or -3, every other |x| < 1) becomes
+    # +-127 and fixes the scale 3/127 (f32)
+    for d in ((32, 96) if quick else (32, 96, 256)):
+        base = rng.uniform(-0.99, 0.99, d)
+        for j in range(d):
+            for sign in (1.0, -1.0):
+                xv = base.copy()
+                xv[j] = 3.0 * sign
+                q, sc = orc.kv_quant_row(si.f16_bits(xv))
+                assert sc == np.float32(3.0) / np.float32(127.0), (d, j, sc)
+                assert int(q[j]) == int(127 * sign), (d, j, q[j])
+                assert np.abs(q.astype(np.int64)).max() == 127
 
 
 def _kv8_block(orc, nkv, d, page, kv, g):
@@ -777,6 +835,6 @@ ALL_PINS = [
     pin_gemv_rational, pin_gemv_exactly_representable, pin_gemv_closed_forms,
     pin_gemv_one_hot, pin_gemv_linearity, pin_gemm_rows,
     pin_silu, pin_ffn, pin_argmax, pin_lmhead, pin_add_rmsnorm, pin_rope, pin_attention,
-    pin_layout_geometry, pin_layout_hand_example, pin_layout_roundtrip, pin_rope_layout,
+    pin_attention_softmax, pin_layout_geometry, pin_layout_hand_example, pin_layout_roundtrip, pin_rope_layout,
     pin_int3, pin_int3_layout, pin_int3_gemm, pin_int3_ffn, pin_kv_quant, pin_kv_append_int8, pin_attention_int8,
 ]

@@ -57,6 +57,11 @@ MUTANTS = [
      "[(((page * 2 + kv) * 16 + t % 16) * src->nkv + g) * d + i]"),
     ("attn_no_scale", "sc[t] = scale * dot;", "sc[t] = dot;"),
     ("attn_unnormalised", "out[h * d + i] = o / den;", "out[h * d + i] = o;"),
+    ("attn_softmax_base2", "sc[t] = exp(sc[t] - mx);", "sc[t] = exp2(sc[t] - mx);"),
+    ("attn_scaled_twice", "sc[t] = scale * dot;", "sc[t] = scale * dot / sqrt((double)d);"),
+    ("attn_magnitude_unnormalised", "a[h * d + i] = m / den;", "a[h * d + i] = m;"),
+    ("kv8_max_skips_last", "for (int64_t i = 0; i < d; ++i) {\n        float a = (float)fabs",
+     "for (int64_t i = 0; i < d - 1; ++i) {\n        float a = (float)fabs"),
     ("int3_group_of_64", "scales[r * G + col / 32]", "scales[r * G + col / 64]"),
     ("int3_last_k_dropped", "for (int64_t col = 0; col < k; ++col) {", "for (int64_t col = 0; col < k - 1; ++col) {"),
     ("int3_zero_point_3", "((double)(q - 4) * s)", "((double)(q - 3) * s)"),

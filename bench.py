@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--gemm-m", type=int, default=256,
                     help="with --only gemm: activation rows of the 16384x3072 GEMM")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate host time budget of the oracle baseline")
     ap.add_argument("--summarize", metavar="RESULTS_DB",
                     help="print per-kernel duration statistics of a rocprofv3 "
@@ -308,15 +308,23 @@ def capture(torch, fn, first: int, count: int):
     return g
 
 
+HOLD_CYCLES = 4_000_000   # device-side delay in front of a timed region
+
+
 def timed(torch, fn, steps: int, warmup: int):
-    """Wall time per call (ms) of exactly `steps` calls fn(warmup), ...,
-    replayed from one HIP graph and bracketed by synchronisation on both
-    sides, after `warmup` untimed calls (their own graph)."""
+    """Device time per call (ms) of exactly `steps` calls fn(warmup), ...,
+    replayed from one HIP graph, after `warmup` untimed calls (their own
+    graph), with synchronisation on both sides.  The start event is queued
+    behind a short bounded spin of the device (torch.cuda._sleep), so the
+    graph is already submitted when the timed region opens: the region holds
+    the steps' device work and the gaps between them, not the host's graph
+    submission, and the figure does not depend on `steps`."""
     gw = capture(torch, fn, 0, max(1, warmup))
     gt = capture(torch, fn, warmup, steps)
     gw.replay()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(HOLD_CYCLES)
     start.record()
     gt.replay()
     end.record()
@@ -324,11 +332,15 @@ def timed(torch, fn, steps: int, warmup: int):
     return start.elapsed_time(end) / steps
 
 
+PER_LAUNCH_MIN = 200   # launches behind every per-kernel figure
+
+
 def per_launch_us(torch, fn, launches: int = 200, warmup: int = 20):
-    """Average device time (us) of one launch of fn: `launches` back-to-back
-    launches (rotating weight copies) replayed from a HIP graph, bracketed by
-    HIP events on the launching stream."""
-    return 1000.0 * timed(torch, fn, launches, warmup)
+    """Average device time (us) of one launch of fn: at least PER_LAUNCH_MIN
+    back-to-back launches (rotating weight copies, so each copy comes back
+    after >= 1 GiB of other bytes) replayed from a HIP graph, bracketed by HIP
+    events on the launching stream."""
+    return 1000.0 * timed(torch, fn, max(launches, PER_LAUNCH_MIN), warmup)
 
 
 def main():
@@ -385,7 +397,16 @@ def main():
         torch.cuda.synchronize()
         del src
     ms = timed(torch, step, K, W)
-    kus = {key: per_launch_us(torch, fn, K, W) for key, fn in launches.items()}
+    # each GEMV alone, over its own rotation of >= 1 GiB of distinct copies
+    # (the layer set's copies plus more clones), so no single-matrix figure is
+    # served from the Infinity Cache
+    kus = {}
+    for key, (n, k) in si.LAYER_SHAPES.items():
+        own = rot[key].items + [rot[key][0].clone()
+                                for _ in range(copies_for(weight_bytes(n, k)) - C)]
+        kus[key] = per_launch_us(torch, lambda i, own=own, key=key:
+                                 q4.gemv(own[i % len(own)], xin[key], outs[key]), K, W)
+        del own
     gbs = step_bytes / (ms * 1e-3) / 1e9
     dom = "gate_up"
     dn, dk = si.LAYER_SHAPES[dom]
@@ -427,14 +448,63 @@ def main():
         },
     })
 
+    # the same four GEMVs as one q4_chain launch, gate_up after O-proj and
+    # down after gate_up (the order a decode layer imposes on them)
+    chain_sets = [[q4.Stage(rot["qkv"][i], x=x3, out=outs["qkv"]),
+                   q4.Stage(rot["o_proj"][i], x=x3, out=outs["o_proj"]),
+                   q4.Stage(rot["gate_up"][i], x=x3, after=1, out=outs["gate_up"]),
+                   q4.Stage(rot["down"][i], x=x8, after=2, out=outs["down"])] for i in range(C)]
+    ms_chain = timed(torch, lambda i: q4.chain(chain_sets[i % C]), K, W)
+    result["layer_set_one_chain_launch"] = {
+        "us": round(ms_chain * 1000, 3), "gbs": round(step_bytes / (ms_chain * 1e-3) / 1e9, 1),
+        "frac": round(step_bytes / (ms_chain * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del chain_sets
+
+    probe_sizes = {"gemv_3072x3072": gemv_bytes(3072, 3072)}
+    probe_sizes.update({key: gemv_bytes(n, k) for key, (n, k) in si.LAYER_SHAPES.items()})
+    probe_sizes.update({"layer_set": step_bytes,
+                        "lm_head_32064x3072": gemv_bytes(32064, 3072, out_bytes=4) + 4})
+    probe = read_probe_leg(torch, q4, probe_sizes, K, W)
+    result["read_probe"] = probe
+    result["per_kernel_frac_of_read_probe"] = {
+        key: round(probe[key]["us"] / kus[key], 4) for key in kus}
+    result["layer_set_frac_of_read_probe"] = round(probe["layer_set"]["us"] / (ms * 1000), 4)
+
     if args.only in ("all", "variants"):
         result["variants"] = variants(torch, q4, si, np, K, W)
+        v = result["variants"]
+        v["gemv_3072x3072"]["frac_of_read_probe"] = round(
+            probe["gemv_3072x3072"]["us"] / v["gemv_3072x3072"]["us"], 4)
+        v["lm_head_32064x3072_f32_argmax"]["frac_of_read_probe"] = round(
+            probe["lm_head_32064x3072"]["us"] / v["lm_head_32064x3072_f32_argmax"]["us"], 4)
 
     if not args.no_cpu_baseline and args.only == "all":
         result["cpu_baseline"] = cpu_baseline(si, inp, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
     return 0
+
+
+def read_probe_leg(torch, q4, sizes: dict, K: int, W: int) -> dict:
+    """The plain streaming read (q4_read_probe) of each size in one launch,
+    over rotating offsets of a buffer >= 1 GiB larger than the size (so the
+    bytes come from HBM), timed as the kernels are: the ceiling each
+    HBM-bound matmul is read against."""
+    big = max(sizes.values())
+    pool = torch.empty(ROTATE_BYTES + big + 4096, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(2048, dtype=torch.int32, device="cuda")
+    out = {}
+    for name, nb in sizes.items():
+        nb = (nb + 15) // 16 * 16          # the probe reads whole 16-byte words
+        stride = (nb + 4095) // 4096 * 4096
+        slots = max(2, ROTATE_BYTES // stride)
+        views = [pool[i * stride:i * stride + nb] for i in range(slots)]
+        us = per_launch_us(torch, lambda i, views=views: q4.read_probe(views[i % len(views)], sink),
+                           K, W)
+        out[name] = {"bytes": nb, "us": round(us, 3), "gbs": round(nb / us / 1e3, 1),
+                     "frac": round(nb / us / 1e3 / PEAK_HBM_GBS, 4)}
+    del pool
+    return out
 
 
 def decode_layer(torch, q4, si, np, K, W, ctx):
@@ -485,10 +555,31 @@ def decode_layer(torch, q4, si, np, K, W, ctx):
 
     ms = timed(torch, step, K, W)
     nb = layer_bytes + kv_read
+
+    # the same layer with O-proj -> add + RMSNorm -> gate/up + SiLU -> down
+    # as one q4_chain launch (each stage reads the previous one's output)
+    for L in layers:
+        L["chain"] = [q4.Stage(L["o"], x=att.view(-1), out=o),
+                      q4.Stage(L["gu"], src=0, residual=res[1], gamma=g2, eps=1e-5,
+                               residual_out=res2, out=h),
+                      q4.Stage(L["down"], src=1, out=y)]
+
+    def step_chain(i):
+        L = layers[i % copies]
+        pos = ctx - 1
+        q4.qkv_rope_append(L["qkv"], x, 32, pos, 10000.0, L["cache"], pt, out=qkv,
+                           norm=(res[0], g1, 1e-5, res[1]))
+        q4.attention_decode(qkv[:3072], L["cache"], pt, ctx, 32, 96 ** -0.5, out=att, ws=ws)
+        q4.chain(L["chain"])
+
+    ms_c = timed(torch, step_chain, K, W)
     return {"us": round(ms * 1000, 3), "ctx": ctx, "launches": 6 if ctx > 256 else 5,
             "weight_bytes": layer_bytes, "kv_bytes_read": kv_read,
             "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
-            "frac": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "layer_copies": copies}
+            "frac": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "layer_copies": copies,
+            "with_chain": {"us": round(ms_c * 1000, 3), "launches": 4 if ctx > 256 else 3,
+                           "gbs": round(nb / (ms_c * 1e-3) / 1e9, 1),
+                           "frac": round(nb / (ms_c * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
 
 
 def variants(torch, q4, si, np, K, W):
@@ -738,30 +829,73 @@ def gemm_only(torch, q4, si, np, K, W, m: int) -> int:
     return 0
 
 
-def cpu_baseline(si, inp, budget_s: float):
-    """The oracle (plain C, f64, one thread) on the host: whole layer-set
-    GEMVs, as many matrices as fit the time budget; rate in the metric's unit
-    (effective GB/s of the same algorithmic bytes)."""
-    import oracle
-    orc = oracle.load()
-    done_bytes, t_total, mats = 0, 0.0, []
-    keys = list(si.LAYER_SHAPES)
-    i = 0
-    while t_total < budget_s and i < 4 * len(keys):
-        key = keys[i % len(keys)]
+def host_cpu():
+    """(usable host threads, CPU model name)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, model
+
+
+def oracle_layer_set(orc, si, inp, threads: int) -> float:
+    """Seconds for the oracle to compute the four layer-set GEMVs once, the
+    rows of each split over `threads` host threads (each thread one call of
+    the oracle on its row range; ctypes releases the interpreter lock, and
+    the rows are independent, so the results are the same bits)."""
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = []
+    for key, (n, k) in si.LAYER_SHAPES.items():
         w, s = inp[key]
         x = inp["x8192"] if key == "down" else inp["x3072"]
-        t = time.perf_counter()
-        orc.gemv(w, s, x)
-        t_total += time.perf_counter() - t
-        done_bytes += gemv_bytes(*si.LAYER_SHAPES[key])
-        mats.append(key)
-        i += 1
-    return {"value": round(done_bytes / t_total / 1e9, 5), "unit": "GB/s", "cores": 1,
+        step = -(-n // threads)
+        jobs += [(w[r:r + step], s[r:r + step], x) for r in range(0, n, step)]
+    t = time.perf_counter()
+    if threads == 1:
+        for w, s, x in jobs:
+            orc.gemv(w, s, x)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda j: orc.gemv(*j), jobs))
+    return time.perf_counter() - t
+
+
+def cpu_baseline(si, inp, budget_s: float):
+    """The oracle (plain C, f64) on the host cores: whole layer sets (the four
+    GEMVs), once on one thread and as many times as fit the budget on every
+    usable host thread; the rate is in the metric's unit (effective GB/s of
+    the same algorithmic bytes).  `value` is the all-thread rate."""
+    import oracle
+    orc = oracle.load()
+    threads, model = host_cpu()
+    set_bytes = sum(gemv_bytes(n, k) for n, k in si.LAYER_SHAPES.values())
+    t1 = oracle_layer_set(orc, si, inp, 1)
+    runs, tn = [], 0.0
+    while tn < budget_s and len(runs) < 20:
+        runs.append(oracle_layer_set(orc, si, inp, threads))
+        tn += runs[-1]
+    best = min(runs)
+    return {"value": round(set_bytes / best / 1e9, 5), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{len(mats)} full GEMVs of the layer set ({','.join(mats)}), "
-                      f"{t_total:.1f} s of single-thread f64 oracle work",
-            "us_per_layer_equiv": round(1e6 * t_total * 63799296 / done_bytes / 1e0, 1)}
+            "sample": f"the four layer-set GEMVs ({set_bytes} algorithmic bytes), {len(runs)} runs "
+                      f"on {threads} threads (fastest taken, {tn:.1f} s in all) and 1 run on one "
+                      f"thread ({t1:.1f} s)",
+            "us_per_layer": round(best * 1e6, 1),
+            "one_thread": {"value": round(set_bytes / t1 / 1e9, 5), "unit": "GB/s",
+                           "us_per_layer": round(t1 * 1e6, 1)},
+            "host": {"threads_usable": threads, "cpu_model": model, "nproc": os.cpu_count()}}
 
 
 if __name__ == "__main__":

@@ -386,6 +386,74 @@ int q4_attention_decode_int8(const uint16_t *q, const void *cache8, const int32_
                              int32_t n_pages, int32_t ctx, int32_t nq, int32_t nkv, int32_t d,
                              float scale, uint16_t *out, void *ws, int64_t ws_bytes, void *stream);
 
+/*
+ * A chain of int4 GEMVs in one launch ([P1] 内核融合: kernels are fused to cut
+ * the dispatches of a decode step; 性能基准: the int4 matmuls dominate it).
+ * Stage i computes, in order,
+ *   xi = x (given) or the y of stage src (src < i);
+ *   with gamma: h = f16(xi + residual) (residual may be NULL: h = xi),
+ *               xi = f16(h * gamma / sqrt(mean(h^2) + eps)), h -> residual_out;
+ *   y  = xi . dequant(W)^T (Q4_LAYOUT_ROWS, f16 [n], as q4_gemv), or
+ *        SiLU(xi . Wg^T) * (xi . Wu^T) (Q4_LAYOUT_GATE_UP, f16 [n], as
+ *        q4_ffn_gate_up_silu),
+ * and does not start computing before stage `after` (< i) has finished.  A
+ * stage waits only for what it names (src, after); stages with neither run
+ * back to back with no grid-wide wait, and every stage's weights start
+ * streaming while the stage before it finishes.
+ *   w          : Q4_LAYOUT_ROWS or Q4_LAYOUT_GATE_UP, k from 1568 to 8192
+ *                (the chain kernel's geometries; Q4_ERR_SHAPE otherwise)
+ *   x          : device f16 [k], 16-byte aligned; NULL exactly when src >= 0
+ *                (then stage src's n must equal this k)
+ *   gamma, residual, residual_out : as q4_add_rmsnorm_gemv (16-byte aligned)
+ *   y          : device f16 [n], 4-byte aligned (2-byte for GATE_UP)
+ *   ws         : q4_chain_workspace_bytes(stages, n_stages) bytes, 256-byte
+ *                aligned, ZERO-FILLED before its first use and then left to
+ *                the library: it carries a launch counter per block from one
+ *                call to the next, so every call on one workspace must be
+ *                made on one stream of one device (calls on other streams
+ *                race).  Word 0 (uint32) is set non-zero by the device if a
+ *                wait ran out of time (2 ms; only when the GPU cannot hold
+ *                all blocks of the launch at once, e.g. beside other work);
+ *                the results of such a call are undefined, and the word stays
+ *                set until the caller clears it.
+ * The launch holds one block of 8 wavefronts per compute unit for its whole
+ * duration.  Errors: NULL, SHAPE, ALIGN, LAYOUT, SIZE, WORKSPACE, ALIAS, HIP.
+ */
+typedef struct q4_chain_stage {
+    const q4_weight *w;
+    const uint16_t *x;
+    int32_t src;
+    int32_t after;
+    const uint16_t *residual;
+    const uint16_t *gamma;
+    float eps;
+    int32_t reserved;         /* 0 */
+    uint16_t *residual_out;
+    uint16_t *y;
+} q4_chain_stage;
+
+/* Workspace bytes q4_chain needs for these stages (0 if they are invalid). */
+int64_t q4_chain_workspace_bytes(const q4_chain_stage *stages, int32_t n_stages);
+
+int q4_chain(const q4_chain_stage *stages, int32_t n_stages, void *ws, int64_t ws_bytes,
+             void *stream);
+
+/*
+ * Measurement aid: a plain streaming read of `bytes` bytes (a multiple of 16)
+ * at `src` (device, 16-byte aligned), the ceiling against which the matmuls' HBM rates are
+ * read (the Zero-TVM article, section 性能基准, keeps its protocol and raw
+ * data beside each figure).  Every 64-lane wavefront reads 1 KiB per load
+ * instruction, two 8 KiB chunks in flight, two blocks of four wavefronts per
+ * compute unit; nothing is computed but an xor of the words read.
+ *   sink       : device, 4-byte aligned, >= 8 * (compute units) bytes (8 KiB
+ *                covers any MI355X partition); receives one word per block
+ *   sink_bytes : its size
+ * Errors: NULL, SHAPE (bytes not a positive multiple of 16), ALIGN, SIZE,
+ * ALIAS, HIP.
+ */
+int q4_read_probe(const void *src, int64_t bytes, uint32_t *sink, int64_t sink_bytes,
+                  void *stream);
+
 /* Static text for a return code. */
 const char *q4_strerror(int code);
 

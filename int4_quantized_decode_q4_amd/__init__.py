@@ -47,9 +47,18 @@ class q4_weight(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
+class q4_chain_stage(ctypes.Structure):
+    _fields_ = [("w", ctypes.POINTER(q4_weight)), ("x", ctypes.c_void_p),
+                ("src", ctypes.c_int32), ("after", ctypes.c_int32),
+                ("residual", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("eps", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("residual_out", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
 _P = ctypes.c_void_p
 _I32, _I64 = ctypes.c_int32, ctypes.c_int64
 _W = ctypes.POINTER(q4_weight)
+_CS = ctypes.POINTER(q4_chain_stage)
 
 _SIGNATURES = {
     "q4_packed_bytes": (_I64, [_I32, _I32, _I32]),
@@ -81,6 +90,9 @@ _SIGNATURES = {
     "q4_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "q4_last_hip_error": (ctypes.c_int, []),
     "q4_layout_geometry": (ctypes.c_int, [_I32, _I32, _P]),
+    "q4_read_probe": (ctypes.c_int, [_P, _I64, _P, _I64, _P]),
+    "q4_chain_workspace_bytes": (_I64, [_CS, _I32]),
+    "q4_chain": (ctypes.c_int, [_CS, _I32, _P, _I64, _P]),
 }
 for _name, (_res, _args) in _SIGNATURES.items():
     _fn = getattr(_lib, _name)
@@ -361,13 +373,23 @@ def qkv_rope_append(w: PackedWeight, x: torch.Tensor, n_q_heads: int, pos: int,
     py = _dev(out, "out", 2, (w.n,))
     pc, pt, npages = None, None, 0
     if kv_cache is not None:
-        if kv_cache.element_size() != 2 or not kv_cache.is_contiguous() or kv_cache.dim() != 5:
-            raise ValueError("kv_cache must be a contiguous 16-bit [pages][2][n_kv][16][d] tensor")
-        pc = kv_cache.data_ptr()
+        if w.layout != LAYOUT_ROPE or w.desc.head_dim < 2:
+            raise ValueError("qkv_rope_append takes a weight packed by pack_rope")
+        d = w.desc.head_dim
+        nkv2 = w.n // d - n_q_heads
+        if n_q_heads < 0 or nkv2 < 0 or nkv2 % 2:
+            raise ValueError(f"{w.n // d} heads of {d} rows do not split into {n_q_heads} q heads "
+                             "and equal k and v heads")
+        if kv_cache.dim() != 5:
+            raise ValueError("kv_cache must be [pages][2][n_kv][16][d]")
         npages = kv_cache.shape[0]
+        pc = _dev(kv_cache, "kv_cache", 2, (npages, 2, nkv2 // 2, 16, d))
         if page_table is None:
             raise ValueError("a page table is needed with a cache")
         pt = _dev(page_table, "page_table", 4)
+        if pos < 0 or page_table.numel() < pos // 16 + 1:
+            raise ValueError(f"page_table has {page_table.numel()} entries; position {pos} needs "
+                             f"{pos // 16 + 1}")
     if norm is None:
         _check(_lib.q4_qkv_rope_append(ctypes.byref(w.desc), px, n_q_heads, pos, float(rope_base),
                                        py, pc, pt, npages, _stream(x)), "q4_qkv_rope_append")
@@ -386,13 +408,15 @@ def attention_decode(q: torch.Tensor, kv_cache: torch.Tensor, page_table: torch.
                      ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out f16 [nq][d]: one decode token's attention over positions 0..ctx-1
     of the paged cache f16 [pages][2][n_kv][16][d] (q4_attention_decode)."""
-    if kv_cache.dim() != 5 or kv_cache.element_size() != 2 or not kv_cache.is_contiguous():
+    if kv_cache.dim() != 5:
         raise ValueError("kv_cache must be a contiguous 16-bit [pages][2][n_kv][16][d] tensor")
     pages, _, nkv, _, d = kv_cache.shape
+    pc = _dev(kv_cache, "kv_cache", 2, (pages, 2, nkv, 16, d))
     pq = _dev(q, "q", 2)
     if q.numel() != n_q_heads * d:
         raise ValueError(f"q has {q.numel()} elements, expected {n_q_heads * d}")
     pt = _dev(page_table, "page_table", 4)
+    _check_table(page_table, ctx)
     if out is None:
         out = torch.empty((n_q_heads, d), dtype=torch.float16, device=q.device)
     po = _dev(out, "out", 2)
@@ -402,7 +426,7 @@ def attention_decode(q: torch.Tensor, kv_cache: torch.Tensor, page_table: torch.
         if ws is None:
             ws = workspace(q.device, need)
         pws = ws.data_ptr()
-    _check(_lib.q4_attention_decode(pq, kv_cache.data_ptr(), pt, pages, ctx, n_q_heads, nkv, d,
+    _check(_lib.q4_attention_decode(pq, pc, pt, pages, ctx, n_q_heads, nkv, d,
                                     float(scale), po, pws, need if need > 0 else 0, _stream(q)),
            "q4_attention_decode")
     return out
@@ -424,6 +448,9 @@ def kv_append_int8(qkv: torch.Tensor, n_q_heads: int, n_kv_heads: int, head_dim:
         raise ValueError(f"cache8 must be [pages][{pb}] bytes")
     pc = _dev(cache8, "cache8", 1)
     pt = _dev(page_table, "page_table", 4)
+    if pos < 0 or page_table.numel() < pos // 16 + 1:
+        raise ValueError(f"page_table has {page_table.numel()} entries; position {pos} needs "
+                         f"{pos // 16 + 1}")
     _check(_lib.q4_kv_append_int8(pq, n_q_heads, n_kv_heads, head_dim, pos, pc, pt,
                                   cache8.shape[0], _stream(qkv)), "q4_kv_append_int8")
 
@@ -441,6 +468,7 @@ def attention_decode_int8(q: torch.Tensor, cache8: torch.Tensor, page_table: tor
     if q.numel() != n_q_heads * head_dim:
         raise ValueError(f"q has {q.numel()} elements, expected {n_q_heads * head_dim}")
     pt = _dev(page_table, "page_table", 4)
+    _check_table(page_table, ctx)
     if out is None:
         out = torch.empty((n_q_heads, head_dim), dtype=torch.float16, device=q.device)
     po = _dev(out, "out", 2)
@@ -457,14 +485,26 @@ def attention_decode_int8(q: torch.Tensor, cache8: torch.Tensor, page_table: tor
     return out
 
 
+def _check_table(page_table: torch.Tensor, ctx: int) -> None:
+    """The page table must cover positions 0 .. ctx - 1 (16 per page)."""
+    if ctx < 1 or page_table.numel() < (ctx + 15) // 16:
+        raise ValueError(f"page_table has {page_table.numel()} entries; a context of {ctx} "
+                         f"needs {(ctx + 15) // 16}")
+
+
 _workspaces: dict = {}
+_retired: list = []
 
 
 def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    """A workspace of at least nbytes on `device`, kept per device."""
+    """A workspace of at least nbytes on `device`, kept per device.  A buffer
+    that is outgrown is replaced but never freed: a HIP graph captured
+    earlier may still hold its address."""
     key = (device.type, device.index)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            _retired.append(ws)
         ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
@@ -490,3 +530,97 @@ def lmhead_f32(w: PackedWeight, x: torch.Tensor, logits: Optional[torch.Tensor] 
     _check(_lib.q4_lmhead_f32(ctypes.byref(w.desc), px, pl, pa, pws, nws, _stream(x)),
            "q4_lmhead_f32")
     return logits, argmax
+
+
+def read_probe(src: torch.Tensor, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """A plain streaming read of every byte of src (q4_read_probe), the
+    measurement ceiling of the matmuls; returns the sink (one word per block)."""
+    if not isinstance(src, torch.Tensor) or not src.is_cuda or not src.is_contiguous():
+        raise TypeError("src must be a contiguous CUDA (HIP) tensor")
+    if sink is None:
+        sink = torch.empty(2048, dtype=torch.int32, device=src.device)
+    ps = _dev(sink, "sink", 4)
+    nbytes = src.numel() * src.element_size()
+    _check(_lib.q4_read_probe(src.data_ptr(), nbytes, ps, sink.numel() * 4, _stream(src)),
+           "q4_read_probe")
+    return sink
+
+
+class Stage:
+    """One stage of `chain`: y = x . dequant(W)^T (a Q4_LAYOUT_ROWS weight)
+    or h = SiLU(x . Wg^T) * (x . Wu^T) (a gate/up weight), where x is given
+    or is the output of stage `src`; with `gamma` the add + RMSNorm prologue
+    runs first (h = x + residual -> residual_out); the stage does not start
+    computing before stage `after` has finished."""
+
+    def __init__(self, w: PackedWeight, x: Optional[torch.Tensor] = None, src: int = -1,
+                 after: int = -1, residual: Optional[torch.Tensor] = None,
+                 gamma: Optional[torch.Tensor] = None, eps: float = 0.0,
+                 residual_out: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+        self.w, self.x, self.src, self.after = w, x, src, after
+        self.residual, self.gamma, self.eps, self.residual_out = residual, gamma, eps, residual_out
+        self.out = out
+
+
+def _chain_descs(stages):
+    arr = (q4_chain_stage * len(stages))()
+    for i, st in enumerate(stages):
+        d = arr[i]
+        d.w = ctypes.pointer(st.w.desc)
+        k, n = st.w.k, st.w.n
+        d.x = None if st.x is None else _dev(st.x, f"stage {i} x", 2, (k,))
+        d.src, d.after = int(st.src), int(st.after)
+        d.residual = None if st.residual is None else _dev(st.residual, f"stage {i} residual", 2, (k,))
+        d.gamma = None if st.gamma is None else _dev(st.gamma, f"stage {i} gamma", 2, (k,))
+        d.eps = float(st.eps)
+        d.reserved = 0
+        d.residual_out = (None if st.residual_out is None else
+                          _dev(st.residual_out, f"stage {i} residual_out", 2, (k,)))
+        if st.out is None:
+            st.out = torch.empty(n, dtype=torch.float16, device=st.w.device)
+        d.y = _dev(st.out, f"stage {i} out", 2, (n,))
+    return arr
+
+
+_chain_ws: dict = {}
+
+
+def chain_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    """The chain workspace of `device` (zero-filled when made, then owned by
+    the library: it carries per-block launch counters from call to call, so
+    all chain calls that share it must run on one stream).  An outgrown one
+    is replaced by a new zero-filled buffer and kept alive, never freed (a
+    captured HIP graph may still use it)."""
+    key = (device.type, device.index)
+    ws = _chain_ws.get(key)
+    if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            _retired.append(ws)
+        ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        _chain_ws[key] = ws
+    return ws
+
+
+def chain(stages, ws: Optional[torch.Tensor] = None):
+    """Run the stages in one launch (q4_chain); returns their outputs."""
+    arr = _chain_descs(stages)
+    need = int(_lib.q4_chain_workspace_bytes(arr, len(stages)))
+    if need <= 0:
+        # the same validation the call does, for its error code
+        _check(_lib.q4_chain(arr, len(stages), None, 0, None), "q4_chain")
+    dev = stages[0].w.device
+    if ws is None:
+        ws = chain_workspace(dev, need)
+    pws = _dev(ws, "ws", 1)
+    _check(_lib.q4_chain(arr, len(stages), pws, ws.numel(), _stream(ws)), "q4_chain")
+    return [st.out for st in stages]
+
+
+def chain_error(ws: Optional[torch.Tensor] = None, device=None) -> int:
+    """Word 0 of a chain workspace (non-zero: a wait of some call ran out of
+    time); synchronises with the device."""
+    if ws is None:
+        ws = _chain_ws.get(("cuda", torch.device(device or "cuda").index or 0))
+        if ws is None:
+            return 0
+    return int(ws[:4].view(torch.int32).item())

@@ -20,7 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libq4.so")
-SOURCES = ["q4_kernels.hip", "q4_gemm.hip", "q4_attention.hip", "q4_api.cpp"]
+SOURCES = ["q4_kernels.hip", "q4_gemm.hip", "q4_attention.hip", "q4_chain.hip", "q4_probe.hip",
+           "q4_api.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -3,6 +3,7 @@
 // stream.  Validation never touches the HIP runtime, so every error path can
 // be exercised on a machine without a GPU.
 #include <stdint.h>
+#include <atomic>
 #include <cmath>
 #include <string.h>
 
@@ -15,6 +16,9 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];   // 0 = not asked yet
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -113,6 +117,24 @@ int pack_common(const uint32_t *w0, const uint16_t *s0, const uint32_t *w1, cons
 }
 
 }  // namespace
+
+int q4::device_cus()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1) {
+            (void)hipGetLastError();
+            c = 256;
+        }
+        g_cus[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
+}
 
 extern "C" {
 
@@ -638,6 +660,203 @@ int q4_attention_decode_int8(const uint16_t *q, const void *cache8, const int32_
                                                 n_pages, ctx, nq, nkv, d, scale, out,
                                                 need > 0 ? ws : nullptr,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------ chain --
+
+namespace {
+
+struct ChainLayout {
+    int64_t epochs, flags[q4::kChainMaxStages], tags[q4::kChainMaxStages], total;
+};
+
+int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
+
+// Workspace offsets: error word, per-block epochs, then the completion flags
+// of every stage another waits `after`, and the tagged output of every stage
+// another reads as `src`.
+ChainLayout chain_layout(const q4_chain_stage *st, int32_t n)
+{
+    ChainLayout l{};
+    int64_t off = 256;
+    l.epochs = off;
+    off += 4 * q4::kChainMaxBlocks;
+    for (int i = 0; i < n; ++i) {
+        bool waited = false, read = false;
+        for (int j = i + 1; j < n; ++j) {
+            waited |= st[j].after == i;
+            read |= st[j].src == i;
+        }
+        l.flags[i] = -1;
+        l.tags[i] = -1;
+        if (waited) {
+            l.flags[i] = off;
+            off += 4 * q4::kChainMaxBlocks;
+        }
+        if (read) {
+            l.tags[i] = off;
+            off = align256(off + 4 * (int64_t)st[i].w->n);
+        }
+    }
+    l.total = off;
+    return l;
+}
+
+// Every check of q4_chain that does not involve the workspace; fills the
+// kernel-side stage descriptors (pointers into the workspace left null).
+int chain_check(const q4_chain_stage *st, int32_t n, q4::ChainArgs *a)
+{
+    if (!st)
+        return Q4_ERR_NULL;
+    if (n < 1 || n > q4::kChainMaxStages)
+        return Q4_ERR_SHAPE;
+    a->n_given = 0;
+    for (int i = 0; i < n; ++i) {
+        const q4_chain_stage &s = st[i];
+        if (!s.w || !s.w->data || !s.y || (s.src < 0 && !s.x))
+            return Q4_ERR_NULL;
+        const bool gate_up = s.w->layout == Q4_LAYOUT_GATE_UP;
+        if (!gate_up && s.w->layout != Q4_LAYOUT_ROWS)
+            return Q4_ERR_LAYOUT;
+        q4::Geometry geo;
+        int64_t rows = 0;
+        const int rc = check_weight(s.w, s.w->layout, &geo, &rows);
+        if (rc != Q4_OK)
+            return rc;
+        const int g = q4::chain_geo_of(geo);
+        if (g < 0)
+            return Q4_ERR_SHAPE;   // k outside 1568 .. 8192 (or a geometry without a chain path)
+        if (s.src >= i || s.after >= i || s.src < -1 || s.after < -1 || (s.src >= 0 && s.x))
+            return Q4_ERR_SHAPE;
+        if (s.src >= 0 && st[s.src].w && st[s.src].w->n != s.w->k)
+            return Q4_ERR_SHAPE;
+        if (s.gamma && (!(s.eps >= 0.f) || !std::isfinite(s.eps)))
+            return Q4_ERR_SHAPE;
+        if ((s.x && !aligned(s.x, 16)) || !aligned(s.y, gate_up ? 2 : 4) ||
+            (s.gamma && !aligned(s.gamma, 16)) || (s.residual && !aligned(s.residual, 16)) ||
+            (s.residual_out && !aligned(s.residual_out, 16)))
+            return Q4_ERR_ALIGN;
+        q4::ChainStageK &k = a->st[i];
+        k = q4::ChainStageK{};
+        k.wd = static_cast<const uint8_t *>(s.w->data);
+        const bool dep = s.src >= 0;
+        k.r = dep && s.gamma ? s.residual : nullptr;
+        k.gamma = dep ? s.gamma : nullptr;
+        k.h_out = dep && s.gamma ? s.residual_out : nullptr;
+        k.y = s.y;
+        if (!dep) {
+            // a given x is staged once per launch; stages that read the same
+            // vector with no prologue share it
+            int g = -1;
+            for (int j = 0; j < a->n_given && g < 0; ++j)
+                if (!s.gamma && a->given[j].x == s.x && a->given[j].gamma == nullptr && a->given[j].k == s.w->k)
+                    g = j;
+            if (g < 0) {
+                g = a->n_given++;
+                const int off = g == 0 ? 0 : a->given[g - 1].off + a->given[g - 1].k / 8;
+                if ((int64_t)off * 8 + s.w->k > q4::kChainGivenHalves)
+                    return Q4_ERR_SHAPE;   // the given vectors exceed the staged-x area
+                a->given[g] = q4::ChainGiven{s.x, s.gamma ? s.residual : nullptr, s.gamma,
+                                             s.gamma ? s.residual_out : nullptr, s.eps, s.w->k, off};
+            }
+            k.xoff = a->given[g].off;
+        }
+        k.tiles = geo.tiles;
+        k.rows = rows;
+        k.n_out = s.w->n;
+        k.k = s.w->k;
+        k.geo = g;
+        k.epi = gate_up ? q4::EPI_SILU : q4::EPI_F16;
+        k.src = s.src;
+        k.after = s.after;
+        k.eps = s.eps;
+    }
+    // outputs overlap no input, no weight and no other output
+    for (int i = 0; i < n; ++i) {
+        const int64_t yb = 2 * (int64_t)st[i].w->n, kb = 2 * (int64_t)st[i].w->k;
+        const void *outs[2] = {st[i].y, st[i].gamma ? st[i].residual_out : nullptr};
+        const int64_t outb[2] = {yb, kb};
+        for (int o = 0; o < 2; ++o) {
+            if (!outs[o])
+                continue;
+            for (int j = 0; j < n; ++j) {
+                const int64_t jk = 2 * (int64_t)st[j].w->k, jy = 2 * (int64_t)st[j].w->n;
+                if (overlap(outs[o], outb[o], st[j].x, jk) || overlap(outs[o], outb[o], st[j].residual, jk) ||
+                    overlap(outs[o], outb[o], st[j].gamma, jk) ||
+                    overlap(outs[o], outb[o], st[j].w->data, st[j].w->bytes))
+                    return Q4_ERR_ALIAS;
+                if (j != i && (overlap(outs[o], outb[o], st[j].y, jy) ||
+                               (st[j].gamma && overlap(outs[o], outb[o], st[j].residual_out, jk))))
+                    return Q4_ERR_ALIAS;
+            }
+        }
+        if (st[i].gamma && st[i].residual_out && overlap(st[i].y, yb, st[i].residual_out, kb))
+            return Q4_ERR_ALIAS;
+    }
+    a->n = n;
+    return Q4_OK;
+}
+
+}  // namespace
+
+int64_t q4_chain_workspace_bytes(const q4_chain_stage *stages, int32_t n_stages)
+{
+    q4::ChainArgs a{};
+    if (chain_check(stages, n_stages, &a) != Q4_OK)
+        return 0;
+    return chain_layout(stages, n_stages).total;
+}
+
+int q4_chain(const q4_chain_stage *stages, int32_t n_stages, void *ws, int64_t ws_bytes, void *stream)
+{
+    q4::ChainArgs a{};
+    int rc = chain_check(stages, n_stages, &a);
+    if (rc != Q4_OK)
+        return rc;
+    const ChainLayout l = chain_layout(stages, n_stages);
+    if (!ws || ws_bytes < l.total)
+        return Q4_ERR_WORKSPACE;
+    if (!aligned(ws, 256))
+        return Q4_ERR_ALIGN;
+    for (int i = 0; i < n_stages; ++i) {
+        const q4_chain_stage &s = stages[i];
+        const int64_t kb = 2 * (int64_t)s.w->k;
+        if (overlap(ws, l.total, s.x, kb) || overlap(ws, l.total, s.residual, kb) ||
+            overlap(ws, l.total, s.gamma, kb) || overlap(ws, l.total, s.w->data, s.w->bytes) ||
+            overlap(ws, l.total, s.y, 2 * (int64_t)s.w->n) ||
+            (s.gamma && overlap(ws, l.total, s.residual_out, kb)))
+            return Q4_ERR_ALIAS;
+    }
+    const int blocks = q4::device_cus();
+    if (blocks > q4::kChainMaxBlocks)
+        return Q4_ERR_SHAPE;
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    a.error = reinterpret_cast<uint32_t *>(base);
+    a.epochs = reinterpret_cast<uint32_t *>(base + l.epochs);
+    for (int i = 0; i < n_stages; ++i) {
+        a.st[i].flags = l.flags[i] >= 0 ? reinterpret_cast<uint32_t *>(base + l.flags[i]) : nullptr;
+        a.st[i].tag = l.tags[i] >= 0 ? reinterpret_cast<uint32_t *>(base + l.tags[i]) : nullptr;
+    }
+    a.wait_ticks = 200000;   // 2 ms of the 100 MHz device clock
+    (void)hipGetLastError();
+    return hip_status(q4::launch_chain(a, blocks, static_cast<hipStream_t>(stream)));
+}
+
+int q4_read_probe(const void *src, int64_t bytes, uint32_t *sink, int64_t sink_bytes, void *stream)
+{
+    if (!src || !sink)
+        return Q4_ERR_NULL;
+    if (bytes < 16 || bytes % 16 != 0)
+        return Q4_ERR_SHAPE;
+    if (!aligned(src, 16) || !aligned(sink, 4))
+        return Q4_ERR_ALIGN;
+    const int cus = q4::device_cus();
+    if (sink_bytes < 4 * q4::read_probe_blocks(bytes, cus))
+        return Q4_ERR_SIZE;
+    if (overlap(sink, sink_bytes, src, bytes))
+        return Q4_ERR_ALIAS;
+    (void)hipGetLastError();
+    return hip_status(q4::launch_read_probe(src, bytes, sink, cus, static_cast<hipStream_t>(stream)));
 }
 
 const char *q4_strerror(int code)

@@ -114,6 +114,67 @@ hipError_t launch_kv_append_int8(const uint16_t *qkv, int32_t nq, int32_t nkv, i
                                  uint8_t *cache8, const int32_t *page_table, int32_t n_pages,
                                  hipStream_t stream);
 
+// Compute units of the current device (hipDeviceAttributeMultiprocessorCount,
+// asked once per device), or 256 -- an MI355X -- when there is no device to
+// ask (host-only sizing queries).  Launch plans size their grids from it.
+int device_cus();
+
+// The plain streaming read (q4_probe.hip): blocks it launches for `bytes`
+// (the sink receives one 32-bit word per block) and the launch.
+int64_t read_probe_blocks(int64_t bytes, int cus);
+hipError_t launch_read_probe(const void *src, int64_t bytes, uint32_t *sink, int cus,
+                             hipStream_t stream);
+
+// ------------------------------------------------------------------ chain --
+// A persistent launch over a sequence of int4 GEMV stages (q4_chain.hip).
+// Stage s reads x (given, or the output of an earlier stage `src`, published
+// with epoch tags), optionally behind the add + RMSNorm prologue, may wait
+// for an earlier stage `after` to be complete, and writes y (f16, or
+// SiLU(g) * u over a gate/up weight).
+constexpr int kChainMaxStages = 6;
+constexpr int kChainWaves = 8;          // wavefronts per block, one block per CU
+constexpr int kChainMaxBlocks = 1024;
+
+// (L, CG) geometries the chain kernel is built for: k from 1568 to 8192.
+enum ChainGeo { CHAIN_G64_1 = 0, CHAIN_G32_3 = 1, CHAIN_G64_2 = 2, CHAIN_G64_3 = 3, CHAIN_G64_4 = 4 };
+int chain_geo_of(const Geometry &geo);   // -1 when the chain kernel has no path for it
+
+struct ChainStageK {
+    const uint8_t *wd;        // packed weight (single pass)
+    const uint16_t *r;        // norm of a dependent x: residual (may be null)
+    const uint16_t *gamma;    // norm of a dependent x: gamma; null = none
+    uint16_t *h_out;          // norm of a dependent x: h = f16(x + r) (may be null)
+    uint16_t *y;              // f16 output [n_out]
+    uint32_t *tag;            // tagged copy of y read by later stages (null: none)
+    uint32_t *flags;          // per-block completion flags of this stage (null: none)
+    int64_t tiles, rows, n_out, k;
+    int32_t geo, epi, src, after;
+    int32_t xoff;             // given x (src < 0): its offset in the staged-x area, in 8-half chunks
+    float eps;
+};
+
+// An input vector given to the chain (x of one or more stages with no src),
+// staged into LDS once at the start of the launch, with its own add +
+// RMSNorm prologue if it has one.
+struct ChainGiven {
+    const uint16_t *x, *r, *gamma;
+    uint16_t *h_out;
+    float eps;
+    int32_t k, off;           // length; offset in the staged-x area, in 8-half chunks
+};
+constexpr int kChainGivenHalves = 16384;   // staged-x area
+
+struct ChainArgs {
+    ChainStageK st[kChainMaxStages];
+    ChainGiven given[kChainMaxStages];
+    int32_t n, n_given;
+    uint32_t *epochs;         // one word per block
+    uint32_t *error;          // set to 1 by a wait that timed out
+    int64_t wait_ticks;       // bound of one wait, in 100 MHz ticks
+};
+
+hipError_t launch_chain(const ChainArgs &a, int blocks, hipStream_t stream);
+
 enum GemmPath { GEMM_PATH_AUTO = 0, GEMM_PATH_VALU = 1, GEMM_PATH_MFMA = 2 };
 
 // Whether the MFMA GEMM kernel takes weights of this geometry (single pass,

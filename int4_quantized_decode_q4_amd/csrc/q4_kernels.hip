@@ -35,26 +35,13 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "q4_device.h"
 #include "q4_geometry.h"
 #include "q4_internal.h"
 #include "q4_lanes.h"
 
 namespace q4 {
 
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
-
-__device__ __forceinline__ uint16_t f16_bits(float v)
-{
-    return __builtin_bit_cast(uint16_t, (_Float16)v);
-}
-
-__device__ __forceinline__ float f16_value(uint16_t b)
-{
-    return (float)__builtin_bit_cast(_Float16, b);
-}
 
 // ---------------------------------------------------------------- packing --
 
@@ -270,15 +257,6 @@ __global__ void unpack3_kernel(const uint8_t *__restrict__ src, int64_t rows, in
 
 // x pairs for one group of 32 k, ordered per word of codes as
 // (x0,x4) (x1,x5) (x2,x6) (x3,x7) to match dot_word's nibble pairs.
-// natural x pairs (x0,x1) (x2,x3) (x4,x5) (x6,x7) of one 8-k word ->
-// (x0,x4) (x1,x5) (x2,x6) (x3,x7), the order the dequant produces
-__device__ __forceinline__ void pair_into(uint32_t *xp, uint4 n)
-{
-    xp[0] = (n.x & 0xFFFFu) | (n.z << 16);
-    xp[1] = (n.x >> 16) | (n.z & 0xFFFF0000u);
-    xp[2] = (n.y & 0xFFFFu) | (n.w << 16);
-    xp[3] = (n.y >> 16) | (n.w & 0xFFFF0000u);
-}
 
 __device__ __forceinline__ void pair3_into(uint32_t *xp, const uint32_t (&n)[16]);
 
@@ -319,57 +297,6 @@ __device__ __forceinline__ void load_x_group(uint32_t *xp, const uint16_t *__res
 // (k <= a few thousand halves, from L2), so no launch or grid barrier is
 // needed; block 0 stores h when the caller asks for it.
 
-__device__ __forceinline__ uint4 residual_add8(uint4 xv, uint4 rv)
-{
-    const uint32_t a[4] = {xv.x, xv.y, xv.z, xv.w}, b[4] = {rv.x, rv.y, rv.z, rv.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const h2 p = as_h2(a[i]), q = as_h2(b[i]);
-        // the f32 sum of two f16 is exact: one rounding, to f16
-        const _Float16 lo = (_Float16)((float)p.x + (float)q.x);
-        const _Float16 hi = (_Float16)((float)p.y + (float)q.y);
-        o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-    }
-    return make_uint4(o[0], o[1], o[2], o[3]);
-}
-
-__device__ __forceinline__ float sumsq8(uint4 v)
-{
-    const uint32_t a[4] = {v.x, v.y, v.z, v.w};
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const h2 p = as_h2(a[i]);
-        s += (float)p.x * (float)p.x;
-        s += (float)p.y * (float)p.y;
-    }
-    return s;
-}
-
-// f16(h * gamma * inv) of 8 halves; h * gamma is exact in f32
-__device__ __forceinline__ uint4 norm8(uint4 hv, uint4 gv, float inv)
-{
-    const uint32_t a[4] = {hv.x, hv.y, hv.z, hv.w}, b[4] = {gv.x, gv.y, gv.z, gv.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const h2 p = as_h2(a[i]), q = as_h2(b[i]);
-        const _Float16 lo = (_Float16)((float)p.x * (float)q.x * inv);
-        const _Float16 hi = (_Float16)((float)p.y * (float)q.y * inv);
-        o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-    }
-    return make_uint4(o[0], o[1], o[2], o[3]);
-}
-
-__device__ __forceinline__ uint4 as_uint4(v4u v) { return make_uint4(v.x, v.y, v.z, v.w); }
-
-__device__ __forceinline__ float inv_rms(float sumsq, int64_t k, float eps)
-{
-    return 1.0f / sqrtf(sumsq / (float)k + eps);
-}
 
 // Sum of one value per thread over the block, in a fixed order (every thread
 // gets the same bits).  scratch: 16 floats of LDS.
@@ -429,50 +356,6 @@ __device__ __forceinline__ void norm_x_group(uint32_t *xp, const uint16_t *__res
     }
 }
 
-// The dequant masks and the f16 exponent pattern, held in VGPRs.  gfx9 VOP3
-// instructions take no literal operands and read at most one SGPR, so with
-// plain constants the compiler splits (w & mask) | magic into a VOP2 and and
-// a VOP2 or (two instructions); from registers it is one v_and_or_b32.
-struct DequantConsts {
-    uint32_t lo, hi, magic;
-};
-
-__device__ __forceinline__ DequantConsts dequant_consts()
-{
-    DequantConsts k;
-    asm("v_mov_b32 %0, 0x000F000F" : "=v"(k.lo));
-    asm("v_mov_b32 %0, 0x00F000F0" : "=v"(k.hi));
-    asm("v_mov_b32 %0, 0x64006400" : "=v"(k.magic));
-    return k;
-}
-
-// 8 codes (canonical nibble order) against their 4 prepared x pairs.
-__device__ __forceinline__ void dot_word(uint32_t w, const uint32_t *xp, float &p1, float &p16,
-                                         const DequantConsts &m)
-{
-    const h2 k1 = {(_Float16)1032.0f, (_Float16)1032.0f};
-    const h2 k16 = {(_Float16)1152.0f, (_Float16)1152.0f};
-    const uint32_t a0 = (w & m.lo) | m.magic;   // 1024 + q0, 1024 + q4
-    const uint32_t a1 = (w & m.hi) | m.magic;   // 1024 + 16 q1, 1024 + 16 q5
-    const uint32_t b = w >> 8;
-    const uint32_t a2 = (b & m.lo) | m.magic;   // q2, q6
-    const uint32_t a3 = (b & m.hi) | m.magic;   // 16 q3, 16 q7
-    p1 = __builtin_amdgcn_fdot2(as_h2(a0) - k1, as_h2(xp[0]), p1, false);
-    p16 = __builtin_amdgcn_fdot2(as_h2(a1) - k16, as_h2(xp[1]), p16, false);
-    p1 = __builtin_amdgcn_fdot2(as_h2(a2) - k1, as_h2(xp[2]), p1, false);
-    p16 = __builtin_amdgcn_fdot2(as_h2(a3) - k16, as_h2(xp[3]), p16, false);
-}
-
-// The 16-byte unit of one (row, group): 4 words of 8 codes.
-__device__ __forceinline__ float dot_unit4(uint4 c, const uint32_t *xp, const DequantConsts &m)
-{
-    float p1 = 0.f, p16 = 0.f;
-    dot_word(c.x, xp + 0, p1, p16, m);
-    dot_word(c.y, xp + 4, p1, p16, m);
-    dot_word(c.z, xp + 8, p1, p16, m);
-    dot_word(c.w, xp + 12, p1, p16, m);
-    return fmaf(p16, 0.0625f, p1);
-}
 
 // int3 (codes 0..7, w = (q - 4) * s).  A group's 32 codes c0..c31 sit in 3
 // device words; word i holds codes 10i + m at bits 3m and 10i + 5 + m at bits
@@ -780,17 +663,6 @@ __device__ __forceinline__ void finish_tile(const float (&acc)[2], int64_t t, in
 #endif
 constexpr int kBlockWaves = Q4_BLOCK_WAVES;
 
-// Buffer resources: a tile (one pass) is addressed through a V# whose
-// num_records is the tile's byte size, or 0 when the wavefront has no such
-// tile; buffer loads past num_records return zeros without touching memory,
-// so prefetches need no branch and the compiler's vmcnt waits stay exact.
-constexpr int kBufferWord3 = 0x00020000;   // gfx9-family raw buffer format
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base, int bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, bytes,
-                                             kBufferWord3);
-}
 
 // Load unit i (u = i / CG, j = i % CG) of a tile into its register slot
 // (int3: 12 bytes, the fourth word unused).
@@ -1214,7 +1086,6 @@ __global__ __launch_bounds__(256) void gemv_multipass_kernel(
 #ifndef Q4_SPLIT_BLOCKS_PER_CU
 #define Q4_SPLIT_BLOCKS_PER_CU 2
 #endif
-constexpr int64_t kCUs = 256;   // MI355X compute units; plans depend on shape only
 
 enum Mode { MODE_SPLIT = 1, MODE_MULTIPASS = 2, MODE_BLOCK = 3 };
 
@@ -1224,9 +1095,11 @@ struct GemvPlan {
     int threads;
 };
 
-// The launch plan depends only on the weight's geometry, so a given shape
-// always runs the same kernel and gives the same bits.
-static GemvPlan plan_gemv(const Geometry &geo)
+// The launch plan depends only on the weight's geometry and the device's
+// compute units.  Every kernel's result is independent of its grid size (a
+// tile's row sums are formed inside one wavefront or added in slot order), so
+// a given shape gives the same bits on any device.
+static GemvPlan plan_gemv(const Geometry &geo, int64_t kCUs)
 {
     if (geo.P > 1) {
         const int64_t waves = geo.tiles < kCUs * 8 ? geo.tiles : kCUs * 8;
@@ -1250,7 +1123,7 @@ static GemvPlan plan_gemv(const Geometry &geo)
 
 int64_t argmax_workspace_bytes(const Geometry &geo)
 {
-    return 8 * plan_gemv(geo).blocks;
+    return 8 * plan_gemv(geo, device_cus()).blocks;
 }
 
 hipError_t launch_pack(const uint32_t *w0, const uint16_t *s0, const uint32_t *w1,
@@ -1351,7 +1224,7 @@ hipError_t launch_gemv3(const Geometry &geo, Epilogue epi, const void *wdata, co
 {
     if (geo.P == 1 && k > kBlockXHalves)
         return hipErrorInvalidValue;
-    const GemvPlan plan = plan_gemv(geo);
+    const GemvPlan plan = plan_gemv(geo, device_cus());
     const uint8_t *wd = static_cast<const uint8_t *>(wdata);
     bool ok = false;
     switch (geo.L) {
@@ -1466,7 +1339,7 @@ hipError_t launch_gemv_family(const Geometry &geo, Epilogue epi, const void *wda
         return hipErrorInvalidValue;
     if (rope != nullptr && (rope->d < 2 || rope->d / 2 > kRopeMaxHalf))
         return hipErrorInvalidValue;
-    const GemvPlan plan = plan_gemv(geo);
+    const GemvPlan plan = plan_gemv(geo, device_cus());
     RopeTab tab{};
     if (rope != nullptr) {
         // the twiddles in f64 on the host, passed to the kernel as f32

@@ -363,3 +363,55 @@ def test_strerror_and_last_error(q4):
     assert len(set(texts.values())) == 9 and all(texts.values())
     assert "unknown" in lib.q4_strerror(-99).decode()
     assert lib.q4_last_hip_error() == 0
+
+
+def test_read_probe_errors(q4):
+    lib = q4.lib
+    S, K = A + 0x100000, A + 0x900000
+    nb = 5320704
+    assert lib.q4_read_probe(None, nb, K, 8192, None) == q4.ERR_NULL
+    assert lib.q4_read_probe(S, nb, None, 8192, None) == q4.ERR_NULL
+    assert lib.q4_read_probe(S, 0, K, 8192, None) == q4.ERR_SHAPE
+    assert lib.q4_read_probe(S, nb + 8, K, 8192, None) == q4.ERR_SHAPE
+    assert lib.q4_read_probe(S + 8, nb, K, 8192, None) == q4.ERR_ALIGN
+    assert lib.q4_read_probe(S, nb, K + 2, 8192, None) == q4.ERR_ALIGN
+    assert lib.q4_read_probe(S, nb, K, 4, None) == q4.ERR_SIZE       # one word, many blocks
+    assert lib.q4_read_probe(S, nb, S + 4096, 8192, None) == q4.ERR_ALIAS
+
+
+def test_chain_errors(q4):
+    lib = q4.lib
+    X, Y, Y2, WS = A + 0x4000000, A + 0x4100000, A + 0x4200000, A + 0x5000000
+    w = weight(q4, n=3072, k=3072)
+    w2 = weight(q4, n=512, k=3072, data=A + 0x2000000)
+    small = weight(q4, n=64, k=1024, data=A + 0x3000000)
+
+    def stages(*specs):
+        arr = (q4.q4_chain_stage * len(specs))()
+        for d, (wt, x, src, after, y) in zip(arr, specs):
+            d.w = ctypes.pointer(wt)
+            d.x, d.src, d.after, d.y = x, src, after, y
+        return arr
+
+    ok = stages((w, X, -1, -1, Y), (w2, None, 0, -1, Y2))
+    need = lib.q4_chain_workspace_bytes(ok, 2)
+    assert need > 0
+    assert lib.q4_chain(ok, 2, WS, need, None) != q4.ERR_NULL   # valid up to the launch
+    assert lib.q4_chain(None, 2, WS, need, None) == q4.ERR_NULL
+    assert lib.q4_chain(ok, 0, WS, need, None) == q4.ERR_SHAPE
+    assert lib.q4_chain(ok, 7, WS, need, None) == q4.ERR_SHAPE
+    assert lib.q4_chain(ok, 2, None, 0, None) == q4.ERR_WORKSPACE
+    assert lib.q4_chain(ok, 2, WS, need - 1, None) == q4.ERR_WORKSPACE
+    assert lib.q4_chain(ok, 2, WS + 128, need, None) == q4.ERR_ALIGN
+    assert lib.q4_chain(ok, 2, X, need, None) == q4.ERR_ALIAS
+    assert lib.q4_chain(stages((w, None, -1, -1, Y),), 1, WS, need, None) == q4.ERR_NULL
+    assert lib.q4_chain(stages((w, X, 0, -1, Y),), 1, WS, need, None) == q4.ERR_SHAPE    # src not earlier
+    assert lib.q4_chain(stages((w, X, -1, 0, Y),), 1, WS, need, None) == q4.ERR_SHAPE    # after not earlier
+    assert lib.q4_chain(stages((w2, X, -1, -1, Y), (w, None, 0, -1, Y2)), 2, WS, need, None) == q4.ERR_SHAPE  # n != k
+    assert lib.q4_chain(stages((small, X, -1, -1, Y),), 1, WS, need, None) == q4.ERR_SHAPE   # k = 1024
+    assert lib.q4_chain(stages((w, X + 8, -1, -1, Y),), 1, WS, need, None) == q4.ERR_ALIGN
+    assert lib.q4_chain(stages((w, X, -1, -1, Y + 2),), 1, WS, need, None) == q4.ERR_ALIGN
+    assert lib.q4_chain(stages((w, X, -1, -1, X),), 1, WS, need, None) == q4.ERR_ALIAS
+    assert lib.q4_chain(stages((w, X, -1, -1, Y), (w2, None, 0, -1, Y)), 2, WS, need, None) == q4.ERR_ALIAS
+    gu = weight(q4, n=3072, k=3072, layout=q4.LAYOUT_ROPE)
+    assert lib.q4_chain(stages((gu, X, -1, -1, Y),), 1, WS, need, None) == q4.ERR_LAYOUT

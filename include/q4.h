@@ -252,6 +252,23 @@ int q4_lmhead_f32(const q4_weight *w, const uint16_t *x, float *logits,
                   int32_t *argmax, void *ws, int64_t ws_bytes, void *stream);
 
 /*
+ * q4_lmhead_f32 for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation, kernels and results, with the argmax candidates kept in a
+ * static device array of the library (64 KiB per GPU, held until the
+ * process ends) instead of a caller workspace.  No hipMalloc, hipFree or
+ * other allocation happens in the call; the first call on a device looks
+ * up the array's address there (hipGetSymbolAddress).  Every call on one
+ * GPU shares that GPU's array, so calls that overlap on one GPU (two
+ * streams, or two host threads) race and must be ordered by the caller.
+ *   w, x, logits, argmax : as q4_lmhead_f32
+ * Errors: as q4_lmhead_f32; WORKSPACE when the candidates would not fit the
+ * 64 KiB array (more than 8192 blocks: never on one MI355X).
+ */
+int q4_lmhead_f32_noalloc(const q4_weight *w, const uint16_t *x, float *logits,
+                          int32_t *argmax, void *stream);
+
+/*
  * Residual add + RMSNorm in front of the matmul, fused into its activation
  * staging ([P1] 内核融合: add_norm merges the residual connection and
  * RMSNorm; here that step also runs inside the QKV or gate/up matmul that

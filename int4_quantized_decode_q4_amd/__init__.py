@@ -85,6 +85,7 @@ _SIGNATURES = {
     "q4_add_rmsnorm_gemv": (ctypes.c_int, [_W, _P, _P, _P, ctypes.c_float, _P, _P, _P]),
     "q4_add_rmsnorm_ffn_gate_up_silu": (ctypes.c_int, [_W, _P, _P, _P, ctypes.c_float, _P, _P, _P]),
     "q4_lmhead_f32": (ctypes.c_int, [_W, _P, _P, _P, _P, _I64, _P]),
+    "q4_lmhead_f32_noalloc": (ctypes.c_int, [_W, _P, _P, _P, _P]),
     "q4_attention_decode": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                            ctypes.c_float, _P, _P, _I64, _P]),
     "q4_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -508,6 +509,18 @@ def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
         ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
+
+
+def lmhead_f32_noalloc(w: PackedWeight, x: torch.Tensor, logits: torch.Tensor,
+                       argmax: Optional[torch.Tensor] = None) -> None:
+    """q4_lmhead_f32 with the argmax candidates in the library's static
+    scratch (q4_lmhead_f32_noalloc): nothing is allocated, so the caller
+    passes the outputs."""
+    px = _dev(x, "x", 2, (w.k,))
+    pl = _dev(logits, "logits", 4, (w.n,))
+    pa = None if argmax is None else _dev(argmax, "argmax", 4, (1,))
+    _check(_lib.q4_lmhead_f32_noalloc(ctypes.byref(w.desc), px, pl, pa, _stream(x)),
+           "q4_lmhead_f32_noalloc")
 
 
 def lmhead_f32(w: PackedWeight, x: torch.Tensor, logits: Optional[torch.Tensor] = None,

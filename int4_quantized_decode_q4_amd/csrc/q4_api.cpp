@@ -118,6 +118,41 @@ int pack_common(const uint32_t *w0, const uint16_t *s0, const uint32_t *w1, cons
 
 }  // namespace
 
+// ------------------------------------------------------- static scratch --
+// The scratch of the allocation-free entry point (q4_lmhead_f32_noalloc):
+// one file-scope device array, present on every GPU the library runs on
+// for the life of the process.  Host code never uses the array's name as an
+// address (on the host it is only a stand-in symbol): its device address is
+// asked for once per device with hipGetSymbolAddress, and that pointer is
+// what the kernels get.
+namespace {
+constexpr int64_t kNoAllocScratchBytes = 64 * 1024;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+std::atomic<void *> g_scratch[kMaxDevices];
+
+// The current device's address of `scratch` (nullptr and *rc = the error on
+// failure).
+void *noalloc_scratch(int *rc)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *rc = hip_status(e != hipSuccess ? e : hipErrorInvalidDevice);
+        return nullptr;
+    }
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            *rc = hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol);
+            return nullptr;
+        }
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+}  // namespace
+
 int q4::device_cus()
 {
     int dev = 0;
@@ -389,8 +424,19 @@ int q4_ffn_gate_up_silu(const q4_weight *w, const uint16_t *x, uint16_t *h, void
                                              static_cast<hipStream_t>(stream)));
 }
 
+// The LM head; scratch = nullptr: the argmax candidates go to the
+// library's static scratch array instead of the caller's workspace.
+static int lmhead_common(const q4_weight *w, const uint16_t *x, float *logits, int32_t *argmax,
+                         void *ws, int64_t ws_bytes, void *stream, bool static_scratch);
+
 int q4_lmhead_f32(const q4_weight *w, const uint16_t *x, float *logits, int32_t *argmax,
                   void *ws, int64_t ws_bytes, void *stream)
+{
+    return lmhead_common(w, x, logits, argmax, ws, ws_bytes, stream, false);
+}
+
+static int lmhead_common(const q4_weight *w, const uint16_t *x, float *logits, int32_t *argmax,
+                         void *ws, int64_t ws_bytes, void *stream, bool static_scratch)
 {
     q4::Geometry geo;
     int64_t rows = 0;
@@ -407,6 +453,16 @@ int q4_lmhead_f32(const q4_weight *w, const uint16_t *x, float *logits, int32_t 
     q4::ArgmaxScratch am{nullptr, nullptr};
     if (argmax) {
         const int64_t need = q4::argmax_workspace_bytes(geo);
+        if (static_scratch) {
+            // the static scratch replaces the workspace: a size check, and
+            // its device address (taken once per device)
+            if (need > kNoAllocScratchBytes)
+                return Q4_ERR_WORKSPACE;
+            ws = noalloc_scratch(&rc);
+            if (!ws)
+                return rc;
+            ws_bytes = kNoAllocScratchBytes;
+        }
         if (!ws || ws_bytes < need)
             return Q4_ERR_WORKSPACE;
         if (!aligned(ws, 256))
@@ -428,6 +484,12 @@ int q4_lmhead_f32(const q4_weight *w, const uint16_t *x, float *logits, int32_t 
                                            static_cast<hipStream_t>(stream)));
     return hip_status(q4::launch_gemv_family(geo, q4::EPI_F32, w->data, x, logits, rows, w->k,
                                              w->n, am, nullptr, nullptr, static_cast<hipStream_t>(stream)));
+}
+
+int q4_lmhead_f32_noalloc(const q4_weight *w, const uint16_t *x, float *logits, int32_t *argmax,
+                          void *stream)
+{
+    return lmhead_common(w, x, logits, argmax, nullptr, 0, stream, true);
 }
 
 // Shared checks of the add + RMSNorm entry points; out is y (gemv) or h

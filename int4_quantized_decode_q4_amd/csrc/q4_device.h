@@ -48,6 +48,14 @@ __device__ __forceinline__ void pair_into(uint32_t *xp, uint4 n)
     xp[3] = (n.y >> 16) | (n.w & 0xFFFF0000u);
 }
 
+// the same permutation as one 16-byte chunk: (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+__device__ __forceinline__ uint4 pair_chunk(uint4 n)
+{
+    uint32_t p[4];
+    pair_into(p, n);
+    return make_uint4(p[0], p[1], p[2], p[3]);
+}
+
 __device__ __forceinline__ uint4 residual_add8(uint4 xv, uint4 rv)
 {
     const uint32_t a[4] = {xv.x, xv.y, xv.z, xv.w}, b[4] = {rv.x, rv.y, rv.z, rv.w};

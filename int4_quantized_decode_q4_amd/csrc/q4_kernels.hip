@@ -742,9 +742,15 @@ __device__ __forceinline__ void lds_x_group(uint32_t *xp, const uint4 *xs, int64
         return;
     }
     if constexpr (FMT == 4) {
+        // staged already paired (pair_chunk)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            pair_into(xp + 4 * q, xs[g * 4 + q]);
+        for (int q = 0; q < 4; ++q) {
+            const uint4 v = xs[g * 4 + q];
+            xp[4 * q] = v.x;
+            xp[4 * q + 1] = v.y;
+            xp[4 * q + 2] = v.z;
+            xp[4 * q + 3] = v.w;
+        }
     } else {
         uint32_t n[16];
 #pragma unroll
@@ -849,12 +855,15 @@ __global__ __launch_bounds__(64 * kBlockWaves) void gemv_block_kernel(
 #pragma unroll
         for (int q = 0; q < kXRounds; ++q)
             if (q < xrounds)
-                xs[threadIdx.x + kThreads * q] = norm8(hv[q], as_uint4(gv[q]), inv);
+                xs[threadIdx.x + kThreads * q] = (FMT == 4)
+                                                      ? pair_chunk(norm8(hv[q], as_uint4(gv[q]), inv))
+                                                      : norm8(hv[q], as_uint4(gv[q]), inv);
     } else {
 #pragma unroll
         for (int q = 0; q < kXRounds; ++q)
             if (q < xrounds)
-                xs[threadIdx.x + kThreads * q] = as_uint4(xv[q]);
+                xs[threadIdx.x + kThreads * q] = (FMT == 4) ? pair_chunk(as_uint4(xv[q]))
+                                                                             : as_uint4(xv[q]);
     }
     __syncthreads();
     uint32_t xp[CG][16];

@@ -639,13 +639,12 @@ def variants(torch, q4, si, np, K, W):
     r3 = Rotation(q4, q4.pack_int3(dev_u32(lw), dev_u16(ls)), copies_for(lm3_bytes))
     lg = torch.empty(32064, dtype=torch.float32, device="cuda")
     am = torch.empty(1, dtype=torch.int32, device="cuda")
-    ws3 = q4.workspace(x3.device, int(q4.lib.q4_workspace_bytes(q4.OP_LMHEAD, 1, 32064, 3072)))
-    usl = per_launch_us(torch, lambda i: q4.lmhead_f32(r3[i], x3, lg, am, ws=ws3), K, W)
+    usl = per_launch_us(torch, lambda i: q4.lmhead_f32(r3[i], x3, lg, am), K, W)
     del r3
     out["int3_ffn_and_lm_head"] = {
         "ffn_us": round(us3, 3), "ffn_gbs": round(gu3_bytes / us3 / 1e3, 1), "ffn_bytes": gu3_bytes,
         "lm_head_us": round(usl, 3), "lm_head_gbs": round(lm3_bytes / usl / 1e3, 1),
-        "lm_head_bytes": lm3_bytes, "lm_head_launches": 2}
+        "lm_head_bytes": lm3_bytes, "lm_head_launches": 1}
 
     # fused gate/up + SiLU, then down
     inp = si.workload(si.FFN, seed=0)

@@ -245,8 +245,13 @@ int q4_ffn_gate_up_silu(const q4_weight *w, const uint16_t *x, uint16_t *h,
  *   argmax : device int32 [1] or NULL; the lowest index holding the maximum
  *            logit (as computed in f32)
  *   ws     : >= q4_workspace_bytes(Q4_OP_LMHEAD, 1, n, k) bytes, 256-byte
- *            aligned, when argmax is not NULL; the argmax then takes a second
- *            small launch on the same stream
+ *            aligned, when argmax is not NULL: each block's candidate and a
+ *            few counters by which the block that finishes last finds out it
+ *            is last and combines the candidates, in the same launch.  The
+ *            counters must be ZERO before the first call on a workspace (a
+ *            zero-filled buffer); each call leaves them zero again, so the
+ *            workspace is then left to LM-head calls (not shared with another
+ *            op's workspace) and calls on it are made in stream order.
  */
 int q4_lmhead_f32(const q4_weight *w, const uint16_t *x, float *logits,
                   int32_t *argmax, void *ws, int64_t ws_bytes, void *stream);
@@ -254,9 +259,10 @@ int q4_lmhead_f32(const q4_weight *w, const uint16_t *x, float *logits,
 /*
  * q4_lmhead_f32 for callers that cannot allocate (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
- * computation, kernels and results, with the argmax candidates kept in a
- * static device array of the library (64 KiB per GPU, held until the
- * process ends) instead of a caller workspace.  No hipMalloc, hipFree or
+ * computation, kernels and results, with the argmax candidates and counters
+ * kept in a static device array of the library (64 KiB per GPU, zero when
+ * the library loads, held until the process ends) instead of a caller
+ * workspace.  No hipMalloc, hipFree or
  * other allocation happens in the call; the first call on a device looks
  * up the array's address there (hipGetSymbolAddress).  Every call on one
  * GPU shares that GPU's array, so calls that overlap on one GPU (two

@@ -511,6 +511,23 @@ def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     return ws
 
 
+_lm_ws: dict = {}
+
+
+def lmhead_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    """The LM head's own workspace on `device`: zero-filled when made, then
+    only used by lmhead_f32 (its counters return to zero after every call);
+    an outgrown one is kept alive, never freed (a graph may hold it)."""
+    key = (device.type, device.index)
+    ws = _lm_ws.get(key)
+    if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            _retired.append(ws)
+        ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        _lm_ws[key] = ws
+    return ws
+
+
 def lmhead_f32_noalloc(w: PackedWeight, x: torch.Tensor, logits: torch.Tensor,
                        argmax: Optional[torch.Tensor] = None) -> None:
     """q4_lmhead_f32 with the argmax candidates in the library's static
@@ -538,7 +555,7 @@ def lmhead_f32(w: PackedWeight, x: torch.Tensor, logits: Optional[torch.Tensor] 
         pa = _dev(argmax, "argmax", 4, (1,))
         need = int(_lib.q4_workspace_bytes(OP_LMHEAD, 1, w.n, w.k))
         if ws is None:
-            ws = workspace(x.device, need)
+            ws = lmhead_workspace(x.device, need)
         pws, nws = _dev(ws, "ws", 1), ws.numel()
     _check(_lib.q4_lmhead_f32(ctypes.byref(w.desc), px, pl, pa, pws, nws, _stream(x)),
            "q4_lmhead_f32")

@@ -472,7 +472,8 @@ static int lmhead_common(const q4_weight *w, const uint16_t *x, float *logits, i
             overlap(argmax, 4, x, 2 * (int64_t)w->k) || overlap(argmax, 4, w->data, w->bytes) ||
             overlap(argmax, 4, logits, lbytes))
             return Q4_ERR_ALIAS;
-        am.partials = static_cast<unsigned long long *>(ws);
+        am.counters = static_cast<uint32_t *>(ws);
+        am.partials = reinterpret_cast<unsigned long long *>(static_cast<uint8_t *>(ws) + q4::kArgmaxCounterBytes);
         am.result = argmax;
     }
     if (overlap(logits, lbytes, x, 2 * (int64_t)w->k) ||

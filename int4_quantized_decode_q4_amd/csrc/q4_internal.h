@@ -53,14 +53,19 @@ struct RopeParam<EPI_ROPE> {
 // Row order of a packed layout: plain, gate/up interleave, rotary pairs.
 enum PackMode { PACK_ROWS = 0, PACK_GATE_UP = 1, PACK_ROPE = 2 };
 
-// Scratch of the LM-head argmax inside the caller's workspace.
+// Scratch of the LM-head argmax inside the caller's workspace: 17 counters
+// of 256 bytes each at the start (at the same place for every weight shape,
+// zero before the first call; every call leaves them zero again), then one
+// 8-byte candidate per launched block.
 struct ArgmaxScratch {
     unsigned long long *partials; // one (f32 bits | index << 32) per block
     int32_t *result;              // device int32 [1]
+    uint32_t *counters;           // the workspace's first kArgmaxCounterBytes
 };
 
-// Bytes of workspace the LM-head argmax needs for a weight of this geometry
-// (one 8-byte candidate per launched block; no initialisation needed).
+constexpr int64_t kArgmaxCounterBytes = 256 * 17;
+
+// Bytes of workspace the LM-head argmax needs for a weight of this geometry.
 int64_t argmax_workspace_bytes(const Geometry &geo);
 
 hipError_t launch_pack(const uint32_t *w0, const uint16_t *s0, const uint32_t *w1,

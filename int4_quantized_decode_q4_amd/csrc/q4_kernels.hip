@@ -497,43 +497,57 @@ __device__ __forceinline__ unsigned long long pack_vi(float v, int i)
            ((unsigned long long)(unsigned int)i << 32);
 }
 
-// Argmax across blocks, step 1: each block publishes its candidate (plain
-// store; the reduce kernel that follows on the stream sees it at the kernel
-// boundary, so no fence or atomic is needed).
+// Argmax across blocks, in the matmul's own launch: each block publishes its
+// candidate and counts itself in; the block that completes the count
+// combines every candidate (max value, then lowest index: the result does
+// not depend on the order they arrive in) and writes the index.  The count
+// is two-level -- 16 counters on separate 256-byte lines, each finished by
+// the last block of its line, which then adds to one top counter -- so no
+// more than (blocks / 16) atomics queue on one address.  A block's candidate
+// store is complete before its atomic (vmcnt wait), and the candidates are
+// read back with device-coherent loads, so no fence is needed; every counter
+// is reset to zero by the block that completes it, ready for the next call.
+constexpr int kArgmaxLines = 16;
+
 __device__ void grid_argmax(float bv, int bi, ArgmaxScratch am)
 {
     __shared__ float sv[16];
     __shared__ int si[16];
+    __shared__ int last;
     block_argmax(bv, bi, sv, si);
-    if (threadIdx.x == 0)
-        am.partials[blockIdx.x] = pack_vi(bv, bi);
-}
-
-// Step 2: one wavefront combines the candidates (max value, then lowest
-// index; the result does not depend on the order they are visited in).  All
-// of a lane's loads in a round are issued before any is used, so the kernel
-// costs about one memory round trip.
-__global__ __launch_bounds__(64) void argmax_reduce_kernel(const unsigned long long *__restrict__ partials,
-                                                           int64_t count, int32_t *__restrict__ result)
-{
-    constexpr int kPerLane = 8;
-    float v = -INFINITY;
-    int i = 0x7fffffff;
-    for (int64_t base = 0; base < count; base += 64 * kPerLane) {
-        unsigned long long pv[kPerLane];
-#pragma unroll
-        for (int q = 0; q < kPerLane; ++q) {
-            const int64_t b = base + q * 64 + threadIdx.x;
-            pv[q] = b < count ? partials[b] : 0x7FFFFFFFFF800000ull;  // (-inf, INT32_MAX)
+    const int nb = gridDim.x, b = blockIdx.x;
+    if (threadIdx.x == 0) {
+        __hip_atomic_store(am.partials + b, pack_vi(bv, bi), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const int line = b % kArgmaxLines;
+        const int lines = nb < kArgmaxLines ? nb : kArgmaxLines;
+        const unsigned in_line = (unsigned)((nb - 1 - line) / kArgmaxLines + 1);
+        uint32_t *ctr = am.counters + 64 * line;
+        int l = 0;
+        if (__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == in_line - 1) {
+            __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            uint32_t *top = am.counters + 64 * kArgmaxLines;
+            if (__hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (unsigned)lines - 1) {
+                __hip_atomic_store(top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                l = 1;
+            }
         }
-#pragma unroll
-        for (int q = 0; q < kPerLane; ++q)
-            better(v, i, __builtin_bit_cast(float, (unsigned int)(pv[q] & 0xFFFFFFFFull)),
-                   (int)(unsigned int)(pv[q] >> 32));
+        last = l;
     }
-    wave_argmax(v, i);
-    if (threadIdx.x == 0)
-        *result = i;
+    __syncthreads();
+    if (last) {
+        float v = -INFINITY;
+        int i = 0x7fffffff;
+        for (int p = threadIdx.x; p < nb; p += blockDim.x) {
+            const unsigned long long k =
+                __hip_atomic_load(am.partials + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            better(v, i, __builtin_bit_cast(float, (unsigned int)(k & 0xFFFFFFFFull)), (int)(unsigned int)(k >> 32));
+        }
+        block_argmax(v, i, sv, si);
+        if (threadIdx.x == 0)
+            *am.result = i;
+    }
 }
 
 // Registers of one pass of one tile: 2*CG code units and 2*CG scales.
@@ -1132,7 +1146,8 @@ static GemvPlan plan_gemv(const Geometry &geo, int64_t kCUs)
 
 int64_t argmax_workspace_bytes(const Geometry &geo)
 {
-    return 8 * plan_gemv(geo, device_cus()).blocks;
+    static_assert(kArgmaxCounterBytes == 256 * (kArgmaxLines + 1), "counter region");
+    return kArgmaxCounterBytes + 8 * plan_gemv(geo, device_cus()).blocks;
 }
 
 hipError_t launch_pack(const uint32_t *w0, const uint16_t *s0, const uint32_t *w1,
@@ -1247,13 +1262,6 @@ hipError_t launch_gemv3(const Geometry &geo, Epilogue epi, const void *wdata, co
     }
     if (!ok)
         return hipErrorInvalidValue;
-    if (epi == EPI_F32 && am.partials != nullptr) {
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-        hipLaunchKernelGGL(argmax_reduce_kernel, dim3(1), dim3(64), 0, stream, am.partials,
-                           plan.blocks, am.result);
-    }
     return hipGetLastError();
 }
 
@@ -1380,13 +1388,6 @@ hipError_t launch_gemv_family(const Geometry &geo, Epilogue epi, const void *wda
     }
     if (!ok)
         return hipErrorInvalidValue;
-    if (epi == EPI_F32 && am.partials != nullptr) {
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-        hipLaunchKernelGGL(argmax_reduce_kernel, dim3(1), dim3(64), 0, stream, am.partials,
-                           plan.blocks, am.result);
-    }
     return hipGetLastError();
 }
 

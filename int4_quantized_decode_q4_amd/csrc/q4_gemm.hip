@@ -13,22 +13,17 @@
 //    serves 8 rows; codes are dequantized once per word (exact q - 8) and
 //    reused for every row.  Multi-pass layouts (k > 8192) use a per-tile
 //    variant that re-reads the x slices of each pass.
-//  * MFMA, small m (m <= 16, or m <= 32 with n < 8192): a block owns 16
-//    weight rows and its 4 wavefronts split the K steps, each an independent
-//    pipeline with its own LDS slice (no block barrier until the final
-//    in-order sum of the 4 partial tiles).
-//  * MFMA, larger m: a block owns 64 or 128 weight rows and BM activation
-//    rows; K is walked in steps of 4 groups (128 k) with a register ring of
-//    steps in flight.
-// In both MFMA kernels each 16-byte unit of codes is dequantized to f16
-// (q - 8) * s (one rounding, relative error <= 2^-11) into LDS, the X slab of
-// the same k range is staged in LDS, and v_mfma_f32_16x16x32_f16 contracts
-// them with f32 accumulation.  Inside each 8-k word the k order in LDS is
-// (0,4,1,5,2,6,3,7) for both operands -- the order the nibble masks produce
-// -- which leaves the contraction unchanged.
+//  * MFMA, m >= 4: the weight-direct kernel.  Each lane loads the 16-byte
+//    unit of codes that is its own A operand (row lane % 16, group slot
+//    lane / 16 of a 4-group K step), dequantizes it to f16 (q - 8) * s (one
+//    rounding, relative error <= 2^-11) in registers, and the step's four
+//    v_mfma_f32_16x16x32_f16 take word w of every unit; only the X slab of
+//    the step, shared by the block's 4 wavefronts, is staged in LDS.  Inside
+//    each 8-k word the k order of both operands is (0,4,1,5,2,6,3,7) -- the
+//    order the nibble masks produce -- which leaves the contraction unchanged.
 // int3 weights (12-byte units of 32 codes, one pass) run through the same
 // kernels with their own dequant: exact (q - 4) pairs on the VALU path, f16
-// (q - 4) * s put back in k order for the MFMA kernels (X is not re-paired).
+// (q - 4) * s put back in k order for the MFMA kernel (X is not re-paired).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -44,6 +39,7 @@ namespace {
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
@@ -199,6 +195,17 @@ __device__ __forceinline__ v4u load_unit_g(__amdgpu_buffer_rsrc_t rs, int off)
         return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
     } else {
         const v3u v = __builtin_amdgcn_raw_buffer_load_b96(rs, off, 0, 0);
+        return v4u{v.x, v.y, v.z, 0u};
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ v4u load_unit_gs(__amdgpu_buffer_rsrc_t rs, int voff, int soff)
+{
+    if constexpr (FMT == 4) {
+        return __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+    } else {
+        const v3u v = __builtin_amdgcn_raw_buffer_load_b96(rs, voff, soff, 0);
         return v4u{v.x, v.y, v.z, 0u};
     }
 }
@@ -506,49 +513,52 @@ __global__ __launch_bounds__(256) void gemm_valu_multipass_kernel(const uint8_t 
 
 // ------------------------------------------------------------ MFMA path --
 
-#ifndef Q4_GEMM_DEPTH_LARGE
-#define Q4_GEMM_DEPTH_LARGE 2
-#endif
 constexpr int kGroupsPerStep = 4;                 // K step: 4 groups = 128 k
 constexpr int kStepK = 32 * kGroupsPerStep;
 constexpr int kLdsRow = kStepK + 8;               // halves per LDS row (+16 B against bank conflicts)
 
-// Block tile BN x BM = (16 NT WN) x (16 MT WM): 4 wavefronts in a WN x WM
-// grid, each owning NT x MT MFMA tiles of 16 x 16.  K steps of 4 groups in
-// layout order (for a row: 4 consecutive 16-byte units, 64 contiguous
-// bytes).  The next step's units, scales and X chunks are loaded into
-// registers while the current step's MFMAs run; dequant and the LDS stores
-// happen between two barriers.
-template <int L, int CG, int NT, int MT, int WN, int WM, int FMT = 4>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint8_t *__restrict__ wd,
-                                                        int64_t wbytes,
-                                                        const uint16_t *__restrict__ X,
-                                                        uint16_t *__restrict__ Y, int64_t m,
-                                                        int64_t n, int64_t k, int64_t nblocks_n,
-                                                        int64_t padded_nblocks_n)
+// Weight-direct MFMA kernel: the weight operand never passes through LDS.
+// The k order inside one v_mfma_f32_16x16x32_f16 is free as long as both
+// operands use the same one, so lane l (row i = l % 16, k block b = l / 16)
+// takes the whole 16-byte unit of weight row i and group slot b of the K
+// step (4 groups = 128 k), and the step's four MFMAs use word w = 0..3 of
+// every lane's unit: MFMA w contracts word w of the step's four groups.
+// Each lane dequantizes its own unit with its own scale straight into the A
+// operand.  The four wavefronts of a block own different weight rows (16 NT
+// each, BN = 64 NT) and share BM = 16 MT activation rows, whose X slab of
+// the step is paired into LDS once per block (double-buffered, one barrier
+// per step) and read back as B operands.  Per step a wavefront does 4 NT MT
+// MFMAs against 4 NT unit dequantizations and 4 MT LDS fragment reads; the
+// per-step part of every load address is uniform and rides in the buffer
+// instruction's scalar offset, so a load costs no address arithmetic.
+template <int L, int CG, int NT, int MT, int FMT = 4>
+__global__ __launch_bounds__(256) void gemm_mfma_wx_kernel(const uint8_t *__restrict__ wd,
+                                                           int64_t wbytes,
+                                                           const uint16_t *__restrict__ X,
+                                                           uint16_t *__restrict__ Y, int64_t m,
+                                                           int64_t n, int64_t k, int64_t nblocks_n,
+                                                           int64_t padded_nblocks_n)
 {
-    static_assert(WN * WM == 4, "four wavefronts");
-    constexpr int BN = 16 * NT * WN, BM = 16 * MT * WM;
+    constexpr int BN = 64 * NT, BM = 16 * MT;
     constexpr int TR = 128 / L;
     constexpr int PB = CG * GFmt<FMT>::PASS;
     constexpr int UB = GFmt<FMT>::UB, US = GFmt<FMT>::US;
-    constexpr int WU = BN * kGroupsPerStep / 256;     // weight units per thread per step
-    constexpr int XC = BM * kGroupsPerStep * 4 / 256; // 16-byte X chunks per thread per step
-    static_assert(WU >= 1 && XC >= 1, "tile too small for 256 threads");
-    constexpr int CBLOCKS = L / kGroupsPerStep;
+    constexpr int CBLOCKS = L / kGroupsPerStep > 0 ? L / kGroupsPerStep : 1;   // L >= 4 on this path
     constexpr int STEPS = CG * CBLOCKS;
-    constexpr int D = BM <= 32 ? 4 : (BM <= 64 ? 2 : Q4_GEMM_DEPTH_LARGE);   // steps in flight
-    __shared__ _Float16 Ws[BN][kLdsRow];
-    __shared__ _Float16 Xs[BM][kLdsRow];
+    constexpr int XC = BM * 16 / 256;                 // 16-byte X chunks per thread per step (MT)
+    // steps in flight: about 112 VGPRs of operands (5 per weight unit and
+    // scale, 4 per X chunk), at least 2, at most the whole K
+    constexpr int PER = 5 * NT + 4 * XC;
+    constexpr int DW = 112 / PER > 2 ? 112 / PER : 2;
+    constexpr int D = DW < STEPS ? DW : (STEPS > 0 ? STEPS : 1);
+    __shared__ _Float16 Xs[2][BM][kLdsRow];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
-    const int wn = wv % WN, wm = wv / WN;
+    const int ri = lane & 15, kb = lane >> 4;
     const int64_t G = k >> 5;
 
-    // XCD-aware order: block ids b, b + 8, b + 16, ... go to the same XCD,
-    // so the M-blocks of one weight slab are spread by a stride of 8 and
-    // share that XCD's L2 for the slab.
+    // XCD-aware order: the M blocks of one weight slab run on one XCD
     const int64_t mblocks = gridDim.x / padded_nblocks_n;
     const int64_t b = blockIdx.x;
     const int64_t grp = b / (8 * mblocks), within = b % (8 * mblocks);
@@ -556,327 +566,194 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint8_t *__restric
     const int64_t mb = within / 8;
     if (nb >= nblocks_n)
         return;
-    const int64_t n0 = nb * BN, mrow0 = mb * BM;
-    const int64_t t0 = n0 / TR;
+    const int64_t nw0 = nb * BN + wv * 16 * NT, mrow0 = mb * BM;
 
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(wd), (short)0, (int)wbytes, 0x00020000);
-    const Masks mk = FMT == 4 ? masks() : Masks{};
-    const Masks3 mk3 = FMT == 3 ? masks3() : Masks3{};
-
-    // per-thread fixed parts of the weight unit addresses
-    int64_t ubase[WU];   // tile byte offset + lane' * US without the (u, j) unit term
-    int64_t sbase[WU];   // tile byte offset of the lane's scale block
-    int urow[WU], ucl[WU], uu[WU];
-#pragma unroll
-    for (int h = 0; h < WU; ++h) {
-        const int q = tid + 256 * h;
-        const int rr = q / kGroupsPerStep, cl = q % kGroupsPerStep;
-        const int64_t tile = t0 + rr / TR;
-        const int sl = (rr % TR) >> 1;
-        urow[h] = rr;
-        ucl[h] = cl;
-        uu[h] = rr & 1;
-        ubase[h] = tile * PB + (int64_t)(sl * L + cl) * US;
-        sbase[h] = tile * PB + 2 * CG * UB + (int64_t)(sl * L + cl) * 4 * CG;
-    }
-
-    // X through a buffer resource too: chunks outside X (rows past m, groups
-    // past k, steps past the end) read as zero without touching memory
     const int xbytes = (int)(m * k * 2);
     const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(X), (short)0, xbytes, 0x00020000);
+    const Masks mk = FMT == 4 ? masks() : Masks{};
+    const Masks3 mk3 = FMT == 3 ? masks3() : Masks3{};
 
-    // D steps of operands kept in flight in registers
-    struct StepRegs {
-        v4u w[WU];
-        uint32_t s[WU];
+    // Per-lane parts of the unit, scale and X offsets (32-bit: this path takes
+    // weights and X below 2 GiB); a step adds a uniform part, passed as the
+    // buffer instruction's scalar offset.  A lane past the end of the weight or
+    // of X gets num_records as its own offset, so it reads zeros whether or not
+    // the scalar offset takes part in the range check.
+    int wvo[NT], svo[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int64_t row = nw0 + 16 * t + ri;
+        const int64_t tile = row / TR;
+        const int sl = (int)((row % TR) >> 1);
+        const int uu = (int)(row & 1);
+        const int64_t uo = tile * PB + (int64_t)uu * CG * UB + (int64_t)(sl * L + kb) * US;
+        const int64_t so = tile * PB + 2 * CG * UB + (int64_t)(sl * L + kb) * 4 * CG + uu * CG * 2;
+        wvo[t] = uo < wbytes ? (int)uo : (int)wbytes;
+        svo[t] = so < wbytes ? (int)so : (int)wbytes;
+    }
+    // X slab of a step: thread q = tid + 256 h takes row q / 16, group slot
+    // cl = (q / 4) % 4, word q % 4 (four threads read one group's 64
+    // contiguous bytes); group slot cl of step (j, cb) is group
+    // (4 cb + cl) CG + j, which exists while 4 cb CG + j < G - cl CG
+    int xvo[XC], xthr[XC];
+#pragma unroll
+    for (int h = 0; h < XC; ++h) {
+        const int q = tid + 256 * h;
+        const int mr = q >> 4, cl = (q >> 2) & 3, wq = q & 3;
+        const int64_t mm = mrow0 + mr;
+        xvo[h] = mm < m ? (int)((mm * k + cl * CG * 32 + wq * 8) * 2) : xbytes;
+        xthr[h] = (int)(G - cl * CG);
+    }
+
+    struct WRegs {
+        v4u w[NT];
+        uint32_t s[NT];
+    };
+    struct XRegs {
         v4u x[XC];
     };
-    StepRegs ring[D];
-    auto load_step = [&](StepRegs &r, int st) {
-        const bool live = st < STEPS;
+    auto load_w = [&](WRegs &r, int st) {
+        if (st >= STEPS)
+            return;                                   // past the end: never used
         const int j = st / CBLOCKS, cb = st % CBLOCKS;
+        const int su = j * UB + cb * kGroupsPerStep * US;
+        const int ss = cb * kGroupsPerStep * 4 * CG + j * 2;
 #pragma unroll
-        for (int h = 0; h < WU; ++h) {
-            const int64_t off = ubase[h] + (int64_t)(uu[h] * CG + j) * UB + cb * kGroupsPerStep * US;
-            const int64_t soff = sbase[h] + (int64_t)cb * kGroupsPerStep * 4 * CG + (uu[h] * CG + j) * 2;
-            // rows past the end of the weight read as zero through the buffer bounds
-            const int wo = (int)(live && off < wbytes ? off : wbytes);
-            const int so = (int)(live && (soff & ~3ll) < wbytes ? (soff & ~3ll) : wbytes);
-            r.w[h] = load_unit_g<FMT>(rs, wo);
-            r.s[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, so, 0, 0) >> ((soff & 2) * 8);
+        for (int t = 0; t < NT; ++t) {
+            r.w[t] = load_unit_gs<FMT>(rs, wvo[t], su);
+            r.s[t] = __builtin_amdgcn_raw_buffer_load_b16(rs, svo[t], ss, 0);
         }
+    };
+    auto load_x = [&](XRegs &r, int st) {
+        if (st >= STEPS)
+            return;
+        const int j = st / CBLOCKS, cb = st % CBLOCKS;
+        const int ug = cb * kGroupsPerStep * CG + j;
+#pragma unroll
+        for (int h = 0; h < XC; ++h)
+            r.x[h] = __builtin_amdgcn_raw_buffer_load_b128(xrs, ug < xthr[h] ? xvo[h] : xbytes, ug * 64, 0);
+    };
+    auto store_x = [&](const XRegs &r, int buf) {
 #pragma unroll
         for (int h = 0; h < XC; ++h) {
             const int q = tid + 256 * h;
-            const int mr = q / (kGroupsPerStep * 4), rest = q % (kGroupsPerStep * 4);
-            const int cl = rest >> 2, wq = rest & 3;
-            const int64_t g = (int64_t)(cb * kGroupsPerStep + cl) * CG + j;
-            const int64_t mm = mrow0 + mr;
-            const int xo = (live && mm < m && g < G) ? (int)((mm * k + g * 32 + wq * 8) * 2) : xbytes;
-            r.x[h] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo, 0, 0);
-        }
-    };
-    auto store_step = [&](const StepRegs &r) {
-#pragma unroll
-        for (int h = 0; h < WU; ++h) {
-            const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(r.s[h] & 0xFFFFu));
-            const h2 sc = {sv, sv};
-            uint4 *dst = reinterpret_cast<uint4 *>(&Ws[urow[h]][ucl[h] * 32]);
-            if constexpr (FMT == 4) {
-                const uint32_t ws4[4] = {r.w[h].x, r.w[h].y, r.w[h].z, r.w[h].w};
-#pragma unroll
-                for (int wq = 0; wq < 4; ++wq) {
-                    h2 a0, a1, a2, a3;
-                    dequant_word_unit(ws4[wq], mk, a0, a1, a2, a3);
-                    // one f16 rounding of (q - 8) * s
-                    dst[wq] = make_uint4(as_u32(a0 * sc), as_u32(a1 * sc), as_u32(a2 * sc), as_u32(a3 * sc));
-                }
-            } else {
-                // one f16 rounding of (q - 4) * s, then back to k order (X stays natural)
-                h2 P[16];
-                dequant_unit3(r.w[h].x, r.w[h].y, r.w[h].z, mk3, P);
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    P[i] = P[i] * sc;
-                uint4 o[4];
-                pairs3_to_k(P, o);
-#pragma unroll
-                for (int wq = 0; wq < 4; ++wq)
-                    dst[wq] = o[wq];
+            {
+                const int mr = q >> 4, cl = (q >> 2) & 3, wq = q & 3;
+                const uint4 xv = make_uint4(r.x[h].x, r.x[h].y, r.x[h].z, r.x[h].w);
+                *reinterpret_cast<uint4 *>(&Xs[buf][mr][cl * 32 + wq * 8]) = FMT == 4 ? pair_word(xv) : xv;
             }
         }
-#pragma unroll
-        for (int h = 0; h < XC; ++h) {
-            const int q = tid + 256 * h;
-            const int mr = q / (kGroupsPerStep * 4), rest = q % (kGroupsPerStep * 4);
-            const int cl = rest >> 2, wq = rest & 3;
-            const uint4 xv = make_uint4(r.x[h].x, r.x[h].y, r.x[h].z, r.x[h].w);
-            *reinterpret_cast<uint4 *>(&Xs[mr][cl * 32 + wq * 8]) = FMT == 4 ? pair_word(xv) : xv;
-        }
     };
-    auto mfma_step = [&](f4 (&acc)[NT][MT]) {
+    auto compute = [&](const WRegs &r, int buf, f4 (&acc)[NT][MT]) {
+        if constexpr (FMT == 4) {
 #pragma unroll
-        for (int ss = 0; ss < kGroupsPerStep; ++ss) {
-            const int kk = ss * 32 + 8 * (lane >> 4);
-            h8 af[NT], bf[MT];
-#pragma unroll
-            for (int i = 0; i < NT; ++i)
-                af[i] = *reinterpret_cast<const h8 *>(&Ws[(wn * NT + i) * 16 + (lane & 15)][kk]);
-#pragma unroll
-            for (int jj = 0; jj < MT; ++jj)
-                bf[jj] = *reinterpret_cast<const h8 *>(&Xs[(wm * MT + jj) * 16 + (lane & 15)][kk]);
-#pragma unroll
-            for (int i = 0; i < NT; ++i)
+            for (int w = 0; w < 4; ++w) {
+                h8 af[NT], bf[MT];
 #pragma unroll
                 for (int jj = 0; jj < MT; ++jj)
-                    acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[jj], acc[i][jj], 0, 0, 0);
+                    bf[jj] = *reinterpret_cast<const h8 *>(&Xs[buf][jj * 16 + ri][kb * 32 + w * 8]);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(r.s[t] & 0xFFFFu));
+                    const h2 sc = {sv, sv};
+                    const uint32_t word = w == 0 ? r.w[t].x : w == 1 ? r.w[t].y : w == 2 ? r.w[t].z : r.w[t].w;
+                    h2 a0, a1, a2, a3;
+                    dequant_word_unit(word, mk, a0, a1, a2, a3);
+                    // one f16 rounding of (q - 8) * s
+                    af[t] = __builtin_bit_cast(h8, make_uint4(as_u32(a0 * sc), as_u32(a1 * sc),
+                                                              as_u32(a2 * sc), as_u32(a3 * sc)));
+                }
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int jj = 0; jj < MT; ++jj)
+                        acc[t][jj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[t], bf[jj], acc[t][jj], 0, 0, 0);
+            }
+        } else {
+            // one f16 rounding of (q - 4) * s, back in k order; X stays natural
+            uint4 ak[NT][4];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(r.s[t] & 0xFFFFu));
+                const h2 sc = {sv, sv};
+                h2 P[16];
+                dequant_unit3(r.w[t].x, r.w[t].y, r.w[t].z, mk3, P);
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    P[q] = P[q] * sc;
+                pairs3_to_k(P, ak[t]);
+            }
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                h8 bf[MT];
+#pragma unroll
+                for (int jj = 0; jj < MT; ++jj)
+                    bf[jj] = *reinterpret_cast<const h8 *>(&Xs[buf][jj * 16 + ri][kb * 32 + w * 8]);
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int jj = 0; jj < MT; ++jj)
+                        acc[t][jj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, ak[t][w]),
+                                                                           bf[jj], acc[t][jj], 0, 0, 0);
+            }
         }
     };
 
     f4 acc[NT][MT];
 #pragma unroll
-    for (int i = 0; i < NT; ++i)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int jj = 0; jj < MT; ++jj)
-            acc[i][jj] = f4{0.f, 0.f, 0.f, 0.f};
-
+            acc[t][jj] = f4{0.f, 0.f, 0.f, 0.f};
+    // W of steps s .. s + D - 1 and X of steps s + 1 .. s + D in registers;
+    // X of step s in LDS buffer s & 1
+    WRegs wr[D];
+    XRegs xr[D];
+    XRegs x0;
+    load_x(x0, 0);
 #pragma unroll
-    for (int i = 0; i < D; ++i)
-        load_step(ring[i], i);
+    for (int i = 0; i < D; ++i) {
+        load_w(wr[i], i);
+        load_x(xr[(i + 1) % D], i + 1);
+    }
+    store_x(x0, 0);
+    __syncthreads();
     for (int st = 0; st < STEPS; st += D) {
 #pragma unroll
         for (int i = 0; i < D; ++i) {
-            if (st + i < STEPS) {
-                __syncthreads();          // the previous step's fragments have been read
-                store_step(ring[i]);
+            const int cur = st + i;
+            if (cur < STEPS) {
+                if (cur + 1 < STEPS)
+                    store_x(xr[(i + 1) % D], (cur + 1) & 1);   // the buffer step cur - 1 read
+                compute(wr[i], cur & 1, acc);
+                load_w(wr[i], cur + D);                        // past the end reads nothing
+                load_x(xr[(i + 1) % D], cur + 1 + D);
                 __syncthreads();
-                load_step(ring[i], st + i + D);   // D steps ahead; past the end reads nothing
-                mfma_step(acc);
             }
         }
     }
-    // D[i][j]: lane holds rows i = 4 (lane / 16) + r (weight rows), column
-    // j = lane % 16 (activation row)
+    // D[i][j]: lane holds weight rows 4 (lane / 16) + r of tile t, activation
+    // row lane % 16 of tile jj
+    const bool vec = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(Y) & 7) == 0;
 #pragma unroll
     for (int jj = 0; jj < MT; ++jj) {
-        const int64_t mm = mrow0 + (wm * MT + jj) * 16 + (lane & 15);
+        const int64_t mm = mrow0 + jj * 16 + ri;
         if (mm >= m)
             continue;
 #pragma unroll
-        for (int i = 0; i < NT; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t nn = n0 + (wn * NT + i) * 16 + 4 * (lane >> 4) + r;
-                if (nn < n)
-                    Y[mm * n + nn] = f16_bits(acc[i][jj][r]);
-            }
-    }
-}
-
-// Small-m MFMA kernel (m <= 32): a block owns 16 weight rows x BM = 16 MT
-// activation rows, and its 4 wavefronts split the K steps (wavefront w takes
-// steps w, w + 4, ...).  Each wavefront is an independent pipeline -- up to
-// six steps of operands in flight in registers, a private LDS slice, no
-// block barrier -- and the four partial sums are added in wavefront order at the
-// end (deterministic).  Many small blocks keep enough weight bytes in flight
-// for the HBM-bound regime.
-template <int L, int CG, int MT, int FMT = 4>
-__global__ __launch_bounds__(256) void gemm_mfma_small_kernel(const uint8_t *__restrict__ wd,
-                                                              int64_t wbytes,
-                                                              const uint16_t *__restrict__ X,
-                                                              uint16_t *__restrict__ Y, int64_t m,
-                                                              int64_t n, int64_t k)
-{
-    constexpr int BM = 16 * MT;
-    constexpr int TR = 128 / L;
-    constexpr int PB = CG * GFmt<FMT>::PASS;
-    constexpr int UB = GFmt<FMT>::UB, US = GFmt<FMT>::US;
-    constexpr int XC = BM * kGroupsPerStep * 4 / 64;   // X chunks per lane per step
-    constexpr int CBLOCKS = L / kGroupsPerStep;
-    constexpr int STEPS = CG * CBLOCKS;
-    // a wavefront with at most 6 steps keeps all of them in flight; longer
-    // K streams 3 steps deep (measured best for k = 3072 and 8192)
-    constexpr int WSTEPS = (STEPS + 3) / 4;
-    constexpr int D = WSTEPS <= 6 ? (WSTEPS > 0 ? WSTEPS : 1) : 3;
-    static_assert(TR <= 16, "16-row blocks need at least 8 lanes per row");
-    __shared__ _Float16 Ws[4][16][kLdsRow];
-    __shared__ _Float16 Xs[4][BM][kLdsRow];
-    __shared__ float red[4][MT][4][64];
-    const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
-    const int64_t G = k >> 5;
-    const int64_t mblocks = (m + BM - 1) / BM;
-    const int64_t nb = blockIdx.x / mblocks, mb = blockIdx.x % mblocks;
-    const int64_t n0 = nb * 16, mrow0 = mb * BM;
-
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(wd), (short)0, (int)wbytes, 0x00020000);
-    const int xbytes = (int)(m * k * 2);
-    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(X), (short)0, xbytes, 0x00020000);
-    const Masks mk = FMT == 4 ? masks() : Masks{};
-    const Masks3 mk3 = FMT == 3 ? masks3() : Masks3{};
-
-    // this lane's weight unit in every step: row lane / 4, group slot lane % 4
-    const int rr = lane >> 2, cl = lane & 3;
-    const int64_t row = n0 + rr;
-    const int64_t tile = row / TR;
-    const int sl = (int)((row % TR) >> 1), uu = (int)(row & 1);
-    const int64_t ubase = tile * PB + (int64_t)(sl * L + cl) * US;
-    const int64_t sbase = tile * PB + 2 * CG * UB + (int64_t)(sl * L + cl) * 4 * CG;
-
-    struct StepRegs {
-        v4u w;
-        uint32_t s;
-        v4u x[XC];
-    };
-    auto load_step = [&](StepRegs &r, int st) {
-        const bool live = st < STEPS;
-        const int j = st / CBLOCKS, cb = st % CBLOCKS;
-        const int64_t off = ubase + (int64_t)(uu * CG + j) * UB + cb * kGroupsPerStep * US;
-        const int64_t soff = sbase + (int64_t)cb * kGroupsPerStep * 4 * CG + (uu * CG + j) * 2;
-        const int wo = (int)(live && off < wbytes ? off : wbytes);
-        const int so = (int)(live && (soff & ~3ll) < wbytes ? (soff & ~3ll) : wbytes);
-        r.w = load_unit_g<FMT>(rs, wo);
-        r.s = __builtin_amdgcn_raw_buffer_load_b32(rs, so, 0, 0) >> ((soff & 2) * 8);
-#pragma unroll
-        for (int h = 0; h < XC; ++h) {
-            const int q = lane + 64 * h;
-            const int mr = q / (kGroupsPerStep * 4), rest = q % (kGroupsPerStep * 4);
-            const int xcl = rest >> 2, wq = rest & 3;
-            const int64_t g = (int64_t)(cb * kGroupsPerStep + xcl) * CG + j;
-            const int64_t mm = mrow0 + mr;
-            const int xo = (live && mm < m && g < G) ? (int)((mm * k + g * 32 + wq * 8) * 2) : xbytes;
-            r.x[h] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo, 0, 0);
-        }
-    };
-    auto run_step = [&](const StepRegs &r, f4 (&acc)[MT]) {
-        {
-            const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(r.s & 0xFFFFu));
-            const h2 sc = {sv, sv};
-            uint4 *dst = reinterpret_cast<uint4 *>(&Ws[wv][rr][cl * 32]);
-            if constexpr (FMT == 4) {
-                const uint32_t ws4[4] = {r.w.x, r.w.y, r.w.z, r.w.w};
-#pragma unroll
-                for (int wq = 0; wq < 4; ++wq) {
-                    h2 a0, a1, a2, a3;
-                    dequant_word_unit(ws4[wq], mk, a0, a1, a2, a3);
-                    dst[wq] = make_uint4(as_u32(a0 * sc), as_u32(a1 * sc), as_u32(a2 * sc), as_u32(a3 * sc));
-                }
+        for (int t = 0; t < NT; ++t) {
+            const int64_t nn = nw0 + 16 * t + 4 * kb;
+            if (vec && nn + 3 < n) {
+                const uint32_t lo = f16_bits(acc[t][jj][0]) | ((uint32_t)f16_bits(acc[t][jj][1]) << 16);
+                const uint32_t hi = f16_bits(acc[t][jj][2]) | ((uint32_t)f16_bits(acc[t][jj][3]) << 16);
+                *reinterpret_cast<uint2 *>(Y + mm * n + nn) = make_uint2(lo, hi);
             } else {
-                h2 P[16];
-                dequant_unit3(r.w.x, r.w.y, r.w.z, mk3, P);
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    P[i] = P[i] * sc;
-                uint4 o[4];
-                pairs3_to_k(P, o);
-#pragma unroll
-                for (int wq = 0; wq < 4; ++wq)
-                    dst[wq] = o[wq];
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < XC; ++h) {
-            const int q = lane + 64 * h;
-            const int mr = q / (kGroupsPerStep * 4), rest = q % (kGroupsPerStep * 4);
-            const int xcl = rest >> 2, wq = rest & 3;
-            const uint4 xv = make_uint4(r.x[h].x, r.x[h].y, r.x[h].z, r.x[h].w);
-            *reinterpret_cast<uint4 *>(&Xs[wv][mr][xcl * 32 + wq * 8]) = FMT == 4 ? pair_word(xv) : xv;
-        }
-        // the wavefront's own LDS slice: its writes must land before its reads
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-        for (int ss = 0; ss < kGroupsPerStep; ++ss) {
-            const int kk = ss * 32 + 8 * (lane >> 4);
-            const h8 a = *reinterpret_cast<const h8 *>(&Ws[wv][lane & 15][kk]);
-#pragma unroll
-            for (int jj = 0; jj < MT; ++jj) {
-                const h8 bx = *reinterpret_cast<const h8 *>(&Xs[wv][jj * 16 + (lane & 15)][kk]);
-                acc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bx, acc[jj], 0, 0, 0);
-            }
-        }
-        // fragments read before the next step overwrites the slice
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    };
-
-    f4 acc[MT];
-#pragma unroll
-    for (int jj = 0; jj < MT; ++jj)
-        acc[jj] = f4{0.f, 0.f, 0.f, 0.f};
-    StepRegs ring[D];
-#pragma unroll
-    for (int i = 0; i < D; ++i)
-        load_step(ring[i], wv + 4 * i);
-    for (int st = wv; st < STEPS; st += 4 * D) {
-#pragma unroll
-        for (int i = 0; i < D; ++i) {
-            const int cur = st + 4 * i;
-            if (cur < STEPS) {
-                run_step(ring[i], acc);
-                load_step(ring[i], cur + 4 * D);   // past the end reads nothing
-            }
-        }
-    }
-#pragma unroll
-    for (int jj = 0; jj < MT; ++jj)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            red[wv][jj][r][lane] = acc[jj][r];
-    __syncthreads();
-    if (wv == 0) {
-#pragma unroll
-        for (int jj = 0; jj < MT; ++jj) {
-            const int64_t mm = mrow0 + jj * 16 + (lane & 15);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float v = ((red[0][jj][r][lane] + red[1][jj][r][lane]) + red[2][jj][r][lane]) +
-                                red[3][jj][r][lane];
-                const int64_t nn = n0 + 4 * (lane >> 4) + r;
-                if (mm < m && nn < n)
-                    Y[mm * n + nn] = f16_bits(v);
+                for (int r = 0; r < 4; ++r)
+                    if (nn + r < n)
+                        Y[mm * n + nn + r] = f16_bits(acc[t][jj][r]);
             }
         }
     }
@@ -919,28 +796,18 @@ hipError_t launch_valu_lc(const Geometry &geo, const uint8_t *wd, const uint16_t
     return hipSuccess;
 }
 
-template <int L, int CG, int NT, int MT, int WN, int WM, int FMT>
-hipError_t launch_mfma_cfg(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
-                           int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
+template <int L, int CG, int NT, int MT, int FMT>
+hipError_t launch_mfma_wx(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
+                          int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
 {
-    constexpr int BN = 16 * NT * WN, BM = 16 * MT * WM;
+    constexpr int BN = 64 * NT, BM = 16 * MT;
     const int64_t nbn = (n + BN - 1) / BN;
-    const int64_t padded = (nbn + 7) / 8 * 8;   // whole groups of 8 for the XCD order
+    const int64_t mbl = (m + BM - 1) / BM;
+    const int64_t padded = mbl > 1 ? (nbn + 7) / 8 * 8 : nbn;
     const int64_t wbytes = geo.tiles * geo.tile_bytes;
-    const dim3 grid((unsigned)(padded * ((m + BM - 1) / BM)));
-    hipLaunchKernelGGL((gemm_mfma_kernel<L, CG, NT, MT, WN, WM, FMT>), grid, dim3(256), 0, stream, wd,
-                       wbytes, X, Y, m, n, k, nbn, padded);
-    return hipGetLastError();
-}
-
-template <int L, int CG, int MT, int FMT>
-hipError_t launch_mfma_small(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
-                             int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
-{
-    const int64_t wbytes = geo.tiles * geo.tile_bytes;
-    const dim3 grid((unsigned)(((n + 15) / 16) * ((m + 16 * MT - 1) / (16 * MT))));
-    hipLaunchKernelGGL((gemm_mfma_small_kernel<L, CG, MT, FMT>), grid, dim3(256), 0, stream, wd, wbytes,
-                       X, Y, m, n, k);
+    const dim3 grid((unsigned)(padded * mbl));
+    hipLaunchKernelGGL((gemm_mfma_wx_kernel<L, CG, NT, MT, FMT>), grid, dim3(256), 0, stream, wd, wbytes,
+                       X, Y, m, n, k, nbn, padded);
     return hipGetLastError();
 }
 
@@ -948,25 +815,19 @@ template <int L, int CG, int FMT>
 hipError_t launch_mfma_lc(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
                           int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
 {
-    // m <= 16: the small kernel always; m <= 32: only while the 64-row tile
-    // kernel would have too few blocks (n < 8192) to stream the weights
-    if (L >= 8 && m <= 16)
-        return launch_mfma_small<L >= 8 ? L : 8, CG, 1, FMT>(geo, wd, X, m, n, k, Y, stream);
-    if (L >= 8 && m <= 32 && n < 8192)
-        return launch_mfma_small<L >= 8 ? L : 8, CG, 2, FMT>(geo, wd, X, m, n, k, Y, stream);
+    // block tiles (64 NT weight rows x 16 MT activation rows) chosen on the
+    // 16384 x 3072 weight, where each keeps 256 blocks or more in flight
+    // (us at m = 4 / 16 / 32 / 64 / 128 / 256: 13.3 / 14.5 / 19.5 / 27.5 /
+    // 37.4 / 52.6)
     if (m <= 16)
-        return launch_mfma_cfg<L, CG, 1, 1, 4, 1, FMT>(geo, wd, X, m, n, k, Y, stream);  // 64 x 16
+        return launch_mfma_wx<L, CG, 1, 1, FMT>(geo, wd, X, m, n, k, Y, stream);
     if (m <= 32)
-        return launch_mfma_cfg<L, CG, 2, 1, 2, 2, FMT>(geo, wd, X, m, n, k, Y, stream);  // 64 x 32
+        return launch_mfma_wx<L, CG, 1, 2, FMT>(geo, wd, X, m, n, k, Y, stream);
     if (m <= 64)
-        return launch_mfma_cfg<L, CG, 2, 2, 2, 2, FMT>(geo, wd, X, m, n, k, Y, stream);  // 64 x 64
-    // up to 128 rows a 128 x 128 tile would leave half the compute units of a
-    // 16384-row weight idle (128 blocks): 128 x 64 takes m = 128 from 57.5 to
-    // 40.3 us; above, 128 x 128 is the faster of the two (60.0 against 63.5 us
-    // at m = 256)
+        return launch_mfma_wx<L, CG, 1, 4, FMT>(geo, wd, X, m, n, k, Y, stream);
     if (m <= 128)
-        return launch_mfma_cfg<L, CG, 4, 2, 2, 2, FMT>(geo, wd, X, m, n, k, Y, stream);  // 128 x 64
-    return launch_mfma_cfg<L, CG, 4, 4, 2, 2, FMT>(geo, wd, X, m, n, k, Y, stream);      // 128 x 128
+        return launch_mfma_wx<L, CG, 2, 4, FMT>(geo, wd, X, m, n, k, Y, stream);
+    return launch_mfma_wx<L, CG, 2, 8, FMT>(geo, wd, X, m, n, k, Y, stream);
 }
 
 template <int L, int FMT>

@@ -21,6 +21,8 @@
 //    the step, shared by the block's 4 wavefronts, is staged in LDS.  Inside
 //    each 8-k word the k order of both operands is (0,4,1,5,2,6,3,7) -- the
 //    order the nibble masks produce -- which leaves the contraction unchanged.
+//    For m <= 16 and k <= 4096 a variant keeps the whole X in LDS, so its
+//    wavefronts stream the weight with no barrier after the first.
 // int3 weights (12-byte units of 32 codes, one pass) run through the same
 // kernels with their own dequant: exact (q - 4) pairs on the VALU path, f16
 // (q - 4) * s put back in k order for the MFMA kernel (X is not re-paired).
@@ -759,6 +761,159 @@ __global__ __launch_bounds__(256) void gemm_mfma_wx_kernel(const uint8_t *__rest
     }
 }
 
+// X-resident MFMA kernel for m <= 16 and k <= 4096: the whole X (16 rows,
+// paired as the weight-direct kernel pairs it) is staged in LDS once, and
+// each of the block's 4 wavefronts then streams the units of its own 16
+// weight rows over the whole of K with no further barrier: the unit loads of
+// up to 16 K steps are in flight in registers, each lane dequantizes its own
+// unit into the A operand as in the weight-direct kernel, and the B operands
+// are read from the resident X.  One block (64 weight rows) per CU: the X
+// copy takes most of the LDS.
+constexpr int kXresMaxK = 4096;               // groups of the layout (L CG) x 32 <= this
+constexpr int kXresRow = kXresMaxK + 8;       // halves per LDS row (+16 B: rows 4 banks apart)
+
+template <int L, int CG, int FMT = 4>
+__global__ __launch_bounds__(256) void gemm_mfma_xres_kernel(const uint8_t *__restrict__ wd,
+                                                             int64_t wbytes,
+                                                             const uint16_t *__restrict__ X,
+                                                             uint16_t *__restrict__ Y, int64_t m,
+                                                             int64_t n, int64_t k)
+{
+    constexpr int TR = 128 / L;
+    constexpr int PB = CG * GFmt<FMT>::PASS;
+    constexpr int UB = GFmt<FMT>::UB, US = GFmt<FMT>::US;
+    constexpr int CBLOCKS = L / kGroupsPerStep > 0 ? L / kGroupsPerStep : 1;   // L >= 4 on this path
+    constexpr int STEPS = CG * CBLOCKS;
+    constexpr int D = STEPS < 12 ? (STEPS > 0 ? STEPS : 1) : 12;     // steps of units in flight
+    constexpr int KL = L * CG * 32;                                  // k of the layout (>= k)
+    __shared__ _Float16 Xs[16][kXresRow];
+    if constexpr (KL > kXresMaxK)
+        return;                       // never launched for such a layout (the launcher checks)
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const int ri = lane & 15, kb = lane >> 4;
+    const int64_t nw0 = (int64_t)blockIdx.x * 64 + wv * 16;
+
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(wd), (short)0, (int)wbytes, 0x00020000);
+    const int xbytes = (int)(m * k * 2);
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(X), (short)0, xbytes, 0x00020000);
+    const Masks mk = FMT == 4 ? masks() : Masks{};
+    const Masks3 mk3 = FMT == 3 ? masks3() : Masks3{};
+
+    // per-lane unit and scale offsets of weight row nw0 + ri, group slot kb;
+    // a step adds a uniform part (scalar offset); rows past the weight read zero
+    int wvo, svo;
+    {
+        const int64_t row = nw0 + ri;
+        const int64_t tile = row / TR;
+        const int sl = (int)((row % TR) >> 1);
+        const int uu = (int)(row & 1);
+        const int64_t uo = tile * PB + (int64_t)uu * CG * UB + (int64_t)(sl * L + kb) * US;
+        const int64_t so = tile * PB + 2 * CG * UB + (int64_t)(sl * L + kb) * 4 * CG + uu * CG * 2;
+        wvo = uo < wbytes ? (int)uo : (int)wbytes;
+        svo = so < wbytes ? (int)so : (int)wbytes;
+    }
+    struct WRegs {
+        v4u w;
+        uint32_t s;
+    };
+    auto load_w = [&](WRegs &r, int st) {
+        if (st >= STEPS)
+            return;                                   // past the end: never used
+        const int j = st / CBLOCKS, cb = st % CBLOCKS;
+        r.w = load_unit_gs<FMT>(rs, wvo, j * UB + cb * kGroupsPerStep * US);
+        r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, svo, cb * kGroupsPerStep * 4 * CG + j * 2, 0);
+    };
+    // X into LDS once: 16 rows x KL halves in 16-byte chunks, rows past m and
+    // groups past k as zeros (int4: paired per 8-k word; int3: natural).  All
+    // of a thread's chunk loads are issued first, then the weight units of
+    // the first D steps, so the X stores wait only for the X loads
+    constexpr int NCH = 16 * (KL / 8);
+    constexpr int PERT = (NCH + 255) / 256 > 0 ? (NCH + 255) / 256 : 1;
+    v4u xv[PERT];
+#pragma unroll
+    for (int h = 0; h < PERT; ++h) {
+        const int q = tid + 256 * h;
+        const int r = q / (KL / 8), ch = q % (KL / 8);
+        const int xo = (q < NCH && r < m && ch * 8 < k) ? (int)(((int64_t)r * k + ch * 8) * 2) : xbytes;
+        xv[h] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo, 0, 0);
+    }
+    WRegs ring[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        load_w(ring[i], i);
+#pragma unroll
+    for (int h = 0; h < PERT; ++h) {
+        const int q = tid + 256 * h;
+        if (q < NCH) {
+            const int r = q / (KL / 8), ch = q % (KL / 8);
+            const uint4 v = make_uint4(xv[h].x, xv[h].y, xv[h].z, xv[h].w);
+            *reinterpret_cast<uint4 *>(&Xs[r][ch * 8]) = FMT == 4 ? pair_word(v) : v;
+        }
+    }
+    __syncthreads();
+
+    f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+    for (int st = 0; st < STEPS; st += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            const int cur = st + i;
+            if (cur < STEPS) {
+                const int j = cur / CBLOCKS, cb = cur % CBLOCKS;
+                const int g = (cb * kGroupsPerStep + kb) * CG + j;   // this lane's group
+                const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(ring[i].s & 0xFFFFu));
+                const h2 sc = {sv, sv};
+                if constexpr (FMT == 4) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const uint32_t word = w == 0 ? ring[i].w.x : w == 1 ? ring[i].w.y
+                                            : w == 2 ? ring[i].w.z : ring[i].w.w;
+                        h2 a0, a1, a2, a3;
+                        dequant_word_unit(word, mk, a0, a1, a2, a3);
+                        // one f16 rounding of (q - 8) * s
+                        const h8 af = __builtin_bit_cast(h8, make_uint4(as_u32(a0 * sc), as_u32(a1 * sc),
+                                                                        as_u32(a2 * sc), as_u32(a3 * sc)));
+                        const h8 bf = *reinterpret_cast<const h8 *>(&Xs[ri][g * 32 + w * 8]);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc, 0, 0, 0);
+                    }
+                } else {
+                    // one f16 rounding of (q - 4) * s, back in k order; X natural
+                    h2 P[16];
+                    dequant_unit3(ring[i].w.x, ring[i].w.y, ring[i].w.z, mk3, P);
+#pragma unroll
+                    for (int q = 0; q < 16; ++q)
+                        P[q] = P[q] * sc;
+                    uint4 ak[4];
+                    pairs3_to_k(P, ak);
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const h8 bf = *reinterpret_cast<const h8 *>(&Xs[ri][g * 32 + w * 8]);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, ak[w]), bf, acc, 0, 0, 0);
+                    }
+                }
+                load_w(ring[i], cur + D);
+            }
+        }
+    }
+    // lane holds weight rows 4 (lane / 16) + r, activation row lane % 16
+    if (ri < m) {
+        const int64_t nn = nw0 + 4 * kb;
+        if ((n & 3) == 0 && (reinterpret_cast<uintptr_t>(Y) & 7) == 0 && nn + 3 < n) {
+            const uint32_t lo = f16_bits(acc[0]) | ((uint32_t)f16_bits(acc[1]) << 16);
+            const uint32_t hi = f16_bits(acc[2]) | ((uint32_t)f16_bits(acc[3]) << 16);
+            *reinterpret_cast<uint2 *>(Y + ri * n + nn) = make_uint2(lo, hi);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (nn + r < n)
+                    Y[ri * n + nn + r] = f16_bits(acc[r]);
+        }
+    }
+}
+
 template <int L, int CG, int FMT>
 hipError_t launch_valu_lc(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
                           int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
@@ -812,13 +967,27 @@ hipError_t launch_mfma_wx(const Geometry &geo, const uint8_t *wd, const uint16_t
 }
 
 template <int L, int CG, int FMT>
+hipError_t launch_mfma_xres(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
+                            int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
+{
+    const int64_t wbytes = geo.tiles * geo.tile_bytes;
+    hipLaunchKernelGGL((gemm_mfma_xres_kernel<L, CG, FMT>), dim3((unsigned)((n + 63) / 64)), dim3(256), 0,
+                       stream, wd, wbytes, X, Y, m, n, k);
+    return hipGetLastError();
+}
+
+template <int L, int CG, int FMT>
 hipError_t launch_mfma_lc(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
                           int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
 {
-    // block tiles (64 NT weight rows x 16 MT activation rows) chosen on the
-    // 16384 x 3072 weight, where each keeps 256 blocks or more in flight
-    // (us at m = 4 / 16 / 32 / 64 / 128 / 256: 13.3 / 14.5 / 19.5 / 27.5 /
-    // 37.4 / 52.6)
+    // m <= 16 with k <= 4096: X resident in LDS (16384 x 3072, m = 16: 13.4
+    // against 14.4 us for the weight-direct kernel); otherwise block tiles of
+    // 64 NT weight rows x 16 MT activation rows chosen on the 16384 x 3072
+    // weight, each keeping 256 blocks in flight (us at m = 32 / 64 / 128 /
+    // 256: 19.2 / 27.5 / 37.1 / 52.0; 64-row slabs with more, shorter M
+    // blocks -- 512 blocks, two per CU -- were slower: 28.3 / 40.4 / 63.7)
+    if (m <= 16 && L * CG * 32 <= kXresMaxK)
+        return launch_mfma_xres<L, CG, FMT>(geo, wd, X, m, n, k, Y, stream);
     if (m <= 16)
         return launch_mfma_wx<L, CG, 1, 1, FMT>(geo, wd, X, m, n, k, Y, stream);
     if (m <= 32)

@@ -465,30 +465,40 @@ __device__ __forceinline__ void better(float &bv, int &bi, float ov, int oi)
     }
 }
 
+// (max, lowest index) over the lanes of a wavefront whose lane index is a
+// multiple of STRIDE (the other lanes hold no candidate): the xor steps of
+// STRIDE and above only, so a GEMV kernel whose rows are finished by lane
+// c == 0 of each L-lane row group takes log2(64 / L) steps instead of 6
+template <int STRIDE>
 __device__ __forceinline__ void wave_argmax(float &bv, int &bi)
 {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
+    for (int off = 32; off >= STRIDE; off >>= 1) {
         const float ov = __shfl_xor(bv, off);
         const int oi = __shfl_xor(bi, off);
         better(bv, bi, ov, oi);
     }
 }
 
-// Block-wide (max, lowest index) of per-thread candidates; result in thread 0.
+// Block-wide (max, lowest index) of per-thread candidates over a block of
+// NWAVES wavefronts; result in thread 0.  The caller orders any later use of
+// sv / si (a block barrier).  The wave count is a template constant: reading
+// blockDim.x costs a load from the dispatch packet, and waiting for it waited
+// for every store the wavefront still had in flight.
+template <int STRIDE, int NWAVES>
 __device__ void block_argmax(float &bv, int &bi, float *sv, int *si)
 {
-    wave_argmax(bv, bi);
-    const int wid = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+    wave_argmax<STRIDE>(bv, bi);
+    const int wid = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) {
         sv[wid] = bv;
         si[wid] = bi;
     }
     __syncthreads();
     if (threadIdx.x == 0)
-        for (int w = 1; w < nwaves; ++w)
+#pragma unroll
+        for (int w = 1; w < NWAVES; ++w)
             better(bv, bi, sv[w], si[w]);
-    __syncthreads();
 }
 
 __device__ __forceinline__ unsigned long long pack_vi(float v, int i)
@@ -509,12 +519,14 @@ __device__ __forceinline__ unsigned long long pack_vi(float v, int i)
 // is reset to zero by the block that completes it, ready for the next call.
 constexpr int kArgmaxLines = 16;
 
+template <int STRIDE, int NWAVES>
 __device__ void grid_argmax(float bv, int bi, ArgmaxScratch am)
 {
+    static_assert(NWAVES <= 16, "one LDS slot per wavefront");
     __shared__ float sv[16];
     __shared__ int si[16];
     __shared__ int last;
-    block_argmax(bv, bi, sv, si);
+    block_argmax<STRIDE, NWAVES>(bv, bi, sv, si);
     const int nb = gridDim.x, b = blockIdx.x;
     if (threadIdx.x == 0) {
         __hip_atomic_store(am.partials + b, pack_vi(bv, bi), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -539,12 +551,12 @@ __device__ void grid_argmax(float bv, int bi, ArgmaxScratch am)
     if (last) {
         float v = -INFINITY;
         int i = 0x7fffffff;
-        for (int p = threadIdx.x; p < nb; p += blockDim.x) {
+        for (int p = threadIdx.x; p < nb; p += 64 * NWAVES) {
             const unsigned long long k =
                 __hip_atomic_load(am.partials + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             better(v, i, __builtin_bit_cast(float, (unsigned int)(k & 0xFFFFFFFFull)), (int)(unsigned int)(k >> 32));
         }
-        block_argmax(v, i, sv, si);
+        block_argmax<1, NWAVES>(v, i, sv, si);
         if (threadIdx.x == 0)
             *am.result = i;
     }
@@ -903,7 +915,7 @@ __global__ __launch_bounds__(64 * kBlockWaves) void gemv_block_kernel(
         }
     }
     if (EPI == EPI_F32 && am.partials != nullptr)
-        grid_argmax(bv, bi, am);
+        grid_argmax<L, kBlockWaves>(bv, bi, am);   // candidates in lanes c == 0
 }
 
 // Split kernel (single-pass weights, long k, few tiles): a block of CG
@@ -1026,7 +1038,7 @@ __global__ __launch_bounds__(64 * CG) void gemv_split_kernel(
         store_rows<EPI>(y0, y1, t * TR + 2 * ss, out, rows, n_out, bv, bi, rp);
     }
     if (EPI == EPI_F32 && am.partials != nullptr)
-        grid_argmax(bv, bi, am);
+        grid_argmax<1, CG>(bv, bi, am);   // candidates in any thread; CG wavefronts
 }
 
 // Multi-pass kernel (k > 8192): a grid-stride loop over tiles that reloads
@@ -1092,7 +1104,7 @@ __global__ __launch_bounds__(256) void gemv_multipass_kernel(
         finish_tile<L, EPI>(acc, t, s, c, out, rows, n_out, bv, bi, rp);
     }
     if (EPI == EPI_F32 && am.partials != nullptr)
-        grid_argmax(bv, bi, am);
+        grid_argmax<L, 4>(bv, bi, am);   // candidates in lanes c == 0; 256 threads
 }
 
 // ----------------------------------------------------------------- launch --

@@ -13,16 +13,20 @@
 //    serves 8 rows; codes are dequantized once per word (exact q - 8) and
 //    reused for every row.  Multi-pass layouts (k > 8192) use a per-tile
 //    variant that re-reads the x slices of each pass.
-//  * MFMA, m >= 4: the weight-direct kernel.  Each lane loads the 16-byte
-//    unit of codes that is its own A operand (row lane % 16, group slot
-//    lane / 16 of a 4-group K step), dequantizes it to f16 (q - 8) * s (one
-//    rounding, relative error <= 2^-11) in registers, and the step's four
-//    v_mfma_f32_16x16x32_f16 take word w of every unit; only the X slab of
-//    the step, shared by the block's 4 wavefronts, is staged in LDS.  Inside
-//    each 8-k word the k order of both operands is (0,4,1,5,2,6,3,7) -- the
-//    order the nibble masks produce -- which leaves the contraction unchanged.
-//    For m <= 16 and k <= 4096 a variant keeps the whole X in LDS, so its
-//    wavefronts stream the weight with no barrier after the first.
+//  * MFMA, 4 <= m <= 128: the K-split kernel.  A block owns 64 weight rows
+//    and up to 128 activation rows; its wavefronts split K, each staging its
+//    own X slices in its own LDS region (no block barrier until the end,
+//    where the partial tiles are added in wavefront order).  Each lane loads
+//    the 16-byte unit of codes that is its own A operand of
+//    v_mfma_f32_32x32x16_f16 (row lane % 32, one of two groups by lane / 32)
+//    and dequantizes it to f16 (q - 8) * s (one rounding, relative error
+//    <= 2^-11) in registers; the step's four MFMAs take word w of every unit.
+//    Inside each 8-k word the k order of both operands is (0,4,1,5,2,6,3,7)
+//    -- the order the nibble masks produce -- which leaves the contraction
+//    unchanged.
+//  * MFMA, m > 128: the weight-direct kernel, the same operand scheme on
+//    v_mfma_f32_16x16x32_f16 with 128 x 128 block tiles whose X slab of a
+//    step is shared by the block's 4 wavefronts (X is read half as often).
 // int3 weights (12-byte units of 32 codes, one pass) run through the same
 // kernels with their own dequant: exact (q - 4) pairs on the VALU path, f16
 // (q - 4) * s put back in k order for the MFMA kernel (X is not re-paired).
@@ -188,6 +192,7 @@ struct GFmt {
     static constexpr int PASS = 2 * UB + 256;   // bytes per group slot per pass (x CG)
 };
 
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef unsigned v3u __attribute__((ext_vector_type(3)));
 
 template <int FMT>
@@ -761,39 +766,62 @@ __global__ __launch_bounds__(256) void gemm_mfma_wx_kernel(const uint8_t *__rest
     }
 }
 
-// X-resident MFMA kernel for m <= 16 and k <= 4096: the whole X (16 rows,
-// paired as the weight-direct kernel pairs it) is staged in LDS once, and
-// each of the block's 4 wavefronts then streams the units of its own 16
-// weight rows over the whole of K with no further barrier: the unit loads of
-// up to 16 K steps are in flight in registers, each lane dequantizes its own
-// unit into the A operand as in the weight-direct kernel, and the B operands
-// are read from the resident X.  One block (64 weight rows) per CU: the X
-// copy takes most of the LDS.
-constexpr int kXresMaxK = 4096;               // groups of the layout (L CG) x 32 <= this
-constexpr int kXresRow = kXresMaxK + 8;       // halves per LDS row (+16 B: rows 4 banks apart)
-
-template <int L, int CG, int FMT = 4>
-__global__ __launch_bounds__(256) void gemm_mfma_xres_kernel(const uint8_t *__restrict__ wd,
-                                                             int64_t wbytes,
-                                                             const uint16_t *__restrict__ X,
-                                                             uint16_t *__restrict__ Y, int64_t m,
-                                                             int64_t n, int64_t k)
+// K-split MFMA kernel (v_mfma_f32_32x32x16_f16).  A block owns 64 weight
+// rows (two A tiles of 32) and BM = 32 MT activation rows, and its NW
+// wavefronts split K instead of the rows: wavefront w takes a contiguous
+// run of the row's steps, a step being one group pair (c, c + 1) of lane
+// positions at one group slot j -- groups (2p) CG + j and (2p + 1) CG + j.
+// Lane l (row l % 32 of a tile, half h = l / 32) loads the 16-byte unit of
+// its row and of group 2p + h (so each row's two units of a step are 32
+// contiguous bytes), dequantizes it to f16 (q - 8) * s in registers, and
+// the step's MFMAs take word w = 0..3 of every unit; the B operand of word
+// w, half h, is the same 8 k of activation row l % 32 (paired as the codes
+// are).  Each wavefront stages its own X slab of a step (BM rows x the two
+// groups) in its own LDS region and reads it back as B operands, so no
+// block barrier is needed until the end, where the NW partial tiles are
+// added in wavefront order through the same LDS and rounded once to f16.
+// Per step a wavefront does 8 MT MFMAs against 8 dequantized words and
+// 4 MT LDS fragment reads; every weight byte is dequantized once per M
+// block, every X byte passes through LDS once per weight slab.
+template <int L, int CG, int MT, int NW, int D, int FMT = 4>
+__global__ __launch_bounds__(64 * NW) void gemm_mfma_ks_kernel(const uint8_t *__restrict__ wd,
+                                                               int64_t wbytes,
+                                                               const uint16_t *__restrict__ X,
+                                                               uint16_t *__restrict__ Y, int64_t m,
+                                                               int64_t n, int64_t k, int64_t nblocks_n,
+                                                               int64_t padded_nblocks_n)
 {
+    constexpr int BM = 32 * MT;
     constexpr int TR = 128 / L;
     constexpr int PB = CG * GFmt<FMT>::PASS;
     constexpr int UB = GFmt<FMT>::UB, US = GFmt<FMT>::US;
-    constexpr int CBLOCKS = L / kGroupsPerStep > 0 ? L / kGroupsPerStep : 1;   // L >= 4 on this path
-    constexpr int STEPS = CG * CBLOCKS;
-    constexpr int D = STEPS < 12 ? (STEPS > 0 ? STEPS : 1) : 12;     // steps of units in flight
-    constexpr int KL = L * CG * 32;                                  // k of the layout (>= k)
-    __shared__ _Float16 Xs[16][kXresRow];
-    if constexpr (KL > kXresMaxK)
-        return;                       // never launched for such a layout (the launcher checks)
+    constexpr int NP = L / 2;                        // lane-position pairs of a row (L >= 4 here)
+    constexpr int PW = NP > NW ? (NP + NW - 1) / NW : 1;   // pairs per wavefront
+    constexpr int SW = PW * CG;                      // steps per wavefront: (pair, slot), slot fastest
+    constexpr int XROW = 64 + 8;                     // halves per slab row (+16 B: rows 4 banks apart)
+    constexpr int XBUF = BM * XROW;                  // halves per slab buffer
+    constexpr int PROW = 64 + 4;                     // floats per row of a partial tile
+    constexpr int REGION = 4 * XBUF > 4 * BM * PROW ? 4 * XBUF : 4 * BM * PROW;   // bytes per wavefront
+    constexpr int XC = BM / 8;                       // 16-byte X pieces per lane per step
+    constexpr int OPT = BM / NW;                     // outputs per thread in the final sum
+    static_assert((OPT == 2 || OPT % 4 == 0) && 64 % OPT == 0 && D >= 2, "unsupported BM / NW / D");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[NW * REGION];
+
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wv = tid >> 6;
-    const int ri = lane & 15, kb = lane >> 4;
-    const int64_t nw0 = (int64_t)blockIdx.x * 64 + wv * 16;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ri = lane & 31, kh = lane >> 5;
+    const int64_t G = k >> 5;
+
+    // XCD-aware order: the M blocks of one weight slab run on one XCD
+    const int64_t mblocks = gridDim.x / padded_nblocks_n;
+    const int64_t b = blockIdx.x;
+    const int64_t grp = b / (8 * mblocks), within = b % (8 * mblocks);
+    const int64_t nb = grp * 8 + within % 8;
+    const int64_t mb = within / 8;
+    if (nb >= nblocks_n)
+        return;
+    const int64_t n0 = nb * 64, m0 = mb * BM;
 
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(wd), (short)0, (int)wbytes, 0x00020000);
@@ -803,114 +831,235 @@ __global__ __launch_bounds__(256) void gemm_mfma_xres_kernel(const uint8_t *__re
     const Masks mk = FMT == 4 ? masks() : Masks{};
     const Masks3 mk3 = FMT == 3 ? masks3() : Masks3{};
 
-    // per-lane unit and scale offsets of weight row nw0 + ri, group slot kb;
-    // a step adds a uniform part (scalar offset); rows past the weight read zero
-    int wvo, svo;
-    {
-        const int64_t row = nw0 + ri;
+    // per-lane unit and scale offsets (lane position c = h of pair 0, slot
+    // j = 0); a step (p, j) adds the uniform 2p US + j UB (units) and a pair
+    // 2p 4 CG (its scale block: the 4 CG bytes of both rows of a lane pair
+    // and every slot) through the scalar offset; rows past n read zero
+    int wvo[2], svo[2], shalf[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int64_t row = n0 + 32 * t + ri;
         const int64_t tile = row / TR;
         const int sl = (int)((row % TR) >> 1);
         const int uu = (int)(row & 1);
-        const int64_t uo = tile * PB + (int64_t)uu * CG * UB + (int64_t)(sl * L + kb) * US;
-        const int64_t so = tile * PB + 2 * CG * UB + (int64_t)(sl * L + kb) * 4 * CG + uu * CG * 2;
-        wvo = uo < wbytes ? (int)uo : (int)wbytes;
-        svo = so < wbytes ? (int)so : (int)wbytes;
+        const int64_t uo = tile * PB + (int64_t)uu * CG * UB + (int64_t)(sl * L + kh) * US;
+        const int64_t so = tile * PB + 2 * CG * UB + (int64_t)(sl * L + kh) * 4 * CG;
+        wvo[t] = (row < n && uo < wbytes) ? (int)uo : (int)wbytes;
+        svo[t] = (row < n && so < wbytes) ? (int)so : (int)wbytes;
+        shalf[t] = uu * CG;                          // this row's first half in the block
     }
-    struct WRegs {
-        v4u w;
-        uint32_t s;
-    };
-    auto load_w = [&](WRegs &r, int st) {
-        if (st >= STEPS)
-            return;                                   // past the end: never used
-        const int j = st / CBLOCKS, cb = st % CBLOCKS;
-        r.w = load_unit_gs<FMT>(rs, wvo, j * UB + cb * kGroupsPerStep * US);
-        r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, svo, cb * kGroupsPerStep * 4 * CG + j * 2, 0);
-    };
-    // X into LDS once: 16 rows x KL halves in 16-byte chunks, rows past m and
-    // groups past k as zeros (int4: paired per 8-k word; int3: natural).  All
-    // of a thread's chunk loads are issued first, then the weight units of
-    // the first D steps, so the X stores wait only for the X loads
-    constexpr int NCH = 16 * (KL / 8);
-    constexpr int PERT = (NCH + 255) / 256 > 0 ? (NCH + 255) / 256 : 1;
-    v4u xv[PERT];
+    // X pieces of a step: piece q = lane + 64 i is row q / 8, half (q / 4) % 2,
+    // 16-byte chunk q % 4 of that half's group; the step adds ga * 64 bytes
+    // (ga = its first group); a half whose group is past k reads zeros
+    int xvo[XC], xthr[XC];
 #pragma unroll
-    for (int h = 0; h < PERT; ++h) {
-        const int q = tid + 256 * h;
-        const int r = q / (KL / 8), ch = q % (KL / 8);
-        const int xo = (q < NCH && r < m && ch * 8 < k) ? (int)(((int64_t)r * k + ch * 8) * 2) : xbytes;
-        xv[h] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo, 0, 0);
+    for (int i = 0; i < XC; ++i) {
+        const int q = lane + 64 * i;
+        const int rr = q >> 3, hh = (q >> 2) & 1, ch = q & 3;
+        const int64_t mm = m0 + rr;
+        xvo[i] = mm < m ? (int)((mm * k + hh * CG * 32 + ch * 8) * 2) : xbytes;
+        xthr[i] = (int)(G - hh * CG);
     }
-    WRegs ring[D];
+
+    struct Regs {
+        v4u w[2];
+        v4u x[XC];
+    };
+    // Every load is issued unconditionally (a branch around loads makes the
+    // compiler wait for all of them at the join): a pair past the row's end
+    // (the last wavefronts' tail) reads zeros through out-of-range offsets.
+    const int p0 = wv * PW;
+    auto load = [&](Regs &r, int i) {
+        if (i >= SW)
+            return;                                   // compile-time: never used
+        const int pr = p0 + i / CG, j = i % CG;
+        const bool live = pr < NP;
+        const int p = live ? pr : 0;
+        const int ga = 2 * p * CG + j;
+#pragma unroll
+        for (int q = 0; q < XC; ++q)
+            r.x[q] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (live && ga < xthr[q]) ? xvo[q] : xbytes,
+                                                           ga * 64, 0);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            r.w[t] = load_unit_gs<FMT>(rs, live ? wvo[t] : (int)wbytes, 2 * p * US + j * UB);
+    };
+    // scale blocks of the wavefront's pairs in SR slots, the block of pair
+    // pi + SR - 1 requested when pair pi starts (at least two steps ahead)
+    constexpr int SA = CG == 1 ? 4 : 2;
+    constexpr int SR = PW < SA ? PW : SA;
+    v4u sblk[SR][2];
+    auto load_s = [&](int pi) {
+        if (pi >= PW)
+            return;                                   // compile-time: never used
+        const bool live = p0 + pi < NP;
+        const int so = 2 * (live ? p0 + pi : 0) * 4 * CG;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int vo = live ? svo[t] : (int)wbytes;
+            v4u &d = sblk[pi % SR][t];
+            if constexpr (CG == 1) {
+                d = v4u{__builtin_amdgcn_raw_buffer_load_b32(rs, vo, so, 0), 0u, 0u, 0u};
+            } else if constexpr (CG == 2) {
+                const v2u v = __builtin_amdgcn_raw_buffer_load_b64(rs, vo, so, 0);
+                d = v4u{v.x, v.y, 0u, 0u};
+            } else if constexpr (CG == 3) {
+                const v3u v = __builtin_amdgcn_raw_buffer_load_b96(rs, vo, so, 0);
+                d = v4u{v.x, v.y, v.z, 0u};
+            } else {
+                d = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, so, 0);
+            }
+        }
+    };
+#pragma unroll
+    for (int pi = 0; pi < SR; ++pi)
+        load_s(pi);
+    // f16 scale of tile t at step i: half u CG + j of the pair's block
+    auto scale_of = [&](int i, int t) -> _Float16 {
+        const int pi = i / CG, j = i % CG;
+        const int hi = shalf[t] + j;
+        const v4u b = sblk[pi % SR][t];
+        const uint32_t d = (hi >> 1) == 0 ? b.x : (hi >> 1) == 1 ? b.y : (hi >> 1) == 2 ? b.z : b.w;
+        return __builtin_bit_cast(_Float16, (uint16_t)((hi & 1) ? (d >> 16) : (d & 0xFFFFu)));
+    };
+    uint8_t *const base = lds + wv * REGION;
+    auto xslab = [&](int buf) { return reinterpret_cast<_Float16 *>(base) + buf * XBUF; };
+    auto store_x = [&](const Regs &r, int buf) {
+        _Float16 *xs = xslab(buf);
+#pragma unroll
+        for (int q = 0; q < XC; ++q) {
+            const int qq = lane + 64 * q;
+            const int rr = qq >> 3, hh = (qq >> 2) & 1, ch = qq & 3;
+            const uint4 v = make_uint4(r.x[q].x, r.x[q].y, r.x[q].z, r.x[q].w);
+            *reinterpret_cast<uint4 *>(xs + rr * XROW + hh * 32 + ch * 8) = FMT == 4 ? pair_word(v) : v;
+        }
+    };
+    f16v acc[2][MT];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int f = 0; f < MT; ++f)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[t][f][e] = 0.f;
+    auto compute = [&](const Regs &r, int i) {
+        const _Float16 *xs = xslab(i & 1);
+        uint4 ak[2][4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const _Float16 sv = scale_of(i, t);
+            const h2 sc = {sv, sv};
+            if constexpr (FMT == 4) {
+                const uint32_t wds[4] = {r.w[t].x, r.w[t].y, r.w[t].z, r.w[t].w};
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    h2 a0, a1, a2, a3;
+                    dequant_word_unit(wds[w], mk, a0, a1, a2, a3);
+                    // one f16 rounding of (q - 8) * s
+                    ak[t][w] = make_uint4(as_u32(a0 * sc), as_u32(a1 * sc), as_u32(a2 * sc), as_u32(a3 * sc));
+                }
+            } else {
+                // one f16 rounding of (q - 4) * s, back in k order; X natural
+                h2 P[16];
+                dequant_unit3(r.w[t].x, r.w[t].y, r.w[t].z, mk3, P);
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    P[q] = P[q] * sc;
+                pairs3_to_k(P, ak[t]);
+            }
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            h8 bf[MT];
+#pragma unroll
+            for (int f = 0; f < MT; ++f)
+                bf[f] = *reinterpret_cast<const h8 *>(xs + (32 * f + ri) * XROW + kh * 32 + w * 8);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int f = 0; f < MT; ++f)
+                    acc[t][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, ak[t][w]), bf[f],
+                                                                      acc[t][f], 0, 0, 0);
+        }
+    };
+
+    // W and X of steps i .. i + D - 1 in registers; X of step i in LDS
+    // buffer i & 1 (written during step i - 1).  The slab is private to the
+    // wavefront: LDS accesses of one wavefront complete in order, and the
+    // empty asm statements keep the compiler from moving them across.
+    Regs ring[D];
 #pragma unroll
     for (int i = 0; i < D; ++i)
-        load_w(ring[i], i);
+        load(ring[i], i);
+    store_x(ring[0], 0);
 #pragma unroll
-    for (int h = 0; h < PERT; ++h) {
-        const int q = tid + 256 * h;
-        if (q < NCH) {
-            const int r = q / (KL / 8), ch = q % (KL / 8);
-            const uint4 v = make_uint4(xv[h].x, xv[h].y, xv[h].z, xv[h].w);
-            *reinterpret_cast<uint4 *>(&Xs[r][ch * 8]) = FMT == 4 ? pair_word(v) : v;
-        }
+    for (int i = 0; i < SW; ++i) {
+        if (i + 1 < SW)
+            store_x(ring[(i + 1) % D], (i + 1) & 1);
+        asm volatile("" ::: "memory");
+        compute(ring[i % D], i);
+        asm volatile("" ::: "memory");
+        load(ring[i % D], i + D);
+        if (i % CG == 0 && i > 0)
+            load_s(i / CG + SR - 1);
     }
-    __syncthreads();
 
-    f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-    for (int st = 0; st < STEPS; st += D) {
+    // partial tile of this wavefront into its own region, [m][n] f32: lane
+    // holds activation row 32 f + l % 32, weight rows 32 t + 8 a + 4 h + e
+    float *P = reinterpret_cast<float *>(base);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int i = 0; i < D; ++i) {
-            const int cur = st + i;
-            if (cur < STEPS) {
-                const int j = cur / CBLOCKS, cb = cur % CBLOCKS;
-                const int g = (cb * kGroupsPerStep + kb) * CG + j;   // this lane's group
-                const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(ring[i].s & 0xFFFFu));
-                const h2 sc = {sv, sv};
-                if constexpr (FMT == 4) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        const uint32_t word = w == 0 ? ring[i].w.x : w == 1 ? ring[i].w.y
-                                            : w == 2 ? ring[i].w.z : ring[i].w.w;
-                        h2 a0, a1, a2, a3;
-                        dequant_word_unit(word, mk, a0, a1, a2, a3);
-                        // one f16 rounding of (q - 8) * s
-                        const h8 af = __builtin_bit_cast(h8, make_uint4(as_u32(a0 * sc), as_u32(a1 * sc),
-                                                                        as_u32(a2 * sc), as_u32(a3 * sc)));
-                        const h8 bf = *reinterpret_cast<const h8 *>(&Xs[ri][g * 32 + w * 8]);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc, 0, 0, 0);
-                    }
-                } else {
-                    // one f16 rounding of (q - 4) * s, back in k order; X natural
-                    h2 P[16];
-                    dequant_unit3(ring[i].w.x, ring[i].w.y, ring[i].w.z, mk3, P);
+        for (int f = 0; f < MT; ++f)
 #pragma unroll
-                    for (int q = 0; q < 16; ++q)
-                        P[q] = P[q] * sc;
-                    uint4 ak[4];
-                    pairs3_to_k(P, ak);
+            for (int a = 0; a < 4; ++a)
+                *reinterpret_cast<f4 *>(P + (32 * f + ri) * PROW + 32 * t + 8 * a + 4 * kh) =
+                    f4{acc[t][f][4 * a], acc[t][f][4 * a + 1], acc[t][f][4 * a + 2], acc[t][f][4 * a + 3]};
+    __syncthreads();
+    // thread: activation row tid / (64 / OPT), weight rows c OPT .. c OPT + OPT - 1
+    constexpr int CPR = 64 / OPT;
+    const int mm = tid / CPR, c = tid % CPR;
+    float sum[OPT];
 #pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        const h8 bf = *reinterpret_cast<const h8 *>(&Xs[ri][g * 32 + w * 8]);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, ak[w]), bf, acc, 0, 0, 0);
-                    }
-                }
-                load_w(ring[i], cur + D);
+    for (int e = 0; e < OPT; ++e)
+        sum[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const float *Pw = reinterpret_cast<const float *>(lds + w * REGION) + mm * PROW + c * OPT;
+        if constexpr (OPT == 2) {
+            const float2 v = *reinterpret_cast<const float2 *>(Pw);
+            sum[0] += v.x;
+            sum[1] += v.y;
+        } else {
+#pragma unroll
+            for (int e = 0; e < OPT; e += 4) {
+                const f4 v = *reinterpret_cast<const f4 *>(Pw + e);
+                sum[e] += v[0];
+                sum[e + 1] += v[1];
+                sum[e + 2] += v[2];
+                sum[e + 3] += v[3];
             }
         }
     }
-    // lane holds weight rows 4 (lane / 16) + r, activation row lane % 16
-    if (ri < m) {
-        const int64_t nn = nw0 + 4 * kb;
-        if ((n & 3) == 0 && (reinterpret_cast<uintptr_t>(Y) & 7) == 0 && nn + 3 < n) {
-            const uint32_t lo = f16_bits(acc[0]) | ((uint32_t)f16_bits(acc[1]) << 16);
-            const uint32_t hi = f16_bits(acc[2]) | ((uint32_t)f16_bits(acc[3]) << 16);
-            *reinterpret_cast<uint2 *>(Y + ri * n + nn) = make_uint2(lo, hi);
-        } else {
+    const int64_t gm = m0 + mm, gn = n0 + c * OPT;
+    if (gm >= m)
+        return;
+    uint16_t *yr = Y + gm * n + gn;
+    if (OPT == 2 && (n % 2) == 0 && (reinterpret_cast<uintptr_t>(Y) & 3) == 0 && gn + 2 <= n) {
+        *reinterpret_cast<uint32_t *>(yr) = f16_bits(sum[0]) | ((uint32_t)f16_bits(sum[OPT - 1]) << 16);
+    } else if (OPT >= 4 && (n % OPT) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0 && gn + OPT <= n) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (nn + r < n)
-                    Y[ri * n + nn + r] = f16_bits(acc[r]);
+        for (int e = 0; e + 3 < OPT; e += 4) {
+            const uint32_t lo = f16_bits(sum[e]) | ((uint32_t)f16_bits(sum[e + 1]) << 16);
+            const uint32_t hi = f16_bits(sum[e + 2]) | ((uint32_t)f16_bits(sum[e + 3]) << 16);
+            *reinterpret_cast<uint2 *>(yr + e) = make_uint2(lo, hi);
         }
+    } else {
+#pragma unroll
+        for (int e = 0; e < OPT; ++e)
+            if (gn + e < n)
+                yr[e] = f16_bits(sum[e]);
     }
 }
 
@@ -966,13 +1115,17 @@ hipError_t launch_mfma_wx(const Geometry &geo, const uint8_t *wd, const uint16_t
     return hipGetLastError();
 }
 
-template <int L, int CG, int FMT>
-hipError_t launch_mfma_xres(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
-                            int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
+template <int L, int CG, int MT, int NW, int D, int FMT>
+hipError_t launch_mfma_ks(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
+                          int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
 {
+    constexpr int BM = 32 * MT;
+    const int64_t nbn = (n + 63) / 64;
+    const int64_t mbl = (m + BM - 1) / BM;
+    const int64_t padded = mbl > 1 ? (nbn + 7) / 8 * 8 : nbn;
     const int64_t wbytes = geo.tiles * geo.tile_bytes;
-    hipLaunchKernelGGL((gemm_mfma_xres_kernel<L, CG, FMT>), dim3((unsigned)((n + 63) / 64)), dim3(256), 0,
-                       stream, wd, wbytes, X, Y, m, n, k);
+    hipLaunchKernelGGL((gemm_mfma_ks_kernel<L, CG, MT, NW, D, FMT>), dim3((unsigned)(padded * mbl)),
+                       dim3(64 * NW), 0, stream, wd, wbytes, X, Y, m, n, k, nbn, padded);
     return hipGetLastError();
 }
 
@@ -980,22 +1133,25 @@ template <int L, int CG, int FMT>
 hipError_t launch_mfma_lc(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
                           int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
 {
-    // m <= 16 with k <= 4096: X resident in LDS (16384 x 3072, m = 16: 13.4
-    // against 14.4 us for the weight-direct kernel); otherwise block tiles of
-    // 64 NT weight rows x 16 MT activation rows chosen on the 16384 x 3072
-    // weight, each keeping 256 blocks in flight (us at m = 32 / 64 / 128 /
-    // 256: 19.2 / 27.5 / 37.1 / 52.0; 64-row slabs with more, shorter M
-    // blocks -- 512 blocks, two per CU -- were slower: 28.3 / 40.4 / 63.7)
-    if (m <= 16 && L * CG * 32 <= kXresMaxK)
-        return launch_mfma_xres<L, CG, FMT>(geo, wd, X, m, n, k, Y, stream);
-    if (m <= 16)
-        return launch_mfma_wx<L, CG, 1, 1, FMT>(geo, wd, X, m, n, k, Y, stream);
+    // K-split kernel up to 128 rows, with the tile and wavefront count that
+    // measured fastest on 16384 x 3072 (us at m = 4 / 16 / 32 / 64 / 128:
+    // 10.8 / 12.3 / 13.8 / 19.3 / 31.4, against 13.0 / 12.9 / 18.4 / 25.9 /
+    // 34.5 for the X-resident and weight-direct kernels it replaced there);
+    // above, the weight-direct kernel's 128 x 128 block tiles read X half as
+    // often (m = 160 / 256: 44.3 / 47.7 us, K-split 45.1 / 54.2)
     if (m <= 32)
-        return launch_mfma_wx<L, CG, 1, 2, FMT>(geo, wd, X, m, n, k, Y, stream);
+        return launch_mfma_ks<L, CG, 1, 16, 2, FMT>(geo, wd, X, m, n, k, Y, stream);
     if (m <= 64)
-        return launch_mfma_wx<L, CG, 1, 4, FMT>(geo, wd, X, m, n, k, Y, stream);
-    if (m <= 128)
-        return launch_mfma_wx<L, CG, 2, 4, FMT>(geo, wd, X, m, n, k, Y, stream);
+        return launch_mfma_ks<L, CG, 2, 8, 3, FMT>(geo, wd, X, m, n, k, Y, stream);
+    // the 4-wavefront tile unrolls 2 L CG / 4 steps per wavefront: beyond
+    // k = 4096 its registers spill, and two 64-row M blocks run instead
+    if constexpr (L * CG <= 128) {
+        if (m <= 128)
+            return launch_mfma_ks<L, CG, 4, 4, 2, FMT>(geo, wd, X, m, n, k, Y, stream);
+    } else {
+        if (m <= 128)
+            return launch_mfma_ks<L, CG, 2, 8, 3, FMT>(geo, wd, X, m, n, k, Y, stream);
+    }
     return launch_mfma_wx<L, CG, 2, 8, FMT>(geo, wd, X, m, n, k, Y, stream);
 }
 

@@ -486,9 +486,22 @@ def main():
 
     if not args.no_cpu_baseline and args.only == "all":
         result["cpu_baseline"] = cpu_baseline(si, inp, args.cpu_seconds)
+    result["library"] = library_stamp(q4)
 
     print(json.dumps(result), flush=True)
     return 0
+
+
+def library_stamp(q4) -> dict:
+    """The source digest stamped into the loaded libq4.so against the digest
+    of the sources in this tree (the build script's sources_digest)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "q4_build", os.path.join(ROOT, "int4_quantized_decode_q4_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    built, tree = q4.source_hash(), b.sources_digest()
+    return {"source_hash": built, "tree_hash": tree, "matches_sources": built == tree}
 
 
 def read_probe_leg(torch, q4, sizes: dict, K: int, W: int) -> dict:

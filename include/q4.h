@@ -203,8 +203,10 @@ int q4_gemv(const q4_weight *w, const uint16_t *x, uint16_t *y, void *stream);
  * batched-prefill form).  m = 1 with Y 4-byte aligned runs the q4_gemv
  * kernels; otherwise m < 4 runs a VALU kernel that reads W once per 8
  * activation rows with exact dequant; m >= 4 dequantizes W to f16
- * (q - 8) * s in LDS (one rounding, relative error <= 2^-11) and contracts
- * with v_mfma_f32_16x16x32_f16, f32 accumulation.
+ * (q - 8) * s in registers (one rounding, relative error <= 2^-11) and
+ * contracts on the matrix cores (v_mfma_f32_32x32x16_f16 up to m = 128,
+ * v_mfma_f32_16x16x32_f16 above), f32 accumulation; the f32 sum of a row is
+ * formed in a fixed order for a given shape (the same bits on every call).
  *   w : Q4_LAYOUT_ROWS, or Q4_LAYOUT_INT3 ((q - 4) * s on the same paths)
  *   X : device f16 [m][k] row-major, 16-byte aligned
  *   Y : device f16 [m][n] row-major, 2-byte aligned
@@ -482,6 +484,11 @@ const char *q4_strerror(int code);
 
 /* hipError_t behind the last Q4_ERR_HIP returned on this thread (0 if none). */
 int q4_last_hip_error(void);
+
+/* Digest of the sources this library was built from (16 hex digits of the
+ * SHA-256 over the kernel/ABI sources and this header, as computed by the
+ * build script), or "unstamped".  Static text; never NULL. */
+const char *q4_source_hash(void);
 
 /* Layout geometry for a weight of `rows` logical rows: out[0..5] = L, CG, P,
  * TR, tiles, tile bytes.  Returns Q4_OK or Q4_ERR_SHAPE/Q4_ERR_NULL. */

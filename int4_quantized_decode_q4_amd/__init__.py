@@ -90,6 +90,7 @@ _SIGNATURES = {
                                            ctypes.c_float, _P, _P, _I64, _P]),
     "q4_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "q4_last_hip_error": (ctypes.c_int, []),
+    "q4_source_hash": (ctypes.c_char_p, []),
     "q4_layout_geometry": (ctypes.c_int, [_I32, _I32, _P]),
     "q4_read_probe": (ctypes.c_int, [_P, _I64, _P, _I64, _P]),
     "q4_chain_workspace_bytes": (_I64, [_CS, _I32]),
@@ -110,6 +111,12 @@ class Q4Error(RuntimeError):
         if code == ERR_HIP:
             msg += f" (hipError {_lib.q4_last_hip_error()})"
         super().__init__(f"{where}: {msg} [{code}]")
+
+
+def source_hash() -> str:
+    """Digest of the sources the loaded libq4.so was built from
+    (q4_source_hash); compare with build.py's sources_digest()."""
+    return _lib.q4_source_hash().decode()
 
 
 def _check(code: int, where: str) -> None:

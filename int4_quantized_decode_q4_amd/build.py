@@ -34,9 +34,27 @@ FLAGS = [
 ]
 
 
+def sources_digest() -> str:
+    """SHA-256 (first 16 hex digits) over the library's sources: every file
+    of csrc/ and include/q4.h, in name order.  The build stamps it into the
+    library (q4_source_hash), so a loaded library can be checked against the
+    sources it claims to come from."""
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(os.listdir(CSRC)) + ["../../include/q4.h"]
+    for name in files:
+        path = os.path.normpath(os.path.join(CSRC, name))
+        if os.path.isfile(path):
+            h.update(name.encode())
+            with open(path, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    stamp = f'-DQ4_SOURCE_HASH="{sources_digest()}"'
+    cmd = [HIPCC, *FLAGS, stamp, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")

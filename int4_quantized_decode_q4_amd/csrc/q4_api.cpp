@@ -940,4 +940,9 @@ const char *q4_strerror(int code)
 
 int q4_last_hip_error(void) { return g_last_hip_error; }
 
+#ifndef Q4_SOURCE_HASH
+#define Q4_SOURCE_HASH "unstamped"
+#endif
+const char *q4_source_hash(void) { return Q4_SOURCE_HASH; }
+
 }  // extern "C"

@@ -1069,7 +1069,8 @@ hipError_t launch_valu_lc(const Geometry &geo, const uint8_t *wd, const uint16_t
 {
     constexpr int PT = Q4_VALU_TILES_IN_FLIGHT;
     const bool single = geo.P == 1;
-    const int64_t cap = single ? 256 * Q4_VALU_BLOCKS_PER_CU : 256 * 8;
+    const int64_t cus = device_cus();
+    const int64_t cap = single ? cus * Q4_VALU_BLOCKS_PER_CU : cus * 8;
     const dim3 grid((unsigned)(geo.tiles < cap ? geo.tiles : cap)), block(64 * CG);
     for (int64_t m0 = 0; m0 < m; m0 += kValuRows) {
         const int64_t mc = m - m0 < kValuRows ? m - m0 : kValuRows;

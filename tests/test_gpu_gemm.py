@@ -145,3 +145,17 @@ def test_gemm_one_row_is_the_gemv(q4, orc, int3):
     Ym = buf[1:].view(1, n)
     q4.gemm(pw, dev_f16(X), out=Ym)
     assert_within(host_f16_as_f64(Ym), ref, tol_f16(ref, a), "gemm m=1, Y 2-byte aligned (VALU kernel)")
+
+
+@pytest.mark.parametrize("n,k", [(777, 8192), (130, 224), (70, 1568), (64, 512), (1000, 4096)])
+@pytest.mark.parametrize("m", [33, 64, 65, 100, 128])
+def test_gemm_k_split_tiles(q4, orc, n, k, m):
+    """the K-split MFMA kernel's three tiles (m <= 32 / 64 / 128) and its
+    k > 4096 fallback tile, on layouts from L = 8 to 64 (steps that run past
+    a row's pairs, several M blocks, ragged n)"""
+    rng = np.random.default_rng(n + 3 * k + 7 * m)
+    w, s = si.draw_weight(rng, n, k)
+    X = si.draw_X(rng, m, k)
+    Y, _ = run(q4, w, s, X)
+    ref, a = orc.gemm(w, s, X)
+    assert_within(host_f16_as_f64(Y), ref, tol_f16(ref, a), f"gemm {n}x{k} m={m}")

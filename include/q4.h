@@ -201,8 +201,8 @@ int q4_gemv(const q4_weight *w, const uint16_t *x, uint16_t *y, void *stream);
 /*
  * Y = X . dequant(W)^T for m activation rows ([P1] 技术限制与诚实声明: the
  * batched-prefill form).  m = 1 with Y 4-byte aligned runs the q4_gemv
- * kernels; otherwise m < 4 runs a VALU kernel that reads W once per 8
- * activation rows with exact dequant; m >= 4 dequantizes W to f16
+ * kernels (otherwise m = 1 runs a VALU kernel that reads W once per 8
+ * activation rows with exact dequant); m >= 2 dequantizes W to f16
  * (q - 8) * s in registers (one rounding, relative error <= 2^-11) and
  * contracts on the matrix cores (v_mfma_f32_32x32x16_f16 up to m = 128,
  * v_mfma_f32_16x16x32_f16 above), f32 accumulation; the f32 sum of a row is
@@ -216,7 +216,7 @@ int q4_gemm(const q4_weight *w, const uint16_t *X, int32_t m, uint16_t *Y,
             void *ws, int64_t ws_bytes, void *stream);
 
 /* GEMM kernel choice for q4_gemm_path. */
-#define Q4_GEMM_AUTO 0   /* what q4_gemm does: MFMA for m >= 4, VALU below (m = 1: q4_gemv) */
+#define Q4_GEMM_AUTO 0   /* what q4_gemm does: MFMA for m >= 2, m = 1: q4_gemv (VALU if Y is only 2-byte aligned) */
 #define Q4_GEMM_VALU 1   /* VALU kernel for any m */
 #define Q4_GEMM_MFMA 2   /* MFMA kernel for any m (falls back to VALU for
                             layouts it does not take: k > 8192 or k < 256) */

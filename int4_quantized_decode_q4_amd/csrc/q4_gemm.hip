@@ -6,14 +6,14 @@
 // prompt processing; the pages give no design for them.
 //
 // Kernels:
-//  * VALU, m < 4 (or a layout the MFMA kernels do not take): the streaming
+//  * VALU, m = 1 (or a layout the MFMA kernels do not take): the streaming
 //    kernel -- CG wavefronts per block walk tiles, wavefront j takes group
 //    slot j of every lane, so each lane keeps that group's x slices for up to
 //    8 activation rows in VGPRs for the whole launch and one pass over W
 //    serves 8 rows; codes are dequantized once per word (exact q - 8) and
 //    reused for every row.  Multi-pass layouts (k > 8192) use a per-tile
 //    variant that re-reads the x slices of each pass.
-//  * MFMA, 4 <= m <= 128: the K-split kernel.  A block owns 64 weight rows
+//  * MFMA, 2 <= m <= 128: the K-split kernel.  A block owns 64 weight rows
 //    and up to 128 activation rows; its wavefronts split K, each staging its
 //    own X slices in its own LDS region (no block barrier until the end,
 //    where the partial tiles are added in wavefront order).  Each lane loads
@@ -1199,10 +1199,11 @@ hipError_t launch_gemm(const Geometry &geo, const void *wdata, const uint16_t *X
                        int64_t n, int64_t k, uint16_t *Y, int path, hipStream_t stream, bool int3)
 {
     const uint8_t *wd = static_cast<const uint8_t *>(wdata);
-    // from 4 rows on the MFMA kernels are faster (16384 x 3072: 13.7 against
-    // 17.4 us at m = 4, 17.4 against 44 us at m = 12); at 1-2 rows the VALU
-    // kernel's single exact pass over W wins
-    bool mfma = (path == GEMM_PATH_MFMA) || (path == GEMM_PATH_AUTO && m >= 4);
+    // from 2 rows on the MFMA kernels are faster (16384 x 3072: 10.9 against
+    // 12.3 us at m = 2, 11.2 against 17.1 us at m = 4); one row with Y not
+    // 4-byte aligned (else the GEMV kernels) takes the VALU kernel's single
+    // exact pass over W
+    bool mfma = (path == GEMM_PATH_MFMA) || (path == GEMM_PATH_AUTO && m >= 2);
     if (mfma && !gemm_mfma_eligible(geo))
         mfma = false;
     // the MFMA kernel addresses the weight and X through 32-bit buffer offsets

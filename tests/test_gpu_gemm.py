@@ -1,5 +1,6 @@
 """q4_gemm / q4_gemm_path on the GPU against the oracle: the VALU kernel
-(m < 4, exact dequant) and the MFMA kernels (m >= 4, f16 dequant), full
+(forced, or m = 1 with Y 2-byte aligned; exact dequant) and the MFMA kernels
+(m >= 2, f16 dequant), full
 checks at moderate sizes and sampled checks at the full prefill shape."""
 import numpy as np
 import pytest

@@ -204,8 +204,8 @@ int q4_gemv(const q4_weight *w, const uint16_t *x, uint16_t *y, void *stream);
  * kernels (otherwise m = 1 runs a VALU kernel that reads W once per 8
  * activation rows with exact dequant); m >= 2 dequantizes W to f16
  * (q - 8) * s in registers (one rounding, relative error <= 2^-11) and
- * contracts on the matrix cores (v_mfma_f32_32x32x16_f16 up to m = 128,
- * v_mfma_f32_16x16x32_f16 above), f32 accumulation; the f32 sum of a row is
+ * contracts on the matrix cores (v_mfma_f32_32x32x16_f16; for m > 128 with
+ * k > 4096, v_mfma_f32_16x16x32_f16), f32 accumulation; the f32 sum of a row is
  * formed in a fixed order for a given shape (the same bits on every call).
  *   w : Q4_LAYOUT_ROWS, or Q4_LAYOUT_INT3 ((q - 4) * s on the same paths)
  *   X : device f16 [m][k] row-major, 16-byte aligned

@@ -13,8 +13,8 @@
 //    serves 8 rows; codes are dequantized once per word (exact q - 8) and
 //    reused for every row.  Multi-pass layouts (k > 8192) use a per-tile
 //    variant that re-reads the x slices of each pass.
-//  * MFMA, 2 <= m <= 128: the K-split kernel.  A block owns 64 weight rows
-//    and up to 128 activation rows; its wavefronts split K, each staging its
+//  * MFMA, m >= 2: the K-split kernel.  A block owns 64 or 128 weight rows
+//    and 32 to 128 activation rows; its wavefronts split K, each staging its
 //    own X slices in its own LDS region (no block barrier until the end,
 //    where the partial tiles are added in wavefront order).  Each lane loads
 //    the 16-byte unit of codes that is its own A operand of
@@ -24,9 +24,9 @@
 //    Inside each 8-k word the k order of both operands is (0,4,1,5,2,6,3,7)
 //    -- the order the nibble masks produce -- which leaves the contraction
 //    unchanged.
-//  * MFMA, m > 128: the weight-direct kernel, the same operand scheme on
-//    v_mfma_f32_16x16x32_f16 with 128 x 128 block tiles whose X slab of a
-//    step is shared by the block's 4 wavefronts (X is read half as often).
+//  * MFMA, m > 128 with k > 4096: the weight-direct kernel, the same operand
+//    scheme on v_mfma_f32_16x16x32_f16 with 128 x 128 block tiles whose X
+//    slab of a step is shared by the block's 4 wavefronts.
 // int3 weights (12-byte units of 32 codes, one pass) run through the same
 // kernels with their own dequant: exact (q - 4) pairs on the VALU path, f16
 // (q - 4) * s put back in k order for the MFMA kernel (X is not re-paired).
@@ -766,8 +766,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_wx_kernel(const uint8_t *__rest
     }
 }
 
-// K-split MFMA kernel (v_mfma_f32_32x32x16_f16).  A block owns 64 weight
-// rows (two A tiles of 32) and BM = 32 MT activation rows, and its NW
+// K-split MFMA kernel (v_mfma_f32_32x32x16_f16).  A block owns BN = 32 NA
+// weight rows (NA A tiles of 32) and BM = 32 MT activation rows, and its NW
 // wavefronts split K instead of the rows: wavefront w takes a contiguous
 // run of the row's steps, a step being one group pair (c, c + 1) of lane
 // positions at one group slot j -- groups (2p) CG + j and (2p + 1) CG + j.
@@ -779,11 +779,12 @@ __global__ __launch_bounds__(256) void gemm_mfma_wx_kernel(const uint8_t *__rest
 // are).  Each wavefront stages its own X slab of a step (BM rows x the two
 // groups) in its own LDS region and reads it back as B operands, so no
 // block barrier is needed until the end, where the NW partial tiles are
-// added in wavefront order through the same LDS and rounded once to f16.
-// Per step a wavefront does 8 MT MFMAs against 8 dequantized words and
-// 4 MT LDS fragment reads; every weight byte is dequantized once per M
-// block, every X byte passes through LDS once per weight slab.
-template <int L, int CG, int MT, int NW, int D, int FMT = 4>
+// added in wavefront order through the same LDS (32 activation rows at a
+// time) and rounded once to f16.  Per step a wavefront does 4 NA MT MFMAs
+// against 4 NA dequantized words and 4 MT LDS fragment reads; every weight
+// byte is dequantized once per M block, every X byte passes through LDS
+// once per weight slab.
+template <int L, int CG, int NA, int MT, int NW, int D, int FMT = 4>
 __global__ __launch_bounds__(64 * NW) void gemm_mfma_ks_kernel(const uint8_t *__restrict__ wd,
                                                                int64_t wbytes,
                                                                const uint16_t *__restrict__ X,
@@ -791,7 +792,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ks_kernel(const uint8_t *__
                                                                int64_t n, int64_t k, int64_t nblocks_n,
                                                                int64_t padded_nblocks_n)
 {
-    constexpr int BM = 32 * MT;
+    constexpr int BM = 32 * MT, BN = 32 * NA;
     constexpr int TR = 128 / L;
     constexpr int PB = CG * GFmt<FMT>::PASS;
     constexpr int UB = GFmt<FMT>::UB, US = GFmt<FMT>::US;
@@ -800,11 +801,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ks_kernel(const uint8_t *__
     constexpr int SW = PW * CG;                      // steps per wavefront: (pair, slot), slot fastest
     constexpr int XROW = 64 + 8;                     // halves per slab row (+16 B: rows 4 banks apart)
     constexpr int XBUF = BM * XROW;                  // halves per slab buffer
-    constexpr int PROW = 64 + 4;                     // floats per row of a partial tile
-    constexpr int REGION = 4 * XBUF > 4 * BM * PROW ? 4 * XBUF : 4 * BM * PROW;   // bytes per wavefront
+    constexpr int PROW = BN + 4;                     // floats per row of a partial tile
+    constexpr int REGION = 4 * XBUF > 4 * 32 * PROW ? 4 * XBUF : 4 * 32 * PROW;   // bytes per wavefront
     constexpr int XC = BM / 8;                       // 16-byte X pieces per lane per step
-    constexpr int OPT = BM / NW;                     // outputs per thread in the final sum
-    static_assert((OPT == 2 || OPT % 4 == 0) && 64 % OPT == 0 && D >= 2, "unsupported BM / NW / D");
+    constexpr int OPT = BN / (2 * NW);               // outputs per thread per 32 rows of the final sum
+    static_assert((OPT == 2 || OPT % 4 == 0) && BN % OPT == 0 && D >= 2, "unsupported BN / NW / D");
     __shared__ __attribute__((aligned(16))) uint8_t lds[NW * REGION];
 
     const int tid = threadIdx.x;
@@ -821,7 +822,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ks_kernel(const uint8_t *__
     const int64_t mb = within / 8;
     if (nb >= nblocks_n)
         return;
-    const int64_t n0 = nb * 64, m0 = mb * BM;
+    const int64_t n0 = nb * BN, m0 = mb * BM;
 
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(wd), (short)0, (int)wbytes, 0x00020000);
@@ -835,9 +836,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ks_kernel(const uint8_t *__
     // j = 0); a step (p, j) adds the uniform 2p US + j UB (units) and a pair
     // 2p 4 CG (its scale block: the 4 CG bytes of both rows of a lane pair
     // and every slot) through the scalar offset; rows past n read zero
-    int wvo[2], svo[2], shalf[2];
+    int wvo[NA], svo[NA], shalf[NA];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < NA; ++t) {
         const int64_t row = n0 + 32 * t + ri;
         const int64_t tile = row / TR;
         const int sl = (int)((row % TR) >> 1);
@@ -862,7 +863,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ks_kernel(const uint8_t *__
     }
 
     struct Regs {
-        v4u w[2];
+        v4u w[NA];
         v4u x[XC];
     };
     // Every load is issued unconditionally (a branch around loads makes the
@@ -881,21 +882,21 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ks_kernel(const uint8_t *__
             r.x[q] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (live && ga < xthr[q]) ? xvo[q] : xbytes,
                                                            ga * 64, 0);
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < NA; ++t)
             r.w[t] = load_unit_gs<FMT>(rs, live ? wvo[t] : (int)wbytes, 2 * p * US + j * UB);
     };
     // scale blocks of the wavefront's pairs in SR slots, the block of pair
     // pi + SR - 1 requested when pair pi starts (at least two steps ahead)
     constexpr int SA = CG == 1 ? 4 : 2;
     constexpr int SR = PW < SA ? PW : SA;
-    v4u sblk[SR][2];
+    v4u sblk[SR][NA];
     auto load_s = [&](int pi) {
         if (pi >= PW)
             return;                                   // compile-time: never used
         const bool live = p0 + pi < NP;
         const int so = 2 * (live ? p0 + pi : 0) * 4 * CG;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < NA; ++t) {
             const int vo = live ? svo[t] : (int)wbytes;
             v4u &d = sblk[pi % SR][t];
             if constexpr (CG == 1) {
@@ -934,9 +935,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ks_kernel(const uint8_t *__
             *reinterpret_cast<uint4 *>(xs + rr * XROW + hh * 32 + ch * 8) = FMT == 4 ? pair_word(v) : v;
         }
     };
-    f16v acc[2][MT];
+    f16v acc[NA][MT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < NA; ++t)
 #pragma unroll
         for (int f = 0; f < MT; ++f)
 #pragma unroll
@@ -944,9 +945,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ks_kernel(const uint8_t *__
                 acc[t][f][e] = 0.f;
     auto compute = [&](const Regs &r, int i) {
         const _Float16 *xs = xslab(i & 1);
-        uint4 ak[2][4];
+        uint4 ak[NA][4];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < NA; ++t) {
             const _Float16 sv = scale_of(i, t);
             const h2 sc = {sv, sv};
             if constexpr (FMT == 4) {
@@ -975,7 +976,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ks_kernel(const uint8_t *__
             for (int f = 0; f < MT; ++f)
                 bf[f] = *reinterpret_cast<const h8 *>(xs + (32 * f + ri) * XROW + kh * 32 + w * 8);
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < NA; ++t)
 #pragma unroll
                 for (int f = 0; f < MT; ++f)
                     acc[t][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, ak[t][w]), bf[f],
@@ -1004,62 +1005,67 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ks_kernel(const uint8_t *__
             load_s(i / CG + SR - 1);
     }
 
-    // partial tile of this wavefront into its own region, [m][n] f32: lane
-    // holds activation row 32 f + l % 32, weight rows 32 t + 8 a + 4 h + e
+    // partial tiles, 32 activation rows at a time: each wavefront writes its
+    // rows 32 f .. 32 f + 31 ([m][n] f32; lane holds activation row 32 f +
+    // l % 32, weight rows 32 t + 8 a + 4 h + e) into its own region, then
+    // every thread adds OPT outputs over the wavefronts in order
     float *P = reinterpret_cast<float *>(base);
+    constexpr int CPR = BN / OPT;
+    const int mm = tid / CPR, c = tid % CPR;
+    const int64_t gn = n0 + c * OPT;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int f = 0; f < MT; ++f) {
+        if (f > 0)
+            __syncthreads();                      // the previous rows have been read
 #pragma unroll
-        for (int f = 0; f < MT; ++f)
+        for (int t = 0; t < NA; ++t)
 #pragma unroll
             for (int a = 0; a < 4; ++a)
-                *reinterpret_cast<f4 *>(P + (32 * f + ri) * PROW + 32 * t + 8 * a + 4 * kh) =
+                *reinterpret_cast<f4 *>(P + ri * PROW + 32 * t + 8 * a + 4 * kh) =
                     f4{acc[t][f][4 * a], acc[t][f][4 * a + 1], acc[t][f][4 * a + 2], acc[t][f][4 * a + 3]};
-    __syncthreads();
-    // thread: activation row tid / (64 / OPT), weight rows c OPT .. c OPT + OPT - 1
-    constexpr int CPR = 64 / OPT;
-    const int mm = tid / CPR, c = tid % CPR;
-    float sum[OPT];
-#pragma unroll
-    for (int e = 0; e < OPT; ++e)
-        sum[e] = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const float *Pw = reinterpret_cast<const float *>(lds + w * REGION) + mm * PROW + c * OPT;
-        if constexpr (OPT == 2) {
-            const float2 v = *reinterpret_cast<const float2 *>(Pw);
-            sum[0] += v.x;
-            sum[1] += v.y;
-        } else {
-#pragma unroll
-            for (int e = 0; e < OPT; e += 4) {
-                const f4 v = *reinterpret_cast<const f4 *>(Pw + e);
-                sum[e] += v[0];
-                sum[e + 1] += v[1];
-                sum[e + 2] += v[2];
-                sum[e + 3] += v[3];
-            }
-        }
-    }
-    const int64_t gm = m0 + mm, gn = n0 + c * OPT;
-    if (gm >= m)
-        return;
-    uint16_t *yr = Y + gm * n + gn;
-    if (OPT == 2 && (n % 2) == 0 && (reinterpret_cast<uintptr_t>(Y) & 3) == 0 && gn + 2 <= n) {
-        *reinterpret_cast<uint32_t *>(yr) = f16_bits(sum[0]) | ((uint32_t)f16_bits(sum[OPT - 1]) << 16);
-    } else if (OPT >= 4 && (n % OPT) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0 && gn + OPT <= n) {
-#pragma unroll
-        for (int e = 0; e + 3 < OPT; e += 4) {
-            const uint32_t lo = f16_bits(sum[e]) | ((uint32_t)f16_bits(sum[e + 1]) << 16);
-            const uint32_t hi = f16_bits(sum[e + 2]) | ((uint32_t)f16_bits(sum[e + 3]) << 16);
-            *reinterpret_cast<uint2 *>(yr + e) = make_uint2(lo, hi);
-        }
-    } else {
+        __syncthreads();
+        float sum[OPT];
 #pragma unroll
         for (int e = 0; e < OPT; ++e)
-            if (gn + e < n)
-                yr[e] = f16_bits(sum[e]);
+            sum[e] = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float *Pw = reinterpret_cast<const float *>(lds + w * REGION) + mm * PROW + c * OPT;
+            if constexpr (OPT == 2) {
+                const float2 v = *reinterpret_cast<const float2 *>(Pw);
+                sum[0] += v.x;
+                sum[1] += v.y;
+            } else {
+#pragma unroll
+                for (int e = 0; e < OPT; e += 4) {
+                    const f4 v = *reinterpret_cast<const f4 *>(Pw + e);
+                    sum[e] += v[0];
+                    sum[e + 1] += v[1];
+                    sum[e + 2] += v[2];
+                    sum[e + 3] += v[3];
+                }
+            }
+        }
+        const int64_t gm = m0 + 32 * f + mm;
+        if (gm < m) {
+            uint16_t *yr = Y + gm * n + gn;
+            if (OPT == 2 && (n % 2) == 0 && (reinterpret_cast<uintptr_t>(Y) & 3) == 0 && gn + 2 <= n) {
+                *reinterpret_cast<uint32_t *>(yr) = f16_bits(sum[0]) | ((uint32_t)f16_bits(sum[OPT - 1]) << 16);
+            } else if (OPT >= 4 && (n % OPT) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0 && gn + OPT <= n) {
+#pragma unroll
+                for (int e = 0; e + 3 < OPT; e += 4) {
+                    const uint32_t lo = f16_bits(sum[e]) | ((uint32_t)f16_bits(sum[e + 1]) << 16);
+                    const uint32_t hi = f16_bits(sum[e + 2]) | ((uint32_t)f16_bits(sum[e + 3]) << 16);
+                    *reinterpret_cast<uint2 *>(yr + e) = make_uint2(lo, hi);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < OPT; ++e)
+                    if (gn + e < n)
+                        yr[e] = f16_bits(sum[e]);
+            }
+        }
     }
 }
 
@@ -1116,16 +1122,16 @@ hipError_t launch_mfma_wx(const Geometry &geo, const uint8_t *wd, const uint16_t
     return hipGetLastError();
 }
 
-template <int L, int CG, int MT, int NW, int D, int FMT>
+template <int L, int CG, int NA, int MT, int NW, int D, int FMT>
 hipError_t launch_mfma_ks(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
                           int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
 {
-    constexpr int BM = 32 * MT;
-    const int64_t nbn = (n + 63) / 64;
+    constexpr int BM = 32 * MT, BN = 32 * NA;
+    const int64_t nbn = (n + BN - 1) / BN;
     const int64_t mbl = (m + BM - 1) / BM;
     const int64_t padded = mbl > 1 ? (nbn + 7) / 8 * 8 : nbn;
     const int64_t wbytes = geo.tiles * geo.tile_bytes;
-    hipLaunchKernelGGL((gemm_mfma_ks_kernel<L, CG, MT, NW, D, FMT>), dim3((unsigned)(padded * mbl)),
+    hipLaunchKernelGGL((gemm_mfma_ks_kernel<L, CG, NA, MT, NW, D, FMT>), dim3((unsigned)(padded * mbl)),
                        dim3(64 * NW), 0, stream, wd, wbytes, X, Y, m, n, k, nbn, padded);
     return hipGetLastError();
 }
@@ -1134,26 +1140,27 @@ template <int L, int CG, int FMT>
 hipError_t launch_mfma_lc(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
                           int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
 {
-    // K-split kernel up to 128 rows, with the tile and wavefront count that
-    // measured fastest on 16384 x 3072 (us at m = 4 / 16 / 32 / 64 / 128:
-    // 10.8 / 12.3 / 13.8 / 19.3 / 31.4, against 13.0 / 12.9 / 18.4 / 25.9 /
-    // 34.5 for the X-resident and weight-direct kernels it replaced there);
-    // above, the weight-direct kernel's 128 x 128 block tiles read X half as
-    // often (m = 160 / 256: 44.3 / 47.7 us, K-split 45.1 / 54.2)
+    // K-split kernel tiles (A tiles NA x 32 weight rows, MT x 32 activation
+    // rows, NW wavefronts, D steps in flight) with the measured fastest per
+    // m on 16384 x 3072, us at m = 4 / 16 / 32 / 64 / 128 / 192 / 256: 10.8 /
+    // 12.3 / 13.8 / 19.3 / 26.6 / 38.1 / 41.2, against 13.0 / 12.9 / 18.4 /
+    // 25.9 / 34.5 / 45.6 / 47.8 for the X-resident and weight-direct kernels
+    // they replaced.  Beyond k = 4096 the 4-wavefront tiles unroll too many
+    // steps per wavefront and spill: two 64-row M blocks of 8 wavefronts up
+    // to m = 128, the weight-direct kernel above.
     if (m <= 32)
-        return launch_mfma_ks<L, CG, 1, 16, 2, FMT>(geo, wd, X, m, n, k, Y, stream);
+        return launch_mfma_ks<L, CG, 2, 1, 16, 2, FMT>(geo, wd, X, m, n, k, Y, stream);
     if (m <= 64)
-        return launch_mfma_ks<L, CG, 2, 8, 3, FMT>(geo, wd, X, m, n, k, Y, stream);
-    // the 4-wavefront tile unrolls 2 L CG / 4 steps per wavefront: beyond
-    // k = 4096 its registers spill, and two 64-row M blocks run instead
+        return launch_mfma_ks<L, CG, 2, 2, 8, 3, FMT>(geo, wd, X, m, n, k, Y, stream);
     if constexpr (L * CG <= 128) {
         if (m <= 128)
-            return launch_mfma_ks<L, CG, 4, 4, 2, FMT>(geo, wd, X, m, n, k, Y, stream);
+            return launch_mfma_ks<L, CG, 4, 2, 8, 2, FMT>(geo, wd, X, m, n, k, Y, stream);
+        return launch_mfma_ks<L, CG, 4, 4, 4, 2, FMT>(geo, wd, X, m, n, k, Y, stream);
     } else {
         if (m <= 128)
-            return launch_mfma_ks<L, CG, 2, 8, 3, FMT>(geo, wd, X, m, n, k, Y, stream);
+            return launch_mfma_ks<L, CG, 2, 2, 8, 3, FMT>(geo, wd, X, m, n, k, Y, stream);
+        return launch_mfma_wx<L, CG, 2, 8, FMT>(geo, wd, X, m, n, k, Y, stream);
     }
-    return launch_mfma_wx<L, CG, 2, 8, FMT>(geo, wd, X, m, n, k, Y, stream);
 }
 
 template <int L, int FMT>

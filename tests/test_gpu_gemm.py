@@ -149,11 +149,12 @@ def test_gemm_one_row_is_the_gemv(q4, orc, int3):
 
 
 @pytest.mark.parametrize("n,k", [(777, 8192), (130, 224), (70, 1568), (64, 512), (1000, 4096)])
-@pytest.mark.parametrize("m", [33, 64, 65, 100, 128])
+@pytest.mark.parametrize("m", [33, 64, 65, 100, 128, 129, 200])
 def test_gemm_k_split_tiles(q4, orc, n, k, m):
-    """the K-split MFMA kernel's three tiles (m <= 32 / 64 / 128) and its
-    k > 4096 fallback tile, on layouts from L = 8 to 64 (steps that run past
-    a row's pairs, several M blocks, ragged n)"""
+    """the K-split MFMA kernel's tiles (64 weight rows for m <= 64, 128 above;
+    32 / 64 / 128 activation rows) and the k > 4096 fallbacks (64-row tiles
+    up to m = 128, the weight-direct kernel above), on layouts from L = 8 to
+    64 (steps that run past a row's pairs, several M blocks, ragged n)"""
     rng = np.random.default_rng(n + 3 * k + 7 * m)
     w, s = si.draw_weight(rng, n, k)
     X = si.draw_X(rng, m, k)

@@ -783,8 +783,10 @@ __global__ __launch_bounds__(256) void gemm_mfma_wx_kernel(const uint8_t *__rest
 // time) and rounded once to f16.  Per step a wavefront does 4 NA MT MFMAs
 // against 4 NA dequantized words and 4 MT LDS fragment reads; every weight
 // byte is dequantized once per M block, every X byte passes through LDS
-// once per weight slab.
-template <int L, int CG, int NA, int MT, int NW, int D, int FMT = 4>
+// once per weight slab.  XR < BM: only the first XR activation rows exist
+// (m <= XR), so only those are loaded and staged; the slab rows past them
+// are zeroed once.
+template <int L, int CG, int NA, int MT, int NW, int D, int FMT = 4, int XR = 32 * MT>
 __global__ __launch_bounds__(64 * NW) void gemm_mfma_ks_kernel(const uint8_t *__restrict__ wd,
                                                                int64_t wbytes,
                                                                const uint16_t *__restrict__ X,
@@ -803,9 +805,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ks_kernel(const uint8_t *__
     constexpr int XBUF = BM * XROW;                  // halves per slab buffer
     constexpr int PROW = BN + 4;                     // floats per row of a partial tile
     constexpr int REGION = 4 * XBUF > 4 * 32 * PROW ? 4 * XBUF : 4 * 32 * PROW;   // bytes per wavefront
-    constexpr int XC = BM / 8;                       // 16-byte X pieces per lane per step
+    constexpr int XC = XR / 8;                       // 16-byte X pieces per lane per step
     constexpr int OPT = BN / (2 * NW);               // outputs per thread per 32 rows of the final sum
     static_assert((OPT == 2 || OPT % 4 == 0) && BN % OPT == 0 && D >= 2, "unsupported BN / NW / D");
+    static_assert(XR % 8 == 0 && XR <= BM, "X rows per slab");
     __shared__ __attribute__((aligned(16))) uint8_t lds[NW * REGION];
 
     const int tid = threadIdx.x;
@@ -992,6 +995,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ks_kernel(const uint8_t *__
 #pragma unroll
     for (int i = 0; i < D; ++i)
         load(ring[i], i);
+    if constexpr (XR < BM) {
+        // rows XR .. BM - 1 of both slab buffers: 16-byte zeros, 8 per row
+#pragma unroll
+        for (int q = lane; q < 2 * (BM - XR) * 8; q += 64) {
+            const int buf = q / ((BM - XR) * 8), rr = XR + (q / 8) % (BM - XR), ch = q % 8;
+            *reinterpret_cast<uint4 *>(xslab(buf) + rr * XROW + ch * 8) = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
     store_x(ring[0], 0);
 #pragma unroll
     for (int i = 0; i < SW; ++i) {
@@ -1122,7 +1133,7 @@ hipError_t launch_mfma_wx(const Geometry &geo, const uint8_t *wd, const uint16_t
     return hipGetLastError();
 }
 
-template <int L, int CG, int NA, int MT, int NW, int D, int FMT>
+template <int L, int CG, int NA, int MT, int NW, int D, int FMT, int XR = 32 * MT>
 hipError_t launch_mfma_ks(const Geometry &geo, const uint8_t *wd, const uint16_t *X, int64_t m,
                           int64_t n, int64_t k, uint16_t *Y, hipStream_t stream)
 {
@@ -1131,7 +1142,7 @@ hipError_t launch_mfma_ks(const Geometry &geo, const uint8_t *wd, const uint16_t
     const int64_t mbl = (m + BM - 1) / BM;
     const int64_t padded = mbl > 1 ? (nbn + 7) / 8 * 8 : nbn;
     const int64_t wbytes = geo.tiles * geo.tile_bytes;
-    hipLaunchKernelGGL((gemm_mfma_ks_kernel<L, CG, NA, MT, NW, D, FMT>), dim3((unsigned)(padded * mbl)),
+    hipLaunchKernelGGL((gemm_mfma_ks_kernel<L, CG, NA, MT, NW, D, FMT, XR>), dim3((unsigned)(padded * mbl)),
                        dim3(64 * NW), 0, stream, wd, wbytes, X, Y, m, n, k, nbn, padded);
     return hipGetLastError();
 }
@@ -1143,11 +1154,16 @@ hipError_t launch_mfma_lc(const Geometry &geo, const uint8_t *wd, const uint16_t
     // K-split kernel tiles (A tiles NA x 32 weight rows, MT x 32 activation
     // rows, NW wavefronts, D steps in flight) with the measured fastest per
     // m on 16384 x 3072, us at m = 4 / 16 / 32 / 64 / 128 / 192 / 256: 10.8 /
-    // 12.3 / 13.8 / 19.3 / 26.6 / 38.1 / 41.2, against 13.0 / 12.9 / 18.4 /
+    // 11.9 / 13.8 / 19.3 / 26.6 / 38.1 / 41.2, against 13.0 / 12.9 / 18.4 /
     // 25.9 / 34.5 / 45.6 / 47.8 for the X-resident and weight-direct kernels
-    // they replaced.  Beyond k = 4096 the 4-wavefront tiles unroll too many
+    // they replaced; up to 8 and 16 rows only those X rows are staged (m =
+    // 16: 11.9 against 12.4 us staging all 32).  Beyond k = 4096 the 4-wavefront tiles unroll too many
     // steps per wavefront and spill: two 64-row M blocks of 8 wavefronts up
     // to m = 128, the weight-direct kernel above.
+    if (m <= 8)
+        return launch_mfma_ks<L, CG, 2, 1, 16, 2, FMT, 8>(geo, wd, X, m, n, k, Y, stream);
+    if (m <= 16)
+        return launch_mfma_ks<L, CG, 2, 1, 16, 2, FMT, 16>(geo, wd, X, m, n, k, Y, stream);
     if (m <= 32)
         return launch_mfma_ks<L, CG, 2, 1, 16, 2, FMT>(geo, wd, X, m, n, k, Y, stream);
     if (m <= 64)

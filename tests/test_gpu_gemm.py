@@ -161,3 +161,20 @@ def test_gemm_k_split_tiles(q4, orc, n, k, m):
     Y, _ = run(q4, w, s, X)
     ref, a = orc.gemm(w, s, X)
     assert_within(host_f16_as_f64(Y), ref, tol_f16(ref, a), f"gemm {n}x{k} m={m}")
+
+
+@pytest.mark.parametrize("m", [5, 64, 200])
+def test_gemm_repeat_bit_identical(q4, orc, m):
+    """the K-split kernel adds its wavefronts' partial tiles in a fixed order:
+    three calls on the same inputs give the same bits (and sit within the
+    oracle's bound)"""
+    rng = np.random.default_rng(900 + m)
+    n, k = 700, 3072
+    w, s = si.draw_weight(rng, n, k)
+    X = si.draw_X(rng, m, k)
+    Y0, pw = run(q4, w, s, X)
+    Xd = dev_f16(X)
+    for _ in range(2):
+        assert np.array_equal(host_u16(q4.gemm(pw, Xd)), host_u16(Y0))
+    ref, a = orc.gemm(w, s, X)
+    assert_within(host_f16_as_f64(Y0), ref, tol_f16(ref, a), f"gemm m={m}")
